@@ -1,0 +1,154 @@
+/*
+ * nha.h -- C ABI of the Native Hybrid Attention (NHA) layer operator for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator (Paper-Notes page "Native Hybrid Attention for Efficient
+ * Sequence Modeling", sections 整体框架 and 关键设计 > 层内混合; gist.science
+ * page, "Mecanismo de Funcionamento"): per (batch, KV head) it keeps m
+ * long-term key/value slots updated by a gated linear RNN,
+ *     K_long <- Diag(alpha_t) K_long + (1 - alpha_t) (x) k,   V_long likewise,
+ * where a token enters the slots only when it leaves the sliding window (token
+ * shift: at step t >= w the token t - w is absorbed with gate alpha_t).  The
+ * slots are concatenated with the w most recent exact tokens and ONE softmax,
+ * scaled by 1/sqrt(d), runs over all m + w keys; RoPE (rotate-half, theta_i =
+ * base^(-2i/d), absolute positions) is applied to the window query/keys only.
+ * w = 0 is a pure gated-slot RNN; w >= T is causal softmax attention plus the m
+ * never-written (zero) slots.
+ *
+ * Three calls follow the pages' statement of the problem:
+ *   nha_fwd          chunkwise-parallel forward over a whole sequence (the
+ *                    "Chunkwise 并行计算" section of the Paper-Notes page);
+ *   nha_bwd          gradients dq, dk, dv, dalpha of the same forward
+ *                    (training, ibid. 局限与展望: the chunk kernel serves training);
+ *   nha_decode_step  one token of recurrent ("RNN mode") inference
+ *                    (ibid. 局限与展望; ai.info page, "Why This Matters").
+ *
+ * ---------------------------------------------------------------- conventions
+ * Pointers: every tensor argument is a DEVICE pointer (hipMalloc'd or from a
+ * framework allocator) unless stated otherwise; the descriptor is a HOST
+ * pointer.  Layouts are dense, row-major, in this dimension order:
+ *     q, o, dO, dq   [B][T][H][d]          k, v, dk, dv  [B][T][Hkv][d]
+ *     alpha          [B][T][Hkv][m]        dalpha        [B][T][Hkv][m] (float)
+ *     lse            [B][H][T] (float)     natural-log sum-exp of the scaled
+ *                                          logits over all m + n_w keys
+ * Query head h reads KV head h / (H / Hkv) (grouped-query attention).
+ * Element type of q, k, v, alpha, o, dO, dq, dk, dv is desc->dtype.
+ * Pointers must be 16-byte aligned.
+ *
+ * Ownership: the caller allocates every buffer, including the workspace and
+ * the decode state.  The library never allocates, frees or synchronises, keeps
+ * no global mutable state, and only enqueues work on the caller's stream
+ * (`stream` is a hipStream_t passed as void*; NULL = the null stream).  Calls
+ * return before the GPU has run; buffers must stay alive until the stream work
+ * completes.  Calls on distinct buffers are thread-safe.
+ *
+ * Errors: every argument check runs on the host before any HIP call and
+ * returns a status; nothing throws across the ABI and nothing aborts.  A
+ * failed launch returns NHA_ERR_HIP.  Faults inside a kernel surface at the
+ * caller's next stream synchronisation, as usual in HIP.
+ *
+ * Determinism: no atomics are used; results are bitwise reproducible for the
+ * same inputs, shapes and device.
+ */
+#ifndef NHA_H_
+#define NHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NHA_OK = 0,
+  NHA_ERR_INVALID_ARG = 1, /* null pointer, negative size, H % Hkv != 0, misaligned pointer */
+  NHA_ERR_UNSUPPORTED = 2, /* valid but not implemented (d, m, C, or tile budget) */
+  NHA_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the *_workspace_size() query */
+  NHA_ERR_HIP = 4          /* a HIP launch failed (no device, bad stream, ...) */
+} nha_status;
+
+typedef enum { NHA_DTYPE_F32 = 0, NHA_DTYPE_BF16 = 1 } nha_dtype;
+
+typedef struct {
+  int32_t B;         /* batch, >= 1 */
+  int32_t T;         /* sequence length, >= 1 (decode: ignored) */
+  int32_t H;         /* query heads, >= 1 */
+  int32_t Hkv;       /* KV heads, >= 1, H % Hkv == 0 */
+  int32_t d;         /* head dim: 32, 64 or 128 */
+  int32_t m;         /* long-term slots: 1 .. 64 */
+  int32_t w;         /* sliding window, >= 0; w >= T allowed (full attention) */
+  int32_t C;         /* chunk length of the chunkwise form: 16, 32 or 64.
+                        Results do not depend on C beyond rounding. */
+  float rope_base;   /* > 0: RoPE base; 0: RoPE disabled */
+  float scale;       /* softmax scale; 0 means 1/sqrt(d) */
+  int32_t dtype;     /* nha_dtype of the tensor arguments */
+} nha_desc;
+
+/* Workspace bytes that nha_fwd / nha_bwd need for this descriptor; 0 when the
+ * descriptor is invalid or unsupported (call nha_check_desc for the reason). */
+size_t nha_fwd_workspace_size(const nha_desc* desc);
+size_t nha_bwd_workspace_size(const nha_desc* desc);
+
+/* Validate a descriptor without touching the GPU. */
+nha_status nha_check_desc(const nha_desc* desc);
+
+/* Decode-state bytes for this descriptor (desc->T is ignored).  Layout, in
+ * this order, each part starting at a 256-byte aligned offset:
+ *   SK   float [B][Hkv][m][d]   long-term key slots
+ *   SV   float [B][Hkv][m][d]   long-term value slots
+ *   RK   dtype [B][Hkv][w][d]   ring of the last w raw (unrotated) keys;
+ *                               position j lives at row j mod w
+ *   RV   dtype [B][Hkv][w][d]   ring of the last w values
+ *   pos  int64 [B][Hkv]         tokens consumed so far (all equal)
+ * A zero-filled state is the state before the first token. */
+size_t nha_decode_state_size(const nha_desc* desc);
+
+/* Forward over the whole sequence.
+ *   q, k, v, alpha  inputs (device), layouts above; alpha in [0, 1]
+ *   o               output (device) [B][T][H][d], desc->dtype
+ *   lse             output (device) [B][H][T] float; may be NULL
+ *   state_out       may be NULL; else a decode state (nha_decode_state_size
+ *                   bytes) that receives the state after token T-1, so that
+ *                   nha_decode_step continues the sequence at position T
+ *   ws, ws_bytes    device workspace of >= nha_fwd_workspace_size bytes
+ *   stream          hipStream_t */
+nha_status nha_fwd(const nha_desc* desc, const void* q, const void* k,
+                   const void* v, const void* alpha, void* o, float* lse,
+                   void* state_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of nha_fwd.
+ *   o, lse          the forward's outputs for the same inputs (lse required)
+ *   dO              gradient of the loss w.r.t. o, [B][T][H][d]
+ *   dq, dk, dv      outputs, desc->dtype, fully overwritten
+ *   dalpha          output float [B][T][Hkv][m], fully overwritten;
+ *                   dalpha_t = 0 for t < w (no absorption happens there).
+ *                   Computed as (E_t - F_t) / alpha_t, so gates that round to
+ *                   0 give large relative errors there. */
+nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k,
+                   const void* v, const void* alpha, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk,
+                   void* dv, float* dalpha, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* One recurrent step at the position stored in the state (per (b, g)).
+ *   q_t [B][H][d], k_t, v_t [B][Hkv][d], alpha_t [B][Hkv][m]  (desc->dtype)
+ *   state           in/out decode state (see nha_decode_state_size)
+ *   o_t             output [B][H][d]
+ * At position t it absorbs the token leaving the window (t >= w) with
+ * alpha_t, pushes (k_t, v_t), reads m slots + min(w, t+1) window tokens
+ * through one softmax, writes o_t and advances the position by one.  The
+ * result equals nha_fwd over the concatenated sequence at row t. */
+nha_status nha_decode_step(const nha_desc* desc, const void* q_t,
+                           const void* k_t, const void* v_t,
+                           const void* alpha_t, void* state, void* o_t,
+                           void* stream);
+
+/* Static string for a status code. */
+const char* nha_status_string(nha_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NHA_H_ */

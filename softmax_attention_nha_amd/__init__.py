@@ -1,0 +1,225 @@
+"""Native Hybrid Attention (NHA) layer operator for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libnha.so`` (the C ABI in ``include/nha.h``).  This
+module only marshals arguments: it checks tensor shapes/dtypes/devices,
+allocates outputs and workspaces through PyTorch, and passes raw device
+pointers plus the current HIP stream.  Every step of the operator runs in the
+library's HIP kernels; there is no fallback path.  If the library is missing,
+``load()`` raises.
+
+    from softmax_attention_nha_amd import fwd, bwd, decode_state, decode_step
+    o, lse = fwd(q, k, v, alpha, w=512)                # q [B,T,H,d], k/v [B,T,Hkv,d]
+    dq, dk, dv, dalpha = bwd(q, k, v, alpha, o, lse, dO, w=512)
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnha.so")
+
+NHA_OK, NHA_ERR_INVALID_ARG, NHA_ERR_UNSUPPORTED, NHA_ERR_WORKSPACE, NHA_ERR_HIP = range(5)
+NHA_DTYPE_F32, NHA_DTYPE_BF16 = 0, 1
+_DTYPES = {torch.float32: NHA_DTYPE_F32, torch.bfloat16: NHA_DTYPE_BF16}
+
+EXPORTED = (
+    "nha_fwd_workspace_size",
+    "nha_bwd_workspace_size",
+    "nha_check_desc",
+    "nha_decode_state_size",
+    "nha_fwd",
+    "nha_bwd",
+    "nha_decode_step",
+    "nha_status_string",
+)
+
+
+class NhaDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("m", ctypes.c_int32),
+        ("w", ctypes.c_int32),
+        ("C", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class NhaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s" % (what, _lib_status(status)))
+
+
+_lib = None
+
+
+def load():
+    """Load libnha.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libnha.so not found at %s: build it with `python -m softmax_attention_nha_amd.build` "
+            "(or __graft_entry__.build())" % LIB_PATH
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    D = ctypes.POINTER(NhaDesc)
+    lib.nha_fwd_workspace_size.argtypes = [D]
+    lib.nha_fwd_workspace_size.restype = sz
+    lib.nha_bwd_workspace_size.argtypes = [D]
+    lib.nha_bwd_workspace_size.restype = sz
+    lib.nha_decode_state_size.argtypes = [D]
+    lib.nha_decode_state_size.restype = sz
+    lib.nha_check_desc.argtypes = [D]
+    lib.nha_check_desc.restype = st
+    lib.nha_fwd.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.nha_fwd.restype = st
+    lib.nha_bwd.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.nha_bwd.restype = st
+    lib.nha_decode_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
+    lib.nha_decode_step.restype = st
+    lib.nha_status_string.argtypes = [st]
+    lib.nha_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _lib_status(s):
+    try:
+        return load().nha_status_string(int(s)).decode()
+    except Exception:  # pragma: no cover - only when the library itself is missing
+        return "status %d" % s
+
+
+def make_desc(B, T, H, Hkv, d, m, w, C=64, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16):
+    return NhaDesc(int(B), int(T), int(H), int(Hkv), int(d), int(m), int(w), int(C), float(rope_base),
+                   float(scale), _DTYPES[dtype])
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s: expected dtype %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _desc_from(q, k, alpha, w, C, rope_base, scale):
+    if q.dim() != 4 or k.dim() != 4 or alpha.dim() != 4:
+        raise ValueError("q, k, alpha must be 4-D: [B,T,H,d], [B,T,Hkv,d], [B,T,Hkv,m]")
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    if q.dtype not in _DTYPES:
+        raise ValueError("dtype must be float32 or bfloat16")
+    return make_desc(B, T, H, Hkv, d, m, w, C, rope_base, scale, q.dtype)
+
+
+def workspace_size(desc, backward=False):
+    lib = load()
+    n = (lib.nha_bwd_workspace_size if backward else lib.nha_fwd_workspace_size)(ctypes.byref(desc))
+    if n == 0:
+        raise NhaError(lib.nha_check_desc(ctypes.byref(desc)), "workspace size")
+    return n
+
+
+def decode_state_size(desc):
+    lib = load()
+    n = lib.nha_decode_state_size(ctypes.byref(desc))
+    if n == 0:
+        raise NhaError(lib.nha_check_desc(ctypes.byref(desc)), "decode state size")
+    return n
+
+
+def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, workspace=None, out=None,
+        lse_out=None):
+    """Chunkwise-parallel forward. Returns (o [B,T,H,d], lse [B,H,T] float32).
+
+    state_out: optional uint8 decode state tensor (decode_state()) that receives
+    the state after the last token."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
+    dev, dt = q.device, q.dtype
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    _check(q, "q", (B, T, H, d), dt, dev)
+    _check(k, "k", (B, T, Hkv, d), dt, dev)
+    _check(v, "v", (B, T, Hkv, d), dt, dev)
+    _check(alpha, "alpha", (B, T, Hkv, m), dt, dev)
+    lib = load()
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    n = workspace_size(desc)
+    ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(n, dtype=torch.uint8, device=dev)
+    rc = lib.nha_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
+                     _ptr(state_out), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_fwd")
+    return o, lse
+
+
+def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, workspace=None):
+    """Gradients of fwd. Returns (dq, dk, dv, dalpha); dalpha is float32."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
+    dev, dt = q.device, q.dtype
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    for t, nm, shp in ((q, "q", (B, T, H, d)), (k, "k", (B, T, Hkv, d)), (v, "v", (B, T, Hkv, d)),
+                       (alpha, "alpha", (B, T, Hkv, m)), (o, "o", (B, T, H, d)), (dO, "dO", (B, T, H, d))):
+        _check(t, nm, shp, dt, dev)
+    _check(lse, "lse", (B, H, T), torch.float32, dev)
+    lib = load()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da = torch.empty((B, T, Hkv, m), dtype=torch.float32, device=dev)
+    n = workspace_size(desc, backward=True)
+    ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(n, dtype=torch.uint8, device=dev)
+    rc = lib.nha_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO),
+                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_bwd")
+    return dq, dk, dv, da
+
+
+def decode_state(B, H, Hkv, d, m, w, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16, device="cuda"):
+    """A zero decode state (the state before the first token)."""
+    desc = make_desc(B, 1, H, Hkv, d, m, w, 64, rope_base, scale, dtype)
+    return torch.zeros(decode_state_size(desc), dtype=torch.uint8, device=device)
+
+
+def decode_step(q_t, k_t, v_t, alpha_t, state, w, rope_base=10000.0, scale=0.0, out=None):
+    """One recurrent step. q_t [B,H,d], k_t/v_t [B,Hkv,d], alpha_t [B,Hkv,m]. Returns o_t [B,H,d]."""
+    B, H, d = q_t.shape
+    Hkv, m = k_t.shape[1], alpha_t.shape[2]
+    dev, dt = q_t.device, q_t.dtype
+    _check(k_t, "k_t", (B, Hkv, d), dt, dev)
+    _check(v_t, "v_t", (B, Hkv, d), dt, dev)
+    _check(alpha_t, "alpha_t", (B, Hkv, m), dt, dev)
+    desc = make_desc(B, 1, H, Hkv, d, m, w, 64, rope_base, scale, dt)
+    if state.numel() < decode_state_size(desc):
+        raise ValueError("decode state too small")
+    o = torch.empty_like(q_t) if out is None else out
+    rc = load().nha_decode_step(ctypes.byref(desc), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(alpha_t), _ptr(state),
+                                _ptr(o), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_decode_step")
+    return o

@@ -1,0 +1,148 @@
+// nha_api.cpp -- the C ABI declared in include/nha.h.
+//
+// Host-side validation, workspace sizing and dispatch.  Every check runs before
+// the first HIP call, so argument errors are reported on hosts without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "nha_internal.h"
+
+using namespace nha;
+
+namespace {
+
+constexpr size_t kMaxDecodeLds = 144 * 1024;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Fill `s` from the descriptor; `need_T` = false for decode (T ignored).
+nha_status make_shape(const nha_desc* d, bool need_T, Shape* s) {
+  if (!d) return NHA_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->Hkv < 1 || d->w < 0 || d->m < 1 || d->d < 1) return NHA_ERR_INVALID_ARG;
+  if (need_T && d->T < 1) return NHA_ERR_INVALID_ARG;
+  if (d->H % d->Hkv) return NHA_ERR_INVALID_ARG;
+  if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return NHA_ERR_INVALID_ARG;
+  if (!(d->scale >= 0.f) || !isfinite(d->scale)) return NHA_ERR_INVALID_ARG;
+  if (d->dtype != NHA_DTYPE_F32 && d->dtype != NHA_DTYPE_BF16) return NHA_ERR_INVALID_ARG;
+  if (d->d != 32 && d->d != 64 && d->d != 128) return NHA_ERR_UNSUPPORTED;
+  if (d->m > 64) return NHA_ERR_UNSUPPORTED;
+  if (d->C != 16 && d->C != 32 && d->C != 64) return NHA_ERR_UNSUPPORTED;
+  s->B = d->B;
+  s->T = need_T ? d->T : 1;
+  s->H = d->H;
+  s->Hkv = d->Hkv;
+  s->d = d->d;
+  s->m = d->m;
+  s->w = d->w;
+  s->C = d->C;
+  s->G = d->H / d->Hkv;
+  s->mp = d->m <= 32 ? 32 : 64;
+  s->NC = (s->T + s->C - 1) / s->C;
+  s->NQ = (s->T + 63) / 64;
+  s->rope = d->rope_base > 0.f;
+  s->win = d->w > 0;
+  s->scale = d->scale > 0.f ? d->scale : 1.f / sqrtf((float)d->d);
+  s->dtype = d->dtype;
+  s->esz = d->dtype == NHA_DTYPE_BF16 ? 2 : 4;
+  // grid limits (y dimension) and int32 row counts inside the kernels
+  if ((long long)s->B * s->H > 65535) return NHA_ERR_UNSUPPORTED;
+  if ((long long)s->B * s->T * s->H > (1LL << 31) / 8) return NHA_ERR_UNSUPPORTED;
+  if ((long long)s->T + s->w > (1LL << 31) - 1) return NHA_ERR_UNSUPPORTED;
+  if (need_T && slot_fwd_lds_bytes(*s) > kMaxLds) return NHA_ERR_UNSUPPORTED;
+  return NHA_OK;
+}
+
+RopeTheta make_theta(const nha_desc* d) {
+  RopeTheta th;
+  memset(&th, 0, sizeof(th));
+  if (d->rope_base > 0.f)
+    for (int i = 0; i < d->d / 2; ++i) th.theta[i] = pow((double)d->rope_base, -2.0 * i / d->d);
+  return th;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nha_status_string(nha_status s) {
+  switch (s) {
+    case NHA_OK: return "NHA_OK";
+    case NHA_ERR_INVALID_ARG: return "NHA_ERR_INVALID_ARG: invalid argument";
+    case NHA_ERR_UNSUPPORTED: return "NHA_ERR_UNSUPPORTED: valid but unsupported shape";
+    case NHA_ERR_WORKSPACE: return "NHA_ERR_WORKSPACE: workspace too small";
+    case NHA_ERR_HIP: return "NHA_ERR_HIP: HIP launch failed";
+  }
+  return "unknown nha_status";
+}
+
+nha_status nha_check_desc(const nha_desc* desc) {
+  Shape s;
+  return make_shape(desc, true, &s);
+}
+
+size_t nha_fwd_workspace_size(const nha_desc* desc) {
+  Shape s;
+  if (make_shape(desc, true, &s) != NHA_OK) return 0;
+  return fwd_ws_layout(s).total;
+}
+
+size_t nha_bwd_workspace_size(const nha_desc* desc) {
+  Shape s;
+  if (make_shape(desc, true, &s) != NHA_OK) return 0;
+  return bwd_ws_bytes(s);
+}
+
+size_t nha_decode_state_size(const nha_desc* desc) {
+  Shape s;
+  if (make_shape(desc, false, &s) != NHA_OK) return 0;
+  return state_layout(s).total;
+}
+
+nha_status nha_fwd(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                   void* o, float* lse, void* state_out, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  nha_status rc = make_shape(desc, true, &s);
+  if (rc != NHA_OK) return rc;
+  if (!q || !k || !v || !alpha || !o || !ws) return NHA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(o) || !aligned16(ws) ||
+      (lse && !aligned16(lse)) || (state_out && !aligned16(state_out)))
+    return NHA_ERR_INVALID_ARG;
+  if (ws_bytes < fwd_ws_layout(s).total) return NHA_ERR_WORKSPACE;
+  FwdPtrs p{q, k, v, alpha, o, lse, state_out, (char*)ws};
+  hipError_t e = launch_fwd(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                   const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* dalpha,
+                   void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  nha_status rc = make_shape(desc, true, &s);
+  if (rc != NHA_OK) return rc;
+  if (!q || !k || !v || !alpha || !o || !lse || !dO || !dq || !dk || !dv || !dalpha || !ws)
+    return NHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
+  if (ws_bytes < bwd_ws_bytes(s)) return NHA_ERR_WORKSPACE;
+  BwdPtrs p{q, k, v, alpha, o, dO, lse, dq, dk, dv, dalpha, (char*)ws};
+  hipError_t e = launch_bwd(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+nha_status nha_decode_step(const nha_desc* desc, const void* q_t, const void* k_t, const void* v_t,
+                           const void* alpha_t, void* state, void* o_t, void* stream) {
+  Shape s;
+  nha_status rc = make_shape(desc, false, &s);
+  if (rc != NHA_OK) return rc;
+  if (!q_t || !k_t || !v_t || !alpha_t || !state || !o_t) return NHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q_t, k_t, v_t, alpha_t, state, o_t};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
+  if ((size_t)16 * (s.m + s.w) > kMaxDecodeLds) return NHA_ERR_UNSUPPORTED;
+  DecodePtrs p{q_t, k_t, v_t, alpha_t, state, o_t};
+  hipError_t e = launch_decode(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,13 @@
+// nha_bwd.hip -- backward kernels of the NHA layer operator (gfx950).
+#include "nha_common.h"
+#include "nha_internal.h"
+
+namespace nha {
+
+size_t bwd_ws_bytes(const Shape& s) { return fwd_ws_layout(s).total; }
+
+hipError_t launch_bwd(const Shape&, const RopeTheta&, const BwdPtrs&, hipStream_t) {
+  return hipErrorNotSupported;
+}
+
+}  // namespace nha

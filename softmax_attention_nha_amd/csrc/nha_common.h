@@ -1,0 +1,157 @@
+// nha_common.h -- device helpers shared by the NHA kernels (gfx950 only).
+//
+// Matrix-core conventions used throughout (one 64-lane wavefront, lane l,
+// g = l / 16, c = l % 16):
+//   16x16 accumulator D (4 floats per lane):  lane l holds D[4g + r][c], r=0..3
+//   K=32 step (v_mfma_f32_16x16x32_bf16):      A frag = A[c][8g .. 8g+7]
+//                                             B frag = B[8g .. 8g+7][c]
+//   K=16 step (v_mfma_f32_16x16x16_bf16):      A frag = A[c][4g .. 4g+3]
+//                                             B frag = B[4g .. 4g+3][c]
+// For float operands the same per-lane fragments (8 or 4 consecutive k) are fed
+// to v_mfma_f32_16x16x4_f32 one k at a time: instruction s uses element s of
+// every lane, i.e. the k-subset {s, 8+s, 16+s, 24+s} (resp. {s, 4+s, ...}).
+// Summation over k is order-free, so both element types share every fragment
+// layout and every kernel is written once for T in {float, __bf16}.
+//
+// Because the K index of a step may be any permutation applied to both
+// operands, an accumulator tile in D layout (lane l holds rows 4g..4g+3 of
+// column c) can feed the next product directly as a B fragment:
+//   K=16: the 4 values themselves;   K=32: rows {4g+r} of block 2s and
+//   {4g+r} of block 2s+1, with the A fragment read in the same order
+//   (A[c][32s + 4g + r] and A[c][32s + 16 + 4g + r]).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#define NHA_LOG2E 1.4426950408889634f
+#define NHA_LN2 0.6931471805599453f
+// Floor of log2(alpha): gates below 2^-80 decay like 2^-80 (their slot is
+// overwritten to within 1e-24 relative either way); keeps every exponent
+// difference finite.
+#define NHA_LOG2A_MIN (-80.0f)
+
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
+template <> struct Vec<float> { typedef floatx8 v8; typedef floatx4 v4; };
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------- MFMA steps
+__device__ __forceinline__ floatx4 mma32(floatx4 acc, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma32(floatx4 acc, floatx8 a, floatx8 b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ floatx4 mma16(floatx4 acc, bf16x4 a, bf16x4 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma16(floatx4 acc, floatx4 a, floatx4 b) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+  return acc;
+}
+
+// ---------------------------------------------------------------- conversions
+template <typename T> __device__ __forceinline__ T to_t(float x);
+template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+// Pack 8 floats into a fragment of T.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 pack8(const float* f) {
+  typename Vec<T>::v8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = to_t<T>(f[i]);
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 pack8(floatx4 a, floatx4 b) {
+  typename Vec<T>::v8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = to_t<T>(a[i]);
+    r[4 + i] = to_t<T>(b[i]);
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v4 pack4(floatx4 a) {
+  typename Vec<T>::v4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = to_t<T>(a[i]);
+  return r;
+}
+
+// ---------------------------------------------------------------- loads / stores
+// 8 consecutive elements (16-byte aligned for bf16, 16-byte aligned for float).
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 ld8(const T* p) {
+  return *reinterpret_cast<const typename Vec<T>::v8*>(p);
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v4 ld4(const T* p) {
+  return *reinterpret_cast<const typename Vec<T>::v4*>(p);
+}
+// Two groups of 4 consecutive elements -> one K=32 fragment (permuted order).
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 ld4x2(const T* p0, const T* p1) {
+  typename Vec<T>::v4 a = ld4(p0), b = ld4(p1);
+  typename Vec<T>::v8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = a[i];
+    r[4 + i] = b[i];
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void st8(T* p, typename Vec<T>::v8 v) {
+  *reinterpret_cast<typename Vec<T>::v8*>(p) = v;
+}
+template <typename T>
+__device__ __forceinline__ void st4(T* p, typename Vec<T>::v4 v) {
+  *reinterpret_cast<typename Vec<T>::v4*>(p) = v;
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 zero8() {
+  typename Vec<T>::v8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = to_t<T>(0.f);
+  return r;
+}
+// 8 consecutive elements converted to float.
+template <typename T>
+__device__ __forceinline__ void ld8f(const T* p, float* f) {
+  typename Vec<T>::v8 v = ld8<T>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = to_f<T>(v[i]);
+}
+
+// ---------------------------------------------------------------- cross-lane
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+// Reduce over the 4 lane groups g (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float max_over_g(float x) {
+  x = fmaxf(x, shfl_xor(x, 16));
+  return fmaxf(x, shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_over_g(float x) {
+  x += shfl_xor(x, 16);
+  return x + shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Padded row pitch (elements) for LDS tiles of T with `cols` columns: keeps
+// 16-byte alignment and shifts consecutive rows across banks.
+__host__ __device__ constexpr int pitch_of(int cols) { return cols + 8; }

@@ -1,0 +1,732 @@
+// nha_fwd.hip -- forward kernels of the NHA layer operator (gfx950).
+//
+// The forward follows the chunkwise-parallel form described on the
+// Paper-Notes page "Native Hybrid Attention for Efficient Sequence Modeling",
+// section 关键设计 > Chunkwise 并行计算 (and the ai.info page, "Methodology in
+// Plain English"): the sequence is cut into chunks of C tokens; inside a chunk
+// the linear-channel (slot) logits come from cumulative / reverse gate
+// products, the window logits are ordinary shifted-window attention, both
+// enter one softmax, and the two value aggregations are summed.  Here the two
+// branches run in separate kernels and meet through the standard merge of two
+// partial softmaxes (the slot branch is handed to the window branch as one
+// "super key" with logit lse_L and value o_L / Z_L), which is exact.
+//
+// Per (batch b, KV head g), with a_t = alpha_t and b_t = 1 - alpha_t for
+// t >= w (a_t = 1, b_t = 0 before: nothing is absorbed yet), kappa_t = k_{t-w},
+// nu_t = v_{t-w} (token shift), the slot state obeys
+//     S_t = a_t (.) S_{t-1} + b_t (x) kappa_t .
+// Within chunk [t0, t0 + C) let G_u = sum_{j=t0..u} log2 a_j (per slot).  Then
+//     S_t = 2^{G_t} S_{t0-1} + sum_{u=t0..t} 2^{G_t - G_u} b_u (x) kappa_u .
+// Every exponent used below is of the form G_later - G_earlier <= 0, so no
+// factor exceeds 1:  the chunk is cut into 16-row blocks J, and a source row u
+// of block J is referred to E_J = G at the last row of J:
+//     2^{G_t - G_u} = 2^{G_t - E_J} * 2^{E_J - G_u}   (t beyond J, u in J),
+// while pairs inside one block use exact running products of a.
+//
+// Kernels, in launch order:
+//   k_rope          q, k -> R_t q, R_t k (rotate-half RoPE, fp64 angle reduction)
+//   k_chunk_gates   per chunk: W^T[i][u] = 2^{G_end - G_u} b_u and 2^{G_end}
+//   k_state_scan    sequential over chunks: S at every chunk start (MFMA)
+//   k_slot_fwd      slot logits, their softmax partial and o_L (MFMA)
+//   k_win_fwd       band-masked window attention seeded with the slot partial
+//   k_export_state  ring buffer + position of the decode state (optional)
+#include "nha_common.h"
+#include "nha_internal.h"
+
+namespace nha {
+
+// ---------------------------------------------------------------- RoPE
+// y[r] = R_pos x[r] for rows r of [B][T][heads][d]; pos = (r / heads) % T.
+// One thread rotates 8 frequency pairs (i, i + d/2).
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope(const T* __restrict__ x, T* __restrict__ y,
+                                              long nrows, int heads, int Tn, int d, RopeTheta th) {
+  long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  int per = d / 16;
+  long r = gid / per;
+  if (r >= nrows) return;
+  int i0 = (int)(gid % per) * 8;
+  int pos = (int)((r / heads) % Tn);
+  const T* xr = x + r * d;
+  T* yr = y + r * d;
+  float a[8], b[8], ya[8], yb[8];
+  ld8f<T>(xr + i0, a);
+  ld8f<T>(xr + i0 + d / 2, b);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    double ang = (double)pos * th.theta[i0 + e];
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+    float sn, cs;
+    sincosf((float)ang, &sn, &cs);
+    ya[e] = a[e] * cs - b[e] * sn;
+    yb[e] = b[e] * cs + a[e] * sn;
+  }
+  st8<T>(yr + i0, pack8<T>(ya));
+  st8<T>(yr + i0 + d / 2, pack8<T>(yb));
+}
+
+// ---------------------------------------------------------------- gate prep
+// grid (NC, B*Hkv), block MP threads (thread = slot i).
+// Wt[unit][c][i][u] = 2^{G_end,i - G_u,i} b_u,i   (0 for padded slots / rows)
+// aend[unit][c][i]  = 2^{G_end,i}
+template <typename T, int C>
+__global__ void k_chunk_gates(const T* __restrict__ alpha, T* __restrict__ Wt, float* __restrict__ aend,
+                              int Tn, int Hkv, int m, int mp, int w, int NC) {
+  int c = blockIdx.x, unit = blockIdx.y, i = threadIdx.x;
+  int b = unit / Hkv, g = unit % Hkv;
+  float G[C], bb[C];
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    int t = c * C + u;
+    float la = 0.f, be = 0.f;
+    if (i < m && t < Tn && t >= w) {
+      float al = to_f<T>(alpha[(((size_t)b * Tn + t) * Hkv + g) * m + i]);
+      la = fmaxf(__log2f(al), NHA_LOG2A_MIN);
+      be = 1.f - al;
+    }
+    acc += la;
+    G[u] = acc;
+    bb[u] = be;
+  }
+  T* dst = Wt + (((size_t)unit * NC + c) * mp + i) * C;
+#pragma unroll
+  for (int u0 = 0; u0 < C; u0 += 8) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = fast_exp2(acc - G[u0 + e]) * bb[u0 + e];
+    st8<T>(dst + u0, pack8<T>(f));
+  }
+  aend[((size_t)unit * NC + c) * mp + i] = fast_exp2(acc);
+}
+
+// ---------------------------------------------------------------- state scan
+// grid (d/16, B*Hkv), one wave.  Lane (g, c) keeps S^T[j0 + 4g + r][16 nb + c]
+// for K and V.  For every chunk: store S (state before the chunk), then
+// S <- aend (.) S + W^T . kappa  (transposed: dS^T = kappa^T W).
+template <typename T, int C, int MP>
+__global__ __launch_bounds__(64) void k_state_scan(const T* __restrict__ kk, const T* __restrict__ vv,
+                                                   const T* __restrict__ Wt, const float* __restrict__ aend,
+                                                   T* __restrict__ sst, float* __restrict__ skout,
+                                                   float* __restrict__ svout, int Tn, int Hkv, int d, int m,
+                                                   int w, int NC) {
+  constexpr int NB = MP / 16;
+  constexpr int PC = pitch_of(C);
+  constexpr bool K16 = (C % 32) != 0;
+  __shared__ T sKt[16 * PC];
+  __shared__ T sVt[16 * PC];
+  const int l = threadIdx.x, g = l >> 4, cc = l & 15;
+  const int j0 = blockIdx.x * 16, unit = blockIdx.y;
+  const int b = unit / Hkv, hg = unit % Hkv;
+  floatx4 SK[NB], SV[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) SK[nb] = SV[nb] = zero4();
+  const size_t chunk_elems = 2 * (size_t)MP * d;
+  for (int c = 0; c < NC; ++c) {
+    // state at the chunk start
+    T* dst = sst + ((size_t)unit * NC + c) * chunk_elems;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int i = 16 * nb + cc;
+      st4<T>(dst + (size_t)i * d + j0 + 4 * g, pack4<T>(SK[nb]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)MP * d + (size_t)(j0 + 4 * g + r) * MP + i] = to_t<T>(SV[nb][r]);
+    }
+    // kappa / nu columns j0..j0+15 of the chunk rows, transposed into LDS
+    if (l < C) {
+      int t = c * C + l;
+      typename Vec<T>::v8 k0 = zero8<T>(), k1 = zero8<T>(), v0 = zero8<T>(), v1 = zero8<T>();
+      if (t >= w && t < Tn) {
+        size_t row = (((size_t)b * Tn + (t - w)) * Hkv + hg) * d + j0;
+        k0 = ld8<T>(kk + row);
+        k1 = ld8<T>(kk + row + 8);
+        v0 = ld8<T>(vv + row);
+        v1 = ld8<T>(vv + row + 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sKt[e * PC + l] = k0[e];
+        sKt[(8 + e) * PC + l] = k1[e];
+        sVt[e * PC + l] = v0[e];
+        sVt[(8 + e) * PC + l] = v1[e];
+      }
+    }
+    __syncthreads();
+    const float* ae = aend + ((size_t)unit * NC + c) * MP;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float a = ae[16 * nb + cc];
+      SK[nb] *= a;
+      SV[nb] *= a;
+    }
+    const T* wsrc = Wt + ((size_t)unit * NC + c) * MP * C;
+    if constexpr (K16) {
+#pragma unroll
+      for (int s = 0; s < C / 16; ++s) {
+        typename Vec<T>::v4 ak = ld4<T>(&sKt[cc * PC + 16 * s + 4 * g]);
+        typename Vec<T>::v4 av = ld4<T>(&sVt[cc * PC + 16 * s + 4 * g]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          typename Vec<T>::v4 bw = ld4<T>(wsrc + (size_t)(16 * nb + cc) * C + 16 * s + 4 * g);
+          SK[nb] = mma16(SK[nb], ak, bw);
+          SV[nb] = mma16(SV[nb], av, bw);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < C / 32; ++s) {
+        typename Vec<T>::v8 ak = ld8<T>(&sKt[cc * PC + 32 * s + 8 * g]);
+        typename Vec<T>::v8 av = ld8<T>(&sVt[cc * PC + 32 * s + 8 * g]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          typename Vec<T>::v8 bw = ld8<T>(wsrc + (size_t)(16 * nb + cc) * C + 32 * s + 8 * g);
+          SK[nb] = mma32(SK[nb], ak, bw);
+          SV[nb] = mma32(SV[nb], av, bw);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (skout) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int i = 16 * nb + cc;
+      if (i < m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          skout[((size_t)unit * m + i) * d + j0 + 4 * g + r] = SK[nb][r];
+          svout[((size_t)unit * m + i) * d + j0 + 4 * g + r] = SV[nb][r];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- slot branch
+// grid (NC, B*H), C/16 waves; wave I owns chunk rows 16I .. 16I+15 (queries
+// are the N = 16 columns of every product).  Outputs the normalised slot
+// partial o_L / Z_L and lse_L = ln(sum_i exp(l_i)) over the m slot logits.
+template <typename T, int D, int MP, int C>
+struct SlotFwdSmem {
+  static constexpr int PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
+  T sSK[MP * PD];   // S^K_{t0-1} [i][d]
+  T sSVt[D * PM];   // S^V_{t0-1}^T [d][i]
+  T sK[C * PD];     // kappa rows [u][d]
+  T sVt[D * PC];    // nu^T [d][u]
+  T sA[C * PM];     // alpha [u][i] (raw gate; a/b derived with the row's t >= w)
+  T sB[C * PM];     // 2^{E_J - G_u} b_u  [u][i]
+  T sBt[MP * PC];   // same, [i][u]
+  float sG[C * MP]; // log2 cumsum [u][i]
+};
+
+template <typename T, int D, int MP, int C>
+__global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
+    const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
+    const T* __restrict__ sst, T* __restrict__ oL, float* __restrict__ lseL, int Tn, int H, int Hkv, int m,
+    int w, int NC, float scale) {
+  using S = SlotFwdSmem<T, D, MP, C>;
+  constexpr int NW = C / 16, NT = NW * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
+  __shared__ S sm;
+  const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, G = H / Hkv, hg = h / G;
+  const int unit = b * Hkv + hg, t0 = c * C;
+
+  // ---- cooperative loads
+  {
+    const T* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
+    for (int e = tid * 8; e < MP * D; e += NT * 8) {
+      int i = e / D, j = e % D;
+      st8<T>(&sm.sSK[i * PD + j], ld8<T>(src + e));
+    }
+    for (int e = tid * 8; e < MP * D; e += NT * 8) {
+      int j = e / MP, i = e % MP;
+      st8<T>(&sm.sSVt[j * PM + i], ld8<T>(src + (size_t)MP * D + e));
+    }
+    for (int e = tid * 8; e < C * D; e += NT * 8) {
+      int u = e / D, j = e % D, t = t0 + u;
+      typename Vec<T>::v8 kv = zero8<T>(), vvv = zero8<T>();
+      if (t >= w && t < Tn) {
+        size_t row = (((size_t)b * Tn + (t - w)) * Hkv + hg) * D + j;
+        kv = ld8<T>(kk + row);
+        vvv = ld8<T>(vv + row);
+      }
+      st8<T>(&sm.sK[u * PD + j], kv);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) sm.sVt[(j + x) * PC + u] = vvv[x];
+    }
+    for (int e = tid; e < C * MP; e += NT) {
+      int u = e / MP, i = e % MP, t = t0 + u;
+      T a = to_t<T>(1.f);
+      if (i < m && t < Tn) a = alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i];
+      sm.sA[u * PM + i] = a;
+    }
+  }
+  __syncthreads();
+  // log2 cumsum of the effective decay (slot per thread)
+  if (tid < MP) {
+    int i = tid;
+    float acc = 0.f;
+    for (int u = 0; u < C; ++u) {
+      int t = t0 + u;
+      float la = 0.f;
+      if (i < m && t < Tn && t >= w) la = fmaxf(__log2f(to_f<T>(sm.sA[u * PM + i])), NHA_LOG2A_MIN);
+      acc += la;
+      sm.sG[u * MP + i] = acc;
+    }
+  }
+  __syncthreads();
+  // B^(J)[u][i] = 2^{E_J - G_u} b_u, E_J = G at the last row of u's block
+  for (int e = tid; e < C * MP; e += NT) {
+    int u = e / MP, i = e % MP, t = t0 + u;
+    int last = (u | 15);
+    float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sm.sA[u * PM + i]) : 0.f;
+    float val = fast_exp2(sm.sG[last * MP + i] - sm.sG[u * MP + i]) * be;
+    T tv = to_t<T>(val);
+    sm.sB[u * PM + i] = tv;
+    sm.sBt[i * PC + u] = tv;
+  }
+  __syncthreads();
+
+  // ---- per-wave work: query rows r0 .. r0+15 of the chunk
+  const int r0 = 16 * I;
+  const int tq = t0 + r0 + cc;  // this lane's query
+  const bool qvalid = tq < Tn;
+  typename Vec<T>::v8 qf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qf[ks] = qvalid ? ld8<T>(q + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<T>();
+
+  // L^T[i][t] = S^K[i] . q_t
+  floatx4 accL[NB];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    accL[mb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      accL[mb] = mma32(accL[mb], ld8<T>(&sm.sSK[(16 * mb + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
+  }
+  // A^T[u][t] = kappa_u . q_t for u in blocks 0..I
+  floatx4 accA[NW];
+#pragma unroll
+  for (int ub = 0; ub < NW; ++ub) {
+    accA[ub] = zero4();
+    if (ub <= I) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        accA[ub] = mma32(accA[ub], ld8<T>(&sm.sK[(16 * ub + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
+    }
+  }
+  // logits (before scale): lg[mb][r] for slot i = 16 mb + 4 g + r ... careful: D layout
+  // of accL is [i = 16 mb + 4 g + r][t = cc].
+  const int urow = r0 + cc;  // this lane's query row inside the chunk
+  float lg[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int i = 16 * mb + 4 * g + r;
+      lg[mb][r] = fast_exp2(sm.sG[urow * MP + i]) * accL[mb][r];
+    }
+  // off-diagonal source blocks J < I
+#pragma unroll
+  for (int J = 0; J < NW; ++J) {
+    if (J < I) {
+      typename Vec<T>::v4 bfr = pack4<T>(accA[J]);  // A^T[16J + 4g + r][t]
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        floatx4 x = mma16(zero4(), ld4<T>(&sm.sBt[(16 * mb + cc) * PC + 16 * J + 4 * g]), bfr);
+        // x = X_J^T[i = 16mb + 4g + r][t]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int i = 16 * mb + 4 * g + r;
+          lg[mb][r] += fast_exp2(sm.sG[urow * MP + i] - sm.sG[(16 * J + 15) * MP + i]) * x[r];
+        }
+      }
+    }
+  }
+  // diagonal block: exact running products.  Lane needs A[t][u] for all u of block I.
+  floatx4 aI = accA[0];
+#pragma unroll
+  for (int ub = 1; ub < NW; ++ub)
+    if (ub == I) aI = accA[ub];
+  float Ad[16];
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ad[4 * gg + r] = __shfl(aI[r], cc + 16 * gg, 64);
+  {
+    float Dp[NB][4], dg[NB][4];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Dp[mb][r] = 1.f, dg[mb][r] = 0.f;
+#pragma unroll
+    for (int uu = 15; uu >= 0; --uu) {
+      if (uu <= cc) {
+        int u = r0 + uu, t = t0 + u;
+        bool absorb = (t >= w) && (t < Tn);
+        float au = Ad[uu];
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+          typename Vec<T>::v4 al = ld4<T>(&sm.sA[u * PM + 16 * mb + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float a = to_f<T>(al[r]);
+            float be = absorb ? 1.f - a : 0.f;
+            dg[mb][r] += au * Dp[mb][r] * be;
+            Dp[mb][r] *= absorb ? a : 1.f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lg[mb][r] += dg[mb][r];
+  }
+  // softmax partial over the m slots (log2 domain)
+  const float sl2 = scale * NHA_LOG2E;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int i = 16 * mb + 4 * g + r;
+      lg[mb][r] = (i < m) ? lg[mb][r] * sl2 : -INFINITY;
+      mx = fmaxf(mx, lg[mb][r]);
+    }
+  mx = max_over_g(mx);
+  float zs = 0.f;
+  float p[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[mb][r] = fast_exp2(lg[mb][r] - mx);
+      zs += p[mb][r];
+    }
+  zs = sum_over_g(zs);
+
+  // values: O^T[d][t] = S^V^T . (p 2^{G_t})^T + sum_J nu_J^T . Atil_J^T
+  floatx4 accO[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
+  {
+    float ph[NB][4];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ph[mb][r] = p[mb][r] * fast_exp2(sm.sG[urow * MP + 16 * mb + 4 * g + r]);
+#pragma unroll
+    for (int s = 0; s < NB / 2; ++s) {
+      float f[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f[r] = ph[2 * s][r], f[4 + r] = ph[2 * s + 1][r];
+      typename Vec<T>::v8 bfr = pack8<T>(f);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        accO[db] = mma32(accO[db],
+                         ld4x2<T>(&sm.sSVt[(16 * db + cc) * PM + 32 * s + 4 * g],
+                                  &sm.sSVt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]),
+                         bfr);
+    }
+  }
+#pragma unroll
+  for (int J = 0; J < NW; ++J) {
+    if (J < I) {
+      // Atil_J^T[u][t] = sum_i B^(J)[u][i] p_t[i] 2^{G_t - E_J}
+      floatx4 at = zero4();
+#pragma unroll
+      for (int s = 0; s < NB / 2; ++s) {
+        float f[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
+          f[r] = p[2 * s][r] * fast_exp2(sm.sG[urow * MP + i0] - sm.sG[(16 * J + 15) * MP + i0]);
+          f[4 + r] = p[2 * s + 1][r] * fast_exp2(sm.sG[urow * MP + i1] - sm.sG[(16 * J + 15) * MP + i1]);
+        }
+        at = mma32(at,
+                   ld4x2<T>(&sm.sB[(16 * J + cc) * PM + 32 * s + 4 * g],
+                            &sm.sB[(16 * J + cc) * PM + 32 * s + 16 + 4 * g]),
+                   pack8<T>(f));
+      }
+      typename Vec<T>::v4 bfr = pack4<T>(at);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        accO[db] = mma16(accO[db], ld4<T>(&sm.sVt[(16 * db + cc) * PC + 16 * J + 4 * g]), bfr);
+    }
+  }
+  // diagonal block of the value side: Atil[t][u] = sum_i p_t[i] Dprod b_u[i]
+  {
+    float Dp[NB][4];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Dp[mb][r] = 1.f;
+    float mine[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int uu = 15; uu >= 0; --uu) {
+      float cu = 0.f;
+      int u = r0 + uu, t = t0 + u;
+      bool absorb = (t >= w) && (t < Tn);
+      if (uu <= cc) {
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+          typename Vec<T>::v4 al = ld4<T>(&sm.sA[u * PM + 16 * mb + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float a = to_f<T>(al[r]);
+            float be = absorb ? 1.f - a : 0.f;
+            cu += p[mb][r] * Dp[mb][r] * be;
+            Dp[mb][r] *= absorb ? a : 1.f;
+          }
+        }
+      }
+      cu = sum_over_g(cu);
+      if ((uu >> 2) == g) mine[uu & 3] = cu;
+    }
+    typename Vec<T>::v4 bfr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bfr[r] = to_t<T>(mine[r]);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      accO[db] = mma16(accO[db], ld4<T>(&sm.sVt[(16 * db + cc) * PC + r0 + 4 * g]), bfr);
+  }
+  // normalised partial + its lse
+  if (qvalid) {
+    float inv = 1.f / zs;
+    T* dst = oL + (((size_t)b * Tn + tq) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db] * inv));
+    if (g == 0) lseL[((size_t)b * H + h) * Tn + tq] = (mx + __log2f(zs)) * NHA_LN2;
+  }
+}
+
+// ---------------------------------------------------------------- window branch
+// grid (ceil(T/64), B*H), 4 waves; wave W owns queries q0 + 16W .. +15.
+// Online softmax in log2 units, seeded with the slot partial as one key of
+// logit lse_L and value o_L / Z_L.  Writes o and lse.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_win_fwd(const T* __restrict__ qr, const T* __restrict__ kr,
+                                                 const T* __restrict__ vv, const T* __restrict__ oL,
+                                                 const float* __restrict__ lseL, T* __restrict__ o,
+                                                 float* __restrict__ lse, int Tn, int H, int Hkv, int w,
+                                                 float scale) {
+  constexpr int PD = pitch_of(D), PK = pitch_of(64);
+  __shared__ T sK[64 * PD];
+  __shared__ T sVt[D * PK];
+  const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int q0 = blockIdx.x * 64, bh = blockIdx.y, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  const int tq = q0 + 16 * W + cc;
+  const bool qvalid = tq < Tn;
+  typename Vec<T>::v8 qf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qf[ks] = qvalid ? ld8<T>(qr + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<T>();
+  // seed with the slot partial
+  float mu = qvalid ? lseL[((size_t)b * H + h) * Tn + tq] * NHA_LOG2E : 0.f;
+  float zl = (g == 0) ? 1.f : 0.f;  // lane-partial normaliser
+  floatx4 accO[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    accO[db] = zero4();
+    if (qvalid) {
+      typename Vec<T>::v4 x = ld4<T>(oL + (((size_t)b * Tn + tq) * H + h) * D + 16 * db + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accO[db][r] = to_f<T>(x[r]);
+    }
+  }
+  const float sl2 = scale * NHA_LOG2E;
+  if (w > 0) {
+    int kmin = q0 - w + 1;
+    if (kmin < 0) kmin = 0;
+    int kmax = q0 + 63;
+    if (kmax > Tn - 1) kmax = Tn - 1;
+    for (int j0 = (kmin / 64) * 64; j0 <= kmax; j0 += 64) {
+      __syncthreads();
+      for (int e = tid * 8; e < 64 * D; e += 256 * 8) {
+        int rr = e / D, j = e % D, key = j0 + rr;
+        typename Vec<T>::v8 kx = zero8<T>(), vx = zero8<T>();
+        if (key < Tn) {
+          size_t row = (((size_t)b * Tn + key) * Hkv + hg) * D + j;
+          kx = ld8<T>(kr + row);
+          vx = ld8<T>(vv + row);
+        }
+        st8<T>(&sK[rr * PD + j], kx);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) sVt[(j + x) * PK + rr] = vx[x];
+      }
+      __syncthreads();
+      const bool full = (j0 + 63 <= q0) && (j0 > q0 + 63 - w) && (j0 + 63 < Tn);
+      float s[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) acc = mma32(acc, ld8<T>(&sK[(16 * mb + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[r] * sl2;
+          if (!full) {
+            int key = j0 + 16 * mb + 4 * g + r;
+            bool ok = key <= tq && key > tq - w && key < Tn;
+            x = ok ? x : -INFINITY;
+          }
+          s[mb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = max_over_g(mx);
+      float mnew = fmaxf(mu, mx);
+      float resc = fast_exp2(mu - mnew);
+      mu = mnew;
+      zl *= resc;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) accO[db] *= resc;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pv = fast_exp2(s[mb][r] - mu);
+          s[mb][r] = pv;
+          zl += pv;
+        }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float f[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[r] = s[2 * st][r], f[4 + r] = s[2 * st + 1][r];
+        typename Vec<T>::v8 bfr = pack8<T>(f);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+          accO[db] = mma32(accO[db],
+                           ld4x2<T>(&sVt[(16 * db + cc) * PK + 32 * st + 4 * g],
+                                    &sVt[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
+                           bfr);
+      }
+    }
+  }
+  float z = sum_over_g(zl);
+  if (qvalid) {
+    float inv = 1.f / z;
+    T* dst = o + (((size_t)b * Tn + tq) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db] * inv));
+    if (g == 0 && lse) lse[((size_t)b * H + h) * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
+  }
+}
+
+// ---------------------------------------------------------------- decode-state export
+// Ring rows for positions max(0, T-w) .. T-1 and the position counter.
+template <typename T>
+__global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ vv, T* __restrict__ rk,
+                               T* __restrict__ rv, long long* __restrict__ pos, int Tn, int Hkv, int d,
+                               int w) {
+  int unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv;
+  int first = Tn - w > 0 ? Tn - w : 0;
+  int nrows = w > 0 ? Tn - first : 0;
+  for (int e = (blockIdx.x * blockDim.x + threadIdx.x) * 8; e < nrows * d; e += gridDim.x * blockDim.x * 8) {
+    int j = first + e / d, x = e % d;
+    size_t src = (((size_t)b * Tn + j) * Hkv + hg) * d + x;
+    size_t dst = ((size_t)unit * w + (j % w)) * d + x;
+    st8<T>(rk + dst, ld8<T>(kk + src));
+    st8<T>(rv + dst, ld8<T>(vv + src));
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) pos[unit] = Tn;
+}
+
+// ---------------------------------------------------------------- host launcher
+template <typename T, int D, int MP, int C>
+static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st) {
+  if constexpr (sizeof(SlotFwdSmem<T, D, MP, C>) > kMaxLds) {
+    return hipErrorInvalidConfiguration;
+  } else {
+  FwdWs L = fwd_ws_layout(s);
+  const T* q = (const T*)p.q;
+  const T* k = (const T*)p.k;
+  const T* v = (const T*)p.v;
+  const T* alpha = (const T*)p.alpha;
+  T* sst = (T*)(p.ws + L.sst);
+  T* wt = (T*)(p.ws + L.wt);
+  float* aend = (float*)(p.ws + L.aend);
+  T* ol = (T*)(p.ws + L.ol);
+  float* lsel = (float*)(p.ws + L.lsel);
+  const int units = s.B * s.Hkv;
+  const T* qr = q;
+  const T* kr = k;
+  if (s.rope && s.win) {
+    T* qrw = (T*)(p.ws + L.qrot);
+    T* krw = (T*)(p.ws + L.krot);
+    long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
+    long thq = nq * (s.d / 16), thk = nk * (s.d / 16);
+    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thq + 255) / 256)), dim3(256), 0, st, q, qrw, nq, s.H, s.T, s.d, th);
+    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thk + 255) / 256)), dim3(256), 0, st, k, krw, nk, s.Hkv, s.T, s.d, th);
+    qr = qrw;
+    kr = krw;
+  }
+  hipLaunchKernelGGL((k_chunk_gates<T, C>), dim3(s.NC, units), dim3(MP), 0, st, alpha, wt, aend, s.T, s.Hkv, s.m,
+                     MP, s.w, s.NC);
+  float* skout = nullptr;
+  float* svout = nullptr;
+  StateLayout SL{};
+  if (p.state_out) {
+    SL = state_layout(s);
+    skout = (float*)((char*)p.state_out + SL.sk);
+    svout = (float*)((char*)p.state_out + SL.sv);
+  }
+  hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, wt, aend, sst, skout,
+                     svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
+  hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
+                     sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
+  hipLaunchKernelGGL((k_win_fwd<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, ol, lsel, (T*)p.o,
+                     p.lse, s.T, s.H, s.Hkv, s.w, s.scale);
+  if (p.state_out && s.w > 0) {
+    char* base = (char*)p.state_out;
+    hipLaunchKernelGGL(k_export_state<T>, dim3(32, units), dim3(256), 0, st, k, v, (T*)(base + SL.rk),
+                       (T*)(base + SL.rv), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w);
+  } else if (p.state_out) {
+    char* base = (char*)p.state_out;
+    hipLaunchKernelGGL(k_export_state<T>, dim3(1, units), dim3(64), 0, st, k, v, (T*)nullptr, (T*)nullptr,
+                       (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0);
+  }
+  return hipGetLastError();
+  }
+}
+
+template <typename T, int MP, int C>
+static hipError_t fwd_d(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st) {
+  switch (s.d) {
+    case 32: return fwd_impl<T, 32, MP, C>(s, th, p, st);
+    case 64: return fwd_impl<T, 64, MP, C>(s, th, p, st);
+    case 128: return fwd_impl<T, 128, MP, C>(s, th, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+template <typename T, int MP>
+static hipError_t fwd_c(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st) {
+  switch (s.C) {
+    case 16: return fwd_d<T, MP, 16>(s, th, p, st);
+    case 32: return fwd_d<T, MP, 32>(s, th, p, st);
+    case 64: return fwd_d<T, MP, 64>(s, th, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+template <typename T>
+static hipError_t fwd_m(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st) {
+  if (s.mp == 32) return fwd_c<T, 32>(s, th, p, st);
+  return fwd_c<T, 64>(s, th, p, st);
+}
+
+hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st) {
+  if (s.dtype == NHA_DTYPE_BF16) return fwd_m<bf16>(s, th, p, st);
+  return fwd_m<float>(s, th, p, st);
+}
+
+size_t slot_fwd_lds_bytes(const Shape& s) {
+  size_t e = s.esz;
+  size_t PD = pitch_of(s.d), PM = pitch_of(s.mp), PC = pitch_of(s.C);
+  return e * (s.mp * PD + s.d * PM + s.C * PD + s.d * PC + 2 * s.C * PM + s.mp * PC) + 4 * (size_t)s.C * s.mp;
+}
+
+}  // namespace nha

@@ -1,0 +1,120 @@
+// nha_internal.h -- host-side plumbing shared by the C ABI and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nha.h"
+
+namespace nha {
+
+// RoPE frequencies theta_i = base^(-2i/d), computed on the host in double.
+struct RopeTheta {
+  double theta[64];
+};
+
+// Problem shape after validation.
+struct Shape {
+  int B, T, H, Hkv, d, m, w, C;
+  int G;      // H / Hkv
+  int mp;     // m padded to a multiple of 32
+  int NC;     // ceil(T / C)
+  int NQ;     // ceil(T / 64) query tiles of the window kernels
+  bool rope;  // RoPE enabled
+  bool win;   // w > 0
+  float scale;
+  int dtype;
+  int esz;    // element bytes
+};
+
+constexpr size_t kMaxLds = 160 * 1024;  // LDS bytes per workgroup on gfx950
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Forward workspace carve-up (offsets in bytes from the workspace base).
+struct FwdWs {
+  size_t sst;    // chunk-start states: [B*Hkv][NC][ SK (mp x d) | SVt (d x mp) ]  (dtype)
+  size_t wt;     // per-chunk absorption weights W^T: [B*Hkv][NC][mp][C]       (dtype)
+  size_t aend;   // per-chunk decay exp(G_end): [B*Hkv][NC][mp]                (float)
+  size_t qrot;   // RoPE'd q: [B][T][H][d]                                       (dtype)
+  size_t krot;   // RoPE'd k: [B][T][Hkv][d]                                     (dtype)
+  size_t ol;     // slot-branch partial output o_L / Z_L: [B][T][H][d]          (dtype)
+  size_t lsel;   // slot-branch partial lse: [B][H][T]                           (float)
+  size_t total;
+};
+
+inline FwdWs fwd_ws_layout(const Shape& s) {
+  FwdWs L;
+  size_t off = 0;
+  size_t units = (size_t)s.B * s.Hkv;
+  L.sst = off;
+  off += align256(units * s.NC * 2 * (size_t)s.mp * s.d * s.esz);
+  L.wt = off;
+  off += align256(units * s.NC * (size_t)s.mp * s.C * s.esz);
+  L.aend = off;
+  off += align256(units * s.NC * (size_t)s.mp * 4);
+  L.qrot = off;
+  if (s.rope && s.win) off += align256((size_t)s.B * s.T * s.H * s.d * s.esz);
+  L.krot = off;
+  if (s.rope && s.win) off += align256((size_t)s.B * s.T * s.Hkv * s.d * s.esz);
+  L.ol = off;
+  off += align256((size_t)s.B * s.T * s.H * s.d * s.esz);
+  L.lsel = off;
+  off += align256((size_t)s.B * s.H * s.T * 4);
+  L.total = off;
+  return L;
+}
+
+// Decode-state carve-up (see nha_decode_state_size in nha.h).
+struct StateLayout {
+  size_t sk, sv, rk, rv, pos, total;
+};
+inline StateLayout state_layout(const Shape& s) {
+  StateLayout L;
+  size_t units = (size_t)s.B * s.Hkv, off = 0;
+  L.sk = off;
+  off += align256(units * s.m * s.d * 4);
+  L.sv = off;
+  off += align256(units * s.m * s.d * 4);
+  L.rk = off;
+  off += align256(units * (size_t)s.w * s.d * s.esz);
+  L.rv = off;
+  off += align256(units * (size_t)s.w * s.d * s.esz);
+  L.pos = off;
+  off += align256(units * 8);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All launches go on `st`.
+struct FwdPtrs {
+  const void *q, *k, *v, *alpha;
+  void* o;
+  float* lse;
+  void* state_out;  // nullable
+  char* ws;
+};
+hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st);
+
+struct DecodePtrs {
+  const void *q, *k, *v, *alpha;
+  void* state;
+  void* o;
+};
+hipError_t launch_decode(const Shape& s, const RopeTheta& th, const DecodePtrs& p, hipStream_t st);
+
+size_t bwd_ws_bytes(const Shape& s);
+struct BwdPtrs {
+  const void *q, *k, *v, *alpha, *o, *dO;
+  const float* lse;
+  void *dq, *dk, *dv;
+  float* dalpha;
+  char* ws;
+};
+hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st);
+
+// LDS bytes the slot kernels need (0 = shape unsupported).
+size_t slot_fwd_lds_bytes(const Shape& s);
+
+}  // namespace nha

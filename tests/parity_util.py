@@ -1,0 +1,62 @@
+"""Helpers for the GPU parity tests: run the HIP path through the binding and
+the fp64 oracle on the same (exactly upcast) inputs, then compare."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import softmax_attention_nha_amd as nha
+
+# Tolerances.  fp32 inputs: max-abs 1e-4.  bf16 inputs with fp32 accumulation:
+# max-abs 2e-2 on outputs and 5e-2 on gradients; in addition (these max-abs
+# gates are loose at the workloads' small output magnitudes) a relative L2
+# error of 1e-2 per tensor.
+TOL = {
+    torch.float32: dict(o=1e-4, lse=1e-4, grad=1e-4, rel=1e-5),
+    torch.bfloat16: dict(o=2e-2, lse=2e-2, grad=5e-2, rel=1e-2),
+}
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(x):
+    return x.detach().float().cpu().double().numpy()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def gpu_fwd(q, k, v, a, w, C, base, state_out=None):
+    d = dev()
+    o, lse = nha.fwd(q.to(d), k.to(d), v.to(d), a.to(d), w, C=C, rope_base=base, state_out=state_out)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_fwd(q, k, v, a, w, base, threads=0):
+    return oracle.fwd(f64(q), f64(k), f64(v), f64(a), w, rope_base=base, threads=threads)
+
+
+def unit_slice(x, b, heads):
+    """Slice batch b and the given head indices (query or KV heads) of [B,T,heads,*]."""
+    return x[b:b + 1, :, heads[0]:heads[-1] + 1].contiguous()
+
+
+def compare(name, got, ref, atol, rel):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s: non-finite values" % name
+    err = np.abs(got - ref)
+    mx = float(err.max()) if err.size else 0.0
+    nrm = float(np.linalg.norm(ref))
+    r = float(np.linalg.norm(got - ref) / nrm) if nrm > 0 else float(np.linalg.norm(got - ref))
+    log("  %-8s max|err|=%.3e  rel-L2=%.3e  max|ref|=%.3e" % (name, mx, r, float(np.abs(ref).max()) if ref.size else 0))
+    assert mx <= atol, "%s: max abs error %.3e > %.1e" % (name, mx, atol)
+    assert r <= rel, "%s: relative L2 error %.3e > %.1e" % (name, r, rel)
+    return mx, r

@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/nha.h, and rejects bad arguments with the documented status
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import softmax_attention_nha_amd as nha
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "nha.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nha_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_exported_set():
+    assert declared_functions() == sorted(nha.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nha.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def desc(**kw):
+    base = dict(B=1, T=256, H=2, Hkv=2, d=32, m=8, w=16, C=16, rope_base=10000.0, scale=0.0, dtype=torch.float32)
+    base.update(kw)
+    return nha.make_desc(**base)
+
+
+def status(d):
+    return nha.load().nha_check_desc(ctypes.byref(d))
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({}, nha.NHA_OK),
+    ({"dtype": torch.bfloat16, "d": 128, "m": 64, "w": 512, "C": 64}, nha.NHA_OK),
+    ({"H": 3}, nha.NHA_ERR_INVALID_ARG),          # H % Hkv != 0
+    ({"B": 0}, nha.NHA_ERR_INVALID_ARG),
+    ({"T": 0}, nha.NHA_ERR_INVALID_ARG),
+    ({"w": -1}, nha.NHA_ERR_INVALID_ARG),
+    ({"m": 0}, nha.NHA_ERR_INVALID_ARG),
+    ({"rope_base": -1.0}, nha.NHA_ERR_INVALID_ARG),
+    ({"scale": -0.5}, nha.NHA_ERR_INVALID_ARG),
+    ({"d": 96}, nha.NHA_ERR_UNSUPPORTED),
+    ({"m": 65}, nha.NHA_ERR_UNSUPPORTED),
+    ({"C": 48}, nha.NHA_ERR_UNSUPPORTED),
+    ({"d": 128, "m": 64, "C": 64}, nha.NHA_ERR_UNSUPPORTED),  # fp32 tiles exceed the LDS budget
+])
+def test_descriptor_validation(kw, expected):
+    assert status(desc(**kw)) == expected
+
+
+def test_sizes_zero_for_invalid_and_positive_for_valid():
+    lib = nha.load()
+    good, bad = desc(), desc(H=3)
+    assert lib.nha_fwd_workspace_size(ctypes.byref(good)) > 0
+    assert lib.nha_bwd_workspace_size(ctypes.byref(good)) > 0
+    assert lib.nha_decode_state_size(ctypes.byref(good)) > 0
+    for f in (lib.nha_fwd_workspace_size, lib.nha_bwd_workspace_size, lib.nha_decode_state_size):
+        assert f(ctypes.byref(bad)) == 0
+
+
+def test_decode_state_size_matches_documented_layout():
+    d = desc(B=2, H=4, Hkv=2, d=64, m=8, w=16, dtype=torch.bfloat16)
+    a256 = lambda x: (x + 255) // 256 * 256
+    units = 2 * 2
+    expect = 2 * a256(units * 8 * 64 * 4) + 2 * a256(units * 16 * 64 * 2) + a256(units * 8)
+    assert nha.decode_state_size(d) == expect
+
+
+A = ctypes.c_void_p(4096)   # 16-byte aligned, never dereferenced on these paths
+MIS = ctypes.c_void_p(4098)  # misaligned
+
+
+def fwd_rc(d, q=A, ws=A, ws_bytes=1 << 40, lse=None):
+    return nha.load().nha_fwd(ctypes.byref(d), q, A, A, A, A, lse, None, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_fwd_argument_errors():
+    d = desc()
+    assert fwd_rc(d, q=ctypes.c_void_p(0)) == nha.NHA_ERR_INVALID_ARG
+    assert fwd_rc(d, q=MIS) == nha.NHA_ERR_INVALID_ARG
+    assert fwd_rc(d, lse=MIS) == nha.NHA_ERR_INVALID_ARG
+    assert fwd_rc(d, ws=ctypes.c_void_p(0)) == nha.NHA_ERR_INVALID_ARG
+    assert fwd_rc(d, ws_bytes=nha.workspace_size(d) - 1) == nha.NHA_ERR_WORKSPACE
+    assert fwd_rc(desc(H=3)) == nha.NHA_ERR_INVALID_ARG
+    assert fwd_rc(desc(d=96)) == nha.NHA_ERR_UNSUPPORTED
+
+
+def test_bwd_argument_errors():
+    lib = nha.load()
+    d = desc()
+    args = [A] * 11
+    rc = lib.nha_bwd(ctypes.byref(d), *args[:5], None, *args[5:10], A, ctypes.c_size_t(1 << 40), None)
+    assert rc == nha.NHA_ERR_INVALID_ARG  # lse is required
+    n = nha.workspace_size(d, backward=True)
+    rc = lib.nha_bwd(ctypes.byref(d), *args[:5], A, *args[5:10], A, ctypes.c_size_t(n - 1), None)
+    assert rc == nha.NHA_ERR_WORKSPACE
+
+
+def test_decode_argument_errors():
+    lib = nha.load()
+    d = desc()
+    assert lib.nha_decode_step(ctypes.byref(d), A, A, A, A, ctypes.c_void_p(0), A, None) == nha.NHA_ERR_INVALID_ARG
+    assert lib.nha_decode_step(ctypes.byref(d), A, A, MIS, A, A, A, None) == nha.NHA_ERR_INVALID_ARG
+    big = desc(w=1 << 20)
+    assert lib.nha_decode_step(ctypes.byref(big), A, A, A, A, A, A, None) == nha.NHA_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_launch_without_device_reports_hip_error():
+    assert fwd_rc(desc()) == nha.NHA_ERR_HIP
+
+
+def test_status_strings():
+    lib = nha.load()
+    for s in range(5):
+        assert lib.nha_status_string(s).startswith(b"NHA_")

@@ -1,0 +1,139 @@
+"""GPU forward parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs come from softmax_attention_nha_amd.inputs (seeded, synthetic, the
+workloads' shapes and distributions); the oracle receives their exact fp64
+upcast.  Small cases compare every element; full-size workloads compare one
+(batch, KV head) unit -- its query heads -- over a causal prefix the oracle
+finishes in seconds (rows t < T' depend only on tokens <= t)."""
+import numpy as np
+import pytest
+import torch
+
+from parity_util import TOL, compare, f64, gpu_fwd, log, oracle_fwd, unit_slice
+from softmax_attention_nha_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def check_full(wl, w=None, base=None, C=None, **draw):
+    w = wl.w if w is None else w
+    base = wl.rope_base if base is None else base
+    C = wl.C if C is None else C
+    log("case %s B=%d T=%d H=%d/%d d=%d m=%d w=%d C=%d base=%g %s %s" % (
+        wl.name, wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, w, C, base, wl.dtype, draw))
+    q, k, v, a = make_inputs(wl, **draw)
+    o, lse = gpu_fwd(q, k, v, a, w, C, base)
+    o_ref, l_ref = oracle_fwd(q, k, v, a, w, base)
+    tol = TOL[wl.dtype]
+    compare("o", f64(o), o_ref, tol["o"], tol["rel"])
+    compare("lse", f64(lse), l_ref, tol["lse"], tol["rel"])
+    return o, lse
+
+
+# ---------------------------------------------------------------- fp32 (max-abs 1e-4)
+@pytest.mark.parametrize("base", [10000.0, 0.0])
+def test_tiny_workload(base):
+    check_full(WORKLOADS["tiny"], base=base)
+
+
+@pytest.mark.parametrize("w", [0, 1, 15, 16, 17, 100, 200, 205])
+def test_fp32_window_sweep_ragged_gqa(w):
+    wl = WORKLOADS["tiny"].with_(T=200, H=4, Hkv=2, seed=11)
+    check_full(wl, w=w)
+
+
+@pytest.mark.parametrize("C,T,w", [(32, 150, 40), (64, 150, 40), (64, 300, 64), (16, 97, 31)])
+def test_fp32_chunk_sizes(C, T, w):
+    wl = WORKLOADS["tiny"].with_(T=T, seed=12)
+    check_full(wl, w=w, C=C)
+
+
+@pytest.mark.parametrize("m,d", [(1, 32), (33, 64), (64, 64), (32, 64)])
+def test_fp32_slots_and_head_dims(m, d):
+    wl = WORKLOADS["tiny"].with_(T=160, m=m, d=d, seed=13)
+    check_full(wl, w=24, C=32)
+
+
+# ---------------------------------------------------------------- bf16, every element at reduced T
+@pytest.mark.parametrize("name,w", [("340m", None), ("1p3b", 0), ("1p3b", 64), ("1p3b", 512), ("1p3b", 2048),
+                                    ("long", None), ("gqa", None)])
+def test_bf16_workloads_reduced(name, w):
+    wl = WORKLOADS[name]
+    wl = wl.with_(B=1, T=576 + 37 if (w is None or w < 600) else 700)
+    check_full(wl, w=w)
+
+
+def test_bf16_stress_logits_and_hard_gates():
+    wl = WORKLOADS["1p3b"].with_(B=1, T=448, H=2, Hkv=2, seed=21)
+    check_full(wl, w=96, qk_scale=1.0, alpha_mu=-2.0)
+
+
+def test_bf16_gates_that_round_to_one_and_zero():
+    wl = WORKLOADS["340m"].with_(B=1, T=320, H=2, Hkv=2, seed=22)
+    q, k, v, a = make_inputs(wl)
+    a = a.clone()
+    a[:, ::7] = 1.0
+    a[:, 3::11] = 0.0
+    log("case alpha with exact 0/1 entries")
+    o, lse = gpu_fwd(q, k, v, a, 64, 64, 10000.0)
+    o_ref, l_ref = oracle_fwd(q, k, v, a, 64, 10000.0)
+    compare("o", f64(o), o_ref, 2e-2, 1e-2)
+    compare("lse", f64(lse), l_ref, 2e-2, 1e-2)
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled
+def check_unit_prefix(wl, w, Tp, b, g):
+    G = wl.H // wl.Hkv
+    log("case %s full-size B=%d T=%d w=%d: unit b=%d g=%d prefix %d" % (wl.name, wl.B, wl.T, w, b, g, Tp))
+    q, k, v, a = make_inputs(wl)
+    o, lse = gpu_fwd(q, k, v, a, w, wl.C, wl.rope_base)
+    hq = list(range(g * G, (g + 1) * G))
+    sl = lambda x, heads: unit_slice(x, b, heads)[:, :Tp]
+    o_ref, l_ref = oracle_fwd(sl(q, hq), sl(k, [g]), sl(v, [g]), sl(a, [g]), w, wl.rope_base)
+    got_o = f64(o[b:b + 1, :Tp, hq[0]:hq[-1] + 1])
+    got_l = f64(lse[b:b + 1, hq[0]:hq[-1] + 1, :Tp])
+    tol = TOL[wl.dtype]
+    compare("o", got_o, o_ref, tol["o"], tol["rel"])
+    compare("lse", got_l, l_ref, tol["lse"], tol["rel"])
+    assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("name,w,Tp", [("340m", None, 2048), ("1p3b", 0, 2048), ("1p3b", 64, 2048),
+                                       ("1p3b", 512, 2048), ("1p3b", 2048, 2048), ("long", None, 8192),
+                                       ("gqa", None, 2304)])
+def test_full_size_workloads_sampled(name, w, Tp):
+    wl = WORKLOADS[name]
+    check_unit_prefix(wl, wl.w if w is None else w, Tp, wl.B - 1, wl.Hkv - 1)
+
+
+@pytest.mark.parametrize("T", [16384, 32768])
+def test_long_context_lengths_sampled(T):
+    wl = WORKLOADS["long"].with_(T=T)
+    check_unit_prefix(wl, wl.w, 2048, 0, wl.Hkv // 2)
+
+
+# ---------------------------------------------------------------- invariants on the GPU path
+def test_chunk_size_does_not_change_results():
+    wl = WORKLOADS["1p3b"].with_(B=1, T=512, H=2, Hkv=2, seed=31)
+    q, k, v, a = make_inputs(wl)
+    outs = [gpu_fwd(q, k, v, a, 100, C, 10000.0)[0].float() for C in (16, 32, 64)]
+    for x in outs[1:]:
+        assert (x - outs[0]).abs().max().item() < 1e-2
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    wl = WORKLOADS["gqa"].with_(T=384, seed=32)
+    q, k, v, a = make_inputs(wl)
+    G = wl.H // wl.Hkv
+    rep = lambda x: x.repeat_interleave(G, dim=2).contiguous()
+    o1, l1 = gpu_fwd(q, k, v, a, 128, 64, wl.rope_base)
+    o2, l2 = gpu_fwd(q, rep(k), rep(v), rep(a), 128, 64, wl.rope_base)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bitwise_deterministic():
+    wl = WORKLOADS["340m"].with_(B=2, T=512, seed=33)
+    q, k, v, a = make_inputs(wl)
+    r = [gpu_fwd(q, k, v, a, 64, 64, 10000.0) for _ in range(3)]
+    for o, l in r[1:]:
+        assert torch.equal(o, r[0][0]) and torch.equal(l, r[0][1])
