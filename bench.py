@@ -1,0 +1,271 @@
+#!/usr/bin/env python
+"""Benchmark of the NHA layer operator (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+
+A step is one pass of the whole training hot path over one batch of synthetic
+input already resident in HBM: nha_fwd (RoPE, gate prep, slot-state scan, slot
+branch, window branch) followed by nha_bwd.  K steps are timed with HIP events
+between two device synchronisations; each kernel launch is also bracketed by
+HIP events recorded by the library on the same stream (nha_fwd_timed /
+nha_bwd_timed), which gives the live per-kernel durations used for the
+roofline of the dominant kernel.  Prints ONE JSON line.
+
+Workload (default): the 1.3B-scale layer shape at 8K tokens -- B=4, H=Hkv=16,
+T=8192, d=128, m=64 slots, w=512, C=64, bf16 inputs with fp32 accumulation,
+RoPE base 10000 -- q,k,v ~ N(0,1)/sqrt(d), alpha = sigmoid(N(4,1)), dO ~ N(0,1).
+
+cpu_baseline: the fp64 oracle (test infrastructure, never tuned) timed on the
+host cores over a bounded sample of the same workload, reported as tokens/s.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import softmax_attention_nha_amd as nha  # noqa: E402
+from softmax_attention_nha_amd.inputs import WORKLOADS, make_inputs  # noqa: E402
+
+METRIC = "NHA layer fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), 1 GPU, T=2K-8K"
+PEAK_TFLOPS = {torch.bfloat16: 2500.0, torch.float32: 157.3}  # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+# ---------------------------------------------------------------- algorithmic work
+def n_win(t, w):
+    return min(w, t + 1)
+
+
+def flops_window(B, H, T, d, w):
+    """QK^T + PV over the band: 4 d flops per (query, window key) pair."""
+    if w <= 0:
+        return 0.0
+    full = max(0, T - w)
+    ramp = min(T, w)
+    pairs = ramp * (ramp + 1) / 2 + full * w
+    return 4.0 * d * B * H * pairs
+
+
+def flops_slot(B, H, T, d, m, w, C):
+    """Slot read (4 m d per query) plus the intra-chunk terms (4d + 4m per
+    (query, earlier absorbed row of the same chunk))."""
+    tot = 0.0
+    for t in range(w, T):
+        c = t - max(C * (t // C), w) + 1
+        tot += 4.0 * m * d + (4.0 * d + 4.0 * m) * c
+    return B * H * tot
+
+
+def flops_state(B, Hkv, T, d, m, w):
+    """Slot-state build: 4 m d per absorbed token (K and V)."""
+    return 4.0 * m * d * B * Hkv * max(0, T - w)
+
+
+def flops_fwd(wl, w):
+    return (flops_window(wl.B, wl.H, wl.T, wl.d, w) + flops_slot(wl.B, wl.H, wl.T, wl.d, wl.m, w, wl.C)
+            + flops_state(wl.B, wl.Hkv, wl.T, wl.d, wl.m, w))
+
+
+def bytes_fwd(wl, e):
+    """Minimum HBM traffic of the forward: read q,k,v,alpha; write o, lse."""
+    return wl.B * (wl.H * wl.T * (2 * wl.d * e + 4) + wl.Hkv * wl.T * (2 * wl.d * e + wl.m * e))
+
+
+def stage_work(stage, wl, w, e):
+    """(bound, algorithmic work per launch, unit) of a stage, for the roofline."""
+    if stage in ("win_fwd",):
+        return "mfma", flops_window(wl.B, wl.H, wl.T, wl.d, w), "flop"
+    if stage in ("win_bwd_dq",):
+        return "mfma", 1.5 * flops_window(wl.B, wl.H, wl.T, wl.d, w), "flop"
+    if stage in ("win_bwd_dkdv",):
+        return "mfma", 2.0 * flops_window(wl.B, wl.H, wl.T, wl.d, w), "flop"
+    if stage == "slot_fwd":
+        return "mfma", flops_slot(wl.B, wl.H, wl.T, wl.d, wl.m, w, wl.C), "flop"
+    if stage == "state_scan":
+        return "mfma", flops_state(wl.B, wl.Hkv, wl.T, wl.d, wl.m, w), "flop"
+    if stage == "rope_q":
+        return "hbm", 2.0 * wl.B * wl.T * wl.H * wl.d * e, "byte"
+    if stage == "rope_k":
+        return "hbm", 2.0 * wl.B * wl.T * wl.Hkv * wl.d * e, "byte"
+    return None, None, None
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, w, q, k, v, a, dO, with_bwd):
+    import oracle  # test infrastructure: only this leg of the benchmark uses it
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+    cores = min(cores, os.cpu_count() or cores)
+    Tp = int(os.environ.get("NHA_CPU_SAMPLE_T", "8192"))
+    Tp = min(Tp, wl.T)
+    units = wl.Hkv  # one batch row, every KV head
+    threads = min(cores, units)
+    f64 = lambda x: x[:1, :Tp].float().double().numpy()
+    qs, ks, vs, as_, ds = f64(q), f64(k), f64(v), f64(a), f64(dO)
+    t0 = time.perf_counter()
+    oracle.fwd(qs, ks, vs, as_, w, rope_base=wl.rope_base, threads=threads)
+    if with_bwd:
+        oracle.bwd(qs, ks, vs, as_, ds, w, rope_base=wl.rope_base, threads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(Tp / dt, 2),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "batch row 0, all %d heads, first %d of %d tokens, %s in fp64 (%.1f s)" % (
+            wl.H, Tp, wl.T, "fwd+bwd" if with_bwd else "fwd", dt),
+    }
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
+    ap.add_argument("--w", type=int, default=None, help="override the window size")
+    ap.add_argument("--T", type=int, default=None, help="override the sequence length")
+    ap.add_argument("--B", type=int, default=None, help="override the batch")
+    ap.add_argument("--fwd-only", action="store_true", help="diagnostic: time the forward alone")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this operator build has no multi-GPU path "
+              "(every (batch, KV head) unit is independent; see DESIGN.md for how it would shard). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS[args.workload]
+    if args.T:
+        wl = wl.with_(T=args.T)
+    if args.B:
+        wl = wl.with_(B=args.B)
+    w = wl.w if args.w is None else args.w
+    dev = torch.device("cuda:0")
+    e = 2 if wl.dtype == torch.bfloat16 else 4
+
+    q, k, v, a, dO = make_inputs(wl, with_grad=True)
+    qd, kd, vd, ad, dOd = (x.to(dev) for x in (q, k, v, a, dO))
+    desc = nha.make_desc(wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, w, wl.C, wl.rope_base, 0.0, wl.dtype)
+    ws = torch.empty(max(nha.workspace_size(desc), nha.workspace_size(desc, backward=True)), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd),
+             torch.empty((wl.B, wl.T, wl.Hkv, wl.m), dtype=torch.float32, device=dev))
+    fstages = nha.stage_names(desc)
+    do_bwd = not args.fwd_only
+    bstages = nha.stage_names(desc, backward=True) if do_bwd else []
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for ev in evs:
+            ev.record()  # materialise the underlying hipEvent_t
+        return evs
+
+    def step(fev=None, bev=None):
+        nha.fwd(qd, kd, vd, ad, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=o, lse_out=lse,
+                events=[x.cuda_event for x in fev] if fev else None)
+        if do_bwd:
+            nha.bwd(qd, kd, vd, ad, o, lse, dOd, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=grads,
+                    events=[x.cuda_event for x in bev] if bev else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    fevs = [new_events(len(fstages) + 1) for _ in range(K)]
+    bevs = [new_events(len(bstages) + 1) for _ in range(K)] if do_bwd else [None] * K
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        step(fevs[i], bevs[i])
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+
+    # per-kernel durations from the live events
+    per = {}
+    for evs, names in ((fevs, fstages), (bevs, bstages)):
+        if not names:
+            continue
+        for j, nm in enumerate(names):
+            per[nm] = sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
+    fwd_ms = sum(per[n] for n in fstages)
+    bwd_ms = sum(per[n] for n in bstages) if do_bwd else 0.0
+
+    F_fwd = flops_fwd(wl, w)
+    F_step = F_fwd * (3.5 if do_bwd else 1.0)  # backward counted as 2.5 x forward (FlashAttention convention)
+    tokens = wl.B * wl.T
+    value = tokens / (ms / 1e3)
+    tflops = F_step / (ms / 1e3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+
+    dom = max(per, key=per.get)
+    bound, work, unit = stage_work(dom, wl, w, e)
+    roof = None
+    if bound is not None:
+        dur = per[dom] / 1e3
+        if bound == "mfma":
+            ach = work / dur / 1e12
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": None, "avg_us": round(per[dom] * 1e3, 2)}
+        else:
+            ach = work / dur / 1e9
+            roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "avg_us": round(per[dom] * 1e3, 2)}
+
+    ok = bool(torch.isfinite(o.float()).all().item())
+    if do_bwd:
+        ok = ok and all(bool(torch.isfinite(g.float()).all().item()) for g in grads)
+
+    line = {
+        "metric": METRIC if do_bwd else METRIC + " [diagnostic: forward only]",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "NHA layer %s: B=%d H=%d Hkv=%d T=%d d=%d m=%d w=%d C=%d rope_base=%g" % (
+                "fwd+bwd" if do_bwd else "fwd", wl.B, wl.H, wl.Hkv, wl.T, wl.d, wl.m, w, wl.C, wl.rope_base),
+            "global_batch": wl.B,
+            "seq_len": wl.T,
+            "parallelism": "single GPU",
+        },
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / peak, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(F_fwd / (fwd_ms / 1e3) / 1e12, 2),
+        "fwd_mfma_peak_frac": round(F_fwd / (fwd_ms / 1e3) / 1e12 / peak, 4),
+        "fwd_hbm_GBs_min_traffic": round(bytes_fwd(wl, e) / (fwd_ms / 1e3) / 1e9, 1),
+        "kernels_us": {kname: round(x * 1e3, 2) for kname, x in per.items()},
+        "outputs_finite": ok,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, w, q, k, v, a, dO, do_bwd)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

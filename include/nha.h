@@ -144,6 +144,31 @@ nha_status nha_decode_step(const nha_desc* desc, const void* q_t,
                            const void* alpha_t, void* state, void* o_t,
                            void* stream);
 
+/* ---------------------------------------------------------------- timing
+ * Kernel launches that one nha_fwd (backward = 0) or nha_bwd (backward = 1)
+ * call enqueues for this descriptor (with_state: nha_fwd with a non-NULL
+ * state_out), in launch order.  Up to `max` static names are stored in
+ * `names` (nullable).  Returns the number of launches, or -1 for an invalid
+ * descriptor. */
+int nha_stage_names(const nha_desc* desc, int backward, int with_state,
+                    const char** names, int max);
+
+/* nha_fwd / nha_bwd that also record timing events: `events` holds n + 1
+ * hipEvent_t handles (passed as void*), n = nha_stage_names(...); events[i]
+ * is recorded on `stream` right before launch i and events[n] after the last
+ * launch, so hipEventElapsedTime(events[i], events[i+1]) is the duration of
+ * launch i.  The events are created and destroyed by the caller.  NULL events
+ * behaves exactly like the untimed call. */
+nha_status nha_fwd_timed(const nha_desc* desc, const void* q, const void* k,
+                         const void* v, const void* alpha, void* o, float* lse,
+                         void* state_out, void* ws, size_t ws_bytes,
+                         void* stream, void* const* events);
+nha_status nha_bwd_timed(const nha_desc* desc, const void* q, const void* k,
+                         const void* v, const void* alpha, const void* o,
+                         const float* lse, const void* dO, void* dq, void* dk,
+                         void* dv, float* dalpha, void* ws, size_t ws_bytes,
+                         void* stream, void* const* events);
+
 /* Static string for a status code. */
 const char* nha_status_string(nha_status s);
 

@@ -32,6 +32,9 @@ EXPORTED = (
     "nha_bwd",
     "nha_decode_step",
     "nha_status_string",
+    "nha_stage_names",
+    "nha_fwd_timed",
+    "nha_bwd_timed",
 )
 
 
@@ -87,6 +90,12 @@ def load():
     lib.nha_bwd.restype = st
     lib.nha_decode_step.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
     lib.nha_decode_step.restype = st
+    lib.nha_stage_names.argtypes = [D, st, st, ctypes.POINTER(ctypes.c_char_p), st]
+    lib.nha_stage_names.restype = st
+    lib.nha_fwd_timed.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.nha_fwd_timed.restype = st
+    lib.nha_bwd_timed.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.nha_bwd_timed.restype = st
     lib.nha_status_string.argtypes = [st]
     lib.nha_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -103,6 +112,23 @@ def _lib_status(s):
 def make_desc(B, T, H, Hkv, d, m, w, C=64, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16):
     return NhaDesc(int(B), int(T), int(H), int(Hkv), int(d), int(m), int(w), int(C), float(rope_base),
                    float(scale), _DTYPES[dtype])
+
+
+def stage_names(desc, backward=False, with_state=False):
+    """Names of the kernel launches one fwd / bwd call enqueues, in order."""
+    lib = load()
+    names = (ctypes.c_char_p * 16)()
+    n = lib.nha_stage_names(ctypes.byref(desc), int(backward), int(with_state), names, 16)
+    if n < 0:
+        raise NhaError(lib.nha_check_desc(ctypes.byref(desc)), "stage names")
+    return [names[i].decode() for i in range(n)]
+
+
+def _events_arg(events):
+    if events is None:
+        return None
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
+    return arr
 
 
 def _ptr(t):
@@ -153,7 +179,7 @@ def decode_state_size(desc):
 
 
 def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, workspace=None, out=None,
-        lse_out=None):
+        lse_out=None, events=None):
     """Chunkwise-parallel forward. Returns (o [B,T,H,d], lse [B,H,T] float32).
 
     state_out: optional uint8 decode state tensor (decode_state()) that receives
@@ -171,14 +197,16 @@ def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, w
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev) if lse_out is None else lse_out
     n = workspace_size(desc)
     ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(n, dtype=torch.uint8, device=dev)
-    rc = lib.nha_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
-                     _ptr(state_out), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    rc = lib.nha_fwd_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
+                           _ptr(state_out), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev),
+                           _events_arg(events))
     if rc != NHA_OK:
         raise NhaError(rc, "nha_fwd")
     return o, lse
 
 
-def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, workspace=None):
+def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, workspace=None, out=None,
+        events=None):
     """Gradients of fwd. Returns (dq, dk, dv, dalpha); dalpha is float32."""
     desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
     dev, dt = q.device, q.dtype
@@ -189,12 +217,16 @@ def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, works
         _check(t, nm, shp, dt, dev)
     _check(lse, "lse", (B, H, T), torch.float32, dev)
     lib = load()
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    da = torch.empty((B, T, Hkv, m), dtype=torch.float32, device=dev)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        da = torch.empty((B, T, Hkv, m), dtype=torch.float32, device=dev)
+    else:
+        dq, dk, dv, da = out
     n = workspace_size(desc, backward=True)
     ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(n, dtype=torch.uint8, device=dev)
-    rc = lib.nha_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO),
-                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    rc = lib.nha_bwd_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
+                           _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                           _stream(dev), _events_arg(events))
     if rc != NHA_OK:
         raise NhaError(rc, "nha_bwd")
     return dq, dk, dv, da

@@ -100,6 +100,12 @@ size_t nha_decode_state_size(const nha_desc* desc) {
 
 nha_status nha_fwd(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
                    void* o, float* lse, void* state_out, void* ws, size_t ws_bytes, void* stream) {
+  return nha_fwd_timed(desc, q, k, v, alpha, o, lse, state_out, ws, ws_bytes, stream, nullptr);
+}
+
+nha_status nha_fwd_timed(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                         void* o, float* lse, void* state_out, void* ws, size_t ws_bytes, void* stream,
+                         void* const* events) {
   Shape s;
   nha_status rc = make_shape(desc, true, &s);
   if (rc != NHA_OK) return rc;
@@ -108,7 +114,7 @@ nha_status nha_fwd(const nha_desc* desc, const void* q, const void* k, const voi
       (lse && !aligned16(lse)) || (state_out && !aligned16(state_out)))
     return NHA_ERR_INVALID_ARG;
   if (ws_bytes < fwd_ws_layout(s).total) return NHA_ERR_WORKSPACE;
-  FwdPtrs p{q, k, v, alpha, o, lse, state_out, (char*)ws};
+  FwdPtrs p{q, k, v, alpha, o, lse, state_out, (char*)ws, events};
   hipError_t e = launch_fwd(s, make_theta(desc), p, (hipStream_t)stream);
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
 }
@@ -116,6 +122,12 @@ nha_status nha_fwd(const nha_desc* desc, const void* q, const void* k, const voi
 nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
                    const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* dalpha,
                    void* ws, size_t ws_bytes, void* stream) {
+  return nha_bwd_timed(desc, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws, ws_bytes, stream, nullptr);
+}
+
+nha_status nha_bwd_timed(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                         const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                         float* dalpha, void* ws, size_t ws_bytes, void* stream, void* const* events) {
   Shape s;
   nha_status rc = make_shape(desc, true, &s);
   if (rc != NHA_OK) return rc;
@@ -125,9 +137,15 @@ nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k, const voi
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
   if (ws_bytes < bwd_ws_bytes(s)) return NHA_ERR_WORKSPACE;
-  BwdPtrs p{q, k, v, alpha, o, dO, lse, dq, dk, dv, dalpha, (char*)ws};
+  BwdPtrs p{q, k, v, alpha, o, dO, lse, dq, dk, dv, dalpha, (char*)ws, events};
   hipError_t e = launch_bwd(s, make_theta(desc), p, (hipStream_t)stream);
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+int nha_stage_names(const nha_desc* desc, int backward, int with_state, const char** names, int max) {
+  Shape s;
+  if (make_shape(desc, true, &s) != NHA_OK) return -1;
+  return backward ? bwd_stages(s, names, max) : fwd_stages(s, with_state != 0, names, max);
 }
 
 nha_status nha_decode_step(const nha_desc* desc, const void* q_t, const void* k_t, const void* v_t,

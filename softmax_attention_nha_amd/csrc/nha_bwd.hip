@@ -6,6 +6,8 @@ namespace nha {
 
 size_t bwd_ws_bytes(const Shape& s) { return fwd_ws_layout(s).total; }
 
+int bwd_stages(const Shape&, const char**, int) { return 0; }
+
 hipError_t launch_bwd(const Shape&, const RopeTheta&, const BwdPtrs&, hipStream_t) {
   return hipErrorNotSupported;
 }

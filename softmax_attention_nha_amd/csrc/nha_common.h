@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef __bf16 bf16;
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
@@ -152,6 +154,88 @@ __device__ __forceinline__ float sum_over_g(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X (linear
+// id n goes to XCD n % 8), and each XCD has its own L2.  xcd_remap turns the
+// linear id into a logical index such that every XCD receives one contiguous
+// range of logical indices: neighbouring tiles (which share K/V rows) then run
+// on the same XCD and hit its L2.  Bijective on [0, N).
+__device__ __forceinline__ int xcd_remap(int lin, int N) {
+  int q = N >> 3, r = N & 7, x = lin & 7, k = lin >> 3;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // Padded row pitch (elements) for LDS tiles of T with `cols` columns: keeps
 // 16-byte alignment and shifts consecutive rows across banks.
 __host__ __device__ constexpr int pitch_of(int cols) { return cols + 8; }
+
+// ---------------------------------------------------------------- tile staging
+// A ROWS-row tile of a row-major [rows][D] operand (row stride `ld` elements);
+// rows outside [lo, hi) read as zero.  NT threads; each thread owns 8-element
+// chunks.  load() issues the global loads into registers (so they can overlap
+// other work), store() writes them to LDS.
+template <typename T, int D, int NT, int ROWS = 64>
+struct RowTile {
+  static constexpr int CH = ROWS * D / 8;         // 8-element chunks per tile
+  static constexpr int PER = (CH + NT - 1) / NT;  // chunks per thread
+  typename Vec<T>::v8 r[PER];
+  __device__ __forceinline__ void load(const T* __restrict__ base, size_t ld, int lo, int hi, int tid) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int e = (tid + k * NT) * 8;
+      int rr = e / D, j = e % D;
+      r[k] = (e < ROWS * D && rr >= lo && rr < hi) ? ld8<T>(base + (size_t)rr * ld + j) : zero8<T>();
+    }
+  }
+  // LDS layout [ROWS][P] (P = row pitch in elements)
+  template <int P>
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int e = (tid + k * NT) * 8;
+      if (e < ROWS * D) st8<T>(lds + (e / D) * P + (e % D), r[k]);
+    }
+  }
+};
+
+// The same tile stored transposed ([D][P], row index contiguous), for operands
+// whose K dimension is the tile's row index.  Thread = (row pair p, column-chunk
+// group): it loads rows 2p and 2p+1 of one 8-column chunk and writes 8 packed
+// pairs, so a wavefront writes consecutive pairs of one LDS row per store
+// (conflict-free) instead of scattering 2-byte values.
+template <typename T, int D, int NT, int ROWS = 64>
+struct PairTileT {
+  static constexpr int NP = ROWS / 2;                // row pairs
+  static constexpr int NG = NT / NP;                 // chunk groups
+  static constexpr int NCH = D / 8;                  // 8-column chunks
+  static constexpr int PER = (NCH + NG - 1) / NG;    // chunks per thread
+  typename Vec<T>::v8 a[PER], b[PER];
+  __device__ __forceinline__ void load(const T* __restrict__ base, size_t ld, int lo, int hi, int tid) {
+    int p = tid % NP, cg = tid / NP;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int c = cg + k * NG;
+      bool ok = c < NCH && cg < NG;
+      int r0 = 2 * p, r1 = 2 * p + 1;
+      a[k] = (ok && r0 >= lo && r0 < hi) ? ld8<T>(base + (size_t)r0 * ld + 8 * c) : zero8<T>();
+      b[k] = (ok && r1 >= lo && r1 < hi) ? ld8<T>(base + (size_t)r1 * ld + 8 * c) : zero8<T>();
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+    int p = tid % NP, cg = tid / NP;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int c = cg + k * NG;
+      if (c < NCH && cg < NG) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          typedef T pair_t __attribute__((ext_vector_type(2)));
+          pair_t v;
+          v[0] = a[k][x];
+          v[1] = b[k][x];
+          *reinterpret_cast<pair_t*>(lds + (8 * c + x) * P + 2 * p) = v;
+        }
+      }
+    }
+  }
+};

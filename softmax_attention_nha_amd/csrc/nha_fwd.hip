@@ -66,53 +66,132 @@ __global__ __launch_bounds__(256) void k_rope(const T* __restrict__ x, T* __rest
 }
 
 // ---------------------------------------------------------------- gate prep
-// grid (NC, B*Hkv), block MP threads (thread = slot i).
+// In-place inclusive cumsum over the C rows of an LDS tile g[u * P + i] (fp32)
+// for columns i < MP, by NT threads: each thread scans a run of rows of one
+// column, then adds the totals of the runs before it.
+template <int C, int MP, int P, int NT>
+__device__ __forceinline__ void lds_col_cumsum(float* g, int tid) {
+  constexpr int PARTS = (NT / MP) < C ? (NT / MP) : C;
+  constexpr int RP = C / PARTS;
+  const int i = tid % MP, part = tid / MP;
+  const bool act = part < PARTS;
+  if (act) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = part * RP; u < (part + 1) * RP; ++u) {
+      acc += g[u * P + i];
+      g[u * P + i] = acc;
+    }
+  }
+  __syncthreads();
+  float off = 0.f;
+  if (act)
+    for (int pp = 0; pp < part; ++pp) off += g[((pp + 1) * RP - 1) * P + i];
+  __syncthreads();
+  if (act && part > 0) {
+#pragma unroll
+    for (int u = part * RP; u < (part + 1) * RP; ++u) g[u * P + i] += off;
+  }
+  __syncthreads();
+}
+
+// Stage a chunk's gates into LDS: la[u][i] = log2 a_u (0 where nothing is
+// absorbed: t < w, t >= T or padded slot), al[u][i] = raw alpha (1 outside).
+template <typename T, int C, int MP, int PG, int PA, int NT>
+__device__ __forceinline__ void stage_gates(const T* __restrict__ alpha, float* la, T* al, int b, int hg, int t0,
+                                            int Tn, int Hkv, int m, int w, int tid) {
+  for (int e = tid; e < C * MP; e += NT) {
+    int u = e / MP, i = e % MP, t = t0 + u;
+    T av = to_t<T>(1.f);
+    if (i < m && t < Tn) av = alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i];
+    float l2 = 0.f;
+    if (i < m && t < Tn && t >= w) l2 = fmaxf(__log2f(to_f<T>(av)), NHA_LOG2A_MIN);
+    la[u * PG + i] = l2;
+    al[u * PA + i] = av;
+  }
+}
+
+// grid (NC, B*Hkv), 256 threads.
 // Wt[unit][c][i][u] = 2^{G_end,i - G_u,i} b_u,i   (0 for padded slots / rows)
 // aend[unit][c][i]  = 2^{G_end,i}
-template <typename T, int C>
-__global__ void k_chunk_gates(const T* __restrict__ alpha, T* __restrict__ Wt, float* __restrict__ aend,
-                              int Tn, int Hkv, int m, int mp, int w, int NC) {
-  int c = blockIdx.x, unit = blockIdx.y, i = threadIdx.x;
-  int b = unit / Hkv, g = unit % Hkv;
-  float G[C], bb[C];
-  float acc = 0.f;
-#pragma unroll
-  for (int u = 0; u < C; ++u) {
-    int t = c * C + u;
-    float la = 0.f, be = 0.f;
-    if (i < m && t < Tn && t >= w) {
-      float al = to_f<T>(alpha[(((size_t)b * Tn + t) * Hkv + g) * m + i]);
-      la = fmaxf(__log2f(al), NHA_LOG2A_MIN);
-      be = 1.f - al;
-    }
-    acc += la;
-    G[u] = acc;
-    bb[u] = be;
+template <typename T, int C, int MP>
+__global__ __launch_bounds__(256) void k_chunk_gates(const T* __restrict__ alpha, T* __restrict__ Wt,
+                                                     float* __restrict__ aend, int Tn, int Hkv, int m, int w,
+                                                     int NC) {
+  constexpr int PG = MP + 1, PA = MP + 2, PW = C + 8;
+  __shared__ float sG[C * PG];
+  __shared__ T sA[C * PA];
+  __shared__ T sW[MP * PW];
+  const int tid = threadIdx.x, c = blockIdx.x, unit = blockIdx.y;
+  const int b = unit / Hkv, hg = unit % Hkv, t0 = c * C;
+  stage_gates<T, C, MP, PG, PA, 256>(alpha, sG, sA, b, hg, t0, Tn, Hkv, m, w, tid);
+  __syncthreads();
+  lds_col_cumsum<C, MP, PG, 256>(sG, tid);
+  for (int e = tid; e < MP * C; e += 256) {
+    int i = e / C, u = e % C, t = t0 + u;
+    float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sA[u * PA + i]) : 0.f;
+    sW[i * PW + u] = to_t<T>(fast_exp2(sG[(C - 1) * PG + i] - sG[u * PG + i]) * be);
   }
-  T* dst = Wt + (((size_t)unit * NC + c) * mp + i) * C;
-#pragma unroll
-  for (int u0 = 0; u0 < C; u0 += 8) {
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = fast_exp2(acc - G[u0 + e]) * bb[u0 + e];
-    st8<T>(dst + u0, pack8<T>(f));
-  }
-  aend[((size_t)unit * NC + c) * mp + i] = fast_exp2(acc);
+  __syncthreads();
+  T* dst = Wt + ((size_t)unit * NC + c) * MP * C;
+  for (int e = tid * 8; e < MP * C; e += 256 * 8) st8<T>(dst + e, ld8<T>(&sW[(e / C) * PW + (e % C)]));
+  if (tid < MP) aend[((size_t)unit * NC + c) * MP + tid] = fast_exp2(sG[(C - 1) * PG + tid]);
 }
 
 // ---------------------------------------------------------------- state scan
 // grid (d/16, B*Hkv), one wave.  Lane (g, c) keeps S^T[j0 + 4g + r][16 nb + c]
-// for K and V.  For every chunk: store S (state before the chunk), then
-// S <- aend (.) S + W^T . kappa  (transposed: dS^T = kappa^T W).
+// for K and V.  For every chunk: store S (the state before the chunk; both
+// halves in [i][d] layout), then S <- aend (.) S + W^T . kappa  (transposed:
+// dS^T = kappa^T W).  The next chunk's rows, weights and decays are loaded
+// while the current chunk's products run.
+template <typename T, int C, int MP>
+struct ScanRegs {
+  static constexpr int NB = MP / 16;
+  static constexpr bool K16 = (C % 32) != 0;
+  static constexpr int KS = K16 ? C / 16 : C / 32;
+  typename Vec<T>::v8 k0, k1, v0, v1;                                // kappa / nu row l, cols j0..j0+15
+  typename std::conditional<K16, typename Vec<T>::v4, typename Vec<T>::v8>::type wf[NB][KS];
+  float ae[NB];
+};
+
+template <typename T, int C, int MP>
+__device__ __forceinline__ void scan_load(ScanRegs<T, C, MP>& R, const T* __restrict__ kk, const T* __restrict__ vv,
+                                          const T* __restrict__ Wt, const float* __restrict__ aend, int c, int unit,
+                                          int b, int hg, int j0, int Tn, int Hkv, int d, int w, int NC, int l) {
+  constexpr int NB = ScanRegs<T, C, MP>::NB, KS = ScanRegs<T, C, MP>::KS;
+  const int g = l >> 4, cc = l & 15;
+  R.k0 = R.k1 = R.v0 = R.v1 = zero8<T>();
+  int t = c * C + l;
+  if (l < C && t >= w && t < Tn) {
+    size_t row = (((size_t)b * Tn + (t - w)) * Hkv + hg) * d + j0;
+    R.k0 = ld8<T>(kk + row);
+    R.k1 = ld8<T>(kk + row + 8);
+    R.v0 = ld8<T>(vv + row);
+    R.v1 = ld8<T>(vv + row + 8);
+  }
+  const T* wsrc = Wt + ((size_t)unit * NC + c) * MP * C;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    R.ae[nb] = aend[((size_t)unit * NC + c) * MP + 16 * nb + cc];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (ScanRegs<T, C, MP>::K16)
+        R.wf[nb][s] = ld4<T>(wsrc + (size_t)(16 * nb + cc) * C + 16 * s + 4 * g);
+      else
+        R.wf[nb][s] = ld8<T>(wsrc + (size_t)(16 * nb + cc) * C + 32 * s + 8 * g);
+    }
+  }
+}
+
 template <typename T, int C, int MP>
 __global__ __launch_bounds__(64) void k_state_scan(const T* __restrict__ kk, const T* __restrict__ vv,
                                                    const T* __restrict__ Wt, const float* __restrict__ aend,
                                                    T* __restrict__ sst, float* __restrict__ skout,
                                                    float* __restrict__ svout, int Tn, int Hkv, int d, int m,
                                                    int w, int NC) {
-  constexpr int NB = MP / 16;
+  using R_t = ScanRegs<T, C, MP>;
+  constexpr int NB = R_t::NB, KS = R_t::KS;
   constexpr int PC = pitch_of(C);
-  constexpr bool K16 = (C % 32) != 0;
   __shared__ T sKt[16 * PC];
   __shared__ T sVt[16 * PC];
   const int l = threadIdx.x, g = l >> 4, cc = l & 15;
@@ -122,70 +201,55 @@ __global__ __launch_bounds__(64) void k_state_scan(const T* __restrict__ kk, con
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) SK[nb] = SV[nb] = zero4();
   const size_t chunk_elems = 2 * (size_t)MP * d;
+  R_t cur, nxt;
+  scan_load<T, C, MP>(cur, kk, vv, Wt, aend, 0, unit, b, hg, j0, Tn, Hkv, d, w, NC, l);
   for (int c = 0; c < NC; ++c) {
-    // state at the chunk start
+    // state at the chunk start, [i][d] layout for both halves
     T* dst = sst + ((size_t)unit * NC + c) * chunk_elems;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       int i = 16 * nb + cc;
       st4<T>(dst + (size_t)i * d + j0 + 4 * g, pack4<T>(SK[nb]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(size_t)MP * d + (size_t)(j0 + 4 * g + r) * MP + i] = to_t<T>(SV[nb][r]);
+      st4<T>(dst + (size_t)MP * d + (size_t)i * d + j0 + 4 * g, pack4<T>(SV[nb]));
     }
-    // kappa / nu columns j0..j0+15 of the chunk rows, transposed into LDS
     if (l < C) {
-      int t = c * C + l;
-      typename Vec<T>::v8 k0 = zero8<T>(), k1 = zero8<T>(), v0 = zero8<T>(), v1 = zero8<T>();
-      if (t >= w && t < Tn) {
-        size_t row = (((size_t)b * Tn + (t - w)) * Hkv + hg) * d + j0;
-        k0 = ld8<T>(kk + row);
-        k1 = ld8<T>(kk + row + 8);
-        v0 = ld8<T>(vv + row);
-        v1 = ld8<T>(vv + row + 8);
-      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        sKt[e * PC + l] = k0[e];
-        sKt[(8 + e) * PC + l] = k1[e];
-        sVt[e * PC + l] = v0[e];
-        sVt[(8 + e) * PC + l] = v1[e];
+        sKt[e * PC + l] = cur.k0[e];
+        sKt[(8 + e) * PC + l] = cur.k1[e];
+        sVt[e * PC + l] = cur.v0[e];
+        sVt[(8 + e) * PC + l] = cur.v1[e];
       }
     }
     __syncthreads();
-    const float* ae = aend + ((size_t)unit * NC + c) * MP;
+    if (c + 1 < NC) scan_load<T, C, MP>(nxt, kk, vv, Wt, aend, c + 1, unit, b, hg, j0, Tn, Hkv, d, w, NC, l);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float a = ae[16 * nb + cc];
-      SK[nb] *= a;
-      SV[nb] *= a;
+      SK[nb] *= cur.ae[nb];
+      SV[nb] *= cur.ae[nb];
     }
-    const T* wsrc = Wt + ((size_t)unit * NC + c) * MP * C;
-    if constexpr (K16) {
 #pragma unroll
-      for (int s = 0; s < C / 16; ++s) {
+    for (int s = 0; s < KS; ++s) {
+      if constexpr (R_t::K16) {
         typename Vec<T>::v4 ak = ld4<T>(&sKt[cc * PC + 16 * s + 4 * g]);
         typename Vec<T>::v4 av = ld4<T>(&sVt[cc * PC + 16 * s + 4 * g]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          typename Vec<T>::v4 bw = ld4<T>(wsrc + (size_t)(16 * nb + cc) * C + 16 * s + 4 * g);
-          SK[nb] = mma16(SK[nb], ak, bw);
-          SV[nb] = mma16(SV[nb], av, bw);
+          SK[nb] = mma16(SK[nb], ak, cur.wf[nb][s]);
+          SV[nb] = mma16(SV[nb], av, cur.wf[nb][s]);
         }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < C / 32; ++s) {
+      } else {
         typename Vec<T>::v8 ak = ld8<T>(&sKt[cc * PC + 32 * s + 8 * g]);
         typename Vec<T>::v8 av = ld8<T>(&sVt[cc * PC + 32 * s + 8 * g]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          typename Vec<T>::v8 bw = ld8<T>(wsrc + (size_t)(16 * nb + cc) * C + 32 * s + 8 * g);
-          SK[nb] = mma32(SK[nb], ak, bw);
-          SV[nb] = mma32(SV[nb], av, bw);
+          SK[nb] = mma32(SK[nb], ak, cur.wf[nb][s]);
+          SV[nb] = mma32(SV[nb], av, cur.wf[nb][s]);
         }
       }
     }
     __syncthreads();
+    cur = nxt;
   }
   if (skout) {
 #pragma unroll
@@ -234,47 +298,26 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
   // ---- cooperative loads
   {
     const T* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
-    for (int e = tid * 8; e < MP * D; e += NT * 8) {
-      int i = e / D, j = e % D;
-      st8<T>(&sm.sSK[i * PD + j], ld8<T>(src + e));
-    }
-    for (int e = tid * 8; e < MP * D; e += NT * 8) {
-      int j = e / MP, i = e % MP;
-      st8<T>(&sm.sSVt[j * PM + i], ld8<T>(src + (size_t)MP * D + e));
-    }
-    for (int e = tid * 8; e < C * D; e += NT * 8) {
-      int u = e / D, j = e % D, t = t0 + u;
-      typename Vec<T>::v8 kv = zero8<T>(), vvv = zero8<T>();
-      if (t >= w && t < Tn) {
-        size_t row = (((size_t)b * Tn + (t - w)) * Hkv + hg) * D + j;
-        kv = ld8<T>(kk + row);
-        vvv = ld8<T>(vv + row);
-      }
-      st8<T>(&sm.sK[u * PD + j], kv);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) sm.sVt[(j + x) * PC + u] = vvv[x];
-    }
-    for (int e = tid; e < C * MP; e += NT) {
-      int u = e / MP, i = e % MP, t = t0 + u;
-      T a = to_t<T>(1.f);
-      if (i < m && t < Tn) a = alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i];
-      sm.sA[u * PM + i] = a;
-    }
+    RowTile<T, D, NT, MP> tsk;
+    PairTileT<T, D, NT, MP> tsv;
+    tsk.load(src, D, 0, MP, tid);
+    tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
+    // chunk row u <-> token t0 + u, absorbing key row t0 + u - w when t0 + u >= w
+    const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+    const T* kb = kk + rbase * D;
+    const T* vb = vv + rbase * D;
+    RowTile<T, D, NT, C> tkap;
+    PairTileT<T, D, NT, C> tnu;
+    tkap.load(kb, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    tnu.load(vb, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    stage_gates<T, C, MP, MP, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    tsk.template store<PD>(sm.sSK, tid);
+    tsv.template store<PM>(sm.sSVt, tid);
+    tkap.template store<PD>(sm.sK, tid);
+    tnu.template store<PC>(sm.sVt, tid);
   }
   __syncthreads();
-  // log2 cumsum of the effective decay (slot per thread)
-  if (tid < MP) {
-    int i = tid;
-    float acc = 0.f;
-    for (int u = 0; u < C; ++u) {
-      int t = t0 + u;
-      float la = 0.f;
-      if (i < m && t < Tn && t >= w) la = fmaxf(__log2f(to_f<T>(sm.sA[u * PM + i])), NHA_LOG2A_MIN);
-      acc += la;
-      sm.sG[u * MP + i] = acc;
-    }
-  }
-  __syncthreads();
+  lds_col_cumsum<C, MP, MP, NT>(sm.sG, tid);
   // B^(J)[u][i] = 2^{E_J - G_u} b_u, E_J = G at the last row of u's block
   for (int e = tid; e < C * MP; e += NT) {
     int u = e / MP, i = e % MP, t = t0 + u;
@@ -505,18 +548,29 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
 // ---------------------------------------------------------------- window branch
 // grid (ceil(T/64), B*H), 4 waves; wave W owns queries q0 + 16W .. +15.
 // Online softmax in log2 units, seeded with the slot partial as one key of
-// logit lse_L and value o_L / Z_L.  Writes o and lse.
+// logit lse_L and value o_L / Z_L.  Key/value tiles of 64 rows are double
+// buffered in LDS; the global loads of tile i+2 are in flight while tile i is
+// computed.  Writes o and lse.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_win_fwd(const T* __restrict__ qr, const T* __restrict__ kr,
-                                                 const T* __restrict__ vv, const T* __restrict__ oL,
-                                                 const float* __restrict__ lseL, T* __restrict__ o,
-                                                 float* __restrict__ lse, int Tn, int H, int Hkv, int w,
-                                                 float scale) {
-  constexpr int PD = pitch_of(D), PK = pitch_of(64);
-  __shared__ T sK[64 * PD];
-  __shared__ T sVt[D * PK];
+struct WinFwdSmem {
+  static constexpr int PD = pitch_of(D), PK = 64 + 4;
+  T k[2][64 * PD];  // RoPE'd keys [key][d]
+  T vt[2][D * PK];  // values, transposed [d][key]
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_win_fwd(const T* __restrict__ qr, const T* __restrict__ kr,
+                                                    const T* __restrict__ vv, const T* __restrict__ oL,
+                                                    const float* __restrict__ lseL, T* __restrict__ o,
+                                                    float* __restrict__ lse, int Tn, int H, int Hkv, int w,
+                                                    float scale) {
+  using S = WinFwdSmem<T, D>;
+  constexpr int PD = S::PD, PK = S::PK;
+  __shared__ S sm;
   const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
-  const int q0 = blockIdx.x * 64, bh = blockIdx.y, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  // logical tile = (query tile, b*H + h), XCD-contiguous
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int q0 = (L % gridDim.x) * 64, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
   const int tq = q0 + 16 * W + cc;
   const bool qvalid = tq < Tn;
   typename Vec<T>::v8 qf[D / 32];
@@ -542,21 +596,26 @@ __global__ __launch_bounds__(256) void k_win_fwd(const T* __restrict__ qr, const
     if (kmin < 0) kmin = 0;
     int kmax = q0 + 63;
     if (kmax > Tn - 1) kmax = Tn - 1;
-    for (int j0 = (kmin / 64) * 64; j0 <= kmax; j0 += 64) {
-      __syncthreads();
-      for (int e = tid * 8; e < 64 * D; e += 256 * 8) {
-        int rr = e / D, j = e % D, key = j0 + rr;
-        typename Vec<T>::v8 kx = zero8<T>(), vx = zero8<T>();
-        if (key < Tn) {
-          size_t row = (((size_t)b * Tn + key) * Hkv + hg) * D + j;
-          kx = ld8<T>(kr + row);
-          vx = ld8<T>(vv + row);
-        }
-        st8<T>(&sK[rr * PD + j], kx);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) sVt[(j + x) * PK + rr] = vx[x];
-      }
-      __syncthreads();
+    const int jfirst = (kmin / 64) * 64;
+    const int ntiles = (kmax - jfirst) / 64 + 1;
+    const size_t ld = (size_t)Hkv * D;
+    const T* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
+    const T* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
+    RowTile<T, D, 256> tk;
+    PairTileT<T, D, 256> tv;
+    tk.load(kbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
+    tv.load(vbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
+    tk.template store<PD>(sm.k[0], tid);
+    tv.template store<PK>(sm.vt[0], tid);
+    __syncthreads();
+    if (ntiles > 1) {
+      tk.load(kbase + (size_t)(jfirst + 64) * ld, ld, 0, Tn - jfirst - 64, tid);
+      tv.load(vbase + (size_t)(jfirst + 64) * ld, ld, 0, Tn - jfirst - 64, tid);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      const int cur = it & 1, j0 = jfirst + 64 * it;
+      const T* sK = sm.k[cur];
+      const T* sVt = sm.vt[cur];
       const bool full = (j0 + 63 <= q0) && (j0 > q0 + 63 - w) && (j0 + 63 < Tn);
       float s[4][4];
       float mx = -INFINITY;
@@ -594,16 +653,25 @@ __global__ __launch_bounds__(256) void k_win_fwd(const T* __restrict__ qr, const
         }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        float f[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) f[r] = s[2 * st][r], f[4 + r] = s[2 * st + 1][r];
-        typename Vec<T>::v8 bfr = pack8<T>(f);
+        typename Vec<T>::v8 bfr = pack8<T>(floatx4{s[2 * st][0], s[2 * st][1], s[2 * st][2], s[2 * st][3]},
+                                           floatx4{s[2 * st + 1][0], s[2 * st + 1][1], s[2 * st + 1][2],
+                                                   s[2 * st + 1][3]});
 #pragma unroll
         for (int db = 0; db < D / 16; ++db)
           accO[db] = mma32(accO[db],
                            ld4x2<T>(&sVt[(16 * db + cc) * PK + 32 * st + 4 * g],
                                     &sVt[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
                            bfr);
+      }
+      if (it + 1 < ntiles) {
+        tk.template store<PD>(sm.k[cur ^ 1], tid);
+        tv.template store<PK>(sm.vt[cur ^ 1], tid);
+      }
+      __syncthreads();
+      if (it + 2 < ntiles) {
+        int jn = j0 + 128;
+        tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+        tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
       }
     }
   }
@@ -653,6 +721,8 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
   T* ol = (T*)(p.ws + L.ol);
   float* lsel = (float*)(p.ws + L.lsel);
   const int units = s.B * s.Hkv;
+  Marks mk;
+  mk.ev = p.events;
   const T* qr = q;
   const T* kr = k;
   if (s.rope && s.win) {
@@ -660,13 +730,16 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     T* krw = (T*)(p.ws + L.krot);
     long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
     long thq = nq * (s.d / 16), thk = nk * (s.d / 16);
+    mk.mark(st);
     hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thq + 255) / 256)), dim3(256), 0, st, q, qrw, nq, s.H, s.T, s.d, th);
+    mk.mark(st);
     hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thk + 255) / 256)), dim3(256), 0, st, k, krw, nk, s.Hkv, s.T, s.d, th);
     qr = qrw;
     kr = krw;
   }
-  hipLaunchKernelGGL((k_chunk_gates<T, C>), dim3(s.NC, units), dim3(MP), 0, st, alpha, wt, aend, s.T, s.Hkv, s.m,
-                     MP, s.w, s.NC);
+  mk.mark(st);
+  hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, wt, aend, s.T, s.Hkv,
+                     s.m, s.w, s.NC);
   float* skout = nullptr;
   float* svout = nullptr;
   StateLayout SL{};
@@ -675,21 +748,27 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     skout = (float*)((char*)p.state_out + SL.sk);
     svout = (float*)((char*)p.state_out + SL.sv);
   }
+  mk.mark(st);
   hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, wt, aend, sst, skout,
                      svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
+  mk.mark(st);
   hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
                      sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
+  mk.mark(st);
   hipLaunchKernelGGL((k_win_fwd<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, ol, lsel, (T*)p.o,
                      p.lse, s.T, s.H, s.Hkv, s.w, s.scale);
   if (p.state_out && s.w > 0) {
     char* base = (char*)p.state_out;
+    mk.mark(st);
     hipLaunchKernelGGL(k_export_state<T>, dim3(32, units), dim3(256), 0, st, k, v, (T*)(base + SL.rk),
                        (T*)(base + SL.rv), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w);
   } else if (p.state_out) {
     char* base = (char*)p.state_out;
+    mk.mark(st);
     hipLaunchKernelGGL(k_export_state<T>, dim3(1, units), dim3(64), 0, st, k, v, (T*)nullptr, (T*)nullptr,
                        (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0);
   }
+  mk.mark(st);
   return hipGetLastError();
   }
 }
@@ -721,6 +800,22 @@ static hipError_t fwd_m(const Shape& s, const RopeTheta& th, const FwdPtrs& p, h
 hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st) {
   if (s.dtype == NHA_DTYPE_BF16) return fwd_m<bf16>(s, th, p, st);
   return fwd_m<float>(s, th, p, st);
+}
+
+int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
+  const char* all[8];
+  int n = 0;
+  if (s.rope && s.win) {
+    all[n++] = "rope_q";
+    all[n++] = "rope_k";
+  }
+  all[n++] = "chunk_gates";
+  all[n++] = "state_scan";
+  all[n++] = "slot_fwd";
+  all[n++] = "win_fwd";
+  if (with_state) all[n++] = "export_state";
+  for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];
+  return n;
 }
 
 size_t slot_fwd_lds_bytes(const Shape& s) {

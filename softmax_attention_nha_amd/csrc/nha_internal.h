@@ -86,6 +86,20 @@ inline StateLayout state_layout(const Shape& s) {
   return L;
 }
 
+// Records caller-provided timing events around consecutive launches.
+struct Marks {
+  void* const* ev = nullptr;
+  int i = 0;
+  void mark(hipStream_t st) {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], st);
+    ++i;
+  }
+};
+
+// Launch sequence of one forward / backward call (names are static strings).
+int fwd_stages(const Shape& s, bool with_state, const char** names, int max);
+int bwd_stages(const Shape& s, const char** names, int max);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All launches go on `st`.
 struct FwdPtrs {
@@ -94,6 +108,7 @@ struct FwdPtrs {
   float* lse;
   void* state_out;  // nullable
   char* ws;
+  void* const* events;  // nullable timing events
 };
 hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st);
 
@@ -111,6 +126,7 @@ struct BwdPtrs {
   void *dq, *dk, *dv;
   float* dalpha;
   char* ws;
+  void* const* events;  // nullable timing events
 };
 hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st);
 
