@@ -89,6 +89,7 @@ size_t nha_fwd_workspace_size(const nha_desc* desc) {
 size_t nha_bwd_workspace_size(const nha_desc* desc) {
   Shape s;
   if (make_shape(desc, true, &s) != NHA_OK) return 0;
+  if (slot_bwd_lds_bytes(s) > kMaxLds) return 0;
   return bwd_ws_bytes(s);
 }
 
@@ -131,6 +132,7 @@ nha_status nha_bwd_timed(const nha_desc* desc, const void* q, const void* k, con
   Shape s;
   nha_status rc = make_shape(desc, true, &s);
   if (rc != NHA_OK) return rc;
+  if (slot_bwd_lds_bytes(s) > kMaxLds) return NHA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !alpha || !o || !lse || !dO || !dq || !dk || !dv || !dalpha || !ws)
     return NHA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws};

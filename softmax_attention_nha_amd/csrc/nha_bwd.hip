@@ -1,15 +1,1047 @@
 // nha_bwd.hip -- backward kernels of the NHA layer operator (gfx950).
+//
+// Gradients of the forward in nha_fwd.hip: one softmax over the m slot logits
+// and the window logits (Paper-Notes page "Native Hybrid Attention for
+// Efficient Sequence Modeling", section 关键设计 > 层内混合: the unified softmax
+// couples the gradients of the long- and short-term memories).  With p the
+// joint probabilities (recomputed from the forward's lse) and D_t = <dO_t, o_t>:
+//     dl = p (dp - D_t)
+// Window branch (band attention with RoPE):
+//     dq_t += R_t^T s sum_j dl_tj R_j k_j,  dk_j += R_j^T s sum_t dl_tj R_t q_t,
+//     dv_j += sum_t p_tj dO_t.
+// Slot branch, per (batch, KV head): the slot states receive the direct
+// sources dSK_t[i] = s dl_ti q_t, dSV_t[i] = p_ti dO_t (summed over the query
+// heads of the group), and their adjoint runs backwards in time,
+//     Lam_t = dS_t + a_{t+1} Lam_{t+1},
+// which is a slot state in reversed time.  Then, for t >= w,
+//     dk_{t-w} += sum_i b_t[i] LamK_t[i]        (dv likewise)
+//     F_t[i]   = <LamK_t[i], k_{t-w}> + <LamV_t[i], v_{t-w}>
+//     A_t[i]   = sum_h dl_ti l_ti + p_ti dp_ti     (l: scaled slot logit)
+//     dalpha_t = (sum_{u>=t} (A_u - b_u F_u)) / alpha_t - F_t
+// (from <Lam_t, S_t> = A_t + <Lam_{t+1}, S_{t+1}> - b_{t+1} F_{t+1}), and
+// dalpha_t = 0 for t < w.  Chunkwise: the adjoint entering chunk c from the
+// right obeys Lin_{c-1} = 2^{G_end} Lin_c + sum_{u in c} 2^{G_u} dS_u.
+//
+// Kernels, in launch order (after the shared prologue: RoPE, gates, state scan):
+//   k_bwd_prep      D_t = <dO_t, o_t>
+//   k_bwd_slot_a    per (b, h, chunk): slot p, dp, dl; dq's slot part;
+//                   adjoint weights 2^{G_u} s dl_u, 2^{G_u} p_u; A_t parts
+//   k_adj_scan      reverse over chunks: Lin_c for every chunk (MFMA)
+//   k_bwd_slot_b    per (b, g, chunk): dk/dv slot parts, F, local dalpha
+//   k_dalpha_carry  sum of the later chunks' (A - b F) per slot
+//   k_dalpha_fix    dalpha += carry / alpha
+//   k_win_bwd_dq    window dq (+ slot part) -> dq
+//   k_win_bwd_dkdv  window dk, dv (+ slot parts at the shifted rows) -> dk, dv
 #include "nha_common.h"
 #include "nha_internal.h"
+#include "nha_slot.h"
 
 namespace nha {
 
-size_t bwd_ws_bytes(const Shape& s) { return fwd_ws_layout(s).total; }
+// ---------------------------------------------------------------- workspace
+struct BwdWs {
+  size_t sst, wt, aend, qrot, krot;  // prologue (same meaning as the forward's)
+  size_t dt;                         // D_t: [B][H][T] float
+  size_t dqs;                        // slot part of dq: [B][T][H][d] float
+  size_t wp;                         // adjoint weights: [B*H][NC][2][mp][C] dtype
+  size_t sdl, pp, acon;              // [B*H][NC*C][mp] float
+  size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp][d] dtype
+  size_t dkap, dnu;                  // slot parts of dk, dv at the key row: [B][T][Hkv][d] float
+  size_t csum, carry;                // [B*Hkv][NC][mp] float
+  size_t total;
+};
 
-int bwd_stages(const Shape&, const char**, int) { return 0; }
+static BwdWs bwd_ws_layout(const Shape& s) {
+  BwdWs L;
+  FwdWs F = fwd_ws_layout(s);
+  L.sst = F.sst;
+  L.wt = F.wt;
+  L.aend = F.aend;
+  L.qrot = F.qrot;
+  L.krot = F.krot;
+  size_t off = F.ol;  // the forward's partial-output region is not needed here
+  const size_t BH = (size_t)s.B * s.H, units = (size_t)s.B * s.Hkv, TT = (size_t)s.NC * s.C;
+  L.dt = off;
+  off += align256(BH * s.T * 4);
+  L.dqs = off;
+  off += align256((size_t)s.B * s.T * s.H * s.d * 4);
+  L.wp = off;
+  off += align256(BH * s.NC * 2 * (size_t)s.mp * s.C * s.esz);
+  L.sdl = off;
+  off += align256(BH * TT * s.mp * 4);
+  L.pp = off;
+  off += align256(BH * TT * s.mp * 4);
+  L.acon = off;
+  off += align256(BH * TT * s.mp * 4);
+  L.lin = off;
+  off += align256(units * s.NC * 2 * (size_t)s.mp * s.d * s.esz);
+  L.dkap = off;
+  off += align256((size_t)s.B * s.T * s.Hkv * s.d * 4);
+  L.dnu = off;
+  off += align256((size_t)s.B * s.T * s.Hkv * s.d * 4);
+  L.csum = off;
+  off += align256(units * s.NC * s.mp * 4);
+  L.carry = off;
+  off += align256(units * s.NC * s.mp * 4);
+  L.total = off;
+  return L;
+}
 
-hipError_t launch_bwd(const Shape&, const RopeTheta&, const BwdPtrs&, hipStream_t) {
-  return hipErrorNotSupported;
+size_t bwd_ws_bytes(const Shape& s) { return bwd_ws_layout(s).total; }
+
+// ---------------------------------------------------------------- D_t
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ o, const T* __restrict__ dO,
+                                                  float* __restrict__ Dt, int Tn, int H, long nrows) {
+  constexpr int TPR = D / 8;  // threads per row (4, 8 or 16), a divisor of 64
+  long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  long r = gid / TPR;
+  int part = (int)(gid % TPR);
+  float acc = 0.f;
+  if (r < nrows) {
+    float a[8], b[8];
+    ld8f<T>(o + r * D + part * 8, a);
+    ld8f<T>(dO + r * D + part * 8, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += a[e] * b[e];
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (r < nrows && part == 0) {
+    long h = r % H, bt = r / H, t = bt % Tn, b = bt / Tn;
+    Dt[(b * H + h) * Tn + t] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- reverse-time slot products
+// For one wave owning chunk rows r0 .. r0+15 (lane: row t = t0 + r0 + cc,
+// slots i = 16 mb + 4 g + r) and one query head's sources W[u][i] on rows
+// vec_u (sW fp32 [u][i]; sVec [u][d]; sVecT [d][u]), with
+//     Lam_t[i] = sum_{u>=t in chunk} 2^{G_u - G_t}[i] W_u[i] vec_u   (+ the
+//     incoming adjoint, handled by the caller):
+//   accO (O^T[d][t]) += sum_i bt_t[i] Lam_t[i]
+//   F[mb][r]         += <Lam_t[i], key_t>
+// Cross-block pairs refer to F_I = G at the last row of the wave's block.
+template <typename T, int D, int MP, int C>
+__device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const float* sW, const float* sG,
+                                         const T* sA, const typename Vec<T>::v8* keyf,
+                                         const float (&bwI)[MP / 16][4], const float (&bt)[MP / 16][4], int I,
+                                         int t0, int w, int Tn, floatx4 (&accO)[D / 16], float (&F)[MP / 16][4]) {
+  constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
+  const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc, rl = r0 + 15;
+  floatx4 accA[NW];  // A[u][t] = vec_u . key_t, D layout [u = 16J + 4g + r][t = cc]
+#pragma unroll
+  for (int J = 0; J < NW; ++J) {
+    accA[J] = zero4();
+    if (J >= I) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        accA[J] = mma32(accA[J], ld8<T>(&sVec[(16 * J + cc) * PD + 32 * ks + 8 * g]), keyf[ks]);
+    }
+  }
+  // later blocks J > I
+#pragma unroll
+  for (int J = 0; J < NW; ++J) {
+    if (J > I) {
+      const int uA = 16 * J + cc;  // A-fragment row of this lane
+      floatx4 mt = zero4();        // M^T[u][t] = sum_i Y[u][i] bwI[t][i]
+#pragma unroll
+      for (int s = 0; s < NB / 2; ++s) {
+        float f[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
+          f[r] = sW[uA * MP + i0] * fast_exp2(sG[uA * MP + i0] - sG[rl * MP + i0]);
+          f[4 + r] = sW[uA * MP + i1] * fast_exp2(sG[uA * MP + i1] - sG[rl * MP + i1]);
+        }
+        typename Vec<T>::v8 bfr = pack8<T>(floatx4{bwI[2 * s][0], bwI[2 * s][1], bwI[2 * s][2], bwI[2 * s][3]},
+                                           floatx4{bwI[2 * s + 1][0], bwI[2 * s + 1][1], bwI[2 * s + 1][2],
+                                                   bwI[2 * s + 1][3]});
+        mt = mma32(mt, pack8<T>(f), bfr);
+      }
+      typename Vec<T>::v4 mfr = pack4<T>(mt);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        accO[db] = mma16(accO[db], ld4<T>(&sVecT[(16 * db + cc) * PC + 16 * J + 4 * g]), mfr);
+      typename Vec<T>::v4 afr = pack4<T>(accA[J]);
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        const int iA = 16 * mb + cc;
+        floatx4 y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int u = 16 * J + 4 * g + r;
+          y[r] = sW[u * MP + iA] * fast_exp2(sG[u * MP + iA] - sG[rl * MP + iA]);
+        }
+        floatx4 x = mma16(zero4(), pack4<T>(y), afr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int i = 16 * mb + 4 * g + r;
+          F[mb][r] += fast_exp2(sG[rl * MP + i] - sG[urow * MP + i]) * x[r];
+        }
+      }
+    }
+  }
+  // same block: u >= t, exact running products D'_{t,u} = prod_{j=t+1..u} a_j
+  floatx4 aI = accA[0];
+#pragma unroll
+  for (int J = 1; J < NW; ++J)
+    if (J == I) aI = accA[J];
+  float Ad[16];
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ad[4 * gg + r] = __shfl(aI[r], cc + 16 * gg, 64);
+  float Dp[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Dp[mb][r] = 1.f;
+  float mine[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int uu = 0; uu < 16; ++uu) {
+    float mp = 0.f;
+    if (uu >= cc) {
+      const int u = r0 + uu;
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        floatx4 w4 = *reinterpret_cast<const floatx4*>(&sW[u * MP + 16 * mb + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          F[mb][r] += Dp[mb][r] * w4[r] * Ad[uu];
+          mp += bt[mb][r] * Dp[mb][r] * w4[r];
+        }
+      }
+      if (uu < 15) {
+        const int u1 = u + 1, t1 = t0 + u1;
+        const bool ab1 = (t1 >= w) && (t1 < Tn);
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+          typename Vec<T>::v4 al = ld4<T>(&sA[u1 * PM + 16 * mb + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Dp[mb][r] *= ab1 ? to_f<T>(al[r]) : 1.f;
+        }
+      }
+    }
+    mp = sum_over_g(mp);
+    if ((uu >> 2) == g) mine[uu & 3] = mp;
+  }
+  typename Vec<T>::v4 bfr;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bfr[r] = to_t<T>(mine[r]);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    accO[db] = mma16(accO[db], ld4<T>(&sVecT[(16 * db + cc) * PC + r0 + 4 * g]), bfr);
+}
+
+// In-place reverse inclusive cumsum over the C rows of an LDS tile (fp32).
+template <int C, int MP, int P, int NT>
+__device__ __forceinline__ void lds_col_rcumsum(float* g, int tid) {
+  constexpr int PARTS = (NT / MP) < C ? (NT / MP) : C;
+  constexpr int RP = C / PARTS;
+  const int i = tid % MP, part = tid / MP;
+  const bool act = part < PARTS;
+  if (act) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = (part + 1) * RP - 1; u >= part * RP; --u) {
+      acc += g[u * P + i];
+      g[u * P + i] = acc;
+    }
+  }
+  __syncthreads();
+  float off = 0.f;
+  if (act)
+    for (int pp = part + 1; pp < PARTS; ++pp) off += g[(pp * RP) * P + i];
+  __syncthreads();
+  if (act && part + 1 < PARTS) {
+#pragma unroll
+    for (int u = part * RP; u < (part + 1) * RP; ++u) g[u * P + i] += off;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- slot pass A
+template <typename T, int D, int MP, int C>
+struct SlotBwdASmem {
+  static constexpr int PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
+  T sSK[MP * PD];   // S^K_{t0-1} [i][d]
+  T sSKt[D * PM];   // S^K_{t0-1}^T [d][i]
+  T sSV[MP * PD];   // S^V_{t0-1} [i][d]
+  T sK[C * PD];     // kappa rows [u][d]
+  T sKt[D * PC];    // kappa^T [d][u]
+  T sV[C * PD];     // nu rows [u][d]
+  T sA[C * PM];
+  T sB[C * PM];
+  T sBt[MP * PC];
+  float sG[C * MP];
+};
+
+// grid (NC, B*H), C/16 waves.
+template <typename T, int D, int MP, int C>
+__global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
+    const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
+    const T* __restrict__ dO, const T* __restrict__ sst, const float* __restrict__ lse,
+    const float* __restrict__ Dt, float* __restrict__ dqs, T* __restrict__ wp, float* __restrict__ sdl,
+    float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m, int w, int NC, float scale) {
+  using S = SlotBwdASmem<T, D, MP, C>;
+  constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
+  __shared__ S sm;
+  const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  const int unit = b * Hkv + hg, t0 = c * C;
+  {
+    const T* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
+    RowTile<T, D, NT, MP> tsk, tsv;
+    PairTileT<T, D, NT, MP> tskt;
+    tsk.load(src, D, 0, MP, tid);
+    tskt.load(src, D, 0, MP, tid);
+    tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
+    const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+    RowTile<T, D, NT, C> tk, tv;
+    PairTileT<T, D, NT, C> tkt;
+    tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    tkt.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    tv.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    stage_gates<T, C, MP, MP, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    tsk.template store<PD>(sm.sSK, tid);
+    tskt.template store<PM>(sm.sSKt, tid);
+    tsv.template store<PD>(sm.sSV, tid);
+    tk.template store<PD>(sm.sK, tid);
+    tkt.template store<PC>(sm.sKt, tid);
+    tv.template store<PD>(sm.sV, tid);
+  }
+  __syncthreads();
+  lds_col_cumsum<C, MP, MP, NT>(sm.sG, tid);
+  for (int e = tid; e < C * MP; e += NT) {
+    int u = e / MP, i = e % MP, t = t0 + u;
+    float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sm.sA[u * PM + i]) : 0.f;
+    T tv = to_t<T>(fast_exp2(sm.sG[(u | 15) * MP + i] - sm.sG[u * MP + i]) * be);
+    sm.sB[u * PM + i] = tv;
+    sm.sBt[i * PC + u] = tv;
+  }
+  __syncthreads();
+
+  const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
+  const bool qvalid = tq < Tn;
+  typename Vec<T>::v8 qf[D / 32], df[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    size_t off = (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g;
+    qf[ks] = qvalid ? ld8<T>(q + off) : zero8<T>();
+    df[ks] = qvalid ? ld8<T>(dO + off) : zero8<T>();
+  }
+  const float lse_t = qvalid ? lse[(size_t)bh * Tn + tq] : 0.f;
+  const float D_t = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  float lg[NB][4], dp[NB][4];
+  slot_read<T, D, MP, C>(sm.sSK, sm.sK, sm.sBt, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+  slot_read<T, D, MP, C>(sm.sSV, sm.sV, sm.sBt, sm.sG, sm.sA, df, I, t0, w, Tn, dp);
+  float p[NB][4], dl[NB][4];
+  float* sdl_row = sdl + ((size_t)bh * NC * C + urow + t0) * MP;
+  float* pp_row = pp + ((size_t)bh * NC * C + urow + t0) * MP;
+  float* ac_row = acon + ((size_t)bh * NC * C + urow + t0) * MP;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    floatx4 vs, vp, va;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int i = 16 * mb + 4 * g + r;
+      float ls = lg[mb][r] * scale;
+      float pv = (i < m && qvalid) ? fast_exp2((ls - lse_t) * NHA_LOG2E) : 0.f;
+      float dlv = pv * (dp[mb][r] - D_t);
+      p[mb][r] = pv;
+      dl[mb][r] = dlv;
+      vs[r] = scale * dlv;
+      vp[r] = pv;
+      va[r] = dlv * ls + pv * dp[mb][r];
+    }
+    *reinterpret_cast<floatx4*>(sdl_row + 16 * mb + 4 * g) = vs;
+    *reinterpret_cast<floatx4*>(pp_row + 16 * mb + 4 * g) = vp;
+    *reinterpret_cast<floatx4*>(ac_row + 16 * mb + 4 * g) = va;
+  }
+  // slot part of dq: s sum_i dl_t[i] SK_t[i]
+  floatx4 accO[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
+  slot_mix<T, D, MP, C, PC>(sm.sSKt, sm.sKt, sm.sB, sm.sG, sm.sA, dl, I, t0, w, Tn, accO);
+  if (qvalid) {
+    float* dst = dqs + (((size_t)b * Tn + tq) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<floatx4*>(dst + 16 * db + 4 * g) = accO[db] * scale;
+  }
+  // adjoint weights 2^{G_u} s dl_u[i] and 2^{G_u} p_u[i], [i][u] layout
+  T* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
+  T* wv = wk + (size_t)MP * C;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int i = 16 * mb + 4 * g + r;
+      float e = fast_exp2(sm.sG[urow * MP + i]);
+      wk[(size_t)i * C + urow] = to_t<T>(e * scale * dl[mb][r]);
+      wv[(size_t)i * C + urow] = to_t<T>(e * p[mb][r]);
+    }
+}
+
+// ---------------------------------------------------------------- adjoint scan
+// grid (d/16, B*Hkv), one wave.  Lane keeps Lam^T[j0 + 4g + r][16 nb + c] for
+// K and V.  Chunks in reverse: store Lin_c (the adjoint entering chunk c from
+// the right, [i][d] layout), then Lam <- aend (.) Lam + sum_h W'_h^T vec_h.
+template <typename T, int C, int MP>
+__global__ __launch_bounds__(64) void k_adj_scan(const T* __restrict__ q, const T* __restrict__ dO,
+                                                 const T* __restrict__ wp, const float* __restrict__ aend,
+                                                 T* __restrict__ lin, int Tn, int H, int Hkv, int d, int NC) {
+  constexpr int NB = MP / 16;
+  constexpr int PC = pitch_of(C);
+  constexpr bool K16 = (C % 32) != 0;
+  __shared__ T sQt[16 * PC];
+  __shared__ T sOt[16 * PC];
+  const int l = threadIdx.x, g = l >> 4, cc = l & 15;
+  const int j0 = blockIdx.x * 16, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  floatx4 LK[NB], LV[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) LK[nb] = LV[nb] = zero4();
+  for (int c = NC - 1; c >= 0; --c) {
+    T* dst = lin + ((size_t)unit * NC + c) * 2 * MP * d;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int i = 16 * nb + cc;
+      st4<T>(dst + (size_t)i * d + j0 + 4 * g, pack4<T>(LK[nb]));
+      st4<T>(dst + (size_t)MP * d + (size_t)i * d + j0 + 4 * g, pack4<T>(LV[nb]));
+      float a = aend[((size_t)unit * NC + c) * MP + i];
+      LK[nb] *= a;
+      LV[nb] *= a;
+    }
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = hg * G + hh, bh = b * H + h;
+      if (l < C) {
+        int t = c * C + l;
+        typename Vec<T>::v8 q0 = zero8<T>(), q1 = zero8<T>(), o0 = zero8<T>(), o1 = zero8<T>();
+        if (t < Tn) {
+          size_t row = (((size_t)b * Tn + t) * H + h) * d + j0;
+          q0 = ld8<T>(q + row);
+          q1 = ld8<T>(q + row + 8);
+          o0 = ld8<T>(dO + row);
+          o1 = ld8<T>(dO + row + 8);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sQt[e * PC + l] = q0[e];
+          sQt[(8 + e) * PC + l] = q1[e];
+          sOt[e * PC + l] = o0[e];
+          sOt[(8 + e) * PC + l] = o1[e];
+        }
+      }
+      __syncthreads();
+      const T* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
+      const T* wv = wk + (size_t)MP * C;
+      if constexpr (K16) {
+#pragma unroll
+        for (int s = 0; s < C / 16; ++s) {
+          typename Vec<T>::v4 aq = ld4<T>(&sQt[cc * PC + 16 * s + 4 * g]);
+          typename Vec<T>::v4 ao = ld4<T>(&sOt[cc * PC + 16 * s + 4 * g]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            LK[nb] = mma16(LK[nb], aq, ld4<T>(wk + (size_t)(16 * nb + cc) * C + 16 * s + 4 * g));
+            LV[nb] = mma16(LV[nb], ao, ld4<T>(wv + (size_t)(16 * nb + cc) * C + 16 * s + 4 * g));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < C / 32; ++s) {
+          typename Vec<T>::v8 aq = ld8<T>(&sQt[cc * PC + 32 * s + 8 * g]);
+          typename Vec<T>::v8 ao = ld8<T>(&sOt[cc * PC + 32 * s + 8 * g]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            LK[nb] = mma32(LK[nb], aq, ld8<T>(wk + (size_t)(16 * nb + cc) * C + 32 * s + 8 * g));
+            LV[nb] = mma32(LV[nb], ao, ld8<T>(wv + (size_t)(16 * nb + cc) * C + 32 * s + 8 * g));
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- slot pass B
+template <typename T, int D, int MP, int C>
+struct SlotBwdBSmem {
+  static constexpr int PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
+  T sL[MP * PD];     // incoming adjoint Lin [i][d]
+  T sLt[D * PM];     // Lin^T [d][i]
+  T sKey[C * PD];    // kappa or nu rows [u][d]
+  T sVec[C * PD];    // q or dO rows of one head [u][d]
+  T sVecT[D * PC];   // same, transposed
+  T sA[C * PM];
+  float sG[C * MP];
+  float sW[C * MP];  // s dl or p of one head [u][i]; later the (A - bF) tile
+};
+
+// grid (NC, B*Hkv), C/16 waves; all query heads of the KV group.
+template <typename T, int D, int MP, int C>
+__global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
+    const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
+    const T* __restrict__ dO, const T* __restrict__ lin, const float* __restrict__ sdl,
+    const float* __restrict__ pp, const float* __restrict__ acon, float* __restrict__ dkap,
+    float* __restrict__ dnu, float* __restrict__ dalpha, float* __restrict__ csum, int Tn, int H, int Hkv, int m,
+    int w, int NC) {
+  using S = SlotBwdBSmem<T, D, MP, C>;
+  constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
+  __shared__ S sm;
+  const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int c = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv, t0 = c * C;
+  const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
+  stage_gates<T, C, MP, MP, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+  __syncthreads();
+  lds_col_cumsum<C, MP, MP, NT>(sm.sG, tid);
+  const bool absorb = (tq >= w) && (tq < Tn);
+  float bt[NB][4], bwI[NB][4], bwE[NB][4], F[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int i = 16 * mb + 4 * g + r;
+      float be = (absorb && i < m) ? 1.f - to_f<T>(sm.sA[urow * PM + i]) : 0.f;
+      float Gt = sm.sG[urow * MP + i];
+      bt[mb][r] = be;
+      bwI[mb][r] = be * fast_exp2(sm.sG[(r0 + 15) * MP + i] - Gt);
+      bwE[mb][r] = be * fast_exp2(sm.sG[(C - 1) * MP + i] - Gt);
+      F[mb][r] = 0.f;
+    }
+  const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+  for (int side = 0; side < 2; ++side) {
+    __syncthreads();
+    {
+      const T* src = lin + (((size_t)unit * NC + c) * 2 + side) * MP * D;
+      RowTile<T, D, NT, MP> tl;
+      PairTileT<T, D, NT, MP> tlt;
+      RowTile<T, D, NT, C> tkey;
+      tl.load(src, D, 0, MP, tid);
+      tlt.load(src, D, 0, MP, tid);
+      tkey.load((side ? vv : kk) + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+      tl.template store<PD>(sm.sL, tid);
+      tlt.template store<PM>(sm.sLt, tid);
+      tkey.template store<PD>(sm.sKey, tid);
+    }
+    __syncthreads();
+    typename Vec<T>::v8 keyf[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) keyf[ks] = ld8<T>(&sm.sKey[urow * PD + 32 * ks + 8 * g]);
+    floatx4 accO[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
+    // incoming adjoint: F += 2^{G_end - G_t} <Lin[i], key_t>,  O += sum_i bwE_t[i] Lin[i]
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+      floatx4 x = zero4();
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) x = mma32(x, ld8<T>(&sm.sL[(16 * mb + cc) * PD + 32 * ks + 8 * g]), keyf[ks]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int i = 16 * mb + 4 * g + r;
+        F[mb][r] += fast_exp2(sm.sG[(C - 1) * MP + i] - sm.sG[urow * MP + i]) * x[r];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NB / 2; ++s) {
+      typename Vec<T>::v8 bfr = pack8<T>(floatx4{bwE[2 * s][0], bwE[2 * s][1], bwE[2 * s][2], bwE[2 * s][3]},
+                                         floatx4{bwE[2 * s + 1][0], bwE[2 * s + 1][1], bwE[2 * s + 1][2],
+                                                 bwE[2 * s + 1][3]});
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        accO[db] = mma32(accO[db],
+                         ld4x2<T>(&sm.sLt[(16 * db + cc) * PM + 32 * s + 4 * g],
+                                  &sm.sLt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]),
+                         bfr);
+    }
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = hg * G + hh, bh = b * H + h;
+      __syncthreads();
+      {
+        const T* vb = (side ? dO : q) + (((size_t)b * Tn + t0) * H + h) * D;
+        RowTile<T, D, NT, C> tv;
+        PairTileT<T, D, NT, C> tvt;
+        tv.load(vb, (size_t)H * D, 0, Tn - t0, tid);
+        tvt.load(vb, (size_t)H * D, 0, Tn - t0, tid);
+        const float* wsrc = (side ? pp : sdl) + ((size_t)bh * NC * C + t0) * MP;
+        for (int e = tid * 4; e < C * MP; e += NT * 4)
+          *reinterpret_cast<floatx4*>(&sm.sW[e]) = *reinterpret_cast<const floatx4*>(wsrc + e);
+        tv.template store<PD>(sm.sVec, tid);
+        tvt.template store<PC>(sm.sVecT, tid);
+      }
+      __syncthreads();
+      slot_rev<T, D, MP, C>(sm.sVec, sm.sVecT, sm.sW, sm.sG, sm.sA, keyf, bwI, bt, I, t0, w, Tn, accO, F);
+    }
+    if (absorb) {
+      float* dst = (side ? dnu : dkap) + (((size_t)b * Tn + (tq - w)) * Hkv + hg) * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) *reinterpret_cast<floatx4*>(dst + 16 * db + 4 * g) = accO[db];
+    }
+  }
+  // X_t = A_t - b_t F_t, its reverse cumsum inside the chunk, local dalpha
+  float X[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[mb][r] = -bt[mb][r] * F[mb][r];
+  for (int hh = 0; hh < G; ++hh) {
+    const float* ar = acon + ((size_t)(b * H + hg * G + hh) * NC * C + t0 + urow) * MP;
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+      floatx4 a4 = *reinterpret_cast<const floatx4*>(ar + 16 * mb + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[mb][r] += a4[r];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+    *reinterpret_cast<floatx4*>(&sm.sW[urow * MP + 16 * mb + 4 * g]) =
+        floatx4{X[mb][0], X[mb][1], X[mb][2], X[mb][3]};
+  __syncthreads();
+  lds_col_rcumsum<C, MP, MP, NT>(sm.sW, tid);
+  if (tid < MP) csum[((size_t)unit * NC + c) * MP + tid] = sm.sW[tid];
+  if (tq < Tn) {
+    float* da = dalpha + (((size_t)b * Tn + tq) * Hkv + hg) * m;
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int i = 16 * mb + 4 * g + r;
+        if (i < m) {
+          float v = 0.f;
+          if (absorb) v = sm.sW[urow * MP + i] / to_f<T>(sm.sA[urow * PM + i]) - F[mb][r];
+          da[i] = v;
+        }
+      }
+  }
+}
+
+// carry[unit][c][i] = sum over later chunks of the chunk totals of (A - b F)
+template <int MP>
+__global__ void k_dalpha_carry(const float* __restrict__ csum, float* __restrict__ carry, int NC) {
+  const int unit = blockIdx.x, i = threadIdx.x;
+  float acc = 0.f;
+  for (int c = NC - 1; c >= 0; --c) {
+    carry[((size_t)unit * NC + c) * MP + i] = acc;
+    acc += csum[((size_t)unit * NC + c) * MP + i];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_dalpha_fix(const T* __restrict__ alpha, const float* __restrict__ carry,
+                                                    float* __restrict__ dalpha, int Tn, int Hkv, int m, int mp,
+                                                    int w, int C, int NC, long n) {
+  long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  int i = (int)(e % m);
+  long r = e / m;
+  int hg = (int)(r % Hkv);
+  long bt = r / Hkv;
+  int t = (int)(bt % Tn), b = (int)(bt / Tn);
+  if (t < w) return;
+  int unit = b * Hkv + hg, c = t / C;
+  dalpha[e] += carry[((size_t)unit * NC + c) * mp + i] / to_f<T>(alpha[e]);
+}
+
+// ---------------------------------------------------------------- window backward: dq
+// grid (ceil(T/64), B*H), 4 waves x 16 queries.  dq = R_t^T s sum_j dl_tj R_j k_j
+// + the slot part.  Per key tile: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, and
+// dq^T += K^T dS^T.
+template <typename T, int D>
+struct WinBwdDqSmem {
+  static constexpr int PD = pitch_of(D), PK = 64 + 4;
+  T k[64 * PD];
+  T v[64 * PD];
+  T kt[D * PK];
+};
+
+__device__ __forceinline__ void rope_cs(double theta, int pos, float& cs, float& sn) {
+  double ang = (double)pos * theta;
+  ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+  sincosf((float)ang, &sn, &cs);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_win_bwd_dq(const T* __restrict__ qr, const T* __restrict__ kr,
+                                                       const T* __restrict__ vv, const T* __restrict__ dO,
+                                                       const float* __restrict__ lse, const float* __restrict__ Dt,
+                                                       const float* __restrict__ dqs, T* __restrict__ dq, int Tn,
+                                                       int H, int Hkv, int w, float scale, RopeTheta th, int rope) {
+  using S = WinBwdDqSmem<T, D>;
+  constexpr int PD = S::PD, PK = S::PK;
+  __shared__ S sm;
+  const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int q0 = (L % gridDim.x) * 64, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  const int tq = q0 + 16 * W + cc;
+  const bool qvalid = tq < Tn;
+  typename Vec<T>::v8 qf[D / 32], df[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    size_t off = (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g;
+    qf[ks] = qvalid ? ld8<T>(qr + off) : zero8<T>();
+    df[ks] = qvalid ? ld8<T>(dO + off) : zero8<T>();
+  }
+  const float lse2 = qvalid ? lse[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
+  const float D_t = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  const float sl2 = scale * NHA_LOG2E;
+  floatx4 acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc[db] = zero4();
+  if (w > 0) {
+    int kmin = q0 - w + 1;
+    if (kmin < 0) kmin = 0;
+    int kmax = q0 + 63;
+    if (kmax > Tn - 1) kmax = Tn - 1;
+    const int jfirst = (kmin / 64) * 64;
+    const int ntiles = (kmax - jfirst) / 64 + 1;
+    const size_t ld = (size_t)Hkv * D;
+    const T* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
+    const T* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
+    RowTile<T, D, 256> tk, tv;
+    PairTileT<T, D, 256> tkt;
+    tk.load(kbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
+    tv.load(vbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
+    tkt.load(kbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
+    for (int it = 0; it < ntiles; ++it) {
+      const int j0 = jfirst + 64 * it;
+      __syncthreads();
+      tk.template store<PD>(sm.k, tid);
+      tv.template store<PD>(sm.v, tid);
+      tkt.template store<PK>(sm.kt, tid);
+      __syncthreads();
+      if (it + 1 < ntiles) {
+        int jn = j0 + 64;
+        tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+        tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+        tkt.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+      }
+      float ds[4][4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        floatx4 s4 = zero4(), dp4 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          s4 = mma32(s4, ld8<T>(&sm.k[(16 * mb + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
+          dp4 = mma32(dp4, ld8<T>(&sm.v[(16 * mb + cc) * PD + 32 * ks + 8 * g]), df[ks]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int key = j0 + 16 * mb + 4 * g + r;
+          bool ok = qvalid && key <= tq && key > tq - w && key < Tn;
+          float pv = ok ? fast_exp2(s4[r] * sl2 - lse2) : 0.f;
+          ds[mb][r] = pv * (dp4[r] - D_t);
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        typename Vec<T>::v8 bfr = pack8<T>(floatx4{ds[2 * st][0], ds[2 * st][1], ds[2 * st][2], ds[2 * st][3]},
+                                           floatx4{ds[2 * st + 1][0], ds[2 * st + 1][1], ds[2 * st + 1][2],
+                                                   ds[2 * st + 1][3]});
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+          acc[db] = mma32(acc[db],
+                          ld4x2<T>(&sm.kt[(16 * db + cc) * PK + 32 * st + 4 * g],
+                                   &sm.kt[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
+                          bfr);
+      }
+    }
+  }
+  if (qvalid) {
+    // acc[db][r] = dq_rot[d = 16 db + 4 g + r] / scale; rotate back by R_t^T
+    constexpr int HB = D / 32;  // d-blocks per half
+    float out[D / 16][4];
+#pragma unroll
+    for (int db = 0; db < HB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int i = 16 * db + 4 * g + r;
+        float x1 = acc[db][r] * scale, x2 = acc[db + HB][r] * scale, cs = 1.f, sn = 0.f;
+        if (rope) rope_cs(th.theta[i], tq, cs, sn);
+        out[db][r] = x1 * cs + x2 * sn;
+        out[db + HB][r] = x2 * cs - x1 * sn;
+      }
+    const float* sl = dqs + (((size_t)b * Tn + tq) * H + h) * D;
+    T* dst = dq + (((size_t)b * Tn + tq) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      floatx4 s4 = *reinterpret_cast<const floatx4*>(sl + 16 * db + 4 * g);
+      st4<T>(dst + 16 * db + 4 * g,
+             pack4<T>(floatx4{out[db][0] + s4[0], out[db][1] + s4[1], out[db][2] + s4[2], out[db][3] + s4[3]}));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- window backward: dk, dv
+// grid (ceil(T/64), B*Hkv), 4 waves x 16 keys.  Loops over the group's query
+// heads and the query tiles whose band reaches the keys.  Per query tile:
+// S = Q K^T, P, dP = dO V^T, dS; dv^T += dO^T P, dk^T += Q^T dS.
+template <typename T, int D>
+struct WinBwdKvSmem {
+  static constexpr int PD = pitch_of(D), PK = 64 + 4;
+  T q[64 * PD];
+  T qt[D * PK];
+  T o[64 * PD];
+  T ot[D * PK];
+  float lse2[64];
+  float dd[64];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_win_bwd_dkdv(
+    const T* __restrict__ qr, const T* __restrict__ kr, const T* __restrict__ vv, const T* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Dt, const float* __restrict__ dkap,
+    const float* __restrict__ dnu, T* __restrict__ dk, T* __restrict__ dv, int Tn, int H, int Hkv, int w,
+    float scale, RopeTheta th, int rope) {
+  using S = WinBwdKvSmem<T, D>;
+  constexpr int PD = S::PD, PK = S::PK;
+  __shared__ S sm;
+  const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int k0 = (L % gridDim.x) * 64, unit = L / gridDim.x, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  const int key = k0 + 16 * W + cc;
+  const bool kvalid = key < Tn;
+  typename Vec<T>::v8 kf[D / 32], vf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    size_t off = (((size_t)b * Tn + key) * Hkv + hg) * D + 32 * ks + 8 * g;
+    kf[ks] = kvalid ? ld8<T>(kr + off) : zero8<T>();
+    vf[ks] = kvalid ? ld8<T>(vv + off) : zero8<T>();
+  }
+  const float sl2 = scale * NHA_LOG2E;
+  floatx4 adk[D / 16], adv[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) adk[db] = adv[db] = zero4();
+  if (w > 0) {
+    int tmax = k0 + 63 + w - 1;
+    if (tmax > Tn - 1) tmax = Tn - 1;
+    const int ntiles = k0 <= tmax ? (tmax - k0) / 64 + 1 : 0;
+    const size_t ld = (size_t)H * D;
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = hg * G + hh, bh = b * H + h;
+      const T* qbase = qr + ((size_t)b * Tn * H + h) * D;
+      const T* obase = dO + ((size_t)b * Tn * H + h) * D;
+      RowTile<T, D, 256> tq, to;
+      PairTileT<T, D, 256> tqt, tot;
+      if (ntiles > 0) {
+        tq.load(qbase + (size_t)k0 * ld, ld, 0, Tn - k0, tid);
+        tqt.load(qbase + (size_t)k0 * ld, ld, 0, Tn - k0, tid);
+        to.load(obase + (size_t)k0 * ld, ld, 0, Tn - k0, tid);
+        tot.load(obase + (size_t)k0 * ld, ld, 0, Tn - k0, tid);
+      }
+      for (int it = 0; it < ntiles; ++it) {
+        const int q0 = k0 + 64 * it;
+        __syncthreads();
+        tq.template store<PD>(sm.q, tid);
+        tqt.template store<PK>(sm.qt, tid);
+        to.template store<PD>(sm.o, tid);
+        tot.template store<PK>(sm.ot, tid);
+        if (tid < 64) {
+          int t = q0 + tid;
+          sm.lse2[tid] = t < Tn ? lse[(size_t)bh * Tn + t] * NHA_LOG2E : 0.f;
+          sm.dd[tid] = t < Tn ? Dt[(size_t)bh * Tn + t] : 0.f;
+        }
+        __syncthreads();
+        if (it + 1 < ntiles) {
+          int qn = q0 + 64;
+          tq.load(qbase + (size_t)qn * ld, ld, 0, Tn - qn, tid);
+          tqt.load(qbase + (size_t)qn * ld, ld, 0, Tn - qn, tid);
+          to.load(obase + (size_t)qn * ld, ld, 0, Tn - qn, tid);
+          tot.load(obase + (size_t)qn * ld, ld, 0, Tn - qn, tid);
+        }
+        float pm[4][4], ds[4][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          floatx4 s4 = zero4(), dp4 = zero4();
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) {
+            s4 = mma32(s4, ld8<T>(&sm.q[(16 * mb + cc) * PD + 32 * ks + 8 * g]), kf[ks]);
+            dp4 = mma32(dp4, ld8<T>(&sm.o[(16 * mb + cc) * PD + 32 * ks + 8 * g]), vf[ks]);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int tl = 16 * mb + 4 * g + r, t = q0 + tl;
+            bool ok = kvalid && t < Tn && key <= t && key > t - w;
+            float pv = ok ? fast_exp2(s4[r] * sl2 - sm.lse2[tl]) : 0.f;
+            pm[mb][r] = pv;
+            ds[mb][r] = pv * (dp4[r] - sm.dd[tl]);
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          typename Vec<T>::v8 pfr = pack8<T>(floatx4{pm[2 * st][0], pm[2 * st][1], pm[2 * st][2], pm[2 * st][3]},
+                                             floatx4{pm[2 * st + 1][0], pm[2 * st + 1][1], pm[2 * st + 1][2],
+                                                     pm[2 * st + 1][3]});
+          typename Vec<T>::v8 dfr = pack8<T>(floatx4{ds[2 * st][0], ds[2 * st][1], ds[2 * st][2], ds[2 * st][3]},
+                                             floatx4{ds[2 * st + 1][0], ds[2 * st + 1][1], ds[2 * st + 1][2],
+                                                     ds[2 * st + 1][3]});
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) {
+            adv[db] = mma32(adv[db],
+                            ld4x2<T>(&sm.ot[(16 * db + cc) * PK + 32 * st + 4 * g],
+                                     &sm.ot[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
+                            pfr);
+            adk[db] = mma32(adk[db],
+                            ld4x2<T>(&sm.qt[(16 * db + cc) * PK + 32 * st + 4 * g],
+                                     &sm.qt[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
+                            dfr);
+          }
+        }
+      }
+    }
+  }
+  if (kvalid) {
+    constexpr int HB = D / 32;
+    float ok[D / 16][4];
+#pragma unroll
+    for (int db = 0; db < HB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int i = 16 * db + 4 * g + r;
+        float x1 = adk[db][r] * scale, x2 = adk[db + HB][r] * scale, cs = 1.f, sn = 0.f;
+        if (rope) rope_cs(th.theta[i], key, cs, sn);
+        ok[db][r] = x1 * cs + x2 * sn;
+        ok[db + HB][r] = x2 * cs - x1 * sn;
+      }
+    const size_t row = (((size_t)b * Tn + key) * Hkv + hg) * D;
+    const bool slot = key + w < Tn;  // this key row is also absorbed (at step key + w)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      floatx4 sk = zero4(), sv = zero4();
+      if (slot) {
+        sk = *reinterpret_cast<const floatx4*>(dkap + row + 16 * db + 4 * g);
+        sv = *reinterpret_cast<const floatx4*>(dnu + row + 16 * db + 4 * g);
+      }
+      st4<T>(dk + row + 16 * db + 4 * g,
+             pack4<T>(floatx4{ok[db][0] + sk[0], ok[db][1] + sk[1], ok[db][2] + sk[2], ok[db][3] + sk[3]}));
+      st4<T>(dv + row + 16 * db + 4 * g, pack4<T>(adv[db] + sv));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host launcher
+template <typename T, int D, int MP, int C>
+static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st) {
+  if constexpr (sizeof(SlotBwdASmem<T, D, MP, C>) > kMaxLds || sizeof(SlotBwdBSmem<T, D, MP, C>) > kMaxLds ||
+                sizeof(WinBwdKvSmem<T, D>) > kMaxLds) {
+    return hipErrorInvalidConfiguration;
+  } else {
+    BwdWs L = bwd_ws_layout(s);
+    char* ws = p.ws;
+    const T* q = (const T*)p.q;
+    const T* k = (const T*)p.k;
+    const T* v = (const T*)p.v;
+    const T* alpha = (const T*)p.alpha;
+    const T* dO = (const T*)p.dO;
+    const int units = s.B * s.Hkv;
+    Marks mk;
+    mk.ev = p.events;
+    ProloguePtrs pp{ws + L.sst, ws + L.wt, (float*)(ws + L.aend), nullptr, nullptr, nullptr, nullptr};
+    if (s.rope && s.win) {
+      pp.qrot = ws + L.qrot;
+      pp.krot = ws + L.krot;
+    }
+    hipError_t e = launch_prologue(s, th, q, k, v, alpha, pp, mk, st);
+    if (e != hipSuccess) return e;
+    const T* qr = pp.qrot ? (const T*)pp.qrot : q;
+    const T* kr = pp.krot ? (const T*)pp.krot : k;
+    float* Dt = (float*)(ws + L.dt);
+    float* dqs = (float*)(ws + L.dqs);
+    T* wpb = (T*)(ws + L.wp);
+    float* sdl = (float*)(ws + L.sdl);
+    float* ppb = (float*)(ws + L.pp);
+    float* acon = (float*)(ws + L.acon);
+    T* lin = (T*)(ws + L.lin);
+    float* dkap = (float*)(ws + L.dkap);
+    float* dnu = (float*)(ws + L.dnu);
+    float* csum = (float*)(ws + L.csum);
+    float* carry = (float*)(ws + L.carry);
+    const long nrows = (long)s.B * s.T * s.H;
+    mk.mark(st);
+    hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
+                       (const T*)p.o, dO, Dt, s.T, s.H, nrows);
+    mk.mark(st);
+    hipLaunchKernelGGL((k_bwd_slot_a<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
+                       dO, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w, s.NC,
+                       s.scale);
+    mk.mark(st);
+    hipLaunchKernelGGL((k_adj_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
+                       (const float*)pp.aend, lin, s.T, s.H, s.Hkv, D, s.NC);
+    mk.mark(st);
+    hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
+                       (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.w, s.NC);
+    mk.mark(st);
+    hipLaunchKernelGGL((k_dalpha_carry<MP>), dim3(units), dim3(MP), 0, st, csum, carry, s.NC);
+    const long na = (long)s.B * s.T * s.Hkv * s.m;
+    mk.mark(st);
+    hipLaunchKernelGGL(k_dalpha_fix<T>, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, st, alpha, carry, p.dalpha,
+                       s.T, s.Hkv, s.m, MP, s.w, C, s.NC, na);
+    mk.mark(st);
+    hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dqs,
+                       (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+    mk.mark(st);
+    hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dkap,
+                       dnu, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+    mk.mark(st);
+    return hipGetLastError();
+  }
+}
+
+template <typename T, int MP, int C>
+static hipError_t bwd_d(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st) {
+  switch (s.d) {
+    case 32: return bwd_impl<T, 32, MP, C>(s, th, p, st);
+    case 64: return bwd_impl<T, 64, MP, C>(s, th, p, st);
+    case 128: return bwd_impl<T, 128, MP, C>(s, th, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+template <typename T, int MP>
+static hipError_t bwd_c(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st) {
+  switch (s.C) {
+    case 16: return bwd_d<T, MP, 16>(s, th, p, st);
+    case 32: return bwd_d<T, MP, 32>(s, th, p, st);
+    case 64: return bwd_d<T, MP, 64>(s, th, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st) {
+  if (s.dtype == NHA_DTYPE_BF16) return s.mp == 32 ? bwd_c<bf16, 32>(s, th, p, st) : bwd_c<bf16, 64>(s, th, p, st);
+  return s.mp == 32 ? bwd_c<float, 32>(s, th, p, st) : bwd_c<float, 64>(s, th, p, st);
+}
+
+int bwd_stages(const Shape& s, const char** names, int max) {
+  const char* all[16];
+  int n = 0;
+  if (s.rope && s.win) {
+    all[n++] = "rope_q";
+    all[n++] = "rope_k";
+  }
+  all[n++] = "chunk_gates";
+  all[n++] = "state_scan";
+  all[n++] = "bwd_prep";
+  all[n++] = "slot_bwd_a";
+  all[n++] = "adj_scan";
+  all[n++] = "slot_bwd_b";
+  all[n++] = "dalpha_carry";
+  all[n++] = "dalpha_fix";
+  all[n++] = "win_bwd_dq";
+  all[n++] = "win_bwd_dkdv";
+  for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];
+  return n;
+}
+
+size_t slot_bwd_lds_bytes(const Shape& s) {
+  size_t e = s.esz;
+  size_t PD = pitch_of(s.d), PM = pitch_of(s.mp), PC = pitch_of(s.C);
+  size_t a = e * (2 * s.mp * PD + s.d * PM + 2 * s.C * PD + s.d * PC + 2 * s.C * PM + s.mp * PC) +
+             4 * (size_t)s.C * s.mp;
+  size_t b = e * (s.mp * PD + s.d * PM + 2 * s.C * PD + s.d * PC + s.C * PM) + 8 * (size_t)s.C * s.mp;
+  size_t kv = e * 2 * (64 * PD + s.d * 68) + 512;
+  size_t mx = a > b ? a : b;
+  return mx > kv ? mx : kv;
 }
 
 }  // namespace nha

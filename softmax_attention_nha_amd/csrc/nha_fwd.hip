@@ -32,6 +32,7 @@
 //   k_export_state  ring buffer + position of the decode state (optional)
 #include "nha_common.h"
 #include "nha_internal.h"
+#include "nha_slot.h"
 
 namespace nha {
 
@@ -66,51 +67,6 @@ __global__ __launch_bounds__(256) void k_rope(const T* __restrict__ x, T* __rest
 }
 
 // ---------------------------------------------------------------- gate prep
-// In-place inclusive cumsum over the C rows of an LDS tile g[u * P + i] (fp32)
-// for columns i < MP, by NT threads: each thread scans a run of rows of one
-// column, then adds the totals of the runs before it.
-template <int C, int MP, int P, int NT>
-__device__ __forceinline__ void lds_col_cumsum(float* g, int tid) {
-  constexpr int PARTS = (NT / MP) < C ? (NT / MP) : C;
-  constexpr int RP = C / PARTS;
-  const int i = tid % MP, part = tid / MP;
-  const bool act = part < PARTS;
-  if (act) {
-    float acc = 0.f;
-#pragma unroll
-    for (int u = part * RP; u < (part + 1) * RP; ++u) {
-      acc += g[u * P + i];
-      g[u * P + i] = acc;
-    }
-  }
-  __syncthreads();
-  float off = 0.f;
-  if (act)
-    for (int pp = 0; pp < part; ++pp) off += g[((pp + 1) * RP - 1) * P + i];
-  __syncthreads();
-  if (act && part > 0) {
-#pragma unroll
-    for (int u = part * RP; u < (part + 1) * RP; ++u) g[u * P + i] += off;
-  }
-  __syncthreads();
-}
-
-// Stage a chunk's gates into LDS: la[u][i] = log2 a_u (0 where nothing is
-// absorbed: t < w, t >= T or padded slot), al[u][i] = raw alpha (1 outside).
-template <typename T, int C, int MP, int PG, int PA, int NT>
-__device__ __forceinline__ void stage_gates(const T* __restrict__ alpha, float* la, T* al, int b, int hg, int t0,
-                                            int Tn, int Hkv, int m, int w, int tid) {
-  for (int e = tid; e < C * MP; e += NT) {
-    int u = e / MP, i = e % MP, t = t0 + u;
-    T av = to_t<T>(1.f);
-    if (i < m && t < Tn) av = alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i];
-    float l2 = 0.f;
-    if (i < m && t < Tn && t >= w) l2 = fmaxf(__log2f(to_f<T>(av)), NHA_LOG2A_MIN);
-    la[u * PG + i] = l2;
-    al[u * PA + i] = av;
-  }
-}
-
 // grid (NC, B*Hkv), 256 threads.
 // Wt[unit][c][i][u] = 2^{G_end,i - G_u,i} b_u,i   (0 for padded slots / rows)
 // aend[unit][c][i]  = 2^{G_end,i}
@@ -338,95 +294,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     qf[ks] = qvalid ? ld8<T>(q + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<T>();
-
-  // L^T[i][t] = S^K[i] . q_t
-  floatx4 accL[NB];
-#pragma unroll
-  for (int mb = 0; mb < NB; ++mb) {
-    accL[mb] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      accL[mb] = mma32(accL[mb], ld8<T>(&sm.sSK[(16 * mb + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
-  }
-  // A^T[u][t] = kappa_u . q_t for u in blocks 0..I
-  floatx4 accA[NW];
-#pragma unroll
-  for (int ub = 0; ub < NW; ++ub) {
-    accA[ub] = zero4();
-    if (ub <= I) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        accA[ub] = mma32(accA[ub], ld8<T>(&sm.sK[(16 * ub + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
-    }
-  }
-  // logits (before scale): lg[mb][r] for slot i = 16 mb + 4 g + r ... careful: D layout
-  // of accL is [i = 16 mb + 4 g + r][t = cc].
-  const int urow = r0 + cc;  // this lane's query row inside the chunk
   float lg[NB][4];
-#pragma unroll
-  for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int i = 16 * mb + 4 * g + r;
-      lg[mb][r] = fast_exp2(sm.sG[urow * MP + i]) * accL[mb][r];
-    }
-  // off-diagonal source blocks J < I
-#pragma unroll
-  for (int J = 0; J < NW; ++J) {
-    if (J < I) {
-      typename Vec<T>::v4 bfr = pack4<T>(accA[J]);  // A^T[16J + 4g + r][t]
-#pragma unroll
-      for (int mb = 0; mb < NB; ++mb) {
-        floatx4 x = mma16(zero4(), ld4<T>(&sm.sBt[(16 * mb + cc) * PC + 16 * J + 4 * g]), bfr);
-        // x = X_J^T[i = 16mb + 4g + r][t]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int i = 16 * mb + 4 * g + r;
-          lg[mb][r] += fast_exp2(sm.sG[urow * MP + i] - sm.sG[(16 * J + 15) * MP + i]) * x[r];
-        }
-      }
-    }
-  }
-  // diagonal block: exact running products.  Lane needs A[t][u] for all u of block I.
-  floatx4 aI = accA[0];
-#pragma unroll
-  for (int ub = 1; ub < NW; ++ub)
-    if (ub == I) aI = accA[ub];
-  float Ad[16];
-#pragma unroll
-  for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Ad[4 * gg + r] = __shfl(aI[r], cc + 16 * gg, 64);
-  {
-    float Dp[NB][4], dg[NB][4];
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Dp[mb][r] = 1.f, dg[mb][r] = 0.f;
-#pragma unroll
-    for (int uu = 15; uu >= 0; --uu) {
-      if (uu <= cc) {
-        int u = r0 + uu, t = t0 + u;
-        bool absorb = (t >= w) && (t < Tn);
-        float au = Ad[uu];
-#pragma unroll
-        for (int mb = 0; mb < NB; ++mb) {
-          typename Vec<T>::v4 al = ld4<T>(&sm.sA[u * PM + 16 * mb + 4 * g]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float a = to_f<T>(al[r]);
-            float be = absorb ? 1.f - a : 0.f;
-            dg[mb][r] += au * Dp[mb][r] * be;
-            Dp[mb][r] *= absorb ? a : 1.f;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lg[mb][r] += dg[mb][r];
-  }
+  slot_read<T, D, MP, C>(sm.sSK, sm.sK, sm.sBt, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
   // softmax partial over the m slots (log2 domain)
   const float sl2 = scale * NHA_LOG2E;
   float mx = -INFINITY;
@@ -449,92 +318,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
       zs += p[mb][r];
     }
   zs = sum_over_g(zs);
-
-  // values: O^T[d][t] = S^V^T . (p 2^{G_t})^T + sum_J nu_J^T . Atil_J^T
   floatx4 accO[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
-  {
-    float ph[NB][4];
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ph[mb][r] = p[mb][r] * fast_exp2(sm.sG[urow * MP + 16 * mb + 4 * g + r]);
-#pragma unroll
-    for (int s = 0; s < NB / 2; ++s) {
-      float f[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) f[r] = ph[2 * s][r], f[4 + r] = ph[2 * s + 1][r];
-      typename Vec<T>::v8 bfr = pack8<T>(f);
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        accO[db] = mma32(accO[db],
-                         ld4x2<T>(&sm.sSVt[(16 * db + cc) * PM + 32 * s + 4 * g],
-                                  &sm.sSVt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]),
-                         bfr);
-    }
-  }
-#pragma unroll
-  for (int J = 0; J < NW; ++J) {
-    if (J < I) {
-      // Atil_J^T[u][t] = sum_i B^(J)[u][i] p_t[i] 2^{G_t - E_J}
-      floatx4 at = zero4();
-#pragma unroll
-      for (int s = 0; s < NB / 2; ++s) {
-        float f[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
-          f[r] = p[2 * s][r] * fast_exp2(sm.sG[urow * MP + i0] - sm.sG[(16 * J + 15) * MP + i0]);
-          f[4 + r] = p[2 * s + 1][r] * fast_exp2(sm.sG[urow * MP + i1] - sm.sG[(16 * J + 15) * MP + i1]);
-        }
-        at = mma32(at,
-                   ld4x2<T>(&sm.sB[(16 * J + cc) * PM + 32 * s + 4 * g],
-                            &sm.sB[(16 * J + cc) * PM + 32 * s + 16 + 4 * g]),
-                   pack8<T>(f));
-      }
-      typename Vec<T>::v4 bfr = pack4<T>(at);
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        accO[db] = mma16(accO[db], ld4<T>(&sm.sVt[(16 * db + cc) * PC + 16 * J + 4 * g]), bfr);
-    }
-  }
-  // diagonal block of the value side: Atil[t][u] = sum_i p_t[i] Dprod b_u[i]
-  {
-    float Dp[NB][4];
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Dp[mb][r] = 1.f;
-    float mine[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int uu = 15; uu >= 0; --uu) {
-      float cu = 0.f;
-      int u = r0 + uu, t = t0 + u;
-      bool absorb = (t >= w) && (t < Tn);
-      if (uu <= cc) {
-#pragma unroll
-        for (int mb = 0; mb < NB; ++mb) {
-          typename Vec<T>::v4 al = ld4<T>(&sm.sA[u * PM + 16 * mb + 4 * g]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float a = to_f<T>(al[r]);
-            float be = absorb ? 1.f - a : 0.f;
-            cu += p[mb][r] * Dp[mb][r] * be;
-            Dp[mb][r] *= absorb ? a : 1.f;
-          }
-        }
-      }
-      cu = sum_over_g(cu);
-      if ((uu >> 2) == g) mine[uu & 3] = cu;
-    }
-    typename Vec<T>::v4 bfr;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bfr[r] = to_t<T>(mine[r]);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      accO[db] = mma16(accO[db], ld4<T>(&sm.sVt[(16 * db + cc) * PC + r0 + 4 * g]), bfr);
-  }
+  slot_mix<T, D, MP, C, PC>(sm.sSVt, sm.sVt, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO);
   // normalised partial + its lse
   if (qvalid) {
     float inv = 1.f / zs;
@@ -706,71 +493,105 @@ __global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ v
 
 // ---------------------------------------------------------------- host launcher
 template <typename T, int D, int MP, int C>
+static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const T* k, const T* v, const T* alpha,
+                          const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+  const int units = s.B * s.Hkv;
+  if (s.rope && s.win) {
+    long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
+    long thq = nq * (s.d / 16), thk = nk * (s.d / 16);
+    mk.mark(st);
+    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thq + 255) / 256)), dim3(256), 0, st, q, (T*)pp.qrot, nq, s.H,
+                       s.T, s.d, th);
+    mk.mark(st);
+    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thk + 255) / 256)), dim3(256), 0, st, k, (T*)pp.krot, nk,
+                       s.Hkv, s.T, s.d, th);
+  }
+  mk.mark(st);
+  hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend, s.T,
+                     s.Hkv, s.m, s.w, s.NC);
+  mk.mark(st);
+  hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
+                     (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
+}
+
+template <typename T, int D, int MP, int C>
 static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st) {
   if constexpr (sizeof(SlotFwdSmem<T, D, MP, C>) > kMaxLds) {
     return hipErrorInvalidConfiguration;
   } else {
-  FwdWs L = fwd_ws_layout(s);
-  const T* q = (const T*)p.q;
-  const T* k = (const T*)p.k;
-  const T* v = (const T*)p.v;
-  const T* alpha = (const T*)p.alpha;
-  T* sst = (T*)(p.ws + L.sst);
-  T* wt = (T*)(p.ws + L.wt);
-  float* aend = (float*)(p.ws + L.aend);
-  T* ol = (T*)(p.ws + L.ol);
-  float* lsel = (float*)(p.ws + L.lsel);
-  const int units = s.B * s.Hkv;
-  Marks mk;
-  mk.ev = p.events;
-  const T* qr = q;
-  const T* kr = k;
-  if (s.rope && s.win) {
-    T* qrw = (T*)(p.ws + L.qrot);
-    T* krw = (T*)(p.ws + L.krot);
-    long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
-    long thq = nq * (s.d / 16), thk = nk * (s.d / 16);
+    FwdWs L = fwd_ws_layout(s);
+    const T* q = (const T*)p.q;
+    const T* k = (const T*)p.k;
+    const T* v = (const T*)p.v;
+    const T* alpha = (const T*)p.alpha;
+    T* ol = (T*)(p.ws + L.ol);
+    float* lsel = (float*)(p.ws + L.lsel);
+    const int units = s.B * s.Hkv;
+    Marks mk;
+    mk.ev = p.events;
+    StateLayout SL{};
+    ProloguePtrs pp{p.ws + L.sst, p.ws + L.wt, (float*)(p.ws + L.aend), nullptr, nullptr, nullptr, nullptr};
+    if (s.rope && s.win) {
+      pp.qrot = p.ws + L.qrot;
+      pp.krot = p.ws + L.krot;
+    }
+    if (p.state_out) {
+      SL = state_layout(s);
+      pp.skout = (float*)((char*)p.state_out + SL.sk);
+      pp.svout = (float*)((char*)p.state_out + SL.sv);
+    }
+    prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st);
+    const T* qr = pp.qrot ? (const T*)pp.qrot : q;
+    const T* kr = pp.krot ? (const T*)pp.krot : k;
     mk.mark(st);
-    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thq + 255) / 256)), dim3(256), 0, st, q, qrw, nq, s.H, s.T, s.d, th);
+    hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
+                       (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
     mk.mark(st);
-    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thk + 255) / 256)), dim3(256), 0, st, k, krw, nk, s.Hkv, s.T, s.d, th);
-    qr = qrw;
-    kr = krw;
+    hipLaunchKernelGGL((k_win_fwd<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, ol, lsel, (T*)p.o,
+                       p.lse, s.T, s.H, s.Hkv, s.w, s.scale);
+    if (p.state_out) {
+      char* base = (char*)p.state_out;
+      mk.mark(st);
+      if (s.w > 0)
+        hipLaunchKernelGGL(k_export_state<T>, dim3(32, units), dim3(256), 0, st, k, v, (T*)(base + SL.rk),
+                           (T*)(base + SL.rv), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w);
+      else
+        hipLaunchKernelGGL(k_export_state<T>, dim3(1, units), dim3(64), 0, st, k, v, (T*)nullptr, (T*)nullptr,
+                           (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0);
+    }
+    mk.mark(st);
+    return hipGetLastError();
   }
-  mk.mark(st);
-  hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, wt, aend, s.T, s.Hkv,
-                     s.m, s.w, s.NC);
-  float* skout = nullptr;
-  float* svout = nullptr;
-  StateLayout SL{};
-  if (p.state_out) {
-    SL = state_layout(s);
-    skout = (float*)((char*)p.state_out + SL.sk);
-    svout = (float*)((char*)p.state_out + SL.sv);
+}
+
+template <typename T, int MP, int C>
+static void prologue_d(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
+                       const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+  switch (s.d) {
+    case 32: return prologue_impl<T, 32, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st);
+    case 64: return prologue_impl<T, 64, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st);
+    case 128: return prologue_impl<T, 128, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st);
   }
-  mk.mark(st);
-  hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, wt, aend, sst, skout,
-                     svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
-  mk.mark(st);
-  hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
-                     sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
-  mk.mark(st);
-  hipLaunchKernelGGL((k_win_fwd<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, ol, lsel, (T*)p.o,
-                     p.lse, s.T, s.H, s.Hkv, s.w, s.scale);
-  if (p.state_out && s.w > 0) {
-    char* base = (char*)p.state_out;
-    mk.mark(st);
-    hipLaunchKernelGGL(k_export_state<T>, dim3(32, units), dim3(256), 0, st, k, v, (T*)(base + SL.rk),
-                       (T*)(base + SL.rv), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w);
-  } else if (p.state_out) {
-    char* base = (char*)p.state_out;
-    mk.mark(st);
-    hipLaunchKernelGGL(k_export_state<T>, dim3(1, units), dim3(64), 0, st, k, v, (T*)nullptr, (T*)nullptr,
-                       (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0);
+}
+template <typename T, int MP>
+static void prologue_c(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
+                       const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+  switch (s.C) {
+    case 16: return prologue_d<T, MP, 16>(s, th, q, k, v, alpha, pp, mk, st);
+    case 32: return prologue_d<T, MP, 32>(s, th, q, k, v, alpha, pp, mk, st);
+    case 64: return prologue_d<T, MP, 64>(s, th, q, k, v, alpha, pp, mk, st);
   }
-  mk.mark(st);
+}
+hipError_t launch_prologue(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
+                           const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+  if (s.dtype == NHA_DTYPE_BF16) {
+    if (s.mp == 32) prologue_c<bf16, 32>(s, th, q, k, v, alpha, pp, mk, st);
+    else prologue_c<bf16, 64>(s, th, q, k, v, alpha, pp, mk, st);
+  } else {
+    if (s.mp == 32) prologue_c<float, 32>(s, th, q, k, v, alpha, pp, mk, st);
+    else prologue_c<float, 64>(s, th, q, k, v, alpha, pp, mk, st);
+  }
   return hipGetLastError();
-  }
 }
 
 template <typename T, int MP, int C>

@@ -101,6 +101,21 @@ int fwd_stages(const Shape& s, bool with_state, const char** names, int max);
 int bwd_stages(const Shape& s, const char** names, int max);
 
 // ---------------------------------------------------------------- launchers
+// Shared first stages of the forward and the backward: RoPE of q and k (when
+// enabled and w > 0), per-chunk gate products, and the scan that writes the
+// slot state at every chunk start (and optionally the final fp32 state).
+struct ProloguePtrs {
+  void* sst;
+  void* wt;
+  float* aend;
+  void* qrot;  // nullable when RoPE is off or w == 0
+  void* krot;
+  float* skout;  // nullable
+  float* svout;
+};
+hipError_t launch_prologue(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
+                           const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st);
+
 // Each returns hipSuccess or the launch error.  All launches go on `st`.
 struct FwdPtrs {
   const void *q, *k, *v, *alpha;
@@ -130,7 +145,8 @@ struct BwdPtrs {
 };
 hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st);
 
-// LDS bytes the slot kernels need (0 = shape unsupported).
+// LDS bytes the largest forward / backward kernel needs for this shape.
 size_t slot_fwd_lds_bytes(const Shape& s);
+size_t slot_bwd_lds_bytes(const Shape& s);
 
 }  // namespace nha

@@ -1,0 +1,239 @@
+// nha_slot.h -- device building blocks of the slot (long-term memory) branch,
+// shared by the forward and backward kernels.
+//
+// Per (batch, KV head), with a_t = alpha_t and b_t = 1 - alpha_t for t >= w
+// (a_t = 1, b_t = 0 before: nothing is absorbed yet) and key_t the absorbed
+// row (k_{t-w}, v_{t-w}: the token shift), the slot state obeys
+//     S_t = a_t (.) S_{t-1} + b_t (x) key_t
+// -- the K^long_t recurrence of the Paper-Notes page "Native Hybrid Attention
+// for Efficient Sequence Modeling", section 关键设计 > 层内混合, with the token
+// shift described there.  Inside a chunk starting at t0, with
+// G_u = sum_{j=t0..u} log2 a_j (per slot),
+//     S_t = 2^{G_t} S_{t0-1} + sum_{u=t0..t} 2^{G_t - G_u} b_u (x) key_u ,
+// the cumulative / reverse gate products of the chunkwise form (ibid.,
+// Chunkwise 并行计算).  Every factor used is 2^{G_later - G_earlier} <= 1:
+// pairs in different 16-row blocks go through a block-boundary reference,
+// pairs inside one block through exact running products of a.
+#pragma once
+#include "nha_common.h"
+
+namespace nha {
+
+// In-place inclusive cumsum over the C rows of an LDS tile g[u * P + i] (fp32)
+// for columns i < MP, by NT threads: each thread scans a run of rows of one
+// column, then adds the totals of the runs before it.
+template <int C, int MP, int P, int NT>
+__device__ __forceinline__ void lds_col_cumsum(float* g, int tid) {
+  constexpr int PARTS = (NT / MP) < C ? (NT / MP) : C;
+  constexpr int RP = C / PARTS;
+  const int i = tid % MP, part = tid / MP;
+  const bool act = part < PARTS;
+  if (act) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = part * RP; u < (part + 1) * RP; ++u) {
+      acc += g[u * P + i];
+      g[u * P + i] = acc;
+    }
+  }
+  __syncthreads();
+  float off = 0.f;
+  if (act)
+    for (int pp = 0; pp < part; ++pp) off += g[((pp + 1) * RP - 1) * P + i];
+  __syncthreads();
+  if (act && part > 0) {
+#pragma unroll
+    for (int u = part * RP; u < (part + 1) * RP; ++u) g[u * P + i] += off;
+  }
+  __syncthreads();
+}
+
+// Stage a chunk's gates into LDS: la[u][i] = log2 a_u (0 where nothing is
+// absorbed: t < w, t >= T or padded slot), al[u][i] = raw alpha (1 outside).
+template <typename T, int C, int MP, int PG, int PA, int NT>
+__device__ __forceinline__ void stage_gates(const T* __restrict__ alpha, float* la, T* al, int b, int hg, int t0,
+                                            int Tn, int Hkv, int m, int w, int tid) {
+  for (int e = tid; e < C * MP; e += NT) {
+    int u = e / MP, i = e % MP, t = t0 + u;
+    T av = to_t<T>(1.f);
+    if (i < m && t < Tn) av = alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i];
+    float l2 = 0.f;
+    if (i < m && t < Tn && t >= w) l2 = fmaxf(__log2f(to_f<T>(av)), NHA_LOG2A_MIN);
+    la[u * PG + i] = l2;
+    al[u * PA + i] = av;
+  }
+}
+
+// ---------------------------------------------------------------- intra-chunk slot products
+// The two products every slot kernel needs, for one wave owning chunk rows
+// r0 .. r0+15 (I = r0 / 16; lane (g, cc) handles row r0 + cc and slots
+// i = 16 mb + 4 g + r).  LDS operands of the chunk:
+//   sG[u*MP + i]  log2 cumsum of the effective decay (fp32)
+//   sA[u*PM + i]  raw gate (a_u = alpha, b_u = 1 - alpha when t0+u >= w)
+//   sB[u*PM + i]  2^{E_J - G_u} b_u,  sBt[i*PC + u] the same (E_J = G at the
+//                 last row of u's 16-row block)
+// and S_t = 2^{G_t} S0 + sum_{u<=t} 2^{G_t - G_u} b_u (x) key_u.
+
+// out[mb][r] = <x_t, S_t[i]> for the wave's rows.  sS: S0 [i][d] (pitch PD);
+// sKey: key rows [u][d] (pitch PD); xf: the rows' vectors as B fragments.
+template <typename T, int D, int MP, int C>
+__device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* sBt, const float* sG, const T* sA,
+                                          const typename Vec<T>::v8* xf, int I, int t0, int w, int Tn,
+                                          float (&out)[MP / 16][4]) {
+  constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
+  const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
+  floatx4 accA[NW];
+#pragma unroll
+  for (int ub = 0; ub < NW; ++ub) {
+    accA[ub] = zero4();
+    if (ub <= I) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        accA[ub] = mma32(accA[ub], ld8<T>(&sKey[(16 * ub + cc) * PD + 32 * ks + 8 * g]), xf[ks]);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    floatx4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) acc = mma32(acc, ld8<T>(&sS[(16 * mb + cc) * PD + 32 * ks + 8 * g]), xf[ks]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[mb][r] = fast_exp2(sG[urow * MP + 16 * mb + 4 * g + r]) * acc[r];
+  }
+  // earlier 16-row blocks J < I of the chunk
+#pragma unroll
+  for (int J = 0; J < NW; ++J) {
+    if (J < I) {
+      typename Vec<T>::v4 bfr = pack4<T>(accA[J]);
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        floatx4 x = mma16(zero4(), ld4<T>(&sBt[(16 * mb + cc) * PC + 16 * J + 4 * g]), bfr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int i = 16 * mb + 4 * g + r;
+          out[mb][r] += fast_exp2(sG[urow * MP + i] - sG[(16 * J + 15) * MP + i]) * x[r];
+        }
+      }
+    }
+  }
+  // same block: exact running products
+  floatx4 aI = accA[0];
+#pragma unroll
+  for (int ub = 1; ub < NW; ++ub)
+    if (ub == I) aI = accA[ub];
+  float Ad[16];
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ad[4 * gg + r] = __shfl(aI[r], cc + 16 * gg, 64);
+  float Dp[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Dp[mb][r] = 1.f;
+#pragma unroll
+  for (int uu = 15; uu >= 0; --uu) {
+    if (uu <= cc) {
+      int u = r0 + uu, t = t0 + u;
+      bool absorb = (t >= w) && (t < Tn);
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        typename Vec<T>::v4 al = ld4<T>(&sA[u * PM + 16 * mb + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a = to_f<T>(al[r]);
+          float be = absorb ? 1.f - a : 0.f;
+          out[mb][r] += Ad[uu] * Dp[mb][r] * be;
+          Dp[mb][r] *= absorb ? a : 1.f;
+        }
+      }
+    }
+  }
+}
+
+// accO (O^T[d][t] in D layout) += sum_i wgt_t[i] S_t[i].  sSt: S0 transposed
+// [d][i] (pitch PM); sKeyT: key rows transposed [d][u] (pitch PCT).
+template <typename T, int D, int MP, int C, int PCT>
+__device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* sB, const float* sG, const T* sA,
+                                         const float (&wgt)[MP / 16][4], int I, int t0, int w, int Tn,
+                                         floatx4 (&accO)[D / 16]) {
+  constexpr int NW = C / 16, NB = MP / 16, PM = pitch_of(MP);
+  const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
+  {
+    float ph[NB][4];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ph[mb][r] = wgt[mb][r] * fast_exp2(sG[urow * MP + 16 * mb + 4 * g + r]);
+#pragma unroll
+    for (int s = 0; s < NB / 2; ++s) {
+      typename Vec<T>::v8 bfr = pack8<T>(floatx4{ph[2 * s][0], ph[2 * s][1], ph[2 * s][2], ph[2 * s][3]},
+                                         floatx4{ph[2 * s + 1][0], ph[2 * s + 1][1], ph[2 * s + 1][2],
+                                                 ph[2 * s + 1][3]});
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        accO[db] = mma32(accO[db],
+                         ld4x2<T>(&sSt[(16 * db + cc) * PM + 32 * s + 4 * g],
+                                  &sSt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]),
+                         bfr);
+    }
+  }
+#pragma unroll
+  for (int J = 0; J < NW; ++J) {
+    if (J < I) {
+      floatx4 at = zero4();
+#pragma unroll
+      for (int s = 0; s < NB / 2; ++s) {
+        float f[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
+          f[r] = wgt[2 * s][r] * fast_exp2(sG[urow * MP + i0] - sG[(16 * J + 15) * MP + i0]);
+          f[4 + r] = wgt[2 * s + 1][r] * fast_exp2(sG[urow * MP + i1] - sG[(16 * J + 15) * MP + i1]);
+        }
+        at = mma32(at,
+                   ld4x2<T>(&sB[(16 * J + cc) * PM + 32 * s + 4 * g], &sB[(16 * J + cc) * PM + 32 * s + 16 + 4 * g]),
+                   pack8<T>(f));
+      }
+      typename Vec<T>::v4 bfr = pack4<T>(at);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        accO[db] = mma16(accO[db], ld4<T>(&sKeyT[(16 * db + cc) * PCT + 16 * J + 4 * g]), bfr);
+    }
+  }
+  float Dp[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Dp[mb][r] = 1.f;
+  float mine[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int uu = 15; uu >= 0; --uu) {
+    float cu = 0.f;
+    int u = r0 + uu, t = t0 + u;
+    bool absorb = (t >= w) && (t < Tn);
+    if (uu <= cc) {
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        typename Vec<T>::v4 al = ld4<T>(&sA[u * PM + 16 * mb + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a = to_f<T>(al[r]);
+          float be = absorb ? 1.f - a : 0.f;
+          cu += wgt[mb][r] * Dp[mb][r] * be;
+          Dp[mb][r] *= absorb ? a : 1.f;
+        }
+      }
+    }
+    cu = sum_over_g(cu);
+    if ((uu >> 2) == g) mine[uu & 3] = cu;
+  }
+  typename Vec<T>::v4 bfr;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bfr[r] = to_t<T>(mine[r]);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    accO[db] = mma16(accO[db], ld4<T>(&sKeyT[(16 * db + cc) * PCT + r0 + 4 * g]), bfr);
+}
+
+}  // namespace nha
