@@ -80,22 +80,40 @@ def bytes_fwd(wl, e):
 
 
 def stage_work(stage, wl, w, e):
-    """(bound, algorithmic work per launch, unit) of a stage, for the roofline."""
-    if stage in ("win_fwd",):
-        return "mfma", flops_window(wl.B, wl.H, wl.T, wl.d, w), "flop"
-    if stage in ("win_bwd_dq",):
-        return "mfma", 1.5 * flops_window(wl.B, wl.H, wl.T, wl.d, w), "flop"
-    if stage in ("win_bwd_dkdv",):
-        return "mfma", 2.0 * flops_window(wl.B, wl.H, wl.T, wl.d, w), "flop"
-    if stage == "slot_fwd":
-        return "mfma", flops_slot(wl.B, wl.H, wl.T, wl.d, wl.m, w, wl.C), "flop"
-    if stage == "state_scan":
-        return "mfma", flops_state(wl.B, wl.Hkv, wl.T, wl.d, wl.m, w), "flop"
-    if stage == "rope_q":
-        return "hbm", 2.0 * wl.B * wl.T * wl.H * wl.d * e, "byte"
-    if stage == "rope_k":
-        return "hbm", 2.0 * wl.B * wl.T * wl.Hkv * wl.d * e, "byte"
-    return None, None, None
+    """(bound, algorithmic work per launch, unit) of every kernel launch.
+
+    Window kernels: flops per (query, in-window key) pair -- forward 4d (QK^T,
+    PV), dq pass 6d (QK^T, dO V^T, dS K), dk/dv pass 8d (QK^T, dO V^T, P^T dO,
+    dS^T Q).  Slot kernels, per query t >= w with c(t) earlier absorbed rows of
+    its chunk: one read (2md + (2d+2m)c) and one mix (same) in the forward;
+    two reads and one mix in pass A of the backward; two reverse reads and two
+    reverse mixes in pass B.  Scans: 4md per absorbed token per KV head
+    (forward) and per token per query head (adjoint).  Memory-bound helpers:
+    the bytes they must move."""
+    B, H, Hkv, T, d, m, C = wl.B, wl.H, wl.Hkv, wl.T, wl.d, wl.m, wl.C
+    fw = flops_window(B, H, T, d, w)
+    fs = flops_slot(B, H, T, d, m, w, C)
+    table = {
+        "win_fwd": ("mfma", fw),
+        "win_bwd_dq": ("mfma", 1.5 * fw),
+        "win_bwd_dkdv": ("mfma", 2.0 * fw),
+        "slot_fwd": ("mfma", fs),
+        "slot_bwd_a": ("mfma", 1.5 * fs),
+        "slot_bwd_b": ("mfma", 2.0 * fs),
+        "state_scan": ("mfma", flops_state(B, Hkv, T, d, m, w)),
+        "adj_scan": ("mfma", 4.0 * m * d * B * H * T),
+        "rope_q": ("hbm", 2.0 * B * T * H * d * e),
+        "rope_k": ("hbm", 2.0 * B * T * Hkv * d * e),
+        "chunk_gates": ("hbm", 2.0 * B * T * Hkv * m * e),
+        "bwd_prep": ("hbm", B * T * H * (2.0 * d * e + 4)),
+        "dalpha_fix": ("hbm", B * T * Hkv * m * (e + 8.0)),
+        "dalpha_carry": ("hbm", 8.0 * B * Hkv * ((T + C - 1) // C) * m),
+        "export_state": ("hbm", 4.0 * B * Hkv * min(w, T) * d * e),
+    }
+    if stage not in table:
+        return None, None, None
+    bound, work = table[stage]
+    return bound, work, "flop" if bound == "mfma" else "byte"
 
 
 # ---------------------------------------------------------------- CPU baseline
