@@ -128,6 +128,7 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
                                          const float (&bwI)[MP / 16][4], const float (&bt)[MP / 16][4], int I,
                                          int t0, int w, int Tn, floatx4 (&accO)[D / 16], float (&F)[MP / 16][4]) {
   constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
+  constexpr int PG = SlotPitch<MP>::PG;
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc, rl = r0 + 15;
   floatx4 accA[NW];  // A[u][t] = vec_u . key_t, D layout [u = 16J + 4g + r][t = cc]
 #pragma unroll
@@ -139,10 +140,11 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
         accA[J] = mma32(accA[J], ld8<T>(&sVec[(16 * J + cc) * PD + 32 * ks + 8 * g]), keyf[ks]);
     }
   }
-  // later blocks J > I
+  // later blocks J > I, and (when factorizable) the block itself with u >= t
+  const bool fast = block_factorizable<MP>(sG, r0);
 #pragma unroll
   for (int J = 0; J < NW; ++J) {
-    if (J > I) {
+    if (J > I || (J == I && fast)) {
       const int uA = 16 * J + cc;  // A-fragment row of this lane
       floatx4 mt = zero4();        // M^T[u][t] = sum_i Y[u][i] bwI[t][i]
 #pragma unroll
@@ -151,19 +153,28 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
-          f[r] = sW[uA * MP + i0] * fast_exp2(sG[uA * MP + i0] - sG[rl * MP + i0]);
-          f[4 + r] = sW[uA * MP + i1] * fast_exp2(sG[uA * MP + i1] - sG[rl * MP + i1]);
+          f[r] = sW[uA * PG + i0] * fast_exp2(sG[uA * PG + i0] - sG[rl * PG + i0]);
+          f[4 + r] = sW[uA * PG + i1] * fast_exp2(sG[uA * PG + i1] - sG[rl * PG + i1]);
         }
         typename Vec<T>::v8 bfr = pack8<T>(floatx4{bwI[2 * s][0], bwI[2 * s][1], bwI[2 * s][2], bwI[2 * s][3]},
                                            floatx4{bwI[2 * s + 1][0], bwI[2 * s + 1][1], bwI[2 * s + 1][2],
                                                    bwI[2 * s + 1][3]});
         mt = mma32(mt, pack8<T>(f), bfr);
       }
+      if (J == I) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt[r] = (4 * g + r >= cc) ? mt[r] : 0.f;  // u >= t
+      }
       typename Vec<T>::v4 mfr = pack4<T>(mt);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
         accO[db] = mma16(accO[db], ld4<T>(&sVecT[(16 * db + cc) * PC + 16 * J + 4 * g]), mfr);
-      typename Vec<T>::v4 afr = pack4<T>(accA[J]);
+      floatx4 av = accA[J];
+      if (J == I) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = (4 * g + r >= cc) ? av[r] : 0.f;  // u >= t
+      }
+      typename Vec<T>::v4 afr = pack4<T>(av);
 #pragma unroll
       for (int mb = 0; mb < NB; ++mb) {
         const int iA = 16 * mb + cc;
@@ -171,17 +182,18 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           int u = 16 * J + 4 * g + r;
-          y[r] = sW[u * MP + iA] * fast_exp2(sG[u * MP + iA] - sG[rl * MP + iA]);
+          y[r] = sW[u * PG + iA] * fast_exp2(sG[u * PG + iA] - sG[rl * PG + iA]);
         }
         floatx4 x = mma16(zero4(), pack4<T>(y), afr);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           int i = 16 * mb + 4 * g + r;
-          F[mb][r] += fast_exp2(sG[rl * MP + i] - sG[urow * MP + i]) * x[r];
+          F[mb][r] += fast_exp2(sG[rl * PG + i] - sG[urow * PG + i]) * x[r];
         }
       }
     }
   }
+  if (fast) return;
   // same block: u >= t, exact running products D'_{t,u} = prod_{j=t+1..u} a_j
   floatx4 aI = accA[0];
 #pragma unroll
@@ -205,7 +217,9 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
       const int u = r0 + uu;
 #pragma unroll
       for (int mb = 0; mb < NB; ++mb) {
-        floatx4 w4 = *reinterpret_cast<const floatx4*>(&sW[u * MP + 16 * mb + 4 * g]);
+        floatx4 w4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w4[r] = sW[u * PG + 16 * mb + 4 * g + r];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           F[mb][r] += Dp[mb][r] * w4[r] * Ad[uu];
@@ -274,7 +288,7 @@ struct SlotBwdASmem {
   T sA[C * PM];
   T sB[C * PM];
   T sBt[MP * PC];
-  float sG[C * MP];
+  float sG[C * SlotPitch<MP>::PG];
 };
 
 // grid (NC, B*H), C/16 waves.
@@ -286,6 +300,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
     float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m, int w, int NC, float scale) {
   using S = SlotBwdASmem<T, D, MP, C>;
   constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
+  constexpr int PG = SlotPitch<MP>::PG;
   __shared__ S sm;
   const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, hg = h / (H / Hkv);
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
     tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
     tkt.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
     tv.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    stage_gates<T, C, MP, MP, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    stage_gates<T, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
     tsk.template store<PD>(sm.sSK, tid);
     tskt.template store<PM>(sm.sSKt, tid);
     tsv.template store<PD>(sm.sSV, tid);
@@ -312,11 +327,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
     tv.template store<PD>(sm.sV, tid);
   }
   __syncthreads();
-  lds_col_cumsum<C, MP, MP, NT>(sm.sG, tid);
+  lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
   for (int e = tid; e < C * MP; e += NT) {
     int u = e / MP, i = e % MP, t = t0 + u;
     float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sm.sA[u * PM + i]) : 0.f;
-    T tv = to_t<T>(fast_exp2(sm.sG[(u | 15) * MP + i] - sm.sG[u * MP + i]) * be);
+    T tv = to_t<T>(fast_exp2(sm.sG[(u | 15) * PG + i] - sm.sG[u * PG + i]) * be);
     sm.sB[u * PM + i] = tv;
     sm.sBt[i * PC + u] = tv;
   }
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int i = 16 * mb + 4 * g + r;
-      float e = fast_exp2(sm.sG[urow * MP + i]);
+      float e = fast_exp2(sm.sG[urow * PG + i]);
       wk[(size_t)i * C + urow] = to_t<T>(e * scale * dl[mb][r]);
       wv[(size_t)i * C + urow] = to_t<T>(e * p[mb][r]);
     }
@@ -397,7 +412,9 @@ __global__ __launch_bounds__(64) void k_adj_scan(const T* __restrict__ q, const 
   __shared__ T sQt[16 * PC];
   __shared__ T sOt[16 * PC];
   const int l = threadIdx.x, g = l >> 4, cc = l & 15;
-  const int j0 = blockIdx.x * 16, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  // the d/16 column blocks of one unit share the adjoint weights: one XCD
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int j0 = (L % gridDim.x) * 16, unit = L / gridDim.x, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
   floatx4 LK[NB], LV[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) LK[nb] = LV[nb] = zero4();
@@ -473,8 +490,8 @@ struct SlotBwdBSmem {
   T sVec[C * PD];    // q or dO rows of one head [u][d]
   T sVecT[D * PC];   // same, transposed
   T sA[C * PM];
-  float sG[C * MP];
-  float sW[C * MP];  // s dl or p of one head [u][i]; later the (A - bF) tile
+  float sG[C * SlotPitch<MP>::PG];
+  float sW[C * SlotPitch<MP>::PG];  // s dl or p of one head [u][i]; later the (A - bF) tile
 };
 
 // grid (NC, B*Hkv), C/16 waves; all query heads of the KV group.
@@ -487,13 +504,14 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
     int w, int NC) {
   using S = SlotBwdBSmem<T, D, MP, C>;
   constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
+  constexpr int PG = SlotPitch<MP>::PG;
   __shared__ S sm;
   const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
   const int c = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv, t0 = c * C;
   const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
-  stage_gates<T, C, MP, MP, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+  stage_gates<T, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
   __syncthreads();
-  lds_col_cumsum<C, MP, MP, NT>(sm.sG, tid);
+  lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
   const bool absorb = (tq >= w) && (tq < Tn);
   float bt[NB][4], bwI[NB][4], bwE[NB][4], F[NB][4];
 #pragma unroll
@@ -502,10 +520,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
     for (int r = 0; r < 4; ++r) {
       int i = 16 * mb + 4 * g + r;
       float be = (absorb && i < m) ? 1.f - to_f<T>(sm.sA[urow * PM + i]) : 0.f;
-      float Gt = sm.sG[urow * MP + i];
+      float Gt = sm.sG[urow * PG + i];
       bt[mb][r] = be;
-      bwI[mb][r] = be * fast_exp2(sm.sG[(r0 + 15) * MP + i] - Gt);
-      bwE[mb][r] = be * fast_exp2(sm.sG[(C - 1) * MP + i] - Gt);
+      bwI[mb][r] = be * fast_exp2(sm.sG[(r0 + 15) * PG + i] - Gt);
+      bwE[mb][r] = be * fast_exp2(sm.sG[(C - 1) * PG + i] - Gt);
       F[mb][r] = 0.f;
     }
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
@@ -539,7 +557,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         int i = 16 * mb + 4 * g + r;
-        F[mb][r] += fast_exp2(sm.sG[(C - 1) * MP + i] - sm.sG[urow * MP + i]) * x[r];
+        F[mb][r] += fast_exp2(sm.sG[(C - 1) * PG + i] - sm.sG[urow * PG + i]) * x[r];
       }
     }
 #pragma unroll
@@ -564,8 +582,12 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
         tv.load(vb, (size_t)H * D, 0, Tn - t0, tid);
         tvt.load(vb, (size_t)H * D, 0, Tn - t0, tid);
         const float* wsrc = (side ? pp : sdl) + ((size_t)bh * NC * C + t0) * MP;
-        for (int e = tid * 4; e < C * MP; e += NT * 4)
-          *reinterpret_cast<floatx4*>(&sm.sW[e]) = *reinterpret_cast<const floatx4*>(wsrc + e);
+        for (int e = tid * 4; e < C * MP; e += NT * 4) {
+          floatx4 x = *reinterpret_cast<const floatx4*>(wsrc + e);
+          int u = e / MP, i = e % MP;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.sW[u * PG + i + r] = x[r];
+        }
         tv.template store<PD>(sm.sVec, tid);
         tvt.template store<PC>(sm.sVecT, tid);
       }
@@ -596,10 +618,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
   __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
-    *reinterpret_cast<floatx4*>(&sm.sW[urow * MP + 16 * mb + 4 * g]) =
-        floatx4{X[mb][0], X[mb][1], X[mb][2], X[mb][3]};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.sW[urow * PG + 16 * mb + 4 * g + r] = X[mb][r];
   __syncthreads();
-  lds_col_rcumsum<C, MP, MP, NT>(sm.sW, tid);
+  lds_col_rcumsum<C, MP, PG, NT>(sm.sW, tid);
   if (tid < MP) csum[((size_t)unit * NC + c) * MP + tid] = sm.sW[tid];
   if (tq < Tn) {
     float* da = dalpha + (((size_t)b * Tn + tq) * Hkv + hg) * m;
@@ -610,7 +632,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
         int i = 16 * mb + 4 * g + r;
         if (i < m) {
           float v = 0.f;
-          if (absorb) v = sm.sW[urow * MP + i] / to_f<T>(sm.sA[urow * PM + i]) - F[mb][r];
+          if (absorb) v = sm.sW[urow * PG + i] / to_f<T>(sm.sA[urow * PM + i]) - F[mb][r];
           da[i] = v;
         }
       }

@@ -151,7 +151,9 @@ __global__ __launch_bounds__(64) void k_state_scan(const T* __restrict__ kk, con
   __shared__ T sKt[16 * PC];
   __shared__ T sVt[16 * PC];
   const int l = threadIdx.x, g = l >> 4, cc = l & 15;
-  const int j0 = blockIdx.x * 16, unit = blockIdx.y;
+  // the d/16 column blocks of one unit share W^T: keep them on one XCD's L2
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int j0 = (L % gridDim.x) * 16, unit = L / gridDim.x;
   const int b = unit / Hkv, hg = unit % Hkv;
   floatx4 SK[NB], SV[NB];
 #pragma unroll
@@ -236,7 +238,7 @@ struct SlotFwdSmem {
   T sA[C * PM];     // alpha [u][i] (raw gate; a/b derived with the row's t >= w)
   T sB[C * PM];     // 2^{E_J - G_u} b_u  [u][i]
   T sBt[MP * PC];   // same, [i][u]
-  float sG[C * MP]; // log2 cumsum [u][i]
+  float sG[C * SlotPitch<MP>::PG]; // log2 cumsum [u][i]
 };
 
 template <typename T, int D, int MP, int C>
@@ -246,6 +248,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
     int w, int NC, float scale) {
   using S = SlotFwdSmem<T, D, MP, C>;
   constexpr int NW = C / 16, NT = NW * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
+  constexpr int PG = SlotPitch<MP>::PG;
   __shared__ S sm;
   const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, G = H / Hkv, hg = h / G;
@@ -266,20 +269,20 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
     PairTileT<T, D, NT, C> tnu;
     tkap.load(kb, (size_t)Hkv * D, w - t0, Tn - t0, tid);
     tnu.load(vb, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    stage_gates<T, C, MP, MP, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    stage_gates<T, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
     tsk.template store<PD>(sm.sSK, tid);
     tsv.template store<PM>(sm.sSVt, tid);
     tkap.template store<PD>(sm.sK, tid);
     tnu.template store<PC>(sm.sVt, tid);
   }
   __syncthreads();
-  lds_col_cumsum<C, MP, MP, NT>(sm.sG, tid);
+  lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
   // B^(J)[u][i] = 2^{E_J - G_u} b_u, E_J = G at the last row of u's block
   for (int e = tid; e < C * MP; e += NT) {
     int u = e / MP, i = e % MP, t = t0 + u;
     int last = (u | 15);
     float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sm.sA[u * PM + i]) : 0.f;
-    float val = fast_exp2(sm.sG[last * MP + i] - sm.sG[u * MP + i]) * be;
+    float val = fast_exp2(sm.sG[last * PG + i] - sm.sG[u * PG + i]) * be;
     T tv = to_t<T>(val);
     sm.sB[u * PM + i] = tv;
     sm.sBt[i * PC + u] = tv;

@@ -19,6 +19,14 @@
 
 namespace nha {
 
+// Row pitch (floats) of the fp32 per-chunk slot tiles (log2 cumsum G, source
+// weights): odd, so the 16 lanes that read one slot column from 16 different
+// rows hit 16 different LDS banks.
+template <int MP>
+struct SlotPitch {
+  static constexpr int PG = MP + 1;
+};
+
 // In-place inclusive cumsum over the C rows of an LDS tile g[u * P + i] (fp32)
 // for columns i < MP, by NT threads: each thread scans a run of rows of one
 // column, then adds the totals of the runs before it.
@@ -68,11 +76,35 @@ __device__ __forceinline__ void stage_gates(const T* __restrict__ alpha, float* 
 // The two products every slot kernel needs, for one wave owning chunk rows
 // r0 .. r0+15 (I = r0 / 16; lane (g, cc) handles row r0 + cc and slots
 // i = 16 mb + 4 g + r).  LDS operands of the chunk:
-//   sG[u*MP + i]  log2 cumsum of the effective decay (fp32)
+//   sG[u*PG + i]  log2 cumsum of the effective decay (fp32, PG = MP + 1)
 //   sA[u*PM + i]  raw gate (a_u = alpha, b_u = 1 - alpha when t0+u >= w)
 //   sB[u*PM + i]  2^{E_J - G_u} b_u,  sBt[i*PC + u] the same (E_J = G at the
 //                 last row of u's 16-row block)
 // and S_t = 2^{G_t} S0 + sum_{u<=t} 2^{G_t - G_u} b_u (x) key_u.
+
+// Same-block pairs can use the block-end reference too (one more masked MFMA
+// instead of per-element running products) when every slot's total decay over
+// the block is mild, >= 2^-16: the factors 2^{G_t - E_I}, 2^{E_I - G_u} are
+// then within [2^-16, 2^16] and the same-block terms, which dominate the slot
+// reads, keep bf16 operand precision relative to their own size.  Stronger
+// decays take the exact fp32 running products: there dalpha's
+// (A - b F) / alpha form cancels, and the same-block terms must stay fp32.
+// Uniform over the wave.
+template <int MP>
+__device__ __forceinline__ bool block_factorizable(const float* sG, int r0) {
+  constexpr int NB = MP / 16, PG = SlotPitch<MP>::PG;
+  const int g = (threadIdx.x & 63) >> 4;
+  bool ok = true;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int i = 16 * mb + 4 * g + r;
+      float before = r0 > 0 ? sG[(r0 - 1) * PG + i] : 0.f;
+      ok = ok && (sG[(r0 + 15) * PG + i] - before >= -16.f);
+    }
+  return __all(ok);
+}
 
 // out[mb][r] = <x_t, S_t[i]> for the wave's rows.  sS: S0 [i][d] (pitch PD);
 // sKey: key rows [u][d] (pitch PD); xf: the rows' vectors as B fragments.
@@ -81,6 +113,7 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
                                           const typename Vec<T>::v8* xf, int I, int t0, int w, int Tn,
                                           float (&out)[MP / 16][4]) {
   constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
+  constexpr int PG = SlotPitch<MP>::PG;
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
   floatx4 accA[NW];
 #pragma unroll
@@ -98,24 +131,32 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) acc = mma32(acc, ld8<T>(&sS[(16 * mb + cc) * PD + 32 * ks + 8 * g]), xf[ks]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) out[mb][r] = fast_exp2(sG[urow * MP + 16 * mb + 4 * g + r]) * acc[r];
+    for (int r = 0; r < 4; ++r) out[mb][r] = fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r]) * acc[r];
   }
-  // earlier 16-row blocks J < I of the chunk
+  // earlier 16-row blocks J < I of the chunk, and (when factorizable) the
+  // block itself with the causal mask u <= t
+  const bool fast = block_factorizable<MP>(sG, r0);
 #pragma unroll
   for (int J = 0; J < NW; ++J) {
-    if (J < I) {
-      typename Vec<T>::v4 bfr = pack4<T>(accA[J]);
+    if (J < I || (J == I && fast)) {
+      floatx4 av = accA[J];
+      if (J == I) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = (4 * g + r <= cc) ? av[r] : 0.f;
+      }
+      typename Vec<T>::v4 bfr = pack4<T>(av);
 #pragma unroll
       for (int mb = 0; mb < NB; ++mb) {
         floatx4 x = mma16(zero4(), ld4<T>(&sBt[(16 * mb + cc) * PC + 16 * J + 4 * g]), bfr);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           int i = 16 * mb + 4 * g + r;
-          out[mb][r] += fast_exp2(sG[urow * MP + i] - sG[(16 * J + 15) * MP + i]) * x[r];
+          out[mb][r] += fast_exp2(sG[urow * PG + i] - sG[(16 * J + 15) * PG + i]) * x[r];
         }
       }
     }
   }
+  if (fast) return;
   // same block: exact running products
   floatx4 aI = accA[0];
 #pragma unroll
@@ -157,14 +198,14 @@ template <typename T, int D, int MP, int C, int PCT>
 __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* sB, const float* sG, const T* sA,
                                          const float (&wgt)[MP / 16][4], int I, int t0, int w, int Tn,
                                          floatx4 (&accO)[D / 16]) {
-  constexpr int NW = C / 16, NB = MP / 16, PM = pitch_of(MP);
+  constexpr int NW = C / 16, NB = MP / 16, PM = pitch_of(MP), PG = SlotPitch<MP>::PG;
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
   {
     float ph[NB][4];
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ph[mb][r] = wgt[mb][r] * fast_exp2(sG[urow * MP + 16 * mb + 4 * g + r]);
+      for (int r = 0; r < 4; ++r) ph[mb][r] = wgt[mb][r] * fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r]);
 #pragma unroll
     for (int s = 0; s < NB / 2; ++s) {
       typename Vec<T>::v8 bfr = pack8<T>(floatx4{ph[2 * s][0], ph[2 * s][1], ph[2 * s][2], ph[2 * s][3]},
@@ -178,9 +219,10 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
                          bfr);
     }
   }
+  const bool fast = block_factorizable<MP>(sG, r0);
 #pragma unroll
   for (int J = 0; J < NW; ++J) {
-    if (J < I) {
+    if (J < I || (J == I && fast)) {
       floatx4 at = zero4();
 #pragma unroll
       for (int s = 0; s < NB / 2; ++s) {
@@ -188,12 +230,16 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
-          f[r] = wgt[2 * s][r] * fast_exp2(sG[urow * MP + i0] - sG[(16 * J + 15) * MP + i0]);
-          f[4 + r] = wgt[2 * s + 1][r] * fast_exp2(sG[urow * MP + i1] - sG[(16 * J + 15) * MP + i1]);
+          f[r] = wgt[2 * s][r] * fast_exp2(sG[urow * PG + i0] - sG[(16 * J + 15) * PG + i0]);
+          f[4 + r] = wgt[2 * s + 1][r] * fast_exp2(sG[urow * PG + i1] - sG[(16 * J + 15) * PG + i1]);
         }
         at = mma32(at,
                    ld4x2<T>(&sB[(16 * J + cc) * PM + 32 * s + 4 * g], &sB[(16 * J + cc) * PM + 32 * s + 16 + 4 * g]),
                    pack8<T>(f));
+      }
+      if (J == I) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) at[r] = (4 * g + r <= cc) ? at[r] : 0.f;  // u <= t
       }
       typename Vec<T>::v4 bfr = pack4<T>(at);
 #pragma unroll
@@ -201,6 +247,7 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
         accO[db] = mma16(accO[db], ld4<T>(&sKeyT[(16 * db + cc) * PCT + 16 * J + 4 * g]), bfr);
     }
   }
+  if (fast) return;
   float Dp[NB][4];
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)

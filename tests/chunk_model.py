@@ -67,6 +67,13 @@ def blocks(n):
     return [(s, min(s + SB, n)) for s in range(0, n, SB)]
 
 
+def factorizable(G, i0, i1):
+    """Same-block pairs use the block-end reference when every slot's total
+    decay over the block is >= 2^-16 (the kernels' test)."""
+    before = G[i0 - 1] if i0 > 0 else np.zeros_like(G[0])
+    return bool(np.all(G[i1 - 1] - before >= -16.0))
+
+
 # ---------------------------------------------------------------- intra-chunk products
 def fwd_read(X, S0, keys, G, a, b, Wts):
     """Forward-in-time read of the chunk's slot states by vectors X [n, d]:
@@ -77,12 +84,18 @@ def fwd_read(X, S0, keys, G, a, b, Wts):
     out = (X @ S0.T) * np.exp2(G)
     A = X @ keys.T  # [t, u]
     for (i0, i1) in blocks(n):
+        fast = factorizable(G, i0, i1)
         for (j0, j1) in blocks(n):
-            if j0 >= i0:
+            if j0 > i0 or (j0 == i0 and not fast):
                 break
             E = G[j1 - 1]
             Bj = np.exp2(E - G[j0:j1]) * b[j0:j1]  # <= 1
-            out[i0:i1] += np.exp2(G[i0:i1] - E) * (A[i0:i1, j0:j1] @ Bj)
+            Aij = A[i0:i1, j0:j1]
+            if j0 == i0:
+                Aij = np.tril(Aij)  # u <= t
+            out[i0:i1] += np.exp2(G[i0:i1] - E) * (Aij @ Bj)
+        if fast:
+            continue
         for t in range(i0, i1):
             Dp = np.ones_like(G[0])
             for u in range(t, i0 - 1, -1):
@@ -97,13 +110,18 @@ def fwd_mix(P, S0, keys, G, a, b):
     n = P.shape[0]
     out = (P * np.exp2(G)) @ S0
     for (i0, i1) in blocks(n):
+        fast = factorizable(G, i0, i1)
         for (j0, j1) in blocks(n):
-            if j0 >= i0:
+            if j0 > i0 or (j0 == i0 and not fast):
                 break
             E = G[j1 - 1]
             Bj = np.exp2(E - G[j0:j1]) * b[j0:j1]
             At = (P[i0:i1] * np.exp2(G[i0:i1] - E)) @ Bj.T  # [t, u]
+            if j0 == i0:
+                At = np.tril(At)
             out[i0:i1] += At @ keys[j0:j1]
+        if fast:
+            continue
         for t in range(i0, i1):
             Dp = np.ones_like(G[0])
             for u in range(t, i0 - 1, -1):
@@ -121,12 +139,17 @@ def rev_mix(Wb, L0, W, vecs, G, a):
     out = (Wb * np.exp2(G[n - 1] - G)) @ L0
     for (i0, i1) in blocks(n):
         F = G[i1 - 1]
+        fast = factorizable(G, i0, i1)
         for (j0, j1) in blocks(n):
-            if j0 <= i0:
+            if j0 < i0 or (j0 == i0 and not fast):
                 continue
-            Y = W[j0:j1] * np.exp2(G[j0:j1] - F)  # <= 1
+            Y = W[j0:j1] * np.exp2(G[j0:j1] - F)  # <= 1 (>= 1 on the block itself)
             M = (Wb[i0:i1] * np.exp2(F - G[i0:i1])) @ Y.T  # [t, u]
+            if j0 == i0:
+                M = np.triu(M)  # u >= t
             out[i0:i1] += M @ vecs[j0:j1]
+        if fast:
+            continue
         for t in range(i0, i1):
             Dp = np.ones_like(G[0])
             for u in range(t, i1):
@@ -144,11 +167,17 @@ def rev_read(Y, L0, W, vecs, G, a):
     A = vecs @ Y.T  # [u, t]
     for (i0, i1) in blocks(n):
         F = G[i1 - 1]
+        fast = factorizable(G, i0, i1)
         for (j0, j1) in blocks(n):
-            if j0 <= i0:
+            if j0 < i0 or (j0 == i0 and not fast):
                 continue
             Yw = W[j0:j1] * np.exp2(G[j0:j1] - F)
-            out[i0:i1] += np.exp2(F - G[i0:i1]) * (A[j0:j1, i0:i1].T @ Yw)
+            Aji = A[j0:j1, i0:i1].T  # [t, u]
+            if j0 == i0:
+                Aji = np.triu(Aji)  # u >= t
+            out[i0:i1] += np.exp2(F - G[i0:i1]) * (Aji @ Yw)
+        if fast:
+            continue
         for t in range(i0, i1):
             Dp = np.ones_like(G[0])
             for u in range(t, i1):

@@ -50,3 +50,20 @@ def test_hard_gates_stay_finite_and_exact():
     ref = oracle.bwd(q, k, v, a, dO, 5, rope_base=100.0)
     for x, r in zip(got, ref):
         np.testing.assert_allclose(x, r, atol=1e-9, rtol=1e-7)
+
+
+def test_exact_zero_gates_take_the_running_product_path():
+    """alpha = 0 in places (log2 floored at -80): a 16-row block whose total
+    decay leaves the 2^-100 range falls back to exact running products."""
+    q, k, v, a, dO = case(1, 80, 2, 1, 8, 4, seed=9)
+    a = a.copy()
+    a[:, 20:24] = 0.0
+    a[:, 50] = 1.0
+    for C in (16, 64):
+        o, l = model_fwd(q, k, v, a, 3, C, base=100.0)
+        o_ref, l_ref = oracle.fwd(q, k, v, a, 3, rope_base=100.0)
+        np.testing.assert_allclose(o, o_ref, atol=1e-12)
+        got = model_bwd(q, k, v, a, dO, 3, C, base=100.0)
+        ref = oracle.bwd(q, k, v, a, dO, 3, rope_base=100.0)
+        for x, r in zip(got[:3], ref[:3]):
+            np.testing.assert_allclose(x, r, atol=1e-10)
