@@ -336,32 +336,36 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
 }
 
 // ---------------------------------------------------------------- window branch
-// grid (ceil(T/64), B*H), 4 waves; wave W owns queries q0 + 16W .. +15.
-// Online softmax in log2 units, seeded with the slot partial as one key of
-// logit lse_L and value o_L / Z_L.  Key/value tiles of 64 rows are double
-// buffered in LDS; the global loads of tile i+2 are in flight while tile i is
-// computed.  Writes o and lse.
+// grid (ceil(T / (16 NWV)), B*H), NWV waves; wave W owns queries q0 + 16W ..
+// +15.  Online softmax in log2 units, seeded with the slot partial as one key
+// of logit lse_L and value o_L / Z_L.  One 64-row K / V tile is staged in LDS
+// at a time and serves all 16 NWV queries; the next tile's global loads are in
+// flight (in registers) while the current one is used.  A wave skips tiles
+// outside its rows' band.  Writes o and lse.
+constexpr int kWinWaves = 8;
+
 template <typename T, int D>
 struct WinFwdSmem {
   static constexpr int PD = pitch_of(D), PK = 64 + 4;
-  T k[2][64 * PD];  // RoPE'd keys [key][d]
-  T vt[2][D * PK];  // values, transposed [d][key]
+  T k[64 * PD];  // RoPE'd keys [key][d]
+  T vt[D * PK];  // values, transposed [d][key]
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void k_win_fwd(const T* __restrict__ qr, const T* __restrict__ kr,
-                                                    const T* __restrict__ vv, const T* __restrict__ oL,
-                                                    const float* __restrict__ lseL, T* __restrict__ o,
-                                                    float* __restrict__ lse, int Tn, int H, int Hkv, int w,
-                                                    float scale) {
+template <typename T, int D, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_win_fwd(const T* __restrict__ qr, const T* __restrict__ kr,
+                                                      const T* __restrict__ vv, const T* __restrict__ oL,
+                                                      const float* __restrict__ lseL, T* __restrict__ o,
+                                                      float* __restrict__ lse, int Tn, int H, int Hkv, int w,
+                                                      float scale) {
   using S = WinFwdSmem<T, D>;
-  constexpr int PD = S::PD, PK = S::PK;
+  constexpr int PD = S::PD, PK = S::PK, NT = NWV * 64, QT = 16 * NWV;
   __shared__ S sm;
   const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
   // logical tile = (query tile, b*H + h), XCD-contiguous
   const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
-  const int q0 = (L % gridDim.x) * 64, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
-  const int tq = q0 + 16 * W + cc;
+  const int q0 = (L % gridDim.x) * QT, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  const int wl = q0 + 16 * W;  // first query of this wave
+  const int tq = wl + cc;
   const bool qvalid = tq < Tn;
   typename Vec<T>::v8 qf[D / 32];
 #pragma unroll
@@ -384,36 +388,39 @@ __global__ __launch_bounds__(256, 2) void k_win_fwd(const T* __restrict__ qr, co
   if (w > 0) {
     int kmin = q0 - w + 1;
     if (kmin < 0) kmin = 0;
-    int kmax = q0 + 63;
+    int kmax = q0 + QT - 1;
     if (kmax > Tn - 1) kmax = Tn - 1;
     const int jfirst = (kmin / 64) * 64;
     const int ntiles = (kmax - jfirst) / 64 + 1;
     const size_t ld = (size_t)Hkv * D;
     const T* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
     const T* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
-    RowTile<T, D, 256> tk;
-    PairTileT<T, D, 256> tv;
+    RowTile<T, D, NT> tk;
+    PairTileT<T, D, NT> tv;
     tk.load(kbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
     tv.load(vbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
-    tk.template store<PD>(sm.k[0], tid);
-    tv.template store<PK>(sm.vt[0], tid);
-    __syncthreads();
-    if (ntiles > 1) {
-      tk.load(kbase + (size_t)(jfirst + 64) * ld, ld, 0, Tn - jfirst - 64, tid);
-      tv.load(vbase + (size_t)(jfirst + 64) * ld, ld, 0, Tn - jfirst - 64, tid);
-    }
     for (int it = 0; it < ntiles; ++it) {
-      const int cur = it & 1, j0 = jfirst + 64 * it;
-      const T* sK = sm.k[cur];
-      const T* sVt = sm.vt[cur];
-      const bool full = (j0 + 63 <= q0) && (j0 > q0 + 63 - w) && (j0 + 63 < Tn);
+      const int j0 = jfirst + 64 * it;
+      __syncthreads();
+      tk.template store<PD>(sm.k, tid);
+      tv.template store<PK>(sm.vt, tid);
+      __syncthreads();
+      if (it + 1 < ntiles) {
+        int jn = j0 + 64;
+        tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+        tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+      }
+      // does this tile meet the band of the wave's rows [wl, wl + 15]?
+      const bool useful = wl < Tn && j0 <= wl + 15 && j0 + 63 > wl - w;
+      if (!useful) continue;
+      const bool full = (j0 + 63 <= wl) && (j0 > wl + 15 - w) && (j0 + 63 < Tn);
       float s[4][4];
       float mx = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         floatx4 acc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) acc = mma32(acc, ld8<T>(&sK[(16 * mb + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
+        for (int ks = 0; ks < D / 32; ++ks) acc = mma32(acc, ld8<T>(&sm.k[(16 * mb + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float x = acc[r] * sl2;
@@ -449,19 +456,9 @@ __global__ __launch_bounds__(256, 2) void k_win_fwd(const T* __restrict__ qr, co
 #pragma unroll
         for (int db = 0; db < D / 16; ++db)
           accO[db] = mma32(accO[db],
-                           ld4x2<T>(&sVt[(16 * db + cc) * PK + 32 * st + 4 * g],
-                                    &sVt[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
+                           ld4x2<T>(&sm.vt[(16 * db + cc) * PK + 32 * st + 4 * g],
+                                    &sm.vt[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
                            bfr);
-      }
-      if (it + 1 < ntiles) {
-        tk.template store<PD>(sm.k[cur ^ 1], tid);
-        tv.template store<PK>(sm.vt[cur ^ 1], tid);
-      }
-      __syncthreads();
-      if (it + 2 < ntiles) {
-        int jn = j0 + 128;
-        tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
-        tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
       }
     }
   }
@@ -550,8 +547,9 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
                        (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
     mk.mark(st);
-    hipLaunchKernelGGL((k_win_fwd<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, ol, lsel, (T*)p.o,
-                       p.lse, s.T, s.H, s.Hkv, s.w, s.scale);
+    hipLaunchKernelGGL((k_win_fwd<T, D, kWinWaves>), dim3((s.T + 16 * kWinWaves - 1) / (16 * kWinWaves), s.B * s.H),
+                       dim3(kWinWaves * 64), 0, st, qr, kr, v, ol, lsel, (T*)p.o, p.lse, s.T, s.H, s.Hkv, s.w,
+                       s.scale);
     if (p.state_out) {
       char* base = (char*)p.state_out;
       mk.mark(st);
