@@ -239,3 +239,35 @@ struct PairTileT {
     }
   }
 };
+
+// ---------------------------------------------------------------- 32x32 tiles
+// 32x32 accumulator (16 floats per lane, h = l / 32, c = l % 32):
+//   lane l holds D[8 (r / 4) + 4 h + r % 4][c], r = 0..15
+// K=16 step (v_mfma_f32_32x32x16_bf16): A frag = A[c][8h .. 8h+7],
+//                                      B frag = B[8h .. 8h+7][c]
+// Float operands use v_mfma_f32_32x32x2_f32 once per element s of the same
+// fragments (k-subset {s, 8 + s}).
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ floatx16 zero16() {
+  floatx16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = 0.f;
+  return r;
+}
+__device__ __forceinline__ floatx16 mma32x32(floatx16 acc, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mma32x32(floatx16 acc, floatx8 a, floatx8 b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+  return acc;
+}
+// 8 consecutive accumulator entries r0 .. r0+7 packed as one fragment of T.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 pack8_at(const floatx16& a, int r0) {
+  typename Vec<T>::v8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = to_t<T>(a[r0 + i]);
+  return r;
+}

@@ -336,13 +336,20 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
 }
 
 // ---------------------------------------------------------------- window branch
-// grid (ceil(T / (16 NWV)), B*H), NWV waves; wave W owns queries q0 + 16W ..
-// +15.  Online softmax in log2 units, seeded with the slot partial as one key
-// of logit lse_L and value o_L / Z_L.  One 64-row K / V tile is staged in LDS
-// at a time and serves all 16 NWV queries; the next tile's global loads are in
-// flight (in registers) while the current one is used.  A wave skips tiles
-// outside its rows' band.  Writes o and lse.
-constexpr int kWinWaves = 8;
+// grid (ceil(T / (32 NWV)), B*H), NWV waves; wave W owns queries q0 + 32W ..
+// +31 and works on 32x32 tiles with the query index as the column:
+// S^T = K Q^T (key rows), O^T += V^T P^T, so every lane holds one query's
+// scores and output column and the softmax bookkeeping stays in the lane
+// (plus its partner lane l ^ 32 for the maximum and the sum).  Online softmax
+// in log2 units, seeded with the slot partial as one key of logit lse_L and
+// value o_L / Z_L; the running maximum is only moved (and O rescaled) when a
+// tile raises it by more than 2^kLazy, which keeps every exponent <= kLazy.
+// One 64-row K / V tile is staged in LDS at a time and serves all 32 NWV
+// queries; the next tile's global loads are in flight (in registers) while
+// the current one is used.  A wave skips tiles outside its rows' band and
+// masks only the tiles that cross the band's edges.  Writes o and lse.
+constexpr int kWinWaves = 4;
+constexpr float kLazy = 8.f;
 
 template <typename T, int D>
 struct WinFwdSmem {
@@ -352,36 +359,39 @@ struct WinFwdSmem {
 };
 
 template <typename T, int D, int NWV>
-__global__ __launch_bounds__(NWV * 64) void k_win_fwd(const T* __restrict__ qr, const T* __restrict__ kr,
+__global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ qr, const T* __restrict__ kr,
                                                       const T* __restrict__ vv, const T* __restrict__ oL,
                                                       const float* __restrict__ lseL, T* __restrict__ o,
                                                       float* __restrict__ lse, int Tn, int H, int Hkv, int w,
                                                       float scale) {
   using S = WinFwdSmem<T, D>;
-  constexpr int PD = S::PD, PK = S::PK, NT = NWV * 64, QT = 16 * NWV;
+  constexpr int PD = S::PD, PK = S::PK, NT = NWV * 64, QT = 32 * NWV;
   __shared__ S sm;
-  const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, hf = l >> 5, c = l & 31;
   // logical tile = (query tile, b*H + h), XCD-contiguous
   const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
   const int q0 = (L % gridDim.x) * QT, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
-  const int wl = q0 + 16 * W;  // first query of this wave
-  const int tq = wl + cc;
+  const int wl = q0 + 32 * W;  // first query of this wave
+  const int tq = wl + c;
   const bool qvalid = tq < Tn;
-  typename Vec<T>::v8 qf[D / 32];
+  const size_t qrow = (((size_t)b * Tn + tq) * H + h) * D;
+  typename Vec<T>::v8 qf[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = qvalid ? ld8<T>(qr + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<T>();
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qvalid ? ld8<T>(qr + qrow + 16 * ks + 8 * hf) : zero8<T>();
   // seed with the slot partial
-  float mu = qvalid ? lseL[((size_t)b * H + h) * Tn + tq] * NHA_LOG2E : 0.f;
-  float zl = (g == 0) ? 1.f : 0.f;  // lane-partial normaliser
-  floatx4 accO[D / 16];
+  float mu = qvalid ? lseL[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
+  float zl = (hf == 0) ? 1.f : 0.f;  // lane-partial normaliser
+  floatx16 acc[D / 32];              // O^T: rows d = 32 dt + 8 i + 4 hf + rr, column = query
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    accO[db] = zero4();
+  for (int dt = 0; dt < D / 32; ++dt) {
+    acc[dt] = zero16();
     if (qvalid) {
-      typename Vec<T>::v4 x = ld4<T>(oL + (((size_t)b * Tn + tq) * H + h) * D + 16 * db + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) accO[db][r] = to_f<T>(x[r]);
+      for (int i = 0; i < 4; ++i) {
+        typename Vec<T>::v4 x = ld4<T>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = to_f<T>(x[rr]);
+      }
     }
   }
   const float sl2 = scale * NHA_LOG2E;
@@ -410,65 +420,75 @@ __global__ __launch_bounds__(NWV * 64) void k_win_fwd(const T* __restrict__ qr, 
         tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
         tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
       }
-      // does this tile meet the band of the wave's rows [wl, wl + 15]?
-      const bool useful = wl < Tn && j0 <= wl + 15 && j0 + 63 > wl - w;
+      // does this tile meet the band of the wave's rows [wl, wl + 31]?
+      const bool useful = wl < Tn && j0 <= wl + 31 && j0 + 63 > wl - w;
       if (!useful) continue;
-      const bool full = (j0 + 63 <= wl) && (j0 > wl + 15 - w) && (j0 + 63 < Tn);
-      float s[4][4];
+      const bool full = (j0 + 63 <= wl) && (j0 > wl + 31 - w) && (j0 + 63 < Tn);
+      floatx16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          s[kb] = mma32x32(s[kb], ld8<T>(&sm.k[(32 * kb + c) * PD + 16 * ks + 8 * hf]), qf[ks]);
+      }
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            bool ok = key <= tq && key > tq - w && key < Tn;
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        floatx4 acc = zero4();
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) acc = mma32(acc, ld8<T>(&sm.k[(16 * mb + cc) * PD + 32 * ks + 8 * g]), qf[ks]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
+      const bool raise = mx > mu + kLazy;
+      if (__any(raise)) {
+        float mnew = raise ? mx : mu;
+        float resc = fast_exp2(mu - mnew);
+        mu = mnew;
+        zl *= resc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = acc[r] * sl2;
-          if (!full) {
-            int key = j0 + 16 * mb + 4 * g + r;
-            bool ok = key <= tq && key > tq - w && key < Tn;
-            x = ok ? x : -INFINITY;
-          }
-          s[mb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= resc;
       }
-      mx = max_over_g(mx);
-      float mnew = fmaxf(mu, mx);
-      float resc = fast_exp2(mu - mnew);
-      mu = mnew;
-      zl *= resc;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) accO[db] *= resc;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float pv = fast_exp2(s[mb][r] - mu);
-          s[mb][r] = pv;
+        for (int r = 0; r < 16; ++r) {
+          float pv = fast_exp2(fmaf(s[kb][r], sl2, -mu));
+          s[kb][r] = pv;
           zl += pv;
         }
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        typename Vec<T>::v8 bfr = pack8<T>(floatx4{s[2 * st][0], s[2 * st][1], s[2 * st][2], s[2 * st][3]},
-                                           floatx4{s[2 * st + 1][0], s[2 * st + 1][1], s[2 * st + 1][2],
-                                                   s[2 * st + 1][3]});
+      for (int st = 0; st < 4; ++st) {
+        typename Vec<T>::v8 bfr = pack8_at<T>(s[st >> 1], 8 * (st & 1));
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-          accO[db] = mma32(accO[db],
-                           ld4x2<T>(&sm.vt[(16 * db + cc) * PK + 32 * st + 4 * g],
-                                    &sm.vt[(16 * db + cc) * PK + 32 * st + 16 + 4 * g]),
-                           bfr);
+        for (int dt = 0; dt < D / 32; ++dt)
+          acc[dt] = mma32x32(acc[dt],
+                             ld4x2<T>(&sm.vt[(32 * dt + c) * PK + 16 * st + 4 * hf],
+                                      &sm.vt[(32 * dt + c) * PK + 16 * st + 8 + 4 * hf]),
+                             bfr);
       }
     }
   }
-  float z = sum_over_g(zl);
+  const float z = zl + shfl_xor(zl, 32);
   if (qvalid) {
-    float inv = 1.f / z;
-    T* dst = o + (((size_t)b * Tn + tq) * H + h) * D;
+    const float inv = 1.f / z;
+    T* dst = o + qrow;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db] * inv));
-    if (g == 0 && lse) lse[((size_t)b * H + h) * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st4<T>(dst + 32 * dt + 8 * i + 4 * hf,
+               pack4<T>(floatx4{acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv, acc[dt][4 * i + 2] * inv,
+                                acc[dt][4 * i + 3] * inv}));
+    if (hf == 0 && lse) lse[(size_t)bh * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
   }
 }
 
@@ -547,7 +567,7 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
                        (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
     mk.mark(st);
-    hipLaunchKernelGGL((k_win_fwd<T, D, kWinWaves>), dim3((s.T + 16 * kWinWaves - 1) / (16 * kWinWaves), s.B * s.H),
+    hipLaunchKernelGGL((k_win_fwd<T, D, kWinWaves>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
                        dim3(kWinWaves * 64), 0, st, qr, kr, v, ol, lsel, (T*)p.o, p.lse, s.T, s.H, s.Hkv, s.w,
                        s.scale);
     if (p.state_out) {
