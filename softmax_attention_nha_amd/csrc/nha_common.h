@@ -96,14 +96,26 @@ __device__ __forceinline__ typename Vec<T>::v4 pack4(floatx4 a) {
 }
 
 // ---------------------------------------------------------------- loads / stores
-// 8 consecutive elements (16-byte aligned for bf16, 16-byte aligned for float).
-template <typename T>
-__device__ __forceinline__ typename Vec<T>::v8 ld8(const T* p) {
-  return *reinterpret_cast<const typename Vec<T>::v8*>(p);
-}
 template <typename T>
 __device__ __forceinline__ typename Vec<T>::v4 ld4(const T* p) {
   return *reinterpret_cast<const typename Vec<T>::v4*>(p);
+}
+// 8 consecutive elements (16-byte aligned; float is read as two halves so
+// that 16-byte alignment suffices for it as well).
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 ld8(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const typename Vec<T>::v8*>(p);
+  } else {
+    typename Vec<T>::v4 a = ld4<T>(p), b = ld4<T>(p + 4);
+    typename Vec<T>::v8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = a[i];
+      r[4 + i] = b[i];
+    }
+    return r;
+  }
 }
 // Two groups of 4 consecutive elements -> one K=32 fragment (permuted order).
 template <typename T>
@@ -154,6 +166,17 @@ __device__ __forceinline__ float sum_over_g(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: the
+// pair returned holds both halves' values in either lane, in some order).
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X (linear
 // id n goes to XCD n % 8), and each XCD has its own L2.  xcd_remap turns the
 // linear id into a logical index such that every XCD receives one contiguous
@@ -197,12 +220,19 @@ struct RowTile {
   }
 };
 
+// Position of row k inside a transposed row when SWZ is set: bits 2 and 3 of
+// k trade places, so that within every 16-row group the rows {4h + r} and
+// {8 + 4h + r} (h = 0, 1; r = 0..3) -- the K=16 step of a 32x32 product fed
+// from an accumulator in D layout -- sit next to each other at 8h .. 8h+7.
+__host__ __device__ constexpr int kswz(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
 // The same tile stored transposed ([D][P], row index contiguous), for operands
 // whose K dimension is the tile's row index.  Thread = (row pair p, column-chunk
 // group): it loads rows 2p and 2p+1 of one 8-column chunk and writes 8 packed
 // pairs, so a wavefront writes consecutive pairs of one LDS row per store
-// (conflict-free) instead of scattering 2-byte values.
-template <typename T, int D, int NT, int ROWS = 64>
+// (conflict-free) instead of scattering 2-byte values.  With SWZ the pair of
+// rows 2p, 2p+1 lands at kswz(2p) (the swap keeps pairs together).
+template <typename T, int D, int NT, int ROWS = 64, bool SWZ = false>
 struct PairTileT {
   static constexpr int NP = ROWS / 2;                // row pairs
   static constexpr int NG = NT / NP;                 // chunk groups
@@ -227,13 +257,25 @@ struct PairTileT {
     for (int k = 0; k < PER; ++k) {
       int c = cg + k * NG;
       if (c < NCH && cg < NG) {
+        const int col = SWZ ? kswz(2 * p) : 2 * p;
+        if constexpr (sizeof(T) == 2) {
+          // bf16: word x/2 of each row holds columns x (low half) and x+1
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          u32x4 wa = __builtin_bit_cast(u32x4, a[k]), wb = __builtin_bit_cast(u32x4, b[k]);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          typedef T pair_t __attribute__((ext_vector_type(2)));
-          pair_t v;
-          v[0] = a[k][x];
-          v[1] = b[k][x];
-          *reinterpret_cast<pair_t*>(lds + (8 * c + x) * P + 2 * p) = v;
+          for (int x = 0; x < 8; ++x) {
+            uint32_t v = __builtin_amdgcn_perm(wb[x >> 1], wa[x >> 1], (x & 1) ? 0x07060302u : 0x05040100u);
+            *reinterpret_cast<uint32_t*>(lds + (8 * c + x) * P + col) = v;
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            typedef T pair_t __attribute__((ext_vector_type(2)));
+            pair_t v;
+            v[0] = a[k][x];
+            v[1] = b[k][x];
+            *reinterpret_cast<pair_t*>(lds + (8 * c + x) * P + col) = v;
+          }
         }
       }
     }
@@ -270,4 +312,52 @@ __device__ __forceinline__ typename Vec<T>::v8 pack8_at(const floatx16& a, int r
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = to_t<T>(a[r0 + i]);
   return r;
+}
+
+// ---------------------------------------------------------------- direct-to-LDS staging (bf16)
+// 64-row bf16 tiles kept unpadded in LDS ([row][D], rows of D/8 16-byte
+// chunks) and filled with global_load_lds_dwordx4: every wave instruction
+// writes 64 x 16 contiguous bytes (lane l at byte 16 l), i.e. 64 / (D/8)
+// whole rows.  The chunk order inside a row is permuted (XOR with a function
+// of the row) so that the two read patterns below meet every bank once:
+//   kind 0 (row-major fragments): lane c reads one chunk of row r0 + c
+//   kind 1 (transposed reads):    16 lanes read 2 neighbouring chunks of 4
+//                                 consecutive rows (ds_read_b64_tr_b16)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+template <int D, int KIND>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if constexpr (KIND == 0) return row & (D / 8 - 1);
+  else return ((0xAC60 >> (4 * (row & 3))) & 15) & (D / 8 - 1);
+}
+
+// Rows [j0, j0 + 64) of a bf16 operand with row stride ld (rows past Tn - 1
+// repeat row Tn - 1; callers mask those keys) into the swizzled tile `lds`.
+// NT threads; each wave issues D/8 / (NT/64) instructions.
+template <int D, int NT, int KIND>
+__device__ __forceinline__ void dma_tile(const bf16* __restrict__ base, size_t ld, int j0, int Tn, bf16* lds,
+                                         int tid) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, NI = 64 / RPI, NW = NT / 64;
+  const int wv = tid >> 6, l = tid & 63;
+#pragma unroll
+  for (int i0 = 0; i0 < NI; i0 += NW) {
+    const int i = i0 + wv;
+    if (NI % NW == 0 || i < NI) {
+      const int r = i * RPI + l / CPR;
+      const int q = (l % CPR) ^ chunk_swz<D, KIND>(r);
+      const int gr = min(j0 + r, Tn - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(base + (size_t)gr * ld + 8 * q),
+                                       (lds_void_t*)(lds + i * RPI * D), 16, 0, 0);
+    }
+  }
+}
+
+// Wait for this wave's outstanding global loads (including the ones that
+// write LDS directly); a barrier must follow before other waves read them.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ bf16x4 ld_tr4(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
 }

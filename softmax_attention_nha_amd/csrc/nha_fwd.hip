@@ -353,9 +353,11 @@ constexpr float kLazy = 8.f;
 
 template <typename T, int D>
 struct WinFwdSmem {
-  static constexpr int PD = pitch_of(D), PK = 64 + 4;
+  // row pitches of 4 (mod 32) dwords: 8 lanes reading 16 bytes each at the
+  // same column of 8 consecutive rows cover the 32 banks once
+  static constexpr int PD = pitch_of(D), PK = 64 + 16 / (int)sizeof(T);
   T k[64 * PD];  // RoPE'd keys [key][d]
-  T vt[D * PK];  // values, transposed [d][key]
+  T vt[D * PK];  // values, transposed [d][kswz(key)]
 };
 
 template <typename T, int D, int NWV>
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ q
                                                       float scale) {
   using S = WinFwdSmem<T, D>;
   constexpr int PD = S::PD, PK = S::PK, NT = NWV * 64, QT = 32 * NWV;
-  __shared__ S sm;
+  __shared__ S sm[2];
   const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, hf = l >> 5, c = l & 31;
   // logical tile = (query tile, b*H + h), XCD-contiguous
   const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
@@ -406,78 +408,104 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ q
     const T* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
     const T* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
     RowTile<T, D, NT> tk;
-    PairTileT<T, D, NT> tv;
+    PairTileT<T, D, NT, 64, true> tv;
     tk.load(kbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
     tv.load(vbase + (size_t)jfirst * ld, ld, 0, Tn - jfirst, tid);
+    tk.template store<PD>(sm[0].k, tid);
+    tv.template store<PK>(sm[0].vt, tid);
+    if (ntiles > 1) {
+      int jn = jfirst + 64;
+      tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+      tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+    }
+    __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
       const int j0 = jfirst + 64 * it;
-      __syncthreads();
-      tk.template store<PD>(sm.k, tid);
-      tv.template store<PK>(sm.vt, tid);
-      __syncthreads();
+      // stage tile it+1 into the other buffer (last read before the previous
+      // barrier) and start the global loads of tile it+2
       if (it + 1 < ntiles) {
-        int jn = j0 + 64;
-        tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
-        tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+        tk.template store<PD>(sm[(it + 1) & 1].k, tid);
+        tv.template store<PK>(sm[(it + 1) & 1].vt, tid);
+        if (it + 2 < ntiles) {
+          int jn = j0 + 128;
+          tk.load(kbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+          tv.load(vbase + (size_t)jn * ld, ld, 0, Tn - jn, tid);
+        }
       }
+      const S& cur = sm[it & 1];
       // does this tile meet the band of the wave's rows [wl, wl + 31]?
       const bool useful = wl < Tn && j0 <= wl + 31 && j0 + 63 > wl - w;
-      if (!useful) continue;
-      const bool full = (j0 + 63 <= wl) && (j0 > wl + 31 - w) && (j0 + 63 < Tn);
-      floatx16 s[2];
+      if (useful) {
+        const bool full = (j0 + 63 <= wl) && (j0 > wl + 31 - w) && (j0 + 63 < Tn);
+        // S^T = K Q^T; the K fragments of step ks+1 are read while step ks runs
+        floatx16 s[2];
+        s[0] = zero16();
+        s[1] = zero16();
+        typename Vec<T>::v8 kfr[2][2];
+        kfr[0][0] = ld8<T>(&cur.k[c * PD + 8 * hf]);
+        kfr[0][1] = ld8<T>(&cur.k[(32 + c) * PD + 8 * hf]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16();
+        for (int ks = 0; ks < D / 16; ++ks) {
+          if (ks + 1 < D / 16) {
+            kfr[(ks + 1) & 1][0] = ld8<T>(&cur.k[c * PD + 16 * (ks + 1) + 8 * hf]);
+            kfr[(ks + 1) & 1][1] = ld8<T>(&cur.k[(32 + c) * PD + 16 * (ks + 1) + 8 * hf]);
+          }
+          s[0] = mma32x32(s[0], kfr[ks & 1][0], qf[ks]);
+          s[1] = mma32x32(s[1], kfr[ks & 1][1], qf[ks]);
+        }
+        // V^T fragments of the first step, read while the softmax runs
+        typename Vec<T>::v8 vfr[2][D / 32];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          s[kb] = mma32x32(s[kb], ld8<T>(&sm.k[(32 * kb + c) * PD + 16 * ks + 8 * hf]), qf[ks]);
-      }
-      if (!full) {
+        for (int dt = 0; dt < D / 32; ++dt) vfr[0][dt] = ld8<T>(&cur.vt[(32 * dt + c) * PK + 8 * hf]);
+        if (!full) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+              bool ok = key <= tq && key > tq - w && key < Tn;
+              s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = max_halves(mx) * sl2;
+        const bool raise = mx > mu + kLazy;
+        if (__any(raise)) {
+          float mnew = raise ? mx : mu;
+          float resc = fast_exp2(mu - mnew);
+          mu = mnew;
+          zl *= resc;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= resc;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            bool ok = key <= tq && key > tq - w && key < Tn;
-            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            float pv = fast_exp2(fmaf(s[kb][r], sl2, -mu));
+            s[kb][r] = pv;
+            zl += pv;
           }
-      }
-      float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int st = 0; st < 4; ++st) {
+          if (st + 1 < 4) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
-      const bool raise = mx > mu + kLazy;
-      if (__any(raise)) {
-        float mnew = raise ? mx : mu;
-        float resc = fast_exp2(mu - mnew);
-        mu = mnew;
-        zl *= resc;
+            for (int dt = 0; dt < D / 32; ++dt)
+              vfr[(st + 1) & 1][dt] = ld8<T>(&cur.vt[(32 * dt + c) * PK + 16 * (st + 1) + 8 * hf]);
+          }
+          typename Vec<T>::v8 bfr = pack8_at<T>(s[st >> 1], 8 * (st & 1));
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= resc;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = fast_exp2(fmaf(s[kb][r], sl2, -mu));
-          s[kb][r] = pv;
-          zl += pv;
+          for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mma32x32(acc[dt], vfr[st & 1][dt], bfr);
         }
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        typename Vec<T>::v8 bfr = pack8_at<T>(s[st >> 1], 8 * (st & 1));
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          acc[dt] = mma32x32(acc[dt],
-                             ld4x2<T>(&sm.vt[(32 * dt + c) * PK + 16 * st + 4 * hf],
-                                      &sm.vt[(32 * dt + c) * PK + 16 * st + 8 + 4 * hf]),
-                             bfr);
-      }
+      }  // useful
+      __syncthreads();
     }
   }
-  const float z = zl + shfl_xor(zl, 32);
+  const float z = sum_halves(zl);
   if (qvalid) {
     const float inv = 1.f / z;
     T* dst = o + qrow;
@@ -488,6 +516,163 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ q
         st4<T>(dst + 32 * dt + 8 * i + 4 * hf,
                pack4<T>(floatx4{acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv, acc[dt][4 * i + 2] * inv,
                                 acc[dt][4 * i + 3] * inv}));
+    if (hf == 0 && lse) lse[(size_t)bh * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
+  }
+}
+
+// bf16 variant of the same kernel: K and V tiles go straight from global
+// memory to LDS (global_load_lds, no staging registers), double-buffered, and
+// the transposed V operand is read with ds_read_b64_tr_b16 from the row-major
+// tile.
+template <int D>
+struct WinFwdSmemB16 {
+  bf16 k[2][64 * D];
+  bf16 v[2][64 * D];
+};
+
+template <int D, int NWV>
+__global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restrict__ qr, const bf16* __restrict__ kr,
+                                                             const bf16* __restrict__ vv, const bf16* __restrict__ oL,
+                                                             const float* __restrict__ lseL, bf16* __restrict__ o,
+                                                             float* __restrict__ lse, int Tn, int H, int Hkv, int w,
+                                                             float scale) {
+  constexpr int NT = NWV * 64, QT = 32 * NWV;
+  __shared__ WinFwdSmemB16<D> sm;
+  const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, hf = l >> 5, c = l & 31, jj = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int q0 = (L % gridDim.x) * QT, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  const int wl = q0 + 32 * W;
+  const int tq = wl + c;
+  const bool qvalid = tq < Tn;
+  const size_t qrow = (((size_t)b * Tn + tq) * H + h) * D;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qvalid ? ld8<bf16>(qr + qrow + 16 * ks + 8 * hf) : zero8<bf16>();
+  float mu = qvalid ? lseL[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
+  float zl = (hf == 0) ? 1.f : 0.f;
+  floatx16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    acc[dt] = zero16();
+    if (qvalid) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 x = ld4<bf16>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = (float)x[rr];
+      }
+    }
+  }
+  // per-lane LDS element offsets of the K fragments (row c, logical chunk
+  // 2 ks + hf) and of the transposed V reads (rows 4 hf + jj / 4 (+8) of each
+  // 16-row step, columns 32 dt + 16 (c / 16) + 4 (jj % 4) ..)
+  int koff[D / 16], voff[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 0>(c));
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int r = 4 * hf + (jj >> 2), d0 = 32 * dt + 16 * (c >> 4) + 4 * (jj & 3);
+    voff[dt] = r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 1>(r)) + (d0 & 7);
+  }
+  const float sl2 = scale * NHA_LOG2E;
+  if (w > 0) {
+    int kmin = q0 - w + 1;
+    if (kmin < 0) kmin = 0;
+    int kmax = q0 + QT - 1;
+    if (kmax > Tn - 1) kmax = Tn - 1;
+    const int jfirst = (kmin / 64) * 64;
+    const int ntiles = (kmax - jfirst) / 64 + 1;
+    const size_t ld = (size_t)Hkv * D;
+    const bf16* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
+    const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
+    dma_tile<D, NT, 0>(kbase, ld, jfirst, Tn, sm.k[0], tid);
+    dma_tile<D, NT, 1>(vbase, ld, jfirst, Tn, sm.v[0], tid);
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int j0 = jfirst + 64 * it, cb = it & 1;
+      if (it + 1 < ntiles) {
+        dma_tile<D, NT, 0>(kbase, ld, j0 + 64, Tn, sm.k[cb ^ 1], tid);
+        dma_tile<D, NT, 1>(vbase, ld, j0 + 64, Tn, sm.v[cb ^ 1], tid);
+      }
+      const bf16* kt = sm.k[cb];
+      const bf16* vt = sm.v[cb];
+      const bool useful = wl < Tn && j0 <= wl + 31 && j0 + 63 > wl - w;
+      if (useful) {
+        const bool full = (j0 + 63 <= wl) && (j0 > wl + 31 - w) && (j0 + 63 < Tn);
+        floatx16 s[2];
+        s[0] = zero16();
+        s[1] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          s[0] = mma32x32(s[0], ld8<bf16>(kt + koff[ks]), qf[ks]);
+          s[1] = mma32x32(s[1], ld8<bf16>(kt + 32 * D + koff[ks]), qf[ks]);
+        }
+        if (!full) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+              bool ok = key <= tq && key > tq - w && key < Tn;
+              s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = max_halves(mx) * sl2;
+        const bool raise = mx > mu + kLazy;
+        if (__any(raise)) {
+          float mnew = raise ? mx : mu;
+          float resc = fast_exp2(mu - mnew);
+          mu = mnew;
+          zl *= resc;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= resc;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float pv = fast_exp2(fmaf(s[kb][r], sl2, -mu));
+            s[kb][r] = pv;
+            zl += pv;
+          }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          bf16x8 bfr = pack8_at<bf16>(s[st >> 1], 8 * (st & 1));
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const bf16* p = vt + 16 * st * D + voff[dt];
+            bf16x4 a0 = ld_tr4(p), a1 = ld_tr4(p + 8 * D);
+            bf16x8 afr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              afr[e] = a0[e];
+              afr[4 + e] = a1[e];
+            }
+            acc[dt] = mma32x32(acc[dt], afr, bfr);
+          }
+        }
+      }  // useful
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+  const float z = sum_halves(zl);
+  if (qvalid) {
+    const float inv = 1.f / z;
+    bf16* dst = o + qrow;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st4<bf16>(dst + 32 * dt + 8 * i + 4 * hf,
+                  pack4<bf16>(floatx4{acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv, acc[dt][4 * i + 2] * inv,
+                                      acc[dt][4 * i + 3] * inv}));
     if (hf == 0 && lse) lse[(size_t)bh * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
   }
 }
@@ -567,9 +752,15 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
                        (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
     mk.mark(st);
-    hipLaunchKernelGGL((k_win_fwd<T, D, kWinWaves>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
-                       dim3(kWinWaves * 64), 0, st, qr, kr, v, ol, lsel, (T*)p.o, p.lse, s.T, s.H, s.Hkv, s.w,
-                       s.scale);
+    if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL((k_win_fwd_b16<D, kWinWaves>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
+                         dim3(kWinWaves * 64), 0, st, qr, kr, v, ol, lsel, (T*)p.o, p.lse, s.T, s.H, s.Hkv, s.w,
+                         s.scale);
+    } else {
+      hipLaunchKernelGGL((k_win_fwd<T, D, kWinWaves>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
+                         dim3(kWinWaves * 64), 0, st, qr, kr, v, ol, lsel, (T*)p.o, p.lse, s.T, s.H, s.Hkv, s.w,
+                         s.scale);
+    }
     if (p.state_out) {
       char* base = (char*)p.state_out;
       mk.mark(st);
