@@ -361,3 +361,73 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 __device__ __forceinline__ bf16x4 ld_tr4(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
 }
+// The same reads from a 32-bit LDS byte address.
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+__device__ __forceinline__ bf16x4 ld_tr4_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(uintptr_t)a);
+}
+__device__ __forceinline__ bf16x8 ld8_at(uint32_t a) { return *(lds_bf16x8_t*)(uintptr_t)a; }
+
+// The same staging issued through inline assembly, so that the compiler does
+// not order later LDS reads of *other* buffers after these loads (it cannot
+// tell the buffers apart).  The caller waits with wait_vmem() and a barrier
+// before anyone reads the tile.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const lds_void_t*)p);
+}
+// A wave-uniform pointer as an SGPR pair.
+__device__ __forceinline__ uint64_t sgpr_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+// Per-lane part (bytes) of the source offset of this wave's instructions
+// relative to their first row; callers compute it once and pass it in.
+template <int D, int NT, int KIND>
+__device__ __forceinline__ uint32_t dma_lane_off(int tid, size_t ld) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int wv = tid >> 6, l = tid & 63;
+  const int r = wv * RPI + l / CPR;
+  const int q = (l % CPR) ^ chunk_swz<D, KIND>(r);
+  return (uint32_t)((l / CPR) * ld * 2 + 16 * q);
+}
+template <int D, int NT, int KIND>
+__device__ __forceinline__ void dma_tile_async(const bf16* __restrict__ base, size_t ld, int j0, int Tn,
+                                               uint32_t lds, uint32_t loff, int tid) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR, NI = 64 / RPI, NW = NT / 64;
+  static_assert(NI % NW == 0, "tile instructions must split evenly over the waves");
+  // rows NW RPI apart share their swizzle, so one lane offset serves every
+  // instruction of the wave
+  static_assert((NW * RPI) % (KIND == 0 ? CPR : 4) == 0, "swizzle period");
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  if (j0 + 64 <= Tn) {
+    // whole tile in range: uniform row base in SGPRs, fixed per-lane offset
+    const uint64_t b0 = sgpr_ptr(base + (size_t)(j0 + wv * RPI) * ld);
+    const uint64_t step = (uint64_t)(NW * RPI) * ld * 2;
+    const uint32_t m00 = __builtin_amdgcn_readfirstlane(lds + (uint32_t)(wv * RPI * D * 2));
+#pragma unroll
+    for (int n = 0; n < NI / NW; ++n) {
+      const uint64_t rowp = b0 + n * step;
+      const uint32_t m0v = m00 + (uint32_t)(n * NW * RPI * D * 2);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(m0v), "v"(loff), "s"(rowp)
+                   : "memory", "m0");
+    }
+  } else {
+    // tail tile: rows past Tn - 1 repeat row Tn - 1
+#pragma unroll
+    for (int i0 = 0; i0 < NI; i0 += NW) {
+      const int i = i0 + wv;
+      const int r = i * RPI + l / CPR;
+      const int q = (l % CPR) ^ chunk_swz<D, KIND>(r);
+      const int gr = min(j0 + r, Tn - 1);
+      const uint32_t off = (uint32_t)((size_t)gr * ld * 2 + 16 * q);
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds + (uint32_t)(i * RPI * D * 2));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(m0v), "v"(off), "s"(sgpr_ptr(base))
+                   : "memory", "m0");
+    }
+  }
+}

@@ -520,16 +520,13 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ q
   }
 }
 
-// bf16 variant of the same kernel: K and V tiles go straight from global
-// memory to LDS (global_load_lds, no staging registers), double-buffered, and
-// the transposed V operand is read with ds_read_b64_tr_b16 from the row-major
-// tile.
-template <int D>
-struct WinFwdSmemB16 {
-  bf16 k[2][64 * D];
-  bf16 v[2][64 * D];
-};
-
+// bf16 variant of the same kernel, software-pipelined: K and V tiles go
+// straight from global memory to LDS (no staging registers; K triple-, V
+// double-buffered) and the transposed V operand is read with
+// ds_read_b64_tr_b16 from the row-major tile.  While the softmax of tile i
+// runs on the vector ALUs, the matrix cores already compute the scores of
+// tile i+1; masks enter as -inf in the initial value of the score
+// accumulators, so only the tiles that cross the band's edges pay for them.
 template <int D, int NWV>
 __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restrict__ qr, const bf16* __restrict__ kr,
                                                              const bf16* __restrict__ vv, const bf16* __restrict__ oL,
@@ -537,10 +534,16 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
                                                              float* __restrict__ lse, int Tn, int H, int Hkv, int w,
                                                              float scale) {
   constexpr int NT = NWV * 64, QT = 32 * NWV;
-  __shared__ WinFwdSmemB16<D> sm;
-  const int tid = threadIdx.x, W = tid >> 6, l = tid & 63, hf = l >> 5, c = l & 31, jj = l & 15;
+  __shared__ bf16 kbuf[3][64 * D];
+  __shared__ bf16 vbuf[2][64 * D];
+  // wave-uniform quantities are pinned to scalar registers (integer division
+  // is expanded on the vector ALUs otherwise)
+  const int tid = threadIdx.x, W = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hf = l >> 5, c = l & 31,
+            jj = l & 15;
   const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
-  const int q0 = (L % gridDim.x) * QT, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  const int q0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * QT), bh = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  const int b = __builtin_amdgcn_readfirstlane(bh / H), h = __builtin_amdgcn_readfirstlane(bh % H),
+            hg = __builtin_amdgcn_readfirstlane(h / (H / Hkv));
   const int wl = q0 + 32 * W;
   const int tq = wl + c;
   const bool qvalid = tq < Tn;
@@ -566,13 +569,15 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
   // per-lane LDS element offsets of the K fragments (row c, logical chunk
   // 2 ks + hf) and of the transposed V reads (rows 4 hf + jj / 4 (+8) of each
   // 16-row step, columns 32 dt + 16 (c / 16) + 4 (jj % 4) ..)
-  int koff[D / 16], voff[D / 32];
+  // byte offsets: K fragment of step ks at koff[ks] (+ 64 D for the second
+  // 32-key block), transposed V reads of column block dt at voff[dt]
+  uint32_t koff[D / 16], voff[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 0>(c));
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = 2 * (c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 0>(c)));
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     const int r = 4 * hf + (jj >> 2), d0 = 32 * dt + 16 * (c >> 4) + 4 * (jj & 3);
-    voff[dt] = r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 1>(r)) + (d0 & 7);
+    voff[dt] = 2 * (r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 1>(r)) + (d0 & 7));
   }
   const float sl2 = scale * NHA_LOG2E;
   if (w > 0) {
@@ -585,81 +590,156 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
     const size_t ld = (size_t)Hkv * D;
     const bf16* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
     const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
-    dma_tile<D, NT, 0>(kbase, ld, jfirst, Tn, sm.k[0], tid);
-    dma_tile<D, NT, 1>(vbase, ld, jfirst, Tn, sm.v[0], tid);
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int j0 = jfirst + 64 * it, cb = it & 1;
-      if (it + 1 < ntiles) {
-        dma_tile<D, NT, 0>(kbase, ld, j0 + 64, Tn, sm.k[cb ^ 1], tid);
-        dma_tile<D, NT, 1>(vbase, ld, j0 + 64, Tn, sm.v[cb ^ 1], tid);
-      }
-      const bf16* kt = sm.k[cb];
-      const bf16* vt = sm.v[cb];
-      const bool useful = wl < Tn && j0 <= wl + 31 && j0 + 63 > wl - w;
-      if (useful) {
-        const bool full = (j0 + 63 <= wl) && (j0 > wl + 31 - w) && (j0 + 63 < Tn);
-        floatx16 s[2];
-        s[0] = zero16();
-        s[1] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          s[0] = mma32x32(s[0], ld8<bf16>(kt + koff[ks]), qf[ks]);
-          s[1] = mma32x32(s[1], ld8<bf16>(kt + 32 * D + koff[ks]), qf[ks]);
-        }
-        if (!full) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-              bool ok = key <= tq && key > tq - w && key < Tn;
-              s[kb][r] = ok ? s[kb][r] : -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
+    const uint32_t kl = lds_addr(&kbuf[0][0]), vl = lds_addr(&vbuf[0][0]);
+    const uint32_t kdo = dma_lane_off<D, NT, 0>(tid, ld), vdo = dma_lane_off<D, NT, 1>(tid, ld);
+    constexpr uint32_t TB = 64 * D * 2;  // bytes per tile
+
+    auto useful = [&](int j0) { return wl < Tn && j0 <= wl + 31 && j0 + 63 > wl - w; };
+    // scores of the tile at j0 outside the band (or of a tile the wave does
+    // not need at all) -> -inf; skipped for tiles inside the band
+    auto mask_tile = [&](floatx16(&x)[2], int j0, bool use) {
+      if (!use || !((j0 + 63 <= wl) && (j0 > wl + 31 - w) && (j0 + 63 < Tn))) {
+        // key - tq = rel + (32 kb + 8 (r / 4) + r % 4) must lie in (-w, hi];
+        // an unused tile takes rel = 1, span = 0, which rejects every key
+        // (one code path keeps the scores in place, without copies)
+        const int rel = use ? j0 + 4 * hf - tq + w - 1 : 1;
+        const uint32_t span = use ? (uint32_t)(min(0, Tn - 1 - tq) + w - 1) : 0u;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = max_halves(mx) * sl2;
-        const bool raise = mx > mu + kLazy;
-        if (__any(raise)) {
-          float mnew = raise ? mx : mu;
-          float resc = fast_exp2(mu - mnew);
-          mu = mnew;
-          zl *= resc;
+          for (int r = 0; r < 16; ++r)
+            if ((uint32_t)(rel + 32 * kb + 8 * (r >> 2) + (r & 3)) > span) x[kb][r] = -INFINITY;
+      }
+    };
+    // One pass over the next tile's scores and/or this tile's softmax, cut
+    // into 2 D/16 short regions (sched_barrier: nothing moves across) of one
+    // score MFMA, the K read RA steps ahead and a slice of the softmax, so
+    // the vector ALUs work while the matrix core runs and no region hoists
+    // more reads than registers allow.  kt: LDS byte address of the next K
+    // tile (kept opaque so that one address per step is formed).
+    constexpr int NG = 2 * (D / 16), RA = 4;
+    auto main_pass = [&](auto do_s, auto do_sm, floatx16(&nx)[2], uint32_t kt, floatx16(&x)[2], bf16x8(&pf)[4],
+                         float& resc, bool& any_raise) {
+      bf16x8 kr[RA];
+      if constexpr (do_s.value) {
+#pragma unroll
+        for (int g = 0; g < RA; ++g) kr[g] = ld8_at(kt + koff[g >> 1] + (g & 1) * 64 * D);
+      }
+      float mx = -INFINITY, zs = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if constexpr (do_s.value) {
+          nx[g & 1] = mma32x32(g < 2 ? zero16() : nx[g & 1], kr[g % RA], qf[g >> 1]);
+          if (g + RA < NG) kr[g % RA] = ld8_at(kt + koff[(g + RA) >> 1] + ((g + RA) & 1) * 64 * D);
+        }
+        if constexpr (do_sm.value) {
+          constexpr int NMAX = NG / 4;                                  // regions computing the maximum
+          constexpr int PER = (32 + NG - NMAX - 2) / (NG - NMAX - 1);  // exponentials per region
+          if (g < NMAX) {
+#pragma unroll
+            for (int e = 0; e < 32 / NMAX; ++e) {
+              const int k = g * (32 / NMAX) + e;
+              mx = fmaxf(mx, x[k >> 4][k & 15]);
+            }
+          } else if (g == NMAX) {
+            mx = max_halves(mx) * sl2;
+            const bool raise = mx > mu + kLazy;
+            const float mnew = raise ? mx : mu;
+            resc = fast_exp2(mu - mnew);
+            mu = mnew;
+            any_raise = __any(raise);
+          } else {
+#pragma unroll
+            for (int e0 = 0; e0 < PER; ++e0) {
+              const int e = (g - NMAX - 1) * PER + e0;
+              if (e < 32) {
+                const float pv = fast_exp2(fmaf(x[e >> 4][e & 15], sl2, -mu));
+                x[e >> 4][e & 15] = pv;
+                zs += pv;
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (do_sm.value) {
+        zl = zl * resc + zs;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) pf[st] = pack8_at<bf16>(x[st >> 1], 8 * (st & 1));
+      }
+    };
+    // O^T += V^T P^T: 4 (D/32) MFMAs, each one's transposed reads issued VA
+    // MFMAs ahead
+    constexpr int NP = 4 * (D / 32), VA = 3;
+    auto pv = [&](const bf16x8(&pf)[4], uint32_t vt) {
+      bf16x8 vr[VA];
+      auto vload = [&](int g) {
+        const uint32_t p = vt + voff[g % (D / 32)] + 32 * (g / (D / 32)) * D;
+        const bf16x4 a0 = ld_tr4_at(p), a1 = ld_tr4_at(p + 16 * D);
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] = a0[e];
+          f[4 + e] = a1[e];
+        }
+        return f;
+      };
+#pragma unroll
+      for (int g = 0; g < VA; ++g) vr[g] = vload(g);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < NP; ++g) {
+        acc[g % (D / 32)] = mma32x32(acc[g % (D / 32)], vr[g % VA], pf[g / (D / 32)]);
+        if (g + VA < NP) vr[g % VA] = vload(g + VA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+
+    dma_tile_async<D, NT, 0>(kbase, ld, jfirst, Tn, kl, kdo, tid);
+    dma_tile_async<D, NT, 1>(vbase, ld, jfirst, Tn, vl, vdo, tid);
+    if (ntiles > 1) dma_tile_async<D, NT, 0>(kbase, ld, jfirst + 64, Tn, kl + TB, kdo, tid);
+    wait_vmem();
+    __syncthreads();
+    floatx16 sa[2], sb[2];
+    bool use_c = useful(jfirst);
+    {
+      bf16x8 pf0[4];
+      float r0;
+      bool a0;
+      main_pass(T_{}, F_{}, sa, __builtin_amdgcn_readfirstlane(kl), sb, pf0, r0, a0);
+    }
+    auto step = [&](floatx16(&cur)[2], floatx16(&nxt)[2], int it) {
+      const int j0 = jfirst + 64 * it;
+      if (it + 2 < ntiles) dma_tile_async<D, NT, 0>(kbase, ld, j0 + 128, Tn, kl + ((it + 2) % 3) * TB, kdo, tid);
+      if (it + 1 < ntiles) dma_tile_async<D, NT, 1>(vbase, ld, j0 + 64, Tn, vl + ((it + 1) & 1) * TB, vdo, tid);
+      const bool use_n = it + 1 < ntiles && useful(j0 + 64);
+      if (use_c || use_n) {
+        // one code path for every case (separate variants would each need
+        // their own registers): a tile this wave does not need is masked to
+        // -inf when it becomes the current one, and past the last tile the
+        // pass reads a stale buffer whose scores are never used
+        const uint32_t ktn = __builtin_amdgcn_readfirstlane(kl + ((it + 1) % 3) * TB);
+        bool any_raise = false;
+        float resc = 1.f;
+        bf16x8 pf[4];
+        mask_tile(cur, j0, use_c);
+        main_pass(T_{}, T_{}, nxt, ktn, cur, pf, resc, any_raise);
+        if (any_raise) {
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= resc;
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pv = fast_exp2(fmaf(s[kb][r], sl2, -mu));
-            s[kb][r] = pv;
-            zl += pv;
-          }
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          bf16x8 bfr = pack8_at<bf16>(s[st >> 1], 8 * (st & 1));
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const bf16* p = vt + 16 * st * D + voff[dt];
-            bf16x4 a0 = ld_tr4(p), a1 = ld_tr4(p + 8 * D);
-            bf16x8 afr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              afr[e] = a0[e];
-              afr[4 + e] = a1[e];
-            }
-            acc[dt] = mma32x32(acc[dt], afr, bfr);
-          }
-        }
-      }  // useful
+        pv(pf, __builtin_amdgcn_readfirstlane(vl + (it & 1) * TB));
+      }
+      use_c = use_n;
       wait_vmem();
       __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+      step(sa, sb, it);
+      if (it + 1 < ntiles) step(sb, sa, it + 1);
     }
   }
   const float z = sum_halves(zl);

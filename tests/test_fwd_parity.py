@@ -63,6 +63,16 @@ def test_bf16_workloads_reduced(name, w):
     check_full(wl, w=w)
 
 
+@pytest.mark.parametrize("d,w,T", [(32, 1, 300), (32, 97, 300), (64, 31, 333), (64, 150, 333), (128, 200, 461),
+                                   (128, 17, 140)])
+def test_bf16_head_dims_ragged_windows(d, w, T):
+    """bf16 at every head dimension with windows that are not a multiple of
+    the 64-key tile, so that waves of one query tile need different key tiles
+    (and skip the rest) and the band edges fall inside tiles."""
+    wl = WORKLOADS["340m"].with_(B=1, T=T, H=4, Hkv=2, d=d, seed=23)
+    check_full(wl, w=w)
+
+
 def test_bf16_stress_logits_and_hard_gates():
     wl = WORKLOADS["1p3b"].with_(B=1, T=448, H=2, Hkv=2, seed=21)
     check_full(wl, w=96, qk_scale=1.0, alpha_mu=-2.0)
