@@ -102,8 +102,8 @@ def stage_work(stage, wl, w, e):
         "slot_bwd_b": ("mfma", 2.0 * fs),
         "state_scan": ("mfma", flops_state(B, Hkv, T, d, m, w)),
         "adj_scan": ("mfma", 4.0 * m * d * B * H * T),
-        "rope_q": ("hbm", 2.0 * B * T * H * d * e),
-        "rope_k": ("hbm", 2.0 * B * T * Hkv * d * e),
+        "rope_cs": ("hbm", 8.0 * T * (d // 2)),
+        "rope": ("hbm", 2.0 * B * T * (H + Hkv) * d * e),
         "chunk_gates": ("hbm", 2.0 * B * T * Hkv * m * e),
         "bwd_prep": ("hbm", B * T * H * (2.0 * d * e + 4)),
         "dalpha_fix": ("hbm", B * T * Hkv * m * (e + 8.0)),

@@ -40,7 +40,7 @@ namespace nha {
 
 // ---------------------------------------------------------------- workspace
 struct BwdWs {
-  size_t sst, wt, aend, qrot, krot;  // prologue (same meaning as the forward's)
+  size_t sst, wt, aend, qrot, krot, rcs;  // prologue (same meaning as the forward's)
   size_t dt;                         // D_t: [B][H][T] float
   size_t dqs;                        // slot part of dq: [B][T][H][d] float
   size_t wp;                         // adjoint weights: [B*H][NC][2][mp][C] dtype
@@ -59,6 +59,7 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   L.aend = F.aend;
   L.qrot = F.qrot;
   L.krot = F.krot;
+  L.rcs = F.rcs;
   size_t off = F.ol;  // the forward's partial-output region is not needed here
   const size_t BH = (size_t)s.B * s.H, units = (size_t)s.B * s.Hkv, TT = (size_t)s.NC * s.C;
   L.dt = off;
@@ -795,6 +796,171 @@ __global__ __launch_bounds__(256) void k_win_bwd_dq(const T* __restrict__ qr, co
   }
 }
 
+// bf16 variant: grid (ceil(T / (32 NWV)), B*H), NWV waves x 32 queries on
+// 32x32 tiles with the query as the column, as in the forward: per 64-key tile
+//   S^T = K Q^T, dP^T = V dO^T, dl^T = P^T (dP^T - D), dq^T += K^T dl^T.
+// K and V tiles go straight to LDS (double-buffered); K is read both as row
+// fragments and transposed (ds_read_b64_tr_b16), hence the two-pattern
+// swizzle (the same for V, so that one set of offsets serves both).
+template <int D, int NWV>
+__global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
+    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vv,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dt,
+    const float* __restrict__ dqs, const float2* __restrict__ rcs, bf16* __restrict__ dq, int Tn, int H, int Hkv,
+    int w, float scale) {
+  constexpr int NT = NWV * 64, QT = 32 * NWV;
+  __shared__ bf16 kbuf[2][64 * D];
+  __shared__ bf16 vbuf[2][64 * D];
+  const int tid = threadIdx.x, W = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hf = l >> 5, c = l & 31,
+            jj = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int q0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * QT), bh = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  const int b = __builtin_amdgcn_readfirstlane(bh / H), h = __builtin_amdgcn_readfirstlane(bh % H),
+            hg = __builtin_amdgcn_readfirstlane(h / (H / Hkv));
+  const int wl = q0 + 32 * W;
+  const int tq = wl + c;
+  const bool qvalid = tq < Tn;
+  const size_t qrow = (((size_t)b * Tn + tq) * H + h) * D;
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qf[ks] = qvalid ? ld8<bf16>(qr + qrow + 16 * ks + 8 * hf) : zero8<bf16>();
+    df[ks] = qvalid ? ld8<bf16>(dO + qrow + 16 * ks + 8 * hf) : zero8<bf16>();
+  }
+  const float lse2 = qvalid ? lse[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
+  const float Dq = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  const float sl2 = scale * NHA_LOG2E;
+  floatx16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = zero16();
+  // byte offsets in a tile: row fragments (row c, logical chunk 2 ks + hf) and
+  // transposed reads (rows 4 hf + jj / 4 (+8) of each 16-row step, columns
+  // 32 dt + 16 (c / 16) + 4 (jj % 4) ..)
+  uint32_t foff[D / 16], toff[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) foff[ks] = 2 * (c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 2>(c)));
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int r = 4 * hf + (jj >> 2), d0 = 32 * dt + 16 * (c >> 4) + 4 * (jj & 3);
+    toff[dt] = 2 * (r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 2>(r)) + (d0 & 7));
+  }
+  if (w > 0) {
+    int kmin = q0 - w + 1;
+    if (kmin < 0) kmin = 0;
+    int kmax = q0 + QT - 1;
+    if (kmax > Tn - 1) kmax = Tn - 1;
+    const int jfirst = (kmin / 64) * 64;
+    const int ntiles = (kmax - jfirst) / 64 + 1;
+    const size_t ld = (size_t)Hkv * D;
+    const bf16* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
+    const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
+    const uint32_t kl = lds_addr(&kbuf[0][0]), vl = lds_addr(&vbuf[0][0]);
+    constexpr uint32_t TB = 64 * D * 2;
+    const uint32_t ldo = dma_lane_off<D, NT, 2>(tid, ld);
+    dma_tile_async<D, NT, 2>(kbase, ld, jfirst, Tn, kl, ldo, tid);
+    dma_tile_async<D, NT, 2>(vbase, ld, jfirst, Tn, vl, ldo, tid);
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int j0 = jfirst + 64 * it, cb = it & 1;
+      if (it + 1 < ntiles) {
+        dma_tile_async<D, NT, 2>(kbase, ld, j0 + 64, Tn, kl + (cb ^ 1) * TB, ldo, tid);
+        dma_tile_async<D, NT, 2>(vbase, ld, j0 + 64, Tn, vl + (cb ^ 1) * TB, ldo, tid);
+      }
+      if (wl < Tn && j0 <= wl + 31 && j0 + 63 > wl - w) {
+        const uint32_t kt = __builtin_amdgcn_readfirstlane(kl + cb * TB);
+        const uint32_t vt = __builtin_amdgcn_readfirstlane(vl + cb * TB);
+        floatx16 x[2], dp[2];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            x[kb] = mma32x32(ks == 0 ? zero16() : x[kb], ld8_at(kt + foff[ks] + kb * 64 * D), qf[ks]);
+            dp[kb] = mma32x32(ks == 0 ? zero16() : dp[kb], ld8_at(vt + foff[ks] + kb * 64 * D), df[ks]);
+          }
+        }
+        if (!((j0 + 63 <= wl) && (j0 > wl + 31 - w) && (j0 + 63 < Tn))) {
+          const int rel = j0 + 4 * hf - tq + w - 1;
+          const uint32_t span = (uint32_t)(min(0, Tn - 1 - tq) + w - 1);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if ((uint32_t)(rel + 32 * kb + 8 * (r >> 2) + (r & 3)) > span) x[kb][r] = -INFINITY;
+        }
+        bf16x8 dsf[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[kb][r] = fast_exp2(fmaf(x[kb][r], sl2, -lse2)) * (dp[kb][r] - Dq);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) dsf[st] = pack8_at<bf16>(x[st >> 1], 8 * (st & 1));
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const uint32_t a = kt + toff[dt] + 32 * st * D;
+            const bf16x4 a0 = ld_tr4_at(a), a1 = ld_tr4_at(a + 16 * D);
+            bf16x8 af;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              af[e] = a0[e];
+              af[4 + e] = a1[e];
+            }
+            acc[dt] = mma32x32(acc[dt], af, dsf[st]);
+          }
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+  if (qvalid) {
+    // acc[dt][4 i + rr] = dq_rot[32 dt + 8 i + 4 hf + rr] / scale; rotate back by R_t^T
+    constexpr int HT = D / 64 > 0 ? D / 64 : 1;  // column blocks per half (D >= 64)
+    float out[D / 32][16];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) out[dt][e] = acc[dt][e] * scale;
+    if (rcs) {
+      if constexpr (D >= 64) {
+        const float2* cs = rcs + (size_t)tq * (D / 2);
+#pragma unroll
+        for (int dt = 0; dt < HT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float2 t = cs[32 * dt + 8 * (e >> 2) + 4 * hf + (e & 3)];
+            const float x1 = out[dt][e], x2 = out[dt + HT][e];
+            out[dt][e] = x1 * t.x + x2 * t.y;
+            out[dt + HT][e] = x2 * t.x - x1 * t.y;
+          }
+      } else {
+        // D = 32: the partner of column d < 16 is d + 16, held by the same
+        // lane at entry e + 8 (8 i + 4 hf + rr with i + 2)
+        const float2* cs = rcs + (size_t)tq * (D / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 t = cs[8 * (e >> 2) + 4 * hf + (e & 3)];
+          const float x1 = out[0][e], x2 = out[0][e + 8];
+          out[0][e] = x1 * t.x + x2 * t.y;
+          out[0][e + 8] = x2 * t.x - x1 * t.y;
+        }
+      }
+    }
+    const float* sl = dqs + qrow;
+    bf16* dst = dq + qrow;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * dt + 8 * i + 4 * hf;
+        const floatx4 s4 = *reinterpret_cast<const floatx4*>(sl + d);
+        st4<bf16>(dst + d, pack4<bf16>(floatx4{out[dt][4 * i] + s4[0], out[dt][4 * i + 1] + s4[1],
+                                                out[dt][4 * i + 2] + s4[2], out[dt][4 * i + 3] + s4[3]}));
+      }
+  }
+}
+
 // ---------------------------------------------------------------- window backward: dk, dv
 // grid (ceil(T/64), B*Hkv), 4 waves x 16 keys.  Loops over the group's query
 // heads and the query tiles whose band reaches the keys.  Per query tile:
@@ -942,6 +1108,194 @@ __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
   }
 }
 
+// bf16 variant: grid (ceil(T / (32 NWV)), B*Hkv), NWV waves x 32 keys on
+// 32x32 tiles with the key as the column.  Per 32-query block of each
+// 64-query tile of each query head of the group:
+//   S' = Q K^T - lse_t / s, dP' = dO V^T - D_t   (the accumulators start at
+//        the per-query terms, read from LDS), P = 2^(s log2e S'), dl = P dP'
+//   dv^T += dO^T P, dk^T += Q^T dl               (transposed tile reads)
+// Q and dO tiles go straight to LDS (double-buffered) with the two-pattern
+// swizzle.
+template <int D, int NWV>
+__global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
+    const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vv,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dt,
+    const float* __restrict__ dkap, const float* __restrict__ dnu, const float2* __restrict__ rcs,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, int Tn, int H, int Hkv, int w, float scale) {
+  constexpr int NT = NWV * 64, KT = 32 * NWV;
+  __shared__ bf16 qbuf[2][64 * D];
+  __shared__ bf16 obuf[2][64 * D];
+  __shared__ float nlb[2][64], ndb[2][64];  // -lse_t / s and -D_t of the tile's queries
+  const int tid = threadIdx.x, W = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hf = l >> 5, c = l & 31,
+            jj = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int k0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * KT),
+            unit = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  const int b = __builtin_amdgcn_readfirstlane(unit / Hkv), hg = __builtin_amdgcn_readfirstlane(unit % Hkv),
+            G = H / Hkv;
+  const int kl = k0 + 32 * W;  // first key of this wave
+  const int key = kl + c;
+  const bool kvalid = key < Tn;
+  const size_t krow = (((size_t)b * Tn + key) * Hkv + hg) * D;
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = kvalid ? ld8<bf16>(kr + krow + 16 * ks + 8 * hf) : zero8<bf16>();
+    vf[ks] = kvalid ? ld8<bf16>(vv + krow + 16 * ks + 8 * hf) : zero8<bf16>();
+  }
+  const float sl2 = scale * NHA_LOG2E, inv_s = 1.f / scale;
+  floatx16 accK[D / 32], accV[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) accK[dt] = accV[dt] = zero16();
+  uint32_t foff[D / 16], toff[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) foff[ks] = 2 * (c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 2>(c)));
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int r = 4 * hf + (jj >> 2), d0 = 32 * dt + 16 * (c >> 4) + 4 * (jj & 3);
+    toff[dt] = 2 * (r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 2>(r)) + (d0 & 7));
+  }
+  int tmax = k0 + KT - 1 + w - 1;
+  if (tmax > Tn - 1) tmax = Tn - 1;
+  const int qfirst = (k0 / 64) * 64;
+  const int ntiles = (w > 0 && k0 <= tmax) ? (tmax - qfirst) / 64 + 1 : 0;
+  const int total = G * ntiles;
+  if (total > 0) {
+    const size_t ld = (size_t)H * D;
+    const uint32_t ql = lds_addr(&qbuf[0][0]), ol = lds_addr(&obuf[0][0]);
+    constexpr uint32_t TB = 64 * D * 2;
+    const uint32_t ldo = dma_lane_off<D, NT, 2>(tid, ld);
+    auto stage = [&](int n, int buf) {
+      const int hh = n / ntiles, q0 = qfirst + 64 * (n - hh * ntiles), h = hg * G + hh;
+      const size_t base = ((size_t)b * Tn * H + h) * D;
+      dma_tile_async<D, NT, 2>(qr + base, ld, q0, Tn, ql + buf * TB, ldo, tid);
+      dma_tile_async<D, NT, 2>(dO + base, ld, q0, Tn, ol + buf * TB, ldo, tid);
+      if (tid < 64) {
+        const int t = q0 + tid;
+        const size_t e = ((size_t)b * H + h) * Tn + t;
+        nlb[buf][tid] = t < Tn ? -lse[e] * inv_s : 0.f;
+        ndb[buf][tid] = t < Tn ? -Dt[e] : 0.f;
+      }
+    };
+    stage(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int n = 0; n < total; ++n) {
+      const int cb = n & 1;
+      if (n + 1 < total) stage(n + 1, cb ^ 1);
+      const int hh = n / ntiles, q0 = qfirst + 64 * (n - hh * ntiles);
+      const uint32_t qt = __builtin_amdgcn_readfirstlane(ql + cb * TB);
+      const uint32_t ot = __builtin_amdgcn_readfirstlane(ol + cb * TB);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qb0 = q0 + 32 * qb;
+        if (kl < Tn && qb0 < Tn && qb0 + 31 >= kl && qb0 <= kl + 31 + w - 1) {
+          floatx16 x, dp;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const floatx4 a = *reinterpret_cast<const floatx4*>(&nlb[cb][32 * qb + 8 * i + 4 * hf]);
+            const floatx4 d4 = *reinterpret_cast<const floatx4*>(&ndb[cb][32 * qb + 8 * i + 4 * hf]);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              x[4 * i + rr] = a[rr];
+              dp[4 * i + rr] = d4[rr];
+            }
+          }
+          if (!((qb0 >= kl + 31) && (qb0 + 31 <= kl + w - 1) && (qb0 + 31 < Tn))) {
+            // query - key = rel + 8 i + rr must lie in [0, min(w - 1, Tn - 1 - key)]
+            const int rel = qb0 + 4 * hf - key;
+            const int span = min(w - 1, Tn - 1 - key);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int dlt = rel + 8 * (e >> 2) + (e & 3);
+              if (dlt < 0 || dlt > span) x[e] = -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks) {
+            x = mma32x32(x, ld8_at(qt + foff[ks] + qb * 64 * D), kf[ks]);
+            dp = mma32x32(dp, ld8_at(ot + foff[ks] + qb * 64 * D), vf[ks]);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(x[e] * sl2);
+            x[e] = p;
+            dp[e] *= p;
+          }
+          const bf16x8 pf0 = pack8_at<bf16>(x, 0), pf1 = pack8_at<bf16>(x, 8);
+          const bf16x8 lf0 = pack8_at<bf16>(dp, 0), lf1 = pack8_at<bf16>(dp, 8);
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+              const uint32_t off = toff[dt] + (32 * qb + 16 * st) * D * 2;
+              const bf16x4 o0 = ld_tr4_at(ot + off), o1 = ld_tr4_at(ot + off + 16 * D);
+              const bf16x4 q0v = ld_tr4_at(qt + off), q1v = ld_tr4_at(qt + off + 16 * D);
+              bf16x8 fo, fq;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                fo[e] = o0[e];
+                fo[4 + e] = o1[e];
+                fq[e] = q0v[e];
+                fq[4 + e] = q1v[e];
+              }
+              accV[dt] = mma32x32(accV[dt], fo, st ? pf1 : pf0);
+              accK[dt] = mma32x32(accK[dt], fq, st ? lf1 : lf0);
+            }
+        }
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+  if (kvalid) {
+    constexpr int HT = D / 64 > 0 ? D / 64 : 1;
+    float ok[D / 32][16];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ok[dt][e] = accK[dt][e] * scale;
+    if (rcs) {
+      const float2* cs = rcs + (size_t)key * (D / 2);
+      if constexpr (D >= 64) {
+#pragma unroll
+        for (int dt = 0; dt < HT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float2 t = cs[32 * dt + 8 * (e >> 2) + 4 * hf + (e & 3)];
+            const float x1 = ok[dt][e], x2 = ok[dt + HT][e];
+            ok[dt][e] = x1 * t.x + x2 * t.y;
+            ok[dt + HT][e] = x2 * t.x - x1 * t.y;
+          }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 t = cs[8 * (e >> 2) + 4 * hf + (e & 3)];
+          const float x1 = ok[0][e], x2 = ok[0][e + 8];
+          ok[0][e] = x1 * t.x + x2 * t.y;
+          ok[0][e + 8] = x2 * t.x - x1 * t.y;
+        }
+      }
+    }
+    const bool slot = key + w < Tn;  // this key row is also absorbed (at step key + w)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * dt + 8 * i + 4 * hf;
+        floatx4 sk = zero4(), sv = zero4();
+        if (slot) {
+          sk = *reinterpret_cast<const floatx4*>(dkap + krow + d);
+          sv = *reinterpret_cast<const floatx4*>(dnu + krow + d);
+        }
+        st4<bf16>(dk + krow + d, pack4<bf16>(floatx4{ok[dt][4 * i] + sk[0], ok[dt][4 * i + 1] + sk[1],
+                                                     ok[dt][4 * i + 2] + sk[2], ok[dt][4 * i + 3] + sk[3]}));
+        st4<bf16>(dv + krow + d, pack4<bf16>(floatx4{accV[dt][4 * i] + sv[0], accV[dt][4 * i + 1] + sv[1],
+                                                     accV[dt][4 * i + 2] + sv[2], accV[dt][4 * i + 3] + sv[3]}));
+      }
+  }
+}
+
 // ---------------------------------------------------------------- host launcher
 template <typename T, int D, int MP, int C>
 static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st) {
@@ -959,10 +1313,11 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     const int units = s.B * s.Hkv;
     Marks mk;
     mk.ev = p.events;
-    ProloguePtrs pp{ws + L.sst, ws + L.wt, (float*)(ws + L.aend), nullptr, nullptr, nullptr, nullptr};
+    ProloguePtrs pp{ws + L.sst, ws + L.wt, (float*)(ws + L.aend), nullptr, nullptr, nullptr, nullptr, nullptr};
     if (s.rope && s.win) {
       pp.qrot = ws + L.qrot;
       pp.krot = ws + L.krot;
+      pp.rcs = (float2*)(ws + L.rcs);
     }
     hipError_t e = launch_prologue(s, th, q, k, v, alpha, pp, mk, st);
     if (e != hipSuccess) return e;
@@ -1000,11 +1355,21 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     hipLaunchKernelGGL(k_dalpha_fix<T>, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, st, alpha, carry, p.dalpha,
                        s.T, s.Hkv, s.m, MP, s.w, C, s.NC, na);
     mk.mark(st);
-    hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dqs,
-                       (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
-    mk.mark(st);
-    hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dkap,
-                       dnu, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+    if constexpr (sizeof(T) == 2) {
+      constexpr int NWV = 4;
+      const unsigned nt = (unsigned)((s.T + 32 * NWV - 1) / (32 * NWV));
+      hipLaunchKernelGGL((k_win_bwd_dq_b16<D, NWV>), dim3(nt, s.B * s.H), dim3(NWV * 64), 0, st, qr, kr, v, dO, p.lse,
+                         Dt, dqs, (const float2*)pp.rcs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale);
+      mk.mark(st);
+      hipLaunchKernelGGL((k_win_bwd_dkdv_b16<D, NWV>), dim3(nt, units), dim3(NWV * 64), 0, st, qr, kr, v, dO, p.lse,
+                         Dt, dkap, dnu, (const float2*)pp.rcs, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale);
+    } else {
+      hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt,
+                         dqs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+      mk.mark(st);
+      hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dkap,
+                         dnu, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+    }
     mk.mark(st);
     return hipGetLastError();
   }
@@ -1038,8 +1403,8 @@ int bwd_stages(const Shape& s, const char** names, int max) {
   const char* all[16];
   int n = 0;
   if (s.rope && s.win) {
-    all[n++] = "rope_q";
-    all[n++] = "rope_k";
+    all[n++] = "rope_cs";
+    all[n++] = "rope";
   }
   all[n++] = "chunk_gates";
   all[n++] = "state_scan";

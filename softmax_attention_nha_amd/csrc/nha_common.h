@@ -327,10 +327,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
+//   kind 2 (both of the above, for a 32-bank LDS): f(r) = 2 (r % 4) + (r / 4) % 2
+//                                 maps 8 consecutive rows to 8 distinct chunk
+//                                 positions and keeps the two chunks of each of
+//                                 4 aligned rows apart
 template <int D, int KIND>
 __device__ __forceinline__ int chunk_swz(int row) {
   if constexpr (KIND == 0) return row & (D / 8 - 1);
-  else return ((0xAC60 >> (4 * (row & 3))) & 15) & (D / 8 - 1);
+  else if constexpr (KIND == 1) return ((0xAC60 >> (4 * (row & 3))) & 15) & (D / 8 - 1);
+  else return (((row & 3) << 1) | ((row >> 2) & 1)) & (D / 8 - 1);
 }
 
 // Rows [j0, j0 + 64) of a bf16 operand with row stride ld (rows past Tn - 1
@@ -398,7 +403,7 @@ __device__ __forceinline__ void dma_tile_async(const bf16* __restrict__ base, si
   static_assert(NI % NW == 0, "tile instructions must split evenly over the waves");
   // rows NW RPI apart share their swizzle, so one lane offset serves every
   // instruction of the wave
-  static_assert((NW * RPI) % (KIND == 0 ? CPR : 4) == 0, "swizzle period");
+  static_assert((NW * RPI) % (KIND == 0 ? CPR : KIND == 1 ? 4 : 8) == 0, "swizzle period");
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   if (j0 + 64 <= Tn) {
     // whole tile in range: uniform row base in SGPRs, fixed per-lane offset

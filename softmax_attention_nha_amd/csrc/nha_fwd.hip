@@ -37,30 +37,46 @@
 namespace nha {
 
 // ---------------------------------------------------------------- RoPE
-// y[r] = R_pos x[r] for rows r of [B][T][heads][d]; pos = (r / heads) % T.
-// One thread rotates 8 frequency pairs (i, i + d/2).
+// cs[t][i] = (cos, sin)(t theta_i) for t < T, i < d/2; the angle is reduced
+// modulo 2 pi in double precision before the single-precision sincos.
+__global__ __launch_bounds__(256) void k_rope_cs(float2* __restrict__ cs, int Tn, int half, RopeTheta th) {
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (long)Tn * half) return;
+  const int t = (int)(e / half), i = (int)(e % half);
+  double ang = (double)t * th.theta[i];
+  ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+  float sn, cn;
+  sincosf((float)ang, &sn, &cn);
+  cs[e] = make_float2(cn, sn);
+}
+
+// y[r] = R_pos x[r] for the nq rows of q ([B][T][Hq][d]) followed by the nk
+// rows of k ([B][T][Hk][d]); pos = (r / heads) % T.  One thread rotates 8
+// frequency pairs (i, i + d/2) with the angles of the cs table.
 template <typename T>
-__global__ __launch_bounds__(256) void k_rope(const T* __restrict__ x, T* __restrict__ y,
-                                              long nrows, int heads, int Tn, int d, RopeTheta th) {
-  long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  int per = d / 16;
+__global__ __launch_bounds__(256) void k_rope(const T* __restrict__ q, const T* __restrict__ k, T* __restrict__ qo,
+                                              T* __restrict__ ko, long nq, long nk, int Hq, int Hk, int Tn, int d,
+                                              const float2* __restrict__ cs) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = d / 16;
   long r = gid / per;
-  if (r >= nrows) return;
-  int i0 = (int)(gid % per) * 8;
-  int pos = (int)((r / heads) % Tn);
-  const T* xr = x + r * d;
-  T* yr = y + r * d;
+  if (r >= nq + nk) return;
+  const bool isq = r < nq;
+  if (!isq) r -= nq;
+  const int heads = isq ? Hq : Hk;
+  const int i0 = (int)(gid % per) * 8;
+  const int pos = (int)((r / heads) % Tn);
+  const T* xr = (isq ? q : k) + r * d;
+  T* yr = (isq ? qo : ko) + r * d;
+  const float2* c = cs + (size_t)pos * (d / 2) + i0;
   float a[8], b[8], ya[8], yb[8];
   ld8f<T>(xr + i0, a);
   ld8f<T>(xr + i0 + d / 2, b);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    double ang = (double)pos * th.theta[i0 + e];
-    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-    float sn, cs;
-    sincosf((float)ang, &sn, &cs);
-    ya[e] = a[e] * cs - b[e] * sn;
-    yb[e] = b[e] * cs + a[e] * sn;
+    const float2 t = c[e];
+    ya[e] = a[e] * t.x - b[e] * t.y;
+    yb[e] = b[e] * t.x + a[e] * t.y;
   }
   st8<T>(yr + i0, pack8<T>(ya));
   st8<T>(yr + i0 + d / 2, pack8<T>(yb));
@@ -782,14 +798,13 @@ static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const
                           const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
   const int units = s.B * s.Hkv;
   if (s.rope && s.win) {
-    long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
-    long thq = nq * (s.d / 16), thk = nk * (s.d / 16);
+    const long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
+    const long ncs = (long)s.T * (s.d / 2), thr = (nq + nk) * (s.d / 16);
     mk.mark(st);
-    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thq + 255) / 256)), dim3(256), 0, st, q, (T*)pp.qrot, nq, s.H,
-                       s.T, s.d, th);
+    hipLaunchKernelGGL(k_rope_cs, dim3((unsigned)((ncs + 255) / 256)), dim3(256), 0, st, pp.rcs, s.T, s.d / 2, th);
     mk.mark(st);
-    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thk + 255) / 256)), dim3(256), 0, st, k, (T*)pp.krot, nk,
-                       s.Hkv, s.T, s.d, th);
+    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, st, q, k, (T*)pp.qrot,
+                       (T*)pp.krot, nq, nk, s.H, s.Hkv, s.T, s.d, (const float2*)pp.rcs);
   }
   mk.mark(st);
   hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend, s.T,
@@ -815,10 +830,11 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     Marks mk;
     mk.ev = p.events;
     StateLayout SL{};
-    ProloguePtrs pp{p.ws + L.sst, p.ws + L.wt, (float*)(p.ws + L.aend), nullptr, nullptr, nullptr, nullptr};
+    ProloguePtrs pp{p.ws + L.sst, p.ws + L.wt, (float*)(p.ws + L.aend), nullptr, nullptr, nullptr, nullptr, nullptr};
     if (s.rope && s.win) {
       pp.qrot = p.ws + L.qrot;
       pp.krot = p.ws + L.krot;
+      pp.rcs = (float2*)(p.ws + L.rcs);
     }
     if (p.state_out) {
       SL = state_layout(s);
@@ -919,8 +935,8 @@ int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
   const char* all[8];
   int n = 0;
   if (s.rope && s.win) {
-    all[n++] = "rope_q";
-    all[n++] = "rope_k";
+    all[n++] = "rope_cs";
+    all[n++] = "rope";
   }
   all[n++] = "chunk_gates";
   all[n++] = "state_scan";

@@ -38,6 +38,7 @@ struct FwdWs {
   size_t aend;   // per-chunk decay exp(G_end): [B*Hkv][NC][mp]                (float)
   size_t qrot;   // RoPE'd q: [B][T][H][d]                                       (dtype)
   size_t krot;   // RoPE'd k: [B][T][Hkv][d]                                     (dtype)
+  size_t rcs;    // RoPE angles (cos, sin)(t theta_i): [T][d/2]                   (float2)
   size_t ol;     // slot-branch partial output o_L / Z_L: [B][T][H][d]          (dtype)
   size_t lsel;   // slot-branch partial lse: [B][H][T]                           (float)
   size_t total;
@@ -57,6 +58,8 @@ inline FwdWs fwd_ws_layout(const Shape& s) {
   if (s.rope && s.win) off += align256((size_t)s.B * s.T * s.H * s.d * s.esz);
   L.krot = off;
   if (s.rope && s.win) off += align256((size_t)s.B * s.T * s.Hkv * s.d * s.esz);
+  L.rcs = off;
+  if (s.rope && s.win) off += align256((size_t)s.T * (s.d / 2) * 8);
   L.ol = off;
   off += align256((size_t)s.B * s.T * s.H * s.d * s.esz);
   L.lsel = off;
@@ -110,6 +113,7 @@ struct ProloguePtrs {
   float* aend;
   void* qrot;  // nullable when RoPE is off or w == 0
   void* krot;
+  float2* rcs;  // RoPE (cos, sin) table, same condition
   float* skout;  // nullable
   float* svout;
 };
