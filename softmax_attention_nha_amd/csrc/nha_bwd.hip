@@ -481,6 +481,148 @@ __global__ __launch_bounds__(64) void k_adj_scan(const T* __restrict__ q, const 
   }
 }
 
+// bf16 variant: the operands of every (chunk, query head) step -- q and dO
+// rows of the wave's 16 columns, both adjoint weight tiles, aend -- stream
+// into an LDS ring NS steps ahead with direct-to-LDS loads (as in the
+// forward scan).  Steps run over chunks in reverse and over the group's
+// heads inside a chunk; the counter wait allows only the later stages'
+// loads to be outstanding (the state stores are not counted, which can only
+// make it wait longer).
+template <int C, int MP>
+struct AdjStage {
+  static constexpr int KB = C * 32;
+  static constexpr int WB = MP * C * 2;
+  static constexpr int NK = (KB + 1023) / 1024, NWI = WB / 1024;
+  static constexpr int OPS = 2 * NK + 2 * NWI + 1;
+  bf16 q[C * 16];
+  bf16 o[C * 16];
+  bf16 wk[MP * C];  // [i][u], 16-byte chunks XOR-swizzled by i
+  bf16 wv[MP * C];
+  float ae[64];
+};
+
+template <int C, int MP, int NS>
+__global__ __launch_bounds__(64) void k_adj_scan_b16(const bf16* __restrict__ q, const bf16* __restrict__ dO,
+                                                     const bf16* __restrict__ wp, const float* __restrict__ aend,
+                                                     bf16* __restrict__ lin, int Tn, int H, int Hkv, int d,
+                                                     int NC) {
+  using St = AdjStage<C, MP>;
+  constexpr int NB = MP / 16, CPR = C / 8;
+  __shared__ St ring[NS];
+  const int l = threadIdx.x, g = l >> 4, cc = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int j0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * 16),
+            unit = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  const int b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  const int nsteps = NC * G;
+  const size_t ld = (size_t)H * d;
+  auto issue = [&](int n, int s) {
+    n = min(n, nsteps - 1);
+    const int c = NC - 1 - n / G, hh = n % G, h = hg * G + hh, bh = b * H + h;
+    const uint32_t base = lds_addr(&ring[s]);
+    const bf16* qb = q + ((size_t)b * Tn * H + h) * d + j0;
+    const bf16* ob = dO + ((size_t)b * Tn * H + h) * d + j0;
+#pragma unroll
+    for (int i = 0; i < St::NK; ++i) {
+      const int e = i * 64 + l, u = e >> 1;
+      const int tr = min(c * C + u, Tn - 1);
+      const uint32_t off = (uint32_t)((size_t)tr * ld * 2 + 16 * (e & 1));
+      const uint32_t mq = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, q) + i * 1024);
+      const uint32_t mo = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, o) + i * 1024);
+      if (e * 16 < St::KB) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(mq), "v"(off), "s"(sgpr_ptr(qb))
+                     : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(mo), "v"(off), "s"(sgpr_ptr(ob))
+                     : "memory", "m0");
+      }
+    }
+    const bf16* wks = wp + (((size_t)bh * NC + c) * 2) * MP * C;
+    const bf16* wvs = wks + (size_t)MP * C;
+#pragma unroll
+    for (int i = 0; i < St::NWI; ++i) {
+      const int e = i * 64 + l, r = e / CPR, p = e % CPR;
+      const uint32_t off = (uint32_t)(16 * (r * CPR + (p ^ (r & (CPR - 1)))));
+      const uint32_t mk = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, wk) + i * 1024);
+      const uint32_t mv = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, wv) + i * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(mk), "v"(off), "s"(sgpr_ptr(wks))
+                   : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(mv), "v"(off), "s"(sgpr_ptr(wvs))
+                   : "memory", "m0");
+    }
+    {
+      const uint32_t off = (uint32_t)(4 * min(l, MP - 1));
+      const uint32_t ma = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, ae));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                   :
+                   : "s"(ma), "v"(off), "s"(sgpr_ptr(aend + ((size_t)unit * NC + c) * MP))
+                   : "memory", "m0");
+    }
+  };
+  floatx4 LK[NB], LV[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) LK[nb] = LV[nb] = zero4();
+  for (int s = 0; s < NS; ++s) issue(s, s);
+  for (int n = 0; n < nsteps; ++n) {
+    const int s = n % NS, c = NC - 1 - n / G, hh = n % G;
+    vm_wait<(NS - 1) * St::OPS>();
+    const St& R = ring[s];
+    if (hh == 0) {
+      // the adjoint entering chunk c from the right, [i][d] layout
+      bf16* dst = lin + ((size_t)unit * NC + c) * 2 * MP * d;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int i = 16 * nb + cc;
+        st4<bf16>(dst + (size_t)i * d + j0 + 4 * g, pack4<bf16>(LK[nb]));
+        st4<bf16>(dst + (size_t)MP * d + (size_t)i * d + j0 + 4 * g, pack4<bf16>(LV[nb]));
+        const float a = R.ae[i];
+        LK[nb] *= a;
+        LV[nb] *= a;
+      }
+    }
+    if constexpr (C % 32 != 0) {
+      const bf16x4 aq = ld_tr4(R.q + (4 * g + (cc >> 2)) * 16 + 4 * (cc & 3));
+      const bf16x4 ao = ld_tr4(R.o + (4 * g + (cc >> 2)) * 16 + 4 * (cc & 3));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int i = 16 * nb + cc, woff = i * C + 8 * ((g >> 1) ^ (i & (CPR - 1))) + 4 * (g & 1);
+        LK[nb] = mma16(LK[nb], aq, *reinterpret_cast<const bf16x4*>(R.wk + woff));
+        LV[nb] = mma16(LV[nb], ao, *reinterpret_cast<const bf16x4*>(R.wv + woff));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < C / 32; ++ks) {
+      const bf16* qp = R.q + (32 * ks + 8 * g + (cc >> 2)) * 16 + 4 * (cc & 3);
+      const bf16* op = R.o + (32 * ks + 8 * g + (cc >> 2)) * 16 + 4 * (cc & 3);
+      const bf16x4 q0 = ld_tr4(qp), q1 = ld_tr4(qp + 4 * 16), o0 = ld_tr4(op), o1 = ld_tr4(op + 4 * 16);
+      bf16x8 aq, ao;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        aq[e] = q0[e];
+        aq[4 + e] = q1[e];
+        ao[e] = o0[e];
+        ao[4 + e] = o1[e];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int i = 16 * nb + cc, woff = i * C + 8 * ((4 * ks + g) ^ (i & (CPR - 1)));
+        LK[nb] = mma32(LK[nb], aq, *reinterpret_cast<const bf16x8*>(R.wk + woff));
+        LV[nb] = mma32(LV[nb], ao, *reinterpret_cast<const bf16x8*>(R.wv + woff));
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(n + NS, s);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ---------------------------------------------------------------- slot pass B
 template <typename T, int D, int MP, int C>
 struct SlotBwdBSmem {
@@ -1343,8 +1485,12 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
                        dO, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w, s.NC,
                        s.scale);
     mk.mark(st);
-    hipLaunchKernelGGL((k_adj_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
-                       (const float*)pp.aend, lin, s.T, s.H, s.Hkv, D, s.NC);
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((k_adj_scan_b16<C, MP, 3>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
+                         (const float*)pp.aend, lin, s.T, s.H, s.Hkv, D, s.NC);
+    else
+      hipLaunchKernelGGL((k_adj_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
+                         (const float*)pp.aend, lin, s.T, s.H, s.Hkv, D, s.NC);
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
                        (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.w, s.NC);

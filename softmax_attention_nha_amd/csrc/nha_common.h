@@ -436,3 +436,26 @@ __device__ __forceinline__ void dma_tile_async(const bf16* __restrict__ base, si
     }
   }
 }
+
+// Vector-memory counter wait of step c of a ring pipeline: NS stages of OPS
+// loads were issued up front, and every step then issued STO stores and the
+// OPS loads of a new stage.  Operations complete in issue order, so this
+// waits exactly for the loads of stage c.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+template <int NS, int OPS, int STO>
+__device__ __forceinline__ void vm_wait_steps(int c) {
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  if (c >= NS - 1) {
+    vm_wait<(NS - 1) * (OPS + STO)>();
+  } else if (c == 0) {
+    vm_wait<(NS - 1) * OPS>();
+  } else if (c == 1) {
+    vm_wait<(NS - 1) * OPS + STO>();
+  } else {
+    vm_wait<(NS - 1) * OPS + 2 * STO>();
+  }
+}

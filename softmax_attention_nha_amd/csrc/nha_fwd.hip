@@ -240,6 +240,168 @@ __global__ __launch_bounds__(64) void k_state_scan(const T* __restrict__ kk, con
   }
 }
 
+// bf16 variant: the chunk operands of the wave's 16 columns (kappa and nu
+// rows, W^T, aend) stream into an LDS ring NS chunks ahead with direct-to-LDS
+// loads, so that a step only waits for loads issued NS - 1 steps earlier.
+// Every step issues the same number of vector-memory operations (the state
+// stores, then the loads of chunk c + NS, clamped to the last chunk past the
+// end), and vector-memory operations complete in issue order, so one counter
+// wait covers exactly the loads of the current chunk.
+template <int C, int MP>
+struct ScanStage {
+  static constexpr int KB = C * 32;           // kappa / nu rows: [u][16 columns]
+  static constexpr int WB = MP * C * 2;       // W^T [i][u], 16-byte chunks XOR-swizzled by i
+  static constexpr int NK = (KB + 1023) / 1024, NWI = WB / 1024;
+  static constexpr int OPS = 2 * NK + NWI + 1;  // direct loads per chunk (+1: aend)
+  bf16 k[C * 16];
+  bf16 v[C * 16];
+  bf16 wt[MP * C];
+  float ae[64];
+};
+
+template <int C, int MP, int NS>
+__global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ kk, const bf16* __restrict__ vv,
+                                                       const bf16* __restrict__ Wt, const float* __restrict__ aend,
+                                                       bf16* __restrict__ sst, float* __restrict__ skout,
+                                                       float* __restrict__ svout, int Tn, int Hkv, int d, int m,
+                                                       int w, int NC) {
+  using St = ScanStage<C, MP>;
+  constexpr int NB = MP / 16, CPR = C / 8;  // W^T 16-byte chunks per row
+  __shared__ St ring[NS];
+  const int l = threadIdx.x, g = l >> 4, cc = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int j0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * 16),
+            unit = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  const int b = unit / Hkv, hg = unit % Hkv;
+  const size_t ld = (size_t)Hkv * d;
+  const bf16* kbase = kk + ((size_t)b * Tn * Hkv + hg) * d + j0;
+  const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * d + j0;
+  // issue the direct loads of chunk c (clamped) into ring slot s
+  auto issue = [&](int c, int s) {
+    c = min(c, NC - 1);
+    const uint32_t base = lds_addr(&ring[s]);
+#pragma unroll
+    for (int i = 0; i < St::NK; ++i) {
+      // 32 rows per instruction, two 16-byte halves per row; absorbed row
+      // t - w of chunk row u (rows outside [0, T) are clamped: their weight is 0)
+      const int e = i * 64 + l, u = e >> 1;
+      const int tr = min(max(c * C + u - w, 0), Tn - 1);
+      const uint32_t off = (uint32_t)((size_t)tr * ld * 2 + 16 * (e & 1));
+      const bool act = e * 16 < St::KB;
+      const uint32_t mk = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, k) + i * 1024);
+      const uint32_t mv = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, v) + i * 1024);
+      if (act) {  // (C = 16: half a wave; still one instruction each)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(mk), "v"(off), "s"(sgpr_ptr(kbase))
+                     : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(mv), "v"(off), "s"(sgpr_ptr(vbase))
+                     : "memory", "m0");
+      }
+    }
+    const bf16* wsrc = Wt + ((size_t)unit * NC + c) * MP * C;
+#pragma unroll
+    for (int i = 0; i < St::NWI; ++i) {
+      const int e = i * 64 + l, r = e / CPR, p = e % CPR;
+      const uint32_t off = (uint32_t)(16 * (r * CPR + (p ^ (r & (CPR - 1)))));
+      const uint32_t mw = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, wt) + i * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(mw), "v"(off), "s"(sgpr_ptr(wsrc))
+                   : "memory", "m0");
+    }
+    {
+      const uint32_t off = (uint32_t)(4 * min(l, MP - 1));
+      const uint32_t ma = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, ae));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                   :
+                   : "s"(ma), "v"(off), "s"(sgpr_ptr(aend + ((size_t)unit * NC + c) * MP))
+                   : "memory", "m0");
+    }
+  };
+  floatx4 SK[NB], SV[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) SK[nb] = SV[nb] = zero4();
+  const size_t chunk_elems = 2 * (size_t)MP * d;
+  for (int s = 0; s < NS; ++s) issue(s, s);
+  for (int c = 0; c < NC; ++c) {
+    const int s = c % NS;
+    // loads of chunk c done: the later chunks' loads (St::OPS each) and the
+    // state stores of the steps since (2 NB each) may still be in flight
+    vm_wait_steps<NS, St::OPS, 2 * NB>(c);
+    const St& R = ring[s];
+    // state at the chunk start, [i][d] layout for both halves
+    bf16* dst = sst + ((size_t)unit * NC + c) * chunk_elems;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int i = 16 * nb + cc;
+      st4<bf16>(dst + (size_t)i * d + j0 + 4 * g, pack4<bf16>(SK[nb]));
+      st4<bf16>(dst + (size_t)MP * d + (size_t)i * d + j0 + 4 * g, pack4<bf16>(SV[nb]));
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float a = R.ae[16 * nb + cc];
+      SK[nb] *= a;
+      SV[nb] *= a;
+    }
+    // dS^T[col][i] += sum_u kappa^T[col][u] W^T[i][u]: A = kappa^T (transposed
+    // reads of the row-major tile), B = W^T rows
+    if constexpr (C % 32 != 0) {
+      // C = 16: one K=16 step
+      const bf16x4 ak = ld_tr4(R.k + (4 * g + (cc >> 2)) * 16 + 4 * (cc & 3));
+      const bf16x4 av = ld_tr4(R.v + (4 * g + (cc >> 2)) * 16 + 4 * (cc & 3));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int i = 16 * nb + cc;
+        const bf16x4 wf = *reinterpret_cast<const bf16x4*>(R.wt + i * C + 8 * ((g >> 1) ^ (i & (CPR - 1))) +
+                                                           4 * (g & 1));
+        SK[nb] = mma16(SK[nb], ak, wf);
+        SV[nb] = mma16(SV[nb], av, wf);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < C / 32; ++ks) {
+      const bf16* kp = R.k + (32 * ks + 8 * g + (cc >> 2)) * 16 + 4 * (cc & 3);
+      const bf16* vp = R.v + (32 * ks + 8 * g + (cc >> 2)) * 16 + 4 * (cc & 3);
+      const bf16x4 k0 = ld_tr4(kp), k1 = ld_tr4(kp + 4 * 16), v0 = ld_tr4(vp), v1 = ld_tr4(vp + 4 * 16);
+      bf16x8 ak, av;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ak[e] = k0[e];
+        ak[4 + e] = k1[e];
+        av[e] = v0[e];
+        av[4 + e] = v1[e];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int i = 16 * nb + cc, q = 4 * ks + g;
+        const bf16x8 wf = *reinterpret_cast<const bf16x8*>(R.wt + i * C + 8 * (q ^ (i & (CPR - 1))));
+        SK[nb] = mma32(SK[nb], ak, wf);
+        SV[nb] = mma32(SV[nb], av, wf);
+      }
+    }
+    // slot s is free again once its reads have completed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(c + NS, s);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (skout) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int i = 16 * nb + cc;
+      if (i < m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          skout[((size_t)unit * m + i) * d + j0 + 4 * g + r] = SK[nb][r];
+          svout[((size_t)unit * m + i) * d + j0 + 4 * g + r] = SV[nb][r];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- slot branch
 // grid (NC, B*H), C/16 waves; wave I owns chunk rows 16I .. 16I+15 (queries
 // are the N = 16 columns of every product).  Outputs the normalised slot
@@ -810,8 +972,12 @@ static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const
   hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend, s.T,
                      s.Hkv, s.m, s.w, s.NC);
   mk.mark(st);
-  hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                     (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
+                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
+  else
+    hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
+                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
 }
 
 template <typename T, int D, int MP, int C>
