@@ -62,6 +62,21 @@ RopeTheta make_theta(const nha_desc* d) {
 
 }  // namespace
 
+namespace nha {
+int device_cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace nha
+
+
 extern "C" {
 
 const char* nha_status_string(nha_status s) {

@@ -419,97 +419,130 @@ struct SlotFwdSmem {
   float sG[C * SlotPitch<MP>::PG]; // log2 cumsum [u][i]
 };
 
+// Operands of one (chunk, head) item held in registers between their global
+// loads and their LDS stores, so that the next item's loads run while the
+// current item is computed.
+template <typename T, int D, int MP, int C, int NT>
+struct SlotFwdRegs {
+  static constexpr int NG = (C * MP + NT - 1) / NT;
+  RowTile<T, D, NT, MP> tsk;
+  PairTileT<T, D, NT, MP> tsv;
+  RowTile<T, D, NT, C> tkap;
+  PairTileT<T, D, NT, C> tnu;
+  T al[NG];
+};
+
+// grid: a persistent set of workgroups (about one per compute unit), C/16
+// waves each, looping over the items (chunk c, head b*H + h); wave I owns
+// chunk rows 16I .. 16I+15 (queries are the N = 16 columns of every product).
+// Outputs the normalised slot partial o_L / Z_L and lse_L = ln(sum_i exp(l_i))
+// over the m slot logits.
 template <typename T, int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
     const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
     const T* __restrict__ sst, T* __restrict__ oL, float* __restrict__ lseL, int Tn, int H, int Hkv, int m,
-    int w, int NC, float scale) {
+    int w, int NC, int nitems, float scale) {
   using S = SlotFwdSmem<T, D, MP, C>;
   constexpr int NW = C / 16, NT = NW * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
   constexpr int PG = SlotPitch<MP>::PG;
+  using R_t = SlotFwdRegs<T, D, MP, C, NT>;
   __shared__ S sm;
   const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
-  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, G = H / Hkv, hg = h / G;
-  const int unit = b * Hkv + hg, t0 = c * C;
-
-  // ---- cooperative loads
-  {
+  const int G = H / Hkv;
+  R_t R;
+  // item n: chunk n % NC of head n / NC
+  auto load = [&](int n) {
+    const int c = n % NC, bh = n / NC, b = bh / H, hg = (bh % H) / G, unit = b * Hkv + hg, t0 = c * C;
     const T* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
-    RowTile<T, D, NT, MP> tsk;
-    PairTileT<T, D, NT, MP> tsv;
-    tsk.load(src, D, 0, MP, tid);
-    tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
+    R.tsk.load(src, D, 0, MP, tid);
+    R.tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
     // chunk row u <-> token t0 + u, absorbing key row t0 + u - w when t0 + u >= w
     const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
-    const T* kb = kk + rbase * D;
-    const T* vb = vv + rbase * D;
-    RowTile<T, D, NT, C> tkap;
-    PairTileT<T, D, NT, C> tnu;
-    tkap.load(kb, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    tnu.load(vb, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    stage_gates<T, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
-    tsk.template store<PD>(sm.sSK, tid);
-    tsv.template store<PM>(sm.sSVt, tid);
-    tkap.template store<PD>(sm.sK, tid);
-    tnu.template store<PC>(sm.sVt, tid);
-  }
-  __syncthreads();
-  lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
-  // B^(J)[u][i] = 2^{E_J - G_u} b_u, E_J = G at the last row of u's block
-  for (int e = tid; e < C * MP; e += NT) {
-    int u = e / MP, i = e % MP, t = t0 + u;
-    int last = (u | 15);
-    float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sm.sA[u * PM + i]) : 0.f;
-    float val = fast_exp2(sm.sG[last * PG + i] - sm.sG[u * PG + i]) * be;
-    T tv = to_t<T>(val);
-    sm.sB[u * PM + i] = tv;
-    sm.sBt[i * PC + u] = tv;
-  }
-  __syncthreads();
+    R.tkap.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    R.tnu.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+#pragma unroll
+    for (int k = 0; k < R_t::NG; ++k) {
+      const int e = tid + k * NT, u = e / MP, i = e % MP, t = t0 + u;
+      R.al[k] = (e < C * MP && i < m && t < Tn) ? alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i] : to_t<T>(1.f);
+    }
+  };
+  if ((int)blockIdx.x < nitems) load(blockIdx.x);
+  for (int n = blockIdx.x; n < nitems; n += gridDim.x) {
+    const int c = n % NC, bh = n / NC, b = bh / H, h = bh % H, t0 = c * C;
+    __syncthreads();  // the previous item's LDS reads are done
+    R.tsk.template store<PD>(sm.sSK, tid);
+    R.tsv.template store<PM>(sm.sSVt, tid);
+    R.tkap.template store<PD>(sm.sK, tid);
+    R.tnu.template store<PC>(sm.sVt, tid);
+    // gates: la[u][i] = log2 a_u (0 where nothing is absorbed), raw alpha
+#pragma unroll
+    for (int k = 0; k < R_t::NG; ++k) {
+      const int e = tid + k * NT, u = e / MP, i = e % MP, t = t0 + u;
+      if (e < C * MP) {
+        sm.sA[u * PM + i] = R.al[k];
+        sm.sG[u * PG + i] =
+            (i < m && t < Tn && t >= w) ? fmaxf(__log2f(to_f<T>(R.al[k])), NHA_LOG2A_MIN) : 0.f;
+      }
+    }
+    __syncthreads();
+    if (n + (int)gridDim.x < nitems) load(n + gridDim.x);  // in flight during this item
+    lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
+    // B^(J)[u][i] = 2^{E_J - G_u} b_u, E_J = G at the last row of u's block
+    for (int e = tid; e < C * MP; e += NT) {
+      int u = e / MP, i = e % MP, t = t0 + u;
+      int last = (u | 15);
+      float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sm.sA[u * PM + i]) : 0.f;
+      float val = fast_exp2(sm.sG[last * PG + i] - sm.sG[u * PG + i]) * be;
+      T tv = to_t<T>(val);
+      sm.sB[u * PM + i] = tv;
+      sm.sBt[i * PC + u] = tv;
+    }
+    __syncthreads();
 
-  // ---- per-wave work: query rows r0 .. r0+15 of the chunk
-  const int r0 = 16 * I;
-  const int tq = t0 + r0 + cc;  // this lane's query
-  const bool qvalid = tq < Tn;
-  typename Vec<T>::v8 qf[D / 32];
+    // ---- per-wave work: query rows r0 .. r0+15 of the chunk
+    const int r0 = 16 * I;
+    const int tq = t0 + r0 + cc;  // this lane's query
+    const bool qvalid = tq < Tn;
+    typename Vec<T>::v8 qf[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = qvalid ? ld8<T>(q + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<T>();
-  float lg[NB][4];
-  slot_read<T, D, MP, C>(sm.sSK, sm.sK, sm.sBt, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
-  // softmax partial over the m slots (log2 domain)
-  const float sl2 = scale * NHA_LOG2E;
-  float mx = -INFINITY;
+    for (int ks = 0; ks < D / 32; ++ks)
+      qf[ks] = qvalid ? ld8<T>(q + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<T>();
+    float lg[NB][4];
+    slot_read<T, D, MP, C>(sm.sSK, sm.sK, sm.sBt, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+    // softmax partial over the m slots (log2 domain)
+    const float sl2 = scale * NHA_LOG2E;
+    float mx = -INFINITY;
 #pragma unroll
-  for (int mb = 0; mb < NB; ++mb)
+    for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int i = 16 * mb + 4 * g + r;
-      lg[mb][r] = (i < m) ? lg[mb][r] * sl2 : -INFINITY;
-      mx = fmaxf(mx, lg[mb][r]);
+      for (int r = 0; r < 4; ++r) {
+        int i = 16 * mb + 4 * g + r;
+        lg[mb][r] = (i < m) ? lg[mb][r] * sl2 : -INFINITY;
+        mx = fmaxf(mx, lg[mb][r]);
+      }
+    mx = max_over_g(mx);
+    float zs = 0.f;
+    float p[NB][4];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[mb][r] = fast_exp2(lg[mb][r] - mx);
+        zs += p[mb][r];
+      }
+    zs = sum_over_g(zs);
+    floatx4 accO[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
+    slot_mix<T, D, MP, C, PC>(sm.sSVt, sm.sVt, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO);
+    // normalised partial + its lse
+    if (qvalid) {
+      float inv = 1.f / zs;
+      T* dst = oL + (((size_t)b * Tn + tq) * H + h) * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db] * inv));
+      if (g == 0) lseL[((size_t)b * H + h) * Tn + tq] = (mx + __log2f(zs)) * NHA_LN2;
     }
-  mx = max_over_g(mx);
-  float zs = 0.f;
-  float p[NB][4];
-#pragma unroll
-  for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[mb][r] = fast_exp2(lg[mb][r] - mx);
-      zs += p[mb][r];
-    }
-  zs = sum_over_g(zs);
-  floatx4 accO[D / 16];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
-  slot_mix<T, D, MP, C, PC>(sm.sSVt, sm.sVt, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO);
-  // normalised partial + its lse
-  if (qvalid) {
-    float inv = 1.f / zs;
-    T* dst = oL + (((size_t)b * Tn + tq) * H + h) * D;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db] * inv));
-    if (g == 0) lseL[((size_t)b * H + h) * Tn + tq] = (mx + __log2f(zs)) * NHA_LN2;
   }
 }
 
@@ -1011,8 +1044,12 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
     mk.mark(st);
-    hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
-                       (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
+    {
+      const int nitems = s.NC * s.B * s.H;
+      const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
+      hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
+                         (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, nitems, s.scale);
+    }
     mk.mark(st);
     if constexpr (sizeof(T) == 2) {
       hipLaunchKernelGGL((k_win_fwd_b16<D, kWinWaves>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),

@@ -120,6 +120,10 @@ struct ProloguePtrs {
 hipError_t launch_prologue(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
                            const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st);
 
+// Compute units of the current device (cached per device); persistent
+// kernels size their grids with it.
+int device_cu_count();
+
 // Each returns hipSuccess or the launch error.  All launches go on `st`.
 struct FwdPtrs {
   const void *q, *k, *v, *alpha;
