@@ -292,42 +292,71 @@ struct SlotBwdASmem {
   float sG[C * SlotPitch<MP>::PG];
 };
 
-// grid (NC, B*H), C/16 waves.
+template <typename T, int D, int MP, int C, int NT>
+struct SlotBwdARegs {
+  static constexpr int NG = (C * MP + NT - 1) / NT;
+  RowTile<T, D, NT, MP> tsk, tsv;
+  PairTileT<T, D, NT, MP> tskt;
+  RowTile<T, D, NT, C> tk, tv;
+  PairTileT<T, D, NT, C> tkt;
+  T al[NG];
+};
+
+// grid: a persistent set of workgroups (about one per compute unit), C/16
+// waves each, looping over the items (chunk c, head b*H + h) with the next
+// item's operands loaded while the current one is computed.
 template <typename T, int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
     const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
     const T* __restrict__ dO, const T* __restrict__ sst, const float* __restrict__ lse,
     const float* __restrict__ Dt, float* __restrict__ dqs, T* __restrict__ wp, float* __restrict__ sdl,
-    float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m, int w, int NC, float scale) {
+    float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m, int w, int NC, int nitems,
+    float scale) {
   using S = SlotBwdASmem<T, D, MP, C>;
   constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
   constexpr int PG = SlotPitch<MP>::PG;
+  using R_t = SlotBwdARegs<T, D, MP, C, NT>;
   __shared__ S sm;
   const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
-  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, hg = h / (H / Hkv);
-  const int unit = b * Hkv + hg, t0 = c * C;
-  {
+  const int G = H / Hkv;
+  R_t R;
+  auto load = [&](int n) {
+    const int c = n % NC, bh = n / NC, b = bh / H, hg = (bh % H) / G, unit = b * Hkv + hg, t0 = c * C;
     const T* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
-    RowTile<T, D, NT, MP> tsk, tsv;
-    PairTileT<T, D, NT, MP> tskt;
-    tsk.load(src, D, 0, MP, tid);
-    tskt.load(src, D, 0, MP, tid);
-    tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
+    R.tsk.load(src, D, 0, MP, tid);
+    R.tskt.load(src, D, 0, MP, tid);
+    R.tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
     const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
-    RowTile<T, D, NT, C> tk, tv;
-    PairTileT<T, D, NT, C> tkt;
-    tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    tkt.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    tv.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    stage_gates<T, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
-    tsk.template store<PD>(sm.sSK, tid);
-    tskt.template store<PM>(sm.sSKt, tid);
-    tsv.template store<PD>(sm.sSV, tid);
-    tk.template store<PD>(sm.sK, tid);
-    tkt.template store<PC>(sm.sKt, tid);
-    tv.template store<PD>(sm.sV, tid);
+    R.tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    R.tkt.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    R.tv.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+#pragma unroll
+    for (int k = 0; k < R_t::NG; ++k) {
+      const int e = tid + k * NT, u = e / MP, i = e % MP, t = t0 + u;
+      R.al[k] = (e < C * MP && i < m && t < Tn) ? alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i] : to_t<T>(1.f);
+    }
+  };
+  if ((int)blockIdx.x < nitems) load(blockIdx.x);
+  for (int n = blockIdx.x; n < nitems; n += gridDim.x) {
+  const int c = n % NC, bh = n / NC, b = bh / H, h = bh % H;
+  const int t0 = c * C;
+  __syncthreads();  // the previous item's LDS reads are done
+  R.tsk.template store<PD>(sm.sSK, tid);
+  R.tskt.template store<PM>(sm.sSKt, tid);
+  R.tsv.template store<PD>(sm.sSV, tid);
+  R.tk.template store<PD>(sm.sK, tid);
+  R.tkt.template store<PC>(sm.sKt, tid);
+  R.tv.template store<PD>(sm.sV, tid);
+#pragma unroll
+  for (int k = 0; k < R_t::NG; ++k) {
+    const int e = tid + k * NT, u = e / MP, i = e % MP, t = t0 + u;
+    if (e < C * MP) {
+      sm.sA[u * PM + i] = R.al[k];
+      sm.sG[u * PG + i] = (i < m && t < Tn && t >= w) ? fmaxf(__log2f(to_f<T>(R.al[k])), NHA_LOG2A_MIN) : 0.f;
+    }
   }
   __syncthreads();
+  if (n + (int)gridDim.x < nitems) load(n + gridDim.x);  // in flight during this item
   lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
   for (int e = tid; e < C * MP; e += NT) {
     int u = e / MP, i = e % MP, t = t0 + u;
@@ -397,6 +426,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
       wk[(size_t)i * C + urow] = to_t<T>(e * scale * dl[mb][r]);
       wv[(size_t)i * C + urow] = to_t<T>(e * p[mb][r]);
     }
+  }
 }
 
 // ---------------------------------------------------------------- adjoint scan
@@ -1481,9 +1511,13 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
                        (const T*)p.o, dO, Dt, s.T, s.H, nrows);
     mk.mark(st);
-    hipLaunchKernelGGL((k_bwd_slot_a<T, D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
-                       dO, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w, s.NC,
-                       s.scale);
+    {
+      const int nitems = s.NC * s.B * s.H;
+      const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
+      hipLaunchKernelGGL((k_bwd_slot_a<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
+                         (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w, s.NC,
+                         nitems, s.scale);
+    }
     mk.mark(st);
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL((k_adj_scan_b16<C, MP, 3>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
