@@ -5,11 +5,14 @@
 
 A step is one pass of the whole training hot path over one batch of synthetic
 input already resident in HBM: nha_fwd (RoPE, gate prep, slot-state scan, slot
-branch, window branch) followed by nha_bwd.  K steps are timed with HIP events
-between two device synchronisations; each kernel launch is also bracketed by
-HIP events recorded by the library on the same stream (nha_fwd_timed /
-nha_bwd_timed), which gives the live per-kernel durations used for the
-roofline of the dominant kernel.  Prints ONE JSON line.
+branch, window branch) followed by its backward, nha_bwd_after_fwd with the
+forward's workspace (the backward reads the forward's RoPE'd q/k, gate
+products and chunk-start states instead of recomputing them, as a training
+step keeps forward intermediates).  K steps are timed with HIP events between
+two device synchronisations; each kernel launch is also bracketed by HIP
+events recorded by the library on the same stream (nha_fwd_timed /
+nha_bwd_after_fwd_timed), which gives the live per-kernel durations used for
+the roofline of the dominant kernel.  Prints ONE JSON line.
 
 Workload (default): the 1.3B-scale layer shape at 8K tokens -- B=4, H=Hkv=16,
 T=8192, d=128, m=64 slots, w=512, C=64, bf16 inputs with fp32 accumulation,
@@ -183,7 +186,7 @@ def main():
              torch.empty((wl.B, wl.T, wl.Hkv, wl.m), dtype=torch.float32, device=dev))
     fstages = nha.stage_names(desc)
     do_bwd = not args.fwd_only
-    bstages = nha.stage_names(desc, backward=True) if do_bwd else []
+    bstages = nha.stage_names(desc, backward=2) if do_bwd else []
 
     def new_events(n):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -196,7 +199,7 @@ def main():
                 events=[x.cuda_event for x in fev] if fev else None)
         if do_bwd:
             nha.bwd(qd, kd, vd, ad, o, lse, dOd, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=grads,
-                    events=[x.cuda_event for x in bev] if bev else None)
+                    events=[x.cuda_event for x in bev] if bev else None, after_fwd=True)
 
     for _ in range(args.warmup):
         step()

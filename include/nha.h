@@ -19,7 +19,8 @@
  *   nha_fwd          chunkwise-parallel forward over a whole sequence (the
  *                    "Chunkwise 并行计算" section of the Paper-Notes page);
  *   nha_bwd          gradients dq, dk, dv, dalpha of the same forward
- *                    (training, ibid. 局限与展望: the chunk kernel serves training);
+ *                    (training, ibid. 局限与展望: the chunk kernel serves training;
+ *                    nha_bwd_after_fwd reuses the forward's workspace);
  *   nha_decode_step  one token of recurrent ("RNN mode") inference
  *                    (ibid. 局限与展望; ai.info page, "Why This Matters").
  *
@@ -37,7 +38,8 @@
  *
  * Ownership: the caller allocates every buffer, including the workspace and
  * the decode state.  The library never allocates, frees or synchronises, keeps
- * no global mutable state, and only enqueues work on the caller's stream
+ * no global mutable state (apart from a per-device cache of the compute-unit
+ * count, used to size persistent grids), and only enqueues work on the caller's stream
  * (`stream` is a hipStream_t passed as void*; NULL = the null stream).  Calls
  * return before the GPU has run; buffers must stay alive until the stream work
  * completes.  Calls on distinct buffers are thread-safe.
@@ -131,6 +133,20 @@ nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k,
                    void* dv, float* dalpha, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* nha_bwd for a workspace that still holds the forward's intermediates.
+ * Precondition: `ws` is the workspace of the nha_fwd call that produced o
+ * and lse for these same inputs and descriptor, and nothing has written to
+ * it since (ws_bytes must still be >= nha_bwd_workspace_size).  The forward's
+ * first stages -- RoPE of q and k, the per-chunk gate products and the slot
+ * state at every chunk start -- are then read from the workspace instead of
+ * being recomputed; results are bitwise identical to nha_bwd.  Violating the
+ * precondition gives wrong gradients without an error. */
+nha_status nha_bwd_after_fwd(const nha_desc* desc, const void* q,
+                             const void* k, const void* v, const void* alpha,
+                             const void* o, const float* lse, const void* dO,
+                             void* dq, void* dk, void* dv, float* dalpha,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* One recurrent step at the position stored in the state (per (b, g)).
  *   q_t [B][H][d], k_t, v_t [B][Hkv][d], alpha_t [B][Hkv][m]  (desc->dtype)
  *   state           in/out decode state (see nha_decode_state_size)
@@ -145,8 +161,9 @@ nha_status nha_decode_step(const nha_desc* desc, const void* q_t,
                            void* stream);
 
 /* ---------------------------------------------------------------- timing
- * Kernel launches that one nha_fwd (backward = 0) or nha_bwd (backward = 1)
- * call enqueues for this descriptor (with_state: nha_fwd with a non-NULL
+ * Kernel launches that one nha_fwd (backward = 0), nha_bwd (backward = 1) or
+ * nha_bwd_after_fwd (backward = 2) call enqueues for this descriptor
+ * (with_state: nha_fwd with a non-NULL
  * state_out), in launch order.  Up to `max` static names are stored in
  * `names` (nullable).  Returns the number of launches, or -1 for an invalid
  * descriptor. */
@@ -168,6 +185,13 @@ nha_status nha_bwd_timed(const nha_desc* desc, const void* q, const void* k,
                          const float* lse, const void* dO, void* dq, void* dk,
                          void* dv, float* dalpha, void* ws, size_t ws_bytes,
                          void* stream, void* const* events);
+nha_status nha_bwd_after_fwd_timed(const nha_desc* desc, const void* q,
+                                   const void* k, const void* v,
+                                   const void* alpha, const void* o,
+                                   const float* lse, const void* dO, void* dq,
+                                   void* dk, void* dv, float* dalpha, void* ws,
+                                   size_t ws_bytes, void* stream,
+                                   void* const* events);
 
 /* Static string for a status code. */
 const char* nha_status_string(nha_status s);

@@ -35,6 +35,8 @@ EXPORTED = (
     "nha_stage_names",
     "nha_fwd_timed",
     "nha_bwd_timed",
+    "nha_bwd_after_fwd",
+    "nha_bwd_after_fwd_timed",
 )
 
 
@@ -96,6 +98,11 @@ def load():
     lib.nha_fwd_timed.restype = st
     lib.nha_bwd_timed.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]
     lib.nha_bwd_timed.restype = st
+    lib.nha_bwd_after_fwd.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.nha_bwd_after_fwd.restype = st
+    lib.nha_bwd_after_fwd_timed.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                            ctypes.POINTER(vp)]
+    lib.nha_bwd_after_fwd_timed.restype = st
     lib.nha_status_string.argtypes = [st]
     lib.nha_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -115,7 +122,8 @@ def make_desc(B, T, H, Hkv, d, m, w, C=64, rope_base=10000.0, scale=0.0, dtype=t
 
 
 def stage_names(desc, backward=False, with_state=False):
-    """Names of the kernel launches one fwd / bwd call enqueues, in order."""
+    """Names of the kernel launches one fwd (backward=0) / bwd (1) /
+    bwd(after_fwd=True) (2) call enqueues, in order."""
     lib = load()
     names = (ctypes.c_char_p * 16)()
     n = lib.nha_stage_names(ctypes.byref(desc), int(backward), int(with_state), names, 16)
@@ -206,8 +214,12 @@ def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, w
 
 
 def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, workspace=None, out=None,
-        events=None):
-    """Gradients of fwd. Returns (dq, dk, dv, dalpha); dalpha is float32."""
+        events=None, after_fwd=False):
+    """Gradients of fwd. Returns (dq, dk, dv, dalpha); dalpha is float32.
+
+    after_fwd=True calls nha_bwd_after_fwd: `workspace` must then be the one
+    the forward of these inputs ran with, untouched since (the forward's RoPE'd
+    q/k, gate products and chunk-start states are read from it)."""
     desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
     dev, dt = q.device, q.dtype
     B, T, H, d = q.shape
@@ -223,10 +235,16 @@ def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, works
     else:
         dq, dk, dv, da = out
     n = workspace_size(desc, backward=True)
-    ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(n, dtype=torch.uint8, device=dev)
-    rc = lib.nha_bwd_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
-                           _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(ws), ctypes.c_size_t(ws.numel()),
-                           _stream(dev), _events_arg(events))
+    if after_fwd:
+        if workspace is None or workspace.numel() < n:
+            raise ValueError("after_fwd needs the forward's workspace, of at least %d bytes" % n)
+        ws = workspace
+    else:
+        ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(
+            n, dtype=torch.uint8, device=dev)
+    fn = lib.nha_bwd_after_fwd_timed if after_fwd else lib.nha_bwd_timed
+    rc = fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(da), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev), _events_arg(events))
     if rc != NHA_OK:
         raise NhaError(rc, "nha_bwd")
     return dq, dk, dv, da

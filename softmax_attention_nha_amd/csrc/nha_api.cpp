@@ -141,9 +141,10 @@ nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k, const voi
   return nha_bwd_timed(desc, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws, ws_bytes, stream, nullptr);
 }
 
-nha_status nha_bwd_timed(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
-                         const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                         float* dalpha, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+static nha_status bwd_common(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                             float* dalpha, void* ws, size_t ws_bytes, void* stream, void* const* events,
+                             bool after_fwd) {
   Shape s;
   nha_status rc = make_shape(desc, true, &s);
   if (rc != NHA_OK) return rc;
@@ -154,15 +155,34 @@ nha_status nha_bwd_timed(const nha_desc* desc, const void* q, const void* k, con
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
   if (ws_bytes < bwd_ws_bytes(s)) return NHA_ERR_WORKSPACE;
-  BwdPtrs p{q, k, v, alpha, o, dO, lse, dq, dk, dv, dalpha, (char*)ws, events};
+  BwdPtrs p{q, k, v, alpha, o, dO, lse, dq, dk, dv, dalpha, (char*)ws, events, after_fwd};
   hipError_t e = launch_bwd(s, make_theta(desc), p, (hipStream_t)stream);
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+nha_status nha_bwd_timed(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                         const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                         float* dalpha, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  return bwd_common(desc, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws, ws_bytes, stream, events, false);
+}
+
+nha_status nha_bwd_after_fwd(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                             float* dalpha, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_common(desc, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws, ws_bytes, stream, nullptr, true);
+}
+
+nha_status nha_bwd_after_fwd_timed(const nha_desc* desc, const void* q, const void* k, const void* v,
+                                   const void* alpha, const void* o, const float* lse, const void* dO, void* dq,
+                                   void* dk, void* dv, float* dalpha, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* events) {
+  return bwd_common(desc, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws, ws_bytes, stream, events, true);
 }
 
 int nha_stage_names(const nha_desc* desc, int backward, int with_state, const char** names, int max) {
   Shape s;
   if (make_shape(desc, true, &s) != NHA_OK) return -1;
-  return backward ? bwd_stages(s, names, max) : fwd_stages(s, with_state != 0, names, max);
+  return backward ? bwd_stages(s, backward == 2, names, max) : fwd_stages(s, with_state != 0, names, max);
 }
 
 nha_status nha_decode_step(const nha_desc* desc, const void* q_t, const void* k_t, const void* v_t,

@@ -1491,8 +1491,10 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
       pp.krot = ws + L.krot;
       pp.rcs = (float2*)(ws + L.rcs);
     }
-    hipError_t e = launch_prologue(s, th, q, k, v, alpha, pp, mk, st);
-    if (e != hipSuccess) return e;
+    if (!p.after_fwd) {
+      hipError_t e = launch_prologue(s, th, q, k, v, alpha, pp, mk, st);
+      if (e != hipSuccess) return e;
+    }
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
     float* Dt = (float*)(ws + L.dt);
@@ -1579,15 +1581,17 @@ hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hip
   return s.mp == 32 ? bwd_c<float, 32>(s, th, p, st) : bwd_c<float, 64>(s, th, p, st);
 }
 
-int bwd_stages(const Shape& s, const char** names, int max) {
+int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max) {
   const char* all[16];
   int n = 0;
-  if (s.rope && s.win) {
-    all[n++] = "rope_cs";
-    all[n++] = "rope";
+  if (!after_fwd) {
+    if (s.rope && s.win) {
+      all[n++] = "rope_cs";
+      all[n++] = "rope";
+    }
+    all[n++] = "chunk_gates";
+    all[n++] = "state_scan";
   }
-  all[n++] = "chunk_gates";
-  all[n++] = "state_scan";
   all[n++] = "bwd_prep";
   all[n++] = "slot_bwd_a";
   all[n++] = "adj_scan";

@@ -101,7 +101,7 @@ struct Marks {
 
 // Launch sequence of one forward / backward call (names are static strings).
 int fwd_stages(const Shape& s, bool with_state, const char** names, int max);
-int bwd_stages(const Shape& s, const char** names, int max);
+int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max);
 
 // ---------------------------------------------------------------- launchers
 // Shared first stages of the forward and the backward: RoPE of q and k (when
@@ -150,6 +150,7 @@ struct BwdPtrs {
   float* dalpha;
   char* ws;
   void* const* events;  // nullable timing events
+  bool after_fwd;       // the workspace already holds this input's forward prologue
 };
 hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st);
 

@@ -104,6 +104,20 @@ def test_bwd_argument_errors():
     n = nha.workspace_size(d, backward=True)
     rc = lib.nha_bwd(ctypes.byref(d), *args[:5], A, *args[5:10], A, ctypes.c_size_t(n - 1), None)
     assert rc == nha.NHA_ERR_WORKSPACE
+    # the variant that reuses the forward's workspace checks the same things
+    rc = lib.nha_bwd_after_fwd(ctypes.byref(d), *args[:5], None, *args[5:10], A, ctypes.c_size_t(1 << 40), None)
+    assert rc == nha.NHA_ERR_INVALID_ARG
+    rc = lib.nha_bwd_after_fwd(ctypes.byref(d), *args[:5], A, *args[5:10], A, ctypes.c_size_t(n - 1), None)
+    assert rc == nha.NHA_ERR_WORKSPACE
+
+
+def test_stage_lists():
+    """The backward after a forward skips the forward's first stages."""
+    d = desc()
+    full, after = nha.stage_names(d, backward=1), nha.stage_names(d, backward=2)
+    fwd = nha.stage_names(d)
+    assert after == [x for x in full if x not in ("rope_cs", "rope", "chunk_gates", "state_scan")]
+    assert full[:len(full) - len(after)] == fwd[:len(full) - len(after)]
 
 
 def test_decode_argument_errors():

@@ -114,3 +114,20 @@ def test_bwd_bitwise_deterministic():
     for x in r[1:]:
         for g0, g1 in zip(r[0], x):
             assert torch.equal(g0, g1)
+
+
+@pytest.mark.parametrize("name,T,C", [("1p3b", 300, 64), ("gqa", 260, 32), ("340m", 200, 16)])
+def test_bwd_after_fwd_matches_bwd(name, T, C):
+    """nha_bwd_after_fwd reads the forward's first stages from its workspace:
+    bitwise the same gradients as the standalone backward."""
+    wl = WORKLOADS[name].with_(B=1, T=T, seed=56)
+    q, k, v, a, dO = (x.to("cuda:0") for x in make_inputs(wl, with_grad=True))
+    desc = nha.make_desc(wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, wl.w, C, wl.rope_base, 0.0, wl.dtype)
+    ws = torch.empty(max(nha.workspace_size(desc), nha.workspace_size(desc, backward=True)), dtype=torch.uint8,
+                     device="cuda:0")
+    o, lse = nha.fwd(q, k, v, a, wl.w, C=C, rope_base=wl.rope_base, workspace=ws)
+    g1 = nha.bwd(q, k, v, a, o, lse, dO, wl.w, C=C, rope_base=wl.rope_base, workspace=ws, after_fwd=True)
+    g2 = nha.bwd(q, k, v, a, o, lse, dO, wl.w, C=C, rope_base=wl.rope_base)
+    torch.cuda.synchronize()
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
