@@ -109,8 +109,7 @@ def stage_work(stage, wl, w, e):
         "rope": ("hbm", 2.0 * B * T * (H + Hkv) * d * e),
         "chunk_gates": ("hbm", 2.0 * B * T * Hkv * m * e),
         "bwd_prep": ("hbm", B * T * H * (2.0 * d * e + 4)),
-        "dalpha_fix": ("hbm", B * T * Hkv * m * (e + 8.0)),
-        "dalpha_carry": ("hbm", 8.0 * B * Hkv * ((T + C - 1) // C) * m),
+        "dalpha_tail": ("hbm", B * T * Hkv * m * (e + 8.0)),
         "export_state": ("hbm", 4.0 * B * Hkv * min(w, T) * d * e),
     }
     if stage not in table:

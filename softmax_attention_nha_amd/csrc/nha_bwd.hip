@@ -28,8 +28,7 @@
 //                   adjoint weights 2^{G_u} s dl_u, 2^{G_u} p_u; A_t parts
 //   k_adj_scan      reverse over chunks: Lin_c for every chunk (MFMA)
 //   k_bwd_slot_b    per (b, g, chunk): dk/dv slot parts, F, local dalpha
-//   k_dalpha_carry  sum of the later chunks' (A - b F) per slot
-//   k_dalpha_fix    dalpha += carry / alpha
+//   k_dalpha_tail   dalpha += (sum of the later chunks' (A - b F)) / alpha
 //   k_win_bwd_dq    window dq (+ slot part) -> dq
 //   k_win_bwd_dkdv  window dk, dv (+ slot parts at the shifted rows) -> dk, dv
 #include "nha_common.h"
@@ -47,7 +46,7 @@ struct BwdWs {
   size_t sdl, pp, acon;              // [B*H][NC*C][mp] float
   size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp][d] dtype
   size_t dkap, dnu;                  // slot parts of dk, dv at the key row: [B][T][Hkv][d] float
-  size_t csum, carry;                // [B*Hkv][NC][mp] float
+  size_t csum;                       // [B*Hkv][NC][mp] float
   size_t total;
 };
 
@@ -81,8 +80,6 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   L.dnu = off;
   off += align256((size_t)s.B * s.T * s.Hkv * s.d * 4);
   L.csum = off;
-  off += align256(units * s.NC * s.mp * 4);
-  L.carry = off;
   off += align256(units * s.NC * s.mp * 4);
   L.total = off;
   return L;
@@ -131,21 +128,19 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
   constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
   constexpr int PG = SlotPitch<MP>::PG;
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc, rl = r0 + 15;
-  floatx4 accA[NW];  // A[u][t] = vec_u . key_t, D layout [u = 16J + 4g + r][t = cc]
-#pragma unroll
-  for (int J = 0; J < NW; ++J) {
-    accA[J] = zero4();
-    if (J >= I) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        accA[J] = mma32(accA[J], ld8<T>(&sVec[(16 * J + cc) * PD + 32 * ks + 8 * g]), keyf[ks]);
-    }
-  }
-  // later blocks J > I, and (when factorizable) the block itself with u >= t
+  // later blocks J > I, and (when factorizable) the block itself with u >= t;
+  // one block per iteration (not unrolled: the blocks are independent and
+  // unrolling only multiplies the live registers)
   const bool fast = block_factorizable<MP>(sG, r0);
+  floatx4 aI = zero4();  // A[u][t] = vec_u . key_t for the wave's own block (exact path)
+#pragma unroll 1
+  for (int J = I; J < NW; ++J) {
+    floatx4 aJ = zero4();  // D layout [u = 16J + 4g + r][t = cc]
 #pragma unroll
-  for (int J = 0; J < NW; ++J) {
-    if (J > I || (J == I && fast)) {
+    for (int ks = 0; ks < D / 32; ++ks)
+      aJ = mma32(aJ, ld8<T>(&sVec[(16 * J + cc) * PD + 32 * ks + 8 * g]), keyf[ks]);
+    if (J == I) aI = aJ;
+    if (J > I || fast) {
       const int uA = 16 * J + cc;  // A-fragment row of this lane
       floatx4 mt = zero4();        // M^T[u][t] = sum_i Y[u][i] bwI[t][i]
 #pragma unroll
@@ -168,9 +163,15 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
       }
       typename Vec<T>::v4 mfr = pack4<T>(mt);
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        accO[db] = mma16(accO[db], ld4<T>(&sVecT[(16 * db + cc) * PC + 16 * J + 4 * g]), mfr);
-      floatx4 av = accA[J];
+      for (int db = 0; db < D / 16; ++db) {
+        typename Vec<T>::v4 at;
+        if constexpr (sizeof(T) == 2)
+          at = ld_tr4(&sVec[(16 * J + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+        else
+          at = ld4<T>(&sVecT[(16 * db + cc) * PC + 16 * J + 4 * g]);
+        accO[db] = mma16(accO[db], at, mfr);
+      }
+      floatx4 av = aJ;
       if (J == I) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) av[r] = (4 * g + r >= cc) ? av[r] : 0.f;  // u >= t
@@ -196,10 +197,6 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
   }
   if (fast) return;
   // same block: u >= t, exact running products D'_{t,u} = prod_{j=t+1..u} a_j
-  floatx4 aI = accA[0];
-#pragma unroll
-  for (int J = 1; J < NW; ++J)
-    if (J == I) aI = accA[J];
   float Ad[16];
 #pragma unroll
   for (int gg = 0; gg < 4; ++gg)
@@ -245,8 +242,14 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
 #pragma unroll
   for (int r = 0; r < 4; ++r) bfr[r] = to_t<T>(mine[r]);
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    accO[db] = mma16(accO[db], ld4<T>(&sVecT[(16 * db + cc) * PC + r0 + 4 * g]), bfr);
+  for (int db = 0; db < D / 16; ++db) {
+    typename Vec<T>::v4 at;
+    if constexpr (sizeof(T) == 2)
+      at = ld_tr4(&sVec[(r0 + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+    else
+      at = ld4<T>(&sVecT[(16 * db + cc) * PC + r0 + 4 * g]);
+    accO[db] = mma16(accO[db], at, bfr);
+  }
 }
 
 // In-place reverse inclusive cumsum over the C rows of an LDS tile (fp32).
@@ -657,11 +660,13 @@ __global__ __launch_bounds__(64) void k_adj_scan_b16(const bf16* __restrict__ q,
 template <typename T, int D, int MP, int C>
 struct SlotBwdBSmem {
   static constexpr int PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
-  T sL[MP * PD];     // incoming adjoint Lin [i][d]
-  T sLt[D * PM];     // Lin^T [d][i]
-  T sKey[C * PD];    // kappa or nu rows [u][d]
-  T sVec[C * PD];    // q or dO rows of one head [u][d]
-  T sVecT[D * PC];   // same, transposed
+  // bf16 reads the transposed operands straight from the row tiles
+  // (ds_read_b64_tr_b16); fp32 keeps transposed copies
+  static constexpr bool TR = sizeof(T) == 2;
+  T sL[MP * PD];                   // incoming adjoint Lin [i][d]
+  T sLt[TR ? 8 : D * PM];          // Lin^T [d][i] (fp32 only)
+  T sVec[C * PD];                  // q or dO rows of one head [u][d]
+  T sVecT[TR ? 8 : D * PC];        // same, transposed (fp32 only)
   T sA[C * PM];
   float sG[C * SlotPitch<MP>::PG];
   float sW[C * SlotPitch<MP>::PG];  // s dl or p of one head [u][i]; later the (A - bF) tile
@@ -669,7 +674,7 @@ struct SlotBwdBSmem {
 
 // grid (NC, B*Hkv), C/16 waves; all query heads of the KV group.
 template <typename T, int D, int MP, int C>
-__global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
+__global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slot_b(
     const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
     const T* __restrict__ dO, const T* __restrict__ lin, const float* __restrict__ sdl,
     const float* __restrict__ pp, const float* __restrict__ acon, float* __restrict__ dkap,
@@ -700,24 +705,26 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
       F[mb][r] = 0.f;
     }
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+#pragma unroll 1
   for (int side = 0; side < 2; ++side) {
     __syncthreads();
     {
       const T* src = lin + (((size_t)unit * NC + c) * 2 + side) * MP * D;
       RowTile<T, D, NT, MP> tl;
-      PairTileT<T, D, NT, MP> tlt;
-      RowTile<T, D, NT, C> tkey;
       tl.load(src, D, 0, MP, tid);
-      tlt.load(src, D, 0, MP, tid);
-      tkey.load((side ? vv : kk) + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
       tl.template store<PD>(sm.sL, tid);
-      tlt.template store<PM>(sm.sLt, tid);
-      tkey.template store<PD>(sm.sKey, tid);
+      if constexpr (!S::TR) {
+        PairTileT<T, D, NT, MP> tlt;
+        tlt.load(src, D, 0, MP, tid);
+        tlt.template store<PM>(sm.sLt, tid);
+      }
     }
-    __syncthreads();
+    // this lane's absorbed key row (zero where nothing is absorbed)
     typename Vec<T>::v8 keyf[D / 32];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) keyf[ks] = ld8<T>(&sm.sKey[urow * PD + 32 * ks + 8 * g]);
+    for (int ks = 0; ks < D / 32; ++ks)
+      keyf[ks] = absorb ? ld8<T>((side ? vv : kk) + (rbase + (long)urow * Hkv) * D + 32 * ks + 8 * g) : zero8<T>();
+    __syncthreads();
     floatx4 accO[D / 16];
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
@@ -739,21 +746,31 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
                                          floatx4{bwE[2 * s + 1][0], bwE[2 * s + 1][1], bwE[2 * s + 1][2],
                                                  bwE[2 * s + 1][3]});
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        accO[db] = mma32(accO[db],
-                         ld4x2<T>(&sm.sLt[(16 * db + cc) * PM + 32 * s + 4 * g],
-                                  &sm.sLt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]),
-                         bfr);
+      for (int db = 0; db < D / 16; ++db) {
+        typename Vec<T>::v8 at;
+        if constexpr (S::TR) {
+          const bf16x4 a0 = ld_tr4(&sm.sL[(32 * s + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+          const bf16x4 a1 = ld_tr4(&sm.sL[(32 * s + 16 + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            at[e] = a0[e];
+            at[4 + e] = a1[e];
+          }
+        } else {
+          at = ld4x2<T>(&sm.sLt[(16 * db + cc) * PM + 32 * s + 4 * g],
+                        &sm.sLt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]);
+        }
+        accO[db] = mma32(accO[db], at, bfr);
+      }
     }
+#pragma unroll 1
     for (int hh = 0; hh < G; ++hh) {
       const int h = hg * G + hh, bh = b * H + h;
       __syncthreads();
       {
         const T* vb = (side ? dO : q) + (((size_t)b * Tn + t0) * H + h) * D;
         RowTile<T, D, NT, C> tv;
-        PairTileT<T, D, NT, C> tvt;
         tv.load(vb, (size_t)H * D, 0, Tn - t0, tid);
-        tvt.load(vb, (size_t)H * D, 0, Tn - t0, tid);
         const float* wsrc = (side ? pp : sdl) + ((size_t)bh * NC * C + t0) * MP;
         for (int e = tid * 4; e < C * MP; e += NT * 4) {
           floatx4 x = *reinterpret_cast<const floatx4*>(wsrc + e);
@@ -762,7 +779,11 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
           for (int r = 0; r < 4; ++r) sm.sW[u * PG + i + r] = x[r];
         }
         tv.template store<PD>(sm.sVec, tid);
-        tvt.template store<PC>(sm.sVecT, tid);
+        if constexpr (!S::TR) {
+          PairTileT<T, D, NT, C> tvt;
+          tvt.load(vb, (size_t)H * D, 0, Tn - t0, tid);
+          tvt.template store<PC>(sm.sVecT, tid);
+        }
       }
       __syncthreads();
       slot_rev<T, D, MP, C>(sm.sVec, sm.sVecT, sm.sW, sm.sG, sm.sA, keyf, bwI, bt, I, t0, w, Tn, accO, F);
@@ -812,31 +833,33 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_b(
   }
 }
 
-// carry[unit][c][i] = sum over later chunks of the chunk totals of (A - b F)
-template <int MP>
-__global__ void k_dalpha_carry(const float* __restrict__ csum, float* __restrict__ carry, int NC) {
-  const int unit = blockIdx.x, i = threadIdx.x;
+// dalpha_t[i] += carry_c[i] / alpha_t[i] for the rows t >= w of chunk c, with
+// carry_c[i] = sum over the later chunks of their totals of (A - b F).
+// grid (NC, B*Hkv), 256 threads: the carry is summed by 256 / MP strided
+// parts (a fixed order) and combined through LDS.
+template <typename T, int MP>
+__global__ __launch_bounds__(256) void k_dalpha_tail(const T* __restrict__ alpha, const float* __restrict__ csum,
+                                                     float* __restrict__ dalpha, int Tn, int Hkv, int m, int w,
+                                                     int C, int NC) {
+  constexpr int NP = 256 / MP;
+  __shared__ float part[NP][MP];
+  const int tid = threadIdx.x, c = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv;
+  const int i = tid % MP, pt = tid / MP;
   float acc = 0.f;
-  for (int c = NC - 1; c >= 0; --c) {
-    carry[((size_t)unit * NC + c) * MP + i] = acc;
-    acc += csum[((size_t)unit * NC + c) * MP + i];
+  for (int c2 = c + 1 + pt; c2 < NC; c2 += NP) acc += csum[((size_t)unit * NC + c2) * MP + i];
+  part[pt][i] = acc;
+  __syncthreads();
+  const int t0 = c * C;
+  for (int e = tid; e < C * m; e += 256) {
+    const int u = e / m, ii = e % m, t = t0 + u;
+    if (t >= w && t < Tn) {
+      float carry = 0.f;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) carry += part[k][ii];
+      const size_t idx = (((size_t)b * Tn + t) * Hkv + hg) * m + ii;
+      dalpha[idx] += carry / to_f<T>(alpha[idx]);
+    }
   }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_dalpha_fix(const T* __restrict__ alpha, const float* __restrict__ carry,
-                                                    float* __restrict__ dalpha, int Tn, int Hkv, int m, int mp,
-                                                    int w, int C, int NC, long n) {
-  long e = (long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n) return;
-  int i = (int)(e % m);
-  long r = e / m;
-  int hg = (int)(r % Hkv);
-  long bt = r / Hkv;
-  int t = (int)(bt % Tn), b = (int)(bt / Tn);
-  if (t < w) return;
-  int unit = b * Hkv + hg, c = t / C;
-  dalpha[e] += carry[((size_t)unit * NC + c) * mp + i] / to_f<T>(alpha[e]);
 }
 
 // ---------------------------------------------------------------- window backward: dq
@@ -1507,7 +1530,6 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     float* dkap = (float*)(ws + L.dkap);
     float* dnu = (float*)(ws + L.dnu);
     float* csum = (float*)(ws + L.csum);
-    float* carry = (float*)(ws + L.carry);
     const long nrows = (long)s.B * s.T * s.H;
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
@@ -1531,11 +1553,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
                        (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.w, s.NC);
     mk.mark(st);
-    hipLaunchKernelGGL((k_dalpha_carry<MP>), dim3(units), dim3(MP), 0, st, csum, carry, s.NC);
-    const long na = (long)s.B * s.T * s.Hkv * s.m;
-    mk.mark(st);
-    hipLaunchKernelGGL(k_dalpha_fix<T>, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, st, alpha, carry, p.dalpha,
-                       s.T, s.Hkv, s.m, MP, s.w, C, s.NC, na);
+    hipLaunchKernelGGL((k_dalpha_tail<T, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, csum, p.dalpha, s.T, s.Hkv,
+                       s.m, s.w, C, s.NC);
     mk.mark(st);
     if constexpr (sizeof(T) == 2) {
       constexpr int NWV = 4;
@@ -1596,8 +1615,7 @@ int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max) {
   all[n++] = "slot_bwd_a";
   all[n++] = "adj_scan";
   all[n++] = "slot_bwd_b";
-  all[n++] = "dalpha_carry";
-  all[n++] = "dalpha_fix";
+  all[n++] = "dalpha_tail";
   all[n++] = "win_bwd_dq";
   all[n++] = "win_bwd_dkdv";
   for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];
@@ -1609,7 +1627,9 @@ size_t slot_bwd_lds_bytes(const Shape& s) {
   size_t PD = pitch_of(s.d), PM = pitch_of(s.mp), PC = pitch_of(s.C);
   size_t a = e * (2 * s.mp * PD + s.d * PM + 2 * s.C * PD + s.d * PC + 2 * s.C * PM + s.mp * PC) +
              4 * (size_t)s.C * s.mp;
-  size_t b = e * (s.mp * PD + s.d * PM + 2 * s.C * PD + s.d * PC + s.C * PM) + 8 * (size_t)s.C * s.mp;
+  size_t b = (e == 2 ? e * (s.mp * PD + s.C * PD + s.C * PM + 16)
+                     : e * (s.mp * PD + s.d * PM + s.C * PD + s.d * PC + s.C * PM)) +
+             8 * (size_t)s.C * (s.mp + 1);
   size_t kv = e * 2 * (64 * PD + s.d * 68) + 512;
   size_t mx = a > b ? a : b;
   return mx > kv ? mx : kv;
