@@ -546,6 +546,108 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
   }
 }
 
+// bf16 variant: grid (NC, B*H), C/16 waves, two workgroups per compute unit.
+// The chunk's two tile pairs go through one pair of LDS row tiles in turn --
+// S0^K and kappa for the logits, then S0^V and nu for the output, whose
+// loads are in flight while the logits are computed -- and the transposed
+// operands are read from the row tiles with ds_read_b64_tr_b16.
+template <int D, int MP, int C>
+struct SlotFwdSmemB16 {
+  static constexpr int PD = pitch_of(D), PM = pitch_of(MP);
+  bf16 tS[MP * PD];  // S0^K, then S0^V  [i][d]
+  bf16 tK[C * PD];   // kappa, then nu    [u][d]
+  bf16 sA[C * PM];   // alpha [u][i]
+  bf16 sB[C * PM];   // 2^{E_J - G_u} b_u [u][i]
+  float sG[C * SlotPitch<MP>::PG];
+};
+
+template <int D, int MP, int C>
+__global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
+    const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
+    const bf16* __restrict__ alpha, const bf16* __restrict__ sst, bf16* __restrict__ oL, float* __restrict__ lseL,
+    int Tn, int H, int Hkv, int m, int w, int NC, float scale) {
+  using S = SlotFwdSmemB16<D, MP, C>;
+  constexpr int NW = C / 16, NT = NW * 64, NB = MP / 16, PD = S::PD, PM = S::PM;
+  constexpr int PG = SlotPitch<MP>::PG;
+  __shared__ S sm;
+  const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int c = L % NC, bh = L / NC, b = bh / H, h = bh % H, G = H / Hkv, hg = h / G;
+  const int unit = b * Hkv + hg, t0 = c * C;
+  const bf16* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
+  // chunk row u <-> token t0 + u, absorbing key row t0 + u - w when t0 + u >= w
+  const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+  {
+    RowTile<bf16, D, NT, MP> ts;
+    RowTile<bf16, D, NT, C> tk;
+    ts.load(src, D, 0, MP, tid);
+    tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    stage_gates<bf16, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    ts.template store<PD>(sm.tS, tid);
+    tk.template store<PD>(sm.tK, tid);
+  }
+  __syncthreads();
+  lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
+  for (int e = tid; e < C * MP; e += NT) {
+    const int u = e / MP, i = e % MP, t = t0 + u;
+    const float be = (i < m && t < Tn && t >= w) ? 1.f - (float)sm.sA[u * PM + i] : 0.f;
+    sm.sB[u * PM + i] = (bf16)(fast_exp2(sm.sG[(u | 15) * PG + i] - sm.sG[u * PG + i]) * be);
+  }
+  __syncthreads();
+  // the output phase's tiles: loads in flight during the logits
+  RowTile<bf16, D, NT, MP> tsv;
+  RowTile<bf16, D, NT, C> tnu;
+  tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
+  tnu.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+
+  const int r0 = 16 * I;
+  const int tq = t0 + r0 + cc;  // this lane's query
+  const bool qvalid = tq < Tn;
+  bf16x8 qf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qf[ks] = qvalid ? ld8<bf16>(q + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<bf16>();
+  float lg[NB][4];
+  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+  // softmax partial over the m slots (log2 domain)
+  const float sl2 = scale * NHA_LOG2E;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * mb + 4 * g + r;
+      lg[mb][r] = (i < m) ? lg[mb][r] * sl2 : -INFINITY;
+      mx = fmaxf(mx, lg[mb][r]);
+    }
+  mx = max_over_g(mx);
+  float zs = 0.f;
+  float p[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[mb][r] = fast_exp2(lg[mb][r] - mx);
+      zs += p[mb][r];
+    }
+  zs = sum_over_g(zs);
+  __syncthreads();  // every wave is done with S0^K and kappa
+  tsv.template store<PD>(sm.tS, tid);
+  tnu.template store<PD>(sm.tK, tid);
+  __syncthreads();
+  floatx4 accO[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
+  slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO);
+  if (qvalid) {
+    const float inv = 1.f / zs;
+    bf16* dst = oL + (((size_t)b * Tn + tq) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) st4<bf16>(dst + 16 * db + 4 * g, pack4<bf16>(accO[db] * inv));
+    if (g == 0) lseL[((size_t)b * H + h) * Tn + tq] = (mx + __log2f(zs)) * NHA_LN2;
+  }
+}
+
 // ---------------------------------------------------------------- window branch
 // grid (ceil(T / (32 NWV)), B*H), NWV waves; wave W owns queries q0 + 32W ..
 // +31 and works on 32x32 tiles with the query index as the column:
@@ -1044,7 +1146,10 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
     mk.mark(st);
-    {
+    if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL((k_slot_fwd_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
+                         (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
+    } else {
       const int nitems = s.NC * s.B * s.H;
       const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
       hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha,

@@ -108,23 +108,15 @@ __device__ __forceinline__ bool block_factorizable(const float* sG, int r0) {
 
 // out[mb][r] = <x_t, S_t[i]> for the wave's rows.  sS: S0 [i][d] (pitch PD);
 // sKey: key rows [u][d] (pitch PD); xf: the rows' vectors as B fragments.
-template <typename T, int D, int MP, int C>
+// TR (bf16 only): sBt is the row tile B [u][i] (pitch PM), read transposed
+// with ds_read_b64_tr_b16; else the transposed copy [i][u] (pitch PC).
+template <typename T, int D, int MP, int C, bool TR = false>
 __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* sBt, const float* sG, const T* sA,
                                           const typename Vec<T>::v8* xf, int I, int t0, int w, int Tn,
                                           float (&out)[MP / 16][4]) {
   constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
   constexpr int PG = SlotPitch<MP>::PG;
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
-  floatx4 accA[NW];
-#pragma unroll
-  for (int ub = 0; ub < NW; ++ub) {
-    accA[ub] = zero4();
-    if (ub <= I) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        accA[ub] = mma32(accA[ub], ld8<T>(&sKey[(16 * ub + cc) * PD + 32 * ks + 8 * g]), xf[ks]);
-    }
-  }
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) {
     floatx4 acc = zero4();
@@ -134,12 +126,19 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
     for (int r = 0; r < 4; ++r) out[mb][r] = fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r]) * acc[r];
   }
   // earlier 16-row blocks J < I of the chunk, and (when factorizable) the
-  // block itself with the causal mask u <= t
+  // block itself with the causal mask u <= t; one block per iteration (not
+  // unrolled: the blocks are independent and unrolling only multiplies the
+  // live registers)
   const bool fast = block_factorizable<MP>(sG, r0);
+  floatx4 aI = zero4();  // A[u][t] of the wave's own block (exact path)
+#pragma unroll 1
+  for (int J = 0; J <= I; ++J) {
+    floatx4 av = zero4();  // A[u][t] = key_u . x_t, D layout [u = 16J + 4g + r][t = cc]
 #pragma unroll
-  for (int J = 0; J < NW; ++J) {
-    if (J < I || (J == I && fast)) {
-      floatx4 av = accA[J];
+    for (int ks = 0; ks < D / 32; ++ks)
+      av = mma32(av, ld8<T>(&sKey[(16 * J + cc) * PD + 32 * ks + 8 * g]), xf[ks]);
+    if (J == I) aI = av;
+    if (J < I || fast) {
       if (J == I) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) av[r] = (4 * g + r <= cc) ? av[r] : 0.f;
@@ -147,7 +146,12 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
       typename Vec<T>::v4 bfr = pack4<T>(av);
 #pragma unroll
       for (int mb = 0; mb < NB; ++mb) {
-        floatx4 x = mma16(zero4(), ld4<T>(&sBt[(16 * mb + cc) * PC + 16 * J + 4 * g]), bfr);
+        typename Vec<T>::v4 bt;
+        if constexpr (TR)
+          bt = ld_tr4(&sBt[(16 * J + 4 * g + (cc >> 2)) * PM + 16 * mb + 4 * (cc & 3)]);
+        else
+          bt = ld4<T>(&sBt[(16 * mb + cc) * PC + 16 * J + 4 * g]);
+        floatx4 x = mma16(zero4(), bt, bfr);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           int i = 16 * mb + 4 * g + r;
@@ -158,10 +162,6 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
   }
   if (fast) return;
   // same block: exact running products
-  floatx4 aI = accA[0];
-#pragma unroll
-  for (int ub = 1; ub < NW; ++ub)
-    if (ub == I) aI = accA[ub];
   float Ad[16];
 #pragma unroll
   for (int gg = 0; gg < 4; ++gg)
@@ -193,12 +193,14 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
 }
 
 // accO (O^T[d][t] in D layout) += sum_i wgt_t[i] S_t[i].  sSt: S0 transposed
-// [d][i] (pitch PM); sKeyT: key rows transposed [d][u] (pitch PCT).
-template <typename T, int D, int MP, int C, int PCT>
+// [d][i] (pitch PM); sKeyT: key rows transposed [d][u] (pitch PCT).  TR
+// (bf16 only): sSt and sKeyT are the row tiles S0 [i][d] and key [u][d]
+// (pitch PD), read transposed with ds_read_b64_tr_b16.
+template <typename T, int D, int MP, int C, int PCT, bool TR = false>
 __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* sB, const float* sG, const T* sA,
                                          const float (&wgt)[MP / 16][4], int I, int t0, int w, int Tn,
                                          floatx4 (&accO)[D / 16]) {
-  constexpr int NW = C / 16, NB = MP / 16, PM = pitch_of(MP), PG = SlotPitch<MP>::PG;
+  constexpr int NW = C / 16, NB = MP / 16, PM = pitch_of(MP), PG = SlotPitch<MP>::PG, PD = pitch_of(D);
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
   {
     float ph[NB][4];
@@ -212,17 +214,27 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
                                          floatx4{ph[2 * s + 1][0], ph[2 * s + 1][1], ph[2 * s + 1][2],
                                                  ph[2 * s + 1][3]});
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        accO[db] = mma32(accO[db],
-                         ld4x2<T>(&sSt[(16 * db + cc) * PM + 32 * s + 4 * g],
-                                  &sSt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]),
-                         bfr);
+      for (int db = 0; db < D / 16; ++db) {
+        typename Vec<T>::v8 at;
+        if constexpr (TR) {
+          const bf16x4 a0 = ld_tr4(&sSt[(32 * s + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+          const bf16x4 a1 = ld_tr4(&sSt[(32 * s + 16 + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            at[e] = a0[e];
+            at[4 + e] = a1[e];
+          }
+        } else {
+          at = ld4x2<T>(&sSt[(16 * db + cc) * PM + 32 * s + 4 * g], &sSt[(16 * db + cc) * PM + 32 * s + 16 + 4 * g]);
+        }
+        accO[db] = mma32(accO[db], at, bfr);
+      }
     }
   }
   const bool fast = block_factorizable<MP>(sG, r0);
-#pragma unroll
-  for (int J = 0; J < NW; ++J) {
-    if (J < I || (J == I && fast)) {
+#pragma unroll 1
+  for (int J = 0; J <= I; ++J) {
+    if (J < I || fast) {
       floatx4 at = zero4();
 #pragma unroll
       for (int s = 0; s < NB / 2; ++s) {
@@ -243,8 +255,14 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
       }
       typename Vec<T>::v4 bfr = pack4<T>(at);
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        accO[db] = mma16(accO[db], ld4<T>(&sKeyT[(16 * db + cc) * PCT + 16 * J + 4 * g]), bfr);
+      for (int db = 0; db < D / 16; ++db) {
+        typename Vec<T>::v4 kt;
+        if constexpr (TR)
+          kt = ld_tr4(&sKeyT[(16 * J + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+        else
+          kt = ld4<T>(&sKeyT[(16 * db + cc) * PCT + 16 * J + 4 * g]);
+        accO[db] = mma16(accO[db], kt, bfr);
+      }
     }
   }
   if (fast) return;
@@ -279,8 +297,14 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
 #pragma unroll
   for (int r = 0; r < 4; ++r) bfr[r] = to_t<T>(mine[r]);
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    accO[db] = mma16(accO[db], ld4<T>(&sKeyT[(16 * db + cc) * PCT + r0 + 4 * g]), bfr);
+  for (int db = 0; db < D / 16; ++db) {
+    typename Vec<T>::v4 kt;
+    if constexpr (TR)
+      kt = ld_tr4(&sKeyT[(r0 + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+    else
+      kt = ld4<T>(&sKeyT[(16 * db + cc) * PCT + r0 + 4 * g]);
+    accO[db] = mma16(accO[db], kt, bfr);
+  }
 }
 
 }  // namespace nha
