@@ -432,6 +432,124 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
   }
 }
 
+// bf16 variant: grid (NC, B*H), C/16 waves, two workgroups per compute unit.
+// One pair of LDS row tiles holds S0^V and nu (for dp), then S0^K and kappa
+// (for the logits and dq's slot part: their transposes are read with
+// ds_read_b64_tr_b16); the second pair's loads are in flight during dp.
+template <int D, int MP, int C>
+struct SlotBwdASmemB16 {
+  static constexpr int PD = pitch_of(D), PM = pitch_of(MP);
+  bf16 tS[MP * PD];  // S0^V, then S0^K  [i][d]
+  bf16 tK[C * PD];   // nu, then kappa   [u][d]
+  bf16 sA[C * PM];
+  bf16 sB[C * PM];   // 2^{E_J - G_u} b_u [u][i]
+  float sG[C * SlotPitch<MP>::PG];
+};
+
+template <int D, int MP, int C>
+__global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
+    const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
+    const bf16* __restrict__ alpha, const bf16* __restrict__ dO, const bf16* __restrict__ sst,
+    const float* __restrict__ lse, const float* __restrict__ Dt, float* __restrict__ dqs, bf16* __restrict__ wp,
+    float* __restrict__ sdl, float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m,
+    int w, int NC, float scale) {
+  using S = SlotBwdASmemB16<D, MP, C>;
+  constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM;
+  constexpr int PG = SlotPitch<MP>::PG;
+  __shared__ S sm;
+  const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int c = L % NC, bh = L / NC, b = bh / H, h = bh % H, hg = h / (H / Hkv);
+  const int unit = b * Hkv + hg, t0 = c * C;
+  const bf16* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
+  const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+  {
+    RowTile<bf16, D, NT, MP> ts;
+    RowTile<bf16, D, NT, C> tk;
+    ts.load(src + (size_t)MP * D, D, 0, MP, tid);
+    tk.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+    stage_gates<bf16, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    ts.template store<PD>(sm.tS, tid);
+    tk.template store<PD>(sm.tK, tid);
+  }
+  __syncthreads();
+  lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
+  for (int e = tid; e < C * MP; e += NT) {
+    const int u = e / MP, i = e % MP, t = t0 + u;
+    const float be = (i < m && t < Tn && t >= w) ? 1.f - (float)sm.sA[u * PM + i] : 0.f;
+    sm.sB[u * PM + i] = (bf16)(fast_exp2(sm.sG[(u | 15) * PG + i] - sm.sG[u * PG + i]) * be);
+  }
+  __syncthreads();
+  RowTile<bf16, D, NT, MP> tsk;
+  RowTile<bf16, D, NT, C> tkap;
+  tsk.load(src, D, 0, MP, tid);
+  tkap.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+
+  const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
+  const bool qvalid = tq < Tn;
+  bf16x8 qf[D / 32], df[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const size_t off = (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g;
+    qf[ks] = qvalid ? ld8<bf16>(q + off) : zero8<bf16>();
+    df[ks] = qvalid ? ld8<bf16>(dO + off) : zero8<bf16>();
+  }
+  const float lse_t = qvalid ? lse[(size_t)bh * Tn + tq] : 0.f;
+  const float D_t = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  float lg[NB][4], dp[NB][4];
+  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, df, I, t0, w, Tn, dp);
+  __syncthreads();  // every wave is done with S0^V and nu
+  tsk.template store<PD>(sm.tS, tid);
+  tkap.template store<PD>(sm.tK, tid);
+  __syncthreads();
+  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+  float p[NB][4], dl[NB][4];
+  float* sdl_row = sdl + ((size_t)bh * NC * C + urow + t0) * MP;
+  float* pp_row = pp + ((size_t)bh * NC * C + urow + t0) * MP;
+  float* ac_row = acon + ((size_t)bh * NC * C + urow + t0) * MP;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    floatx4 vs, vp, va;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * mb + 4 * g + r;
+      const float ls = lg[mb][r] * scale;
+      const float pv = (i < m && qvalid) ? fast_exp2((ls - lse_t) * NHA_LOG2E) : 0.f;
+      const float dlv = pv * (dp[mb][r] - D_t);
+      p[mb][r] = pv;
+      dl[mb][r] = dlv;
+      vs[r] = scale * dlv;
+      vp[r] = pv;
+      va[r] = dlv * ls + pv * dp[mb][r];
+    }
+    *reinterpret_cast<floatx4*>(sdl_row + 16 * mb + 4 * g) = vs;
+    *reinterpret_cast<floatx4*>(pp_row + 16 * mb + 4 * g) = vp;
+    *reinterpret_cast<floatx4*>(ac_row + 16 * mb + 4 * g) = va;
+  }
+  // slot part of dq: s sum_i dl_t[i] SK_t[i]
+  floatx4 accO[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
+  slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, dl, I, t0, w, Tn, accO);
+  if (qvalid) {
+    float* dst = dqs + (((size_t)b * Tn + tq) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<floatx4*>(dst + 16 * db + 4 * g) = accO[db] * scale;
+  }
+  // adjoint weights 2^{G_u} s dl_u[i] and 2^{G_u} p_u[i], [i][u] layout
+  bf16* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
+  bf16* wv = wk + (size_t)MP * C;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * mb + 4 * g + r;
+      const float e = fast_exp2(sm.sG[urow * PG + i]);
+      wk[(size_t)i * C + urow] = (bf16)(e * scale * dl[mb][r]);
+      wv[(size_t)i * C + urow] = (bf16)(e * p[mb][r]);
+    }
+}
+
 // ---------------------------------------------------------------- adjoint scan
 // grid (d/16, B*Hkv), one wave.  Lane keeps Lam^T[j0 + 4g + r][16 nb + c] for
 // K and V.  Chunks in reverse: store Lin_c (the adjoint entering chunk c from
@@ -1535,7 +1653,11 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
                        (const T*)p.o, dO, Dt, s.T, s.H, nrows);
     mk.mark(st);
-    {
+    if constexpr (sizeof(T) == 2) {
+      hipLaunchKernelGGL((k_bwd_slot_a_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v,
+                         alpha, dO, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w,
+                         s.NC, s.scale);
+    } else {
       const int nitems = s.NC * s.B * s.H;
       const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
       hipLaunchKernelGGL((k_bwd_slot_a<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
