@@ -145,6 +145,118 @@ def cpu_baseline(wl, w, q, k, v, a, dO, with_bwd):
     }
 
 
+# ---------------------------------------------------------------- HBM traffic from counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+STAGE_KERNEL = {  # stage name -> kernel symbol fragment in the profiler's output
+    "slot_bwd_b": "k_bwd_slot_b", "slot_bwd_a": "k_bwd_slot_a", "slot_fwd": "k_slot_fwd", "win_fwd": "k_win_fwd",
+    "win_bwd_dq": "k_win_bwd_dq", "win_bwd_dkdv": "k_win_bwd_dkdv", "adj_scan": "k_adj_scan",
+    "state_scan": "k_state_scan",
+}
+
+
+def source_digest():
+    """sha256 over the kernel sources: counters taken on other sources are stale."""
+    import hashlib
+
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "softmax_attention_nha_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(src, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()
+
+
+def copy_calibrate(mib):
+    """Three plain copies of `mib` MiB: the per-dispatch FETCH_SIZE / WRITE_SIZE
+    of this kernel against its known byte count gives the counters' scale."""
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+
+
+def _pmc_per_dispatch(folder, counter, name_part):
+    """Mean value of `counter` per dispatch of the kernels whose name contains
+    name_part, from a rocprofv3 --pmc --output-format csv folder."""
+    import csv
+    import glob
+
+    vals = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    key = (f, r["Dispatch_Id"])
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit("no %s values for %s under %s" % (counter, name_part, folder))
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def traffic_summary(dirs, kernel, copy_mib):
+    fetch, nf = _pmc_per_dispatch(dirs[0], "FETCH_SIZE", kernel)
+    write, nw = _pmc_per_dispatch(dirs[1], "WRITE_SIZE", kernel)
+    cf, _ = _pmc_per_dispatch(dirs[2], "FETCH_SIZE", "copy")
+    cw, _ = _pmc_per_dispatch(dirs[3], "WRITE_SIZE", "copy")
+    n = copy_mib * (1 << 20)
+    ff, fw = cf * 1024.0 / n, cw * 1024.0 / n  # counter bytes per true byte, from the copy
+    out = {
+        "kernel": kernel,
+        "fetch_kib_per_dispatch": round(fetch, 1),
+        "write_kib_per_dispatch": round(write, 1),
+        "dispatches": [nf, nw],
+        "copy_mib": copy_mib,
+        "copy_fetch_kib": round(cf, 1),
+        "copy_write_kib": round(cw, 1),
+        "fetch_scale": round(ff, 4),
+        "write_scale": round(fw, 4),
+        "hbm_bytes_per_launch": round(fetch * 1024.0 / ff + write * 1024.0 / fw),
+        "source_sha256": source_digest(),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+def trace_summary(folder):
+    """Markdown table (calls, average and total duration per kernel) of a
+    rocprofv3 --kernel-trace --stats --output-format csv folder."""
+    import csv
+    import glob
+    import re
+
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    print("| kernel | calls | avg us | % of GPU time |")
+    print("|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        m = re.search(r"(k_[a-z0-9_]+)", r["Name"])
+        name = m.group(1) if m else r["Name"][:40]
+        print("| %s | %s | %.1f | %.1f |" % (name, r["Calls"], float(r["AverageNs"]) / 1e3,
+                                           100.0 * float(r["TotalDurationNs"]) / tot))
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage` from profiles/traffic.json, or None when
+    absent, for another kernel, or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != STAGE_KERNEL.get(stage) or t.get("source_sha256") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -157,7 +269,25 @@ def main():
     ap.add_argument("--B", type=int, default=None, help="override the batch")
     ap.add_argument("--fwd-only", action="store_true", help="diagnostic: time the forward alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="run 3 plain device copies of MIB MiB (a known-size kernel for the HBM counters) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                           "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc output folders into profiles/traffic.json and exit")
+    ap.add_argument("--traffic-kernel", default="k_bwd_slot_b", help="kernel name for --traffic-summary")
+    ap.add_argument("--traffic-copy-mib", type=int, default=1024)
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print a markdown table of a rocprofv3 --kernel-trace --stats csv folder and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.copy_calibrate:
+        copy_calibrate(args.copy_calibrate)
+        return
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary, args.traffic_kernel, args.traffic_copy_mib)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this operator build has no multi-GPU path "
@@ -241,11 +371,12 @@ def main():
         if bound == "mfma":
             ach = work / dur / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": None, "avg_us": round(per[dom] * 1e3, 2)}
+                    "frac": round(ach / peak, 4), "traffic": measured_traffic(dom), "avg_us": round(per[dom] * 1e3, 2)}
         else:
             ach = work / dur / 1e9
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "avg_us": round(per[dom] * 1e3, 2)}
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom),
+                    "avg_us": round(per[dom] * 1e3, 2)}
 
     ok = bool(torch.isfinite(o.float()).all().item())
     if do_bwd:
