@@ -372,15 +372,16 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
 
   const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
   const bool qvalid = tq < Tn;
+  const int tqc = qvalid ? tq : Tn - 1;  // clamped row: loads stay unconditional
   typename Vec<T>::v8 qf[D / 32], df[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    size_t off = (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g;
-    qf[ks] = qvalid ? ld8<T>(q + off) : zero8<T>();
-    df[ks] = qvalid ? ld8<T>(dO + off) : zero8<T>();
+    const size_t off = (((size_t)b * Tn + tqc) * H + h) * D + 32 * ks + 8 * g;
+    qf[ks] = ld8_sel<T>(q + off, qvalid);
+    df[ks] = ld8_sel<T>(dO + off, qvalid);
   }
-  const float lse_t = qvalid ? lse[(size_t)bh * Tn + tq] : 0.f;
-  const float D_t = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  const float lse_r = lse[(size_t)bh * Tn + tqc], lse_t = qvalid ? lse_r : 0.f;
+  const float D_r = Dt[(size_t)bh * Tn + tqc], D_t = qvalid ? D_r : 0.f;
   float lg[NB][4], dp[NB][4];
   slot_read<T, D, MP, C>(sm.sSK, sm.sK, sm.sBt, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
   slot_read<T, D, MP, C>(sm.sSV, sm.sV, sm.sBt, sm.sG, sm.sA, df, I, t0, w, Tn, dp);
@@ -464,11 +465,13 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   const bf16* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
   {
+    GateTile<bf16, C, MP, NT> gt;
     RowTile<bf16, D, NT, MP> ts;
     RowTile<bf16, D, NT, C> tk;
+    gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
     ts.load(src + (size_t)MP * D, D, 0, MP, tid);
     tk.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    stage_gates<bf16, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
     ts.template store<PD>(sm.tS, tid);
     tk.template store<PD>(sm.tK, tid);
   }
@@ -487,15 +490,16 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
 
   const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
   const bool qvalid = tq < Tn;
+  const int tqc = qvalid ? tq : Tn - 1;  // clamped row: loads stay unconditional
   bf16x8 qf[D / 32], df[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    const size_t off = (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g;
-    qf[ks] = qvalid ? ld8<bf16>(q + off) : zero8<bf16>();
-    df[ks] = qvalid ? ld8<bf16>(dO + off) : zero8<bf16>();
+    const size_t off = (((size_t)b * Tn + tqc) * H + h) * D + 32 * ks + 8 * g;
+    qf[ks] = ld8_sel<bf16>(q + off, qvalid);
+    df[ks] = ld8_sel<bf16>(dO + off, qvalid);
   }
-  const float lse_t = qvalid ? lse[(size_t)bh * Tn + tq] : 0.f;
-  const float D_t = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  const float lse_r = lse[(size_t)bh * Tn + tqc], lse_t = qvalid ? lse_r : 0.f;
+  const float D_r = Dt[(size_t)bh * Tn + tqc], D_t = qvalid ? D_r : 0.f;
   float lg[NB][4], dp[NB][4];
   slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, df, I, t0, w, Tn, dp);
   __syncthreads();  // every wave is done with S0^V and nu
@@ -837,11 +841,13 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
         tlt.template store<PM>(sm.sLt, tid);
       }
     }
-    // this lane's absorbed key row (zero where nothing is absorbed)
+    // this lane's absorbed key row (zero where nothing is absorbed; the
+    // address is clamped to a real row either way)
+    const size_t krow = (((size_t)b * Tn + min(max(tq - w, 0), Tn - 1)) * Hkv + hg) * D;
     typename Vec<T>::v8 keyf[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      keyf[ks] = absorb ? ld8<T>((side ? vv : kk) + (rbase + (long)urow * Hkv) * D + 32 * ks + 8 * g) : zero8<T>();
+      keyf[ks] = ld8_sel<T>((side ? vv : kk) + krow + 32 * ks + 8 * g, absorb);
     __syncthreads();
     floatx4 accO[D / 16];
 #pragma unroll
@@ -890,11 +896,16 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
         RowTile<T, D, NT, C> tv;
         tv.load(vb, (size_t)H * D, 0, Tn - t0, tid);
         const float* wsrc = (side ? pp : sdl) + ((size_t)bh * NC * C + t0) * MP;
-        for (int e = tid * 4; e < C * MP; e += NT * 4) {
-          floatx4 x = *reinterpret_cast<const floatx4*>(wsrc + e);
-          int u = e / MP, i = e % MP;
+        constexpr int WIT = C * MP / (NT * 4);  // every load first, then the LDS writes
+        static_assert(WIT * NT * 4 == C * MP, "tile split");
+        floatx4 xw[WIT];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm.sW[u * PG + i + r] = x[r];
+        for (int k = 0; k < WIT; ++k) xw[k] = *reinterpret_cast<const floatx4*>(wsrc + (tid + k * NT) * 4);
+#pragma unroll
+        for (int k = 0; k < WIT; ++k) {
+          const int e = (tid + k * NT) * 4, u = e / MP, i = e % MP;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.sW[u * PG + i + r] = xw[k][r];
         }
         tv.template store<PD>(sm.sVec, tid);
         if constexpr (!S::TR) {
@@ -954,28 +965,86 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
 // dalpha_t[i] += carry_c[i] / alpha_t[i] for the rows t >= w of chunk c, with
 // carry_c[i] = sum over the later chunks of their totals of (A - b F).
 // grid (NC, B*Hkv), 256 threads: the carry is summed by 256 / MP strided
-// parts (a fixed order) and combined through LDS.
-template <typename T, int MP>
+// parts (a fixed order) and combined through LDS.  Loads are issued in
+// batches before their first use (one memory round trip per batch).
+template <typename T, int MP, int C>
 __global__ __launch_bounds__(256) void k_dalpha_tail(const T* __restrict__ alpha, const float* __restrict__ csum,
                                                      float* __restrict__ dalpha, int Tn, int Hkv, int m, int w,
-                                                     int C, int NC) {
-  constexpr int NP = 256 / MP;
+                                                     int NC) {
+  constexpr int NP = 256 / MP, BATCH = 16;
   __shared__ float part[NP][MP];
+  __shared__ float carry[MP];
   const int tid = threadIdx.x, c = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv;
-  const int i = tid % MP, pt = tid / MP;
-  float acc = 0.f;
-  for (int c2 = c + 1 + pt; c2 < NC; c2 += NP) acc += csum[((size_t)unit * NC + c2) * MP + i];
-  part[pt][i] = acc;
+  {
+    const int i = tid % MP, pt = tid / MP;
+    const float* cs = csum + (size_t)unit * NC * MP + i;
+    float acc = 0.f;
+    for (int c0 = c + 1 + pt; c0 < NC; c0 += BATCH * NP) {
+      float x[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const int c2 = c0 + k * NP;
+        x[k] = cs[(size_t)(c2 < NC ? c2 : NC - 1) * MP];
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) acc += (c0 + k * NP < NC) ? x[k] : 0.f;
+    }
+    part[pt][i] = acc;
+  }
+  __syncthreads();
+  if (tid < MP) {
+    float x = 0.f;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) x += part[k][tid];
+    carry[tid] = x;
+  }
   __syncthreads();
   const int t0 = c * C;
-  for (int e = tid; e < C * m; e += 256) {
-    const int u = e / m, ii = e % m, t = t0 + u;
-    if (t >= w && t < Tn) {
-      float carry = 0.f;
+  if (m % 8 == 0) {
+    // 8 consecutive slots of one row per thread
+    constexpr int PR = MP / 8, NV = C * PR, IT = (NV + 255) / 256;
+    floatx4 d0[IT], d1[IT];
+    typename Vec<T>::v8 av[IT];
 #pragma unroll
-      for (int k = 0; k < NP; ++k) carry += part[k][ii];
-      const size_t idx = (((size_t)b * Tn + t) * Hkv + hg) * m + ii;
-      dalpha[idx] += carry / to_f<T>(alpha[idx]);
+    for (int k = 0; k < IT; ++k) {
+      const int e = tid + 256 * k, u = e / PR, i0 = (e % PR) * 8, t = t0 + u;
+      const int tc = t < Tn ? t : Tn - 1, ic = i0 < m ? i0 : m - 8;
+      const size_t idx = (((size_t)b * Tn + tc) * Hkv + hg) * m + ic;
+      d0[k] = *reinterpret_cast<const floatx4*>(dalpha + idx);
+      d1[k] = *reinterpret_cast<const floatx4*>(dalpha + idx + 4);
+      av[k] = ld8<T>(alpha + idx);
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int e = tid + 256 * k, u = e / PR, i0 = (e % PR) * 8, t = t0 + u;
+      if (e < NV && i0 < m && t >= w && t < Tn) {
+        const size_t idx = (((size_t)b * Tn + t) * Hkv + hg) * m + i0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          d0[k][r] += carry[i0 + r] / to_f<T>(av[k][r]);
+          d1[k][r] += carry[i0 + 4 + r] / to_f<T>(av[k][4 + r]);
+        }
+        *reinterpret_cast<floatx4*>(dalpha + idx) = d0[k];
+        *reinterpret_cast<floatx4*>(dalpha + idx + 4) = d1[k];
+      }
+    }
+  } else {
+    constexpr int IT = (C * MP + 255) / 256;
+    float dv[IT];
+    T av[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int e = tid + 256 * k, u = e / MP, i = e % MP, t = t0 + u;
+      const int tc = t < Tn ? t : Tn - 1, ic = i < m ? i : m - 1;
+      const size_t idx = (((size_t)b * Tn + tc) * Hkv + hg) * m + ic;
+      dv[k] = dalpha[idx];
+      av[k] = alpha[idx];
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int e = tid + 256 * k, u = e / MP, i = e % MP, t = t0 + u;
+      if (e < C * MP && i < m && t >= w && t < Tn)
+        dalpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i] = dv[k] + carry[i] / to_f<T>(av[k]);
     }
   }
 }
@@ -1012,15 +1081,16 @@ __global__ __launch_bounds__(256) void k_win_bwd_dq(const T* __restrict__ qr, co
   const int q0 = (L % gridDim.x) * 64, bh = L / gridDim.x, b = bh / H, h = bh % H, hg = h / (H / Hkv);
   const int tq = q0 + 16 * W + cc;
   const bool qvalid = tq < Tn;
+  const int tqc = qvalid ? tq : Tn - 1;
   typename Vec<T>::v8 qf[D / 32], df[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    size_t off = (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g;
-    qf[ks] = qvalid ? ld8<T>(qr + off) : zero8<T>();
-    df[ks] = qvalid ? ld8<T>(dO + off) : zero8<T>();
+    const size_t off = (((size_t)b * Tn + tqc) * H + h) * D + 32 * ks + 8 * g;
+    qf[ks] = ld8_sel<T>(qr + off, qvalid);
+    df[ks] = ld8_sel<T>(dO + off, qvalid);
   }
-  const float lse2 = qvalid ? lse[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
-  const float D_t = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  const float lse_r = lse[(size_t)bh * Tn + tqc], lse2 = qvalid ? lse_r * NHA_LOG2E : 0.f;
+  const float D_r = Dt[(size_t)bh * Tn + tqc], D_t = qvalid ? D_r : 0.f;
   const float sl2 = scale * NHA_LOG2E;
   floatx4 acc[D / 16];
 #pragma unroll
@@ -1133,15 +1203,16 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
   const int wl = q0 + 32 * W;
   const int tq = wl + c;
   const bool qvalid = tq < Tn;
-  const size_t qrow = (((size_t)b * Tn + tq) * H + h) * D;
+  const int tqc = qvalid ? tq : Tn - 1;
+  const size_t qrow = (((size_t)b * Tn + tqc) * H + h) * D;
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    qf[ks] = qvalid ? ld8<bf16>(qr + qrow + 16 * ks + 8 * hf) : zero8<bf16>();
-    df[ks] = qvalid ? ld8<bf16>(dO + qrow + 16 * ks + 8 * hf) : zero8<bf16>();
+    qf[ks] = ld8_sel<bf16>(qr + qrow + 16 * ks + 8 * hf, qvalid);
+    df[ks] = ld8_sel<bf16>(dO + qrow + 16 * ks + 8 * hf, qvalid);
   }
-  const float lse2 = qvalid ? lse[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
-  const float Dq = qvalid ? Dt[(size_t)bh * Tn + tq] : 0.f;
+  const float lse_r = lse[(size_t)bh * Tn + tqc], lse2 = qvalid ? lse_r * NHA_LOG2E : 0.f;
+  const float D_r = Dt[(size_t)bh * Tn + tqc], Dq = qvalid ? D_r : 0.f;
   const float sl2 = scale * NHA_LOG2E;
   floatx16 acc[D / 32];
 #pragma unroll
@@ -1306,9 +1377,9 @@ __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
   typename Vec<T>::v8 kf[D / 32], vf[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    size_t off = (((size_t)b * Tn + key) * Hkv + hg) * D + 32 * ks + 8 * g;
-    kf[ks] = kvalid ? ld8<T>(kr + off) : zero8<T>();
-    vf[ks] = kvalid ? ld8<T>(vv + off) : zero8<T>();
+    const size_t off = (((size_t)b * Tn + (kvalid ? key : Tn - 1)) * Hkv + hg) * D + 32 * ks + 8 * g;
+    kf[ks] = ld8_sel<T>(kr + off, kvalid);
+    vf[ks] = ld8_sel<T>(vv + off, kvalid);
   }
   const float sl2 = scale * NHA_LOG2E;
   floatx4 adk[D / 16], adv[D / 16];
@@ -1449,12 +1520,12 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
   const int kl = k0 + 32 * W;  // first key of this wave
   const int key = kl + c;
   const bool kvalid = key < Tn;
-  const size_t krow = (((size_t)b * Tn + key) * Hkv + hg) * D;
+  const size_t krow = (((size_t)b * Tn + (kvalid ? key : Tn - 1)) * Hkv + hg) * D;
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    kf[ks] = kvalid ? ld8<bf16>(kr + krow + 16 * ks + 8 * hf) : zero8<bf16>();
-    vf[ks] = kvalid ? ld8<bf16>(vv + krow + 16 * ks + 8 * hf) : zero8<bf16>();
+    kf[ks] = ld8_sel<bf16>(kr + krow + 16 * ks + 8 * hf, kvalid);
+    vf[ks] = ld8_sel<bf16>(vv + krow + 16 * ks + 8 * hf, kvalid);
   }
   const float sl2 = scale * NHA_LOG2E, inv_s = 1.f / scale;
   floatx16 accK[D / 32], accV[D / 32];
@@ -1675,8 +1746,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
                        (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.w, s.NC);
     mk.mark(st);
-    hipLaunchKernelGGL((k_dalpha_tail<T, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, csum, p.dalpha, s.T, s.Hkv,
-                       s.m, s.w, C, s.NC);
+    hipLaunchKernelGGL((k_dalpha_tail<T, MP, C>), dim3(s.NC, units), dim3(256), 0, st, alpha, csum, p.dalpha, s.T,
+                       s.Hkv, s.m, s.w, s.NC);
     mk.mark(st);
     if constexpr (sizeof(T) == 2) {
       constexpr int NWV = 4;

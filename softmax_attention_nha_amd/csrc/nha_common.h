@@ -144,6 +144,60 @@ __device__ __forceinline__ typename Vec<T>::v8 zero8() {
   for (int i = 0; i < 8; ++i) r[i] = to_t<T>(0.f);
   return r;
 }
+// 8 elements at p when ok, else zeros.  The load itself is unconditional, so
+// p must be readable either way (callers clamp the row): a load under a branch
+// makes the compiler wait for it before the branch joins, which serialises
+// every load issued before it.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 ld8_sel(const T* p, bool ok) {
+  const typename Vec<T>::v8 v = ld8<T>(p);
+  return ok ? v : zero8<T>();
+}
+
+// Buffer-resource loads: a resource covers [p, p + bytes) and a load whose
+// offset falls outside returns zeros without touching memory, so ragged tile
+// edges need neither branches nor masks (the offset is unsigned: a row before
+// the covered range wraps to a huge offset and reads as zeros too).  The
+// resource lives in SGPRs: p and bytes must be uniform over the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  const uintptr_t a = (uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a),
+                 hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uintptr_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+// 16 bytes at byte offset off
+__device__ __forceinline__ bf16x8 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16x8*) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ floatx8 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx8*) {
+  const floatx4 a = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  const floatx4 b = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+  floatx8 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+  return v;
+}
+// 8 elements of T at element offset off (zeros outside the resource)
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return buf_ld16(r, off * (uint32_t)sizeof(T), (typename Vec<T>::v8*)nullptr);
+}
+// Resource over rows [lo, hi) of a row-major tile with leading dimension ld
+// (elements), clipped to [0, rows): element (rr, j) sits at element offset
+// (rr - max(lo, 0)) * ld + j.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, size_t ld, int lo, int hi, int rows,
+                                                           int width, int& first) {
+  first = lo > 0 ? lo : 0;
+  const int last = hi < rows ? hi : rows;
+  const uint32_t bytes = last > first ? (uint32_t)(((size_t)(last - first - 1) * ld + width) * sizeof(T)) : 0u;
+  return buf_rsrc(base + (size_t)first * ld, bytes);
+}
+
 // 8 consecutive elements converted to float.
 template <typename T>
 __device__ __forceinline__ void ld8f(const T* p, float* f) {
@@ -201,12 +255,14 @@ struct RowTile {
   static constexpr int CH = ROWS * D / 8;         // 8-element chunks per tile
   static constexpr int PER = (CH + NT - 1) / NT;  // chunks per thread
   typename Vec<T>::v8 r[PER];
+  // rows rr in [lo, hi) (and < ROWS) are read, the others are zero
   __device__ __forceinline__ void load(const T* __restrict__ base, size_t ld, int lo, int hi, int tid) {
+    int first;
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc<T>(base, ld, lo, hi, ROWS, D, first);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      int e = (tid + k * NT) * 8;
-      int rr = e / D, j = e % D;
-      r[k] = (e < ROWS * D && rr >= lo && rr < hi) ? ld8<T>(base + (size_t)rr * ld + j) : zero8<T>();
+      const int e = (tid + k * NT) * 8, rr = e / D, j = e % D;
+      r[k] = buf_ld8<T>(rs, (uint32_t)((rr - first) * (int)ld + j));
     }
   }
   // LDS layout [ROWS][P] (P = row pitch in elements)
@@ -240,14 +296,14 @@ struct PairTileT {
   static constexpr int PER = (NCH + NG - 1) / NG;    // chunks per thread
   typename Vec<T>::v8 a[PER], b[PER];
   __device__ __forceinline__ void load(const T* __restrict__ base, size_t ld, int lo, int hi, int tid) {
-    int p = tid % NP, cg = tid / NP;
+    const int p = tid % NP, cg = tid / NP;
+    int first;
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc<T>(base, ld, lo, hi, ROWS, D, first);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      int c = cg + k * NG;
-      bool ok = c < NCH && cg < NG;
-      int r0 = 2 * p, r1 = 2 * p + 1;
-      a[k] = (ok && r0 >= lo && r0 < hi) ? ld8<T>(base + (size_t)r0 * ld + 8 * c) : zero8<T>();
-      b[k] = (ok && r1 >= lo && r1 < hi) ? ld8<T>(base + (size_t)r1 * ld + 8 * c) : zero8<T>();
+      const int c = cg + k * NG, cl = c < NCH ? c : NCH - 1;
+      a[k] = buf_ld8<T>(rs, (uint32_t)((2 * p - first) * (int)ld + 8 * cl));
+      b[k] = buf_ld8<T>(rs, (uint32_t)((2 * p + 1 - first) * (int)ld + 8 * cl));
     }
   }
   template <int P>
@@ -258,10 +314,11 @@ struct PairTileT {
       int c = cg + k * NG;
       if (c < NCH && cg < NG) {
         const int col = SWZ ? kswz(2 * p) : 2 * p;
+        const typename Vec<T>::v8 ak = a[k], bk = b[k];
         if constexpr (sizeof(T) == 2) {
           // bf16: word x/2 of each row holds columns x (low half) and x+1
           typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-          u32x4 wa = __builtin_bit_cast(u32x4, a[k]), wb = __builtin_bit_cast(u32x4, b[k]);
+          u32x4 wa = __builtin_bit_cast(u32x4, ak), wb = __builtin_bit_cast(u32x4, bk);
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
             uint32_t v = __builtin_amdgcn_perm(wb[x >> 1], wa[x >> 1], (x & 1) ? 0x07060302u : 0x05040100u);
@@ -272,8 +329,8 @@ struct PairTileT {
           for (int x = 0; x < 8; ++x) {
             typedef T pair_t __attribute__((ext_vector_type(2)));
             pair_t v;
-            v[0] = a[k][x];
-            v[1] = b[k][x];
+            v[0] = ak[x];
+            v[1] = bk[x];
             *reinterpret_cast<pair_t*>(lds + (8 * c + x) * P + col) = v;
           }
         }

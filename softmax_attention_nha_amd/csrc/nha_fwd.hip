@@ -506,7 +506,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
     typename Vec<T>::v8 qf[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      qf[ks] = qvalid ? ld8<T>(q + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<T>();
+      qf[ks] = ld8_sel<T>(q + (((size_t)b * Tn + (qvalid ? tq : Tn - 1)) * H + h) * D + 32 * ks + 8 * g, qvalid);
     float lg[NB][4];
     slot_read<T, D, MP, C>(sm.sSK, sm.sK, sm.sBt, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
     // softmax partial over the m slots (log2 domain)
@@ -578,11 +578,13 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   // chunk row u <-> token t0 + u, absorbing key row t0 + u - w when t0 + u >= w
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
   {
+    GateTile<bf16, C, MP, NT> gt;
     RowTile<bf16, D, NT, MP> ts;
     RowTile<bf16, D, NT, C> tk;
+    gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
     ts.load(src, D, 0, MP, tid);
     tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-    stage_gates<bf16, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+    gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
     ts.template store<PD>(sm.tS, tid);
     tk.template store<PD>(sm.tK, tid);
   }
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   bf16x8 qf[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = qvalid ? ld8<bf16>(q + (((size_t)b * Tn + tq) * H + h) * D + 32 * ks + 8 * g) : zero8<bf16>();
+    qf[ks] = ld8_sel<bf16>(q + (((size_t)b * Tn + (qvalid ? tq : Tn - 1)) * H + h) * D + 32 * ks + 8 * g, qvalid);
   float lg[NB][4];
   slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
   // softmax partial over the m slots (log2 domain)
@@ -689,24 +691,24 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ q
   const int wl = q0 + 32 * W;  // first query of this wave
   const int tq = wl + c;
   const bool qvalid = tq < Tn;
-  const size_t qrow = (((size_t)b * Tn + tq) * H + h) * D;
+  const int tqc = qvalid ? tq : Tn - 1;  // clamped row: loads stay unconditional
+  const size_t qrow = (((size_t)b * Tn + tqc) * H + h) * D;
   typename Vec<T>::v8 qf[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qvalid ? ld8<T>(qr + qrow + 16 * ks + 8 * hf) : zero8<T>();
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8_sel<T>(qr + qrow + 16 * ks + 8 * hf, qvalid);
   // seed with the slot partial
-  float mu = qvalid ? lseL[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
+  const float lse_l = lseL[(size_t)bh * Tn + tqc];  // unconditional load (clamped row)
+  float mu = qvalid ? lse_l * NHA_LOG2E : 0.f;
   float zl = (hf == 0) ? 1.f : 0.f;  // lane-partial normaliser
   floatx16 acc[D / 32];              // O^T: rows d = 32 dt + 8 i + 4 hf + rr, column = query
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     acc[dt] = zero16();
-    if (qvalid) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        typename Vec<T>::v4 x = ld4<T>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
+    for (int i = 0; i < 4; ++i) {
+      typename Vec<T>::v4 x = ld4<T>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = to_f<T>(x[rr]);
-      }
+      for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? to_f<T>(x[rr]) : 0.f;
     }
   }
   const float sl2 = scale * NHA_LOG2E;
@@ -860,23 +862,23 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
   const int wl = q0 + 32 * W;
   const int tq = wl + c;
   const bool qvalid = tq < Tn;
-  const size_t qrow = (((size_t)b * Tn + tq) * H + h) * D;
+  const int tqc = qvalid ? tq : Tn - 1;  // clamped row: loads stay unconditional
+  const size_t qrow = (((size_t)b * Tn + tqc) * H + h) * D;
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qvalid ? ld8<bf16>(qr + qrow + 16 * ks + 8 * hf) : zero8<bf16>();
-  float mu = qvalid ? lseL[(size_t)bh * Tn + tq] * NHA_LOG2E : 0.f;
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8_sel<bf16>(qr + qrow + 16 * ks + 8 * hf, qvalid);
+  const float lse_l = lseL[(size_t)bh * Tn + tqc];  // unconditional load (clamped row)
+  float mu = qvalid ? lse_l * NHA_LOG2E : 0.f;
   float zl = (hf == 0) ? 1.f : 0.f;
   floatx16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     acc[dt] = zero16();
-    if (qvalid) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 x = ld4<bf16>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 x = ld4<bf16>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = (float)x[rr];
-      }
+      for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? (float)x[rr] : 0.f;
     }
   }
   // per-lane LDS element offsets of the K fragments (row c, logical chunk

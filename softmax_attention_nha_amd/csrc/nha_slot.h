@@ -56,20 +56,71 @@ __device__ __forceinline__ void lds_col_cumsum(float* g, int tid) {
   __syncthreads();
 }
 
-// Stage a chunk's gates into LDS: la[u][i] = log2 a_u (0 where nothing is
-// absorbed: t < w, t >= T or padded slot), al[u][i] = raw alpha (1 outside).
+// A chunk's gates, staged into LDS as la[u][i] = log2 a_u (0 where nothing
+// is absorbed: t < w, t >= T or padded slot) and al[u][i] = raw alpha (1
+// outside).  load() issues every load of the tile (rows and slots clamped into
+// range, so no load is conditional) and stage() consumes them: issuing load()
+// before other tiles' loads lets stage() wait for the gates alone.  16-byte
+// pieces of the rows when m is a multiple of 8, else one element per load.
+template <typename T, int C, int MP, int NT>
+struct GateTile {
+  static constexpr int PR = MP / 8, NV = C * PR, ITV = (NV + NT - 1) / NT, ITS = (C * MP + NT - 1) / NT;
+  typename Vec<T>::v8 xv[ITV];
+  T xs[ITS];
+  __device__ __forceinline__ void load(const T* __restrict__ alpha, int b, int hg, int t0, int Tn, int Hkv, int m,
+                                       int tid) {
+    if (m % 8 == 0) {
+#pragma unroll
+      for (int k = 0; k < ITV; ++k) {
+        const int e = tid + k * NT, u = e / PR, i0 = (e % PR) * 8, t = t0 + u;
+        xv[k] = ld8<T>(alpha + (((size_t)b * Tn + (t < Tn ? t : Tn - 1)) * Hkv + hg) * m + (i0 < m ? i0 : m - 8));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < ITS; ++k) {
+        const int e = tid + k * NT, u = e / MP, i = e % MP, t = t0 + u;
+        xs[k] = alpha[(((size_t)b * Tn + (t < Tn ? t : Tn - 1)) * Hkv + hg) * m + (i < m ? i : m - 1)];
+      }
+    }
+  }
+  template <int PG, int PA>
+  __device__ __forceinline__ void stage(float* la, T* al, int t0, int Tn, int m, int w, int tid) const {
+    const T one = to_t<T>(1.f);
+    if (m % 8 == 0) {
+#pragma unroll
+      for (int k = 0; k < ITV; ++k) {
+        const int e = tid + k * NT, u = e / PR, i0 = (e % PR) * 8, t = t0 + u;
+        if (e < NV) {
+          const bool real = i0 < m && t < Tn, act = real && t >= w;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const T av = real ? xv[k][j] : one;
+            la[u * PG + i0 + j] = act ? fmaxf(__log2f(to_f<T>(av)), NHA_LOG2A_MIN) : 0.f;
+            al[u * PA + i0 + j] = av;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < ITS; ++k) {
+        const int e = tid + k * NT, u = e / MP, i = e % MP, t = t0 + u;
+        if (e < C * MP) {
+          const bool real = i < m && t < Tn;
+          const T av = real ? xs[k] : one;
+          la[u * PG + i] = (real && t >= w) ? fmaxf(__log2f(to_f<T>(av)), NHA_LOG2A_MIN) : 0.f;
+          al[u * PA + i] = av;
+        }
+      }
+    }
+  }
+};
+
 template <typename T, int C, int MP, int PG, int PA, int NT>
 __device__ __forceinline__ void stage_gates(const T* __restrict__ alpha, float* la, T* al, int b, int hg, int t0,
                                             int Tn, int Hkv, int m, int w, int tid) {
-  for (int e = tid; e < C * MP; e += NT) {
-    int u = e / MP, i = e % MP, t = t0 + u;
-    T av = to_t<T>(1.f);
-    if (i < m && t < Tn) av = alpha[(((size_t)b * Tn + t) * Hkv + hg) * m + i];
-    float l2 = 0.f;
-    if (i < m && t < Tn && t >= w) l2 = fmaxf(__log2f(to_f<T>(av)), NHA_LOG2A_MIN);
-    la[u * PG + i] = l2;
-    al[u * PA + i] = av;
-  }
+  GateTile<T, C, MP, NT> gt;
+  gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
+  gt.template stage<PG, PA>(la, al, t0, Tn, m, w, tid);
 }
 
 // ---------------------------------------------------------------- intra-chunk slot products
