@@ -44,7 +44,8 @@ struct BwdWs {
   size_t dqs;                        // slot part of dq: [B][T][H][d] float
   size_t wp;                         // adjoint weights: [B*H][NC][2][mp][C] dtype
   size_t sdl, pp, acon;              // [B*H][NC*C][mp] float
-  size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp][d] dtype
+  size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp x d] dtype
+                                     // (fp32 [i][d] rows, bf16 column blocks [d/16][i][16])
   size_t dkap, dnu;                  // slot parts of dk, dv at the key row: [B][T][Hkv][d] float
   size_t csum;                       // [B*Hkv][NC][mp] float
   size_t total;
@@ -466,10 +467,10 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
   {
     GateTile<bf16, C, MP, NT> gt;
-    RowTile<bf16, D, NT, MP> ts;
+    BlockedTile<bf16, D, NT, MP> ts;
     RowTile<bf16, D, NT, C> tk;
     gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
-    ts.load(src + (size_t)MP * D, D, 0, MP, tid);
+    ts.load(src + (size_t)MP * D, tid);
     tk.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
     gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
     ts.template store<PD>(sm.tS, tid);
@@ -483,9 +484,9 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
     sm.sB[u * PM + i] = (bf16)(fast_exp2(sm.sG[(u | 15) * PG + i] - sm.sG[u * PG + i]) * be);
   }
   __syncthreads();
-  RowTile<bf16, D, NT, MP> tsk;
+  BlockedTile<bf16, D, NT, MP> tsk;
   RowTile<bf16, D, NT, C> tkap;
-  tsk.load(src, D, 0, MP, tid);
+  tsk.load(src, tid);
   tkap.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
 
   const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
@@ -730,13 +731,14 @@ __global__ __launch_bounds__(64) void k_adj_scan_b16(const bf16* __restrict__ q,
     vm_wait<(NS - 1) * St::OPS>();
     const St& R = ring[s];
     if (hh == 0) {
-      // the adjoint entering chunk c from the right, [i][d] layout
-      bf16* dst = lin + ((size_t)unit * NC + c) * 2 * MP * d;
+      // the adjoint entering chunk c from the right, both halves in column
+      // blocks [d/16][i][16] (one contiguous 2 KB piece per half for this wave)
+      bf16* dst = lin + ((size_t)unit * NC + c) * 2 * MP * d + (size_t)j0 * MP;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int i = 16 * nb + cc;
-        st4<bf16>(dst + (size_t)i * d + j0 + 4 * g, pack4<bf16>(LK[nb]));
-        st4<bf16>(dst + (size_t)MP * d + (size_t)i * d + j0 + 4 * g, pack4<bf16>(LV[nb]));
+        st4<bf16>(dst + i * 16 + 4 * g, pack4<bf16>(LK[nb]));
+        st4<bf16>(dst + (size_t)MP * d + i * 16 + 4 * g, pack4<bf16>(LV[nb]));
         const float a = R.ae[i];
         LK[nb] *= a;
         LV[nb] *= a;
@@ -832,10 +834,14 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
     __syncthreads();
     {
       const T* src = lin + (((size_t)unit * NC + c) * 2 + side) * MP * D;
-      RowTile<T, D, NT, MP> tl;
-      tl.load(src, D, 0, MP, tid);
-      tl.template store<PD>(sm.sL, tid);
-      if constexpr (!S::TR) {
+      if constexpr (S::TR) {  // bf16 adjoints are stored in column blocks [d/16][i][16]
+        BlockedTile<T, D, NT, MP> tl;
+        tl.load(src, tid);
+        tl.template store<PD>(sm.sL, tid);
+      } else {
+        RowTile<T, D, NT, MP> tl;
+        tl.load(src, D, 0, MP, tid);
+        tl.template store<PD>(sm.sL, tid);
         PairTileT<T, D, NT, MP> tlt;
         tlt.load(src, D, 0, MP, tid);
         tlt.template store<PM>(sm.sLt, tid);

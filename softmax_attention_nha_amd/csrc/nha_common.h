@@ -276,6 +276,31 @@ struct RowTile {
   }
 };
 
+// A [ROWS][D] tile kept in HBM in column blocks of 16, [D / 16][ROWS][16]
+// (what a scan wave owning 16 columns writes contiguously), loaded with
+// contiguous 16-byte pieces and stored to LDS in row layout [ROWS][P].
+template <typename T, int D, int NT, int ROWS>
+struct BlockedTile {
+  static constexpr int CH = ROWS * D / 8;
+  static constexpr int PER = (CH + NT - 1) / NT;
+  typename Vec<T>::v8 r[PER];
+  __device__ __forceinline__ void load(const T* __restrict__ src, int tid) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int q = tid + k * NT;
+      r[k] = ld8<T>(src + 8 * (q < CH ? q : CH - 1));
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int q = tid + k * NT, e = 8 * q, jb = e / (ROWS * 16), rem = e % (ROWS * 16);
+      if (q < CH) st8<T>(lds + (rem / 16) * P + 16 * jb + (rem % 16), r[k]);
+    }
+  }
+};
+
 // Position of row k inside a transposed row when SWZ is set: bits 2 and 3 of
 // k trade places, so that within every 16-row group the rows {4h + r} and
 // {8 + 4h + r} (h = 0, 1; r = 0..3) -- the K=16 step of a 32x32 product fed

@@ -332,13 +332,14 @@ __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ 
     // state stores of the steps since (2 NB each) may still be in flight
     vm_wait_steps<NS, St::OPS, 2 * NB>(c);
     const St& R = ring[s];
-    // state at the chunk start, [i][d] layout for both halves
-    bf16* dst = sst + ((size_t)unit * NC + c) * chunk_elems;
+    // state at the chunk start, both halves in column blocks [d/16][i][16]:
+    // this wave's block is one contiguous 2 KB piece of each half
+    bf16* dst = sst + ((size_t)unit * NC + c) * chunk_elems + (size_t)j0 * MP;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int i = 16 * nb + cc;
-      st4<bf16>(dst + (size_t)i * d + j0 + 4 * g, pack4<bf16>(SK[nb]));
-      st4<bf16>(dst + (size_t)MP * d + (size_t)i * d + j0 + 4 * g, pack4<bf16>(SV[nb]));
+      st4<bf16>(dst + i * 16 + 4 * g, pack4<bf16>(SK[nb]));
+      st4<bf16>(dst + (size_t)MP * d + i * 16 + 4 * g, pack4<bf16>(SV[nb]));
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -579,10 +580,10 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
   {
     GateTile<bf16, C, MP, NT> gt;
-    RowTile<bf16, D, NT, MP> ts;
+    BlockedTile<bf16, D, NT, MP> ts;
     RowTile<bf16, D, NT, C> tk;
     gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
-    ts.load(src, D, 0, MP, tid);
+    ts.load(src, tid);
     tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
     gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
     ts.template store<PD>(sm.tS, tid);
@@ -597,9 +598,9 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   }
   __syncthreads();
   // the output phase's tiles: loads in flight during the logits
-  RowTile<bf16, D, NT, MP> tsv;
+  BlockedTile<bf16, D, NT, MP> tsv;
   RowTile<bf16, D, NT, C> tnu;
-  tsv.load(src + (size_t)MP * D, D, 0, MP, tid);
+  tsv.load(src + (size_t)MP * D, tid);
   tnu.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
 
   const int r0 = 16 * I;

@@ -33,7 +33,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Forward workspace carve-up (offsets in bytes from the workspace base).
 struct FwdWs {
-  size_t sst;    // chunk-start states: [B*Hkv][NC][ SK | SV ], each mp x d, [i][d]   (dtype)
+  size_t sst;    // chunk-start states: [B*Hkv][NC][ SK | SV ], each mp x d (dtype): fp32 as
+                 // [i][d] rows, bf16 in column blocks [d/16][i][16]
   size_t wt;     // per-chunk absorption weights W^T: [B*Hkv][NC][mp][C]       (dtype)
   size_t aend;   // per-chunk decay exp(G_end): [B*Hkv][NC][mp]                (float)
   size_t qrot;   // RoPE'd q: [B][T][H][d]                                       (dtype)
