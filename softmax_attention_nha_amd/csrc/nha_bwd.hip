@@ -46,7 +46,7 @@ struct BwdWs {
   size_t sdl, pp, acon;              // [B*H][NC*C][mp] float
   size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp x d] dtype
                                      // (fp32 [i][d] rows, bf16 column blocks [d/16][i][16])
-  size_t dkap, dnu;                  // slot parts of dk, dv at the key row: [B][T][Hkv][d] float
+  size_t dkap, dnu;                  // slot parts of dk, dv at the key row: [B][T][Hkv][d] dtype
   size_t csum;                       // [B*Hkv][NC][mp] float
   size_t total;
 };
@@ -77,9 +77,9 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   L.lin = off;
   off += align256(units * s.NC * 2 * (size_t)s.mp * s.d * s.esz);
   L.dkap = off;
-  off += align256((size_t)s.B * s.T * s.Hkv * s.d * 4);
+  off += align256((size_t)s.B * s.T * s.Hkv * s.d * s.esz);
   L.dnu = off;
-  off += align256((size_t)s.B * s.T * s.Hkv * s.d * 4);
+  off += align256((size_t)s.B * s.T * s.Hkv * s.d * s.esz);
   L.csum = off;
   off += align256(units * s.NC * s.mp * 4);
   L.total = off;
@@ -801,8 +801,8 @@ template <typename T, int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slot_b(
     const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
     const T* __restrict__ dO, const T* __restrict__ lin, const float* __restrict__ sdl,
-    const float* __restrict__ pp, const float* __restrict__ acon, float* __restrict__ dkap,
-    float* __restrict__ dnu, float* __restrict__ dalpha, float* __restrict__ csum, int Tn, int H, int Hkv, int m,
+    const float* __restrict__ pp, const float* __restrict__ acon, T* __restrict__ dkap,
+    T* __restrict__ dnu, float* __restrict__ dalpha, float* __restrict__ csum, int Tn, int H, int Hkv, int m,
     int w, int NC) {
   using S = SlotBwdBSmem<T, D, MP, C>;
   constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
@@ -924,9 +924,9 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
       slot_rev<T, D, MP, C>(sm.sVec, sm.sVecT, sm.sW, sm.sG, sm.sA, keyf, bwI, bt, I, t0, w, Tn, accO, F);
     }
     if (absorb) {
-      float* dst = (side ? dnu : dkap) + (((size_t)b * Tn + (tq - w)) * Hkv + hg) * D;
+      T* dst = (side ? dnu : dkap) + (((size_t)b * Tn + (tq - w)) * Hkv + hg) * D;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) *reinterpret_cast<floatx4*>(dst + 16 * db + 4 * g) = accO[db];
+      for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db]));
     }
   }
   // X_t = A_t - b_t F_t, its reverse cumsum inside the chunk, local dalpha
@@ -1369,8 +1369,8 @@ struct WinBwdKvSmem {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
     const T* __restrict__ qr, const T* __restrict__ kr, const T* __restrict__ vv, const T* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dt, const float* __restrict__ dkap,
-    const float* __restrict__ dnu, T* __restrict__ dk, T* __restrict__ dv, int Tn, int H, int Hkv, int w,
+    const float* __restrict__ lse, const float* __restrict__ Dt, const T* __restrict__ dkap,
+    const T* __restrict__ dnu, T* __restrict__ dk, T* __restrict__ dv, int Tn, int H, int Hkv, int w,
     float scale, RopeTheta th, int rope) {
   using S = WinBwdKvSmem<T, D>;
   constexpr int PD = S::PD, PK = S::PK;
@@ -1488,8 +1488,12 @@ __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
     for (int db = 0; db < D / 16; ++db) {
       floatx4 sk = zero4(), sv = zero4();
       if (slot) {
-        sk = *reinterpret_cast<const floatx4*>(dkap + row + 16 * db + 4 * g);
-        sv = *reinterpret_cast<const floatx4*>(dnu + row + 16 * db + 4 * g);
+        const typename Vec<T>::v4 xk = ld4<T>(dkap + row + 16 * db + 4 * g), xv = ld4<T>(dnu + row + 16 * db + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sk[r] = to_f<T>(xk[r]);
+          sv[r] = to_f<T>(xv[r]);
+        }
       }
       st4<T>(dk + row + 16 * db + 4 * g,
              pack4<T>(floatx4{ok[db][0] + sk[0], ok[db][1] + sk[1], ok[db][2] + sk[2], ok[db][3] + sk[3]}));
@@ -1510,7 +1514,7 @@ template <int D, int NWV>
 __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vv,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dt,
-    const float* __restrict__ dkap, const float* __restrict__ dnu, const float2* __restrict__ rcs,
+    const bf16* __restrict__ dkap, const bf16* __restrict__ dnu, const float2* __restrict__ rcs,
     bf16* __restrict__ dk, bf16* __restrict__ dv, int Tn, int H, int Hkv, int w, float scale) {
   constexpr int NT = NWV * 64, KT = 32 * NWV;
   __shared__ bf16 qbuf[2][64 * D];
@@ -1675,8 +1679,12 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
         const int d = 32 * dt + 8 * i + 4 * hf;
         floatx4 sk = zero4(), sv = zero4();
         if (slot) {
-          sk = *reinterpret_cast<const floatx4*>(dkap + krow + d);
-          sv = *reinterpret_cast<const floatx4*>(dnu + krow + d);
+          const bf16x4 xk = ld4<bf16>(dkap + krow + d), xv = ld4<bf16>(dnu + krow + d);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sk[r] = (float)xk[r];
+            sv[r] = (float)xv[r];
+          }
         }
         st4<bf16>(dk + krow + d, pack4<bf16>(floatx4{ok[dt][4 * i] + sk[0], ok[dt][4 * i + 1] + sk[1],
                                                      ok[dt][4 * i + 2] + sk[2], ok[dt][4 * i + 3] + sk[3]}));
@@ -1722,8 +1730,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     float* ppb = (float*)(ws + L.pp);
     float* acon = (float*)(ws + L.acon);
     T* lin = (T*)(ws + L.lin);
-    float* dkap = (float*)(ws + L.dkap);
-    float* dnu = (float*)(ws + L.dnu);
+    T* dkap = (T*)(ws + L.dkap);
+    T* dnu = (T*)(ws + L.dnu);
     float* csum = (float*)(ws + L.csum);
     const long nrows = (long)s.B * s.T * s.H;
     mk.mark(st);
