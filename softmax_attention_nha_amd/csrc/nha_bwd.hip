@@ -41,7 +41,7 @@ namespace nha {
 struct BwdWs {
   size_t sst, wt, aend, qrot, krot, rcs;  // prologue (same meaning as the forward's)
   size_t dt;                         // D_t: [B][H][T] float
-  size_t dqs;                        // slot part of dq: [B][T][H][d] float
+  size_t dqs;                        // slot part of dq: [B][T][H][d] dtype
   size_t wp;                         // adjoint weights: [B*H][NC][2][mp][C] dtype
   size_t sdl, pp, acon;              // [B*H][NC*C][mp] float
   size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp x d] dtype
@@ -65,7 +65,7 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   L.dt = off;
   off += align256(BH * s.T * 4);
   L.dqs = off;
-  off += align256((size_t)s.B * s.T * s.H * s.d * 4);
+  off += align256((size_t)s.B * s.T * s.H * s.d * s.esz);
   L.wp = off;
   off += align256(BH * s.NC * 2 * (size_t)s.mp * s.C * s.esz);
   L.sdl = off;
@@ -313,7 +313,7 @@ template <typename T, int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
     const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
     const T* __restrict__ dO, const T* __restrict__ sst, const float* __restrict__ lse,
-    const float* __restrict__ Dt, float* __restrict__ dqs, T* __restrict__ wp, float* __restrict__ sdl,
+    const float* __restrict__ Dt, T* __restrict__ dqs, T* __restrict__ wp, float* __restrict__ sdl,
     float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m, int w, int NC, int nitems,
     float scale) {
   using S = SlotBwdASmem<T, D, MP, C>;
@@ -415,9 +415,9 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_slot_a(
   for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
   slot_mix<T, D, MP, C, PC>(sm.sSKt, sm.sKt, sm.sB, sm.sG, sm.sA, dl, I, t0, w, Tn, accO);
   if (qvalid) {
-    float* dst = dqs + (((size_t)b * Tn + tq) * H + h) * D;
+    T* dst = dqs + (((size_t)b * Tn + tq) * H + h) * D;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<floatx4*>(dst + 16 * db + 4 * g) = accO[db] * scale;
+    for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db] * scale));
   }
   // adjoint weights 2^{G_u} s dl_u[i] and 2^{G_u} p_u[i], [i][u] layout
   T* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
@@ -452,7 +452,7 @@ template <int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
     const bf16* __restrict__ alpha, const bf16* __restrict__ dO, const bf16* __restrict__ sst,
-    const float* __restrict__ lse, const float* __restrict__ Dt, float* __restrict__ dqs, bf16* __restrict__ wp,
+    const float* __restrict__ lse, const float* __restrict__ Dt, bf16* __restrict__ dqs, bf16* __restrict__ wp,
     float* __restrict__ sdl, float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m,
     int w, int NC, float scale) {
   using S = SlotBwdASmemB16<D, MP, C>;
@@ -537,9 +537,9 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
   slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, dl, I, t0, w, Tn, accO);
   if (qvalid) {
-    float* dst = dqs + (((size_t)b * Tn + tq) * H + h) * D;
+    bf16* dst = dqs + (((size_t)b * Tn + tq) * H + h) * D;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<floatx4*>(dst + 16 * db + 4 * g) = accO[db] * scale;
+    for (int db = 0; db < D / 16; ++db) st4<bf16>(dst + 16 * db + 4 * g, pack4<bf16>(accO[db] * scale));
   }
   // adjoint weights 2^{G_u} s dl_u[i] and 2^{G_u} p_u[i], [i][u] layout
   bf16* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
@@ -1077,7 +1077,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_win_bwd_dq(const T* __restrict__ qr, const T* __restrict__ kr,
                                                        const T* __restrict__ vv, const T* __restrict__ dO,
                                                        const float* __restrict__ lse, const float* __restrict__ Dt,
-                                                       const float* __restrict__ dqs, T* __restrict__ dq, int Tn,
+                                                       const T* __restrict__ dqs, T* __restrict__ dq, int Tn,
                                                        int H, int Hkv, int w, float scale, RopeTheta th, int rope) {
   using S = WinBwdDqSmem<T, D>;
   constexpr int PD = S::PD, PK = S::PK;
@@ -1174,11 +1174,14 @@ __global__ __launch_bounds__(256) void k_win_bwd_dq(const T* __restrict__ qr, co
         out[db][r] = x1 * cs + x2 * sn;
         out[db + HB][r] = x2 * cs - x1 * sn;
       }
-    const float* sl = dqs + (((size_t)b * Tn + tq) * H + h) * D;
+    const T* sl = dqs + (((size_t)b * Tn + tq) * H + h) * D;
     T* dst = dq + (((size_t)b * Tn + tq) * H + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      floatx4 s4 = *reinterpret_cast<const floatx4*>(sl + 16 * db + 4 * g);
+      const typename Vec<T>::v4 x4 = ld4<T>(sl + 16 * db + 4 * g);
+      floatx4 s4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s4[r] = to_f<T>(x4[r]);
       st4<T>(dst + 16 * db + 4 * g,
              pack4<T>(floatx4{out[db][0] + s4[0], out[db][1] + s4[1], out[db][2] + s4[2], out[db][3] + s4[3]}));
     }
@@ -1195,7 +1198,7 @@ template <int D, int NWV>
 __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vv,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dt,
-    const float* __restrict__ dqs, const float2* __restrict__ rcs, bf16* __restrict__ dq, int Tn, int H, int Hkv,
+    const bf16* __restrict__ dqs, const float2* __restrict__ rcs, bf16* __restrict__ dq, int Tn, int H, int Hkv,
     int w, float scale) {
   constexpr int NT = NWV * 64, QT = 32 * NWV;
   __shared__ bf16 kbuf[2][64 * D];
@@ -1337,14 +1340,15 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
         }
       }
     }
-    const float* sl = dqs + qrow;
+    const bf16* sl = dqs + qrow;
     bf16* dst = dq + qrow;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * dt + 8 * i + 4 * hf;
-        const floatx4 s4 = *reinterpret_cast<const floatx4*>(sl + d);
+        const bf16x4 x4 = ld4<bf16>(sl + d);
+        const floatx4 s4{(float)x4[0], (float)x4[1], (float)x4[2], (float)x4[3]};
         st4<bf16>(dst + d, pack4<bf16>(floatx4{out[dt][4 * i] + s4[0], out[dt][4 * i + 1] + s4[1],
                                                 out[dt][4 * i + 2] + s4[2], out[dt][4 * i + 3] + s4[3]}));
       }
@@ -1724,7 +1728,7 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
     float* Dt = (float*)(ws + L.dt);
-    float* dqs = (float*)(ws + L.dqs);
+    T* dqs = (T*)(ws + L.dqs);
     T* wpb = (T*)(ws + L.wp);
     float* sdl = (float*)(ws + L.sdl);
     float* ppb = (float*)(ws + L.pp);
