@@ -134,6 +134,11 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
   // unrolling only multiplies the live registers)
   const bool fast = block_factorizable<MP>(sG, r0);
   floatx4 aI = zero4();  // A[u][t] = vec_u . key_t for the wave's own block (exact path)
+  // sum over the blocks of Y^T A; its factor 2^{G_rl - G_t} does not depend on
+  // the block and is applied once after the loop
+  floatx4 xs[NB];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) xs[mb] = zero4();
 #pragma unroll 1
   for (int J = I; J < NW; ++J) {
     floatx4 aJ = zero4();  // D layout [u = 16J + 4g + r][t = cc]
@@ -187,15 +192,17 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
           int u = 16 * J + 4 * g + r;
           y[r] = sW[u * PG + iA] * fast_exp2(sG[u * PG + iA] - sG[rl * PG + iA]);
         }
-        floatx4 x = mma16(zero4(), pack4<T>(y), afr);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int i = 16 * mb + 4 * g + r;
-          F[mb][r] += fast_exp2(sG[rl * PG + i] - sG[urow * PG + i]) * x[r];
-        }
+        xs[mb] = mma16(xs[mb], pack4<T>(y), afr);
       }
     }
   }
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * mb + 4 * g + r;
+      F[mb][r] += fast_exp2(sG[rl * PG + i] - sG[urow * PG + i]) * xs[mb][r];
+    }
   if (fast) return;
   // same block: u >= t, exact running products D'_{t,u} = prod_{j=t+1..u} a_j
   float Ad[16];
