@@ -23,7 +23,7 @@
 // right obeys Lin_{c-1} = 2^{G_end} Lin_c + sum_{u in c} 2^{G_u} dS_u.
 //
 // Kernels, in launch order (after the shared prologue: RoPE, gates, state scan):
-//   k_bwd_prep      D_t = <dO_t, o_t>
+//   k_bwd_prep      D_t = <dO_t, o_t> (fp32; bf16 computes it in slot pass A)
 //   k_bwd_slot_a    per (b, h, chunk): slot p, dp, dl; dq's slot part;
 //                   adjoint weights 2^{G_u} s dl_u, 2^{G_u} p_u; A_t parts
 //   k_adj_scan      reverse over chunks: Lin_c for every chunk (MFMA)
@@ -458,8 +458,9 @@ struct SlotBwdASmemB16 {
 template <int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
-    const bf16* __restrict__ alpha, const bf16* __restrict__ dO, const bf16* __restrict__ sst,
-    const float* __restrict__ lse, const float* __restrict__ Dt, bf16* __restrict__ dqs, bf16* __restrict__ wp,
+    const bf16* __restrict__ alpha, const bf16* __restrict__ dO, const bf16* __restrict__ o,
+    const bf16* __restrict__ sst, const float* __restrict__ lse, float* __restrict__ Dt, bf16* __restrict__ dqs,
+    bf16* __restrict__ wp,
     float* __restrict__ sdl, float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m,
     int w, int NC, float scale) {
   using S = SlotBwdASmemB16<D, MP, C>;
@@ -499,15 +500,24 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
   const bool qvalid = tq < Tn;
   const int tqc = qvalid ? tq : Tn - 1;  // clamped row: loads stay unconditional
-  bf16x8 qf[D / 32], df[D / 32];
+  bf16x8 qf[D / 32], df[D / 32], of[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
     const size_t off = (((size_t)b * Tn + tqc) * H + h) * D + 32 * ks + 8 * g;
     qf[ks] = ld8_sel<bf16>(q + off, qvalid);
     df[ks] = ld8_sel<bf16>(dO + off, qvalid);
+    of[ks] = ld8<bf16>(o + off);
   }
   const float lse_r = lse[(size_t)bh * Tn + tqc], lse_t = qvalid ? lse_r : 0.f;
-  const float D_r = Dt[(size_t)bh * Tn + tqc], D_t = qvalid ? D_r : 0.f;
+  // D_t = <dO_t, o_t>: the four lanes of a query hold a quarter of the row
+  // each; written here for the window kernels
+  float D_t = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) D_t += (float)df[ks][e] * (float)of[ks][e];
+  D_t = sum_over_g(D_t);
+  if (qvalid && g == 0) Dt[(size_t)bh * Tn + tq] = D_t;
   float lg[NB][4], dp[NB][4];
   slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, df, I, t0, w, Tn, dp);
   __syncthreads();  // every wave is done with S0^V and nu
@@ -838,6 +848,14 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
 #pragma unroll 1
   for (int side = 0; side < 2; ++side) {
+    // this lane's absorbed key row (zero where nothing is absorbed; the
+    // address is clamped to a real row either way), loaded together with the
+    // incoming adjoint tile
+    const size_t krow = (((size_t)b * Tn + min(max(tq - w, 0), Tn - 1)) * Hkv + hg) * D;
+    typename Vec<T>::v8 keyf[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      keyf[ks] = ld8_sel<T>((side ? vv : kk) + krow + 32 * ks + 8 * g, absorb);
     __syncthreads();
     {
       const T* src = lin + (((size_t)unit * NC + c) * 2 + side) * MP * D;
@@ -854,13 +872,6 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
         tlt.template store<PM>(sm.sLt, tid);
       }
     }
-    // this lane's absorbed key row (zero where nothing is absorbed; the
-    // address is clamped to a real row either way)
-    const size_t krow = (((size_t)b * Tn + min(max(tq - w, 0), Tn - 1)) * Hkv + hg) * D;
-    typename Vec<T>::v8 keyf[D / 32];
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      keyf[ks] = ld8_sel<T>((side ? vv : kk) + krow + 32 * ks + 8 * g, absorb);
     __syncthreads();
     floatx4 accO[D / 16];
 #pragma unroll
@@ -1745,15 +1756,17 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     T* dnu = (T*)(ws + L.dnu);
     float* csum = (float*)(ws + L.csum);
     const long nrows = (long)s.B * s.T * s.H;
-    mk.mark(st);
-    hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
-                       (const T*)p.o, dO, Dt, s.T, s.H, nrows);
-    mk.mark(st);
     if constexpr (sizeof(T) == 2) {
+      // bf16: pass A also computes D_t
+      mk.mark(st);
       hipLaunchKernelGGL((k_bwd_slot_a_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v,
-                         alpha, dO, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w,
-                         s.NC, s.scale);
+                         alpha, dO, (const T*)p.o, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H,
+                         s.Hkv, s.m, s.w, s.NC, s.scale);
     } else {
+      mk.mark(st);
+      hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
+                         (const T*)p.o, dO, Dt, s.T, s.H, nrows);
+      mk.mark(st);
       const int nitems = s.NC * s.B * s.H;
       const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
       hipLaunchKernelGGL((k_bwd_slot_a<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
@@ -1829,7 +1842,7 @@ int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max) {
     all[n++] = "chunk_gates";
     all[n++] = "state_scan";
   }
-  all[n++] = "bwd_prep";
+  if (s.dtype != NHA_DTYPE_BF16) all[n++] = "bwd_prep";  // bf16: inside slot pass A
   all[n++] = "slot_bwd_a";
   all[n++] = "adj_scan";
   all[n++] = "slot_bwd_b";
