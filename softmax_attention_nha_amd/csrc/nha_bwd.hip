@@ -558,18 +558,35 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) st4<bf16>(dst + 16 * db + 4 * g, pack4<bf16>(accO[db] * scale));
   }
-  // adjoint weights 2^{G_u} s dl_u[i] and 2^{G_u} p_u[i], [i][u] layout
-  bf16* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
-  bf16* wv = wk + (size_t)MP * C;
+  // adjoint weights 2^{G_u} s dl_u[i] and 2^{G_u} p_u[i], [i][u] layout:
+  // transposed through LDS (the row tiles are free once every wave is done)
+  // and written with 16-byte stores
+  float ew[NB][4];
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ew[mb][r] = fast_exp2(sm.sG[urow * PG + 16 * mb + 4 * g + r]);
+  __syncthreads();
+  constexpr int PW = C + 8;  // row pitch of the [i][u] staging tiles
+  static_assert(2 * MP * PW * sizeof(bf16) <= sizeof(S), "staging tiles fit the shared tiles");
+  bf16* tw_k = reinterpret_cast<bf16*>(&sm);
+  bf16* tw_v = tw_k + MP * PW;
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * mb + 4 * g + r;
-      const float e = fast_exp2(sm.sG[urow * PG + i]);
-      wk[(size_t)i * C + urow] = (bf16)(e * scale * dl[mb][r]);
-      wv[(size_t)i * C + urow] = (bf16)(e * p[mb][r]);
+      tw_k[i * PW + urow] = (bf16)(ew[mb][r] * scale * dl[mb][r]);
+      tw_v[i * PW + urow] = (bf16)(ew[mb][r] * p[mb][r]);
     }
+  __syncthreads();
+  bf16* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
+  bf16* wv = wk + (size_t)MP * C;
+  for (int e = tid * 8; e < MP * C; e += NT * 8) {
+    const int i = e / C, u = e % C;
+    st8<bf16>(wk + e, *reinterpret_cast<const bf16x8*>(&tw_k[i * PW + u]));
+    st8<bf16>(wv + e, *reinterpret_cast<const bf16x8*>(&tw_v[i * PW + u]));
+  }
 }
 
 // ---------------------------------------------------------------- adjoint scan
