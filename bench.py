@@ -83,39 +83,72 @@ def bytes_fwd(wl, e):
 
 
 def stage_work(stage, wl, w, e):
-    """(bound, algorithmic work per launch, unit) of every kernel launch.
+    """(flops, bytes) of one launch of `stage`: the algorithmic flops of the
+    part of the method it computes, and the bytes it must move given the
+    data each kernel reads and writes (its inputs and outputs, each once).
 
-    Window kernels: flops per (query, in-window key) pair -- forward 4d (QK^T,
-    PV), dq pass 6d (QK^T, dO V^T, dS K), dk/dv pass 8d (QK^T, dO V^T, P^T dO,
-    dS^T Q).  Slot kernels, per query t >= w with c(t) earlier absorbed rows of
-    its chunk: one read (2md + (2d+2m)c) and one mix (same) in the forward;
-    two reads and one mix in pass A of the backward; two reverse reads and two
-    reverse mixes in pass B.  Scans: 4md per absorbed token per KV head
-    (forward) and per token per query head (adjoint).  Memory-bound helpers:
-    the bytes they must move."""
+    Flops: window kernels 4d per (query, in-window key) pair in the forward,
+    6d (dq pass: QK^T, dO V^T, dS K) and 8d (dk/dv pass: QK^T, dO V^T, P^T dO,
+    dS^T Q) in the backward; slot kernels, per query t >= w with c(t) earlier
+    absorbed rows of its chunk, one read (2md + (2d+2m)c) and one mix (same)
+    in the forward, two reads and one mix in pass A, two reverse reads and two
+    reverse mixes in pass B; scans 4md per absorbed token per KV head
+    (forward) and per token per query head (adjoint).  Bytes: per launch,
+    summed over its work items (formulas below; e = element bytes, mp = m
+    padded to 32 or 64, per chunk of C rows)."""
     B, H, Hkv, T, d, m, C = wl.B, wl.H, wl.Hkv, wl.T, wl.d, wl.m, wl.C
+    G, NC = H // Hkv, -(-T // C)
+    mp = 32 if m <= 32 else 64
+    units = B * Hkv
     fw = flops_window(B, H, T, d, w)
     fs = flops_slot(B, H, T, d, m, w, C)
+    absorbed = max(0, T - w)
     table = {
-        "win_fwd": ("mfma", fw),
-        "win_bwd_dq": ("mfma", 1.5 * fw),
-        "win_bwd_dkdv": ("mfma", 2.0 * fw),
-        "slot_fwd": ("mfma", fs),
-        "slot_bwd_a": ("mfma", 1.5 * fs),
-        "slot_bwd_b": ("mfma", 2.0 * fs),
-        "state_scan": ("mfma", flops_state(B, Hkv, T, d, m, w)),
-        "adj_scan": ("mfma", 4.0 * m * d * B * H * T),
-        "rope_cs": ("hbm", 8.0 * T * (d // 2)),
-        "rope": ("hbm", 2.0 * B * T * (H + Hkv) * d * e),
-        "chunk_gates": ("hbm", 2.0 * B * T * Hkv * m * e),
-        "bwd_prep": ("hbm", B * T * H * (2.0 * d * e + 4)),
-        "dalpha_tail": ("hbm", B * T * Hkv * m * (e + 8.0)),
-        "export_state": ("hbm", 4.0 * B * Hkv * min(w, T) * d * e),
+        "rope_cs": (0.0, 8.0 * T * (d // 2)),
+        "rope": (0.0, 2.0 * B * T * (H + Hkv) * d * e),
+        "chunk_gates": (0.0, B * T * Hkv * m * e + units * NC * mp * (C * e + 4.0)),
+        "state_scan": (flops_state(B, Hkv, T, d, m, w),
+                       2.0 * B * Hkv * absorbed * d * e + units * NC * (mp * C * e + 4.0 * mp + 2.0 * mp * d * e)),
+        "slot_fwd": (fs, B * H * NC * (2.0 * mp * d * e + 4.0 * C * d * e + C * m * e + 4.0 * C)),
+        "win_fwd": (fw, B * T * (3.0 * H * d * e + 2.0 * Hkv * d * e + 8.0 * H)),
+        "bwd_prep": (0.0, B * T * H * (2.0 * d * e + 4)),
+        "slot_bwd_a": (1.5 * fs, B * H * NC * (2.0 * mp * d * e + 6.0 * C * d * e + C * m * e + 8.0 * C
+                                              + 2.0 * mp * C * e + 12.0 * C * mp)),
+        "adj_scan": (4.0 * m * d * B * H * T,
+                     units * NC * (G * (2.0 * C * d * e + 2.0 * mp * C * e) + 4.0 * mp + 2.0 * mp * d * e)),
+        "slot_bwd_b": (2.0 * fs, units * NC * (2.0 * mp * d * e + 4.0 * C * d * e + C * m * e + 4.0 * C * m
+                                               + 4.0 * mp + G * (2.0 * C * d * e + 12.0 * C * mp))),
+        "dalpha_tail": (0.0, B * T * Hkv * m * (e + 8.0)),
+        "win_bwd_dq": (1.5 * fw, B * T * (4.0 * H * d * e + 2.0 * Hkv * d * e + 8.0 * H)),
+        "win_bwd_dkdv": (2.0 * fw, B * T * (2.0 * H * d * e + 6.0 * Hkv * d * e + 8.0 * H)),
+        "export_state": (0.0, 4.0 * B * Hkv * min(w, T) * d * e),
     }
-    if stage not in table:
-        return None, None, None
-    bound, work = table[stage]
-    return bound, work, "flop" if bound == "mfma" else "byte"
+    return table.get(stage, (None, None))
+
+
+def roofline(stage, us, wl, w, e):
+    """Roofline of one kernel: the binding ceiling is min(P, I * BW) with
+    I = flops / bytes; both fractions are reported."""
+    flops, nbytes = stage_work(stage, wl, w, e)
+    if flops is None:
+        return None
+    dur = us / 1e6
+    peak = PEAK_TFLOPS[wl.dtype]
+    tf = flops / dur / 1e12
+    gbs = nbytes / dur / 1e9
+    mfma_bound = flops > 0 and flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    r = {"kernel": stage}
+    if mfma_bound:
+        r.update(bound="mfma", achieved=round(tf, 2), peak=peak, unit="TFLOP/s", frac=round(tf / peak, 4))
+    else:
+        r.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                 frac=round(gbs / PEAK_HBM_GBS, 4))
+    r.update(traffic=measured_traffic(stage), avg_us=round(us, 2),
+             flops_per_launch=flops, bytes_per_launch=nbytes,
+             intensity_flop_per_byte=round(flops / nbytes, 1),
+             mfma_tflops=round(tf, 2), mfma_frac=round(tf / peak, 4),
+             hbm_GBs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+    return r
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -257,6 +290,98 @@ def measured_traffic(stage):
     return t.get("hbm_bytes_per_launch")
 
 
+# ---------------------------------------------------------------- sweeps
+# (label, workload, overrides, window, with backward, decode tokens after the forward)
+SWEEP = [
+    ("w_sweep", "1p3b", {}, 0, True, 0),
+    ("w_sweep", "1p3b", {}, 64, True, 0),
+    ("w_sweep", "1p3b", {}, 512, True, 0),
+    ("w_sweep", "1p3b", {}, 2048, True, 0),  # w = T: causal attention plus the m slot keys
+    ("T_sweep", "long", {"T": 8192}, 512, False, 256),
+    ("T_sweep", "long", {"T": 16384}, 512, False, 256),
+    ("T_sweep", "long", {"T": 32768}, 512, False, 256),
+    ("config", "340m", {}, 64, True, 0),
+    ("config", "gqa", {}, 2048, True, 0),
+    ("config", "headline", {}, 512, True, 0),
+]
+
+
+def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
+    """Whole-call times (HIP events around each call) of one configuration."""
+    dev = torch.device("cuda:0")
+    e = 2 if wl.dtype == torch.bfloat16 else 4
+    q, k, v, a, dO = make_inputs(wl, T_total=wl.T + ndec, with_grad=True)
+    T = wl.T
+    qd, kd, vd, ad, dOd = (x[:, :T].contiguous().to(dev) for x in (q, k, v, a, dO))
+    desc = nha.make_desc(wl.B, T, wl.H, wl.Hkv, wl.d, wl.m, w, wl.C, wl.rope_base, 0.0, wl.dtype)
+    ws = torch.empty(max(nha.workspace_size(desc), nha.workspace_size(desc, backward=with_bwd)), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((wl.B, wl.H, T), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd),
+             torch.empty((wl.B, T, wl.Hkv, wl.m), dtype=torch.float32, device=dev))
+    state = nha.decode_state(wl.B, wl.H, wl.Hkv, wl.d, wl.m, w, wl.rope_base, 0.0, wl.dtype, dev) if ndec else None
+
+    def fwd():
+        nha.fwd(qd, kd, vd, ad, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=o, lse_out=lse,
+                state_out=state)
+
+    def bwd():
+        nha.bwd(qd, kd, vd, ad, o, lse, dOd, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=grads,
+                after_fwd=True)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    for _ in range(warmup):
+        fwd()
+        if with_bwd:
+            bwd()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[3 * i].record()
+        fwd()
+        ev[3 * i + 1].record()
+        if with_bwd:
+            bwd()
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    fwd_ms = sorted(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps))[steps // 2]
+    bwd_ms = sorted(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))[steps // 2]
+    F = flops_fwd(wl, w)
+    peak = PEAK_TFLOPS[wl.dtype]
+    line = {
+        "sweep": label,
+        "workload": "B=%d H=%d Hkv=%d T=%d d=%d m=%d w=%d C=%d %s" % (
+            wl.B, wl.H, wl.Hkv, T, wl.d, wl.m, w, wl.C, "bf16" if e == 2 else "f32"),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tokens_per_s": round(wl.B * T / (fwd_ms / 1e3), 1),
+        "fwd_gflop": round(F / 1e9, 2),
+        "fwd_tflops": round(F / (fwd_ms / 1e3) / 1e12, 2),
+        "fwd_mfma_frac": round(F / (fwd_ms / 1e3) / 1e12 / peak, 4),
+        "fwd_hbm_frac": round(bytes_fwd(wl.with_(T=T), e) / (fwd_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        "full_causal_attention_gflop": round(4.0 * wl.d * wl.B * wl.H * T * (T + 1) / 2 / 1e9, 2),
+    }
+    if with_bwd:
+        line.update(bwd_ms=round(bwd_ms, 4),
+                    fwdbwd_tokens_per_s=round(wl.B * T / ((fwd_ms + bwd_ms) / 1e3), 1),
+                    step_tflops=round(3.5 * F / ((fwd_ms + bwd_ms) / 1e3) / 1e12, 2),
+                    step_mfma_frac=round(3.5 * F / ((fwd_ms + bwd_ms) / 1e3) / 1e12 / peak, 4))
+    if ndec:
+        # the state left by the forward, then ndec recurrent steps on the next tokens
+        fwd()
+        toks = [[x[:, T + i].contiguous().to(dev) for x in (q, k, v, a)] for i in range(ndec)]
+        outs = torch.empty((wl.B, wl.H, wl.d), dtype=wl.dtype, device=dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(ndec):
+            nha.decode_step(toks[i][0], toks[i][1], toks[i][2], toks[i][3], state, w, rope_base=wl.rope_base,
+                            out=outs)
+        e1.record()
+        torch.cuda.synchronize()
+        line["decode_us_per_token"] = round(e0.elapsed_time(e1) * 1e3 / ndec, 2)
+    print(json.dumps(line), flush=True)
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -276,6 +401,8 @@ def main():
                     help="turn four rocprofv3 --pmc output folders into profiles/traffic.json and exit")
     ap.add_argument("--traffic-kernel", default="k_bwd_slot_b", help="kernel name for --traffic-summary")
     ap.add_argument("--traffic-copy-mib", type=int, default=1024)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the w sweep, the T sweep (with decode), the other configurations; one JSON line each")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print a markdown table of a rocprofv3 --kernel-trace --stats csv folder and exit")
     args = ap.parse_args()
@@ -294,6 +421,11 @@ def main():
               "(every (batch, KV head) unit is independent; see DESIGN.md for how it would shard). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        for label, name, over, w, with_bwd, ndec in SWEEP:
+            sweep_point(label, WORKLOADS[name].with_(**over), w, with_bwd, ndec, max(args.steps // 2, 5),
+                        max(args.warmup // 2, 2))
+        return
 
     wl = WORKLOADS[args.workload]
     if args.T:
@@ -364,19 +496,7 @@ def main():
     peak = PEAK_TFLOPS[wl.dtype]
 
     dom = max(per, key=per.get)
-    bound, work, unit = stage_work(dom, wl, w, e)
-    roof = None
-    if bound is not None:
-        dur = per[dom] / 1e3
-        if bound == "mfma":
-            ach = work / dur / 1e12
-            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": measured_traffic(dom), "avg_us": round(per[dom] * 1e3, 2)}
-        else:
-            ach = work / dur / 1e9
-            roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom),
-                    "avg_us": round(per[dom] * 1e3, 2)}
+    roof = roofline(dom, per[dom] * 1e3, wl, w, e)
 
     ok = bool(torch.isfinite(o.float()).all().item())
     if do_bwd:
@@ -409,6 +529,7 @@ def main():
         "fwd_tflops": round(F_fwd / (fwd_ms / 1e3) / 1e12, 2),
         "fwd_mfma_peak_frac": round(F_fwd / (fwd_ms / 1e3) / 1e12 / peak, 4),
         "fwd_hbm_GBs_min_traffic": round(bytes_fwd(wl, e) / (fwd_ms / 1e3) / 1e9, 1),
+        "fwd_hbm_frac": round(bytes_fwd(wl, e) / (fwd_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "kernels_us": {kname: round(x * 1e3, 2) for kname, x in per.items()},
         "outputs_finite": ok,
         "roofline": roof,
