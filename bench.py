@@ -379,6 +379,21 @@ def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
         e1.record()
         torch.cuda.synchronize()
         line["decode_us_per_token"] = round(e0.elapsed_time(e1) * 1e3 / ndec, 2)
+        line["decode_note"] = "eager: one Python call per token (host-bound); graph: the same calls captured in a HIP graph"
+        # the same ndec steps captured once in a HIP graph (the state keeps
+        # advancing between replays; only the timing is of interest here)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(ndec):
+                nha.decode_step(toks[i][0], toks[i][1], toks[i][2], toks[i][3], state, w, rope_base=wl.rope_base,
+                                out=outs)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        line["decode_graph_us_per_token"] = round(e0.elapsed_time(e1) * 1e3 / ndec, 2)
     print(json.dumps(line), flush=True)
 
 

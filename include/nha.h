@@ -102,7 +102,11 @@ nha_status nha_check_desc(const nha_desc* desc);
  *   RK   dtype [B][Hkv][w][d]   ring of the last w raw (unrotated) keys;
  *                               position j lives at row j mod w
  *   RV   dtype [B][Hkv][w][d]   ring of the last w values
+ *   RKR  dtype [B][Hkv][w][d]   the same keys with RoPE applied at their
+ *                               positions (present only when rope_base > 0)
  *   pos  int64 [B][Hkv]         tokens consumed so far (all equal)
+ *   part float [B*H][32][d+4]   scratch of one decode step (no meaning
+ *                               between calls)
  * A zero-filled state is the state before the first token. */
 size_t nha_decode_state_size(const nha_desc* desc);
 
@@ -154,7 +158,10 @@ nha_status nha_bwd_after_fwd(const nha_desc* desc, const void* q,
  * At position t it absorbs the token leaving the window (t >= w) with
  * alpha_t, pushes (k_t, v_t), reads m slots + min(w, t+1) window tokens
  * through one softmax, writes o_t and advances the position by one.  The
- * result equals nha_fwd over the concatenated sequence at row t. */
+ * result equals nha_fwd over the concatenated sequence at row t.  Two
+ * launches: the keys of each (b, g) are split over several workgroups whose
+ * partial softmax results a second launch merges.  m + w > 4096 returns
+ * NHA_ERR_UNSUPPORTED. */
 nha_status nha_decode_step(const nha_desc* desc, const void* q_t,
                            const void* k_t, const void* v_t,
                            const void* alpha_t, void* state, void* o_t,

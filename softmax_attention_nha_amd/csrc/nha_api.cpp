@@ -11,7 +11,6 @@ using namespace nha;
 
 namespace {
 
-constexpr size_t kMaxDecodeLds = 144 * 1024;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -194,7 +193,7 @@ nha_status nha_decode_step(const nha_desc* desc, const void* q_t, const void* k_
   const void* ptrs[] = {q_t, k_t, v_t, alpha_t, state, o_t};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
-  if ((size_t)16 * (s.m + s.w) > kMaxDecodeLds) return NHA_ERR_UNSUPPORTED;
+  if ((long long)s.m + s.w > (long long)kDecodeSplitMax * kDecodeKeysPerSplit) return NHA_ERR_UNSUPPORTED;
   DecodePtrs p{q_t, k_t, v_t, alpha_t, state, o_t};
   hipError_t e = launch_decode(s, make_theta(desc), p, (hipStream_t)stream);
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;

@@ -1074,11 +1074,12 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
 }
 
 // ---------------------------------------------------------------- decode-state export
-// Ring rows for positions max(0, T-w) .. T-1 and the position counter.
+// Ring rows for positions max(0, T-w) .. T-1 (raw keys, values and, with
+// RoPE, the RoPE'd keys the forward computed) and the position counter.
 template <typename T>
-__global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ vv, T* __restrict__ rk,
-                               T* __restrict__ rv, long long* __restrict__ pos, int Tn, int Hkv, int d,
-                               int w) {
+__global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ kr,
+                               T* __restrict__ rk, T* __restrict__ rv, T* __restrict__ rkr,
+                               long long* __restrict__ pos, int Tn, int Hkv, int d, int w) {
   int unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv;
   int first = Tn - w > 0 ? Tn - w : 0;
   int nrows = w > 0 ? Tn - first : 0;
@@ -1088,6 +1089,7 @@ __global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ v
     size_t dst = ((size_t)unit * w + (j % w)) * d + x;
     st8<T>(rk + dst, ld8<T>(kk + src));
     st8<T>(rv + dst, ld8<T>(vv + src));
+    if (kr) st8<T>(rkr + dst, ld8<T>(kr + src));
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) pos[unit] = Tn;
 }
@@ -1172,11 +1174,12 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       char* base = (char*)p.state_out;
       mk.mark(st);
       if (s.w > 0)
-        hipLaunchKernelGGL(k_export_state<T>, dim3(32, units), dim3(256), 0, st, k, v, (T*)(base + SL.rk),
-                           (T*)(base + SL.rv), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w);
+        hipLaunchKernelGGL(k_export_state<T>, dim3(32, units), dim3(256), 0, st, k, v,
+                           s.rope ? (const T*)pp.krot : (const T*)nullptr, (T*)(base + SL.rk), (T*)(base + SL.rv),
+                           (T*)(base + SL.rkr), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w);
       else
-        hipLaunchKernelGGL(k_export_state<T>, dim3(1, units), dim3(64), 0, st, k, v, (T*)nullptr, (T*)nullptr,
-                           (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0);
+        hipLaunchKernelGGL(k_export_state<T>, dim3(1, units), dim3(64), 0, st, k, v, (const T*)nullptr,
+                           (T*)nullptr, (T*)nullptr, (T*)nullptr, (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0);
     }
     mk.mark(st);
     return hipGetLastError();

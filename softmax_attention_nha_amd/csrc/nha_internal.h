@@ -70,8 +70,12 @@ inline FwdWs fwd_ws_layout(const Shape& s) {
 }
 
 // Decode-state carve-up (see nha_decode_state_size in nha.h).
+// The decode step splits each (batch, KV head)'s keys over up to
+// kDecodeSplitMax workgroups; their partial softmax results are combined by a
+// second launch through the `part` region of the state.
+constexpr int kDecodeSplitMax = 32;
 struct StateLayout {
-  size_t sk, sv, rk, rv, pos, total;
+  size_t sk, sv, rk, rv, rkr, pos, part, total;
 };
 inline StateLayout state_layout(const Shape& s) {
   StateLayout L;
@@ -84,10 +88,27 @@ inline StateLayout state_layout(const Shape& s) {
   off += align256(units * (size_t)s.w * s.d * s.esz);
   L.rv = off;
   off += align256(units * (size_t)s.w * s.d * s.esz);
+  L.rkr = off;  // RoPE'd keys of the ring (only with RoPE)
+  off += align256(s.rope ? units * (size_t)s.w * s.d * s.esz : 0);
   L.pos = off;
   off += align256(units * 8);
+  L.part = off;  // [B*H][kDecodeSplitMax][d + 4] float: max, sum, -, -, o
+  off += align256((size_t)s.B * s.H * kDecodeSplitMax * (s.d + 4) * 4);
   L.total = off;
   return L;
+}
+// Workgroups per (batch, KV head) of a decode step: enough to fill the chip,
+// at least 8 keys each, at most kDecodeKeysPerSplit (so m + w <=
+// kDecodeSplitMax * kDecodeKeysPerSplit, checked by the API).
+constexpr int kDecodeKeysPerSplit = 128;
+inline int decode_splits(const Shape& s) {
+  const int units = s.B * s.Hkv, keys = s.m + s.w;
+  int ns = 512 / (units > 0 ? units : 1);
+  if (ns > kDecodeSplitMax) ns = kDecodeSplitMax;
+  if (ns > keys / 8) ns = keys / 8;
+  const int need = (keys + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;
+  if (ns < need) ns = need;
+  return ns < 1 ? 1 : ns;
 }
 
 // Records caller-provided timing events around consecutive launches.

@@ -68,11 +68,15 @@ def test_sizes_zero_for_invalid_and_positive_for_valid():
         assert f(ctypes.byref(bad)) == 0
 
 
-def test_decode_state_size_matches_documented_layout():
-    d = desc(B=2, H=4, Hkv=2, d=64, m=8, w=16, dtype=torch.bfloat16)
+@pytest.mark.parametrize("rope_base", [10000.0, 0.0])
+def test_decode_state_size_matches_documented_layout(rope_base):
+    """SK, SV, RK, RV, RKR (RoPE only), pos, then the 32-split scratch."""
+    d = desc(B=2, H=4, Hkv=2, d=64, m=8, w=16, dtype=torch.bfloat16, rope_base=rope_base)
     a256 = lambda x: (x + 255) // 256 * 256
     units = 2 * 2
-    expect = 2 * a256(units * 8 * 64 * 4) + 2 * a256(units * 16 * 64 * 2) + a256(units * 8)
+    rings = 3 if rope_base > 0 else 2
+    expect = (2 * a256(units * 8 * 64 * 4) + rings * a256(units * 16 * 64 * 2) + a256(units * 8)
+              + a256(2 * 4 * 32 * (64 + 4) * 4))
     assert nha.decode_state_size(d) == expect
 
 
