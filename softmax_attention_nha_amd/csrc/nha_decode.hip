@@ -13,15 +13,20 @@
 //   2. reads the m slots (raw q, no RoPE) and the min(w, t+1) window tokens
 //      (RoPE'd q and keys) through one softmax scaled by `scale`;
 //   3. pushes (k_t, v_t) into ring row t mod w and advances the position.
-// Two launches.  k_dec_split: grid (NS, B*Hkv); workgroup s takes the keys
+// Two launches.  k_dec_split, grid (NS, B*Hkv): workgroup s takes the keys
 // s, s + NS, s + 2 NS, ... of the list [m slots; window tokens], absorbs its
 // own slot rows (every slot row has one owner, so the state is updated in
 // place without races), and leaves per query head a partial softmax (max,
-// sum, unnormalised output) in the state's scratch.  k_dec_combine: one
-// workgroup per (batch, KV head) merges the NS partials of each head of the
-// group (the standard max / sum rescaling), then pushes the token into the
-// rings -- after every split has read ring row t mod w -- and advances the
-// position.  A key is handled by D/8 lanes, 8 channels each.
+// sum, unnormalised output) in the state's scratch.  A key is handled by D/8
+// lanes, 8 channels each; all rows a lane needs are loaded before their first
+// use (two memory round trips: the position, then the ring rows it selects),
+// and the D/8 partial dot products of a lane's D/16 keys are summed by a
+// halving butterfly (D/16 lane exchanges per head instead of one log2(D/8)
+// reduction per key).  k_dec_merge, one workgroup per (batch, KV head):
+// merges the NS partials of each head of the group in split order (the
+// standard max / sum rescaling), writes o_t, pushes the token into the rings
+// -- after every split has read ring row t mod w -- and advances the
+// position.  No atomics: o_t is bitwise reproducible.
 #include "nha_common.h"
 #include "nha_internal.h"
 
@@ -33,30 +38,20 @@ __device__ __forceinline__ void dec_angle(double theta, long long pos, float& cs
   sincosf((float)ang, &sn, &cs);
 }
 
-// Rotate-half RoPE of one lane's 8 channels x[0..7] = row[8 li .. 8 li + 7]
-// at position `pos`: the partner channels (i +- D/2) sit in lane li ^ (LPK/2)
-// of the same key group.
-template <int D>
-__device__ __forceinline__ void dec_rope(float (&x)[8], int li, long long pos, const RopeTheta& th) {
-  constexpr int LPK = D / 8, HALF = D / 2;
-  float y[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = __shfl_xor(x[e], LPK / 2, 64);
-  const bool first = 8 * li < HALF;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int ch = 8 * li + e, i = ch % HALF;
-    float cs, sn;
-    dec_angle(th.theta[i], pos, cs, sn);
-    x[e] = first ? x[e] * cs - y[e] * sn : x[e] * cs + y[e] * sn;
-  }
-}
-
 template <typename T>
 __device__ __forceinline__ void ld8f_row(const T* p, float (&x)[8]) {
   const typename Vec<T>::v8 v = ld8<T>(p);
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = to_f<T>(v[e]);
+}
+
+__device__ __forceinline__ void ld8f_f32(const float* p, float (&x)[8]) {
+  const floatx4 a0 = *reinterpret_cast<const floatx4*>(p), a1 = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = a0[r];
+    x[4 + r] = a1[r];
+  }
 }
 
 // Sum over the LPK lanes of one key group (lanes 16-aligned blocks of LPK).
@@ -67,6 +62,19 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Rotate-half RoPE of one lane's 8 channels with precomputed (cos, sin) of
+// their angles; the partner channels (i +- D/2) sit in lane li ^ (LPK/2).
+template <int D>
+__device__ __forceinline__ void dec_rope_cs(float (&x)[8], int li, const float (&cs)[8], const float (&sn)[8]) {
+  constexpr int LPK = D / 8, HALF = D / 2;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = __shfl_xor(x[e], LPK / 2, 64);
+  const bool first = 8 * li < HALF;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = first ? x[e] * cs[e] - y[e] * sn[e] : x[e] * cs[e] + y[e] * sn[e];
+}
+
 constexpr int kDecGH = 4;  // query heads per pass
 
 template <typename T, int D>
@@ -75,57 +83,110 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
                                                    float* __restrict__ SK, float* __restrict__ SV,
                                                    const T* __restrict__ RK, const T* __restrict__ RV,
                                                    const T* __restrict__ RKR, const long long* __restrict__ pos,
-                                                   float* __restrict__ part, int H, int Hkv, int m, int w,
-                                                   int NS, float scale, RopeTheta th, int rope) {
-  constexpr int LPK = D / 8, NG = 256 / LPK, PP = D + 4;
+                                                   float* __restrict__ part, int H, int Hkv, int m, int w, int NS,
+                                                   float scale, RopeTheta th, int rope) {
+  constexpr int LPK = D / 8, NG = 256 / LPK, KPG = kDecodeKeysPerSplit / NG, PP = D + 4, HALF = D / 2;
+  static_assert(2 * KPG == LPK, "a lane's keys halve once per lane bit but the lowest");
   __shared__ float lg[kDecGH][kDecodeKeysPerSplit];  // logits of this split's keys (log2 units)
   __shared__ float red[kDecGH][4];
-  const int tid = threadIdx.x, grp = tid / LPK, li = tid % LPK;
+  __shared__ float wsum[4][kDecGH][D + 1];
+  const int tid = threadIdx.x, grp = tid / LPK, li = tid % LPK, wv = tid >> 6;
   const int s = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  const size_t krow = ((size_t)b * Hkv + hg) * D + 8 * li;  // this lane's channels of k_t / v_t
+  // rows that do not depend on the position: the new token, its gates and
+  // this group's slot rows (slot e = key index e < m; address clamped)
+  float knew[8], vnew[8];
+  ld8f_row<T>(kin + krow, knew);
+  ld8f_row<T>(vin + krow, vnew);
+  float* sk = SK + (size_t)unit * m * D + 8 * li;
+  float* sv = SV + (size_t)unit * m * D + 8 * li;
+  float xk[KPG][8], xv[KPG][8], ga[KPG];
+#pragma unroll
+  for (int kk = 0; kk < KPG; ++kk) {
+    const int e = min(s + NS * (grp + NG * kk), m - 1);
+    ld8f_f32(sk + (size_t)e * D, xk[kk]);
+    ld8f_f32(sv + (size_t)e * D, xv[kk]);
+    ga[kk] = to_f<T>(alpha[((size_t)b * Hkv + hg) * m + e]);
+  }
   const long long t = pos[unit];
   const long long nwin = (w == 0) ? 0 : (t + 1 < w ? t + 1 : w);
   const int nkeys = m + (int)nwin;
   const long long jfirst = t - nwin + 1;
   const int nmine = nkeys > s ? (nkeys - s + NS - 1) / NS : 0;  // keys of this split
-  float* sk = SK + (size_t)unit * m * D;
-  float* sv = SV + (size_t)unit * m * D;
-  // 1. absorb this split's slot rows (slot i = key index i < m)
-  if (t >= w) {
-    float kap[8], nu[8];
-    if (w > 0) {
-      const size_t rr = (size_t)(t % w) * D + 8 * li;
-      ld8f_row<T>(RK + (size_t)unit * w * D + rr, kap);
-      ld8f_row<T>(RV + (size_t)unit * w * D + rr, nu);
-    } else {
-      ld8f_row<T>(kin + ((size_t)b * Hkv + hg) * D + 8 * li, kap);
-      ld8f_row<T>(vin + ((size_t)b * Hkv + hg) * D + 8 * li, nu);
-    }
-    const T* al = alpha + ((size_t)b * Hkv + hg) * m;
-    for (int j = grp; j < nmine; j += NG) {
-      const int e = s + NS * j;
-      if (e >= m) break;
-      const float a = to_f<T>(al[e]);
-      float* rk_ = sk + (size_t)e * D + 8 * li;
-      float* rv_ = sv + (size_t)e * D + 8 * li;
-      floatx4 k0 = *reinterpret_cast<const floatx4*>(rk_), k1 = *reinterpret_cast<const floatx4*>(rk_ + 4);
-      floatx4 v0 = *reinterpret_cast<const floatx4*>(rv_), v1 = *reinterpret_cast<const floatx4*>(rv_ + 4);
+  // the token leaving the window (ring row t mod w; k_t itself when w = 0),
+  // and this group's window rows (RoPE'd keys when RoPE is on)
+  float kap[8], nu[8];
+  typename Vec<T>::v8 wk[KPG], wvr[KPG];  // raw rows, converted when selected
+  if (w > 0) {
+    const T* rk = RK + (size_t)unit * w * D + 8 * li;
+    const T* rv = RV + (size_t)unit * w * D + 8 * li;
+    const T* rkw = (rope ? RKR : RK) + (size_t)unit * w * D + 8 * li;
+    const size_t ra = (size_t)(t % w) * D;
+    ld8f_row<T>(rk + ra, kap);
+    ld8f_row<T>(rv + ra, nu);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        k0[r] = a * k0[r] + (1.f - a) * kap[r];
-        k1[r] = a * k1[r] + (1.f - a) * kap[4 + r];
-        v0[r] = a * v0[r] + (1.f - a) * nu[r];
-        v1[r] = a * v1[r] + (1.f - a) * nu[4 + r];
-      }
-      *reinterpret_cast<floatx4*>(rk_) = k0;
-      *reinterpret_cast<floatx4*>(rk_ + 4) = k1;
-      *reinterpret_cast<floatx4*>(rv_) = v0;
-      *reinterpret_cast<floatx4*>(rv_ + 4) = v1;
+    for (int kk = 0; kk < KPG; ++kk) {
+      const int e = s + NS * (grp + NG * kk);
+      // window position jfirst + e - m, clamped into the ring's valid rows
+      long long jp = jfirst + (e - m);
+      jp = jp < jfirst ? jfirst : (jp > t ? t : jp);
+      const size_t rr = (size_t)(jp % w) * D;
+      wk[kk] = ld8<T>(rkw + rr);
+      wvr[kk] = ld8<T>(rv + rr);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      kap[r] = knew[r];
+      nu[r] = vnew[r];
     }
   }
-  // the new token's key (position t), RoPE'd, for the split that owns it
-  float knew[8];
-  ld8f_row<T>(kin + ((size_t)b * Hkv + hg) * D + 8 * li, knew);
-  if (rope) dec_rope<D>(knew, li, t, th);
+  // this lane's RoPE factors at position t (a channel and its partner share
+  // the angle)
+  float cs[8], sn[8];
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dec_angle(th.theta[(8 * li + e) % HALF], t, cs[e], sn[e]);
+  }
+  float knr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) knr[r] = knew[r];
+  if (rope) dec_rope_cs<D>(knr, li, cs, sn);
+  // 1. absorb this group's slot rows and select every key's K and V rows
+  bool isslot[KPG];
+#pragma unroll
+  for (int kk = 0; kk < KPG; ++kk) {
+    const int j = grp + NG * kk, e = s + NS * j;
+    isslot[kk] = e < m;
+    if (j < nmine && e < m) {
+      if (t >= w) {
+        const float a = ga[kk];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          xk[kk][r] = a * xk[kk][r] + (1.f - a) * kap[r];
+          xv[kk][r] = a * xv[kk][r] + (1.f - a) * nu[r];
+        }
+        float* rk_ = sk + (size_t)e * D;
+        float* rv_ = sv + (size_t)e * D;
+        *reinterpret_cast<floatx4*>(rk_) = floatx4{xk[kk][0], xk[kk][1], xk[kk][2], xk[kk][3]};
+        *reinterpret_cast<floatx4*>(rk_ + 4) = floatx4{xk[kk][4], xk[kk][5], xk[kk][6], xk[kk][7]};
+        *reinterpret_cast<floatx4*>(rv_) = floatx4{xv[kk][0], xv[kk][1], xv[kk][2], xv[kk][3]};
+        *reinterpret_cast<floatx4*>(rv_ + 4) = floatx4{xv[kk][4], xv[kk][5], xv[kk][6], xv[kk][7]};
+      }
+    } else if (jfirst + (e - m) == t) {  // the new token
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        xk[kk][r] = knr[r];
+        xv[kk][r] = vnew[r];
+      }
+    } else if (w > 0) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        xk[kk][r] = to_f<T>(wk[kk][r]);
+        xv[kk][r] = to_f<T>(wvr[kk][r]);
+      }
+    }
+  }
   const float sl2 = scale * NHA_LOG2E;
   for (int h0 = 0; h0 < G; h0 += kDecGH) {
     const int nh = (G - h0) < kDecGH ? (G - h0) : kDecGH;
@@ -136,48 +197,48 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
       ld8f_row<T>(q + ((size_t)b * H + h) * D + 8 * li, qs[hh]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qr[hh][e] = qs[hh][e];
-      if (rope) dec_rope<D>(qr[hh], li, t, th);
+      if (rope && hh < nh) dec_rope_cs<D>(qr[hh], li, cs, sn);
     }
-    // 2a. logits (log2 units) of this split's keys
-    for (int j = grp; j < nmine; j += NG) {
-      const int e = s + NS * j;
-      float x[8];
-      bool slot = e < m;
-      if (slot) {
-        const float* row = sk + (size_t)e * D + 8 * li;
-        const floatx4 a0 = *reinterpret_cast<const floatx4*>(row), a1 = *reinterpret_cast<const floatx4*>(row + 4);
+    // 2a. logits (log2 units) of this group's keys: lane li ends up with the
+    // full dot product of key (li >> 1) & (KPG - 1) of its group
+    const int kmine = (li >> 1) & (KPG - 1), jmine = grp + NG * kmine;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = a0[r];
-          x[4 + r] = a1[r];
+    for (int hh = 0; hh < kDecGH; ++hh) {
+      if (hh < nh) {
+        float P[KPG];
+#pragma unroll
+        for (int kk = 0; kk < KPG; ++kk) {
+          float acc = 0.f;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) acc += xk[kk][r] * (isslot[kk] ? qs[hh][r] : qr[hh][r]);
+          P[kk] = acc;
         }
-      } else {
-        const long long jp = jfirst + (e - m);
-        if (jp == t) {
+        // halving butterfly: at lane bit msk = LPK/2, LPK/4, .., 2 the lane
+        // keeps the upper half of its keys if that bit is set, the lower half
+        // otherwise, adding its partner's part of the kept half
 #pragma unroll
-          for (int r = 0; r < 8; ++r) x[r] = knew[r];
-        } else {
-          const T* ring = (rope ? RKR : RK) + ((size_t)unit * w + (size_t)(jp % w)) * D + 8 * li;
-          ld8f_row<T>(ring, x);
+        for (int lvl = 0; (KPG >> lvl) > 1; ++lvl) {
+          const int n = KPG >> lvl, msk = LPK >> (lvl + 1);
+          const bool up = (li & msk) != 0;
+#pragma unroll
+          for (int i = 0; i < n / 2; ++i) {
+            const float snd = up ? P[i] : P[i + n / 2];
+            const float rcv = __shfl_xor(snd, msk, 64);
+            P[i] = (up ? P[i + n / 2] : P[i]) + rcv;
+          }
         }
-      }
-#pragma unroll
-      for (int hh = 0; hh < kDecGH; ++hh) {
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) acc += x[r] * (slot ? qs[hh][r] : qr[hh][r]);
-        acc = group_sum<LPK>(acc);
-        if (li == 0 && hh < nh) lg[hh][j] = acc * sl2;
+        P[0] += __shfl_xor(P[0], 1, 64);
+        if ((li & 1) == 0 && jmine < nmine) lg[hh][jmine] = P[0] * sl2;
       }
     }
     __syncthreads();
-    // 2b. max and sum per head over this split's keys
+    // 2b. max per head over this split's keys
     for (int hh = 0; hh < nh; ++hh) {
       float mx = -INFINITY;
       for (int j = tid; j < nmine; j += 256) mx = fmaxf(mx, lg[hh][j]);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      if ((tid & 63) == 0) red[hh][tid >> 6] = mx;
+      for (int o2 = 1; o2 < 64; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
+      if ((tid & 63) == 0) red[hh][wv] = mx;
     }
     __syncthreads();
     float mxh[kDecGH];
@@ -187,39 +248,27 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
       if (hh < nh)
         for (int x = 0; x < 4; ++x) mxh[hh] = fmaxf(mxh[hh], red[hh][x]);
     }
-    __syncthreads();
-    // 2c. p = 2^(l - max) and the unnormalised output of this split
+    // 2c. p = 2^(l - max) and the unnormalised output of this group's keys
     float oa[kDecGH][8];
+    float zs[kDecGH];
 #pragma unroll
-    for (int hh = 0; hh < kDecGH; ++hh)
+    for (int hh = 0; hh < kDecGH; ++hh) {
+      zs[hh] = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) oa[hh][r] = 0.f;
-    float zs[kDecGH] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = grp; j < nmine; j += NG) {
-      const int e = s + NS * j;
-      float x[8];
-      if (e < m) {
-        const float* row = sv + (size_t)e * D + 8 * li;
-        const floatx4 a0 = *reinterpret_cast<const floatx4*>(row), a1 = *reinterpret_cast<const floatx4*>(row + 4);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = a0[r];
-          x[4 + r] = a1[r];
-        }
-      } else {
-        const long long jp = jfirst + (e - m);
-        if (jp == t)
-          ld8f_row<T>(vin + ((size_t)b * Hkv + hg) * D + 8 * li, x);
-        else
-          ld8f_row<T>(RV + ((size_t)unit * w + (size_t)(jp % w)) * D + 8 * li, x);
-      }
+    for (int kk = 0; kk < KPG; ++kk) {
+      const int j = grp + NG * kk;
+      if (j < nmine) {
 #pragma unroll
-      for (int hh = 0; hh < kDecGH; ++hh) {
-        if (hh < nh) {
-          const float p = fast_exp2(lg[hh][j] - mxh[hh]);
-          zs[hh] += p;
+        for (int hh = 0; hh < kDecGH; ++hh) {
+          if (hh < nh) {
+            const float p = fast_exp2(lg[hh][j] - mxh[hh]);
+            zs[hh] += p;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) oa[hh][r] += p * x[r];
+            for (int r = 0; r < 8; ++r) oa[hh][r] += p * xv[kk][r];
+          }
         }
       }
     }
@@ -227,16 +276,15 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
     // same channels are LPK lanes apart), then across the 4 waves in LDS
 #pragma unroll
     for (int hh = 0; hh < kDecGH; ++hh) {
+      if (hh >= nh) continue;
 #pragma unroll
-      for (int o = LPK; o < 64; o <<= 1) {
-        zs[hh] += __shfl_xor(zs[hh], o, 64);
+      for (int o2 = LPK; o2 < 64; o2 <<= 1) {
+        zs[hh] += __shfl_xor(zs[hh], o2, 64);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) oa[hh][r] += __shfl_xor(oa[hh][r], o, 64);
+        for (int r = 0; r < 8; ++r) oa[hh][r] += __shfl_xor(oa[hh][r], o2, 64);
       }
     }
-    const int wv = tid >> 6;
     // lanes 0 .. LPK-1 of each wave hold the wave's sums for channels 8 li ..
-    __shared__ float wsum[4][kDecGH][D + 1];
     if ((tid & 63) < LPK) {
 #pragma unroll
       for (int hh = 0; hh < kDecGH; ++hh) {
@@ -250,7 +298,8 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
       const int hh = e / (D + 1), c = e % (D + 1);
       const float v = wsum[0][hh][c] + wsum[1][hh][c] + wsum[2][hh][c] + wsum[3][hh][c];
       float* dst = part + (((size_t)(b * H + hg * G + h0 + hh)) * kDecodeSplitMax + s) * PP;
-      if (c < D) dst[4 + c] = v;
+      if (c < D)
+        dst[4 + c] = v;
       else {
         dst[0] = mxh[hh];
         dst[1] = v;
@@ -260,48 +309,80 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
   }
 }
 
-// One workgroup (D threads) per (batch, KV head): merge the partials of each
-// query head of the group, write o_t, push the token into the rings and
+// One workgroup (256 threads) per (batch, KV head): merge the partials of
+// each query head of the group, write o_t, push the token into the rings and
 // advance the position.
 template <typename T, int D>
-__global__ __launch_bounds__(128) void k_dec_combine(const float* __restrict__ part, const T* __restrict__ kin,
-                                                     const T* __restrict__ vin, T* __restrict__ RK,
-                                                     T* __restrict__ RV, T* __restrict__ RKR,
-                                                     long long* __restrict__ pos, T* __restrict__ o, int H,
-                                                     int Hkv, int w, int NS, RopeTheta th, int rope) {
-  constexpr int PP = D + 4;
-  const int c = threadIdx.x, unit = blockIdx.x, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+__global__ __launch_bounds__(256) void k_dec_merge(const float* __restrict__ part, const T* __restrict__ kin,
+                                                   const T* __restrict__ vin, T* __restrict__ RK, T* __restrict__ RV,
+                                                   T* __restrict__ RKR, long long* __restrict__ pos,
+                                                   T* __restrict__ o, int H, int Hkv, int w, int NS, RopeTheta th,
+                                                   int rope) {
+  constexpr int PP = D + 4, HALF = D / 2, SG = 256 / D, PER = (kDecodeSplitMax + SG - 1) / SG;
+  __shared__ float fs[kDecodeSplitMax];  // per-split factors 2^(max_s - M)
+  __shared__ float acc_s[SG * D];
+  __shared__ float zred[SG];
+  const int tid = threadIdx.x, unit = blockIdx.x, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
   const long long t = pos[unit];
-  if (c < D) {
-    for (int hh = 0; hh < G; ++hh) {
-      const float* pr = part + ((size_t)(b * H + hg * G + hh)) * kDecodeSplitMax * PP;
-      float M = -INFINITY;
-      for (int s = 0; s < NS; ++s) M = fmaxf(M, pr[s * PP]);
-      float z = 0.f, acc = 0.f;
-      for (int s = 0; s < NS; ++s) {
-        const float f = fast_exp2(pr[s * PP] - M);
-        z += f * pr[s * PP + 1];
-        acc += f * pr[s * PP + 4 + c];
-      }
-      o[((size_t)b * H + hg * G + hh) * D + c] = to_t<T>(acc / z);
+  for (int hh = 0; hh < G; ++hh) {
+    const float* pr = part + ((size_t)(b * H + hg * G + hh)) * kDecodeSplitMax * PP;
+    // thread (sp, c) sums channel c over the splits sp, sp + SG, ...: every
+    // load first (addresses clamped), then the sums in split order
+    const int c = tid % D, sp = tid / D;
+    float xo[PER], xz[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int sx = min(sp + SG * i, NS - 1);
+      xo[i] = pr[sx * PP + 4 + c];
+      xz[i] = pr[sx * PP + 1];
     }
-    if (w > 0) {
-      const size_t src = ((size_t)b * Hkv + hg) * D, dst = ((size_t)unit * w + (size_t)(t % w)) * D;
-      const float x = to_f<T>(kin[src + c]);
-      RK[dst + c] = kin[src + c];
-      RV[dst + c] = vin[src + c];
-      if (rope) {
-        constexpr int HALF = D / 2;
-        const int i = c % HALF;
-        const float pair = to_f<T>(kin[src + (c < HALF ? c + HALF : c - HALF)]);
-        float cs, sn;
-        dec_angle(th.theta[i], t, cs, sn);
-        RKR[dst + c] = to_t<T>(c < HALF ? x * cs - pair * sn : x * cs + pair * sn);
+    if (tid < 64) {
+      const float mx = tid < NS ? pr[tid * PP] : -INFINITY;
+      float M = mx;
+#pragma unroll
+      for (int o2 = 1; o2 < 64; o2 <<= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+      if (tid < NS) fs[tid] = fast_exp2(mx - M);
+    }
+    __syncthreads();
+    float acc = 0.f, z = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int sx = sp + SG * i;
+      if (sx < NS) {
+        acc += fs[sx] * xo[i];
+        z += fs[sx] * xz[i];
       }
+    }
+    // then the SG split groups in a fixed order through LDS
+    acc_s[sp * D + c] = acc;
+    if (c == 0) zred[sp] = z;
+    __syncthreads();
+    if (tid < D) {
+      float a2 = 0.f, z2 = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < SG; ++g2) {
+        a2 += acc_s[g2 * D + tid];
+        z2 += zred[g2];
+      }
+      o[((size_t)b * H + hg * G + hh) * D + tid] = to_t<T>(a2 / z2);
+    }
+    __syncthreads();
+  }
+  // push (k_t, v_t) into ring row t mod w (and the key with RoPE at t)
+  if (w > 0 && tid < D) {
+    const size_t src = ((size_t)b * Hkv + hg) * D, dst = ((size_t)unit * w + (size_t)(t % w)) * D;
+    const float x = to_f<T>(kin[src + tid]);
+    RK[dst + tid] = kin[src + tid];
+    RV[dst + tid] = vin[src + tid];
+    if (rope) {
+      const int i = tid % HALF;
+      const float pair = to_f<T>(kin[src + (tid < HALF ? tid + HALF : tid - HALF)]);
+      float cs, sn;
+      dec_angle(th.theta[i], t, cs, sn);
+      RKR[dst + tid] = to_t<T>(tid < HALF ? x * cs - pair * sn : x * cs + pair * sn);
     }
   }
-  __syncthreads();
-  if (c == 0) pos[unit] = t + 1;
+  if (tid == 0) pos[unit] = t + 1;
 }
 
 template <typename T, int D>
@@ -312,9 +393,9 @@ static hipError_t decode_impl(const Shape& s, const RopeTheta& th, const DecodeP
   hipLaunchKernelGGL((k_dec_split<T, D>), dim3(NS, units), dim3(256), 0, st, (const T*)p.q, (const T*)p.k,
                      (const T*)p.v, (const T*)p.alpha, (float*)(base + L.sk), (float*)(base + L.sv),
                      (const T*)(base + L.rk), (const T*)(base + L.rv), (const T*)(base + L.rkr),
-                     (const long long*)(base + L.pos), (float*)(base + L.part), s.H, s.Hkv, s.m, s.w, NS, s.scale,
-                     th, s.rope ? 1 : 0);
-  hipLaunchKernelGGL((k_dec_combine<T, D>), dim3(units), dim3(128), 0, st, (const float*)(base + L.part),
+                     (const long long*)(base + L.pos), (float*)(base + L.part), s.H, s.Hkv, s.m, s.w, NS, s.scale, th,
+                     s.rope ? 1 : 0);
+  hipLaunchKernelGGL((k_dec_merge<T, D>), dim3(units), dim3(256), 0, st, (const float*)(base + L.part),
                      (const T*)p.k, (const T*)p.v, (T*)(base + L.rk), (T*)(base + L.rv), (T*)(base + L.rkr),
                      (long long*)(base + L.pos), (T*)p.o, s.H, s.Hkv, s.w, NS, th, s.rope ? 1 : 0);
   return hipGetLastError();

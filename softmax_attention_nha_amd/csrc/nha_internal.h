@@ -103,7 +103,7 @@ inline StateLayout state_layout(const Shape& s) {
 constexpr int kDecodeKeysPerSplit = 128;
 inline int decode_splits(const Shape& s) {
   const int units = s.B * s.Hkv, keys = s.m + s.w;
-  int ns = 512 / (units > 0 ? units : 1);
+  int ns = 256 / (units > 0 ? units : 1);
   if (ns > kDecodeSplitMax) ns = kDecodeSplitMax;
   if (ns > keys / 8) ns = keys / 8;
   const int need = (keys + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;

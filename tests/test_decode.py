@@ -81,3 +81,44 @@ def test_gqa_decode_bf16():
     od, (q, k, v, a), _ = run_decode(wl, T0, steps, w, wl.rope_base)
     o_ref, _ = oracle_fwd(q, k, v, a, w, wl.rope_base)
     compare("o_dec", f64(od), o_ref[:, T0:], 2e-2, 1e-2)
+
+
+def test_decode_many_sequences_bf16():
+    # B >> 1: every (sequence, KV head) unit steps independently (one split each)
+    wl = WORKLOADS["340m"].with_(B=24, T=96, H=8, Hkv=4, m=16, seed=44)
+    T0, steps, w = 96, 12, 64
+    log("case decode batched bf16 B=%d T0=%d w=%d" % (wl.B, T0, w))
+    od, (q, k, v, a), _ = run_decode(wl, T0, steps, w, wl.rope_base)
+    o_ref, _ = oracle_fwd(q, k, v, a, w, wl.rope_base)
+    compare("o_dec", f64(od), o_ref[:, T0:], 2e-2, 1e-2)
+
+
+def test_decode_most_keys_per_step():
+    # m + w = 4096, the largest key list a step takes: 32 workgroups of 128 keys
+    wl = WORKLOADS["1p3b"].with_(B=1, T=4100, H=2, Hkv=2, seed=45)
+    T0, steps, w = 4100, 3, 4096 - wl.m
+    log("case decode max keys bf16 m=%d w=%d" % (wl.m, w))
+    od, (q, k, v, a), _ = run_decode(wl, T0, steps, w, wl.rope_base)
+    o_ref, _ = oracle_fwd(q, k, v, a, w, wl.rope_base)
+    compare("o_dec", f64(od), o_ref[:, T0:], 2e-2, 1e-2)
+
+
+def test_decode_bitwise_reproducible():
+    # the partial softmax results of the key splits are merged in split order
+    wl = WORKLOADS["long"].with_(T=700)
+    T0, steps = 600, 6
+    log("case decode determinism bf16")
+    d = torch.device("cuda:0")
+    q, k, v, a = make_inputs(wl, T_total=T0 + steps)
+    state = nha.decode_state(wl.B, wl.H, wl.Hkv, wl.d, wl.m, wl.w, wl.rope_base, dtype=wl.dtype, device=d)
+    gpu_fwd(q[:, :T0].contiguous(), k[:, :T0].contiguous(), v[:, :T0].contiguous(), a[:, :T0].contiguous(),
+            wl.w, wl.C, wl.rope_base, state_out=state)
+    runs = []
+    for _ in range(2):
+        st = state.clone()
+        outs = [nha.decode_step(*(x[:, t].contiguous().to(d) for x in (q, k, v, a)), st, wl.w,
+                                rope_base=wl.rope_base) for t in range(T0, T0 + steps)]
+        torch.cuda.synchronize()
+        runs.append((torch.stack(outs, 1).cpu(), st.cpu()))
+    assert torch.equal(runs[0][0], runs[1][0])
+    assert torch.equal(runs[0][1], runs[1][1])
