@@ -303,7 +303,19 @@ SWEEP = [
     ("config", "340m", {}, 64, True, 0),
     ("config", "gqa", {}, 2048, True, 0),
     ("config", "headline", {}, 512, True, 0),
+    # many sequences decoding together (B = 32 at 2K tokens of prefix each)
+    ("decode_batched", "long", {"B": 32, "T": 2048}, 512, False, 64),
 ]
+# The operator benchmark shape the pages describe (NHA with m = 32 slots and
+# w = 32 against a 64-slot gated-slot model and full attention, over the
+# sequence length); the pages print no B, H, d or T list, so these are one
+# sequence of 16 heads of dimension 128 at T = 2K .. 32K.  NHA w = 0, m = 64
+# is the gated-slot point; w = T the full causal attention curve (plus m null
+# slots).
+for _T in (2048, 4096, 8192, 16384, 32768):
+    SWEEP.append(("operator_nha_m32_w32", "long", {"T": _T, "m": 32}, 32, True, 0))
+    SWEEP.append(("operator_slots_m64_w0", "long", {"T": _T, "m": 64}, 0, True, 0))
+    SWEEP.append(("operator_full_attention_w_eq_T", "long", {"T": _T, "m": 32}, _T, True, 0))
 
 
 def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
@@ -378,8 +390,9 @@ def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
                             out=outs)
         e1.record()
         torch.cuda.synchronize()
-        line["decode_us_per_token"] = round(e0.elapsed_time(e1) * 1e3 / ndec, 2)
-        line["decode_note"] = "eager: one Python call per token (host-bound); graph: the same calls captured in a HIP graph"
+        line["decode_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / ndec, 2)
+        line["decode_note"] = ("one step = one token of each of the B sequences; eager: one Python call per step "
+                               "(host-bound); graph: the same calls captured in a HIP graph")
         # the same ndec steps captured once in a HIP graph (the state keeps
         # advancing between replays; only the timing is of interest here)
         g = torch.cuda.CUDAGraph()
@@ -393,7 +406,8 @@ def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
         g.replay()
         e1.record()
         torch.cuda.synchronize()
-        line["decode_graph_us_per_token"] = round(e0.elapsed_time(e1) * 1e3 / ndec, 2)
+        line["decode_graph_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / ndec, 2)
+        line["decode_graph_tokens_per_s"] = round(wl.B * ndec / (e0.elapsed_time(e1) / 1e3), 1)
     print(json.dumps(line), flush=True)
 
 

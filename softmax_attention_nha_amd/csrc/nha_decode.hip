@@ -77,7 +77,7 @@ __device__ __forceinline__ void dec_rope_cs(float (&x)[8], int li, const float (
 
 constexpr int kDecGH = 4;  // query heads per pass
 
-template <typename T, int D>
+template <typename T, int D, int KPG>
 __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, const T* __restrict__ kin,
                                                    const T* __restrict__ vin, const T* __restrict__ alpha,
                                                    float* __restrict__ SK, float* __restrict__ SV,
@@ -85,8 +85,9 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
                                                    const T* __restrict__ RKR, const long long* __restrict__ pos,
                                                    float* __restrict__ part, int H, int Hkv, int m, int w, int NS,
                                                    float scale, RopeTheta th, int rope) {
-  constexpr int LPK = D / 8, NG = 256 / LPK, KPG = kDecodeKeysPerSplit / NG, PP = D + 4, HALF = D / 2;
-  static_assert(2 * KPG == LPK, "a lane's keys halve once per lane bit but the lowest");
+  // KPG keys per group of LPK lanes; a split takes at most KPG * NG keys
+  constexpr int LPK = D / 8, NG = 256 / LPK, PP = D + 4, HALF = D / 2, LPR = LPK / KPG;
+  static_assert(KPG >= 1 && LPR >= 2 && KPG * NG <= kDecodeKeysPerSplit, "keys per lane group");
   __shared__ float lg[kDecGH][kDecodeKeysPerSplit];  // logits of this split's keys (log2 units)
   __shared__ float red[kDecGH][4];
   __shared__ float wsum[4][kDecGH][D + 1];
@@ -200,8 +201,8 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
       if (rope && hh < nh) dec_rope_cs<D>(qr[hh], li, cs, sn);
     }
     // 2a. logits (log2 units) of this group's keys: lane li ends up with the
-    // full dot product of key (li >> 1) & (KPG - 1) of its group
-    const int kmine = (li >> 1) & (KPG - 1), jmine = grp + NG * kmine;
+    // full dot product of key li / LPR of its group
+    const int kmine = li / LPR, jmine = grp + NG * kmine;
 #pragma unroll
     for (int hh = 0; hh < kDecGH; ++hh) {
       if (hh < nh) {
@@ -213,9 +214,10 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
           for (int r = 0; r < 8; ++r) acc += xk[kk][r] * (isslot[kk] ? qs[hh][r] : qr[hh][r]);
           P[kk] = acc;
         }
-        // halving butterfly: at lane bit msk = LPK/2, LPK/4, .., 2 the lane
+        // halving butterfly: at lane bit msk = LPK/2, LPK/4, .., LPR the lane
         // keeps the upper half of its keys if that bit is set, the lower half
-        // otherwise, adding its partner's part of the kept half
+        // otherwise, adding its partner's part of the kept half; the lane bits
+        // below LPR then sum the one key left
 #pragma unroll
         for (int lvl = 0; (KPG >> lvl) > 1; ++lvl) {
           const int n = KPG >> lvl, msk = LPK >> (lvl + 1);
@@ -227,8 +229,9 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
             P[i] = (up ? P[i + n / 2] : P[i]) + rcv;
           }
         }
-        P[0] += __shfl_xor(P[0], 1, 64);
-        if ((li & 1) == 0 && jmine < nmine) lg[hh][jmine] = P[0] * sl2;
+#pragma unroll
+        for (int msk = LPR / 2; msk >= 1; msk >>= 1) P[0] += __shfl_xor(P[0], msk, 64);
+        if (li % LPR == 0 && jmine < nmine) lg[hh][jmine] = P[0] * sl2;
       }
     }
     __syncthreads();
@@ -389,12 +392,15 @@ template <typename T, int D>
 static hipError_t decode_impl(const Shape& s, const RopeTheta& th, const DecodePtrs& p, hipStream_t st) {
   StateLayout L = state_layout(s);
   char* base = (char*)p.state;
-  const int NS = decode_splits(s), units = s.B * s.Hkv;
-  hipLaunchKernelGGL((k_dec_split<T, D>), dim3(NS, units), dim3(256), 0, st, (const T*)p.q, (const T*)p.k,
-                     (const T*)p.v, (const T*)p.alpha, (float*)(base + L.sk), (float*)(base + L.sv),
-                     (const T*)(base + L.rk), (const T*)(base + L.rv), (const T*)(base + L.rkr),
-                     (const long long*)(base + L.pos), (float*)(base + L.part), s.H, s.Hkv, s.m, s.w, NS, s.scale, th,
-                     s.rope ? 1 : 0);
+  const DecodeSplit sp = decode_splits(s);
+  const int NS = sp.ns, units = s.B * s.Hkv;
+  // half-size key groups (fewer registers, more workgroups per CU) whenever
+  // the keys fit them
+  auto split = sp.small ? k_dec_split<T, D, D / 32 < 1 ? 1 : D / 32> : k_dec_split<T, D, D / 16>;
+  hipLaunchKernelGGL(split, dim3(NS, units), dim3(256), 0, st, (const T*)p.q, (const T*)p.k, (const T*)p.v,
+                     (const T*)p.alpha, (float*)(base + L.sk), (float*)(base + L.sv), (const T*)(base + L.rk),
+                     (const T*)(base + L.rv), (const T*)(base + L.rkr), (const long long*)(base + L.pos),
+                     (float*)(base + L.part), s.H, s.Hkv, s.m, s.w, NS, s.scale, th, s.rope ? 1 : 0);
   hipLaunchKernelGGL((k_dec_merge<T, D>), dim3(units), dim3(256), 0, st, (const float*)(base + L.part),
                      (const T*)p.k, (const T*)p.v, (T*)(base + L.rk), (T*)(base + L.rv), (T*)(base + L.rkr),
                      (long long*)(base + L.pos), (T*)p.o, s.H, s.Hkv, s.w, NS, th, s.rope ? 1 : 0);

@@ -99,16 +99,28 @@ inline StateLayout state_layout(const Shape& s) {
 }
 // Workgroups per (batch, KV head) of a decode step: enough to fill the chip,
 // at least 8 keys each, at most kDecodeKeysPerSplit (so m + w <=
-// kDecodeSplitMax * kDecodeKeysPerSplit, checked by the API).
+// kDecodeSplitMax * kDecodeKeysPerSplit, checked by the API).  `small`: every
+// split has at most kDecodeKeysPerSplit / 2 keys, so the half-size key groups
+// serve it.
 constexpr int kDecodeKeysPerSplit = 128;
-inline int decode_splits(const Shape& s) {
+struct DecodeSplit {
+  int ns;
+  bool small;
+};
+inline DecodeSplit decode_splits(const Shape& s) {
   const int units = s.B * s.Hkv, keys = s.m + s.w;
   int ns = 256 / (units > 0 ? units : 1);
   if (ns > kDecodeSplitMax) ns = kDecodeSplitMax;
   if (ns > keys / 8) ns = keys / 8;
+  const int half = kDecodeKeysPerSplit / 2;
+  const int need_small = (keys + half - 1) / half;
+  if (need_small <= kDecodeSplitMax) {
+    if (ns < need_small) ns = need_small;
+    return {ns < 1 ? 1 : ns, true};
+  }
   const int need = (keys + kDecodeKeysPerSplit - 1) / kDecodeKeysPerSplit;
   if (ns < need) ns = need;
-  return ns < 1 ? 1 : ns;
+  return {ns < 1 ? 1 : ns, false};
 }
 
 // Records caller-provided timing events around consecutive launches.
