@@ -187,14 +187,21 @@ STAGE_KERNEL = {  # stage name -> kernel symbol fragment in the profiler's outpu
 }
 
 
-def source_digest():
-    """sha256 over the kernel sources: counters taken on other sources are stale."""
+# translation unit of each kernel that counters are taken for
+KERNEL_SOURCE = {"k_bwd_slot_b": "nha_bwd.hip", "k_bwd_slot_a": "nha_bwd.hip", "k_adj_scan": "nha_bwd.hip",
+                 "k_win_bwd_dq": "nha_bwd.hip", "k_win_bwd_dkdv": "nha_bwd.hip", "k_slot_fwd": "nha_fwd.hip",
+                 "k_win_fwd": "nha_fwd.hip", "k_state_scan": "nha_fwd.hip"}
+
+
+def source_digest(kernel):
+    """sha256 over the kernel's translation unit and the shared headers:
+    counters taken on other sources are stale."""
     import hashlib
 
     h = hashlib.sha256()
     src = os.path.join(ROOT, "softmax_attention_nha_amd", "csrc")
     for f in sorted(os.listdir(src)):
-        if f.endswith((".hip", ".h", ".cpp")):
+        if f.endswith(".h") or f == KERNEL_SOURCE.get(kernel, "nha_bwd.hip"):
             with open(os.path.join(src, f), "rb") as fh:
                 h.update(f.encode() + fh.read())
     return h.hexdigest()
@@ -248,7 +255,7 @@ def traffic_summary(dirs, kernel, copy_mib):
         "fetch_scale": round(ff, 4),
         "write_scale": round(fw, 4),
         "hbm_bytes_per_launch": round(fetch * 1024.0 / ff + write * 1024.0 / fw),
-        "source_sha256": source_digest(),
+        "source_sha256": source_digest(kernel),
     }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
@@ -285,7 +292,7 @@ def measured_traffic(stage):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel") != STAGE_KERNEL.get(stage) or t.get("source_sha256") != source_digest():
+    if t.get("kernel") != STAGE_KERNEL.get(stage) or t.get("source_sha256") != source_digest(t.get("kernel")):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -432,6 +439,7 @@ def main():
     ap.add_argument("--traffic-copy-mib", type=int, default=1024)
     ap.add_argument("--sweep", action="store_true",
                     help="time the w sweep, the T sweep (with decode), the other configurations; one JSON line each")
+    ap.add_argument("--only", metavar="LABEL", help="with --sweep: only the points of this sweep label")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print a markdown table of a rocprofv3 --kernel-trace --stats csv folder and exit")
     args = ap.parse_args()
@@ -452,6 +460,8 @@ def main():
         sys.exit(2)
     if args.sweep:
         for label, name, over, w, with_bwd, ndec in SWEEP:
+            if args.only and label != args.only:
+                continue
             sweep_point(label, WORKLOADS[name].with_(**over), w, with_bwd, ndec, max(args.steps // 2, 5),
                         max(args.warmup // 2, 2))
         return
