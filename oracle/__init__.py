@@ -13,6 +13,9 @@ Parity status of its parts (details in the tests that pin them):
     library routines and an independent brute force;
   * backward: pinned by central finite differences of the forward and by
     torch.autograd through an independent fp64 torch formulation;
+  * initial slot states and their gradients: pinned by the same closed form
+    (with the decayed initial state added), its autograd, finite differences
+    and the frozen-gate case;
   * which gate absorbs a shifted token (alpha_t versus alpha_{t-w}) and the
     rotate-half RoPE pairing: the pages do not fix them -- parity unpinned for
     those two choices (self-consistency only).
@@ -48,9 +51,9 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.POINTER(ctypes.c_double)
         i, dbl = ctypes.c_int, ctypes.c_double
-        lib.nha_oracle_fwd.argtypes = [i] * 7 + [dbl, dbl] + [P] * 8 + [i]
+        lib.nha_oracle_fwd.argtypes = [i] * 7 + [dbl, dbl] + [P] * 10 + [i]
         lib.nha_oracle_fwd.restype = i
-        lib.nha_oracle_bwd.argtypes = [i] * 7 + [dbl, dbl] + [P] * 9 + [i]
+        lib.nha_oracle_bwd.argtypes = [i] * 7 + [dbl, dbl] + [P] * 13 + [i]
         lib.nha_oracle_bwd.restype = i
         _lib = lib
     return _lib
@@ -74,20 +77,30 @@ def _dims(q, k, alpha):
     return B, T, H, Hkv, d, m
 
 
-def fwd(q, k, v, alpha, w, rope_base=10000.0, scale=0.0, threads=0, want_state=False):
+def _s0(s0, B, Hkv, m, d):
+    if s0 is None:
+        return None, None
+    s0k, s0v = _f64(s0[0]), _f64(s0[1])
+    assert s0k.shape == (B, Hkv, m, d) and s0v.shape == (B, Hkv, m, d)
+    return s0k, s0v
+
+
+def fwd(q, k, v, alpha, w, rope_base=10000.0, scale=0.0, threads=0, want_state=False, s0=None):
     """Forward. Arrays in the operator's layouts (see nha_oracle.c).
 
-    Returns (o [B,T,H,d], lse [B,H,T]) and, with want_state, also the final
-    slot states (SK, SV) each [B,Hkv,m,d]."""
+    s0: optional initial slot states (S0K, S0V), each [B,Hkv,m,d] (zero when
+    None).  Returns (o [B,T,H,d], lse [B,H,T]) and, with want_state, also the
+    final slot states (SK, SV) each [B,Hkv,m,d]."""
     q, k, v, alpha = _f64(q), _f64(k), _f64(v), _f64(alpha)
     B, T, H, Hkv, d, m = _dims(q, k, alpha)
+    s0k, s0v = _s0(s0, B, Hkv, m, d)
     o = np.zeros((B, T, H, d))
     lse = np.zeros((B, H, T))
     sk = np.zeros((B, Hkv, m, d)) if want_state else None
     sv = np.zeros((B, Hkv, m, d)) if want_state else None
     rc = _load().nha_oracle_fwd(B, T, H, Hkv, d, m, int(w), float(rope_base), float(scale),
-                                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
-                                _ptr(sk), _ptr(sv), int(threads))
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s0k), _ptr(s0v), _ptr(o),
+                                _ptr(lse), _ptr(sk), _ptr(sv), int(threads))
     if rc:
         raise ValueError("oracle: invalid dimensions")
     if want_state:
@@ -95,17 +108,23 @@ def fwd(q, k, v, alpha, w, rope_base=10000.0, scale=0.0, threads=0, want_state=F
     return o, lse
 
 
-def bwd(q, k, v, alpha, dO, w, rope_base=10000.0, scale=0.0, threads=0):
-    """Backward. Returns (dq, dk, dv, dalpha) in the input layouts."""
+def bwd(q, k, v, alpha, dO, w, rope_base=10000.0, scale=0.0, threads=0, s0=None, want_ds0=False):
+    """Backward. Returns (dq, dk, dv, dalpha) in the input layouts, and with
+    want_ds0 also the gradients (dS0K, dS0V) of the initial slot states."""
     q, k, v, alpha, dO = _f64(q), _f64(k), _f64(v), _f64(alpha), _f64(dO)
     B, T, H, Hkv, d, m = _dims(q, k, alpha)
+    s0k, s0v = _s0(s0, B, Hkv, m, d)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     da = np.zeros_like(alpha)
+    ds0k = np.zeros((B, Hkv, m, d)) if want_ds0 else None
+    ds0v = np.zeros((B, Hkv, m, d)) if want_ds0 else None
     rc = _load().nha_oracle_bwd(B, T, H, Hkv, d, m, int(w), float(rope_base), float(scale),
-                                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(dO),
-                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), int(threads))
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s0k), _ptr(s0v), _ptr(dO),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(ds0k), _ptr(ds0v), int(threads))
     if rc:
         raise ValueError("oracle: invalid dimensions")
+    if want_ds0:
+        return dq, dk, dv, da, ds0k, ds0v
     return dq, dk, dv, da

@@ -20,7 +20,12 @@
  *      design-motivation paragraph of that same section.  Reading adopted for
  *      the gate index: the printed recurrence keeps its time index t and only
  *      the token entering changes to k_{t-w} (so w = 0 is the printed
- *      recurrence exactly).  Slots start at zero.
+ *      recurrence exactly).  Slots start at the given initial states S0
+ *      (s0k, s0v; zero when NULL): the ai.info page ("Future Directions",
+ *      item 1) names learnable initial slot states as the next step, and the
+ *      operator takes them as inputs and returns their gradients.  As for
+ *      the zero start, a state is only decayed by the step that absorbs a
+ *      token, so S0 is kept unchanged until t = w.
  *   2. window   keys j in [max(0, t-w+1), t]  (the current token and the w-1
  *      before it; w = 0 gives an empty window -> a pure linear RNN, per the
  *      整体框架 / 层间混合 sections).
@@ -44,13 +49,16 @@
  *                           + <LamV_t[i], SV_{t-1}[i] - v_{t-w}>
  *   window: dq_t += R_t^T s sum_j dl^W_j R_j k_j,
  *           dk_j += R_j^T s dl^W_j R_t q_t, dv_j += p^W_j dO_t.
+ *   initial states: dS0 = a_0 Lam_0 (the adjoint carried to before t = 0).
  * The reverse sweep recomputes states segment by segment from checkpoints
  * spaced every SEG tokens.
  *
  * Layouts (row-major, C order):
  *   q, o, dq, dO : [B][T][H][d]      k, v, dk, dv : [B][T][Hkv][d]
  *   alpha, dalpha: [B][T][Hkv][m]    lse          : [B][H][T]
- *   sk_out, sv_out (final slot states, nullable): [B][Hkv][m][d]
+ *   s0k, s0v (initial slot states, nullable = zero), sk_out, sv_out (final
+ *   slot states, nullable), ds0k, ds0v (gradients of s0k, s0v, nullable):
+ *   [B][Hkv][m][d]
  * Query head h reads KV head h / (H / Hkv).
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC nha_oracle.c -o liboracle.so -lm
@@ -202,8 +210,8 @@ static void rotate_keys(const dims_t* D, const double* cs, const double* sn,
 int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w,
                    double rope_base, double scale, const double* q,
                    const double* k, const double* v, const double* alpha,
-                   double* o, double* lse, double* sk_out, double* sv_out,
-                   int nthreads) {
+                   const double* s0k, const double* s0v, double* o,
+                   double* lse, double* sk_out, double* sv_out, int nthreads) {
   dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale};
   const dims_t* D = &Dm;
   if (check_dims(D)) return 1;
@@ -219,6 +227,8 @@ int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w,
     int b = u / Hkv, g = u % Hkv;
     double* SK = (double*)calloc((size_t)m * d + 1, sizeof(double));
     double* SV = (double*)calloc((size_t)m * d + 1, sizeof(double));
+    if (s0k) memcpy(SK, s0k + (size_t)u * m * d, sizeof(double) * m * d);
+    if (s0v) memcpy(SV, s0v + (size_t)u * m * d, sizeof(double) * m * d);
     double* kr = (double*)malloc(sizeof(double) * ((size_t)T * d + 1));
     double* qr = (double*)malloc(sizeof(double) * d);
     double* p = (double*)malloc(sizeof(double) * (m + (size_t)(w < T ? w : T) + 1));
@@ -253,8 +263,9 @@ int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w,
 int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w,
                    double rope_base, double scale, const double* q,
                    const double* k, const double* v, const double* alpha,
-                   const double* dO, double* dq, double* dk, double* dv,
-                   double* dalpha, int nthreads) {
+                   const double* s0k, const double* s0v, const double* dO,
+                   double* dq, double* dk, double* dv, double* dalpha,
+                   double* ds0k, double* ds0v, int nthreads) {
   dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale};
   const dims_t* D = &Dm;
   if (check_dims(D)) return 1;
@@ -296,6 +307,8 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w,
     {
       double* SK = (double*)calloc(md + 1, sizeof(double));
       double* SV = (double*)calloc(md + 1, sizeof(double));
+      if (s0k) memcpy(SK, s0k + (size_t)u * md, sizeof(double) * md);
+      if (s0v) memcpy(SV, s0v + (size_t)u * md, sizeof(double) * md);
       for (int t = 0; t < T; ++t) {
         if (t % SEG == 0) {
           memcpy(ckK + (size_t)(t / SEG) * md, SK, sizeof(double) * md);
@@ -416,6 +429,9 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w,
         }
       }
     }
+    /* LK/LV now hold a_0 Lam_0: the gradient of the initial states */
+    if (ds0k) memcpy(ds0k + (size_t)u * md, LK, sizeof(double) * md);
+    if (ds0v) memcpy(ds0v + (size_t)u * md, LV, sizeof(double) * md);
     /* window dk: un-rotate and add */
     for (int t = 0; t < T; ++t) {
       rope_apply_T(D, cs, sn, t, dkr + (size_t)t * d, tmp);

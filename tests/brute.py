@@ -32,8 +32,10 @@ def rope_complex(x, base):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def slot_states(x, alpha, w):
-    """Closed-form slot states. x: [B,T,Hkv,d], alpha: [B,T,Hkv,m] -> [B,T,Hkv,m,d]."""
+def slot_states(x, alpha, w, s0=None):
+    """Closed-form slot states. x: [B,T,Hkv,d], alpha: [B,T,Hkv,m] -> [B,T,Hkv,m,d].
+    s0: optional initial state [B,Hkv,m,d], decayed by every absorbing step:
+    S_t += (prod_{u<=t, u>=w} alpha_u) S0."""
     B, T, Hkv, d = x.shape
     m = alpha.shape[-1]
     t_idx = torch.arange(T)
@@ -48,17 +50,21 @@ def slot_states(x, alpha, w):
     if w < T:
         xs[:, w:] = x[:, : T - w]  # x_{u-w} at step u
     coef = dec * mask[None, :, :, None, None] * beta[:, None]  # [B,t,u,Hkv,m]
-    return torch.einsum("btugm,bugd->btgmd", coef, xs)
+    S = torch.einsum("btugm,bugd->btgmd", coef, xs)
+    if s0 is not None:
+        S = S + torch.exp(Lc)[..., None] * s0[:, None]
+    return S
 
 
-def nha_brute(q, k, v, alpha, w, base=10000.0, scale=0.0):
-    """Returns (o [B,T,H,d], lse [B,H,T]); all inputs fp64 torch tensors."""
+def nha_brute(q, k, v, alpha, w, base=10000.0, scale=0.0, s0=None):
+    """Returns (o [B,T,H,d], lse [B,H,T]); all inputs fp64 torch tensors.
+    s0: optional initial slot states (S0K, S0V), each [B,Hkv,m,d]."""
     B, T, H, d = q.shape
     Hkv, m = k.shape[2], alpha.shape[-1]
     G = H // Hkv
     s = scale if scale else 1.0 / math.sqrt(d)
-    SK = slot_states(k, alpha, w)  # [B,T,Hkv,m,d]
-    SV = slot_states(v, alpha, w)
+    SK = slot_states(k, alpha, w, None if s0 is None else s0[0])  # [B,T,Hkv,m,d]
+    SV = slot_states(v, alpha, w, None if s0 is None else s0[1])
     qr = rope_complex(q, base)
     kr = rope_complex(k, base)
     rep = lambda x: x.repeat_interleave(G, dim=2)  # KV head -> query heads

@@ -297,3 +297,93 @@ def test_prefix_causality():
     o2, l2 = oracle.fwd(q[:, :9], k[:, :9], v[:, :9], a[:, :9], w)
     np.testing.assert_allclose(o1[:, :9], o2, atol=1e-14)
     np.testing.assert_allclose(l1[:, :, :9], l2, atol=1e-14)
+
+
+# ---------------------------------------------------------------- initial slot states
+# Learnable initial slot states (ai.info page, "Future Directions", item 1):
+# S_{-1} = S0 instead of zero; a state is only decayed by a step that absorbs,
+# so S0 is unchanged until t = w and decays by prod alpha afterwards.
+def rand_s0(B, Hkv, m, d, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((B, Hkv, m, d)) * 0.8, rng.standard_normal((B, Hkv, m, d))
+
+
+@pytest.mark.parametrize("w", [0, 3, 12])
+def test_initial_state_matches_closed_form(w):
+    B, T, H, Hkv, d, m = 2, 11, 4, 2, 8, 5
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=50 + w)
+    s0 = rand_s0(B, Hkv, m, d, seed=60 + w)
+    o, lse, sk, sv = oracle.fwd(q, k, v, a, w, rope_base=100.0, s0=s0, want_state=True)
+    o_ref, l_ref = nha_brute(t64(q), t64(k), t64(v), t64(a), w, 100.0, s0=(t64(s0[0]), t64(s0[1])))
+    np.testing.assert_allclose(o, o_ref.numpy(), atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref.numpy(), atol=1e-12)
+    from brute import slot_states
+    np.testing.assert_allclose(sk, slot_states(t64(k), t64(a), w, t64(s0[0]))[:, -1].numpy(), atol=1e-12)
+    np.testing.assert_allclose(sv, slot_states(t64(v), t64(a), w, t64(s0[1]))[:, -1].numpy(), atol=1e-12)
+
+
+def test_initial_state_with_frozen_gates_is_attention_over_fixed_extra_keys():
+    # alpha = 1: nothing is absorbed and nothing decays, so every query sees
+    # the m fixed keys S0K (raw q, no RoPE) with values S0V beside its window
+    B, T, H, Hkv, d, m, w = 1, 9, 2, 2, 4, 3, 4
+    q, k, v, _ = rand_case(B, T, H, Hkv, d, m, seed=71)
+    a = np.ones((B, T, Hkv, m))
+    s0 = rand_s0(B, Hkv, m, d, seed=72)
+    o, lse = oracle.fwd(q, k, v, a, w, rope_base=0.0, s0=s0)
+    s = 1.0 / math.sqrt(d)
+    for t in range(T):
+        for h in range(H):
+            ls = s * (s0[0][0, h] @ q[0, t, h])  # m slot logits
+            j = np.arange(max(0, t - w + 1), t + 1)
+            lw = s * (k[0, j, h] @ q[0, t, h])
+            lg = np.concatenate([ls, lw])
+            p = scipy.special.softmax(lg)
+            ref = p[:m] @ s0[1][0, h] + p[m:] @ v[0, j, h]
+            np.testing.assert_allclose(o[0, t, h], ref, atol=1e-13)
+            assert abs(lse[0, h, t] - scipy.special.logsumexp(lg)) < 1e-13
+
+
+@pytest.mark.parametrize("w", [0, 3, 12])
+def test_initial_state_gradients_match_autograd_of_closed_form(w):
+    B, T, H, Hkv, d, m = 1, 12, 4, 2, 4, 3
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=80 + w)
+    s0 = rand_s0(B, Hkv, m, d, seed=90 + w)
+    dO = np.random.default_rng(97).standard_normal(q.shape)
+    dq, dk, dv, da, ds0k, ds0v = oracle.bwd(q, k, v, a, dO, w, rope_base=100.0, s0=s0, want_ds0=True)
+    tq, tk, tv, ta, t0k, t0v = (t64(x).requires_grad_(True) for x in (q, k, v, a, s0[0], s0[1]))
+    o, _ = nha_brute(tq, tk, tv, ta, w, 100.0, s0=(t0k, t0v))
+    (o * t64(dO)).sum().backward()
+    for got, ref in ((dq, tq), (dk, tk), (dv, tv), (da, ta), (ds0k, t0k), (ds0v, t0v)):
+        np.testing.assert_allclose(got, ref.grad.numpy(), atol=1e-11)
+
+
+def test_initial_state_gradients_match_finite_differences():
+    B, T, H, Hkv, d, m, w = 1, 10, 2, 1, 4, 3, 3
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=33)
+    s0 = rand_s0(B, Hkv, m, d, seed=34)
+    dO = np.random.default_rng(96).standard_normal(q.shape)
+    g = oracle.bwd(q, k, v, a, dO, w, rope_base=50.0, s0=s0, want_ds0=True)
+    rng = np.random.default_rng(2)
+    h = 1e-6
+    for which in (0, 1):
+        for _ in range(12):
+            idx = tuple(rng.integers(0, n) for n in s0[which].shape)
+            sp = [s0[0].copy(), s0[1].copy()]
+            sm = [s0[0].copy(), s0[1].copy()]
+            sp[which][idx] += h
+            sm[which][idx] -= h
+            fp = (oracle.fwd(q, k, v, a, w, rope_base=50.0, s0=sp)[0] * dO).sum()
+            fm = (oracle.fwd(q, k, v, a, w, rope_base=50.0, s0=sm)[0] * dO).sum()
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - g[4 + which][idx]) < 1e-7 * max(1.0, abs(fd)), (which, idx, fd)
+
+
+def test_zero_initial_state_is_the_default():
+    B, T, H, Hkv, d, m, w = 1, 13, 2, 2, 4, 3, 4
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=35)
+    z = (np.zeros((B, Hkv, m, d)), np.zeros((B, Hkv, m, d)))
+    dO = np.random.default_rng(3).standard_normal(q.shape)
+    for x, y in zip(oracle.fwd(q, k, v, a, w), oracle.fwd(q, k, v, a, w, s0=z)):
+        assert np.array_equal(x, y)
+    for x, y in zip(oracle.bwd(q, k, v, a, dO, w), oracle.bwd(q, k, v, a, dO, w, s0=z)):
+        assert np.array_equal(x, y)
