@@ -167,6 +167,34 @@ nha_status nha_decode_step(const nha_desc* desc, const void* q_t,
                            const void* alpha_t, void* state, void* o_t,
                            void* stream);
 
+/* ---------------------------------------------------------------- initial slot states
+ * Learnable initial memory-slot states (the ai.info page, "Future
+ * Directions", item 1: parameter-efficient finetuning on slot initial
+ * states).  The slots start from S0 instead of zero; as for the zero start a
+ * state is only decayed by a step that absorbs a token, so S0 is unchanged
+ * until t = w and is scaled by the product of alpha_u (w <= u <= t) after.
+ *   s0k, s0v    device, float [B][Hkv][m][d] (S0 of the key and value slots),
+ *               16-byte aligned, required (pass zeros for the zero start)
+ * nha_fwd_s0: nha_fwd starting from S0 (state_out then holds the state after
+ *   token T-1 of this segment, S0 decayed and all absorptions included).
+ * nha_bwd_s0: nha_bwd of nha_fwd_s0 (recomputes the forward's prologue with
+ *   S0), also writing
+ *   ds0k, ds0v  device, float [B][Hkv][m][d]: gradients of the loss w.r.t.
+ *               s0k, s0v (per batch row: a state shared over the batch gets
+ *               the sum over b), fully overwritten.
+ * Errors as for nha_fwd / nha_bwd; a NULL or misaligned s0k, s0v, ds0k or ds0v
+ * returns NHA_ERR_INVALID_ARG. */
+nha_status nha_fwd_s0(const nha_desc* desc, const void* q, const void* k,
+                      const void* v, const void* alpha, const float* s0k,
+                      const float* s0v, void* o, float* lse, void* state_out,
+                      void* ws, size_t ws_bytes, void* stream);
+nha_status nha_bwd_s0(const nha_desc* desc, const void* q, const void* k,
+                      const void* v, const void* alpha, const float* s0k,
+                      const float* s0v, const void* o, const float* lse,
+                      const void* dO, void* dq, void* dk, void* dv,
+                      float* dalpha, float* ds0k, float* ds0v, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- timing
  * Kernel launches that one nha_fwd (backward = 0), nha_bwd (backward = 1) or
  * nha_bwd_after_fwd (backward = 2) call enqueues for this descriptor

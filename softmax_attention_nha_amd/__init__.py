@@ -37,6 +37,8 @@ EXPORTED = (
     "nha_bwd_timed",
     "nha_bwd_after_fwd",
     "nha_bwd_after_fwd_timed",
+    "nha_fwd_s0",
+    "nha_bwd_s0",
 )
 
 
@@ -103,6 +105,10 @@ def load():
     lib.nha_bwd_after_fwd_timed.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                             ctypes.POINTER(vp)]
     lib.nha_bwd_after_fwd_timed.restype = st
+    lib.nha_fwd_s0.argtypes = [D] + [vp] * 10 + [sz, vp]
+    lib.nha_fwd_s0.restype = st
+    lib.nha_bwd_s0.argtypes = [D] + [vp] * 16 + [sz, vp]
+    lib.nha_bwd_s0.restype = st
     lib.nha_status_string.argtypes = [st]
     lib.nha_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -186,12 +192,20 @@ def decode_state_size(desc):
     return n
 
 
+def _check_s0(s0, B, Hkv, m, d, dev):
+    if len(s0) != 2:
+        raise ValueError("s0 must be (S0K, S0V)")
+    for t, nm in zip(s0, ("s0k", "s0v")):
+        _check(t, nm, (B, Hkv, m, d), torch.float32, dev)
+
+
 def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, workspace=None, out=None,
-        lse_out=None, events=None):
+        lse_out=None, events=None, s0=None):
     """Chunkwise-parallel forward. Returns (o [B,T,H,d], lse [B,H,T] float32).
 
     state_out: optional uint8 decode state tensor (decode_state()) that receives
-    the state after the last token."""
+    the state after the last token.  s0: optional initial slot states
+    (S0K, S0V), float32 [B,Hkv,m,d] each (nha_fwd_s0; no timing events)."""
     desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
     dev, dt = q.device, q.dtype
     B, T, H, d = q.shape
@@ -205,6 +219,13 @@ def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, w
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev) if lse_out is None else lse_out
     n = workspace_size(desc)
     ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(n, dtype=torch.uint8, device=dev)
+    if s0 is not None:
+        _check_s0(s0, B, Hkv, m, d, dev)
+        rc = lib.nha_fwd_s0(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s0[0]), _ptr(s0[1]),
+                            _ptr(o), _ptr(lse), _ptr(state_out), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+        if rc != NHA_OK:
+            raise NhaError(rc, "nha_fwd_s0")
+        return o, lse
     rc = lib.nha_fwd_timed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
                            _ptr(state_out), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev),
                            _events_arg(events))
@@ -214,12 +235,14 @@ def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, w
 
 
 def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, workspace=None, out=None,
-        events=None, after_fwd=False):
+        events=None, after_fwd=False, s0=None):
     """Gradients of fwd. Returns (dq, dk, dv, dalpha); dalpha is float32.
 
     after_fwd=True calls nha_bwd_after_fwd: `workspace` must then be the one
     the forward of these inputs ran with, untouched since (the forward's RoPE'd
-    q/k, gate products and chunk-start states are read from it)."""
+    q/k, gate products and chunk-start states are read from it).  s0: the
+    forward's initial slot states (S0K, S0V) (nha_bwd_s0); the result then ends
+    with their gradients: (dq, dk, dv, dalpha, dS0K, dS0V)."""
     desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
     dev, dt = q.device, q.dtype
     B, T, H, d = q.shape
@@ -242,6 +265,17 @@ def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, works
     else:
         ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(
             n, dtype=torch.uint8, device=dev)
+    if s0 is not None:
+        if after_fwd:
+            raise ValueError("s0 with after_fwd is not provided (nha_bwd_s0 recomputes the prologue)")
+        _check_s0(s0, B, Hkv, m, d, dev)
+        ds0k, ds0v = torch.empty_like(s0[0]), torch.empty_like(s0[1])
+        rc = lib.nha_bwd_s0(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s0[0]), _ptr(s0[1]),
+                            _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(ds0k),
+                            _ptr(ds0v), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+        if rc != NHA_OK:
+            raise NhaError(rc, "nha_bwd_s0")
+        return dq, dk, dv, da, ds0k, ds0v
     fn = lib.nha_bwd_after_fwd_timed if after_fwd else lib.nha_bwd_timed
     rc = fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
             _ptr(dk), _ptr(dv), _ptr(da), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev), _events_arg(events))

@@ -134,6 +134,24 @@ nha_status nha_fwd_timed(const nha_desc* desc, const void* q, const void* k, con
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
 }
 
+nha_status nha_fwd_s0(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                      const float* s0k, const float* s0v, void* o, float* lse, void* state_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  Shape s;
+  nha_status rc = make_shape(desc, true, &s);
+  if (rc != NHA_OK) return rc;
+  if (!q || !k || !v || !alpha || !o || !ws || !s0k || !s0v) return NHA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(o) || !aligned16(ws) ||
+      !aligned16(s0k) || !aligned16(s0v) || (lse && !aligned16(lse)) || (state_out && !aligned16(state_out)))
+    return NHA_ERR_INVALID_ARG;
+  if (ws_bytes < fwd_ws_layout(s).total) return NHA_ERR_WORKSPACE;
+  FwdPtrs p{q, k, v, alpha, o, lse, state_out, (char*)ws, nullptr};
+  p.s0k = s0k;
+  p.s0v = s0v;
+  hipError_t e = launch_fwd(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
 nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
                    const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* dalpha,
                    void* ws, size_t ws_bytes, void* stream) {
@@ -143,7 +161,8 @@ nha_status nha_bwd(const nha_desc* desc, const void* q, const void* k, const voi
 static nha_status bwd_common(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
                              const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                              float* dalpha, void* ws, size_t ws_bytes, void* stream, void* const* events,
-                             bool after_fwd) {
+                             bool after_fwd, const float* s0k = nullptr, const float* s0v = nullptr,
+                             float* ds0k = nullptr, float* ds0v = nullptr) {
   Shape s;
   nha_status rc = make_shape(desc, true, &s);
   if (rc != NHA_OK) return rc;
@@ -155,6 +174,10 @@ static nha_status bwd_common(const nha_desc* desc, const void* q, const void* k,
     if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
   if (ws_bytes < bwd_ws_bytes(s)) return NHA_ERR_WORKSPACE;
   BwdPtrs p{q, k, v, alpha, o, dO, lse, dq, dk, dv, dalpha, (char*)ws, events, after_fwd};
+  p.s0k = s0k;
+  p.s0v = s0v;
+  p.ds0k = ds0k;
+  p.ds0v = ds0v;
   hipError_t e = launch_bwd(s, make_theta(desc), p, (hipStream_t)stream);
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
 }
@@ -176,6 +199,16 @@ nha_status nha_bwd_after_fwd_timed(const nha_desc* desc, const void* q, const vo
                                    void* dk, void* dv, float* dalpha, void* ws, size_t ws_bytes, void* stream,
                                    void* const* events) {
   return bwd_common(desc, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws, ws_bytes, stream, events, true);
+}
+
+nha_status nha_bwd_s0(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                      const float* s0k, const float* s0v, const void* o, const float* lse, const void* dO, void* dq,
+                      void* dk, void* dv, float* dalpha, float* ds0k, float* ds0v, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!s0k || !s0v || !ds0k || !ds0v) return NHA_ERR_INVALID_ARG;
+  if (!aligned16(s0k) || !aligned16(s0v) || !aligned16(ds0k) || !aligned16(ds0v)) return NHA_ERR_INVALID_ARG;
+  return bwd_common(desc, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws, ws_bytes, stream, nullptr, false, s0k,
+                    s0v, ds0k, ds0v);
 }
 
 int nha_stage_names(const nha_desc* desc, int backward, int with_state, const char** names, int max) {

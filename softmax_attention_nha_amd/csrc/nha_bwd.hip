@@ -596,7 +596,9 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
 template <typename T, int C, int MP>
 __global__ __launch_bounds__(64) void k_adj_scan(const T* __restrict__ q, const T* __restrict__ dO,
                                                  const T* __restrict__ wp, const float* __restrict__ aend,
-                                                 T* __restrict__ lin, int Tn, int H, int Hkv, int d, int NC) {
+                                                 T* __restrict__ lin, float* __restrict__ ds0k,
+                                                 float* __restrict__ ds0v, int Tn, int H, int Hkv, int d, int m,
+                                                 int NC) {
   constexpr int NB = MP / 16;
   constexpr int PC = pitch_of(C);
   constexpr bool K16 = (C % 32) != 0;
@@ -669,6 +671,8 @@ __global__ __launch_bounds__(64) void k_adj_scan(const T* __restrict__ q, const 
       __syncthreads();
     }
   }
+  // the adjoint carried to before the first token: the initial states' gradient
+  store_slot_state<NB>(LK, LV, ds0k, ds0v, unit, m, d, j0, g, cc);
 }
 
 // bf16 variant: the operands of every (chunk, query head) step -- q and dO
@@ -694,7 +698,8 @@ struct AdjStage {
 template <int C, int MP, int NS>
 __global__ __launch_bounds__(64) void k_adj_scan_b16(const bf16* __restrict__ q, const bf16* __restrict__ dO,
                                                      const bf16* __restrict__ wp, const float* __restrict__ aend,
-                                                     bf16* __restrict__ lin, int Tn, int H, int Hkv, int d,
+                                                     bf16* __restrict__ lin, float* __restrict__ ds0k,
+                                                     float* __restrict__ ds0v, int Tn, int H, int Hkv, int d, int m,
                                                      int NC) {
   using St = AdjStage<C, MP>;
   constexpr int NB = MP / 16, CPR = C / 8;
@@ -812,6 +817,8 @@ __global__ __launch_bounds__(64) void k_adj_scan_b16(const bf16* __restrict__ q,
     issue(n + NS, s);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the adjoint carried to before the first token: the initial states' gradient
+  store_slot_state<NB>(LK, LV, ds0k, ds0v, unit, m, d, j0, g, cc);
 }
 
 // ---------------------------------------------------------------- slot pass B
@@ -1751,6 +1758,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     Marks mk;
     mk.ev = p.events;
     ProloguePtrs pp{ws + L.sst, ws + L.wt, (float*)(ws + L.aend), nullptr, nullptr, nullptr, nullptr, nullptr};
+    pp.s0k = p.s0k;
+    pp.s0v = p.s0v;
     if (s.rope && s.win) {
       pp.qrot = ws + L.qrot;
       pp.krot = ws + L.krot;
@@ -1793,10 +1802,10 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     mk.mark(st);
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL((k_adj_scan_b16<C, MP, 3>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
-                         (const float*)pp.aend, lin, s.T, s.H, s.Hkv, D, s.NC);
+                         (const float*)pp.aend, lin, p.ds0k, p.ds0v, s.T, s.H, s.Hkv, D, s.m, s.NC);
     else
       hipLaunchKernelGGL((k_adj_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
-                         (const float*)pp.aend, lin, s.T, s.H, s.Hkv, D, s.NC);
+                         (const float*)pp.aend, lin, p.ds0k, p.ds0v, s.T, s.H, s.Hkv, D, s.m, s.NC);
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
                        (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.w, s.NC);

@@ -523,6 +523,40 @@ __device__ __forceinline__ void dma_tile_async(const bf16* __restrict__ base, si
 // loads were issued up front, and every step then issued STO stores and the
 // OPS loads of a new stage.  Operations complete in issue order, so this
 // waits exactly for the loads of stage c.
+// Slot-state registers of a scan wave (16 columns j0 + 4 g + r of slots
+// i = 16 nb + cc): the initial states s0k / s0v [unit][m][d] (fp32), or zero
+// when they are null; padded slots i >= m are zero.
+template <int NB>
+__device__ __forceinline__ void init_slot_state(floatx4 (&SK)[NB], floatx4 (&SV)[NB], const float* s0k,
+                                                const float* s0v, int unit, int m, int d, int j0, int g, int cc) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    SK[nb] = SV[nb] = zero4();
+    const int i = 16 * nb + cc;
+    if (s0k && i < m) {
+      const size_t e = ((size_t)unit * m + i) * d + j0 + 4 * g;
+      SK[nb] = *reinterpret_cast<const floatx4*>(s0k + e);
+      SV[nb] = *reinterpret_cast<const floatx4*>(s0v + e);
+    }
+  }
+}
+
+// The same registers out to ds0k / ds0v [unit][m][d] (fp32) when not null.
+template <int NB>
+__device__ __forceinline__ void store_slot_state(const floatx4 (&SK)[NB], const floatx4 (&SV)[NB], float* ok,
+                                                 float* ov, int unit, int m, int d, int j0, int g, int cc) {
+  if (!ok) return;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int i = 16 * nb + cc;
+    if (i < m) {
+      const size_t e = ((size_t)unit * m + i) * d + j0 + 4 * g;
+      *reinterpret_cast<floatx4*>(ok + e) = SK[nb];
+      *reinterpret_cast<floatx4*>(ov + e) = SV[nb];
+    }
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt field");

@@ -159,7 +159,8 @@ template <typename T, int C, int MP>
 __global__ __launch_bounds__(64) void k_state_scan(const T* __restrict__ kk, const T* __restrict__ vv,
                                                    const T* __restrict__ Wt, const float* __restrict__ aend,
                                                    T* __restrict__ sst, float* __restrict__ skout,
-                                                   float* __restrict__ svout, int Tn, int Hkv, int d, int m,
+                                                   float* __restrict__ svout, const float* __restrict__ s0k,
+                                                   const float* __restrict__ s0v, int Tn, int Hkv, int d, int m,
                                                    int w, int NC) {
   using R_t = ScanRegs<T, C, MP>;
   constexpr int NB = R_t::NB, KS = R_t::KS;
@@ -172,8 +173,7 @@ __global__ __launch_bounds__(64) void k_state_scan(const T* __restrict__ kk, con
   const int j0 = (L % gridDim.x) * 16, unit = L / gridDim.x;
   const int b = unit / Hkv, hg = unit % Hkv;
   floatx4 SK[NB], SV[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) SK[nb] = SV[nb] = zero4();
+  init_slot_state<NB>(SK, SV, s0k, s0v, unit, m, d, j0, g, cc);
   const size_t chunk_elems = 2 * (size_t)MP * d;
   R_t cur, nxt;
   scan_load<T, C, MP>(cur, kk, vv, Wt, aend, 0, unit, b, hg, j0, Tn, Hkv, d, w, NC, l);
@@ -263,7 +263,8 @@ template <int C, int MP, int NS>
 __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ kk, const bf16* __restrict__ vv,
                                                        const bf16* __restrict__ Wt, const float* __restrict__ aend,
                                                        bf16* __restrict__ sst, float* __restrict__ skout,
-                                                       float* __restrict__ svout, int Tn, int Hkv, int d, int m,
+                                                       float* __restrict__ svout, const float* __restrict__ s0k,
+                                                       const float* __restrict__ s0v, int Tn, int Hkv, int d, int m,
                                                        int w, int NC) {
   using St = ScanStage<C, MP>;
   constexpr int NB = MP / 16, CPR = C / 8;  // W^T 16-byte chunks per row
@@ -322,8 +323,7 @@ __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ 
     }
   };
   floatx4 SK[NB], SV[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) SK[nb] = SV[nb] = zero4();
+  init_slot_state<NB>(SK, SV, s0k, s0v, unit, m, d, j0, g, cc);
   const size_t chunk_elems = 2 * (size_t)MP * d;
   for (int s = 0; s < NS; ++s) issue(s, s);
   for (int c = 0; c < NC; ++c) {
@@ -1114,10 +1114,12 @@ static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const
   mk.mark(st);
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
+                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
+                       s.w, s.NC);
   else
     hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, s.T, s.Hkv, D, s.m, s.w, s.NC);
+                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
+                       s.w, s.NC);
 }
 
 template <typename T, int D, int MP, int C>
@@ -1137,6 +1139,8 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     mk.ev = p.events;
     StateLayout SL{};
     ProloguePtrs pp{p.ws + L.sst, p.ws + L.wt, (float*)(p.ws + L.aend), nullptr, nullptr, nullptr, nullptr, nullptr};
+    pp.s0k = p.s0k;
+    pp.s0v = p.s0v;
     if (s.rope && s.win) {
       pp.qrot = p.ws + L.qrot;
       pp.krot = p.ws + L.krot;

@@ -150,6 +150,8 @@ struct ProloguePtrs {
   float2* rcs;  // RoPE (cos, sin) table, same condition
   float* skout;  // nullable
   float* svout;
+  const float* s0k = nullptr;  // initial slot states [B*Hkv][m][d], nullable = zero
+  const float* s0v = nullptr;
 };
 hipError_t launch_prologue(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
                            const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st);
@@ -166,6 +168,8 @@ struct FwdPtrs {
   void* state_out;  // nullable
   char* ws;
   void* const* events;  // nullable timing events
+  const float* s0k = nullptr;  // initial slot states [B*Hkv][m][d], nullable = zero
+  const float* s0v = nullptr;
 };
 hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st);
 
@@ -185,6 +189,10 @@ struct BwdPtrs {
   char* ws;
   void* const* events;  // nullable timing events
   bool after_fwd;       // the workspace already holds this input's forward prologue
+  const float* s0k = nullptr;  // initial slot states [B*Hkv][m][d], nullable = zero
+  const float* s0v = nullptr;
+  float* ds0k = nullptr;  // their gradients, nullable
+  float* ds0v = nullptr;
 };
 hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st);
 

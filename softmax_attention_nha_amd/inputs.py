@@ -86,3 +86,13 @@ def make_inputs(wl: Workload, T_total=None, with_grad=False, alpha_mu=None, qk_s
     if with_grad:
         out.append(dO.to(wl.dtype).contiguous())
     return tuple(out)
+
+
+def make_initial_state(wl: Workload, seed_offset=1000):
+    """Initial slot states (S0K, S0V), each float32 [B, Hkv, m, d] ~ N(0,1)/sqrt(d)
+    (the scale of the keys and values), from their own seeded generator."""
+    g = torch.Generator(device="cpu").manual_seed(wl.seed + seed_offset)
+    shp = (wl.B, wl.Hkv, wl.m, wl.d)
+    s0k = torch.randn(shp, generator=g, dtype=torch.float32) / wl.d ** 0.5
+    s0v = torch.randn(shp, generator=g, dtype=torch.float32) / wl.d ** 0.5
+    return s0k.contiguous(), s0v.contiguous()

@@ -115,6 +115,27 @@ def test_bwd_argument_errors():
     assert rc == nha.NHA_ERR_WORKSPACE
 
 
+def test_initial_state_argument_errors():
+    lib = nha.load()
+    d = desc()
+    big = ctypes.c_size_t(1 << 40)
+    # nha_fwd_s0(desc, q, k, v, alpha, s0k, s0v, o, lse, state_out, ws, ws_bytes, stream)
+    assert lib.nha_fwd_s0(ctypes.byref(d), A, A, A, A, None, A, A, None, None, A, big, None) == nha.NHA_ERR_INVALID_ARG
+    assert lib.nha_fwd_s0(ctypes.byref(d), A, A, A, A, A, MIS, A, None, None, A, big, None) == nha.NHA_ERR_INVALID_ARG
+    n = nha.workspace_size(d)
+    rc = lib.nha_fwd_s0(ctypes.byref(d), A, A, A, A, A, A, A, None, None, A, ctypes.c_size_t(n - 1), None)
+    assert rc == nha.NHA_ERR_WORKSPACE
+    # nha_bwd_s0(desc, q, k, v, alpha, s0k, s0v, o, lse, dO, dq, dk, dv, dalpha, ds0k, ds0v, ws, ws_bytes, stream)
+    args = [A] * 15
+    rc = lib.nha_bwd_s0(ctypes.byref(d), *args[:13], None, A, A, big, None)
+    assert rc == nha.NHA_ERR_INVALID_ARG  # ds0k is required
+    rc = lib.nha_bwd_s0(ctypes.byref(d), *args[:7], None, *args[8:15], A, big, None)
+    assert rc == nha.NHA_ERR_INVALID_ARG  # lse is required
+    nb = nha.workspace_size(d, backward=True)
+    rc = lib.nha_bwd_s0(ctypes.byref(d), *args, A, ctypes.c_size_t(nb - 1), None)
+    assert rc == nha.NHA_ERR_WORKSPACE
+
+
 def test_stage_lists():
     """The backward after a forward skips the forward's first stages."""
     d = desc()
