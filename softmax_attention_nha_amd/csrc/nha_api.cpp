@@ -73,6 +73,30 @@ int device_cu_count() {
   }
   return cached[dev];
 }
+
+Fork side_fork(bool enabled) {
+  Fork none;
+  if (!enabled) return none;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return none;
+  static thread_local Fork cache[64];
+  Fork& c = cache[dev];
+  if (!c.side) {
+    hipStream_t s = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return none;
+    if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      (void)hipStreamDestroy(s);
+      return none;
+    }
+    c.side = s;
+    c.ev_fork = a;
+    c.ev_join = b;
+  }
+  return c;
+}
 }  // namespace nha
 
 

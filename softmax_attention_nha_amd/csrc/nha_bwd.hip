@@ -1757,6 +1757,7 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     const int units = s.B * s.Hkv;
     Marks mk;
     mk.ev = p.events;
+    const Fork fk = side_fork(p.events == nullptr);
     ProloguePtrs pp{ws + L.sst, ws + L.wt, (float*)(ws + L.aend), nullptr, nullptr, nullptr, nullptr, nullptr};
     pp.s0k = p.s0k;
     pp.s0v = p.s0v;
@@ -1766,7 +1767,7 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
       pp.rcs = (float2*)(ws + L.rcs);
     }
     if (!p.after_fwd) {
-      hipError_t e = launch_prologue(s, th, q, k, v, alpha, pp, mk, st);
+      hipError_t e = launch_prologue(s, th, q, k, v, alpha, pp, mk, st, fk);
       if (e != hipSuccess) return e;
     }
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
@@ -1799,35 +1800,50 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
                          (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w, s.NC,
                          nitems, s.scale);
     }
+    // the adjoint scan, and beside it on the side stream the window dq (needs
+    // D_t and the slot part of dq), enqueued after the scan so that the scan's
+    // workgroups are placed first; joined before pass B.  A two-stage ring
+    // (41 KB of LDS) leaves room for a dq workgroup (64 KB) beside two scan
+    // waves on a CU and is as fast alone as three stages.
+    fk.record(st);
     mk.mark(st);
     if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((k_adj_scan_b16<C, MP, 3>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
+      hipLaunchKernelGGL((k_adj_scan_b16<C, MP, 2>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
                          (const float*)pp.aend, lin, p.ds0k, p.ds0v, s.T, s.H, s.Hkv, D, s.m, s.NC);
     else
       hipLaunchKernelGGL((k_adj_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
                          (const float*)pp.aend, lin, p.ds0k, p.ds0v, s.T, s.H, s.Hkv, D, s.m, s.NC);
+    const hipStream_t sq = fk.follow(st);
+    mk.mark(sq);
+    if constexpr (sizeof(T) == 2) {
+      constexpr int NWV = 4;
+      const unsigned nt = (unsigned)((s.T + 32 * NWV - 1) / (32 * NWV));
+      hipLaunchKernelGGL((k_win_bwd_dq_b16<D, NWV>), dim3(nt, s.B * s.H), dim3(NWV * 64), 0, sq, qr, kr, v, dO,
+                         p.lse, Dt, dqs, (const float2*)pp.rcs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale);
+    } else {
+      hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, sq, qr, kr, v, dO, p.lse, Dt,
+                         dqs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+    }
+    fk.join(st);
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
                        (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.w, s.NC);
-    mk.mark(st);
-    hipLaunchKernelGGL((k_dalpha_tail<T, MP, C>), dim3(s.NC, units), dim3(256), 0, st, alpha, csum, p.dalpha, s.T,
+    // the dalpha carry on the side stream, beside the window dk/dv
+    const hipStream_t sa = fk.begin(st);
+    mk.mark(sa);
+    hipLaunchKernelGGL((k_dalpha_tail<T, MP, C>), dim3(s.NC, units), dim3(256), 0, sa, alpha, csum, p.dalpha, s.T,
                        s.Hkv, s.m, s.w, s.NC);
     mk.mark(st);
     if constexpr (sizeof(T) == 2) {
       constexpr int NWV = 4;
       const unsigned nt = (unsigned)((s.T + 32 * NWV - 1) / (32 * NWV));
-      hipLaunchKernelGGL((k_win_bwd_dq_b16<D, NWV>), dim3(nt, s.B * s.H), dim3(NWV * 64), 0, st, qr, kr, v, dO, p.lse,
-                         Dt, dqs, (const float2*)pp.rcs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale);
-      mk.mark(st);
       hipLaunchKernelGGL((k_win_bwd_dkdv_b16<D, NWV>), dim3(nt, units), dim3(NWV * 64), 0, st, qr, kr, v, dO, p.lse,
                          Dt, dkap, dnu, (const float2*)pp.rcs, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale);
     } else {
-      hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt,
-                         dqs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
-      mk.mark(st);
       hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dkap,
                          dnu, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
     }
+    fk.join(st);
     mk.mark(st);
     return hipGetLastError();
   }
@@ -1861,19 +1877,19 @@ int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max) {
   const char* all[16];
   int n = 0;
   if (!after_fwd) {
+    all[n++] = "chunk_gates";
+    all[n++] = "state_scan";
     if (s.rope && s.win) {
       all[n++] = "rope_cs";
       all[n++] = "rope";
     }
-    all[n++] = "chunk_gates";
-    all[n++] = "state_scan";
   }
   if (s.dtype != NHA_DTYPE_BF16) all[n++] = "bwd_prep";  // bf16: inside slot pass A
   all[n++] = "slot_bwd_a";
   all[n++] = "adj_scan";
+  all[n++] = "win_bwd_dq";
   all[n++] = "slot_bwd_b";
   all[n++] = "dalpha_tail";
-  all[n++] = "win_bwd_dq";
   all[n++] = "win_bwd_dkdv";
   for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];
   return n;

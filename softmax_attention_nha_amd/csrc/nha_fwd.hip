@@ -1097,20 +1097,12 @@ __global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ v
 // ---------------------------------------------------------------- host launcher
 template <typename T, int D, int MP, int C>
 static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const T* k, const T* v, const T* alpha,
-                          const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+                          const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk) {
   const int units = s.B * s.Hkv;
-  if (s.rope && s.win) {
-    const long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
-    const long ncs = (long)s.T * (s.d / 2), thr = (nq + nk) * (s.d / 16);
-    mk.mark(st);
-    hipLaunchKernelGGL(k_rope_cs, dim3((unsigned)((ncs + 255) / 256)), dim3(256), 0, st, pp.rcs, s.T, s.d / 2, th);
-    mk.mark(st);
-    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, st, q, k, (T*)pp.qrot,
-                       (T*)pp.krot, nq, nk, s.H, s.Hkv, s.T, s.d, (const float2*)pp.rcs);
-  }
   mk.mark(st);
   hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend, s.T,
                      s.Hkv, s.m, s.w, s.NC);
+  if (s.rope && s.win) fk.record(st);
   mk.mark(st);
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
@@ -1120,6 +1112,21 @@ static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const
     hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
                        (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
                        s.w, s.NC);
+  if (s.rope && s.win) {
+    // RoPE (HBM-bound, no LDS) on the side stream beside the state scan (bound
+    // by its chain of dependent steps; the gate products, HBM-bound too, run
+    // before both), enqueued after the scan so that the scan's workgroups are
+    // placed first; joined at the end
+    const hipStream_t rs = fk.follow(st);
+    const long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
+    const long ncs = (long)s.T * (s.d / 2), thr = (nq + nk) * (s.d / 16);
+    mk.mark(rs);
+    hipLaunchKernelGGL(k_rope_cs, dim3((unsigned)((ncs + 255) / 256)), dim3(256), 0, rs, pp.rcs, s.T, s.d / 2, th);
+    mk.mark(rs);
+    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, rs, q, k, (T*)pp.qrot,
+                       (T*)pp.krot, nq, nk, s.H, s.Hkv, s.T, s.d, (const float2*)pp.rcs);
+  }
+  if (s.rope && s.win) fk.join(st);
 }
 
 template <typename T, int D, int MP, int C>
@@ -1151,7 +1158,7 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       pp.skout = (float*)((char*)p.state_out + SL.sk);
       pp.svout = (float*)((char*)p.state_out + SL.sv);
     }
-    prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st);
+    prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st, side_fork(p.events == nullptr));
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
     mk.mark(st);
@@ -1192,30 +1199,34 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
 
 template <typename T, int MP, int C>
 static void prologue_d(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
-                       const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+                       const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk) {
   switch (s.d) {
-    case 32: return prologue_impl<T, 32, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st);
-    case 64: return prologue_impl<T, 64, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st);
-    case 128: return prologue_impl<T, 128, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st);
+    case 32:
+      return prologue_impl<T, 32, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st, fk);
+    case 64:
+      return prologue_impl<T, 64, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st, fk);
+    case 128:
+      return prologue_impl<T, 128, MP, C>(s, th, (const T*)q, (const T*)k, (const T*)v, (const T*)alpha, pp, mk, st,
+                                          fk);
   }
 }
 template <typename T, int MP>
 static void prologue_c(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
-                       const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+                       const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk) {
   switch (s.C) {
-    case 16: return prologue_d<T, MP, 16>(s, th, q, k, v, alpha, pp, mk, st);
-    case 32: return prologue_d<T, MP, 32>(s, th, q, k, v, alpha, pp, mk, st);
-    case 64: return prologue_d<T, MP, 64>(s, th, q, k, v, alpha, pp, mk, st);
+    case 16: return prologue_d<T, MP, 16>(s, th, q, k, v, alpha, pp, mk, st, fk);
+    case 32: return prologue_d<T, MP, 32>(s, th, q, k, v, alpha, pp, mk, st, fk);
+    case 64: return prologue_d<T, MP, 64>(s, th, q, k, v, alpha, pp, mk, st, fk);
   }
 }
 hipError_t launch_prologue(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
-                           const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st) {
+                           const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk) {
   if (s.dtype == NHA_DTYPE_BF16) {
-    if (s.mp == 32) prologue_c<bf16, 32>(s, th, q, k, v, alpha, pp, mk, st);
-    else prologue_c<bf16, 64>(s, th, q, k, v, alpha, pp, mk, st);
+    if (s.mp == 32) prologue_c<bf16, 32>(s, th, q, k, v, alpha, pp, mk, st, fk);
+    else prologue_c<bf16, 64>(s, th, q, k, v, alpha, pp, mk, st, fk);
   } else {
-    if (s.mp == 32) prologue_c<float, 32>(s, th, q, k, v, alpha, pp, mk, st);
-    else prologue_c<float, 64>(s, th, q, k, v, alpha, pp, mk, st);
+    if (s.mp == 32) prologue_c<float, 32>(s, th, q, k, v, alpha, pp, mk, st, fk);
+    else prologue_c<float, 64>(s, th, q, k, v, alpha, pp, mk, st, fk);
   }
   return hipGetLastError();
 }
@@ -1252,12 +1263,12 @@ hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hip
 int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
   const char* all[8];
   int n = 0;
+  all[n++] = "chunk_gates";
+  all[n++] = "state_scan";
   if (s.rope && s.win) {
     all[n++] = "rope_cs";
     all[n++] = "rope";
   }
-  all[n++] = "chunk_gates";
-  all[n++] = "state_scan";
   all[n++] = "slot_fwd";
   all[n++] = "win_fwd";
   if (with_state) all[n++] = "export_state";

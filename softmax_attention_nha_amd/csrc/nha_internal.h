@@ -123,6 +123,43 @@ inline DecodeSplit decode_splits(const Shape& s) {
   return {ns < 1 ? 1 : ns, false};
 }
 
+// A second stream for the launches of one call that do not depend on each
+// other (RoPE beside the gate products and the state scan; the window dq
+// beside the adjoint scan; the dalpha carry beside the window dk/dv).  The
+// side stream is created once per thread and device (default priority,
+// non-blocking) with two events; every call joins its side-stream work back
+// into the caller's stream before it returns, so the caller sees one stream.
+// `side` is null -- everything runs on the caller's stream, in order -- for
+// the timed calls (their per-launch events measure one kernel each) and when
+// the stream cannot be created.
+struct Fork {
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // fork point: the side stream's next launches start after everything
+  // enqueued on `main` so far (launches enqueued on `main` after this point
+  // are not waited for)
+  void record(hipStream_t main) const {
+    if (side) (void)hipEventRecord(ev_fork, main);
+  }
+  // the stream for launches that follow the last fork point
+  hipStream_t follow(hipStream_t main) const {
+    if (!side) return main;
+    (void)hipStreamWaitEvent(side, ev_fork, 0);
+    return side;
+  }
+  hipStream_t begin(hipStream_t main) const {
+    record(main);
+    return follow(main);
+  }
+  // `main` continues after everything enqueued on the side stream so far
+  void join(hipStream_t main) const {
+    if (!side) return;
+    (void)hipEventRecord(ev_join, side);
+    (void)hipStreamWaitEvent(main, ev_join, 0);
+  }
+};
+Fork side_fork(bool enabled);
+
 // Records caller-provided timing events around consecutive launches.
 struct Marks {
   void* const* ev = nullptr;
@@ -154,7 +191,7 @@ struct ProloguePtrs {
   const float* s0v = nullptr;
 };
 hipError_t launch_prologue(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
-                           const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st);
+                           const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk);
 
 // Compute units of the current device (cached per device); persistent
 // kernels size their grids with it.

@@ -131,3 +131,37 @@ def test_bwd_after_fwd_matches_bwd(name, T, C):
     torch.cuda.synchronize()
     for x, y in zip(g1, g2):
         assert torch.equal(x, y)
+
+
+def test_side_stream_results_equal_one_stream_results():
+    # the production calls run independent launches on the library's side
+    # stream; the timed calls run every launch in order on the caller's
+    # stream: both must give bitwise the same results
+    wl = WORKLOADS["1p3b"].with_(B=2, T=640, H=4, Hkv=2, seed=61)
+    w = 128
+    log("case side stream vs one stream bf16")
+    d = torch.device("cuda:0")
+    q, k, v, a, dO = (x.to(d) for x in make_inputs(wl, with_grad=True))
+    desc = nha.make_desc(wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, w, wl.C, wl.rope_base, 0.0, wl.dtype)
+
+    def events(n):
+        # the Event objects own the HIP events: keep them alive until the
+        # stream has passed every record
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()
+        return evs
+
+    res, keep = [], []
+    for timed in (False, True):
+        fe = events(len(nha.stage_names(desc)) + 1) if timed else None
+        be = events(len(nha.stage_names(desc, backward=1)) + 1) if timed else None
+        keep.append((fe, be))
+        o, lse = nha.fwd(q, k, v, a, w, C=wl.C, rope_base=wl.rope_base,
+                         events=[e.cuda_event for e in fe] if timed else None)
+        g = nha.bwd(q, k, v, a, o, lse, dO, w, C=wl.C, rope_base=wl.rope_base,
+                    events=[e.cuda_event for e in be] if timed else None)
+        torch.cuda.synchronize()
+        res.append((o, lse) + tuple(g))
+    for x, y in zip(*res):
+        assert torch.equal(x, y)
