@@ -263,6 +263,64 @@ def traffic_summary(dirs, kernel, copy_mib):
     print(json.dumps(out))
 
 
+def _kernel_short(name):
+    """Short kernel name from a demangled (nha::k_x<...>(...)) or mangled
+    (_ZN3nha<len>k_x...) profiler name; None for other kernels."""
+    if "nha::" in name:
+        return name.split("nha::")[1].split("<")[0].split("(")[0]
+    if name.startswith("_ZN3nha"):
+        rest = name[len("_ZN3nha"):]
+        digits = ""
+        while rest and rest[0].isdigit():
+            digits, rest = digits + rest[0], rest[1:]
+        return rest[: int(digits)] if digits else None
+    return None
+
+
+def counter_summary(folders):
+    """Markdown table of per-kernel SQ counters (mean per dispatch) from a
+    rocprofv3 --pmc csv folder, with the executed bf16 MFMA work
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop) and, given a --kernel-trace
+    --stats folder as well, its rate against the kernel's average duration;
+    LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; LDS
+    wait share = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES."""
+    import csv
+    import glob
+
+    folder = folders[0]
+    vals = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                k = _kernel_short(r["Kernel_Name"])
+                if not k:
+                    continue
+                d = vals.setdefault(k, {}).setdefault((f, r["Dispatch_Id"]), {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = {}
+    if len(folders) > 1:
+        for f in glob.glob(os.path.join(folders[1], "**", "*kernel_stats.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    k = _kernel_short(r["Name"])
+                    if k:
+                        dur[k] = float(r["AverageNs"]) / 1e3
+    print("| kernel | dispatches | executed bf16 MFMA GFLOP | avg us (trace) | MFMA TFLOP/s (% of 2500) "
+          "| LDS bank-conflict / LDS active | LDS wait / wave cycles |")
+    print("|---|---|---|---|---|---|---|")
+    for k, disp in sorted(vals.items()):
+        n = len(disp)
+        mean = lambda c: sum(x.get(c, 0.0) for x in disp.values()) / n
+        gf = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / 1e9
+        lds_act = mean("SQ_LDS_IDX_ACTIVE")
+        bc = mean("SQ_LDS_BANK_CONFLICT") / lds_act if lds_act else 0.0
+        wc = mean("SQ_WAVE_CYCLES")
+        lw = mean("SQ_WAIT_INST_LDS") / wc if wc else 0.0
+        us = dur.get(k)
+        rate = ("%.0f (%.1f %%)" % (gf / us * 1e3, gf / us * 1e3 / 25)) if us and gf else "—"
+        print("| %s | %d | %.2f | %s | %s | %.3f | %.3f |" % (k, n, gf, "%.1f" % us if us else "—", rate, bc, lw))
+
+
 def trace_summary(folder):
     """Markdown table (calls, average and total duration per kernel) of a
     rocprofv3 --kernel-trace --stats --output-format csv folder."""
@@ -443,11 +501,17 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="time the w sweep, the T sweep (with decode), the other configurations; one JSON line each")
     ap.add_argument("--only", metavar="LABEL", help="with --sweep: only the points of this sweep label")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="print a markdown table of per-kernel SQ counters from a rocprofv3 --pmc csv folder "
+                         "(and, optionally, a --kernel-trace --stats folder for the durations) and exit")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print a markdown table of a rocprofv3 --kernel-trace --stats csv folder and exit")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.copy_calibrate:
         copy_calibrate(args.copy_calibrate)

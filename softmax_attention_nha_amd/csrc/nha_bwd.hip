@@ -1271,13 +1271,16 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
   // byte offsets in a tile: row fragments (row c, logical chunk 2 ks + hf) and
   // transposed reads (rows 4 hf + jj / 4 (+8) of each 16-row step, columns
   // 32 dt + 16 (c / 16) + 4 (jj % 4) ..)
-  uint32_t foff[D / 16], toff[D / 32];
+  // (toff8: the same 8 rows further on; the swizzle repeats every 16 rows,
+  // not every 8)
+  uint32_t foff[D / 16], toff[D / 32], toff8[D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) foff[ks] = 2 * (c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 2>(c)));
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     const int r = 4 * hf + (jj >> 2), d0 = 32 * dt + 16 * (c >> 4) + 4 * (jj & 3);
     toff[dt] = 2 * (r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 2>(r)) + (d0 & 7));
+    toff8[dt] = 2 * ((r + 8) * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 2>(r + 8)) + (d0 & 7));
   }
   if (w > 0) {
     int kmin = q0 - w + 1;
@@ -1334,8 +1337,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
         for (int st = 0; st < 4; ++st)
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
-            const uint32_t a = kt + toff[dt] + 32 * st * D;
-            const bf16x4 a0 = ld_tr4_at(a), a1 = ld_tr4_at(a + 16 * D);
+            const bf16x4 a0 = ld_tr4_at(kt + toff[dt] + 32 * st * D), a1 = ld_tr4_at(kt + toff8[dt] + 32 * st * D);
             bf16x8 af;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1587,13 +1589,14 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
   floatx16 accK[D / 32], accV[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) accK[dt] = accV[dt] = zero16();
+  // (the kind-3 swizzle repeats every 8 rows: rows r + 8 are 16 D bytes on)
   uint32_t foff[D / 16], toff[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) foff[ks] = 2 * (c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 2>(c)));
+  for (int ks = 0; ks < D / 16; ++ks) foff[ks] = 2 * (c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 3>(c)));
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     const int r = 4 * hf + (jj >> 2), d0 = 32 * dt + 16 * (c >> 4) + 4 * (jj & 3);
-    toff[dt] = 2 * (r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 2>(r)) + (d0 & 7));
+    toff[dt] = 2 * (r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 3>(r)) + (d0 & 7));
   }
   int tmax = k0 + KT - 1 + w - 1;
   if (tmax > Tn - 1) tmax = Tn - 1;
@@ -1604,12 +1607,12 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
     const size_t ld = (size_t)H * D;
     const uint32_t ql = lds_addr(&qbuf[0][0]), ol = lds_addr(&obuf[0][0]);
     constexpr uint32_t TB = 64 * D * 2;
-    const uint32_t ldo = dma_lane_off<D, NT, 2>(tid, ld);
+    const uint32_t ldo = dma_lane_off<D, NT, 3>(tid, ld);
     auto stage = [&](int n, int buf) {
       const int hh = n / ntiles, q0 = qfirst + 64 * (n - hh * ntiles), h = hg * G + hh;
       const size_t base = ((size_t)b * Tn * H + h) * D;
-      dma_tile_async<D, NT, 2>(qr + base, ld, q0, Tn, ql + buf * TB, ldo, tid);
-      dma_tile_async<D, NT, 2>(dO + base, ld, q0, Tn, ol + buf * TB, ldo, tid);
+      dma_tile_async<D, NT, 3>(qr + base, ld, q0, Tn, ql + buf * TB, ldo, tid);
+      dma_tile_async<D, NT, 3>(dO + base, ld, q0, Tn, ol + buf * TB, ldo, tid);
       if (tid < 64) {
         const int t = q0 + tid;
         const size_t e = ((size_t)b * H + h) * Tn + t;

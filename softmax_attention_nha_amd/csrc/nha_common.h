@@ -409,15 +409,40 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-//   kind 2 (both of the above, for a 32-bank LDS): f(r) = 2 (r % 4) + (r / 4) % 2
-//                                 maps 8 consecutive rows to 8 distinct chunk
-//                                 positions and keeps the two chunks of each of
-//                                 4 aligned rows apart
+//   kind 2 (both of the above) on gfx950's 64 banks x 4 bytes, where a
+//                                 16-byte read serves 16 lanes (256 bytes) per
+//                                 pass and a ds_read_b64_tr_b16 32 lanes:
+//     D = 128 (a row fills the 64 banks): f(r) = 4 (r % 4) + (r / 4) % 4 is a
+//       permutation of the 16 chunk positions over 16 consecutive rows (row
+//       reads), and gives 4 aligned rows 4 different 4-chunk groups (the 4
+//       chunks each such row gives a transposed read);
+//     D = 64 (two rows per 64 banks): f(r) = 4 ((r / 2) % 2) + (r / 4) % 4 is
+//       distinct over the 8 even (and the 8 odd) rows of 16, and puts rows r
+//       and r + 2 of an aligned 4 (same bank half) in different 4-chunk groups;
+//     D = 32 (four rows per 64 banks): f(r) = (r / 4) % 4 is distinct over the
+//       4 rows of 16 that share a bank quarter; transposed reads of 4 aligned
+//       rows fall in 4 different quarters whatever the permutation.
+//   kind 3 (both, repeating every 8 rows, so that a transposed read can
+//                                 reach the second group of 8 rows with a
+//                                 constant offset): the transposed condition
+//                                 above holds, row reads are 2-way:
+//     D = 128: 4 (r % 4) + (r / 4) % 2;  D = 64: 4 ((r / 2) % 2) + 2 (r % 2) +
+//     (r / 4) % 2;  D = 32: (r / 4) % 2.
+//   (The kinds 0 and 1 satisfy the same conditions for one pattern each; kind
+//   2 repeats every 16 rows.)
 template <int D, int KIND>
 __device__ __forceinline__ int chunk_swz(int row) {
   if constexpr (KIND == 0) return row & (D / 8 - 1);
   else if constexpr (KIND == 1) return ((0xAC60 >> (4 * (row & 3))) & 15) & (D / 8 - 1);
-  else return (((row & 3) << 1) | ((row >> 2) & 1)) & (D / 8 - 1);
+  else if constexpr (KIND == 2) {
+    if constexpr (D >= 128) return (((row & 3) << 2) | ((row >> 2) & 3)) & (D / 8 - 1);
+    else if constexpr (D == 64) return ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) & (D / 8 - 1);
+    else return ((row >> 2) & 3) & (D / 8 - 1);
+  } else {
+    if constexpr (D >= 128) return (((row & 3) << 2) | ((row >> 2) & 1)) & (D / 8 - 1);
+    else if constexpr (D == 64) return ((((row >> 1) & 1) << 2) | ((row & 1) << 1) | ((row >> 2) & 1)) & (D / 8 - 1);
+    else return ((row >> 2) & 1) & (D / 8 - 1);
+  }
 }
 
 // Rows [j0, j0 + 64) of a bf16 operand with row stride ld (rows past Tn - 1
