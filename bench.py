@@ -569,7 +569,10 @@ def main():
                     events=[x.cuda_event for x in bev] if bev else None, after_fwd=True)
 
     for _ in range(args.warmup):
-        step()
+        if args.one_stream:  # warm up the same one-stream launch order that is timed
+            step(new_events(len(fstages) + 1), new_events(len(bstages) + 1) if do_bwd else None)
+        else:
+            step()
     torch.cuda.synchronize()
     K = args.steps
     # the timed region: K steps of the production calls (independent launches
