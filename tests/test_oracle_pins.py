@@ -387,3 +387,44 @@ def test_zero_initial_state_is_the_default():
         assert np.array_equal(x, y)
     for x, y in zip(oracle.bwd(q, k, v, a, dO, w), oracle.bwd(q, k, v, a, dO, w, s0=z)):
         assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------- no slots (m = 0)
+# The ablation with no long-term memory (the gist.science page's flexibility
+# section: the layer spans a pure window model at one end): m = 0 leaves
+# plain (sliding-window) causal softmax attention with RoPE, which torch's
+# scaled_dot_product_attention computes directly.
+@pytest.mark.parametrize("w", [1, 4, 13, 20])
+def test_no_slots_is_sliding_window_rope_attention(w):
+    B, T, H, Hkv, d = 1, 13, 4, 2, 8
+    q, k, v, a = rand_case(B, T, H, Hkv, d, 0, seed=91)
+    o, lse = oracle.fwd(q, k, v, a, w, rope_base=300.0)
+    qr, kr = rope_complex(t64(q), 300.0), rope_complex(t64(k), 300.0)
+    tt = torch.arange(T)
+    band = (tt[None, :] <= tt[:, None]) & (tt[None, :] >= tt[:, None] - w + 1)
+    for h in range(H):
+        g = h // (H // Hkv)
+        ref = F.scaled_dot_product_attention(qr[0, :, h][None], kr[0, :, g][None], t64(v)[0, :, g][None],
+                                             attn_mask=band[None])[0]
+        np.testing.assert_allclose(o[0, :, h], ref.numpy(), atol=1e-12)
+        lg = (qr[0, :, h] @ kr[0, :, g].T) / math.sqrt(d)
+        np.testing.assert_allclose(lse[0, h], torch.logsumexp(lg.masked_fill(~band, float("-inf")), -1).numpy(),
+                                   atol=1e-12)
+
+
+@pytest.mark.parametrize("w", [3, 13])
+def test_no_slots_gradients_match_autograd_of_attention(w):
+    B, T, H, Hkv, d = 1, 13, 2, 1, 8
+    q, k, v, a = rand_case(B, T, H, Hkv, d, 0, seed=92)
+    dO = np.random.default_rng(5).standard_normal(q.shape)
+    dq, dk, dv, da = oracle.bwd(q, k, v, a, dO, w, rope_base=300.0)
+    assert da.shape == (B, T, Hkv, 0)
+    tq, tk, tv = (t64(x).requires_grad_(True) for x in (q, k, v))
+    qr, kr = rope_complex(tq, 300.0), rope_complex(tk, 300.0)
+    tt = torch.arange(T)
+    band = (tt[None, :] <= tt[:, None]) & (tt[None, :] >= tt[:, None] - w + 1)
+    o = torch.stack([F.scaled_dot_product_attention(qr[0, :, h][None], kr[0, :, 0][None], tv[0, :, 0][None],
+                                                    attn_mask=band[None])[0] for h in range(H)], 1)[None]
+    (o * t64(dO)).sum().backward()
+    for got, ref in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(got, ref.grad.numpy(), atol=1e-11)
