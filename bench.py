@@ -59,7 +59,9 @@ def flops_window(B, H, T, d, w):
 
 def flops_slot(B, H, T, d, m, w, C):
     """Slot read (4 m d per query) plus the intra-chunk terms (4d + 4m per
-    (query, earlier absorbed row of the same chunk))."""
+    (query, earlier absorbed row of the same chunk)); none without slots."""
+    if m == 0:
+        return 0.0
     tot = 0.0
     for t in range(w, T):
         c = t - max(C * (t // C), w) + 1
@@ -370,6 +372,8 @@ SWEEP = [
     ("config", "headline", {}, 512, True, 0),
     # many sequences decoding together (B = 32 at 2K tokens of prefix each)
     ("decode_batched", "long", {"B": 32, "T": 2048}, 512, False, 64),
+    # ablation: no slots (m = 0, sliding-window attention alone) at the headline shape
+    ("ablation_no_slots", "headline", {"m": 0}, 512, True, 0),
 ]
 # The operator benchmark shape the pages describe (NHA with m = 32 slots and
 # w = 32 against a 64-slot gated-slot model and full attention, over the

@@ -17,7 +17,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Fill `s` from the descriptor; `need_T` = false for decode (T ignored).
 nha_status make_shape(const nha_desc* d, bool need_T, Shape* s) {
   if (!d) return NHA_ERR_INVALID_ARG;
-  if (d->B < 1 || d->H < 1 || d->Hkv < 1 || d->w < 0 || d->m < 1 || d->d < 1) return NHA_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->Hkv < 1 || d->w < 0 || d->m < 0 || d->d < 1) return NHA_ERR_INVALID_ARG;
+  if (d->m == 0 && d->w < 1) return NHA_ERR_INVALID_ARG;  // no slots and no window: no keys
   if (need_T && d->T < 1) return NHA_ERR_INVALID_ARG;
   if (d->H % d->Hkv) return NHA_ERR_INVALID_ARG;
   if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return NHA_ERR_INVALID_ARG;
@@ -148,7 +149,7 @@ nha_status nha_fwd_timed(const nha_desc* desc, const void* q, const void* k, con
   Shape s;
   nha_status rc = make_shape(desc, true, &s);
   if (rc != NHA_OK) return rc;
-  if (!q || !k || !v || !alpha || !o || !ws) return NHA_ERR_INVALID_ARG;
+  if (!q || !k || !v || (!alpha && s.m > 0) || !o || !ws) return NHA_ERR_INVALID_ARG;  // m = 0: no gates
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(o) || !aligned16(ws) ||
       (lse && !aligned16(lse)) || (state_out && !aligned16(state_out)))
     return NHA_ERR_INVALID_ARG;
@@ -191,8 +192,8 @@ static nha_status bwd_common(const nha_desc* desc, const void* q, const void* k,
   nha_status rc = make_shape(desc, true, &s);
   if (rc != NHA_OK) return rc;
   if (slot_bwd_lds_bytes(s) > kMaxLds) return NHA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !alpha || !o || !lse || !dO || !dq || !dk || !dv || !dalpha || !ws)
-    return NHA_ERR_INVALID_ARG;
+  if (!q || !k || !v || ((!alpha || !dalpha) && s.m > 0) || !o || !lse || !dO || !dq || !dk || !dv || !ws)
+    return NHA_ERR_INVALID_ARG;  // m = 0: no gates, no dalpha
   const void* ptrs[] = {q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ws};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
@@ -246,7 +247,7 @@ nha_status nha_decode_step(const nha_desc* desc, const void* q_t, const void* k_
   Shape s;
   nha_status rc = make_shape(desc, false, &s);
   if (rc != NHA_OK) return rc;
-  if (!q_t || !k_t || !v_t || !alpha_t || !state || !o_t) return NHA_ERR_INVALID_ARG;
+  if (!q_t || !k_t || !v_t || (!alpha_t && s.m > 0) || !state || !o_t) return NHA_ERR_INVALID_ARG;
   const void* ptrs[] = {q_t, k_t, v_t, alpha_t, state, o_t};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;

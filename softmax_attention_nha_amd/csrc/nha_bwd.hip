@@ -1216,14 +1216,16 @@ __global__ __launch_bounds__(256) void k_win_bwd_dq(const T* __restrict__ qr, co
         out[db][r] = x1 * cs + x2 * sn;
         out[db + HB][r] = x2 * cs - x1 * sn;
       }
-    const T* sl = dqs + (((size_t)b * Tn + tq) * H + h) * D;
+    const T* sl = dqs + (((size_t)b * Tn + tq) * H + h) * D;  // (null: no slots)
     T* dst = dq + (((size_t)b * Tn + tq) * H + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      const typename Vec<T>::v4 x4 = ld4<T>(sl + 16 * db + 4 * g);
-      floatx4 s4;
+      floatx4 s4 = zero4();
+      if (dqs) {
+        const typename Vec<T>::v4 x4 = ld4<T>(sl + 16 * db + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s4[r] = to_f<T>(x4[r]);
+        for (int r = 0; r < 4; ++r) s4[r] = to_f<T>(x4[r]);
+      }
       st4<T>(dst + 16 * db + 4 * g,
              pack4<T>(floatx4{out[db][0] + s4[0], out[db][1] + s4[1], out[db][2] + s4[2], out[db][3] + s4[3]}));
     }
@@ -1384,15 +1386,18 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
         }
       }
     }
-    const bf16* sl = dqs + qrow;
+    const bf16* sl = dqs + qrow;  // (null: no slots)
     bf16* dst = dq + qrow;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * dt + 8 * i + 4 * hf;
-        const bf16x4 x4 = ld4<bf16>(sl + d);
-        const floatx4 s4{(float)x4[0], (float)x4[1], (float)x4[2], (float)x4[3]};
+        floatx4 s4 = zero4();
+        if (dqs) {
+          const bf16x4 x4 = ld4<bf16>(sl + d);
+          s4 = floatx4{(float)x4[0], (float)x4[1], (float)x4[2], (float)x4[3]};
+        }
         st4<bf16>(dst + d, pack4<bf16>(floatx4{out[dt][4 * i] + s4[0], out[dt][4 * i + 1] + s4[1],
                                                 out[dt][4 * i + 2] + s4[2], out[dt][4 * i + 3] + s4[3]}));
       }
@@ -1531,7 +1536,8 @@ __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
         ok[db + HB][r] = x2 * cs - x1 * sn;
       }
     const size_t row = (((size_t)b * Tn + key) * Hkv + hg) * D;
-    const bool slot = key + w < Tn;  // this key row is also absorbed (at step key + w)
+    // this key row is also absorbed (at step key + w); dkap null: no slots
+    const bool slot = dkap != nullptr && key + w < Tn;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       floatx4 sk = zero4(), sv = zero4();
@@ -1720,7 +1726,8 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
         }
       }
     }
-    const bool slot = key + w < Tn;  // this key row is also absorbed (at step key + w)
+    // this key row is also absorbed (at step key + w); dkap null: no slots
+    const bool slot = dkap != nullptr && key + w < Tn;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -1786,6 +1793,33 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     T* dnu = (T*)(ws + L.dnu);
     float* csum = (float*)(ws + L.csum);
     const long nrows = (long)s.B * s.T * s.H;
+    if (s.m == 0) {
+      // no slots: D_t, then the window dq and dk/dv with no slot parts
+      mk.mark(st);
+      hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
+                         (const T*)p.o, dO, Dt, s.T, s.H, nrows);
+      mk.mark(st);
+      if constexpr (sizeof(T) == 2) {
+        constexpr int NWV = 4;
+        const unsigned nt = (unsigned)((s.T + 32 * NWV - 1) / (32 * NWV));
+        hipLaunchKernelGGL((k_win_bwd_dq_b16<D, NWV>), dim3(nt, s.B * s.H), dim3(NWV * 64), 0, st, qr, kr, v, dO,
+                           p.lse, Dt, (const T*)nullptr, (const float2*)pp.rcs, (T*)p.dq, s.T, s.H, s.Hkv, s.w,
+                           s.scale);
+        mk.mark(st);
+        hipLaunchKernelGGL((k_win_bwd_dkdv_b16<D, NWV>), dim3(nt, units), dim3(NWV * 64), 0, st, qr, kr, v, dO,
+                           p.lse, Dt, (const T*)nullptr, (const T*)nullptr, (const float2*)pp.rcs, (T*)p.dk,
+                           (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale);
+      } else {
+        hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt,
+                           (const T*)nullptr, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+        mk.mark(st);
+        hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt,
+                           (const T*)nullptr, (const T*)nullptr, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale,
+                           th, s.rope ? 1 : 0);
+      }
+      mk.mark(st);
+      return hipGetLastError();
+    }
     if constexpr (sizeof(T) == 2) {
       // bf16: pass A also computes D_t
       mk.mark(st);
@@ -1880,12 +1914,21 @@ int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max) {
   const char* all[16];
   int n = 0;
   if (!after_fwd) {
-    all[n++] = "chunk_gates";
-    all[n++] = "state_scan";
+    if (s.m > 0) {
+      all[n++] = "chunk_gates";
+      all[n++] = "state_scan";
+    }
     if (s.rope && s.win) {
       all[n++] = "rope_cs";
       all[n++] = "rope";
     }
+  }
+  if (s.m == 0) {  // no slots
+    all[n++] = "bwd_prep";
+    all[n++] = "win_bwd_dq";
+    all[n++] = "win_bwd_dkdv";
+    for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];
+    return n;
   }
   if (s.dtype != NHA_DTYPE_BF16) all[n++] = "bwd_prep";  // bf16: inside slot pass A
   all[n++] = "slot_bwd_a";

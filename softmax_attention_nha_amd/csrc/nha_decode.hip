@@ -104,10 +104,16 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
   float xk[KPG][8], xv[KPG][8], ga[KPG];
 #pragma unroll
   for (int kk = 0; kk < KPG; ++kk) {
-    const int e = min(s + NS * (grp + NG * kk), m - 1);
-    ld8f_f32(sk + (size_t)e * D, xk[kk]);
-    ld8f_f32(sv + (size_t)e * D, xv[kk]);
-    ga[kk] = to_f<T>(alpha[((size_t)b * Hkv + hg) * m + e]);
+    if (m > 0) {
+      const int e = min(s + NS * (grp + NG * kk), m - 1);
+      ld8f_f32(sk + (size_t)e * D, xk[kk]);
+      ld8f_f32(sv + (size_t)e * D, xv[kk]);
+      ga[kk] = to_f<T>(alpha[((size_t)b * Hkv + hg) * m + e]);
+    } else {  // no slots
+#pragma unroll
+      for (int r = 0; r < 8; ++r) xk[kk][r] = xv[kk][r] = 0.f;
+      ga[kk] = 1.f;
+    }
   }
   const long long t = pos[unit];
   const long long nwin = (w == 0) ? 0 : (t + 1 < w ? t + 1 : w);

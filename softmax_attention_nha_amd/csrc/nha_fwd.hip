@@ -666,6 +666,9 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
 // masks only the tiles that cross the band's edges.  Writes o and lse.
 constexpr int kWinWaves = 4;
 constexpr float kLazy = 8.f;
+// running maximum (log2 units) of an empty softmax: finite, so that
+// 2^(score - max) of a masked score is 0, and below every real logit
+constexpr float kEmptyMax = -1e30f;
 
 template <typename T, int D>
 struct WinFwdSmem {
@@ -697,19 +700,23 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ q
   typename Vec<T>::v8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8_sel<T>(qr + qrow + 16 * ks + 8 * hf, qvalid);
-  // seed with the slot partial
-  const float lse_l = lseL[(size_t)bh * Tn + tqc];  // unconditional load (clamped row)
-  float mu = qvalid ? lse_l * NHA_LOG2E : 0.f;
-  float zl = (hf == 0) ? 1.f : 0.f;  // lane-partial normaliser
-  floatx16 acc[D / 32];              // O^T: rows d = 32 dt + 8 i + 4 hf + rr, column = query
+  // seed with the slot partial (no slots, oL null: an empty softmax, whose
+  // running maximum is a finite floor that the query's own key raises)
+  const bool seeded = oL != nullptr;
+  const float lse_l = seeded ? lseL[(size_t)bh * Tn + tqc] : 0.f;  // unconditional load (clamped row)
+  float mu = qvalid ? (seeded ? lse_l * NHA_LOG2E : kEmptyMax) : 0.f;
+  float zl = (hf == 0 && seeded) ? 1.f : 0.f;  // lane-partial normaliser
+  floatx16 acc[D / 32];                        // O^T: rows d = 32 dt + 8 i + 4 hf + rr, column = query
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     acc[dt] = zero16();
+    if (seeded) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      typename Vec<T>::v4 x = ld4<T>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
+      for (int i = 0; i < 4; ++i) {
+        typename Vec<T>::v4 x = ld4<T>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? to_f<T>(x[rr]) : 0.f;
+        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? to_f<T>(x[rr]) : 0.f;
+      }
     }
   }
   const float sl2 = scale * NHA_LOG2E;
@@ -868,18 +875,22 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8_sel<bf16>(qr + qrow + 16 * ks + 8 * hf, qvalid);
-  const float lse_l = lseL[(size_t)bh * Tn + tqc];  // unconditional load (clamped row)
-  float mu = qvalid ? lse_l * NHA_LOG2E : 0.f;
-  float zl = (hf == 0) ? 1.f : 0.f;
+  // seed with the slot partial, or (no slots) an empty softmax
+  const bool seeded = oL != nullptr;
+  const float lse_l = seeded ? lseL[(size_t)bh * Tn + tqc] : 0.f;  // unconditional load (clamped row)
+  float mu = qvalid ? (seeded ? lse_l * NHA_LOG2E : kEmptyMax) : 0.f;
+  float zl = (hf == 0 && seeded) ? 1.f : 0.f;
   floatx16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     acc[dt] = zero16();
+    if (seeded) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x4 x = ld4<bf16>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 x = ld4<bf16>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? (float)x[rr] : 0.f;
+        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? (float)x[rr] : 0.f;
+      }
     }
   }
   // per-lane LDS element offsets of the K fragments (row c, logical chunk
@@ -1099,19 +1110,23 @@ template <typename T, int D, int MP, int C>
 static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const T* k, const T* v, const T* alpha,
                           const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk) {
   const int units = s.B * s.Hkv;
-  mk.mark(st);
-  hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend, s.T,
-                     s.Hkv, s.m, s.w, s.NC);
+  if (s.m > 0) {  // (no slots: no gates and no states)
+    mk.mark(st);
+    hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend,
+                       s.T, s.Hkv, s.m, s.w, s.NC);
+  }
   if (s.rope && s.win) fk.record(st);
-  mk.mark(st);
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
-                       s.w, s.NC);
-  else
-    hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
-                       s.w, s.NC);
+  if (s.m > 0) {
+    mk.mark(st);
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
+                         (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
+                         s.w, s.NC);
+    else
+      hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
+                         (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
+                         s.w, s.NC);
+  }
   if (s.rope && s.win) {
     // RoPE (HBM-bound, no LDS) on the side stream beside the state scan (bound
     // by its chain of dependent steps; the gate products, HBM-bound too, run
@@ -1161,15 +1176,20 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st, side_fork(p.events == nullptr));
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
-    mk.mark(st);
-    if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((k_slot_fwd_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
-                         (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
+    if (s.m > 0) {
+      mk.mark(st);
+      if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((k_slot_fwd_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v,
+                           alpha, (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
+      } else {
+        const int nitems = s.NC * s.B * s.H;
+        const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
+        hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
+                           (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, nitems, s.scale);
+      }
     } else {
-      const int nitems = s.NC * s.B * s.H;
-      const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
-      hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
-                         (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, nitems, s.scale);
+      ol = nullptr;  // the window kernel starts from an empty softmax
+      lsel = nullptr;
     }
     mk.mark(st);
     if constexpr (sizeof(T) == 2) {
@@ -1263,13 +1283,15 @@ hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hip
 int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
   const char* all[8];
   int n = 0;
-  all[n++] = "chunk_gates";
-  all[n++] = "state_scan";
+  if (s.m > 0) {
+    all[n++] = "chunk_gates";
+    all[n++] = "state_scan";
+  }
   if (s.rope && s.win) {
     all[n++] = "rope_cs";
     all[n++] = "rope";
   }
-  all[n++] = "slot_fwd";
+  if (s.m > 0) all[n++] = "slot_fwd";
   all[n++] = "win_fwd";
   if (with_state) all[n++] = "export_state";
   for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];

@@ -46,7 +46,9 @@ def status(d):
     ({"B": 0}, nha.NHA_ERR_INVALID_ARG),
     ({"T": 0}, nha.NHA_ERR_INVALID_ARG),
     ({"w": -1}, nha.NHA_ERR_INVALID_ARG),
-    ({"m": 0}, nha.NHA_ERR_INVALID_ARG),
+    ({"m": 0, "w": 0}, nha.NHA_ERR_INVALID_ARG),  # no slots and no window: no keys
+    ({"m": 0, "w": 8}, nha.NHA_OK),                # no slots: sliding-window attention
+    ({"m": -1}, nha.NHA_ERR_INVALID_ARG),
     ({"rope_base": -1.0}, nha.NHA_ERR_INVALID_ARG),
     ({"scale": -0.5}, nha.NHA_ERR_INVALID_ARG),
     ({"d": 96}, nha.NHA_ERR_UNSUPPORTED),
