@@ -51,9 +51,9 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.POINTER(ctypes.c_double)
         i, dbl = ctypes.c_int, ctypes.c_double
-        lib.nha_oracle_fwd.argtypes = [i] * 7 + [dbl, dbl] + [P] * 10 + [i]
+        lib.nha_oracle_fwd.argtypes = [i] * 8 + [dbl, dbl] + [P] * 10 + [i]
         lib.nha_oracle_fwd.restype = i
-        lib.nha_oracle_bwd.argtypes = [i] * 7 + [dbl, dbl] + [P] * 13 + [i]
+        lib.nha_oracle_bwd.argtypes = [i] * 8 + [dbl, dbl] + [P] * 13 + [i]
         lib.nha_oracle_bwd.restype = i
         _lib = lib
     return _lib
@@ -85,8 +85,11 @@ def _s0(s0, B, Hkv, m, d):
     return s0k, s0v
 
 
-def fwd(q, k, v, alpha, w, rope_base=10000.0, scale=0.0, threads=0, want_state=False, s0=None):
+def fwd(q, k, v, alpha, w, rope_base=10000.0, scale=0.0, threads=0, want_state=False, s0=None, token_shift=True):
     """Forward. Arrays in the operator's layouts (see nha_oracle.c).
+
+    token_shift=False: the ablation in which every token enters the slots at
+    its own step (absorption shift 0 instead of w).
 
     s0: optional initial slot states (S0K, S0V), each [B,Hkv,m,d] (zero when
     None).  Returns (o [B,T,H,d], lse [B,H,T]) and, with want_state, also the
@@ -98,7 +101,7 @@ def fwd(q, k, v, alpha, w, rope_base=10000.0, scale=0.0, threads=0, want_state=F
     lse = np.zeros((B, H, T))
     sk = np.zeros((B, Hkv, m, d)) if want_state else None
     sv = np.zeros((B, Hkv, m, d)) if want_state else None
-    rc = _load().nha_oracle_fwd(B, T, H, Hkv, d, m, int(w), float(rope_base), float(scale),
+    rc = _load().nha_oracle_fwd(B, T, H, Hkv, d, m, int(w), -1 if token_shift else 0, float(rope_base), float(scale),
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s0k), _ptr(s0v), _ptr(o),
                                 _ptr(lse), _ptr(sk), _ptr(sv), int(threads))
     if rc:
@@ -108,7 +111,8 @@ def fwd(q, k, v, alpha, w, rope_base=10000.0, scale=0.0, threads=0, want_state=F
     return o, lse
 
 
-def bwd(q, k, v, alpha, dO, w, rope_base=10000.0, scale=0.0, threads=0, s0=None, want_ds0=False):
+def bwd(q, k, v, alpha, dO, w, rope_base=10000.0, scale=0.0, threads=0, s0=None, want_ds0=False,
+        token_shift=True):
     """Backward. Returns (dq, dk, dv, dalpha) in the input layouts, and with
     want_ds0 also the gradients (dS0K, dS0V) of the initial slot states."""
     q, k, v, alpha, dO = _f64(q), _f64(k), _f64(v), _f64(alpha), _f64(dO)
@@ -120,7 +124,7 @@ def bwd(q, k, v, alpha, dO, w, rope_base=10000.0, scale=0.0, threads=0, s0=None,
     da = np.zeros_like(alpha)
     ds0k = np.zeros((B, Hkv, m, d)) if want_ds0 else None
     ds0v = np.zeros((B, Hkv, m, d)) if want_ds0 else None
-    rc = _load().nha_oracle_bwd(B, T, H, Hkv, d, m, int(w), float(rope_base), float(scale),
+    rc = _load().nha_oracle_bwd(B, T, H, Hkv, d, m, int(w), -1 if token_shift else 0, float(rope_base), float(scale),
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s0k), _ptr(s0v), _ptr(dO),
                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(ds0k), _ptr(ds0v), int(threads))
     if rc:

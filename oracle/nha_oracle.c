@@ -20,7 +20,10 @@
  *      design-motivation paragraph of that same section.  Reading adopted for
  *      the gate index: the printed recurrence keeps its time index t and only
  *      the token entering changes to k_{t-w} (so w = 0 is the printed
- *      recurrence exactly).  Slots start at the given initial states S0
+ *      recurrence exactly).  The token-shift ablation of the ai.info page's
+ *      findings (every token absorbed at its own step while the window still
+ *      holds it) is the shift sh = 0 in place of w: absorb k_{t-sh} for
+ *      t >= sh (sh < 0 selects sh = w, the method itself).  Slots start at the given initial states S0
  *      (s0k, s0v; zero when NULL): the ai.info page ("Future Directions",
  *      item 1) names learnable initial slot states as the next step, and the
  *      operator takes them as inputs and returns their gradients.  As for
@@ -43,10 +46,10 @@
  * chain rule (not from the chunkwise form):
  *   dl = p (dp - D_t),  D_t = <dO_t, o_t>
  *   dS^K_t[i] += s dl^L_i q_t,  dS^V_t[i] += p^L_i dO_t      (direct sources)
- *   Lam_t = dS_t + a_{t+1} Lam_{t+1}, a_u = alpha_u if u >= w else 1
- *   for t >= w: dk_{t-w} += sum_i (1-alpha_t[i]) LamK_t[i]   (same for v)
- *               dalpha_t[i] = <LamK_t[i], SK_{t-1}[i] - k_{t-w}>
- *                           + <LamV_t[i], SV_{t-1}[i] - v_{t-w}>
+ *   Lam_t = dS_t + a_{t+1} Lam_{t+1}, a_u = alpha_u if u >= sh else 1
+ *   for t >= sh: dk_{t-sh} += sum_i (1-alpha_t[i]) LamK_t[i]   (same for v)
+ *               dalpha_t[i] = <LamK_t[i], SK_{t-1}[i] - k_{t-sh}>
+ *                           + <LamV_t[i], SV_{t-1}[i] - v_{t-sh}>
  *   window: dq_t += R_t^T s sum_j dl^W_j R_j k_j,
  *           dk_j += R_j^T s dl^W_j R_t q_t, dv_j += p^W_j dO_t.
  *   initial states: dS0 = a_0 Lam_0 (the adjoint carried to before t = 0).
@@ -76,6 +79,7 @@
 typedef struct {
   int B, T, H, Hkv, d, m, w;
   double base, scale;
+  int sh; /* absorption shift: token t - sh enters the slots at step t >= sh */
 } dims_t;
 
 static int check_dims(const dims_t* D) {
@@ -207,12 +211,12 @@ static void rotate_keys(const dims_t* D, const double* cs, const double* sn,
     rope_apply(D, cs, sn, t, k + KIDX(b, t, g), kr + (size_t)t * D->d);
 }
 
-int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w,
+int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
                    double rope_base, double scale, const double* q,
                    const double* k, const double* v, const double* alpha,
                    const double* s0k, const double* s0v, double* o,
                    double* lse, double* sk_out, double* sv_out, int nthreads) {
-  dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale};
+  dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale, shift < 0 ? w : shift};
   const dims_t* D = &Dm;
   if (check_dims(D)) return 1;
   if (Dm.scale == 0.0) Dm.scale = 1.0 / sqrt((double)d);
@@ -236,9 +240,9 @@ int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w,
     const double* vg = v + KIDX(b, 0, g);
     size_t vstride = (size_t)Hkv * d;
     for (int t = 0; t < T; ++t) {
-      if (t >= w) {
-        absorb(m, d, alpha + AIDX(b, t, g), k + KIDX(b, t - w, g), SK);
-        absorb(m, d, alpha + AIDX(b, t, g), v + KIDX(b, t - w, g), SV);
+      if (t >= Dm.sh) {
+        absorb(m, d, alpha + AIDX(b, t, g), k + KIDX(b, t - Dm.sh, g), SK);
+        absorb(m, d, alpha + AIDX(b, t, g), v + KIDX(b, t - Dm.sh, g), SV);
       }
       for (int hh = 0; hh < G; ++hh) {
         int h = g * G + hh, nw;
@@ -260,13 +264,13 @@ int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w,
   return 0;
 }
 
-int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w,
+int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
                    double rope_base, double scale, const double* q,
                    const double* k, const double* v, const double* alpha,
                    const double* s0k, const double* s0v, const double* dO,
                    double* dq, double* dk, double* dv, double* dalpha,
                    double* ds0k, double* ds0v, int nthreads) {
-  dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale};
+  dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale, shift < 0 ? w : shift};
   const dims_t* D = &Dm;
   if (check_dims(D)) return 1;
   if (Dm.scale == 0.0) Dm.scale = 1.0 / sqrt((double)d);
@@ -314,9 +318,9 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w,
           memcpy(ckK + (size_t)(t / SEG) * md, SK, sizeof(double) * md);
           memcpy(ckV + (size_t)(t / SEG) * md, SV, sizeof(double) * md);
         }
-        if (t >= w) {
-          absorb(m, d, alpha + AIDX(b, t, g), k + KIDX(b, t - w, g), SK);
-          absorb(m, d, alpha + AIDX(b, t, g), v + KIDX(b, t - w, g), SV);
+        if (t >= Dm.sh) {
+          absorb(m, d, alpha + AIDX(b, t, g), k + KIDX(b, t - Dm.sh, g), SK);
+          absorb(m, d, alpha + AIDX(b, t, g), v + KIDX(b, t - Dm.sh, g), SV);
         }
       }
       free(SK);
@@ -337,9 +341,9 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w,
         double* nV = stV + (size_t)(t - t0 + 1) * md;
         memcpy(nK, nK - md, sizeof(double) * md);
         memcpy(nV, nV - md, sizeof(double) * md);
-        if (t >= w) {
-          absorb(m, d, alpha + AIDX(b, t, g), k + KIDX(b, t - w, g), nK);
-          absorb(m, d, alpha + AIDX(b, t, g), v + KIDX(b, t - w, g), nV);
+        if (t >= Dm.sh) {
+          absorb(m, d, alpha + AIDX(b, t, g), k + KIDX(b, t - Dm.sh, g), nK);
+          absorb(m, d, alpha + AIDX(b, t, g), v + KIDX(b, t - Dm.sh, g), nV);
         }
       }
       for (int t = t1 - 1; t >= t0; --t) {
@@ -395,12 +399,12 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w,
           }
         }
         /* LK/LV now hold Lam_t. */
-        if (t >= w) {
+        if (t >= Dm.sh) {
           const double* a = alpha + AIDX(b, t, g);
-          const double* kap = k + KIDX(b, t - w, g);
-          const double* nu = v + KIDX(b, t - w, g);
-          double* dkk = dk + KIDX(b, t - w, g);
-          double* dvv = dv + KIDX(b, t - w, g);
+          const double* kap = k + KIDX(b, t - Dm.sh, g);
+          const double* nu = v + KIDX(b, t - Dm.sh, g);
+          double* dkk = dk + KIDX(b, t - Dm.sh, g);
+          double* dvv = dv + KIDX(b, t - Dm.sh, g);
           double* da = dalpha + AIDX(b, t, g);
           for (int i = 0; i < m; ++i) {
             const double* lk = LK + (size_t)i * d;

@@ -56,15 +56,18 @@ def slot_states(x, alpha, w, s0=None):
     return S
 
 
-def nha_brute(q, k, v, alpha, w, base=10000.0, scale=0.0, s0=None):
+def nha_brute(q, k, v, alpha, w, base=10000.0, scale=0.0, s0=None, shift=None):
     """Returns (o [B,T,H,d], lse [B,H,T]); all inputs fp64 torch tensors.
-    s0: optional initial slot states (S0K, S0V), each [B,Hkv,m,d]."""
+    s0: optional initial slot states (S0K, S0V), each [B,Hkv,m,d].
+    shift: the absorption shift of the slots (None: w, the method; 0: every
+    token enters the slots at its own step)."""
     B, T, H, d = q.shape
     Hkv, m = k.shape[2], alpha.shape[-1]
     G = H // Hkv
     s = scale if scale else 1.0 / math.sqrt(d)
-    SK = slot_states(k, alpha, w, None if s0 is None else s0[0])  # [B,T,Hkv,m,d]
-    SV = slot_states(v, alpha, w, None if s0 is None else s0[1])
+    sh = w if shift is None else shift
+    SK = slot_states(k, alpha, sh, None if s0 is None else s0[0])  # [B,T,Hkv,m,d]
+    SV = slot_states(v, alpha, sh, None if s0 is None else s0[1])
     qr = rope_complex(q, base)
     kr = rope_complex(k, base)
     rep = lambda x: x.repeat_interleave(G, dim=2)  # KV head -> query heads

@@ -428,3 +428,43 @@ def test_no_slots_gradients_match_autograd_of_attention(w):
     (o * t64(dO)).sum().backward()
     for got, ref in ((dq, tq), (dk, tk), (dv, tv)):
         np.testing.assert_allclose(got, ref.grad.numpy(), atol=1e-11)
+
+
+# ---------------------------------------------------------------- no token shift
+# The token-shift ablation (ai.info page, findings: both memories and the
+# token shift are needed): every token enters the slots at its own step,
+# absorption shift 0, while the window still holds it.
+@pytest.mark.parametrize("w", [0, 3, 12])
+def test_no_token_shift_matches_closed_form(w):
+    B, T, H, Hkv, d, m = 2, 11, 4, 2, 8, 5
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=110 + w)
+    o, lse = oracle.fwd(q, k, v, a, w, rope_base=100.0, token_shift=False)
+    o_ref, l_ref = nha_brute(t64(q), t64(k), t64(v), t64(a), w, 100.0, shift=0)
+    np.testing.assert_allclose(o, o_ref.numpy(), atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref.numpy(), atol=1e-12)
+    if w == 0:  # with no window the shift is 0 either way
+        o2, _ = oracle.fwd(q, k, v, a, w, rope_base=100.0)
+        assert np.array_equal(o, o2)
+
+
+def test_no_token_shift_zero_gates_hold_the_current_token():
+    # alpha = 0: every slot equals the raw current key / value
+    B, T, H, Hkv, d, m, w = 1, 9, 1, 1, 4, 3, 4
+    q, k, v, _ = rand_case(B, T, H, Hkv, d, m, seed=120)
+    a = np.zeros((B, T, Hkv, m))
+    _, _, sk, sv = oracle.fwd(q, k, v, a, w, rope_base=0.0, want_state=True, token_shift=False)
+    np.testing.assert_array_equal(sk[0, 0], np.repeat(k[0, -1, 0][None], m, 0))
+    np.testing.assert_array_equal(sv[0, 0], np.repeat(v[0, -1, 0][None], m, 0))
+
+
+@pytest.mark.parametrize("w", [0, 3, 12])
+def test_no_token_shift_gradients_match_autograd(w):
+    B, T, H, Hkv, d, m = 1, 12, 2, 1, 4, 3
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=130 + w)
+    dO = np.random.default_rng(95).standard_normal(q.shape)
+    dq, dk, dv, da = oracle.bwd(q, k, v, a, dO, w, rope_base=100.0, token_shift=False)
+    tq, tk, tv, ta = (t64(x).requires_grad_(True) for x in (q, k, v, a))
+    o, _ = nha_brute(tq, tk, tv, ta, w, 100.0, shift=0)
+    (o * t64(dO)).sum().backward()
+    for got, ref in ((dq, tq), (dk, tk), (dv, tv), (da, ta)):
+        np.testing.assert_allclose(got, ref.grad.numpy(), atol=1e-11)
