@@ -74,9 +74,11 @@ def flops_state(B, Hkv, T, d, m, w):
     return 4.0 * m * d * B * Hkv * max(0, T - w)
 
 
-def flops_fwd(wl, w):
-    return (flops_window(wl.B, wl.H, wl.T, wl.d, w) + flops_slot(wl.B, wl.H, wl.T, wl.d, wl.m, w, wl.C)
-            + flops_state(wl.B, wl.Hkv, wl.T, wl.d, wl.m, w))
+def flops_fwd(wl, w, sh=None):
+    """sh: the slots' absorption shift (None: w; 0 without token shift)."""
+    sh = w if sh is None else sh
+    return (flops_window(wl.B, wl.H, wl.T, wl.d, w) + flops_slot(wl.B, wl.H, wl.T, wl.d, wl.m, sh, wl.C)
+            + flops_state(wl.B, wl.Hkv, wl.T, wl.d, wl.m, sh))
 
 
 def bytes_fwd(wl, e):
@@ -374,6 +376,8 @@ SWEEP = [
     ("decode_batched", "long", {"B": 32, "T": 2048}, 512, False, 64),
     # ablation: no slots (m = 0, sliding-window attention alone) at the headline shape
     ("ablation_no_slots", "headline", {"m": 0}, 512, True, 0),
+    # ablation: no token shift (every token enters the slots at its own step)
+    ("ablation_no_token_shift", "headline", {}, 512, True, 0),
 ]
 # The operator benchmark shape the pages describe (NHA with m = 32 slots and
 # w = 32 against a 64-slot gated-slot model and full attention, over the
@@ -394,7 +398,8 @@ def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
     q, k, v, a, dO = make_inputs(wl, T_total=wl.T + ndec, with_grad=True)
     T = wl.T
     qd, kd, vd, ad, dOd = (x[:, :T].contiguous().to(dev) for x in (q, k, v, a, dO))
-    desc = nha.make_desc(wl.B, T, wl.H, wl.Hkv, wl.d, wl.m, w, wl.C, wl.rope_base, 0.0, wl.dtype)
+    shift = label != "ablation_no_token_shift"
+    desc = nha.make_desc(wl.B, T, wl.H, wl.Hkv, wl.d, wl.m, w, wl.C, wl.rope_base, 0.0, wl.dtype, shift)
     ws = torch.empty(max(nha.workspace_size(desc), nha.workspace_size(desc, backward=with_bwd)), dtype=torch.uint8,
                      device=dev)
     o = torch.empty_like(qd)
@@ -405,11 +410,11 @@ def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
 
     def fwd():
         nha.fwd(qd, kd, vd, ad, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=o, lse_out=lse,
-                state_out=state)
+                state_out=state, token_shift=shift)
 
     def bwd():
         nha.bwd(qd, kd, vd, ad, o, lse, dOd, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=grads,
-                after_fwd=True)
+                after_fwd=True, token_shift=shift)
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     for _ in range(warmup):
@@ -427,7 +432,7 @@ def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
     torch.cuda.synchronize()
     fwd_ms = sorted(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps))[steps // 2]
     bwd_ms = sorted(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps))[steps // 2]
-    F = flops_fwd(wl, w)
+    F = flops_fwd(wl, w, None if shift else 0)
     peak = PEAK_TFLOPS[wl.dtype]
     line = {
         "sweep": label,

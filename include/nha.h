@@ -78,13 +78,19 @@ typedef struct {
   int32_t H;         /* query heads, >= 1 */
   int32_t Hkv;       /* KV heads, >= 1, H % Hkv == 0 */
   int32_t d;         /* head dim: 32, 64 or 128 */
-  int32_t m;         /* long-term slots: 1 .. 64 */
+  int32_t m;         /* long-term slots: 0 .. 64 (0: no slots, sliding-window
+                        attention alone; then w >= 1 and alpha, dalpha may be
+                        NULL) */
   int32_t w;         /* sliding window, >= 0; w >= T allowed (full attention) */
   int32_t C;         /* chunk length of the chunkwise form: 16, 32 or 64.
                         Results do not depend on C beyond rounding. */
   float rope_base;   /* > 0: RoPE base; 0: RoPE disabled */
   float scale;       /* softmax scale; 0 means 1/sqrt(d) */
   int32_t dtype;     /* nha_dtype of the tensor arguments */
+  int32_t no_token_shift; /* 0: the method -- a token enters the slots when it
+                        leaves the window (at step t + w); 1: the token-shift
+                        ablation -- every token enters the slots at its own
+                        step t while the window still holds it */
 } nha_desc;
 
 /* Workspace bytes that nha_fwd / nha_bwd need for this descriptor; 0 when the

@@ -55,6 +55,7 @@ class NhaDesc(ctypes.Structure):
         ("rope_base", ctypes.c_float),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("no_token_shift", ctypes.c_int32),
     ]
 
 
@@ -122,9 +123,11 @@ def _lib_status(s):
         return "status %d" % s
 
 
-def make_desc(B, T, H, Hkv, d, m, w, C=64, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16):
+def make_desc(B, T, H, Hkv, d, m, w, C=64, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16, token_shift=True):
+    """token_shift=False: the ablation in which every token enters the slots
+    at its own step (instead of when it leaves the window)."""
     return NhaDesc(int(B), int(T), int(H), int(Hkv), int(d), int(m), int(w), int(C), float(rope_base),
-                   float(scale), _DTYPES[dtype])
+                   float(scale), _DTYPES[dtype], 0 if token_shift else 1)
 
 
 def stage_names(desc, backward=False, with_state=False):
@@ -166,14 +169,14 @@ def _check(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
-def _desc_from(q, k, alpha, w, C, rope_base, scale):
+def _desc_from(q, k, alpha, w, C, rope_base, scale, token_shift=True):
     if q.dim() != 4 or k.dim() != 4 or alpha.dim() != 4:
         raise ValueError("q, k, alpha must be 4-D: [B,T,H,d], [B,T,Hkv,d], [B,T,Hkv,m]")
     B, T, H, d = q.shape
     Hkv, m = k.shape[2], alpha.shape[3]
     if q.dtype not in _DTYPES:
         raise ValueError("dtype must be float32 or bfloat16")
-    return make_desc(B, T, H, Hkv, d, m, w, C, rope_base, scale, q.dtype)
+    return make_desc(B, T, H, Hkv, d, m, w, C, rope_base, scale, q.dtype, token_shift)
 
 
 def workspace_size(desc, backward=False):
@@ -200,13 +203,14 @@ def _check_s0(s0, B, Hkv, m, d, dev):
 
 
 def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, workspace=None, out=None,
-        lse_out=None, events=None, s0=None):
+        lse_out=None, events=None, s0=None, token_shift=True):
     """Chunkwise-parallel forward. Returns (o [B,T,H,d], lse [B,H,T] float32).
 
     state_out: optional uint8 decode state tensor (decode_state()) that receives
     the state after the last token.  s0: optional initial slot states
-    (S0K, S0V), float32 [B,Hkv,m,d] each (nha_fwd_s0; no timing events)."""
-    desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
+    (S0K, S0V), float32 [B,Hkv,m,d] each (nha_fwd_s0; no timing events).
+    token_shift=False: the ablation without token shift."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale, token_shift)
     dev, dt = q.device, q.dtype
     B, T, H, d = q.shape
     Hkv, m = k.shape[2], alpha.shape[3]
@@ -235,15 +239,16 @@ def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, w
 
 
 def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, workspace=None, out=None,
-        events=None, after_fwd=False, s0=None):
+        events=None, after_fwd=False, s0=None, token_shift=True):
     """Gradients of fwd. Returns (dq, dk, dv, dalpha); dalpha is float32.
 
     after_fwd=True calls nha_bwd_after_fwd: `workspace` must then be the one
     the forward of these inputs ran with, untouched since (the forward's RoPE'd
     q/k, gate products and chunk-start states are read from it).  s0: the
     forward's initial slot states (S0K, S0V) (nha_bwd_s0); the result then ends
-    with their gradients: (dq, dk, dv, dalpha, dS0K, dS0V)."""
-    desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
+    with their gradients: (dq, dk, dv, dalpha, dS0K, dS0V).  token_shift as
+    for fwd."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale, token_shift)
     dev, dt = q.device, q.dtype
     B, T, H, d = q.shape
     Hkv, m = k.shape[2], alpha.shape[3]
@@ -290,7 +295,7 @@ def decode_state(B, H, Hkv, d, m, w, rope_base=10000.0, scale=0.0, dtype=torch.b
     return torch.zeros(decode_state_size(desc), dtype=torch.uint8, device=device)
 
 
-def decode_step(q_t, k_t, v_t, alpha_t, state, w, rope_base=10000.0, scale=0.0, out=None):
+def decode_step(q_t, k_t, v_t, alpha_t, state, w, rope_base=10000.0, scale=0.0, out=None, token_shift=True):
     """One recurrent step. q_t [B,H,d], k_t/v_t [B,Hkv,d], alpha_t [B,Hkv,m]. Returns o_t [B,H,d]."""
     B, H, d = q_t.shape
     Hkv, m = k_t.shape[1], alpha_t.shape[2]
@@ -298,7 +303,7 @@ def decode_step(q_t, k_t, v_t, alpha_t, state, w, rope_base=10000.0, scale=0.0, 
     _check(k_t, "k_t", (B, Hkv, d), dt, dev)
     _check(v_t, "v_t", (B, Hkv, d), dt, dev)
     _check(alpha_t, "alpha_t", (B, Hkv, m), dt, dev)
-    desc = make_desc(B, 1, H, Hkv, d, m, w, 64, rope_base, scale, dt)
+    desc = make_desc(B, 1, H, Hkv, d, m, w, 64, rope_base, scale, dt, token_shift)
     if state.numel() < decode_state_size(desc):
         raise ValueError("decode state too small")
     o = torch.empty_like(q_t) if out is None else out

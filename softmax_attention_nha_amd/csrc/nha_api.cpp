@@ -24,6 +24,7 @@ nha_status make_shape(const nha_desc* d, bool need_T, Shape* s) {
   if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return NHA_ERR_INVALID_ARG;
   if (!(d->scale >= 0.f) || !isfinite(d->scale)) return NHA_ERR_INVALID_ARG;
   if (d->dtype != NHA_DTYPE_F32 && d->dtype != NHA_DTYPE_BF16) return NHA_ERR_INVALID_ARG;
+  if (d->no_token_shift != 0 && d->no_token_shift != 1) return NHA_ERR_INVALID_ARG;
   if (d->d != 32 && d->d != 64 && d->d != 128) return NHA_ERR_UNSUPPORTED;
   if (d->m > 64) return NHA_ERR_UNSUPPORTED;
   if (d->C != 16 && d->C != 32 && d->C != 64) return NHA_ERR_UNSUPPORTED;
@@ -34,6 +35,7 @@ nha_status make_shape(const nha_desc* d, bool need_T, Shape* s) {
   s->d = d->d;
   s->m = d->m;
   s->w = d->w;
+  s->sh = d->no_token_shift ? 0 : d->w;
   s->C = d->C;
   s->G = d->H / d->Hkv;
   s->mp = d->m <= 32 ? 32 : 64;

@@ -1423,7 +1423,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
     const T* __restrict__ qr, const T* __restrict__ kr, const T* __restrict__ vv, const T* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dt, const T* __restrict__ dkap,
-    const T* __restrict__ dnu, T* __restrict__ dk, T* __restrict__ dv, int Tn, int H, int Hkv, int w,
+    const T* __restrict__ dnu, T* __restrict__ dk, T* __restrict__ dv, int Tn, int H, int Hkv, int w, int sh,
     float scale, RopeTheta th, int rope) {
   using S = WinBwdKvSmem<T, D>;
   constexpr int PD = S::PD, PK = S::PK;
@@ -1536,8 +1536,8 @@ __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
         ok[db + HB][r] = x2 * cs - x1 * sn;
       }
     const size_t row = (((size_t)b * Tn + key) * Hkv + hg) * D;
-    // this key row is also absorbed (at step key + w); dkap null: no slots
-    const bool slot = dkap != nullptr && key + w < Tn;
+    // this key row is also absorbed (at step key + sh); dkap null: no slots
+    const bool slot = dkap != nullptr && key + sh < Tn;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       floatx4 sk = zero4(), sv = zero4();
@@ -1569,7 +1569,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
     const bf16* __restrict__ qr, const bf16* __restrict__ kr, const bf16* __restrict__ vv,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dt,
     const bf16* __restrict__ dkap, const bf16* __restrict__ dnu, const float2* __restrict__ rcs,
-    bf16* __restrict__ dk, bf16* __restrict__ dv, int Tn, int H, int Hkv, int w, float scale) {
+    bf16* __restrict__ dk, bf16* __restrict__ dv, int Tn, int H, int Hkv, int w, int sh, float scale) {
   constexpr int NT = NWV * 64, KT = 32 * NWV;
   __shared__ bf16 qbuf[2][64 * D];
   __shared__ bf16 obuf[2][64 * D];
@@ -1726,8 +1726,8 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
         }
       }
     }
-    // this key row is also absorbed (at step key + w); dkap null: no slots
-    const bool slot = dkap != nullptr && key + w < Tn;
+    // this key row is also absorbed (at step key + sh); dkap null: no slots
+    const bool slot = dkap != nullptr && key + sh < Tn;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -1808,13 +1808,13 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
         mk.mark(st);
         hipLaunchKernelGGL((k_win_bwd_dkdv_b16<D, NWV>), dim3(nt, units), dim3(NWV * 64), 0, st, qr, kr, v, dO,
                            p.lse, Dt, (const T*)nullptr, (const T*)nullptr, (const float2*)pp.rcs, (T*)p.dk,
-                           (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale);
+                           (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.sh, s.scale);
       } else {
         hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt,
                            (const T*)nullptr, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
         mk.mark(st);
         hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt,
-                           (const T*)nullptr, (const T*)nullptr, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale,
+                           (const T*)nullptr, (const T*)nullptr, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.sh, s.scale,
                            th, s.rope ? 1 : 0);
       }
       mk.mark(st);
@@ -1825,7 +1825,7 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
       mk.mark(st);
       hipLaunchKernelGGL((k_bwd_slot_a_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v,
                          alpha, dO, (const T*)p.o, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H,
-                         s.Hkv, s.m, s.w, s.NC, s.scale);
+                         s.Hkv, s.m, s.sh, s.NC, s.scale);
     } else {
       mk.mark(st);
       hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
@@ -1834,7 +1834,7 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
       const int nitems = s.NC * s.B * s.H;
       const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
       hipLaunchKernelGGL((k_bwd_slot_a<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
-                         (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.w, s.NC,
+                         (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.sh, s.NC,
                          nitems, s.scale);
     }
     // the adjoint scan, and beside it on the side stream the window dq (needs
@@ -1864,21 +1864,22 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     fk.join(st);
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
-                       (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.w, s.NC);
+                       (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.sh, s.NC);
     // the dalpha carry on the side stream, beside the window dk/dv
     const hipStream_t sa = fk.begin(st);
     mk.mark(sa);
     hipLaunchKernelGGL((k_dalpha_tail<T, MP, C>), dim3(s.NC, units), dim3(256), 0, sa, alpha, csum, p.dalpha, s.T,
-                       s.Hkv, s.m, s.w, s.NC);
+                       s.Hkv, s.m, s.sh, s.NC);
     mk.mark(st);
     if constexpr (sizeof(T) == 2) {
       constexpr int NWV = 4;
       const unsigned nt = (unsigned)((s.T + 32 * NWV - 1) / (32 * NWV));
       hipLaunchKernelGGL((k_win_bwd_dkdv_b16<D, NWV>), dim3(nt, units), dim3(NWV * 64), 0, st, qr, kr, v, dO, p.lse,
-                         Dt, dkap, dnu, (const float2*)pp.rcs, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale);
+                         Dt, dkap, dnu, (const float2*)pp.rcs, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.sh,
+                         s.scale);
     } else {
       hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dkap,
-                         dnu, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
+                         dnu, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.sh, s.scale, th, s.rope ? 1 : 0);
     }
     fk.join(st);
     mk.mark(st);

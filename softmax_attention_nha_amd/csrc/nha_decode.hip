@@ -9,7 +9,7 @@
 //      t mod w; the current k_t when w = 0), with gate alpha_t:
 //        S <- Diag(alpha_t) S + (1 - alpha_t) (x) k_{t-w}   (same for V)
 //      -- the K^long_t recurrence of section 关键设计 > 层内混合 with its token
-//      shift;
+//      shift (without the token shift, the ablation: k_t itself at every step);
 //   2. reads the m slots (raw q, no RoPE) and the min(w, t+1) window tokens
 //      (RoPE'd q and keys) through one softmax scaled by `scale`;
 //   3. pushes (k_t, v_t) into ring row t mod w and advances the position.
@@ -83,8 +83,8 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
                                                    float* __restrict__ SK, float* __restrict__ SV,
                                                    const T* __restrict__ RK, const T* __restrict__ RV,
                                                    const T* __restrict__ RKR, const long long* __restrict__ pos,
-                                                   float* __restrict__ part, int H, int Hkv, int m, int w, int NS,
-                                                   float scale, RopeTheta th, int rope) {
+                                                   float* __restrict__ part, int H, int Hkv, int m, int w, int sh,
+                                                   int NS, float scale, RopeTheta th, int rope) {
   // KPG keys per group of LPK lanes; a split takes at most KPG * NG keys
   constexpr int LPK = D / 8, NG = 256 / LPK, PP = D + 4, HALF = D / 2, LPR = LPK / KPG;
   static_assert(KPG >= 1 && LPR >= 2 && KPG * NG <= kDecodeKeysPerSplit, "keys per lane group");
@@ -120,8 +120,9 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
   const int nkeys = m + (int)nwin;
   const long long jfirst = t - nwin + 1;
   const int nmine = nkeys > s ? (nkeys - s + NS - 1) / NS : 0;  // keys of this split
-  // the token leaving the window (ring row t mod w; k_t itself when w = 0),
-  // and this group's window rows (RoPE'd keys when RoPE is on)
+  // the token absorbed at this step: the one leaving the window (ring row
+  // t mod w), or k_t itself when w = 0 or without token shift (sh = 0); and
+  // this group's window rows (RoPE'd keys when RoPE is on)
   float kap[8], nu[8];
   typename Vec<T>::v8 wk[KPG], wvr[KPG];  // raw rows, converted when selected
   if (w > 0) {
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
       wk[kk] = ld8<T>(rkw + rr);
       wvr[kk] = ld8<T>(rv + rr);
     }
-  } else {
+  }
+  if (sh == 0) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       kap[r] = knew[r];
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
     const int j = grp + NG * kk, e = s + NS * j;
     isslot[kk] = e < m;
     if (j < nmine && e < m) {
-      if (t >= w) {
+      if (t >= sh) {
         const float a = ga[kk];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -406,7 +408,7 @@ static hipError_t decode_impl(const Shape& s, const RopeTheta& th, const DecodeP
   hipLaunchKernelGGL(split, dim3(NS, units), dim3(256), 0, st, (const T*)p.q, (const T*)p.k, (const T*)p.v,
                      (const T*)p.alpha, (float*)(base + L.sk), (float*)(base + L.sv), (const T*)(base + L.rk),
                      (const T*)(base + L.rv), (const T*)(base + L.rkr), (const long long*)(base + L.pos),
-                     (float*)(base + L.part), s.H, s.Hkv, s.m, s.w, NS, s.scale, th, s.rope ? 1 : 0);
+                     (float*)(base + L.part), s.H, s.Hkv, s.m, s.w, s.sh, NS, s.scale, th, s.rope ? 1 : 0);
   hipLaunchKernelGGL((k_dec_merge<T, D>), dim3(units), dim3(256), 0, st, (const float*)(base + L.part),
                      (const T*)p.k, (const T*)p.v, (T*)(base + L.rk), (T*)(base + L.rv), (T*)(base + L.rkr),
                      (long long*)(base + L.pos), (T*)p.o, s.H, s.Hkv, s.w, NS, th, s.rope ? 1 : 0);

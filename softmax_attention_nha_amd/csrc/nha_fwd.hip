@@ -1113,7 +1113,7 @@ static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const
   if (s.m > 0) {  // (no slots: no gates and no states)
     mk.mark(st);
     hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend,
-                       s.T, s.Hkv, s.m, s.w, s.NC);
+                       s.T, s.Hkv, s.m, s.sh, s.NC);
   }
   if (s.rope && s.win) fk.record(st);
   if (s.m > 0) {
@@ -1121,11 +1121,11 @@ static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
                          (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
-                         s.w, s.NC);
+                         s.sh, s.NC);
     else
       hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
                          (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
-                         s.w, s.NC);
+                         s.sh, s.NC);
   }
   if (s.rope && s.win) {
     // RoPE (HBM-bound, no LDS) on the side stream beside the state scan (bound
@@ -1180,12 +1180,12 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       mk.mark(st);
       if constexpr (sizeof(T) == 2) {
         hipLaunchKernelGGL((k_slot_fwd_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v,
-                           alpha, (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, s.scale);
+                           alpha, (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.sh, s.NC, s.scale);
       } else {
         const int nitems = s.NC * s.B * s.H;
         const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
         hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
-                           (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.w, s.NC, nitems, s.scale);
+                           (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.sh, s.NC, nitems, s.scale);
       }
     } else {
       ol = nullptr;  // the window kernel starts from an empty softmax

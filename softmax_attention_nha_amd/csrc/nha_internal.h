@@ -16,6 +16,7 @@ struct RopeTheta {
 // Problem shape after validation.
 struct Shape {
   int B, T, H, Hkv, d, m, w, C;
+  int sh;     // absorption shift: token t - sh enters the slots at step t >= sh (w, or 0 without token shift)
   int G;      // H / Hkv
   int mp;     // m padded to a multiple of 32
   int NC;     // ceil(T / C)

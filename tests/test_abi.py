@@ -165,3 +165,11 @@ def test_status_strings():
     lib = nha.load()
     for s in range(5):
         assert lib.nha_status_string(s).startswith(b"NHA_")
+
+
+def test_token_shift_switch_validation():
+    d = desc()
+    d.no_token_shift = 1
+    assert status(d) == nha.NHA_OK
+    d.no_token_shift = 2
+    assert status(d) == nha.NHA_ERR_INVALID_ARG
