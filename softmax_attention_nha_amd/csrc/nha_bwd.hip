@@ -852,10 +852,71 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
   const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
   const int c = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv, t0 = c * C;
   const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
-  stage_gates<T, C, MP, PG, PM, NT>(alpha, sm.sG, sm.sA, b, hg, t0, Tn, Hkv, m, w, tid);
+  const bool absorb = (tq >= w) && (tq < Tn);
+  // one query head's source rows (q or dO) and fp32 weights (s dl or p),
+  // loaded into registers and then written to LDS
+  constexpr int WIT = C * MP / (NT * 4);
+  static_assert(WIT * NT * 4 == C * MP, "tile split");
+  // with one wave (C = 16) a lane would hold too much of the tiles at once:
+  // the first head then loads after the adjoint phase, like the others
+  constexpr bool EARLY = NT >= 128;
+  struct HeadTile {
+    RowTile<T, D, NT, C> tv;
+    PairTileT<T, D, NT, C> tvt;  // fp32 only
+    floatx4 xw[WIT];
+  };
+  auto load_head = [&](int side, int hh, HeadTile& ht) {
+    const int h = hg * G + hh, bh = b * H + h;
+    const T* vb = (side ? dO : q) + (((size_t)b * Tn + t0) * H + h) * D;
+    ht.tv.load(vb, (size_t)H * D, 0, Tn - t0, tid);
+    if constexpr (!S::TR) ht.tvt.load(vb, (size_t)H * D, 0, Tn - t0, tid);
+    const float* wsrc = (side ? pp : sdl) + ((size_t)bh * NC * C + t0) * MP;
+#pragma unroll
+    for (int k = 0; k < WIT; ++k) ht.xw[k] = *reinterpret_cast<const floatx4*>(wsrc + (tid + k * NT) * 4);
+  };
+  auto store_head = [&](const HeadTile& ht) {
+#pragma unroll
+    for (int k = 0; k < WIT; ++k) {
+      const int e = (tid + k * NT) * 4, u = e / MP, i = e % MP;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.sW[u * PG + i + r] = ht.xw[k][r];
+    }
+    ht.tv.template store<PD>(sm.sVec, tid);
+    if constexpr (!S::TR) ht.tvt.template store<PC>(sm.sVecT, tid);
+  };
+  // the loads of one side: this lane's absorbed key row (zero where nothing
+  // is absorbed; the address is clamped to a real row either way), the
+  // incoming adjoint tile and (two waves or more) the first query head's
+  // tiles, all in flight together
+  struct SideLoads {
+    typename Vec<T>::v8 keyf[D / 32];
+    BlockedTile<T, D, NT, MP> tlb;  // bf16 adjoints are stored in column blocks [d/16][i][16]
+    RowTile<T, D, NT, MP> tlr;      // fp32: row layout, plus a transposed copy
+    PairTileT<T, D, NT, MP> tlt;
+    HeadTile ht;
+  };
+  auto issue = [&](int side, SideLoads& L) {
+    const size_t krow = (((size_t)b * Tn + min(max(tq - w, 0), Tn - 1)) * Hkv + hg) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      L.keyf[ks] = ld8_sel<T>((side ? vv : kk) + krow + 32 * ks + 8 * g, absorb);
+    const T* lsrc = lin + (((size_t)unit * NC + c) * 2 + side) * MP * D;
+    if constexpr (S::TR) {
+      L.tlb.load(lsrc, tid);
+    } else if constexpr (EARLY) {
+      L.tlr.load(lsrc, D, 0, MP, tid);
+      L.tlt.load(lsrc, D, 0, MP, tid);
+    }
+    if constexpr (EARLY) load_head(side, 0, L.ht);
+  };
+  SideLoads sl[2];
+  // (two waves or more) side 0's loads go out right behind the gate loads
+  GateTile<T, C, MP, NT> gt;
+  gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
+  if constexpr (EARLY) issue(0, sl[0]);
+  gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
   __syncthreads();
   lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
-  const bool absorb = (tq >= w) && (tq < Tn);
   float bt[NB][4], bwI[NB][4], bwE[NB][4], F[NB][4];
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
@@ -869,33 +930,25 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
       bwE[mb][r] = be * fast_exp2(sm.sG[(C - 1) * PG + i] - Gt);
       F[mb][r] = 0.f;
     }
-  const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
-#pragma unroll 1
+  // with side 0's loads issued early, both sides are unrolled so that each
+  // side's loads live in registers of their own only from their issue to
+  // their LDS stores; a single wave keeps one set and the loop
+#pragma unroll(EARLY ? 2 : 1)
   for (int side = 0; side < 2; ++side) {
-    // this lane's absorbed key row (zero where nothing is absorbed; the
-    // address is clamped to a real row either way), loaded together with the
-    // incoming adjoint tile
-    const size_t krow = (((size_t)b * Tn + min(max(tq - w, 0), Tn - 1)) * Hkv + hg) * D;
-    typename Vec<T>::v8 keyf[D / 32];
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      keyf[ks] = ld8_sel<T>((side ? vv : kk) + krow + 32 * ks + 8 * g, absorb);
+    const int li = EARLY ? side : 0;
+    if (side == 1 || !EARLY) issue(side, sl[li]);
+    SideLoads& L = sl[li];
+    const T* lsrc = lin + (((size_t)unit * NC + c) * 2 + side) * MP * D;
     __syncthreads();
-    {
-      const T* src = lin + (((size_t)unit * NC + c) * 2 + side) * MP * D;
-      if constexpr (S::TR) {  // bf16 adjoints are stored in column blocks [d/16][i][16]
-        BlockedTile<T, D, NT, MP> tl;
-        tl.load(src, tid);
-        tl.template store<PD>(sm.sL, tid);
-      } else {
-        RowTile<T, D, NT, MP> tl;
-        tl.load(src, D, 0, MP, tid);
-        tl.template store<PD>(sm.sL, tid);
-        PairTileT<T, D, NT, MP> tlt;
-        tlt.load(src, D, 0, MP, tid);
-        tlt.template store<PM>(sm.sLt, tid);
-      }
+    if constexpr (S::TR) {
+      L.tlb.template store<PD>(sm.sL, tid);
+    } else {  // one wave: one fp32 copy in registers at a time
+      if constexpr (!EARLY) L.tlr.load(lsrc, D, 0, MP, tid);
+      L.tlr.template store<PD>(sm.sL, tid);
+      if constexpr (!EARLY) L.tlt.load(lsrc, D, 0, MP, tid);
+      L.tlt.template store<PM>(sm.sLt, tid);
     }
+    if constexpr (EARLY) store_head(L.ht);
     __syncthreads();
     floatx4 accO[D / 16];
 #pragma unroll
@@ -905,7 +958,7 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
     for (int mb = 0; mb < NB; ++mb) {
       floatx4 x = zero4();
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) x = mma32(x, ld8<T>(&sm.sL[(16 * mb + cc) * PD + 32 * ks + 8 * g]), keyf[ks]);
+      for (int ks = 0; ks < D / 32; ++ks) x = mma32(x, ld8<T>(&sm.sL[(16 * mb + cc) * PD + 32 * ks + 8 * g]), L.keyf[ks]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         int i = 16 * mb + 4 * g + r;
@@ -937,33 +990,14 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
     }
 #pragma unroll 1
     for (int hh = 0; hh < G; ++hh) {
-      const int h = hg * G + hh, bh = b * H + h;
-      __syncthreads();
-      {
-        const T* vb = (side ? dO : q) + (((size_t)b * Tn + t0) * H + h) * D;
-        RowTile<T, D, NT, C> tv;
-        tv.load(vb, (size_t)H * D, 0, Tn - t0, tid);
-        const float* wsrc = (side ? pp : sdl) + ((size_t)bh * NC * C + t0) * MP;
-        constexpr int WIT = C * MP / (NT * 4);  // every load first, then the LDS writes
-        static_assert(WIT * NT * 4 == C * MP, "tile split");
-        floatx4 xw[WIT];
-#pragma unroll
-        for (int k = 0; k < WIT; ++k) xw[k] = *reinterpret_cast<const floatx4*>(wsrc + (tid + k * NT) * 4);
-#pragma unroll
-        for (int k = 0; k < WIT; ++k) {
-          const int e = (tid + k * NT) * 4, u = e / MP, i = e % MP;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.sW[u * PG + i + r] = xw[k][r];
-        }
-        tv.template store<PD>(sm.sVec, tid);
-        if constexpr (!S::TR) {
-          PairTileT<T, D, NT, C> tvt;
-          tvt.load(vb, (size_t)H * D, 0, Tn - t0, tid);
-          tvt.template store<PC>(sm.sVecT, tid);
-        }
+      if (hh > 0 || !EARLY) {
+        HeadTile hn;
+        load_head(side, hh, hn);
+        __syncthreads();
+        store_head(hn);
+        __syncthreads();
       }
-      __syncthreads();
-      slot_rev<T, D, MP, C>(sm.sVec, sm.sVecT, sm.sW, sm.sG, sm.sA, keyf, bwI, bt, I, t0, w, Tn, accO, F);
+      slot_rev<T, D, MP, C>(sm.sVec, sm.sVecT, sm.sW, sm.sG, sm.sA, L.keyf, bwI, bt, I, t0, w, Tn, accO, F);
     }
     if (absorb) {
       T* dst = (side ? dnu : dkap) + (((size_t)b * Tn + (tq - w)) * Hkv + hg) * D;
