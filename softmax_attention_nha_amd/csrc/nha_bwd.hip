@@ -473,6 +473,14 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   const int unit = b * Hkv + hg, t0 = c * C;
   const bf16* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+  const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
+  const bool qvalid = tq < Tn;
+  const int tqc = qvalid ? tq : Tn - 1;  // clamped row: loads stay unconditional
+  // this lane's q, dO and o rows and lse go out with the first tiles: the
+  // slot reads then wait on no global load, and the second pair of tiles
+  // (issued after the first barrier) stays in flight while they run
+  bf16x8 qf[D / 32], df[D / 32], of[D / 32];
+  float lse_r;
   {
     GateTile<bf16, C, MP, NT> gt;
     BlockedTile<bf16, D, NT, MP> ts;
@@ -480,6 +488,14 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
     gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
     ts.load(src + (size_t)MP * D, tid);
     tk.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const size_t off = (((size_t)b * Tn + tqc) * H + h) * D + 32 * ks + 8 * g;
+      qf[ks] = ld8_sel<bf16>(q + off, qvalid);
+      df[ks] = ld8_sel<bf16>(dO + off, qvalid);
+      of[ks] = ld8<bf16>(o + off);
+    }
+    lse_r = lse[(size_t)bh * Tn + tqc];
     gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
     ts.template store<PD>(sm.tS, tid);
     tk.template store<PD>(sm.tK, tid);
@@ -496,19 +512,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   RowTile<bf16, D, NT, C> tkap;
   tsk.load(src, tid);
   tkap.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-
-  const int r0 = 16 * I, urow = r0 + cc, tq = t0 + urow;
-  const bool qvalid = tq < Tn;
-  const int tqc = qvalid ? tq : Tn - 1;  // clamped row: loads stay unconditional
-  bf16x8 qf[D / 32], df[D / 32], of[D / 32];
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    const size_t off = (((size_t)b * Tn + tqc) * H + h) * D + 32 * ks + 8 * g;
-    qf[ks] = ld8_sel<bf16>(q + off, qvalid);
-    df[ks] = ld8_sel<bf16>(dO + off, qvalid);
-    of[ks] = ld8<bf16>(o + off);
-  }
-  const float lse_r = lse[(size_t)bh * Tn + tqc], lse_t = qvalid ? lse_r : 0.f;
+  const float lse_t = qvalid ? lse_r : 0.f;
   // D_t = <dO_t, o_t>: the four lanes of a query hold a quarter of the row
   // each; written here for the window kernels
   float D_t = 0.f;

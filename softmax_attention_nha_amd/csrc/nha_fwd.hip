@@ -578,6 +578,13 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   const bf16* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
   // chunk row u <-> token t0 + u, absorbing key row t0 + u - w when t0 + u >= w
   const long rbase = ((long)b * Tn + (t0 - w)) * Hkv + hg;
+  const int r0 = 16 * I;
+  const int tq = t0 + r0 + cc;  // this lane's query
+  const bool qvalid = tq < Tn;
+  // this lane's query row goes out with the first tiles: the logits then
+  // wait on no global load, and the output phase's tiles (issued after the
+  // first barrier) stay in flight while they are computed
+  bf16x8 qf[D / 32];
   {
     GateTile<bf16, C, MP, NT> gt;
     BlockedTile<bf16, D, NT, MP> ts;
@@ -585,6 +592,9 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
     gt.load(alpha, b, hg, t0, Tn, Hkv, m, tid);
     ts.load(src, tid);
     tk.load(kk + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      qf[ks] = ld8_sel<bf16>(q + (((size_t)b * Tn + (qvalid ? tq : Tn - 1)) * H + h) * D + 32 * ks + 8 * g, qvalid);
     gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
     ts.template store<PD>(sm.tS, tid);
     tk.template store<PD>(sm.tK, tid);
@@ -602,14 +612,6 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   RowTile<bf16, D, NT, C> tnu;
   tsv.load(src + (size_t)MP * D, tid);
   tnu.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
-
-  const int r0 = 16 * I;
-  const int tq = t0 + r0 + cc;  // this lane's query
-  const bool qvalid = tq < Tn;
-  bf16x8 qf[D / 32];
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = ld8_sel<bf16>(q + (((size_t)b * Tn + (qvalid ? tq : Tn - 1)) * H + h) * D + 32 * ks + 8 * g, qvalid);
   float lg[NB][4];
   slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
   // softmax partial over the m slots (log2 domain)
