@@ -241,26 +241,32 @@ def _pmc_per_dispatch(folder, counter, name_part):
     return sum(vals.values()) / len(vals), len(vals)
 
 
-def traffic_summary(dirs, kernel, copy_mib):
-    fetch, nf = _pmc_per_dispatch(dirs[0], "FETCH_SIZE", kernel)
-    write, nw = _pmc_per_dispatch(dirs[1], "WRITE_SIZE", kernel)
+def traffic_summary(dirs, kernels, copy_mib):
+    """profiles/traffic.json: per-launch HBM bytes of each kernel in `kernels`
+    (comma-separated), its FETCH_SIZE / WRITE_SIZE scaled by what the same
+    counters read for a plain copy of copy_mib MiB."""
     cf, _ = _pmc_per_dispatch(dirs[2], "FETCH_SIZE", "copy")
     cw, _ = _pmc_per_dispatch(dirs[3], "WRITE_SIZE", "copy")
     n = copy_mib * (1 << 20)
     ff, fw = cf * 1024.0 / n, cw * 1024.0 / n  # counter bytes per true byte, from the copy
     out = {
-        "kernel": kernel,
-        "fetch_kib_per_dispatch": round(fetch, 1),
-        "write_kib_per_dispatch": round(write, 1),
-        "dispatches": [nf, nw],
         "copy_mib": copy_mib,
         "copy_fetch_kib": round(cf, 1),
         "copy_write_kib": round(cw, 1),
         "fetch_scale": round(ff, 4),
         "write_scale": round(fw, 4),
-        "hbm_bytes_per_launch": round(fetch * 1024.0 / ff + write * 1024.0 / fw),
-        "source_sha256": source_digest(kernel),
+        "kernels": {},
     }
+    for kernel in kernels.split(","):
+        fetch, nf = _pmc_per_dispatch(dirs[0], "FETCH_SIZE", kernel)
+        write, nw = _pmc_per_dispatch(dirs[1], "WRITE_SIZE", kernel)
+        out["kernels"][kernel] = {
+            "fetch_kib_per_dispatch": round(fetch, 1),
+            "write_kib_per_dispatch": round(write, 1),
+            "dispatches": [nf, nw],
+            "hbm_bytes_per_launch": round(fetch * 1024.0 / ff + write * 1024.0 / fw),
+            "source_sha256": source_digest(kernel),
+        }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -354,9 +360,11 @@ def measured_traffic(stage):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel") != STAGE_KERNEL.get(stage) or t.get("source_sha256") != source_digest(t.get("kernel")):
+    kernel = STAGE_KERNEL.get(stage)
+    e = t.get("kernels", {}).get(kernel)
+    if e is None or e.get("source_sha256") != source_digest(kernel):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return e.get("hbm_bytes_per_launch")
 
 
 # ---------------------------------------------------------------- sweeps
@@ -505,7 +513,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR"),
                     help="turn four rocprofv3 --pmc output folders into profiles/traffic.json and exit")
-    ap.add_argument("--traffic-kernel", default="k_bwd_slot_b", help="kernel name for --traffic-summary")
+    ap.add_argument("--traffic-kernel", default="k_bwd_slot_b,k_win_bwd_dkdv",
+                    help="kernel names (comma-separated) for --traffic-summary")
     ap.add_argument("--traffic-copy-mib", type=int, default=1024)
     ap.add_argument("--sweep", action="store_true",
                     help="time the w sweep, the T sweep (with decode), the other configurations; one JSON line each")
