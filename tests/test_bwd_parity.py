@@ -78,6 +78,13 @@ def test_tiny_workload(base):
 
 
 # ---------------------------------------------------------------- bf16, every element at reduced T
+@pytest.mark.parametrize("C", [16, 32])
+def test_bf16_chunk_sizes_gqa(C):
+    # one- and two-wave slot workgroups (C = 16, 32: the two load orders of
+    # slot pass B) at d = 128, m = 64, two query heads per KV head, ragged T
+    check(WORKLOADS["1p3b"].with_(B=1, T=261, H=4, Hkv=2, seed=57), w=40, C=C)
+
+
 @pytest.mark.parametrize("name,w", [("340m", None), ("1p3b", 0), ("1p3b", 64), ("1p3b", 512), ("1p3b", 2048),
                                     ("gqa", None)])
 def test_bf16_workloads_reduced(name, w):

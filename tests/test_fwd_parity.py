@@ -55,6 +55,14 @@ def test_fp32_slots_and_head_dims(m, d):
 
 
 # ---------------------------------------------------------------- bf16, every element at reduced T
+@pytest.mark.parametrize("C", [16, 32])
+def test_bf16_chunk_sizes_gqa(C):
+    # one- and two-wave slot workgroups (C = 16, 32) at d = 128, m = 64 with
+    # two query heads per KV head and a ragged last chunk
+    wl = WORKLOADS["1p3b"].with_(B=1, T=261, H=4, Hkv=2, seed=14)
+    check_full(wl, w=40, C=C)
+
+
 @pytest.mark.parametrize("name,w", [("340m", None), ("1p3b", 0), ("1p3b", 64), ("1p3b", 512), ("1p3b", 2048),
                                     ("long", None), ("gqa", None)])
 def test_bf16_workloads_reduced(name, w):
