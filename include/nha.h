@@ -37,12 +37,27 @@
  * Pointers must be 16-byte aligned.
  *
  * Ownership: the caller allocates every buffer, including the workspace and
- * the decode state.  The library never allocates, frees or synchronises, keeps
- * no global mutable state (apart from a per-device cache of the compute-unit
- * count, used to size persistent grids), and only enqueues work on the caller's stream
- * (`stream` is a hipStream_t passed as void*; NULL = the null stream).  Calls
- * return before the GPU has run; buffers must stay alive until the stream work
- * completes.  Calls on distinct buffers are thread-safe.
+ * the decode state; the library never allocates device memory, frees it or
+ * synchronises the host with the GPU.  Calls return before the GPU has run;
+ * buffers must stay alive until the stream work completes.  Calls on distinct
+ * buffers are thread-safe.  `stream` is a hipStream_t passed as void* (NULL =
+ * the null stream).
+ *
+ * Library state, the whole of it:
+ *   - a per-device cache of the compute-unit count (read once with
+ *     hipDeviceGetAttribute; sizes persistent grids);
+ *   - per calling thread and device, ONE side stream (default priority,
+ *     hipStreamNonBlocking) and two events (timing disabled), created by the
+ *     first nha_fwd, nha_fwd_s0, nha_bwd, nha_bwd_after_fwd or nha_bwd_s0 call
+ *     of that thread on that device, kept until nha_release_side_streams().
+ *     Those calls fork independent launches onto the side stream (RoPE beside
+ *     the slot-state scan; the window dq beside the adjoint scan; the dalpha
+ *     carry beside the window dk/dv) after an event recorded on `stream`, and
+ *     make `stream` wait for the side stream before they return, so each call
+ *     still behaves as one operation ordered on `stream`.  If the side
+ *     stream cannot be created, every launch goes on `stream`.  The *_timed
+ *     calls with non-NULL events and the decode step never use it.  Results
+ *     are bitwise the same either way.
  *
  * Errors: every argument check runs on the host before any HIP call and
  * returns a status; nothing throws across the ABI and nothing aborts.  A
@@ -233,6 +248,16 @@ nha_status nha_bwd_after_fwd_timed(const nha_desc* desc, const void* q,
                                    void* dk, void* dv, float* dalpha, void* ws,
                                    size_t ws_bytes, void* stream,
                                    void* const* events);
+
+/* Destroy the side stream and the two events that nha_fwd, nha_fwd_s0,
+ * nha_bwd, nha_bwd_after_fwd and nha_bwd_s0 created for the CALLING thread
+ * (on every device it used); the next such call creates them again.  Work
+ * already enqueued on them completes normally (HIP releases the handles once
+ * it has).  Call it before a thread exits, or after a device reset (the
+ * cached handles are then stale).  Other threads' streams are untouched.
+ * Returns NHA_OK, or NHA_ERR_HIP if a destroy call failed (the handles are
+ * forgotten either way).  With nothing to release it makes no HIP call. */
+nha_status nha_release_side_streams(void);
 
 /* Static string for a status code. */
 const char* nha_status_string(nha_status s);

@@ -39,6 +39,7 @@ EXPORTED = (
     "nha_bwd_after_fwd_timed",
     "nha_fwd_s0",
     "nha_bwd_s0",
+    "nha_release_side_streams",
 )
 
 
@@ -110,6 +111,8 @@ def load():
     lib.nha_fwd_s0.restype = st
     lib.nha_bwd_s0.argtypes = [D] + [vp] * 16 + [sz, vp]
     lib.nha_bwd_s0.restype = st
+    lib.nha_release_side_streams.argtypes = []
+    lib.nha_release_side_streams.restype = st
     lib.nha_status_string.argtypes = [st]
     lib.nha_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -169,6 +172,21 @@ def _check(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _check_bytes(t, name, nbytes, device):
+    """A raw device buffer (workspace, decode state): contiguous uint8 on
+    `device` holding at least `nbytes` bytes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.uint8:
+        raise ValueError("%s: expected dtype torch.uint8, got %s" % (name, t.dtype))
+    if t.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < nbytes:
+        raise ValueError("%s: %d bytes needed for this shape, got %d" % (name, nbytes, t.numel()))
+
+
 def _desc_from(q, k, alpha, w, C, rope_base, scale, token_shift=True):
     if q.dim() != 4 or k.dim() != 4 or alpha.dim() != 4:
         raise ValueError("q, k, alpha must be 4-D: [B,T,H,d], [B,T,Hkv,d], [B,T,Hkv,m]")
@@ -195,6 +213,15 @@ def decode_state_size(desc):
     return n
 
 
+def _workspace(workspace, n, dev):
+    """The caller's workspace when it is large enough, else a new one."""
+    if workspace is not None:
+        _check_bytes(workspace, "workspace", 0, dev)
+        if workspace.numel() >= n:
+            return workspace
+    return torch.empty(n, dtype=torch.uint8, device=dev)
+
+
 def _check_s0(s0, B, Hkv, m, d, dev):
     if len(s0) != 2:
         raise ValueError("s0 must be (S0K, S0V)")
@@ -219,10 +246,16 @@ def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, w
     _check(v, "v", (B, T, Hkv, d), dt, dev)
     _check(alpha, "alpha", (B, T, Hkv, m), dt, dev)
     lib = load()
+    if out is not None:
+        _check(out, "out", (B, T, H, d), dt, dev)
+    if lse_out is not None:
+        _check(lse_out, "lse_out", (B, H, T), torch.float32, dev)
+    if state_out is not None:
+        _check_bytes(state_out, "state_out", decode_state_size(desc), dev)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev) if lse_out is None else lse_out
     n = workspace_size(desc)
-    ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(n, dtype=torch.uint8, device=dev)
+    ws = _workspace(workspace, n, dev)
     if s0 is not None:
         _check_s0(s0, B, Hkv, m, d, dev)
         rc = lib.nha_fwd_s0(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(s0[0]), _ptr(s0[1]),
@@ -261,15 +294,21 @@ def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, works
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         da = torch.empty((B, T, Hkv, m), dtype=torch.float32, device=dev)
     else:
+        if len(out) != 4:
+            raise ValueError("out must be (dq, dk, dv, dalpha)")
         dq, dk, dv, da = out
+        _check(dq, "dq", (B, T, H, d), dt, dev)
+        _check(dk, "dk", (B, T, Hkv, d), dt, dev)
+        _check(dv, "dv", (B, T, Hkv, d), dt, dev)
+        _check(da, "dalpha", (B, T, Hkv, m), torch.float32, dev)
     n = workspace_size(desc, backward=True)
     if after_fwd:
-        if workspace is None or workspace.numel() < n:
+        if workspace is None:
             raise ValueError("after_fwd needs the forward's workspace, of at least %d bytes" % n)
+        _check_bytes(workspace, "workspace", n, dev)
         ws = workspace
     else:
-        ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(
-            n, dtype=torch.uint8, device=dev)
+        ws = _workspace(workspace, n, dev)
     if s0 is not None:
         if after_fwd:
             raise ValueError("s0 with after_fwd is not provided (nha_bwd_s0 recomputes the prologue)")
@@ -289,6 +328,13 @@ def bwd(q, k, v, alpha, o, lse, dO, w, C=64, rope_base=10000.0, scale=0.0, works
     return dq, dk, dv, da
 
 
+def release_side_streams():
+    """Destroy the calling thread's library side streams (nha_release_side_streams)."""
+    rc = load().nha_release_side_streams()
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_release_side_streams")
+
+
 def decode_state(B, H, Hkv, d, m, w, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16, device="cuda"):
     """A zero decode state (the state before the first token)."""
     desc = make_desc(B, 1, H, Hkv, d, m, w, 64, rope_base, scale, dtype)
@@ -297,15 +343,21 @@ def decode_state(B, H, Hkv, d, m, w, rope_base=10000.0, scale=0.0, dtype=torch.b
 
 def decode_step(q_t, k_t, v_t, alpha_t, state, w, rope_base=10000.0, scale=0.0, out=None, token_shift=True):
     """One recurrent step. q_t [B,H,d], k_t/v_t [B,Hkv,d], alpha_t [B,Hkv,m]. Returns o_t [B,H,d]."""
+    if q_t.dim() != 3 or k_t.dim() != 3 or alpha_t.dim() != 3:
+        raise ValueError("q_t, k_t, alpha_t must be 3-D: [B,H,d], [B,Hkv,d], [B,Hkv,m]")
     B, H, d = q_t.shape
     Hkv, m = k_t.shape[1], alpha_t.shape[2]
     dev, dt = q_t.device, q_t.dtype
+    if dt not in _DTYPES:
+        raise ValueError("dtype must be float32 or bfloat16")
+    _check(q_t, "q_t", (B, H, d), dt, dev)
     _check(k_t, "k_t", (B, Hkv, d), dt, dev)
     _check(v_t, "v_t", (B, Hkv, d), dt, dev)
     _check(alpha_t, "alpha_t", (B, Hkv, m), dt, dev)
     desc = make_desc(B, 1, H, Hkv, d, m, w, 64, rope_base, scale, dt, token_shift)
-    if state.numel() < decode_state_size(desc):
-        raise ValueError("decode state too small")
+    _check_bytes(state, "state", decode_state_size(desc), dev)
+    if out is not None:
+        _check(out, "out", (B, H, d), dt, dev)
     o = torch.empty_like(q_t) if out is None else out
     rc = load().nha_decode_step(ctypes.byref(desc), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(alpha_t), _ptr(state),
                                 _ptr(o), _stream(dev))

@@ -40,12 +40,25 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
+def _stale(src, headers_mtime):
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    return os.path.getmtime(obj) < max(os.path.getmtime(src), headers_mtime)
+
+
+def build(verbose=True, incremental=False):
+    """Compile every source (incremental=True: only those whose object is older
+    than the source or any header) and link libnha.so."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    headers = glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
+    hm = max(os.path.getmtime(h) for h in headers)
+    todo = [x for x in srcs if _stale(x, hm)] if incremental else srcs
+    jobs = max(1, min(len(todo), int(os.environ.get("MAX_JOBS", "8"))))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(OBJ, os.path.basename(x) + ".o") for x in srcs]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     subprocess.check_call(cmd)
@@ -56,4 +69,4 @@ def build(verbose=True):
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv)

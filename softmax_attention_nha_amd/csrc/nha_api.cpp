@@ -77,13 +77,16 @@ int device_cu_count() {
   return cached[dev];
 }
 
+// The calling thread's side stream and events, per device (created on first
+// use, released by nha_release_side_streams).
+static thread_local Fork side_cache[64];
+
 Fork side_fork(bool enabled) {
   Fork none;
   if (!enabled) return none;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return none;
-  static thread_local Fork cache[64];
-  Fork& c = cache[dev];
+  Fork& c = side_cache[dev];
   if (!c.side) {
     hipStream_t s = nullptr;
     hipEvent_t a = nullptr, b = nullptr;
@@ -114,6 +117,25 @@ const char* nha_status_string(nha_status s) {
     case NHA_ERR_HIP: return "NHA_ERR_HIP: HIP launch failed";
   }
   return "unknown nha_status";
+}
+
+nha_status nha_release_side_streams(void) {
+  nha_status rc = NHA_OK;
+  int cur = -1;
+  bool have_cur = false;
+  for (int dev = 0; dev < 64; ++dev) {
+    Fork& c = side_cache[dev];
+    if (!c.side) continue;
+    if (!have_cur) have_cur = hipGetDevice(&cur) == hipSuccess;
+    // the handles belong to `dev`: destroy them with it current
+    if (hipSetDevice(dev) != hipSuccess) rc = NHA_ERR_HIP;
+    if (hipEventDestroy(c.ev_fork) != hipSuccess) rc = NHA_ERR_HIP;
+    if (hipEventDestroy(c.ev_join) != hipSuccess) rc = NHA_ERR_HIP;
+    if (hipStreamDestroy(c.side) != hipSuccess) rc = NHA_ERR_HIP;
+    c = Fork();
+  }
+  if (have_cur && hipSetDevice(cur) != hipSuccess) rc = NHA_ERR_HIP;
+  return rc;
 }
 
 nha_status nha_check_desc(const nha_desc* desc) {

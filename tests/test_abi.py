@@ -173,3 +173,73 @@ def test_token_shift_switch_validation():
     assert status(d) == nha.NHA_OK
     d.no_token_shift = 2
     assert status(d) == nha.NHA_ERR_INVALID_ARG
+
+
+def test_release_side_streams_without_any_is_a_no_op():
+    # nothing was created by this thread: no HIP call, NHA_OK
+    assert nha.load().nha_release_side_streams() == nha.NHA_OK
+    nha.release_side_streams()
+
+
+# ---------------------------------------------------------------- binding checks (raise before any library call)
+def _cpu_inputs(B=1, T=64, H=2, Hkv=2, d=32, m=8, dtype=torch.float32):
+    q = torch.zeros(B, T, H, d, dtype=dtype)
+    k = torch.zeros(B, T, Hkv, d, dtype=dtype)
+    return q, k, k.clone(), torch.zeros(B, T, Hkv, m, dtype=dtype)
+
+
+def test_binding_rejects_a_too_small_or_mistyped_decode_state():
+    q, k, v, a = _cpu_inputs()
+    d = nha.make_desc(1, 64, 2, 2, 32, 8, 16, 16, 10000.0, 0.0, torch.float32)
+    n = nha.decode_state_size(d)
+    with pytest.raises(ValueError, match="state_out"):
+        nha.fwd(q, k, v, a, 16, C=16, state_out=torch.zeros(n - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="state_out"):
+        nha.fwd(q, k, v, a, 16, C=16, state_out=torch.zeros(n, dtype=torch.float32))
+    # a state sized for bf16 rings is too small for fp32 ones
+    nb = nha.decode_state_size(nha.make_desc(1, 64, 2, 2, 32, 8, 16, 16, 10000.0, 0.0, torch.bfloat16))
+    assert nb < n
+    with pytest.raises(ValueError, match="state_out"):
+        nha.fwd(q, k, v, a, 16, C=16, state_out=torch.zeros(nb, dtype=torch.uint8))
+    # a state sized without RoPE (no RoPE'd ring) is too small with RoPE
+    nr = nha.decode_state_size(nha.make_desc(1, 64, 2, 2, 32, 8, 16, 16, 0.0, 0.0, torch.float32))
+    assert nr < n
+    with pytest.raises(ValueError, match="state_out"):
+        nha.fwd(q, k, v, a, 16, C=16, state_out=torch.zeros(nr, dtype=torch.uint8))
+
+
+def test_binding_rejects_mismatched_outputs():
+    q, k, v, a = _cpu_inputs()
+    with pytest.raises(ValueError, match="out"):
+        nha.fwd(q, k, v, a, 16, C=16, out=torch.zeros(1, 64, 2, 16))
+    with pytest.raises(ValueError, match="lse_out"):
+        nha.fwd(q, k, v, a, 16, C=16, lse_out=torch.zeros(1, 2, 64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="workspace"):
+        nha.fwd(q, k, v, a, 16, C=16, workspace=torch.zeros(16, dtype=torch.float32))
+    o, lse = torch.zeros_like(q), torch.zeros(1, 2, 64)
+    good = (torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v), torch.zeros(1, 64, 2, 8))
+    for i, name in enumerate(("dq", "dk", "dv", "dalpha")):
+        bad = list(good)
+        bad[i] = bad[i][:, :32].contiguous()
+        with pytest.raises(ValueError, match=name):
+            nha.bwd(q, k, v, a, o, lse, q, 16, C=16, out=tuple(bad))
+    with pytest.raises(ValueError, match="workspace"):
+        nha.bwd(q, k, v, a, o, lse, q, 16, C=16, out=good, after_fwd=True,
+                workspace=torch.zeros(8, dtype=torch.uint8))
+
+
+def test_binding_decode_step_checks_every_tensor():
+    B, H, Hkv, d, m, w = 1, 2, 2, 32, 8, 16
+    q = torch.zeros(B, H, d)
+    k = torch.zeros(B, Hkv, d)
+    a = torch.zeros(B, Hkv, m)
+    n = nha.decode_state_size(nha.make_desc(B, 1, H, Hkv, d, m, w, 64, 10000.0, 0.0, torch.float32))
+    state = torch.zeros(n, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q_t"):
+        nha.decode_step(torch.zeros(B, H, 2 * d)[:, :, ::2], k, k, a, state, w)  # non-contiguous
+    with pytest.raises(ValueError, match="out"):
+        nha.decode_step(q, k, k, a, state, w, out=torch.zeros(B, H, d + 1))
+    with pytest.raises(ValueError, match="state"):
+        nha.decode_step(q, k, k, a, state[: n - 8], w)
+    with pytest.raises(ValueError, match="state"):
+        nha.decode_step(q, k, k, a, torch.zeros(n, dtype=torch.int8), w)
