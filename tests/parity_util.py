@@ -60,3 +60,46 @@ def compare(name, got, ref, atol, rel):
     assert mx <= atol, "%s: max abs error %.3e > %.1e" % (name, mx, atol)
     assert r <= rel, "%s: relative L2 error %.3e > %.1e" % (name, r, rel)
     return mx, r
+
+
+def _per_head(x, b, heads):
+    """[B,T,*,d] -> one sequence per listed head: [len(heads),T,1,d] (fp64)."""
+    return np.ascontiguousarray(f64(x[b, :, heads[0]:heads[-1] + 1]).transpose(1, 0, 2)[:, :, None, :])
+
+
+def oracle_units(q, k, v, a, dO, w, base, units, G, Tp=None):
+    """The fp64 oracle on the (b, g) units listed, with every query head of a
+    unit run as a sequence of its own over its KV head (the operator is
+    grouped-query attention: a query head reads only its KV head, and the
+    loss is a sum over query heads, so dk, dv and dalpha of a unit are the sums
+    of the per-head gradients -- the GQA invariant the oracle pins check).
+    The oracle's threads then cover every (unit, query head).  Tp: first Tp
+    tokens only (forward: rows t < Tp depend on tokens <= t only).
+    Returns per unit: (o [1,T,G,d], lse [1,G,T]) when dO is None, else
+    (dq [1,T,G,d], dk, dv [1,T,1,d], dalpha [1,T,1,m])."""
+    qs, ks, vs, as_, ds = [], [], [], [], []
+    for (b, g) in units:
+        hq = list(range(g * G, (g + 1) * G))
+        qs.append(_per_head(q, b, hq))
+        rep = lambda x: np.repeat(_per_head(x, b, [g]), G, axis=0)
+        ks.append(rep(k))
+        vs.append(rep(v))
+        as_.append(rep(a))
+        if dO is not None:
+            ds.append(_per_head(dO, b, hq))
+    cut = lambda xs: np.ascontiguousarray(np.concatenate(xs)[:, :Tp] if Tp else np.concatenate(xs))
+    if dO is None:
+        o, lse = oracle.fwd(cut(qs), cut(ks), cut(vs), cut(as_), w, rope_base=base)
+        out = []
+        for i in range(len(units)):
+            oo = o[i * G:(i + 1) * G, :, 0].transpose(1, 0, 2)[None]
+            ll = lse[i * G:(i + 1) * G, 0][None]
+            out.append((oo, ll))
+        return out
+    dq, dk, dv, da = oracle.bwd(cut(qs), cut(ks), cut(vs), cut(as_), cut(ds), w, rope_base=base)
+    out = []
+    for i in range(len(units)):
+        s = slice(i * G, (i + 1) * G)
+        out.append((dq[s, :, 0].transpose(1, 0, 2)[None], dk[s].sum(0, keepdims=True),
+                    dv[s].sum(0, keepdims=True), da[s].sum(0, keepdims=True)))
+    return out
