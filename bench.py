@@ -87,19 +87,25 @@ def bytes_fwd(wl, e):
 
 
 def stage_work(stage, wl, w, e):
-    """(flops, bytes) of one launch of `stage`: the algorithmic flops of the
-    part of the method it computes, and the bytes it must move given the
-    data each kernel reads and writes (its inputs and outputs, each once).
+    """(flops, algorithmic bytes, implementation bytes) of one launch of `stage`.
 
-    Flops: window kernels 4d per (query, in-window key) pair in the forward,
-    6d (dq pass: QK^T, dO V^T, dS K) and 8d (dk/dv pass: QK^T, dO V^T, P^T dO,
-    dS^T Q) in the backward; slot kernels, per query t >= w with c(t) earlier
-    absorbed rows of its chunk, one read (2md + (2d+2m)c) and one mix (same)
-    in the forward, two reads and one mix in pass A, two reverse reads and two
-    reverse mixes in pass B; scans 4md per absorbed token per KV head
-    (forward) and per token per query head (adjoint).  Bytes: per launch,
-    summed over its work items (formulas below; e = element bytes, mp = m
-    padded to 32 or 64, per chunk of C rows)."""
+    Flops: the algorithmic flops of the part of the method the kernel
+    computes -- window kernels 4d per (query, in-window key) pair in the
+    forward, 6d (dq pass: QK^T, dO V^T, dS K) and 8d (dk/dv pass: QK^T, dO V^T,
+    P^T dO, dS^T Q) in the backward; slot kernels, per query t >= w with c(t)
+    earlier absorbed rows of its chunk, one read (2md + (2d+2m)c) and one mix
+    (same) in the forward, two reads and one mix in pass A, two reverse reads
+    and two reverse mixes in pass B; scans 4md per absorbed token per KV head
+    (forward) and per token per query head (adjoint).
+
+    Algorithmic bytes: the operator's own tensors the kernel reads or writes,
+    each once -- q, k, v, alpha, dO (inputs), o, dq, dk, dv, dalpha (outputs),
+    and the per-row softmax statistics lse and D_t = <dO_t, o_t> (4 bytes per
+    (row, head)).  RoPE'd q/k stand in for q/k.  Implementation bytes: the
+    workspace intermediates the kernel moves between launches (gate products,
+    chunk-start states, slot partials, adjoints, slot parts of the gradients),
+    reported apart and not counted in the roofline.  e = element bytes, mp = m
+    padded to 32 or 64, NC chunks of C rows."""
     B, H, Hkv, T, d, m, C = wl.B, wl.H, wl.Hkv, wl.T, wl.d, wl.m, wl.C
     G, NC = H // Hkv, -(-T // C)
     mp = 32 if m <= 32 else 64
@@ -107,33 +113,38 @@ def stage_work(stage, wl, w, e):
     fw = flops_window(B, H, T, d, w)
     fs = flops_slot(B, H, T, d, m, w, C)
     absorbed = max(0, T - w)
+    BT = float(B * T)
+    q_b, kv_b, a_b = BT * H * d * e, BT * Hkv * d * e, BT * Hkv * m * e  # one of q (or o, dO, dq); k; alpha
+    row = BT * H * 4.0  # lse or D
     table = {
-        "rope_cs": (0.0, 8.0 * T * (d // 2)),
-        "rope": (0.0, 2.0 * B * T * (H + Hkv) * d * e),
-        "chunk_gates": (0.0, B * T * Hkv * m * e + units * NC * mp * (C * e + 4.0)),
-        "state_scan": (flops_state(B, Hkv, T, d, m, w),
-                       2.0 * B * Hkv * absorbed * d * e + units * NC * (mp * C * e + 4.0 * mp + 2.0 * mp * d * e)),
-        "slot_fwd": (fs, B * H * NC * (2.0 * mp * d * e + 4.0 * C * d * e + C * m * e + 4.0 * C)),
-        "win_fwd": (fw, B * T * (3.0 * H * d * e + 2.0 * Hkv * d * e + 8.0 * H)),
-        "bwd_prep": (0.0, B * T * H * (2.0 * d * e + 4)),
-        "slot_bwd_a": (1.5 * fs, B * H * NC * (2.0 * mp * d * e + 6.0 * C * d * e + C * m * e + 8.0 * C
-                                              + 2.0 * mp * C * e + 12.0 * C * mp)),
-        "adj_scan": (4.0 * m * d * B * H * T,
-                     units * NC * (G * (2.0 * C * d * e + 2.0 * mp * C * e) + 4.0 * mp + 2.0 * mp * d * e)),
-        "slot_bwd_b": (2.0 * fs, units * NC * (2.0 * mp * d * e + 4.0 * C * d * e + C * m * e + 4.0 * C * m
-                                               + 4.0 * mp + G * (2.0 * C * d * e + 12.0 * C * mp))),
-        "dalpha_tail": (0.0, B * T * Hkv * m * (e + 8.0)),
-        "win_bwd_dq": (1.5 * fw, B * T * (4.0 * H * d * e + 2.0 * Hkv * d * e + 8.0 * H)),
-        "win_bwd_dkdv": (2.0 * fw, B * T * (2.0 * H * d * e + 6.0 * Hkv * d * e + 8.0 * H)),
-        "export_state": (0.0, 4.0 * B * Hkv * min(w, T) * d * e),
+        "rope_cs": (0.0, 0.0, 8.0 * T * (d // 2)),
+        "rope": (0.0, q_b + kv_b, q_b + kv_b),
+        "chunk_gates": (0.0, a_b, units * NC * mp * (C * e + 4.0)),
+        "state_scan": (flops_state(B, Hkv, T, d, m, w), 2.0 * B * Hkv * absorbed * d * e,
+                       units * NC * (mp * C * e + 4.0 * mp + 2.0 * mp * d * e)),
+        "slot_fwd": (fs, q_b + 2 * kv_b + a_b, B * H * NC * 2.0 * mp * d * e + q_b + row),
+        "win_fwd": (fw, 2 * q_b + 2 * kv_b + row, q_b + row),
+        "bwd_prep": (0.0, 2 * q_b + row, 0.0),
+        "slot_bwd_a": (1.5 * fs, 3 * q_b + 2 * kv_b + a_b + 2 * row,
+                       B * H * NC * (2.0 * mp * d * e + 2.0 * mp * C * e + 12.0 * C * mp) + q_b),
+        "adj_scan": (4.0 * m * d * B * H * T, 2 * q_b,
+                     units * NC * (G * 2.0 * mp * C * e + 4.0 * mp + 2.0 * mp * d * e)),
+        "slot_bwd_b": (2.0 * fs, 2 * kv_b + a_b + BT * Hkv * m * 4.0 + 2 * q_b,
+                       units * NC * (2.0 * mp * d * e + 4.0 * mp + G * 12.0 * C * mp) + 2 * kv_b),
+        "dalpha_tail": (0.0, a_b + 2 * BT * Hkv * m * 4.0, units * NC * mp * 4.0),
+        "win_bwd_dq": (1.5 * fw, 3 * q_b + 2 * kv_b + 2 * row, q_b),
+        "win_bwd_dkdv": (2.0 * fw, 2 * q_b + 4 * kv_b + 2 * row, 2 * kv_b),
+        "export_state": (0.0, 4.0 * B * Hkv * min(w, T) * d * e, 0.0),
     }
-    return table.get(stage, (None, None))
+    return table.get(stage, (None, None, None))
 
 
 def roofline(stage, us, wl, w, e):
-    """Roofline of one kernel: the binding ceiling is min(P, I * BW) with
-    I = flops / bytes; both fractions are reported."""
-    flops, nbytes = stage_work(stage, wl, w, e)
+    """Roofline of one kernel against its algorithmic work: intensity I =
+    flops / algorithmic bytes; bound "mfma" when I is at or above the ridge
+    P / BW, else "hbm"; frac = achieved / peak of that bound.  Both fractions
+    and the implementation traffic are reported beside it."""
+    flops, nbytes, impl = stage_work(stage, wl, w, e)
     if flops is None:
         return None
     dur = us / 1e6
@@ -147,9 +158,12 @@ def roofline(stage, us, wl, w, e):
     else:
         r.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                  frac=round(gbs / PEAK_HBM_GBS, 4))
-    r.update(traffic=measured_traffic(stage), avg_us=round(us, 2),
-             flops_per_launch=flops, bytes_per_launch=nbytes,
-             intensity_flop_per_byte=round(flops / nbytes, 1),
+    tr = measured_traffic(stage)
+    r.update(traffic=tr.get("fetch_write") if tr else None,
+             traffic_dram_requests=tr.get("dram_requests") if tr else None,
+             avg_us=round(us, 2), flops_per_launch=flops, algorithmic_bytes_per_launch=nbytes,
+             implementation_bytes_per_launch=impl,
+             intensity_flop_per_byte=round(flops / nbytes, 1) if nbytes else None,
              mfma_tflops=round(tf, 2), mfma_frac=round(tf / peak, 4),
              hbm_GBs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
     return r
@@ -179,7 +193,117 @@ def cpu_baseline(wl, w, q, k, v, a, dO, with_bwd):
         "kind": "oracle",
         "sample": "batch row 0, all %d heads, first %d of %d tokens, %s in fp64 (%.1f s)" % (
             wl.H, Tp, wl.T, "fwd+bwd" if with_bwd else "fwd", dt),
+        "threads_note": "cores = OpenMP threads the oracle ran with: min(host CPUs, %d KV heads of the batch row)" % (
+            units),
+        "host_cpu_model": _cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
+        "host_cpus_available": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ---------------------------------------------------------------- context figures
+def copy_bandwidth(mib=1024, reps=5):
+    """Attainable HBM bandwidth: a plain device copy of `mib` MiB (read + write
+    bytes over the median event time)."""
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    t = sorted(ts)[reps // 2]
+    del src, dst
+    return {"bytes": 2 * n, "GBs": round(2 * n / t / 1e9, 1), "note": "torch device copy of %d MiB, median of %d" % (
+        mib, reps)}
+
+
+def device_clock_under_load(run_step, seconds=1.5):
+    """The engine clock while the step runs: enqueue about `seconds` of steps,
+    then read rocm-smi's current clock levels while they execute."""
+    import subprocess
+
+    t0 = time.perf_counter()
+    run_step()
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-4)
+    for _ in range(max(1, int(seconds / per))):
+        run_step()
+    out = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [x.strip() for x in r.stdout.splitlines() if "sclk" in x.lower() or "mclk" in x.lower()]
+        out = {"rocm_smi": lines[:4], "note": "rocm-smi --showclocks while about %.1f s of steps ran" % seconds}
+    except (OSError, subprocess.SubprocessError) as ex:
+        out = {"rocm_smi": None, "note": "rocm-smi unavailable: %s" % type(ex).__name__}
+    torch.cuda.synchronize()
+    props = torch.cuda.get_device_properties(0)
+    rate = getattr(props, "clock_rate", None)
+    if rate:
+        out["max_engine_clock_MHz"] = round(rate / 1e3)
+    return out
+
+
+def b1_timings(steps, flush_mib=512):
+    """The headline shape at B = 1 (151 MB of algorithmic forward traffic fits
+    the 256 MB Infinity Cache): median fwd / bwd times with warm caches, and
+    with a flush_mib buffer written before every call."""
+    wl = WORKLOADS["headline"].with_(B=1)
+    dev = torch.device("cuda:0")
+    q, k, v, a, dO = (x.to(dev) for x in make_inputs(wl, with_grad=True))
+    desc = nha.make_desc(wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, wl.w, wl.C, wl.rope_base, 0.0, wl.dtype)
+    ws = torch.empty(max(nha.workspace_size(desc), nha.workspace_size(desc, backward=True)), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty((wl.B, wl.T, wl.Hkv, wl.m), dtype=torch.float32, device=dev))
+    junk = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    res = {}
+    for flush in (False, True):
+        tf, tb = [], []
+        for i in range(steps + 2):
+            if flush:
+                junk.fill_(float(i))
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            nha.fwd(q, k, v, a, wl.w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=o, lse_out=lse)
+            e1.record()
+            if flush:
+                junk.fill_(float(-i))
+                e1b = torch.cuda.Event(enable_timing=True)
+                e1b.record()
+            else:
+                e1b = e1
+            nha.bwd(q, k, v, a, o, lse, dO, wl.w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=grads,
+                    after_fwd=True)
+            e2.record()
+            e2.synchronize()
+            if i >= 2:
+                tf.append(e0.elapsed_time(e1))
+                tb.append(e1b.elapsed_time(e2))
+        res["flushed" if flush else "warm"] = {"fwd_ms": round(sorted(tf)[len(tf) // 2], 4),
+                                               "bwd_ms": round(sorted(tb)[len(tb) // 2], 4)}
+    res["workload"] = "B=1 H=16 T=8192 d=128 m=64 w=512 C=64 bf16"
+    res["flush"] = "a %d MiB buffer written before each fwd and each bwd (flushed)" % flush_mib
+    del junk, ws
+    return res
 
 
 # ---------------------------------------------------------------- HBM traffic from counters
@@ -241,10 +365,18 @@ def _pmc_per_dispatch(folder, counter, name_part):
     return sum(vals.values()) / len(vals), len(vals)
 
 
-def traffic_summary(dirs, kernels, copy_mib):
+def traffic_summary(dirs, kernels, copy_mib, dram_dirs=None):
     """profiles/traffic.json: per-launch HBM bytes of each kernel in `kernels`
-    (comma-separated), its FETCH_SIZE / WRITE_SIZE scaled by what the same
-    counters read for a plain copy of copy_mib MiB."""
+    (comma-separated), two ways:
+      fetch_write    its FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
+                     what the same counters read for a plain copy of copy_mib
+                     MiB (dirs: kernel FETCH, kernel WRITE, copy FETCH, copy
+                     WRITE runs);
+      dram_requests  32 B x (TCC_EA0_RDREQ_DRAM_32B + TCC_EA0_WRREQ_WRITE_DRAM_32B)
+                     -- the L2's requests to memory counted in 32-byte units
+                     (64- and 128-byte requests count 2 and 4) -- from one run
+                     with both counters (dram_dirs: kernel run, copy run); the
+                     copy's reading is reported beside it as the check."""
     cf, _ = _pmc_per_dispatch(dirs[2], "FETCH_SIZE", "copy")
     cw, _ = _pmc_per_dispatch(dirs[3], "WRITE_SIZE", "copy")
     n = copy_mib * (1 << 20)
@@ -257,16 +389,28 @@ def traffic_summary(dirs, kernels, copy_mib):
         "write_scale": round(fw, 4),
         "kernels": {},
     }
+    if dram_dirs:
+        crd, _ = _pmc_per_dispatch(dram_dirs[1], "TCC_EA0_RDREQ_DRAM_32B", "copy")
+        cwr, _ = _pmc_per_dispatch(dram_dirs[1], "TCC_EA0_WRREQ_WRITE_DRAM_32B", "copy")
+        out["copy_dram_read_bytes"] = round(32.0 * crd)
+        out["copy_dram_write_bytes"] = round(32.0 * cwr)
     for kernel in kernels.split(","):
         fetch, nf = _pmc_per_dispatch(dirs[0], "FETCH_SIZE", kernel)
         write, nw = _pmc_per_dispatch(dirs[1], "WRITE_SIZE", kernel)
-        out["kernels"][kernel] = {
+        ent = {
             "fetch_kib_per_dispatch": round(fetch, 1),
             "write_kib_per_dispatch": round(write, 1),
             "dispatches": [nf, nw],
             "hbm_bytes_per_launch": round(fetch * 1024.0 / ff + write * 1024.0 / fw),
             "source_sha256": source_digest(kernel),
         }
+        if dram_dirs:
+            rd, nr = _pmc_per_dispatch(dram_dirs[0], "TCC_EA0_RDREQ_DRAM_32B", kernel)
+            wr, _ = _pmc_per_dispatch(dram_dirs[0], "TCC_EA0_WRREQ_WRITE_DRAM_32B", kernel)
+            ent["dram_read_bytes"] = round(32.0 * rd)
+            ent["dram_write_bytes"] = round(32.0 * wr)
+            ent["dram_request_bytes_per_launch"] = round(32.0 * (rd + wr))
+        out["kernels"][kernel] = ent
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -353,8 +497,9 @@ def trace_summary(folder):
 
 
 def measured_traffic(stage):
-    """HBM bytes per launch of `stage` from profiles/traffic.json, or None when
-    absent, for another kernel, or taken on other kernel sources."""
+    """HBM bytes per launch of `stage` from profiles/traffic.json --
+    {"fetch_write": .., "dram_requests": ..} -- or None when absent, for
+    another kernel, or taken on other kernel sources."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
@@ -364,7 +509,7 @@ def measured_traffic(stage):
     e = t.get("kernels", {}).get(kernel)
     if e is None or e.get("source_sha256") != source_digest(kernel):
         return None
-    return e.get("hbm_bytes_per_launch")
+    return {"fetch_write": e.get("hbm_bytes_per_launch"), "dram_requests": e.get("dram_request_bytes_per_launch")}
 
 
 # ---------------------------------------------------------------- sweeps
@@ -505,6 +650,8 @@ def main():
     ap.add_argument("--B", type=int, default=None, help="override the batch")
     ap.add_argument("--fwd-only", action="store_true", help="diagnostic: time the forward alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context figures (device clock, copy bandwidth, B = 1 warm / flushed timings)")
     ap.add_argument("--one-stream", action="store_true",
                     help="skip the production-call region: time only the one-stream pass with an event around "
                          "every launch (for kernel traces whose averages match the per-kernel events)")
@@ -516,6 +663,9 @@ def main():
     ap.add_argument("--traffic-kernel", default="k_bwd_slot_b,k_win_bwd_dkdv",
                     help="kernel names (comma-separated) for --traffic-summary")
     ap.add_argument("--traffic-copy-mib", type=int, default=1024)
+    ap.add_argument("--traffic-dram", nargs=2, metavar=("KERNEL_DIR", "COPY_DIR"),
+                    help="with --traffic-summary: rocprofv3 --pmc folders of one run each with "
+                         "TCC_EA0_RDREQ_DRAM_32B and TCC_EA0_WRREQ_WRITE_DRAM_32B (kernel run, copy run)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the w sweep, the T sweep (with decode), the other configurations; one JSON line each")
     ap.add_argument("--only", metavar="LABEL", help="with --sweep: only the points of this sweep label")
@@ -535,7 +685,7 @@ def main():
         copy_calibrate(args.copy_calibrate)
         return
     if args.traffic_summary:
-        traffic_summary(args.traffic_summary, args.traffic_kernel, args.traffic_copy_mib)
+        traffic_summary(args.traffic_summary, args.traffic_kernel, args.traffic_copy_mib, args.traffic_dram)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -683,6 +833,10 @@ def main():
         "outputs_finite": ok,
         "roofline": roof,
     }
+    if not args.no_context and args.workload == "headline" and do_bwd:
+        line["device_clock"] = device_clock_under_load(step)
+        line["copy_bandwidth"] = copy_bandwidth()
+        line["b1"] = b1_timings(max(5, K // 2))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, w, q, k, v, a, dO, do_bwd)
     print(json.dumps(line), flush=True)
