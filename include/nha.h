@@ -56,8 +56,9 @@
  *     make `stream` wait for the side stream before they return, so each call
  *     still behaves as one operation ordered on `stream`.  If the side
  *     stream cannot be created, every launch goes on `stream`.  The *_timed
- *     calls with non-NULL events and the decode step never use it.  Results
- *     are bitwise the same either way.
+ *     calls with non-NULL events, the decode step and nha_fwd_noalloc never
+ *     use it.  Results are bitwise the same either way.
+ *   - nha_fwd_noalloc's scratch array (see there).
  *
  * Errors: every argument check runs on the host before any HIP call and
  * returns a status; nothing throws across the ABI and nothing aborts.  A
@@ -187,6 +188,30 @@ nha_status nha_decode_step(const nha_desc* desc, const void* q_t,
                            const void* k_t, const void* v_t,
                            const void* alpha_t, void* state, void* o_t,
                            void* stream);
+
+/* ---------------------------------------------------------------- allocation-free forward
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same result as nha_fwd (bitwise: the same kernels, every launch
+ * on `stream`), with the workspace taken from a library-owned scratch array
+ * of NHA_NOALLOC_SCRATCH_BYTES bytes that every GPU the library runs on holds
+ * from module load until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no stream or event creation); the first call on a
+ * device looks the array's address up once (hipGetSymbolAddress).
+ *   Arguments as for nha_fwd, without ws / ws_bytes.
+ *   Limit: a descriptor whose nha_fwd_workspace_size exceeds
+ *   NHA_NOALLOC_SCRATCH_BYTES returns NHA_ERR_WORKSPACE before any HIP call
+ *   (e.g. d = 128, m = 64, H = 16, w = 512 fits up to about 2800 tokens of
+ *   batch; use nha_fwd with a workspace beyond that).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (different streams, or different host threads, without ordering
+ *   between them) race and give wrong results.  The array keeps the last
+ *   call's contents; nothing in it has to start at zero (each call writes
+ *   every region before reading it). */
+#define NHA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+nha_status nha_fwd_noalloc(const nha_desc* desc, const void* q, const void* k,
+                           const void* v, const void* alpha, void* o,
+                           float* lse, void* state_out, void* stream);
 
 /* ---------------------------------------------------------------- initial slot states
  * Learnable initial memory-slot states (the ai.info page, "Future

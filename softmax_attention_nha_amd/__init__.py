@@ -40,6 +40,7 @@ EXPORTED = (
     "nha_fwd_s0",
     "nha_bwd_s0",
     "nha_release_side_streams",
+    "nha_fwd_noalloc",
 )
 
 
@@ -111,6 +112,8 @@ def load():
     lib.nha_fwd_s0.restype = st
     lib.nha_bwd_s0.argtypes = [D] + [vp] * 16 + [sz, vp]
     lib.nha_bwd_s0.restype = st
+    lib.nha_fwd_noalloc.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.nha_fwd_noalloc.restype = st
     lib.nha_release_side_streams.argtypes = []
     lib.nha_release_side_streams.restype = st
     lib.nha_status_string.argtypes = [st]
@@ -268,6 +271,35 @@ def fwd(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, state_out=None, w
                            _events_arg(events))
     if rc != NHA_OK:
         raise NhaError(rc, "nha_fwd")
+    return o, lse
+
+
+def fwd_noalloc(q, k, v, alpha, w, C=64, rope_base=10000.0, scale=0.0, out=None, lse_out=None, state_out=None,
+                token_shift=True):
+    """nha_fwd_noalloc: the forward without a workspace argument (the library's
+    scratch array serves as one; shapes whose workspace exceeds it raise
+    NhaError with NHA_ERR_WORKSPACE).  Returns (o, lse)."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale, token_shift)
+    dev, dt = q.device, q.dtype
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    _check(q, "q", (B, T, H, d), dt, dev)
+    _check(k, "k", (B, T, Hkv, d), dt, dev)
+    _check(v, "v", (B, T, Hkv, d), dt, dev)
+    _check(alpha, "alpha", (B, T, Hkv, m), dt, dev)
+    if out is not None:
+        _check(out, "out", (B, T, H, d), dt, dev)
+    if lse_out is not None:
+        _check(lse_out, "lse_out", (B, H, T), torch.float32, dev)
+    if state_out is not None:
+        _check_bytes(state_out, "state_out", decode_state_size(desc), dev)
+    lib = load()
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    rc = lib.nha_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse),
+                             _ptr(state_out), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_fwd_noalloc")
     return o, lse
 
 

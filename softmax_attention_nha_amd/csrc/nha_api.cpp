@@ -183,6 +183,24 @@ nha_status nha_fwd_timed(const nha_desc* desc, const void* q, const void* k, con
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
 }
 
+nha_status nha_fwd_noalloc(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                           void* o, float* lse, void* state_out, void* stream) {
+  Shape s;
+  nha_status rc = make_shape(desc, true, &s);
+  if (rc != NHA_OK) return rc;
+  if (!q || !k || !v || (!alpha && s.m > 0) || !o) return NHA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(o) ||
+      (lse && !aligned16(lse)) || (state_out && !aligned16(state_out)))
+    return NHA_ERR_INVALID_ARG;
+  if (fwd_ws_layout(s).total > kNoallocScratchBytes) return NHA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (noalloc_scratch(&scratch) != hipSuccess || !scratch) return NHA_ERR_HIP;
+  FwdPtrs p{q, k, v, alpha, o, lse, state_out, (char*)scratch, nullptr};
+  p.one_stream = true;
+  hipError_t e = launch_fwd(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
 nha_status nha_fwd_s0(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
                       const float* s0k, const float* s0v, void* o, float* lse, void* state_out, void* ws,
                       size_t ws_bytes, void* stream) {

@@ -1175,7 +1175,7 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       pp.skout = (float*)((char*)p.state_out + SL.sk);
       pp.svout = (float*)((char*)p.state_out + SL.sv);
     }
-    prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st, side_fork(p.events == nullptr));
+    prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st, side_fork(p.events == nullptr && !p.one_stream));
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
     if (s.m > 0) {

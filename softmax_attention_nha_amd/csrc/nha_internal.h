@@ -208,6 +208,7 @@ struct FwdPtrs {
   void* const* events;  // nullable timing events
   const float* s0k = nullptr;  // initial slot states [B*Hkv][m][d], nullable = zero
   const float* s0v = nullptr;
+  bool one_stream = false;      // every launch on the caller's stream (no side stream)
 };
 hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st);
 
@@ -233,6 +234,12 @@ struct BwdPtrs {
   float* ds0v = nullptr;
 };
 hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st);
+
+// The device address of the allocation-free forward's scratch array on the
+// current device (looked up once per device with hipGetSymbolAddress) and its
+// size in bytes.
+constexpr size_t kNoallocScratchBytes = NHA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
 
 // LDS bytes the largest forward / backward kernel needs for this shape.
 size_t slot_fwd_lds_bytes(const Shape& s);
