@@ -42,6 +42,16 @@
  *      section, and "Fusão Nativa via Softmax Único" on the gist.science page),
  *      o_t = sum_i p_i SV[i] + sum_j p_j v_j,  lse_t = mu + ln Z.
  *
+ * Weighted-fusion ablation (lam non-NULL, [B][T][H] in [0, 1]): the slot
+ * logits and the window logits each get their own softmax and the two reads
+ * are mixed, o_t = lam_t o^L_t + (1 - lam_t) o^W_t.  This is the variant the
+ * ai.info page's findings ("Unified softmax beats weighted fusion") compare
+ * the unified softmax with -- a fixed coefficient (lam constant) or a learned
+ * sequence-dependent one (lam per token, its gradient returned) -- and the
+ * separate-then-summed intra-layer hybrids of the Paper-Notes page's 现有痛点
+ * paragraph.  lse then holds the slot softmax's lse and lse_w the window's;
+ * it needs m >= 1 and w >= 1 (both softmaxes non-empty).
+ *
  * Backward: the adjoint of the same per-token recurrence, written from the
  * chain rule (not from the chunkwise form):
  *   dl = p (dp - D_t),  D_t = <dO_t, o_t>
@@ -53,6 +63,10 @@
  *   window: dq_t += R_t^T s sum_j dl^W_j R_j k_j,
  *           dk_j += R_j^T s dl^W_j R_t q_t, dv_j += p^W_j dO_t.
  *   initial states: dS0 = a_0 Lam_0 (the adjoint carried to before t = 0).
+ *   weighted fusion: with cL = lam_t, cW = 1 - lam_t and each branch's own
+ *   probabilities, dl^L = cL p^L (dp^L - <dO, o^L>), dl^W = cW p^W (dp^W -
+ *   <dO, o^W>), the value sources carry cL p^L and cW p^W, and
+ *   dlam_t = <dO_t, o^L_t - o^W_t>.
  * The reverse sweep recomputes states segment by segment from checkpoints
  * spaced every SEG tokens.
  *
@@ -163,45 +177,73 @@ static void absorb(int m, int d, const double* a, const double* x, double* S) {
 /* Logits and probabilities for one query at time t of head h (group g).
  * SK/SV: state after the absorption at t.  kr: rotated keys of this (b,g).
  * Writes p (length m + nw), returns lse; o_out (nullable) gets the output. */
+/* softmax over p[0..n) in place; returns its lse (-inf when n = 0) */
+static double softmax_inplace(double* p, int n) {
+  double mu = -INFINITY, Z = 0.0;
+  for (int e = 0; e < n; ++e)
+    if (p[e] > mu) mu = p[e];
+  for (int e = 0; e < n; ++e) {
+    p[e] = exp(p[e] - mu);
+    Z += p[e];
+  }
+  for (int e = 0; e < n; ++e) p[e] /= Z;
+  return mu + log(Z);
+}
+
+/* Logits and probabilities for one query at time t of head h (group g).
+ * SK/SV: state after the absorption at t.  kr: rotated keys of this (b,g).
+ * Unified softmax (mix = NULL): p (length m + nw) is one softmax over all
+ * logits, o_out (nullable) the output; returns the lse.
+ * Weighted fusion (mix = {lam}): p[0..m) is the softmax of the slot logits,
+ * p[m..m+nw) that of the window logits; oL, oW (nullable) get the two reads
+ * and o_out lam oL + (1 - lam) oW; returns the slot lse, *lse_w the window's. */
+typedef struct {
+  double lam;
+  double* oL;
+  double* oW;
+  double lse_w;
+} mix_t;
+
 static double read_step(const dims_t* D, const double* cs, const double* sn,
                         int t, const double* qv, const double* SK,
                         const double* SV, const double* kr, const double* vg,
                         size_t vstride, double* qr, double* p, double* o_out,
-                        int* nw_out) {
+                        int* nw_out, mix_t* mix) {
   int d = D->d, m = D->m, w = D->w;
   double s = D->scale;
   int j0 = t - w + 1;
   if (j0 < 0) j0 = 0;
   int nw = (w > 0) ? (t - j0 + 1) : 0;
   rope_apply(D, cs, sn, t, qv, qr);
-  double mu = -INFINITY;
-  for (int i = 0; i < m; ++i) {
-    p[i] = s * dot(SK + (size_t)i * d, qv, d);
-    if (p[i] > mu) mu = p[i];
+  for (int i = 0; i < m; ++i) p[i] = s * dot(SK + (size_t)i * d, qv, d);
+  for (int j = 0; j < nw; ++j) p[m + j] = s * dot(qr, kr + (size_t)(j0 + j) * d, d);
+  double lse;
+  if (!mix) {
+    lse = softmax_inplace(p, m + nw);
+  } else {
+    lse = softmax_inplace(p, m);
+    mix->lse_w = softmax_inplace(p + m, nw);
   }
-  for (int j = 0; j < nw; ++j) {
-    p[m + j] = s * dot(qr, kr + (size_t)(j0 + j) * d, d);
-    if (p[m + j] > mu) mu = p[m + j];
-  }
-  double Z = 0.0;
-  for (int e = 0; e < m + nw; ++e) {
-    p[e] = exp(p[e] - mu);
-    Z += p[e];
-  }
-  for (int e = 0; e < m + nw; ++e) p[e] /= Z;
+  double cL = mix ? mix->lam : 1.0, cW = mix ? 1.0 - mix->lam : 1.0;
   if (o_out) {
     for (int c = 0; c < d; ++c) o_out[c] = 0.0;
+    if (mix && mix->oL)
+      for (int c = 0; c < d; ++c) mix->oL[c] = mix->oW[c] = 0.0;
     for (int i = 0; i < m; ++i) {
       const double* r = SV + (size_t)i * d;
-      for (int c = 0; c < d; ++c) o_out[c] += p[i] * r[c];
+      for (int c = 0; c < d; ++c) o_out[c] += cL * p[i] * r[c];
+      if (mix && mix->oL)
+        for (int c = 0; c < d; ++c) mix->oL[c] += p[i] * r[c];
     }
     for (int j = 0; j < nw; ++j) {
       const double* r = vg + (size_t)(j0 + j) * vstride;
-      for (int c = 0; c < d; ++c) o_out[c] += p[m + j] * r[c];
+      for (int c = 0; c < d; ++c) o_out[c] += cW * p[m + j] * r[c];
+      if (mix && mix->oW)
+        for (int c = 0; c < d; ++c) mix->oW[c] += p[m + j] * r[c];
     }
   }
   *nw_out = nw;
-  return mu + log(Z);
+  return lse;
 }
 
 /* rotated keys of one (b, g): kr[t][d] */
@@ -214,11 +256,13 @@ static void rotate_keys(const dims_t* D, const double* cs, const double* sn,
 int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
                    double rope_base, double scale, const double* q,
                    const double* k, const double* v, const double* alpha,
-                   const double* s0k, const double* s0v, double* o,
-                   double* lse, double* sk_out, double* sv_out, int nthreads) {
+                   const double* s0k, const double* s0v, const double* lam,
+                   double* o, double* lse, double* lse_w, double* sk_out,
+                   double* sv_out, int nthreads) {
   dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale, shift < 0 ? w : shift};
   const dims_t* D = &Dm;
   if (check_dims(D)) return 1;
+  if (lam && (m < 1 || w < 1)) return 1;
   if (Dm.scale == 0.0) Dm.scale = 1.0 / sqrt((double)d);
   double *cs, *sn;
   rope_tables(D, &cs, &sn);
@@ -246,9 +290,11 @@ int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
       }
       for (int hh = 0; hh < G; ++hh) {
         int h = g * G + hh, nw;
+        mix_t mx = {lam ? lam[((size_t)b * T + t) * H + h] : 0.0, NULL, NULL, 0.0};
         double l = read_step(D, cs, sn, t, q + QIDX(b, t, h), SK, SV, kr, vg,
-                             vstride, qr, p, o + QIDX(b, t, h), &nw);
+                             vstride, qr, p, o + QIDX(b, t, h), &nw, lam ? &mx : NULL);
         if (lse) lse[((size_t)b * H + h) * T + t] = l;
+        if (lam && lse_w) lse_w[((size_t)b * H + h) * T + t] = mx.lse_w;
       }
     }
     if (sk_out) memcpy(sk_out + (size_t)u * m * d, SK, sizeof(double) * m * d);
@@ -267,12 +313,14 @@ int nha_oracle_fwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
 int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
                    double rope_base, double scale, const double* q,
                    const double* k, const double* v, const double* alpha,
-                   const double* s0k, const double* s0v, const double* dO,
-                   double* dq, double* dk, double* dv, double* dalpha,
-                   double* ds0k, double* ds0v, int nthreads) {
+                   const double* s0k, const double* s0v, const double* lam,
+                   const double* dO, double* dq, double* dk, double* dv,
+                   double* dalpha, double* ds0k, double* ds0v, double* dlam,
+                   int nthreads) {
   dims_t Dm = {B, T, H, Hkv, d, m, w, rope_base, scale, shift < 0 ? w : shift};
   const dims_t* D = &Dm;
   if (check_dims(D)) return 1;
+  if (lam && (m < 1 || w < 1)) return 1;
   if (Dm.scale == 0.0) Dm.scale = 1.0 / sqrt((double)d);
   double s = Dm.scale;
   double *cs, *sn;
@@ -304,6 +352,8 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
     double* dl = (double*)malloc(sizeof(double) * (m + (size_t)wmax + 1));
     double* qr = (double*)malloc(sizeof(double) * d);
     double* ov = (double*)malloc(sizeof(double) * d);
+    double* oL = (double*)malloc(sizeof(double) * d);
+    double* oW = (double*)malloc(sizeof(double) * d);
     double* dqr = (double*)malloc(sizeof(double) * d);
     double* tmp = (double*)malloc(sizeof(double) * d);
     rotate_keys(D, cs, sn, k, b, g, kr);
@@ -356,17 +406,29 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
           int h = g * G + hh, nw;
           const double* qv = q + QIDX(b, t, h);
           const double* dov = dO + QIDX(b, t, h);
-          read_step(D, cs, sn, t, qv, SK, SV, kr, vg, vstride, qr, p, ov, &nw);
+          mix_t mx = {lam ? lam[((size_t)b * T + t) * H + h] : 0.0, oL, oW, 0.0};
+          read_step(D, cs, sn, t, qv, SK, SV, kr, vg, vstride, qr, p, ov, &nw, lam ? &mx : NULL);
           int j0 = t - w + 1;
           if (j0 < 0) j0 = 0;
-          double Dt = dot(dov, ov, d);
+          /* unified: one softmax, cL = cW = 1 and D_L = D_W = <dO, o>;
+             weighted: each branch's own softmax, scaled by its coefficient */
+          double cL = 1.0, cW = 1.0, DL, DW;
+          if (lam) {
+            cL = mx.lam;
+            cW = 1.0 - mx.lam;
+            DL = dot(dov, oL, d);
+            DW = dot(dov, oW, d);
+            if (dlam) dlam[((size_t)b * T + t) * H + h] = DL - DW;
+          } else {
+            DL = DW = dot(dov, ov, d);
+          }
           for (int i = 0; i < m; ++i) {
             double dp = dot(dov, SV + (size_t)i * d, d);
-            dl[i] = p[i] * (dp - Dt);
+            dl[i] = cL * p[i] * (dp - DL);
           }
           for (int j = 0; j < nw; ++j) {
             double dp = dot(dov, vg + (size_t)(j0 + j) * vstride, d);
-            dl[m + j] = p[m + j] * (dp - Dt);
+            dl[m + j] = cW * p[m + j] * (dp - DW);
           }
           /* dq: slots (unrotated) + window (rotated frame, then R_t^T) */
           double* dqv = dq + QIDX(b, t, h);
@@ -383,7 +445,7 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
             for (int c = 0; c < d; ++c) {
               dqr[c] += s * dl[m + j] * r[c];
               dr[c] += s * dl[m + j] * qr[c];
-              dvr[c] += p[m + j] * dov[c];
+              dvr[c] += cW * p[m + j] * dov[c];
             }
           }
           rope_apply_T(D, cs, sn, t, dqr, tmp);
@@ -394,7 +456,7 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
             double* rv = LV + (size_t)i * d;
             for (int c = 0; c < d; ++c) {
               rk[c] += s * dl[i] * qv[c];
-              rv[c] += p[i] * dov[c];
+              rv[c] += cL * p[i] * dov[c];
             }
           }
         }
@@ -454,6 +516,8 @@ int nha_oracle_bwd(int B, int T, int H, int Hkv, int d, int m, int w, int shift,
     free(dl);
     free(qr);
     free(ov);
+    free(oL);
+    free(oW);
     free(dqr);
     free(tmp);
   }

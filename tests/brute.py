@@ -56,11 +56,14 @@ def slot_states(x, alpha, w, s0=None):
     return S
 
 
-def nha_brute(q, k, v, alpha, w, base=10000.0, scale=0.0, s0=None, shift=None):
+def nha_brute(q, k, v, alpha, w, base=10000.0, scale=0.0, s0=None, shift=None, lam=None):
     """Returns (o [B,T,H,d], lse [B,H,T]); all inputs fp64 torch tensors.
     s0: optional initial slot states (S0K, S0V), each [B,Hkv,m,d].
     shift: the absorption shift of the slots (None: w, the method; 0: every
-    token enters the slots at its own step)."""
+    token enters the slots at its own step).
+    lam: [B,T,H] -- the weighted-fusion ablation: torch.softmax over the slot
+    logits and, separately, over the window logits; o = lam o_slot + (1 - lam)
+    o_window; lse is then [2,B,H,T] (slot, window)."""
     B, T, H, d = q.shape
     Hkv, m = k.shape[2], alpha.shape[-1]
     G = H // Hkv
@@ -79,6 +82,12 @@ def nha_brute(q, k, v, alpha, w, base=10000.0, scale=0.0, s0=None, shift=None):
     tt = t_idx[:, None]
     inwin = (jj <= tt) & (jj >= tt - w + 1) if w > 0 else torch.zeros(T, T, dtype=torch.bool)
     lW = lW.masked_fill(~inwin[None, :, None, :], float("-inf"))
+    if lam is not None:
+        oL = torch.einsum("bthm,bthmd->bthd", torch.softmax(lL, dim=-1), SVh)
+        oW = torch.einsum("bthj,bjhd->bthd", torch.softmax(lW, dim=-1), vh)
+        o = lam[..., None] * oL + (1.0 - lam[..., None]) * oW
+        lse = torch.stack([torch.logsumexp(lL, dim=-1), torch.logsumexp(lW, dim=-1)])  # [2,B,T,H]
+        return o, lse.permute(0, 1, 3, 2).contiguous()
     logits = torch.cat([lL, lW], dim=-1)
     lse = torch.logsumexp(logits, dim=-1)  # [B,T,H]
     p = torch.softmax(logits, dim=-1)

@@ -468,3 +468,88 @@ def test_no_token_shift_gradients_match_autograd(w):
     (o * t64(dO)).sum().backward()
     for got, ref in ((dq, tq), (dk, tk), (dv, tv), (da, ta)):
         np.testing.assert_allclose(got, ref.grad.numpy(), atol=1e-11)
+
+
+# ---------------------------------------------------------------- weighted fusion
+# The ablation the ai.info page's findings compare the unified softmax with
+# ("Unified softmax beats weighted fusion": a fixed-coefficient weighted sum,
+# and a learnable sequence-dependent coefficient), i.e. the separate-then-
+# summed intra-layer hybrids of the Paper-Notes page's 现有痛点 paragraph: the
+# slot and window logits each get their own softmax and o = lam o^L +
+# (1 - lam) o^W.
+def rand_lam(B, T, H, seed):
+    return np.random.default_rng(seed).uniform(0.05, 0.95, (B, T, H))
+
+
+@pytest.mark.parametrize("w", [1, 3, 12])
+def test_weighted_fusion_matches_closed_form(w):
+    B, T, H, Hkv, d, m = 2, 11, 4, 2, 8, 5
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=140 + w)
+    lam = rand_lam(B, T, H, 141 + w)
+    o, lse = oracle.fwd(q, k, v, a, w, rope_base=100.0, lam=lam)
+    o_ref, l_ref = nha_brute(t64(q), t64(k), t64(v), t64(a), w, 100.0, lam=t64(lam))
+    assert lse.shape == (2, B, H, T)
+    np.testing.assert_allclose(o, o_ref.numpy(), atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("w", [2, 13])
+def test_weighted_fusion_coefficient_zero_is_sliding_window_attention(w):
+    # lam = 0 keeps only the window's own softmax: plain sliding-window RoPE
+    # attention (torch scaled_dot_product_attention)
+    B, T, H, Hkv, d, m = 1, 13, 4, 2, 8, 3
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=150 + w)
+    o, lse = oracle.fwd(q, k, v, a, w, rope_base=300.0, lam=np.zeros((B, T, H)))
+    qr, kr = rope_complex(t64(q), 300.0), rope_complex(t64(k), 300.0)
+    tt = torch.arange(T)
+    band = (tt[None, :] <= tt[:, None]) & (tt[None, :] >= tt[:, None] - w + 1)
+    for h in range(H):
+        g = h // (H // Hkv)
+        ref = F.scaled_dot_product_attention(qr[0, :, h][None], kr[0, :, g][None], t64(v)[0, :, g][None],
+                                             attn_mask=band[None])[0]
+        np.testing.assert_allclose(o[0, :, h], ref.numpy(), atol=1e-12)
+
+
+def test_weighted_fusion_zero_gates_read_the_shifted_token():
+    # lam = 1 and alpha = 0: every slot holds the raw (k, v)_{t-w}, so the
+    # slot softmax reads exactly v_{t-w} (and the m zero slots, i.e. 0, for t < w)
+    B, T, H, Hkv, d, m, w = 1, 12, 2, 1, 4, 3, 4
+    q, k, v, _ = rand_case(B, T, H, Hkv, d, m, seed=160)
+    a = np.zeros((B, T, Hkv, m))
+    o, _ = oracle.fwd(q, k, v, a, w, rope_base=100.0, lam=np.ones((B, T, H)))
+    ref = np.zeros_like(o)
+    ref[0, w:, :, :] = v[0, :T - w, 0][:, None, :]
+    np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+@pytest.mark.parametrize("w", [1, 5, 12])
+def test_weighted_fusion_gradients_match_autograd(w):
+    B, T, H, Hkv, d, m = 1, 12, 2, 1, 4, 3
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=170 + w)
+    lam = rand_lam(B, T, H, 171 + w)
+    dO = np.random.default_rng(172).standard_normal(q.shape)
+    dq, dk, dv, da, dlam = oracle.bwd(q, k, v, a, dO, w, rope_base=100.0, lam=lam)
+    tq, tk, tv, ta, tl = (t64(x).requires_grad_(True) for x in (q, k, v, a, lam))
+    o, _ = nha_brute(tq, tk, tv, ta, w, 100.0, lam=tl)
+    (o * t64(dO)).sum().backward()
+    for got, ref in ((dq, tq), (dk, tk), (dv, tv), (da, ta), (dlam, tl)):
+        np.testing.assert_allclose(got, ref.grad.numpy(), atol=1e-11)
+
+
+def test_weighted_fusion_coefficient_gradient_matches_finite_differences():
+    B, T, H, Hkv, d, m, w = 1, 10, 2, 1, 4, 3, 3
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=180)
+    lam = rand_lam(B, T, H, 181)
+    dO = np.random.default_rng(182).standard_normal(q.shape)
+    dlam = oracle.bwd(q, k, v, a, dO, w, rope_base=50.0, lam=lam)[-1]
+    h = 1e-6
+    rng = np.random.default_rng(183)
+    for _ in range(10):
+        idx = tuple(rng.integers(0, n) for n in lam.shape)
+        lp, lm = lam.copy(), lam.copy()
+        lp[idx] += h
+        lm[idx] -= h
+        fp = (oracle.fwd(q, k, v, a, w, rope_base=50.0, lam=lp)[0] * dO).sum()
+        fm = (oracle.fwd(q, k, v, a, w, rope_base=50.0, lam=lm)[0] * dO).sum()
+        fd = (fp - fm) / (2 * h)
+        assert abs(fd - dlam[idx]) < 1e-7 * max(1.0, abs(fd))
