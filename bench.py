@@ -531,6 +531,9 @@ SWEEP = [
     ("ablation_no_slots", "headline", {"m": 0}, 512, True, 0),
     # ablation: no token shift (every token enters the slots at its own step)
     ("ablation_no_token_shift", "headline", {}, 512, True, 0),
+    # ablation: weighted fusion (separate slot and window softmaxes mixed by a
+    # per-token coefficient, with its gradient)
+    ("ablation_weighted_fusion", "headline", {}, 512, True, 0),
 ]
 # The operator benchmark shape the pages describe (NHA with m = 32 slots and
 # w = 32 against a 64-slot gated-slot model and full attention, over the
@@ -568,6 +571,22 @@ def sweep_point(label, wl, w, with_bwd, ndec, steps, warmup):
     def bwd():
         nha.bwd(qd, kd, vd, ad, o, lse, dOd, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=grads,
                 after_fwd=True, token_shift=shift)
+
+    if label == "ablation_weighted_fusion":
+        from softmax_attention_nha_amd.inputs import make_lam
+
+        lam = make_lam(wl).to(dev)
+        ws = torch.empty(nha.weighted_workspace_size(desc), dtype=torch.uint8, device=dev)
+        lse2 = torch.empty((2, wl.B, wl.H, T), dtype=torch.float32, device=dev)
+        wgrads = grads + (torch.empty((wl.B, T, wl.H), dtype=torch.float32, device=dev),)
+
+        def fwd():  # noqa: F811 -- the ablation's own calls
+            nha.fwd_weighted(qd, kd, vd, ad, lam, w, C=wl.C, rope_base=wl.rope_base, workspace=ws, out=o,
+                             lse_out=lse2)
+
+        def bwd():  # noqa: F811 -- recomputes both reads, then the gradients incl. dlam
+            nha.bwd_weighted(qd, kd, vd, ad, lam, dOd, w, C=wl.C, rope_base=wl.rope_base, workspace=ws,
+                             out=wgrads)
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     for _ in range(warmup):

@@ -241,6 +241,37 @@ nha_status nha_bwd_s0(const nha_desc* desc, const void* q, const void* k,
                       float* dalpha, float* ds0k, float* ds0v, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- weighted fusion (ablation)
+ * The variant the ai.info page's findings compare the method with ("Unified
+ * softmax beats weighted fusion": a fixed-coefficient weighted sum, and a
+ * learnable sequence-dependent coefficient) -- the separate-then-summed
+ * intra-layer fusion of the Paper-Notes page's 现有痛点 paragraph: the m slot
+ * logits and the window logits each get their OWN softmax, and per token t
+ * and query head h
+ *     o_t = lam_t o^slot_t + (1 - lam_t) o^window_t .
+ * Slots, token shift, RoPE and gates are exactly as in nha_fwd (no_token_shift
+ * applies too).  Needs m >= 1 and w >= 1 (else NHA_ERR_INVALID_ARG).
+ *   lam     device float [B][T][H], the coefficient of the slot read (a fixed
+ *           coefficient is a constant-filled tensor)
+ *   ws      device workspace of nha_weighted_workspace_size bytes, shared by
+ *           both calls (0 for an invalid descriptor or m = 0 or w = 0)
+ * nha_fwd_weighted writes o [B][T][H][d] (desc->dtype) and, when lse2 is not
+ *   NULL, lse2 [2][B][H][T] float: the slot softmax's lse, then the window's.
+ * nha_bwd_weighted recomputes both reads and writes dq, dk, dv, dalpha as
+ *   nha_bwd does, and dlam [B][T][H] float (= <dO_t, o^slot_t - o^window_t>;
+ *   NULL: not wanted, e.g. a fixed coefficient).  Other errors as nha_fwd /
+ *   nha_bwd. */
+size_t nha_weighted_workspace_size(const nha_desc* desc);
+nha_status nha_fwd_weighted(const nha_desc* desc, const void* q, const void* k,
+                            const void* v, const void* alpha, const float* lam,
+                            void* o, float* lse2, void* ws, size_t ws_bytes,
+                            void* stream);
+nha_status nha_bwd_weighted(const nha_desc* desc, const void* q, const void* k,
+                            const void* v, const void* alpha, const float* lam,
+                            const void* dO, void* dq, void* dk, void* dv,
+                            float* dalpha, float* dlam, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- timing
  * Kernel launches that one nha_fwd (backward = 0), nha_bwd (backward = 1) or
  * nha_bwd_after_fwd (backward = 2) call enqueues for this descriptor

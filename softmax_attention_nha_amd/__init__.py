@@ -41,6 +41,9 @@ EXPORTED = (
     "nha_bwd_s0",
     "nha_release_side_streams",
     "nha_fwd_noalloc",
+    "nha_weighted_workspace_size",
+    "nha_fwd_weighted",
+    "nha_bwd_weighted",
 )
 
 
@@ -114,6 +117,12 @@ def load():
     lib.nha_bwd_s0.restype = st
     lib.nha_fwd_noalloc.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.nha_fwd_noalloc.restype = st
+    lib.nha_weighted_workspace_size.argtypes = [D]
+    lib.nha_weighted_workspace_size.restype = sz
+    lib.nha_fwd_weighted.argtypes = [D] + [vp] * 8 + [sz, vp]
+    lib.nha_fwd_weighted.restype = st
+    lib.nha_bwd_weighted.argtypes = [D] + [vp] * 12 + [sz, vp]
+    lib.nha_bwd_weighted.restype = st
     lib.nha_release_side_streams.argtypes = []
     lib.nha_release_side_streams.restype = st
     lib.nha_status_string.argtypes = [st]
@@ -365,6 +374,83 @@ def release_side_streams():
     rc = load().nha_release_side_streams()
     if rc != NHA_OK:
         raise NhaError(rc, "nha_release_side_streams")
+
+
+def weighted_workspace_size(desc):
+    lib = load()
+    n = lib.nha_weighted_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        rc = lib.nha_check_desc(ctypes.byref(desc))
+        raise NhaError(rc if rc != NHA_OK else NHA_ERR_INVALID_ARG, "weighted workspace size")
+    return n
+
+
+def _check_lam(lam, B, T, H, dev):
+    _check(lam, "lam", (B, T, H), torch.float32, dev)
+
+
+def fwd_weighted(q, k, v, alpha, lam, w, C=64, rope_base=10000.0, scale=0.0, workspace=None, out=None,
+                 lse_out=None, token_shift=True):
+    """The weighted-fusion ablation (nha_fwd_weighted): separate slot and
+    window softmaxes, o = lam o_slot + (1 - lam) o_window with lam float32
+    [B,T,H].  Returns (o, lse2) with lse2 [2,B,H,T] (slot, window)."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale, token_shift)
+    dev, dt = q.device, q.dtype
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    for t, nm, shp in ((q, "q", (B, T, H, d)), (k, "k", (B, T, Hkv, d)), (v, "v", (B, T, Hkv, d)),
+                       (alpha, "alpha", (B, T, Hkv, m))):
+        _check(t, nm, shp, dt, dev)
+    _check_lam(lam, B, T, H, dev)
+    if out is not None:
+        _check(out, "out", (B, T, H, d), dt, dev)
+    if lse_out is not None:
+        _check(lse_out, "lse_out", (2, B, H, T), torch.float32, dev)
+    lib = load()
+    o = torch.empty_like(q) if out is None else out
+    lse2 = torch.empty((2, B, H, T), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    ws = _workspace(workspace, weighted_workspace_size(desc), dev)
+    rc = lib.nha_fwd_weighted(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(lam), _ptr(o),
+                              _ptr(lse2), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_fwd_weighted")
+    return o, lse2
+
+
+def bwd_weighted(q, k, v, alpha, lam, dO, w, C=64, rope_base=10000.0, scale=0.0, workspace=None, out=None,
+                 want_dlam=True, token_shift=True):
+    """Gradients of fwd_weighted: (dq, dk, dv, dalpha, dlam) -- dlam float32
+    [B,T,H], or None with want_dlam=False (a fixed coefficient)."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale, token_shift)
+    dev, dt = q.device, q.dtype
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    for t, nm, shp in ((q, "q", (B, T, H, d)), (k, "k", (B, T, Hkv, d)), (v, "v", (B, T, Hkv, d)),
+                       (alpha, "alpha", (B, T, Hkv, m)), (dO, "dO", (B, T, H, d))):
+        _check(t, nm, shp, dt, dev)
+    _check_lam(lam, B, T, H, dev)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        da = torch.empty((B, T, Hkv, m), dtype=torch.float32, device=dev)
+        dlam = torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_dlam else None
+    else:
+        if len(out) != 5:
+            raise ValueError("out must be (dq, dk, dv, dalpha, dlam or None)")
+        dq, dk, dv, da, dlam = out
+        _check(dq, "dq", (B, T, H, d), dt, dev)
+        _check(dk, "dk", (B, T, Hkv, d), dt, dev)
+        _check(dv, "dv", (B, T, Hkv, d), dt, dev)
+        _check(da, "dalpha", (B, T, Hkv, m), torch.float32, dev)
+        if dlam is not None:
+            _check(dlam, "dlam", (B, T, H), torch.float32, dev)
+    lib = load()
+    ws = _workspace(workspace, weighted_workspace_size(desc), dev)
+    rc = lib.nha_bwd_weighted(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(lam), _ptr(dO),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(dlam), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_bwd_weighted")
+    return dq, dk, dv, da, dlam
 
 
 def decode_state(B, H, Hkv, d, m, w, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16, device="cuda"):

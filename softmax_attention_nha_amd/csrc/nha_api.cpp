@@ -201,6 +201,50 @@ nha_status nha_fwd_noalloc(const nha_desc* desc, const void* q, const void* k, c
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
 }
 
+size_t nha_weighted_workspace_size(const nha_desc* desc) {
+  Shape s;
+  if (make_shape(desc, true, &s) != NHA_OK || s.m < 1 || s.w < 1) return 0;
+  if (slot_bwd_lds_bytes(s) > kMaxLds) return 0;
+  return weighted_ws_bytes(s);
+}
+
+nha_status nha_fwd_weighted(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                            const float* lam, void* o, float* lse2, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  nha_status rc = make_shape(desc, true, &s);
+  if (rc != NHA_OK) return rc;
+  if (s.m < 1 || s.w < 1) return NHA_ERR_INVALID_ARG;  // both softmaxes need keys
+  if (!q || !k || !v || !alpha || !lam || !o || !ws) return NHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, alpha, lam, o, ws};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
+  if (lse2 && !aligned16(lse2)) return NHA_ERR_INVALID_ARG;
+  if (slot_bwd_lds_bytes(s) > kMaxLds) return NHA_ERR_UNSUPPORTED;
+  if (ws_bytes < weighted_ws_bytes(s)) return NHA_ERR_WORKSPACE;
+  WeightedPtrs p{q, k, v, alpha, lam, o, lse2, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, (char*)ws};
+  hipError_t e = launch_fwd_weighted(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+nha_status nha_bwd_weighted(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
+                            const float* lam, const void* dO, void* dq, void* dk, void* dv, float* dalpha,
+                            float* dlam, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  nha_status rc = make_shape(desc, true, &s);
+  if (rc != NHA_OK) return rc;
+  if (s.m < 1 || s.w < 1) return NHA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !alpha || !lam || !dO || !dq || !dk || !dv || !dalpha || !ws) return NHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, alpha, lam, dO, dq, dk, dv, dalpha, ws};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
+  if (dlam && !aligned16(dlam)) return NHA_ERR_INVALID_ARG;
+  if (slot_bwd_lds_bytes(s) > kMaxLds) return NHA_ERR_UNSUPPORTED;
+  if (ws_bytes < weighted_ws_bytes(s)) return NHA_ERR_WORKSPACE;
+  WeightedPtrs p{q, k, v, alpha, lam, nullptr, nullptr, dO, dq, dk, dv, dalpha, dlam, (char*)ws};
+  hipError_t e = launch_bwd_weighted(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
 nha_status nha_fwd_s0(const nha_desc* desc, const void* q, const void* k, const void* v, const void* alpha,
                       const float* s0k, const float* s0v, void* o, float* lse, void* state_out, void* ws,
                       size_t ws_bytes, void* stream) {

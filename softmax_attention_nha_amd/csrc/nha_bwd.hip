@@ -1821,6 +1821,11 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
     float* Dt = (float*)(ws + L.dt);
+    // the window kernels' dO, lse and D_t: the unified softmax's, or (weighted
+    // fusion) the window branch's own
+    const T* dOw = p.win_dO ? (const T*)p.win_dO : dO;
+    const float* lsew = p.win_lse ? p.win_lse : p.lse;
+    const float* Dw = p.win_D ? p.win_D : Dt;
     T* dqs = (T*)(ws + L.dqs);
     T* wpb = (T*)(ws + L.wp);
     float* sdl = (float*)(ws + L.sdl);
@@ -1893,10 +1898,10 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     if constexpr (sizeof(T) == 2) {
       constexpr int NWV = 4;
       const unsigned nt = (unsigned)((s.T + 32 * NWV - 1) / (32 * NWV));
-      hipLaunchKernelGGL((k_win_bwd_dq_b16<D, NWV>), dim3(nt, s.B * s.H), dim3(NWV * 64), 0, sq, qr, kr, v, dO,
-                         p.lse, Dt, dqs, (const float2*)pp.rcs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale);
+      hipLaunchKernelGGL((k_win_bwd_dq_b16<D, NWV>), dim3(nt, s.B * s.H), dim3(NWV * 64), 0, sq, qr, kr, v, dOw,
+                         lsew, Dw, dqs, (const float2*)pp.rcs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale);
     } else {
-      hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, sq, qr, kr, v, dO, p.lse, Dt,
+      hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, sq, qr, kr, v, dOw, lsew, Dw,
                          dqs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
     }
     fk.join(st);
@@ -1912,11 +1917,11 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     if constexpr (sizeof(T) == 2) {
       constexpr int NWV = 4;
       const unsigned nt = (unsigned)((s.T + 32 * NWV - 1) / (32 * NWV));
-      hipLaunchKernelGGL((k_win_bwd_dkdv_b16<D, NWV>), dim3(nt, units), dim3(NWV * 64), 0, st, qr, kr, v, dO, p.lse,
-                         Dt, dkap, dnu, (const float2*)pp.rcs, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.sh,
+      hipLaunchKernelGGL((k_win_bwd_dkdv_b16<D, NWV>), dim3(nt, units), dim3(NWV * 64), 0, st, qr, kr, v, dOw, lsew,
+                         Dw, dkap, dnu, (const float2*)pp.rcs, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.sh,
                          s.scale);
     } else {
-      hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dO, p.lse, Dt, dkap,
+      hipLaunchKernelGGL((k_win_bwd_dkdv<T, D>), dim3(s.NQ, units), dim3(256), 0, st, qr, kr, v, dOw, lsew, Dw, dkap,
                          dnu, (T*)p.dk, (T*)p.dv, s.T, s.H, s.Hkv, s.w, s.sh, s.scale, th, s.rope ? 1 : 0);
     }
     fk.join(st);

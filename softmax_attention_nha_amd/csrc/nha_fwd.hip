@@ -1156,8 +1156,8 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     const T* k = (const T*)p.k;
     const T* v = (const T*)p.v;
     const T* alpha = (const T*)p.alpha;
-    T* ol = (T*)(p.ws + L.ol);
-    float* lsel = (float*)(p.ws + L.lsel);
+    T* ol = p.ol_dst ? (T*)p.ol_dst : (T*)(p.ws + L.ol);
+    float* lsel = p.lsel_dst ? p.lsel_dst : (float*)(p.ws + L.lsel);
     const int units = s.B * s.Hkv;
     Marks mk;
     mk.ev = p.events;
@@ -1189,7 +1189,8 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
         hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
                            (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.sh, s.NC, nitems, s.scale);
       }
-    } else {
+    }
+    if (s.m == 0 || p.separate) {
       ol = nullptr;  // the window kernel starts from an empty softmax
       lsel = nullptr;
     }

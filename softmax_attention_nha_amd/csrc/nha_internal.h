@@ -209,6 +209,13 @@ struct FwdPtrs {
   const float* s0k = nullptr;  // initial slot states [B*Hkv][m][d], nullable = zero
   const float* s0v = nullptr;
   bool one_stream = false;      // every launch on the caller's stream (no side stream)
+  // weighted-fusion ablation: the window branch starts from an empty softmax
+  // (its own) instead of the slot partial and writes its own normalised read
+  // to o and its lse to lse; the slot partial o_L / Z_L and its lse go to
+  // ol_dst / lsel_dst (null: the workspace)
+  bool separate = false;
+  void* ol_dst = nullptr;
+  float* lsel_dst = nullptr;
 };
 hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hipStream_t st);
 
@@ -232,6 +239,11 @@ struct BwdPtrs {
   const float* s0v = nullptr;
   float* ds0k = nullptr;  // their gradients, nullable
   float* ds0v = nullptr;
+  // weighted-fusion ablation: the window kernels' own dO, lse and D_t (null:
+  // the slot kernels' dO, lse and D_t, i.e. the unified softmax)
+  const void* win_dO = nullptr;
+  const float* win_lse = nullptr;
+  const float* win_D = nullptr;
 };
 hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hipStream_t st);
 
@@ -240,6 +252,23 @@ hipError_t launch_bwd(const Shape& s, const RopeTheta& th, const BwdPtrs& p, hip
 // size in bytes.
 constexpr size_t kNoallocScratchBytes = NHA_NOALLOC_SCRATCH_BYTES;
 hipError_t noalloc_scratch(void** ptr);
+
+// Weighted-fusion ablation (separate slot and window softmaxes mixed by a
+// per-(token, head) coefficient lam [B][T][H] fp32).
+size_t weighted_ws_bytes(const Shape& s);
+struct WeightedPtrs {
+  const void *q, *k, *v, *alpha;
+  const float* lam;
+  void* o;       // forward output (nullable in the backward)
+  float* lse2;   // forward: nullable [2][B][H][T] (slot lse, window lse)
+  const void* dO;  // backward
+  void *dq, *dk, *dv;
+  float* dalpha;
+  float* dlam;   // nullable
+  char* ws;
+};
+hipError_t launch_fwd_weighted(const Shape& s, const RopeTheta& th, const WeightedPtrs& p, hipStream_t st);
+hipError_t launch_bwd_weighted(const Shape& s, const RopeTheta& th, const WeightedPtrs& p, hipStream_t st);
 
 // LDS bytes the largest forward / backward kernel needs for this shape.
 size_t slot_fwd_lds_bytes(const Shape& s);

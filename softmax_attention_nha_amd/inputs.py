@@ -96,3 +96,11 @@ def make_initial_state(wl: Workload, seed_offset=1000):
     s0k = torch.randn(shp, generator=g, dtype=torch.float32) / wl.d ** 0.5
     s0v = torch.randn(shp, generator=g, dtype=torch.float32) / wl.d ** 0.5
     return s0k.contiguous(), s0v.contiguous()
+
+
+def make_lam(wl: Workload, T_total=None, seed_offset=2000):
+    """Fusion coefficients for the weighted-fusion ablation: float32 [B, T, H],
+    sigmoid(N(0, 1)) per (token, head), from their own seeded generator."""
+    T = wl.T if T_total is None else T_total
+    g = torch.Generator(device="cpu").manual_seed(wl.seed + seed_offset)
+    return torch.sigmoid(torch.randn((wl.B, T, wl.H), generator=g, dtype=torch.float32)).contiguous()

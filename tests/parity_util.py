@@ -67,7 +67,7 @@ def _per_head(x, b, heads):
     return np.ascontiguousarray(f64(x[b, :, heads[0]:heads[-1] + 1]).transpose(1, 0, 2)[:, :, None, :])
 
 
-def oracle_units(q, k, v, a, dO, w, base, units, G, Tp=None):
+def oracle_units(q, k, v, a, dO, w, base, units, G, Tp=None, lam=None):
     """The fp64 oracle on the (b, g) units listed, with every query head of a
     unit run as a sequence of its own over its KV head (the operator is
     grouped-query attention: a query head reads only its KV head, and the
@@ -75,12 +75,16 @@ def oracle_units(q, k, v, a, dO, w, base, units, G, Tp=None):
     of the per-head gradients -- the GQA invariant the oracle pins check).
     The oracle's threads then cover every (unit, query head).  Tp: first Tp
     tokens only (forward: rows t < Tp depend on tokens <= t only).
+    lam: [B,T,H] coefficients of the weighted-fusion ablation (then lse is
+    [2,1,G,T] and the gradients end with dlam [1,T,G]).
     Returns per unit: (o [1,T,G,d], lse [1,G,T]) when dO is None, else
     (dq [1,T,G,d], dk, dv [1,T,1,d], dalpha [1,T,1,m])."""
-    qs, ks, vs, as_, ds = [], [], [], [], []
+    qs, ks, vs, as_, ds, ls = [], [], [], [], [], []
     for (b, g) in units:
         hq = list(range(g * G, (g + 1) * G))
         qs.append(_per_head(q, b, hq))
+        if lam is not None:
+            ls.append(np.ascontiguousarray(f64(lam[b, :, g * G:(g + 1) * G]).T[:, :, None]))
         rep = lambda x: np.repeat(_per_head(x, b, [g]), G, axis=0)
         ks.append(rep(k))
         vs.append(rep(v))
@@ -88,18 +92,28 @@ def oracle_units(q, k, v, a, dO, w, base, units, G, Tp=None):
         if dO is not None:
             ds.append(_per_head(dO, b, hq))
     cut = lambda xs: np.ascontiguousarray(np.concatenate(xs)[:, :Tp] if Tp else np.concatenate(xs))
+    lm = cut(ls)[..., 0] if lam is not None else None  # [units*G, T, 1] -> [units*G, T]
+    if lm is not None:
+        lm = lm[:, :, None]
     if dO is None:
-        o, lse = oracle.fwd(cut(qs), cut(ks), cut(vs), cut(as_), w, rope_base=base)
+        o, lse = oracle.fwd(cut(qs), cut(ks), cut(vs), cut(as_), w, rope_base=base, lam=lm)
         out = []
         for i in range(len(units)):
             oo = o[i * G:(i + 1) * G, :, 0].transpose(1, 0, 2)[None]
-            ll = lse[i * G:(i + 1) * G, 0][None]
+            if lam is None:
+                ll = lse[i * G:(i + 1) * G, 0][None]
+            else:
+                ll = lse[:, i * G:(i + 1) * G, 0][:, None]
             out.append((oo, ll))
         return out
-    dq, dk, dv, da = oracle.bwd(cut(qs), cut(ks), cut(vs), cut(as_), cut(ds), w, rope_base=base)
+    r = oracle.bwd(cut(qs), cut(ks), cut(vs), cut(as_), cut(ds), w, rope_base=base, lam=lm)
+    dq, dk, dv, da = r[:4]
     out = []
     for i in range(len(units)):
         s = slice(i * G, (i + 1) * G)
-        out.append((dq[s, :, 0].transpose(1, 0, 2)[None], dk[s].sum(0, keepdims=True),
-                    dv[s].sum(0, keepdims=True), da[s].sum(0, keepdims=True)))
+        one = (dq[s, :, 0].transpose(1, 0, 2)[None], dk[s].sum(0, keepdims=True),
+               dv[s].sum(0, keepdims=True), da[s].sum(0, keepdims=True))
+        if lam is not None:
+            one += (r[4][s, :, 0].T[None],)
+        out.append(one)
     return out

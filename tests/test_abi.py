@@ -243,3 +243,26 @@ def test_binding_decode_step_checks_every_tensor():
         nha.decode_step(q, k, k, a, state[: n - 8], w)
     with pytest.raises(ValueError, match="state"):
         nha.decode_step(q, k, k, a, torch.zeros(n, dtype=torch.int8), w)
+
+
+def test_weighted_fusion_argument_errors():
+    lib = nha.load()
+    big = ctypes.c_size_t(1 << 40)
+    d = desc()
+    n = lib.nha_weighted_workspace_size(ctypes.byref(d))
+    assert n >= max(nha.workspace_size(d), nha.workspace_size(d, backward=True))
+    for bad in (desc(m=0, w=8), desc(w=0), desc(H=3)):  # both softmaxes need keys; invalid shape
+        assert lib.nha_weighted_workspace_size(ctypes.byref(bad)) == 0
+        assert lib.nha_fwd_weighted(ctypes.byref(bad), A, A, A, A, A, A, None, A, big, None) == nha.NHA_ERR_INVALID_ARG
+    # nha_fwd_weighted(desc, q, k, v, alpha, lam, o, lse2, ws, ws_bytes, stream)
+    assert lib.nha_fwd_weighted(ctypes.byref(d), A, A, A, A, None, A, None, A, big, None) == nha.NHA_ERR_INVALID_ARG
+    assert lib.nha_fwd_weighted(ctypes.byref(d), A, A, A, A, MIS, A, None, A, big, None) == nha.NHA_ERR_INVALID_ARG
+    assert lib.nha_fwd_weighted(ctypes.byref(d), A, A, A, A, A, A, None, A, ctypes.c_size_t(n - 1),
+                                None) == nha.NHA_ERR_WORKSPACE
+    # nha_bwd_weighted(desc, q, k, v, alpha, lam, dO, dq, dk, dv, dalpha, dlam, ws, ws_bytes, stream)
+    args = [A] * 10
+    assert lib.nha_bwd_weighted(ctypes.byref(d), *args[:4], None, *args[5:10], None, A, big,
+                                None) == nha.NHA_ERR_INVALID_ARG
+    assert lib.nha_bwd_weighted(ctypes.byref(d), *args, MIS, A, big, None) == nha.NHA_ERR_INVALID_ARG
+    assert lib.nha_bwd_weighted(ctypes.byref(d), *args, None, A, ctypes.c_size_t(n - 1),
+                                None) == nha.NHA_ERR_WORKSPACE

@@ -172,3 +172,17 @@ def test_side_stream_results_equal_one_stream_results():
         res.append((o, lse) + tuple(g))
     for x, y in zip(*res):
         assert torch.equal(x, y)
+
+
+def test_release_side_streams_then_call_again():
+    # the production calls create the thread's side stream on first use;
+    # releasing it and calling again recreates it, with the same results
+    wl = WORKLOADS["340m"].with_(B=1, T=200, H=4, Hkv=2, seed=62)
+    q, k, v, a, dO = make_inputs(wl, with_grad=True)
+    log("case release side streams")
+    r1 = gpu_fwd_bwd(q, k, v, a, dO, 64, 64, 10000.0)
+    nha.release_side_streams()
+    nha.release_side_streams()  # nothing left: a no-op
+    r2 = gpu_fwd_bwd(q, k, v, a, dO, 64, 64, 10000.0)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
