@@ -241,6 +241,46 @@ nha_status nha_bwd_s0(const nha_desc* desc, const void* q, const void* k,
                       float* dalpha, float* ds0k, float* ds0v, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- chunked prefill
+ * A segment of desc->T tokens that continues a decode state -- the state
+ * nha_fwd(state_out), nha_decode_step or a previous segment left after pos0
+ * tokens: its slot states, its ring of the last w keys and values, and the
+ * absorptions those ring tokens still owe (the ai.info page, "Future
+ * Directions", item 1: context carried across segments in the slot states).
+ * nha_fwd over the whole sequence and nha_fwd_continue over its pieces give
+ * the same o and lse up to rounding.
+ *   pos0      tokens the state has consumed (its position counter; all
+ *             (batch, KV head) units equal).  The library does not read the
+ *             counter back: pass the value the state holds.
+ *   state_in  device decode state (layout: nha_decode_state_size) -- read
+ *             only; its slots SK, SV, ring RK, RV are used (RKR and the
+ *             scratch part are not)
+ *   state_out nullable; receives the state after the segment (pos0 + T
+ *             tokens); may be state_in itself
+ *   ws        device workspace of nha_continue_workspace_size bytes (serves
+ *             both calls and every pos0)
+ * nha_bwd_continue: gradients of the segment's loss w.r.t. its inputs (dq,
+ *   dk, dv, dalpha as nha_bwd), w.r.t. the state's slots (ds0k, ds0v float
+ *   [B][Hkv][m][d]) and, nullable, w.r.t. its ring keys and values (drk, drv
+ *   dtype [B][Hkv][w][d] in ring layout; rows holding no token are zero).  o
+ *   and lse are the segment's forward outputs; state_in is the state the
+ *   forward started from (keep a copy if the forward overwrote it).
+ * The token-shift ablation (no_token_shift = 1) returns NHA_ERR_UNSUPPORTED;
+ * pos0 < 0 returns NHA_ERR_INVALID_ARG; other errors as nha_fwd / nha_bwd. */
+size_t nha_continue_workspace_size(const nha_desc* desc);
+nha_status nha_fwd_continue(const nha_desc* desc, long long pos0,
+                            const void* state_in, const void* q,
+                            const void* k, const void* v, const void* alpha,
+                            void* o, float* lse, void* state_out, void* ws,
+                            size_t ws_bytes, void* stream);
+nha_status nha_bwd_continue(const nha_desc* desc, long long pos0,
+                            const void* state_in, const void* q,
+                            const void* k, const void* v, const void* alpha,
+                            const void* o, const float* lse, const void* dO,
+                            void* dq, void* dk, void* dv, float* dalpha,
+                            float* ds0k, float* ds0v, void* drk, void* drv,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- weighted fusion (ablation)
  * The variant the ai.info page's findings compare the method with ("Unified
  * softmax beats weighted fusion": a fixed-coefficient weighted sum, and a

@@ -44,6 +44,9 @@ EXPORTED = (
     "nha_weighted_workspace_size",
     "nha_fwd_weighted",
     "nha_bwd_weighted",
+    "nha_continue_workspace_size",
+    "nha_fwd_continue",
+    "nha_bwd_continue",
 )
 
 
@@ -123,6 +126,13 @@ def load():
     lib.nha_fwd_weighted.restype = st
     lib.nha_bwd_weighted.argtypes = [D] + [vp] * 12 + [sz, vp]
     lib.nha_bwd_weighted.restype = st
+    ll = ctypes.c_longlong
+    lib.nha_continue_workspace_size.argtypes = [D]
+    lib.nha_continue_workspace_size.restype = sz
+    lib.nha_fwd_continue.argtypes = [D, ll] + [vp] * 9 + [sz, vp]
+    lib.nha_fwd_continue.restype = st
+    lib.nha_bwd_continue.argtypes = [D, ll] + [vp] * 17 + [sz, vp]
+    lib.nha_bwd_continue.restype = st
     lib.nha_release_side_streams.argtypes = []
     lib.nha_release_side_streams.restype = st
     lib.nha_status_string.argtypes = [st]
@@ -451,6 +461,79 @@ def bwd_weighted(q, k, v, alpha, lam, dO, w, C=64, rope_base=10000.0, scale=0.0,
     if rc != NHA_OK:
         raise NhaError(rc, "nha_bwd_weighted")
     return dq, dk, dv, da, dlam
+
+
+def continue_workspace_size(desc):
+    lib = load()
+    n = lib.nha_continue_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        rc = lib.nha_check_desc(ctypes.byref(desc))
+        raise NhaError(rc if rc != NHA_OK else NHA_ERR_UNSUPPORTED, "continue workspace size")
+    return n
+
+
+def fwd_continue(q, k, v, alpha, w, state_in, pos0, C=64, rope_base=10000.0, scale=0.0, state_out=None,
+                 workspace=None, out=None, lse_out=None):
+    """Chunked prefill (nha_fwd_continue): the forward over a segment that
+    continues `state_in` (a decode state after pos0 tokens).  state_out may be
+    state_in itself.  Returns (o, lse) of the segment."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
+    dev, dt = q.device, q.dtype
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    for t, nm, shp in ((q, "q", (B, T, H, d)), (k, "k", (B, T, Hkv, d)), (v, "v", (B, T, Hkv, d)),
+                       (alpha, "alpha", (B, T, Hkv, m))):
+        _check(t, nm, shp, dt, dev)
+    n_state = decode_state_size(desc)
+    _check_bytes(state_in, "state_in", n_state, dev)
+    if state_out is not None:
+        _check_bytes(state_out, "state_out", n_state, dev)
+    if out is not None:
+        _check(out, "out", (B, T, H, d), dt, dev)
+    if lse_out is not None:
+        _check(lse_out, "lse_out", (B, H, T), torch.float32, dev)
+    lib = load()
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    ws = _workspace(workspace, continue_workspace_size(desc), dev)
+    rc = lib.nha_fwd_continue(ctypes.byref(desc), ctypes.c_longlong(int(pos0)), _ptr(state_in), _ptr(q), _ptr(k),
+                              _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(state_out), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_fwd_continue")
+    return o, lse
+
+
+def bwd_continue(q, k, v, alpha, o, lse, dO, w, state_in, pos0, C=64, rope_base=10000.0, scale=0.0,
+                 workspace=None, want_ring=True):
+    """Gradients of fwd_continue: (dq, dk, dv, dalpha, dS0K, dS0V, dRK, dRV) --
+    the last four w.r.t. the state it continued (slots float32 [B,Hkv,m,d];
+    ring keys / values in the state's ring layout [B,Hkv,w,d], None with
+    want_ring=False)."""
+    desc = _desc_from(q, k, alpha, w, C, rope_base, scale)
+    dev, dt = q.device, q.dtype
+    B, T, H, d = q.shape
+    Hkv, m = k.shape[2], alpha.shape[3]
+    for t, nm, shp in ((q, "q", (B, T, H, d)), (k, "k", (B, T, Hkv, d)), (v, "v", (B, T, Hkv, d)),
+                       (alpha, "alpha", (B, T, Hkv, m)), (o, "o", (B, T, H, d)), (dO, "dO", (B, T, H, d))):
+        _check(t, nm, shp, dt, dev)
+    _check(lse, "lse", (B, H, T), torch.float32, dev)
+    _check_bytes(state_in, "state_in", decode_state_size(desc), dev)
+    lib = load()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da = torch.empty((B, T, Hkv, m), dtype=torch.float32, device=dev)
+    ds0k = torch.empty((B, Hkv, m, d), dtype=torch.float32, device=dev)
+    ds0v = torch.empty_like(ds0k)
+    drk = torch.empty((B, Hkv, w, d), dtype=dt, device=dev) if want_ring and w > 0 else None
+    drv = torch.empty_like(drk) if drk is not None else None
+    ws = _workspace(workspace, continue_workspace_size(desc), dev)
+    rc = lib.nha_bwd_continue(ctypes.byref(desc), ctypes.c_longlong(int(pos0)), _ptr(state_in), _ptr(q), _ptr(k),
+                              _ptr(v), _ptr(alpha), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                              _ptr(da), _ptr(ds0k), _ptr(ds0v), _ptr(drk), _ptr(drv), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != NHA_OK:
+        raise NhaError(rc, "nha_bwd_continue")
+    return dq, dk, dv, da, ds0k, ds0v, drk, drv
 
 
 def decode_state(B, H, Hkv, d, m, w, rope_base=10000.0, scale=0.0, dtype=torch.bfloat16, device="cuda"):

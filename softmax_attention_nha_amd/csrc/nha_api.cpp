@@ -59,7 +59,26 @@ RopeTheta make_theta(const nha_desc* d) {
   memset(&th, 0, sizeof(th));
   if (d->rope_base > 0.f)
     for (int i = 0; i < d->d / 2; ++i) th.theta[i] = pow((double)d->rope_base, -2.0 * i / d->d);
+  th.pos0 = 0;
   return th;
+}
+
+// Shapes of a continued segment: s (the segment), se (P = min(pos0, w) ring
+// rows prepended) and the RoPE position of extended row 0.
+nha_status cont_shapes(const nha_desc* desc, long long pos0, Shape* s, Shape* se, RopeTheta* th) {
+  nha_status rc = make_shape(desc, true, s);
+  if (rc != NHA_OK) return rc;
+  if (pos0 < 0 || pos0 > (1LL << 40)) return NHA_ERR_INVALID_ARG;
+  if (desc->no_token_shift) return NHA_ERR_UNSUPPORTED;
+  const long long P = pos0 < desc->w ? pos0 : desc->w;
+  if ((long long)desc->T + P > (1LL << 31) - 1) return NHA_ERR_UNSUPPORTED;
+  nha_desc de = *desc;
+  de.T = desc->T + (int)P;
+  rc = make_shape(&de, true, se);
+  if (rc != NHA_OK) return rc;
+  *th = make_theta(desc);
+  th->pos0 = pos0 - P;
+  return NHA_OK;
 }
 
 }  // namespace
@@ -242,6 +261,57 @@ nha_status nha_bwd_weighted(const nha_desc* desc, const void* q, const void* k, 
   if (ws_bytes < weighted_ws_bytes(s)) return NHA_ERR_WORKSPACE;
   WeightedPtrs p{q, k, v, alpha, lam, nullptr, nullptr, dO, dq, dk, dv, dalpha, dlam, (char*)ws};
   hipError_t e = launch_bwd_weighted(s, make_theta(desc), p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+size_t nha_continue_workspace_size(const nha_desc* desc) {
+  Shape s, se;
+  RopeTheta th;
+  if (cont_shapes(desc, desc ? desc->w : 0, &s, &se, &th) != NHA_OK) return 0;  // P = w: the largest
+  if (slot_bwd_lds_bytes(se) > kMaxLds) return 0;
+  const size_t f = cont_ws_bytes(se, false), b = cont_ws_bytes(se, true);
+  return f > b ? f : b;
+}
+
+nha_status nha_fwd_continue(const nha_desc* desc, long long pos0, const void* state_in, const void* q, const void* k,
+                            const void* v, const void* alpha, void* o, float* lse, void* state_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Shape s, se;
+  RopeTheta th;
+  nha_status rc = cont_shapes(desc, pos0, &s, &se, &th);
+  if (rc != NHA_OK) return rc;
+  if (!state_in || !q || !k || !v || (!alpha && s.m > 0) || !o || !ws) return NHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {state_in, q, k, v, alpha, o, ws};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
+  if ((lse && !aligned16(lse)) || (state_out && !aligned16(state_out))) return NHA_ERR_INVALID_ARG;
+  if (ws_bytes < cont_ws_bytes(se, false)) return NHA_ERR_WORKSPACE;
+  ContPtrs p{q, k, v, alpha, state_in, o, lse, state_out, nullptr, nullptr, nullptr, nullptr, nullptr,
+             nullptr, nullptr, nullptr, nullptr, (char*)ws};
+  hipError_t e = launch_fwd_continue(s, se, th, p, (hipStream_t)stream);
+  return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
+}
+
+nha_status nha_bwd_continue(const nha_desc* desc, long long pos0, const void* state_in, const void* q, const void* k,
+                            const void* v, const void* alpha, const void* o, const float* lse, const void* dO,
+                            void* dq, void* dk, void* dv, float* dalpha, float* ds0k, float* ds0v, void* drk,
+                            void* drv, void* ws, size_t ws_bytes, void* stream) {
+  Shape s, se;
+  RopeTheta th;
+  nha_status rc = cont_shapes(desc, pos0, &s, &se, &th);
+  if (rc != NHA_OK) return rc;
+  if (slot_bwd_lds_bytes(se) > kMaxLds) return NHA_ERR_UNSUPPORTED;
+  if (!state_in || !q || !k || !v || ((!alpha || !dalpha) && s.m > 0) || !o || !lse || !dO || !dq || !dk || !dv ||
+      !ds0k || !ds0v || !ws)
+    return NHA_ERR_INVALID_ARG;
+  const void* ptrs[] = {state_in, q, k, v, alpha, o, lse, dO, dq, dk, dv, dalpha, ds0k, ds0v, ws};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return NHA_ERR_INVALID_ARG;
+  if ((drk && !aligned16(drk)) || (drv && !aligned16(drv))) return NHA_ERR_INVALID_ARG;
+  if (ws_bytes < cont_ws_bytes(se, true)) return NHA_ERR_WORKSPACE;
+  ContPtrs p{q, k, v, alpha, state_in, (void*)o, (float*)lse, nullptr, dO, dq, dk, dv, dalpha, ds0k, ds0v,
+             drk, drv, (char*)ws};
+  hipError_t e = launch_bwd_continue(s, se, th, p, (hipStream_t)stream);
   return e == hipSuccess ? NHA_OK : NHA_ERR_HIP;
 }
 

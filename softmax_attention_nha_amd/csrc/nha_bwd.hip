@@ -1147,7 +1147,7 @@ struct WinBwdDqSmem {
   T kt[D * PK];
 };
 
-__device__ __forceinline__ void rope_cs(double theta, int pos, float& cs, float& sn) {
+__device__ __forceinline__ void rope_cs(double theta, long long pos, float& cs, float& sn) {
   double ang = (double)pos * theta;
   ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
   sincosf((float)ang, &sn, &cs);
@@ -1250,7 +1250,7 @@ __global__ __launch_bounds__(256) void k_win_bwd_dq(const T* __restrict__ qr, co
       for (int r = 0; r < 4; ++r) {
         int i = 16 * db + 4 * g + r;
         float x1 = acc[db][r] * scale, x2 = acc[db + HB][r] * scale, cs = 1.f, sn = 0.f;
-        if (rope) rope_cs(th.theta[i], tq, cs, sn);
+        if (rope) rope_cs(th.theta[i], th.pos0 + tq, cs, sn);
         out[db][r] = x1 * cs + x2 * sn;
         out[db + HB][r] = x2 * cs - x1 * sn;
       }
@@ -1569,7 +1569,7 @@ __global__ __launch_bounds__(256) void k_win_bwd_dkdv(
       for (int r = 0; r < 4; ++r) {
         int i = 16 * db + 4 * g + r;
         float x1 = adk[db][r] * scale, x2 = adk[db + HB][r] * scale, cs = 1.f, sn = 0.f;
-        if (rope) rope_cs(th.theta[i], key, cs, sn);
+        if (rope) rope_cs(th.theta[i], th.pos0 + key, cs, sn);
         ok[db][r] = x1 * cs + x2 * sn;
         ok[db + HB][r] = x2 * cs - x1 * sn;
       }

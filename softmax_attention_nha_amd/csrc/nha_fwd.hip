@@ -37,13 +37,13 @@
 namespace nha {
 
 // ---------------------------------------------------------------- RoPE
-// cs[t][i] = (cos, sin)(t theta_i) for t < T, i < d/2; the angle is reduced
-// modulo 2 pi in double precision before the single-precision sincos.
+// cs[t][i] = (cos, sin)((pos0 + t) theta_i) for t < T, i < d/2; the angle is
+// reduced modulo 2 pi in double precision before the single-precision sincos.
 __global__ __launch_bounds__(256) void k_rope_cs(float2* __restrict__ cs, int Tn, int half, RopeTheta th) {
   const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (long)Tn * half) return;
   const int t = (int)(e / half), i = (int)(e % half);
-  double ang = (double)t * th.theta[i];
+  double ang = (double)(th.pos0 + t) * th.theta[i];
   ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
   float sn, cn;
   sincosf((float)ang, &sn, &cn);
@@ -1088,23 +1088,25 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
 
 // ---------------------------------------------------------------- decode-state export
 // Ring rows for positions max(0, T-w) .. T-1 (raw keys, values and, with
-// RoPE, the RoPE'd keys the forward computed) and the position counter.
+// RoPE, the RoPE'd keys the forward computed) and the position counter; row j
+// of the sequence is absolute position pos0 + j (pos0 > 0 for a continued
+// segment).
 template <typename T>
 __global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ kr,
                                T* __restrict__ rk, T* __restrict__ rv, T* __restrict__ rkr,
-                               long long* __restrict__ pos, int Tn, int Hkv, int d, int w) {
+                               long long* __restrict__ pos, int Tn, int Hkv, int d, int w, long long pos0) {
   int unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv;
   int first = Tn - w > 0 ? Tn - w : 0;
   int nrows = w > 0 ? Tn - first : 0;
   for (int e = (blockIdx.x * blockDim.x + threadIdx.x) * 8; e < nrows * d; e += gridDim.x * blockDim.x * 8) {
     int j = first + e / d, x = e % d;
     size_t src = (((size_t)b * Tn + j) * Hkv + hg) * d + x;
-    size_t dst = ((size_t)unit * w + (j % w)) * d + x;
+    size_t dst = ((size_t)unit * w + (size_t)((pos0 + j) % w)) * d + x;
     st8<T>(rk + dst, ld8<T>(kk + src));
     st8<T>(rv + dst, ld8<T>(vv + src));
     if (kr) st8<T>(rkr + dst, ld8<T>(kr + src));
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) pos[unit] = Tn;
+  if (blockIdx.x == 0 && threadIdx.x == 0) pos[unit] = pos0 + Tn;
 }
 
 // ---------------------------------------------------------------- host launcher
@@ -1210,10 +1212,11 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       if (s.w > 0)
         hipLaunchKernelGGL(k_export_state<T>, dim3(32, units), dim3(256), 0, st, k, v,
                            s.rope ? (const T*)pp.krot : (const T*)nullptr, (T*)(base + SL.rk), (T*)(base + SL.rv),
-                           (T*)(base + SL.rkr), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w);
+                           (T*)(base + SL.rkr), (long long*)(base + SL.pos), s.T, s.Hkv, s.d, s.w, th.pos0);
       else
         hipLaunchKernelGGL(k_export_state<T>, dim3(1, units), dim3(64), 0, st, k, v, (const T*)nullptr,
-                           (T*)nullptr, (T*)nullptr, (T*)nullptr, (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0);
+                           (T*)nullptr, (T*)nullptr, (T*)nullptr, (long long*)(base + SL.pos), s.T, s.Hkv, s.d, 0,
+                           th.pos0);
     }
     mk.mark(st);
     return hipGetLastError();

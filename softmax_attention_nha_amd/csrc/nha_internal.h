@@ -8,9 +8,12 @@
 
 namespace nha {
 
-// RoPE frequencies theta_i = base^(-2i/d), computed on the host in double.
+// RoPE frequencies theta_i = base^(-2i/d), computed on the host in double,
+// and the position of row 0 of the sequence (0, or where a continued segment
+// starts): row t is rotated by (pos0 + t) theta_i.
 struct RopeTheta {
   double theta[64];
+  long long pos0;
 };
 
 // Problem shape after validation.
@@ -269,6 +272,28 @@ struct WeightedPtrs {
 };
 hipError_t launch_fwd_weighted(const Shape& s, const RopeTheta& th, const WeightedPtrs& p, hipStream_t st);
 hipError_t launch_bwd_weighted(const Shape& s, const RopeTheta& th, const WeightedPtrs& p, hipStream_t st);
+
+// Chunked prefill: a segment continuing a decode state.  s is the segment's
+// shape, se the extended shape (T + P rows: the P = min(pos0, w) ring tokens
+// first); th.pos0 = pos0 - P, the absolute position of extended row 0.
+struct ContPtrs {
+  const void *q, *k, *v, *alpha;
+  const void* state_in;
+  void* o;          // forward: output; backward: the forward's output (read)
+  float* lse;       // forward: nullable output; backward: the forward's lse (read)
+  void* state_out;  // forward, nullable
+  const void* dO;
+  void *dq, *dk, *dv;
+  float* dalpha;
+  float *ds0k, *ds0v;  // gradients of the state's slots, [B][Hkv][m][d]
+  void *drk, *drv;     // gradients of the state's ring keys / values, ring layout, nullable
+  char* ws;
+};
+size_t cont_ws_bytes(const Shape& se, bool bwd);
+hipError_t launch_fwd_continue(const Shape& s, const Shape& se, const RopeTheta& th, const ContPtrs& p,
+                               hipStream_t st);
+hipError_t launch_bwd_continue(const Shape& s, const Shape& se, const RopeTheta& th, const ContPtrs& p,
+                               hipStream_t st);
 
 // LDS bytes the largest forward / backward kernel needs for this shape.
 size_t slot_fwd_lds_bytes(const Shape& s);

@@ -553,3 +553,28 @@ def test_weighted_fusion_coefficient_gradient_matches_finite_differences():
         fm = (oracle.fwd(q, k, v, a, w, rope_base=50.0, lam=lm)[0] * dO).sum()
         fd = (fp - fm) / (2 * h)
         assert abs(fd - dlam[idx]) < 1e-7 * max(1.0, abs(fd))
+
+
+# ---------------------------------------------------------------- chunked prefill
+# A segment that continues the state after pos0 tokens is the whole-sequence
+# forward of [the P = min(pos0, w) window tokens; the segment] started from the
+# slot states at pos0 (the reduction the continued-segment calls implement):
+# its rows P.. equal the whole sequence's rows pos0.., and its final state the
+# whole sequence's.  RoPE positions: the oracle rotates row e by e, the whole
+# sequence by pos0 - P + e; logits depend on differences only.
+@pytest.mark.parametrize("w,pos0", [(4, 0), (4, 2), (4, 9), (6, 6), (0, 5), (30, 11)])
+def test_continued_segment_is_the_whole_sequence(w, pos0):
+    B, T, H, Hkv, d, m = 1, 20, 2, 1, 8, 3
+    q, k, v, a = rand_case(B, T, H, Hkv, d, m, seed=190 + w + pos0)
+    o, lse, sk, sv = oracle.fwd(q, k, v, a, w, rope_base=100.0, want_state=True)
+    _, _, s1k, s1v = oracle.fwd(q[:, :pos0], k[:, :pos0], v[:, :pos0], a[:, :pos0], w, rope_base=100.0,
+                                want_state=True)
+    P = min(pos0, w)
+    ext = lambda x, fill: np.concatenate([np.full_like(x[:, :P], fill) if fill is not None else x[:, pos0 - P:pos0],
+                                          x[:, pos0:]], axis=1)
+    qe, ke, ve, ae = ext(q, 0.0), ext(k, None), ext(v, None), ext(a, 1.0)
+    oe, le, ek, ev = oracle.fwd(qe, ke, ve, ae, w, rope_base=100.0, s0=(s1k, s1v), want_state=True)
+    np.testing.assert_allclose(oe[:, P:], o[:, pos0:], atol=1e-12)
+    np.testing.assert_allclose(le[:, :, P:], lse[:, :, pos0:], atol=1e-12)
+    np.testing.assert_allclose(ek, sk, atol=1e-13)
+    np.testing.assert_allclose(ev, sv, atol=1e-13)
