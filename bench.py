@@ -122,8 +122,10 @@ def stage_work(stage, wl, w, e):
         "chunk_gates": (0.0, a_b, units * NC * mp * (C * e + 4.0)),
         "state_scan": (flops_state(B, Hkv, T, d, m, w), 2.0 * B * Hkv * absorbed * d * e,
                        units * NC * (mp * C * e + 4.0 * mp + 2.0 * mp * d * e)),
-        "slot_fwd": (fs, q_b + 2 * kv_b + a_b, B * H * NC * 2.0 * mp * d * e + q_b + row),
-        "win_fwd": (fw, 2 * q_b + 2 * kv_b + row, q_b + row),
+        # the window branch runs first (into the workspace); the slot kernel
+        # merges it and writes o and lse
+        "slot_fwd": (fs, 2 * q_b + 2 * kv_b + a_b + row, B * H * NC * 2.0 * mp * d * e + (q_b + row if w else 0)),
+        "win_fwd": (fw, q_b + 2 * kv_b, q_b + row),
         "bwd_prep": (0.0, 2 * q_b + row, 0.0),
         "slot_bwd_a": (1.5 * fs, 3 * q_b + 2 * kv_b + a_b + 2 * row,
                        B * H * NC * (2.0 * mp * d * e + 2.0 * mp * C * e + 12.0 * C * mp) + q_b),

@@ -1329,21 +1329,31 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
     if (kmax > Tn - 1) kmax = Tn - 1;
     const int jfirst = (kmin / 64) * 64;
     const int ntiles = (kmax - jfirst) / 64 + 1;
+    // key tiles in a rotated order (step it takes the tile X = it mod
+    // ntiles): the workgroups of neighbouring query tiles, resident together
+    // on one XCD, then read each key tile at the same step, and all but the
+    // first hit the XCD's L2
+    const int rot = (ntiles - (jfirst / 64) % ntiles) % ntiles;
+    auto tile_j0 = [&](int it) {
+      const int jr = it + rot >= ntiles ? it + rot - ntiles : it + rot;
+      return jfirst + 64 * jr;
+    };
     const size_t ld = (size_t)Hkv * D;
     const bf16* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
     const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
     const uint32_t kl = lds_addr(&kbuf[0][0]), vl = lds_addr(&vbuf[0][0]);
     constexpr uint32_t TB = 64 * D * 2;
     const uint32_t ldo = dma_lane_off<D, NT, 2>(tid, ld);
-    dma_tile_async<D, NT, 2>(kbase, ld, jfirst, Tn, kl, ldo, tid);
-    dma_tile_async<D, NT, 2>(vbase, ld, jfirst, Tn, vl, ldo, tid);
+    dma_tile_async<D, NT, 2>(kbase, ld, tile_j0(0), Tn, kl, ldo, tid);
+    dma_tile_async<D, NT, 2>(vbase, ld, tile_j0(0), Tn, vl, ldo, tid);
     wait_vmem();
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
-      const int j0 = jfirst + 64 * it, cb = it & 1;
+      const int j0 = tile_j0(it), cb = it & 1;
       if (it + 1 < ntiles) {
-        dma_tile_async<D, NT, 2>(kbase, ld, j0 + 64, Tn, kl + (cb ^ 1) * TB, ldo, tid);
-        dma_tile_async<D, NT, 2>(vbase, ld, j0 + 64, Tn, vl + (cb ^ 1) * TB, ldo, tid);
+        const int jn = tile_j0(it + 1);
+        dma_tile_async<D, NT, 2>(kbase, ld, jn, Tn, kl + (cb ^ 1) * TB, ldo, tid);
+        dma_tile_async<D, NT, 2>(vbase, ld, jn, Tn, vl + (cb ^ 1) * TB, ldo, tid);
       }
       if (wl < Tn && j0 <= wl + 31 && j0 + 63 > wl - w) {
         const uint32_t kt = __builtin_amdgcn_readfirstlane(kl + cb * TB);
@@ -1647,13 +1657,23 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
   const int qfirst = (k0 / 64) * 64;
   const int ntiles = (w > 0 && k0 <= tmax) ? (tmax - qfirst) / 64 + 1 : 0;
   const int total = G * ntiles;
+  // query tiles in a rotated order: step j takes the tile X of the band with
+  // X = j (mod ntiles), so the workgroups of neighbouring key tiles (same
+  // XCD, same time) read each query tile at the same step and all but the
+  // first find it in L2 (in band order a tile came back only after every
+  // resident workgroup had streamed ~2 tiles, the size of the L2)
+  const int rot = ntiles > 0 ? (ntiles - (qfirst / 64) % ntiles) % ntiles : 0;
+  auto tile_q0 = [&](int jt) {
+    const int jr = jt + rot >= ntiles ? jt + rot - ntiles : jt + rot;
+    return qfirst + 64 * jr;
+  };
   if (total > 0) {
     const size_t ld = (size_t)H * D;
     const uint32_t ql = lds_addr(&qbuf[0][0]), ol = lds_addr(&obuf[0][0]);
     constexpr uint32_t TB = 64 * D * 2;
     const uint32_t ldo = dma_lane_off<D, NT, 3>(tid, ld);
     auto stage = [&](int n, int buf) {
-      const int hh = n / ntiles, q0 = qfirst + 64 * (n - hh * ntiles), h = hg * G + hh;
+      const int hh = n / ntiles, q0 = tile_q0(n - hh * ntiles), h = hg * G + hh;
       const size_t base = ((size_t)b * Tn * H + h) * D;
       dma_tile_async<D, NT, 3>(qr + base, ld, q0, Tn, ql + buf * TB, ldo, tid);
       dma_tile_async<D, NT, 3>(dO + base, ld, q0, Tn, ol + buf * TB, ldo, tid);
@@ -1670,7 +1690,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
     for (int n = 0; n < total; ++n) {
       const int cb = n & 1;
       if (n + 1 < total) stage(n + 1, cb ^ 1);
-      const int hh = n / ntiles, q0 = qfirst + 64 * (n - hh * ntiles);
+      const int hh = n / ntiles, q0 = tile_q0(n - hh * ntiles);
       const uint32_t qt = __builtin_amdgcn_readfirstlane(ql + cb * TB);
       const uint32_t ot = __builtin_amdgcn_readfirstlane(ol + cb * TB);
 #pragma unroll

@@ -404,6 +404,53 @@ __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ 
 }
 
 // ---------------------------------------------------------------- slot branch
+// The end of a slot-branch row: lane (g, cc) of a wave holds, for query row
+// tq, the unnormalised slot read accO (channels 16 db + 4 g .. + 3), its sum
+// zs and maximum mx (log2 units).  Without the window branch (o_w null) it
+// stores the normalised partial o_L / Z_L and lse_L; with it, the window
+// branch's normalised read o_W and lse_W (loaded by load(), early) are merged
+// as two partial softmaxes:  o = (Z_L o_L/Z_L + Z_W o_W/Z_W) / (Z_L + Z_W)
+// with Z = 2^{lse log2 e} referred to their common maximum, and lse = ln(Z_L
+// + Z_W).
+template <typename T, int D>
+struct WinPartial {
+  typename Vec<T>::v4 ow[D / 16];
+  float lw;
+  bool on;
+  __device__ __forceinline__ void load(const T* o_w, const float* lse_w, int b, int h, int row, int Tn, int H,
+                                       int g) {
+    on = o_w != nullptr;
+    if (!on) return;
+    const T* src = o_w + (((size_t)b * Tn + row) * H + h) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) ow[db] = ld4<T>(src + 16 * db);
+    lw = lse_w[((size_t)b * H + h) * Tn + row];
+  }
+  __device__ __forceinline__ void store(const floatx4 (&accO)[D / 16], float zs, float mx, T* out, float* lse_out,
+                                        int b, int h, int tq, int Tn, int H, int g) const {
+    T* dst = out + (((size_t)b * Tn + tq) * H + h) * D + 4 * g;
+    const float a = mx + __log2f(zs);  // slot lse, log2 units
+    if (!on) {
+      const float inv = 1.f / zs;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db, pack4<T>(accO[db] * inv));
+      if (g == 0 && lse_out) lse_out[((size_t)b * H + h) * Tn + tq] = a * NHA_LN2;
+      return;
+    }
+    const float bw = lw * NHA_LOG2E, M = fmaxf(a, bw);
+    const float wl = fast_exp2(a - M), ww = fast_exp2(bw - M), inv = 1.f / (wl + ww);
+    const float cl = wl * inv / zs, cw = ww * inv;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      floatx4 y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = accO[db][r] * cl + to_f<T>(ow[db][r]) * cw;
+      st4<T>(dst + 16 * db, pack4<T>(y));
+    }
+    if (g == 0 && lse_out) lse_out[((size_t)b * H + h) * Tn + tq] = (M + __log2f(wl + ww)) * NHA_LN2;
+  }
+};
+
 // grid (NC, B*H), C/16 waves; wave I owns chunk rows 16I .. 16I+15 (queries
 // are the N = 16 columns of every product).  Outputs the normalised slot
 // partial o_L / Z_L and lse_L = ln(sum_i exp(l_i)) over the m slot logits.
@@ -436,13 +483,15 @@ struct SlotFwdRegs {
 // grid: a persistent set of workgroups (about one per compute unit), C/16
 // waves each, looping over the items (chunk c, head b*H + h); wave I owns
 // chunk rows 16I .. 16I+15 (queries are the N = 16 columns of every product).
-// Outputs the normalised slot partial o_L / Z_L and lse_L = ln(sum_i exp(l_i))
-// over the m slot logits.
+// Without oW: outputs the normalised slot partial o_L / Z_L and lse_L =
+// ln(sum_i exp(l_i)) over the m slot logits.  With oW (the window branch's
+// normalised read and its lse, computed first): merges the two partial
+// softmaxes -- weights e^{lse_L}, e^{lse_W} -- and outputs o and lse.
 template <typename T, int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
     const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
-    const T* __restrict__ sst, T* __restrict__ oL, float* __restrict__ lseL, int Tn, int H, int Hkv, int m,
-    int w, int NC, int nitems, float scale) {
+    const T* __restrict__ sst, const T* __restrict__ oW, const float* __restrict__ lseW, T* __restrict__ oL,
+    float* __restrict__ lseL, int Tn, int H, int Hkv, int m, int w, int NC, int nitems, float scale) {
   using S = SlotFwdSmem<T, D, MP, C>;
   constexpr int NW = C / 16, NT = NW * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
   constexpr int PG = SlotPitch<MP>::PG;
@@ -510,6 +559,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
       qf[ks] = ld8_sel<T>(q + (((size_t)b * Tn + (qvalid ? tq : Tn - 1)) * H + h) * D + 32 * ks + 8 * g, qvalid);
     float lg[NB][4];
     slot_read<T, D, MP, C>(sm.sSK, sm.sK, sm.sBt, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+    WinPartial<T, D> wp;
+    wp.load(oW, lseW, b, h, qvalid ? tq : Tn - 1, Tn, H, g);
     // softmax partial over the m slots (log2 domain)
     const float sl2 = scale * NHA_LOG2E;
     float mx = -INFINITY;
@@ -536,14 +587,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_slot_fwd(
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
     slot_mix<T, D, MP, C, PC>(sm.sSVt, sm.sVt, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO);
-    // normalised partial + its lse
-    if (qvalid) {
-      float inv = 1.f / zs;
-      T* dst = oL + (((size_t)b * Tn + tq) * H + h) * D;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) st4<T>(dst + 16 * db + 4 * g, pack4<T>(accO[db] * inv));
-      if (g == 0) lseL[((size_t)b * H + h) * Tn + tq] = (mx + __log2f(zs)) * NHA_LN2;
-    }
+    // normalised partial + its lse, or merged with the window branch
+    if (qvalid) wp.store(accO, zs, mx, oL, lseL, b, h, tq, Tn, H, g);
   }
 }
 
@@ -565,8 +610,9 @@ struct SlotFwdSmemB16 {
 template <int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
-    const bf16* __restrict__ alpha, const bf16* __restrict__ sst, bf16* __restrict__ oL, float* __restrict__ lseL,
-    int Tn, int H, int Hkv, int m, int w, int NC, float scale) {
+    const bf16* __restrict__ alpha, const bf16* __restrict__ sst, const bf16* __restrict__ oW,
+    const float* __restrict__ lseW, bf16* __restrict__ oL, float* __restrict__ lseL, int Tn, int H, int Hkv, int m,
+    int w, int NC, float scale) {
   using S = SlotFwdSmemB16<D, MP, C>;
   constexpr int NW = C / 16, NT = NW * 64, NB = MP / 16, PD = S::PD, PM = S::PM;
   constexpr int PG = SlotPitch<MP>::PG;
@@ -614,6 +660,10 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   tnu.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
   float lg[NB][4];
   slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+  // the window branch's read for this lane's row (its query row registers
+  // are free now): in flight during the slot softmax and the output phase
+  WinPartial<bf16, D> wp;
+  wp.load(oW, lseW, b, h, qvalid ? tq : Tn - 1, Tn, H, g);
   // softmax partial over the m slots (log2 domain)
   const float sl2 = scale * NHA_LOG2E;
   float mx = -INFINITY;
@@ -644,13 +694,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
   slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO);
-  if (qvalid) {
-    const float inv = 1.f / zs;
-    bf16* dst = oL + (((size_t)b * Tn + tq) * H + h) * D;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) st4<bf16>(dst + 16 * db + 4 * g, pack4<bf16>(accO[db] * inv));
-    if (g == 0) lseL[((size_t)b * H + h) * Tn + tq] = (mx + __log2f(zs)) * NHA_LN2;
-  }
+  if (qvalid) wp.store(accO, zs, mx, oL, lseL, b, h, tq, Tn, H, g);
 }
 
 // ---------------------------------------------------------------- window branch
@@ -916,6 +960,15 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
     if (kmax > Tn - 1) kmax = Tn - 1;
     const int jfirst = (kmin / 64) * 64;
     const int ntiles = (kmax - jfirst) / 64 + 1;
+    // key tiles in a rotated order (step it takes the tile X = it mod
+    // ntiles): the workgroups of neighbouring query tiles, resident together
+    // on one XCD, then read each key tile at the same step, and all but the
+    // first hit the XCD's L2
+    const int rot = (ntiles - (jfirst / 64) % ntiles) % ntiles;
+    auto tile_j0 = [&](int it) {
+      const int jr = it + rot >= ntiles ? it + rot - ntiles : it + rot;
+      return jfirst + 64 * jr;
+    };
     const size_t ld = (size_t)Hkv * D;
     const bf16* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
     const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
@@ -1027,13 +1080,13 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
     using T_ = std::true_type;
     using F_ = std::false_type;
 
-    dma_tile_async<D, NT, 0>(kbase, ld, jfirst, Tn, kl, kdo, tid);
-    dma_tile_async<D, NT, 1>(vbase, ld, jfirst, Tn, vl, vdo, tid);
-    if (ntiles > 1) dma_tile_async<D, NT, 0>(kbase, ld, jfirst + 64, Tn, kl + TB, kdo, tid);
+    dma_tile_async<D, NT, 0>(kbase, ld, tile_j0(0), Tn, kl, kdo, tid);
+    dma_tile_async<D, NT, 1>(vbase, ld, tile_j0(0), Tn, vl, vdo, tid);
+    if (ntiles > 1) dma_tile_async<D, NT, 0>(kbase, ld, tile_j0(1), Tn, kl + TB, kdo, tid);
     wait_vmem();
     __syncthreads();
     floatx16 sa[2], sb[2];
-    bool use_c = useful(jfirst);
+    bool use_c = useful(tile_j0(0));
     {
       bf16x8 pf0[4];
       float r0;
@@ -1041,10 +1094,12 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
       main_pass(T_{}, F_{}, sa, __builtin_amdgcn_readfirstlane(kl), sb, pf0, r0, a0);
     }
     auto step = [&](floatx16(&cur)[2], floatx16(&nxt)[2], int it) {
-      const int j0 = jfirst + 64 * it;
-      if (it + 2 < ntiles) dma_tile_async<D, NT, 0>(kbase, ld, j0 + 128, Tn, kl + ((it + 2) % 3) * TB, kdo, tid);
-      if (it + 1 < ntiles) dma_tile_async<D, NT, 1>(vbase, ld, j0 + 64, Tn, vl + ((it + 1) & 1) * TB, vdo, tid);
-      const bool use_n = it + 1 < ntiles && useful(j0 + 64);
+      const int j0 = tile_j0(it);
+      if (it + 2 < ntiles)
+        dma_tile_async<D, NT, 0>(kbase, ld, tile_j0(it + 2), Tn, kl + ((it + 2) % 3) * TB, kdo, tid);
+      if (it + 1 < ntiles)
+        dma_tile_async<D, NT, 1>(vbase, ld, tile_j0(it + 1), Tn, vl + ((it + 1) & 1) * TB, vdo, tid);
+      const bool use_n = it + 1 < ntiles && useful(tile_j0(it + 1));
       if (use_c || use_n) {
         // one code path for every case (separate variants would each need
         // their own registers): a tile this wave does not need is masked to
@@ -1110,42 +1165,58 @@ __global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ v
 }
 
 // ---------------------------------------------------------------- host launcher
+template <typename T, int C, int MP>
+static void launch_gates(const Shape& s, const T* alpha, const ProloguePtrs& pp, hipStream_t st) {
+  hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, s.B * s.Hkv), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend,
+                     s.T, s.Hkv, s.m, s.sh, s.NC);
+}
+
+template <typename T, int D, int C, int MP>
+static void launch_scan(const Shape& s, const T* k, const T* v, const ProloguePtrs& pp, hipStream_t st) {
+  const int units = s.B * s.Hkv;
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
+                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
+                       s.sh, s.NC);
+  else
+    hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
+                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
+                       s.sh, s.NC);
+}
+
+// RoPE table, then the RoPE'd q and k rows (two launches)
+template <typename T>
+static void launch_rope(const Shape& s, const RopeTheta& th, const T* q, const T* k, const ProloguePtrs& pp,
+                        Marks& mk, hipStream_t rs) {
+  const long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
+  const long ncs = (long)s.T * (s.d / 2), thr = (nq + nk) * (s.d / 16);
+  mk.mark(rs);
+  hipLaunchKernelGGL(k_rope_cs, dim3((unsigned)((ncs + 255) / 256)), dim3(256), 0, rs, pp.rcs, s.T, s.d / 2, th);
+  mk.mark(rs);
+  hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, rs, q, k, (T*)pp.qrot,
+                     (T*)pp.krot, nq, nk, s.H, s.Hkv, s.T, s.d, (const float2*)pp.rcs);
+}
+
 template <typename T, int D, int MP, int C>
 static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const T* k, const T* v, const T* alpha,
                           const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk) {
-  const int units = s.B * s.Hkv;
   if (s.m > 0) {  // (no slots: no gates and no states)
     mk.mark(st);
-    hipLaunchKernelGGL((k_chunk_gates<T, C, MP>), dim3(s.NC, units), dim3(256), 0, st, alpha, (T*)pp.wt, pp.aend,
-                       s.T, s.Hkv, s.m, s.sh, s.NC);
+    launch_gates<T, C, MP>(s, alpha, pp, st);
   }
   if (s.rope && s.win) fk.record(st);
   if (s.m > 0) {
     mk.mark(st);
-    if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                         (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
-                         s.sh, s.NC);
-    else
-      hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                         (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
-                         s.sh, s.NC);
+    launch_scan<T, D, C, MP>(s, k, v, pp, st);
   }
   if (s.rope && s.win) {
     // RoPE (HBM-bound, no LDS) on the side stream beside the state scan (bound
     // by its chain of dependent steps; the gate products, HBM-bound too, run
     // before both), enqueued after the scan so that the scan's workgroups are
     // placed first; joined at the end
-    const hipStream_t rs = fk.follow(st);
-    const long nq = (long)s.B * s.T * s.H, nk = (long)s.B * s.T * s.Hkv;
-    const long ncs = (long)s.T * (s.d / 2), thr = (nq + nk) * (s.d / 16);
-    mk.mark(rs);
-    hipLaunchKernelGGL(k_rope_cs, dim3((unsigned)((ncs + 255) / 256)), dim3(256), 0, rs, pp.rcs, s.T, s.d / 2, th);
-    mk.mark(rs);
-    hipLaunchKernelGGL(k_rope<T>, dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, rs, q, k, (T*)pp.qrot,
-                       (T*)pp.krot, nq, nk, s.H, s.Hkv, s.T, s.d, (const float2*)pp.rcs);
+    launch_rope<T>(s, th, q, k, pp, mk, fk.follow(st));
+    fk.join(st);
   }
-  if (s.rope && s.win) fk.join(st);
 }
 
 template <typename T, int D, int MP, int C>
@@ -1158,8 +1229,6 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     const T* k = (const T*)p.k;
     const T* v = (const T*)p.v;
     const T* alpha = (const T*)p.alpha;
-    T* ol = p.ol_dst ? (T*)p.ol_dst : (T*)(p.ws + L.ol);
-    float* lsel = p.lsel_dst ? p.lsel_dst : (float*)(p.ws + L.lsel);
     const int units = s.B * s.Hkv;
     Marks mk;
     mk.ev = p.events;
@@ -1177,34 +1246,67 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       pp.skout = (float*)((char*)p.state_out + SL.sk);
       pp.svout = (float*)((char*)p.state_out + SL.sv);
     }
-    prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st, side_fork(p.events == nullptr && !p.one_stream));
+    const Fork fk = side_fork(p.events == nullptr && !p.one_stream);
     const T* qr = pp.qrot ? (const T*)pp.qrot : q;
     const T* kr = pp.krot ? (const T*)pp.krot : k;
-    if (s.m > 0) {
+    // slot branch: its normalised partial and lse (o_w null), or the final
+    // output merged with the window branch's partial (o_w, lse_w)
+    auto slot = [&](const T* o_w, const float* lse_w, T* out, float* lse_out) {
       mk.mark(st);
       if constexpr (sizeof(T) == 2) {
         hipLaunchKernelGGL((k_slot_fwd_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v,
-                           alpha, (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.sh, s.NC, s.scale);
+                           alpha, (const T*)pp.sst, o_w, lse_w, out, lse_out, s.T, s.H, s.Hkv, s.m, s.sh, s.NC,
+                           s.scale);
       } else {
         const int nitems = s.NC * s.B * s.H;
         const int nwg = nitems < device_cu_count() ? nitems : device_cu_count();
         hipLaunchKernelGGL((k_slot_fwd<T, D, MP, C>), dim3(nwg), dim3(C / 16 * 64), 0, st, q, k, v, alpha,
-                           (const T*)pp.sst, ol, lsel, s.T, s.H, s.Hkv, s.m, s.sh, s.NC, nitems, s.scale);
+                           (const T*)pp.sst, o_w, lse_w, out, lse_out, s.T, s.H, s.Hkv, s.m, s.sh, s.NC, nitems,
+                           s.scale);
       }
-    }
-    if (s.m == 0 || p.separate) {
-      ol = nullptr;  // the window kernel starts from an empty softmax
-      lsel = nullptr;
-    }
-    mk.mark(st);
-    if constexpr (sizeof(T) == 2) {
-      hipLaunchKernelGGL((k_win_fwd_b16<D, kWinWaves>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
-                         dim3(kWinWaves * 64), 0, st, qr, kr, v, ol, lsel, (T*)p.o, p.lse, s.T, s.H, s.Hkv, s.w,
-                         s.scale);
+    };
+    // window branch, started from the slot partial (seed) or an empty softmax
+    auto window = [&](hipStream_t ws_, const T* seed, const float* seed_lse, T* out, float* lse_out) {
+      mk.mark(ws_);
+      if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((k_win_fwd_b16<D, kWinWaves>),
+                           dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H), dim3(kWinWaves * 64), 0,
+                           ws_, qr, kr, v, seed, seed_lse, out, lse_out, s.T, s.H, s.Hkv, s.w, s.scale);
+      } else {
+        hipLaunchKernelGGL((k_win_fwd<T, D, kWinWaves>),
+                           dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H), dim3(kWinWaves * 64), 0,
+                           ws_, qr, kr, v, seed, seed_lse, out, lse_out, s.T, s.H, s.Hkv, s.w, s.scale);
+      }
+    };
+    if (s.m > 0 && s.win && !p.separate) {
+      // both branches: the window branch (RoPE, then band attention from an
+      // empty softmax into the workspace) on the side stream, beside the gate
+      // products and the slot-state scan it does not depend on; the slot
+      // kernel then merges the two partial softmaxes into o and lse
+      T* ow = (T*)(p.ws + L.ol);
+      float* lw = (float*)(p.ws + L.lsel);
+      fk.record(st);
+      mk.mark(st);
+      launch_gates<T, C, MP>(s, alpha, pp, st);
+      mk.mark(st);
+      launch_scan<T, D, C, MP>(s, k, v, pp, st);
+      const hipStream_t rs = fk.follow(st);
+      if (s.rope) launch_rope<T>(s, th, q, k, pp, mk, rs);
+      window(rs, nullptr, nullptr, ow, lw);
+      fk.join(st);
+      slot(ow, lw, (T*)p.o, p.lse);
+    } else if (s.m > 0 && !s.win && !p.separate) {
+      // no window: the slot branch is the whole softmax
+      prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st, fk);
+      slot(nullptr, nullptr, (T*)p.o, p.lse);
     } else {
-      hipLaunchKernelGGL((k_win_fwd<T, D, kWinWaves>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
-                         dim3(kWinWaves * 64), 0, st, qr, kr, v, ol, lsel, (T*)p.o, p.lse, s.T, s.H, s.Hkv, s.w,
-                         s.scale);
+      // no slots (the window alone), or the weighted-fusion ablation (the
+      // slot partial to ol_dst, the window's own read to o)
+      prologue_impl<T, D, MP, C>(s, th, q, k, v, alpha, pp, mk, st, fk);
+      if (s.m > 0)
+        slot(nullptr, nullptr, p.ol_dst ? (T*)p.ol_dst : (T*)(p.ws + L.ol),
+             p.lsel_dst ? p.lsel_dst : (float*)(p.ws + L.lsel));
+      window(st, nullptr, nullptr, (T*)p.o, p.lse);
     }
     if (p.state_out) {
       char* base = (char*)p.state_out;
@@ -1297,8 +1399,8 @@ int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
     all[n++] = "rope_cs";
     all[n++] = "rope";
   }
+  if (s.win) all[n++] = "win_fwd";  // (first: the slot kernel merges it)
   if (s.m > 0) all[n++] = "slot_fwd";
-  all[n++] = "win_fwd";
   if (with_state) all[n++] = "export_state";
   for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];
   return n;
