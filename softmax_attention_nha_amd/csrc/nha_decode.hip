@@ -396,12 +396,291 @@ __global__ __launch_bounds__(256) void k_dec_merge(const float* __restrict__ par
   if (tid == 0) pos[unit] = t + 1;
 }
 
+// Single-launch step for many units (B * Hkv at least the compute-unit
+// count: one workgroup per unit already fills the chip).  The workgroup walks
+// the key list [m slots; window tokens] in passes of KPN keys (the split
+// kernel's key-group layout, contiguous keys per pass), keeps each head's
+// softmax as a running (max, sum, unnormalised output) in LDS, rescaled when a
+// pass raises the maximum, and then writes o_t, pushes the token into the
+// rings and advances the position -- after a barrier behind the last read of
+// ring row t mod w.  Heads of the group go kDecGH at a time; the slot rows are
+// absorbed (in place, each by its one owner lane group) in the first head
+// pass only, later head passes read them back.
+template <typename T, int D, int KPG, int GH>
+__global__ __launch_bounds__(256) void k_dec_fused(const T* __restrict__ q, const T* __restrict__ kin,
+                                                   const T* __restrict__ vin, const T* __restrict__ alpha,
+                                                   float* __restrict__ SK, float* __restrict__ SV, T* __restrict__ RK,
+                                                   T* __restrict__ RV, T* __restrict__ RKR, long long* __restrict__ pos,
+                                                   T* __restrict__ o, int H, int Hkv, int m, int w, int sh,
+                                                   float scale, RopeTheta th, int rope) {
+  constexpr int LPK = D / 8, NG = 256 / LPK, HALF = D / 2, LPR = LPK / KPG, KPN = KPG * NG;
+  static_assert(KPG >= 1 && LPR >= 2, "keys per lane group");
+  __shared__ float lg[GH][KPN];  // logits of this pass's keys (log2 units)
+  __shared__ float red[GH][4];
+  __shared__ float wsum[4][GH][D + 1];
+  __shared__ float run_o[GH][D];  // running unnormalised output of each head of the pass
+  __shared__ float run_m[GH], run_z[GH];
+  const int tid = threadIdx.x, grp = tid / LPK, li = tid % LPK, wv = tid >> 6;
+  const int unit = blockIdx.x, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  const size_t krow = ((size_t)b * Hkv + hg) * D + 8 * li;
+  float knew[8], vnew[8];
+  ld8f_row<T>(kin + krow, knew);
+  ld8f_row<T>(vin + krow, vnew);
+  float* sk = SK + (size_t)unit * m * D + 8 * li;
+  float* sv = SV + (size_t)unit * m * D + 8 * li;
+  const long long t = pos[unit];
+  const long long nwin = (w == 0) ? 0 : (t + 1 < w ? t + 1 : w);
+  const int nkeys = m + (int)nwin;
+  const long long jfirst = t - nwin + 1;
+  const int npass = (nkeys + KPN - 1) / KPN;
+  // the token absorbed at this step (ring row t mod w, or k_t itself)
+  float kap[8], nu[8];
+  const T* rkw = (rope ? RKR : RK) + (size_t)unit * w * D + 8 * li;
+  const T* rvw = RV + (size_t)unit * w * D + 8 * li;
+  if (w > 0) {
+    const size_t ra = (size_t)(t % w) * D;
+    ld8f_row<T>(RK + (size_t)unit * w * D + 8 * li + ra, kap);
+    ld8f_row<T>(rvw + ra, nu);
+  }
+  if (sh == 0) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      kap[r] = knew[r];
+      nu[r] = vnew[r];
+    }
+  }
+  float cs[8], sn[8];
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dec_angle(th.theta[(8 * li + e) % HALF], t, cs[e], sn[e]);
+  }
+  float knr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) knr[r] = knew[r];
+  if (rope) dec_rope_cs<D>(knr, li, cs, sn);
+  const float sl2 = scale * NHA_LOG2E;
+  for (int h0 = 0; h0 < G; h0 += GH) {
+    const int nh = (G - h0) < GH ? (G - h0) : GH;
+    float qs[GH][8], qr[GH][8];
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh) {
+      const int h = hg * G + h0 + (hh < nh ? hh : 0);
+      ld8f_row<T>(q + ((size_t)b * H + h) * D + 8 * li, qs[hh]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qr[hh][e] = qs[hh][e];
+      if (rope && hh < nh) dec_rope_cs<D>(qr[hh], li, cs, sn);
+    }
+    for (int e = tid; e < GH * D; e += 256) run_o[e / D][e % D] = 0.f;
+    if (tid < GH) {
+      run_m[tid] = -INFINITY;
+      run_z[tid] = 0.f;
+    }
+    // the window rows of a pass go out one pass ahead (raw, converted when
+    // the pass starts), so each pass waits on no load of its own
+    typename Vec<T>::v8 pk[KPG], pv[KPG];
+    auto fetch = [&](int pass) {
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk) {
+        long long jp = jfirst + (pass * KPN + grp + NG * kk - m);  // window position, clamped to the valid rows
+        jp = jp < jfirst ? jfirst : (jp > t ? t : jp);
+        if (w > 0) {
+          const size_t rr = (size_t)(jp % w) * D;
+          pk[kk] = ld8<T>(rkw + rr);
+          pv[kk] = ld8<T>(rvw + rr);
+        }
+      }
+    };
+    fetch(0);
+    for (int pass = 0; pass < npass; ++pass) {
+      const int ebase = pass * KPN, nmine = min(KPN, nkeys - ebase);
+      // this group's keys: slot rows (absorbed here in the first head pass)
+      // or window rows
+      float xk[KPG][8], xv[KPG][8];
+      bool isslot[KPG];
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk) {
+        const int j = grp + NG * kk, e = ebase + j;
+        isslot[kk] = e < m;
+        if (e < m) {
+          ld8f_f32(sk + (size_t)e * D, xk[kk]);
+          ld8f_f32(sv + (size_t)e * D, xv[kk]);
+          if (h0 == 0 && j < nmine && t >= sh) {
+            const float a = to_f<T>(alpha[((size_t)b * Hkv + hg) * m + e]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              xk[kk][r] = a * xk[kk][r] + (1.f - a) * kap[r];
+              xv[kk][r] = a * xv[kk][r] + (1.f - a) * nu[r];
+            }
+            float* rk_ = sk + (size_t)e * D;
+            float* rv_ = sv + (size_t)e * D;
+            *reinterpret_cast<floatx4*>(rk_) = floatx4{xk[kk][0], xk[kk][1], xk[kk][2], xk[kk][3]};
+            *reinterpret_cast<floatx4*>(rk_ + 4) = floatx4{xk[kk][4], xk[kk][5], xk[kk][6], xk[kk][7]};
+            *reinterpret_cast<floatx4*>(rv_) = floatx4{xv[kk][0], xv[kk][1], xv[kk][2], xv[kk][3]};
+            *reinterpret_cast<floatx4*>(rv_ + 4) = floatx4{xv[kk][4], xv[kk][5], xv[kk][6], xv[kk][7]};
+          }
+        } else if (jfirst + (e - m) == t) {  // the new token
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            xk[kk][r] = knr[r];
+            xv[kk][r] = vnew[r];
+          }
+        } else if (w > 0) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            xk[kk][r] = to_f<T>(pk[kk][r]);
+            xv[kk][r] = to_f<T>(pv[kk][r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) xk[kk][r] = xv[kk][r] = 0.f;
+        }
+      }
+      if (pass + 1 < npass) fetch(pass + 1);
+      // logits: lane li ends with the full dot product of key li / LPR of its group
+      const int kmine = li / LPR, jmine = grp + NG * kmine;
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) {
+        if (hh < nh) {
+          float P[KPG];
+#pragma unroll
+          for (int kk = 0; kk < KPG; ++kk) {
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc += xk[kk][r] * (isslot[kk] ? qs[hh][r] : qr[hh][r]);
+            P[kk] = acc;
+          }
+#pragma unroll
+          for (int lvl = 0; (KPG >> lvl) > 1; ++lvl) {
+            const int n = KPG >> lvl, msk = LPK >> (lvl + 1);
+            const bool up = (li & msk) != 0;
+#pragma unroll
+            for (int i = 0; i < n / 2; ++i) {
+              const float snd = up ? P[i] : P[i + n / 2];
+              const float rcv = __shfl_xor(snd, msk, 64);
+              P[i] = (up ? P[i + n / 2] : P[i]) + rcv;
+            }
+          }
+#pragma unroll
+          for (int msk = LPR / 2; msk >= 1; msk >>= 1) P[0] += __shfl_xor(P[0], msk, 64);
+          if (li % LPR == 0 && jmine < nmine) lg[hh][jmine] = P[0] * sl2;
+        }
+      }
+      __syncthreads();
+      for (int hh = 0; hh < nh; ++hh) {
+        float mx = -INFINITY;
+        for (int j = tid; j < nmine; j += 256) mx = fmaxf(mx, lg[hh][j]);
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
+        if ((tid & 63) == 0) red[hh][wv] = mx;
+      }
+      __syncthreads();
+      // the pass's maximum joins the running one
+      float mnew[GH], fold[GH];
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) {
+        float mp = -INFINITY;
+        if (hh < nh)
+          for (int x = 0; x < 4; ++x) mp = fmaxf(mp, red[hh][x]);
+        const float mr = hh < nh ? run_m[hh] : 0.f;
+        mnew[hh] = fmaxf(mr, mp);
+        fold[hh] = hh < nh ? fast_exp2(mr - mnew[hh]) : 0.f;  // 0 on the first pass (mr = -inf)
+      }
+      float oa[GH][8], zs[GH];
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) {
+        zs[hh] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) oa[hh][r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < KPG; ++kk) {
+        const int j = grp + NG * kk;
+        if (j < nmine) {
+#pragma unroll
+          for (int hh = 0; hh < GH; ++hh) {
+            if (hh < nh) {
+              const float p = fast_exp2(lg[hh][j] - mnew[hh]);
+              zs[hh] += p;
+#pragma unroll
+              for (int r = 0; r < 8; ++r) oa[hh][r] += p * xv[kk][r];
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) {
+        if (hh >= nh) continue;
+#pragma unroll
+        for (int o2 = LPK; o2 < 64; o2 <<= 1) {
+          zs[hh] += __shfl_xor(zs[hh], o2, 64);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) oa[hh][r] += __shfl_xor(oa[hh][r], o2, 64);
+        }
+      }
+      if ((tid & 63) < LPK) {
+#pragma unroll
+        for (int hh = 0; hh < GH; ++hh) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) wsum[wv][hh][8 * li + r] = oa[hh][r];
+          if (li == 0) wsum[wv][hh][D] = zs[hh];
+        }
+      }
+      __syncthreads();
+      // running state <- fold * running + this pass (each element by one thread)
+      for (int e = tid; e < nh * (D + 1); e += 256) {
+        const int hh = e / (D + 1), c = e % (D + 1);
+        const float v = wsum[0][hh][c] + wsum[1][hh][c] + wsum[2][hh][c] + wsum[3][hh][c];
+        if (c < D)
+          run_o[hh][c] = run_o[hh][c] * fold[hh] + v;
+        else
+          run_z[hh] = run_z[hh] * fold[hh] + v;
+      }
+      __syncthreads();
+      if (tid < nh) run_m[tid] = mnew[tid];
+      __syncthreads();
+    }
+    for (int e = tid; e < nh * D; e += 256) {
+      const int hh = e / D, c = e % D;
+      o[((size_t)b * H + hg * G + h0 + hh) * D + c] = to_t<T>(run_o[hh][c] / run_z[hh]);
+    }
+    __syncthreads();
+  }
+  // every read of ring row t mod w is behind the barriers above: push (k_t,
+  // v_t) there (and the key with RoPE at t) and advance the position
+  if (w > 0 && tid < D) {
+    const size_t src = ((size_t)b * Hkv + hg) * D, dst = ((size_t)unit * w + (size_t)(t % w)) * D;
+    const float x = to_f<T>(kin[src + tid]);
+    RK[dst + tid] = kin[src + tid];
+    RV[dst + tid] = vin[src + tid];
+    if (rope) {
+      const int i = tid % HALF;
+      const float pair = to_f<T>(kin[src + (tid < HALF ? tid + HALF : tid - HALF)]);
+      float c2, s2;
+      dec_angle(th.theta[i], t, c2, s2);
+      RKR[dst + tid] = to_t<T>(tid < HALF ? x * c2 - pair * s2 : x * c2 + pair * s2);
+    }
+  }
+  if (tid == 0) pos[unit] = t + 1;
+}
+
 template <typename T, int D>
 static hipError_t decode_impl(const Shape& s, const RopeTheta& th, const DecodePtrs& p, hipStream_t st) {
   StateLayout L = state_layout(s);
   char* base = (char*)p.state;
+  const int units = s.B * s.Hkv;
+  if (units >= device_cu_count()) {
+    // one workgroup per unit fills the chip: one launch, no partials
+    // one query head per KV head: one head per pass, twice the keys per
+    // lane group; else four heads per pass
+    auto fused = s.G == 1 ? k_dec_fused<T, D, D / 32 < 1 ? 1 : D / 32, 1> : k_dec_fused<T, D, D / 32 < 1 ? 1 : D / 32, kDecGH>;
+    hipLaunchKernelGGL(fused, dim3(units), dim3(256), 0, st, (const T*)p.q, (const T*)p.k, (const T*)p.v,
+                       (const T*)p.alpha, (float*)(base + L.sk), (float*)(base + L.sv), (T*)(base + L.rk),
+                       (T*)(base + L.rv), (T*)(base + L.rkr), (long long*)(base + L.pos), (T*)p.o, s.H, s.Hkv, s.m,
+                       s.w, s.sh, s.scale, th, s.rope ? 1 : 0);
+    return hipGetLastError();
+  }
   const DecodeSplit sp = decode_splits(s);
-  const int NS = sp.ns, units = s.B * s.Hkv;
+  const int NS = sp.ns;
   // half-size key groups (fewer registers, more workgroups per CU) whenever
   // the keys fit them
   auto split = sp.small ? k_dec_split<T, D, D / 32 < 1 ? 1 : D / 32> : k_dec_split<T, D, D / 16>;

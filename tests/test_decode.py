@@ -122,3 +122,20 @@ def test_decode_bitwise_reproducible():
         runs.append((torch.stack(outs, 1).cpu(), st.cpu()))
     assert torch.equal(runs[0][0], runs[1][0])
     assert torch.equal(runs[0][1], runs[1][1])
+
+
+@pytest.mark.parametrize("B,H,Hkv,d,m,w,T0", [(64, 16, 4, 64, 16, 64, 96), (32, 64, 8, 128, 32, 48, 60),
+                                               (256, 2, 1, 32, 8, 0, 20), (128, 4, 2, 128, 64, 200, 230)])
+def test_decode_single_launch_many_units(B, H, Hkv, d, m, w, T0):
+    """B * Hkv >= the compute-unit count: one workgroup per (sequence, KV
+    head) walks all its keys in passes (single launch) -- incl. two passes of
+    query heads (G = 8) and no window (w = 0)."""
+    wl = WORKLOADS["340m"].with_(B=B, T=T0, H=H, Hkv=Hkv, d=d, m=m, seed=46)
+    steps = 6
+    log("case decode single launch B=%d H=%d/%d d=%d m=%d w=%d T0=%d" % (B, H, Hkv, d, m, w, T0))
+    od, (q, k, v, a), st = run_decode(wl, T0, steps, w, wl.rope_base)
+    o_ref, _ = oracle_fwd(q, k, v, a, w, wl.rope_base)
+    compare("o_dec", f64(od), o_ref[:, T0:], 2e-2, 1e-2)
+    # and bitwise reproducible
+    od2, _, st2 = run_decode(wl, T0, steps, w, wl.rope_base)
+    assert torch.equal(od, od2) and torch.equal(st, st2)
