@@ -1644,14 +1644,20 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) accK[dt] = accV[dt] = zero16();
   // (the kind-3 swizzle repeats every 8 rows: rows r + 8 are 16 D bytes on)
-  uint32_t foff[D / 16], toff[D / 32];
+  // LDS byte offsets of the row fragment of step ks (row c, chunk 2 ks + hf
+  // under the swizzle) and of the transposed reads of column block dt: the
+  // swizzle is an XOR, which splits into a per-lane base and the step index
+  // XORed with the swizzle's upper bits -- two registers instead of one per
+  // step (this kernel has none to spare)
+  const int swc = chunk_swz<D, 3>(c), fs = swc >> 1;
+  const uint32_t fb = 2 * (c * D + 8 * (hf ^ (swc & 1)));
+  auto foff = [&](int ks) { return fb + 32u * (uint32_t)(ks ^ fs); };
+  const int tr_ = 4 * hf + (jj >> 2), swr = chunk_swz<D, 3>(tr_), ts = swr >> 2;
+  const uint32_t tb = 2 * (tr_ * D + 8 * ((2 * (c >> 4) + ((jj & 3) >> 1)) ^ (swr & 3)) + 4 * (jj & 1));
+  uint32_t toffa[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) foff[ks] = 2 * (c * D + 8 * ((2 * ks + hf) ^ chunk_swz<D, 3>(c)));
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int r = 4 * hf + (jj >> 2), d0 = 32 * dt + 16 * (c >> 4) + 4 * (jj & 3);
-    toff[dt] = 2 * (r * D + 8 * ((d0 >> 3) ^ chunk_swz<D, 3>(r)) + (d0 & 7));
-  }
+  for (int dt = 0; dt < D / 32; ++dt) toffa[dt] = tb + 64u * (uint32_t)(dt ^ ts);
+  auto toff = [&](int dt) { return toffa[dt]; };
   int tmax = k0 + KT - 1 + w - 1;
   if (tmax > Tn - 1) tmax = Tn - 1;
   const int qfirst = (k0 / 64) * 64;
@@ -1720,8 +1726,8 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
           }
 #pragma unroll
           for (int ks = 0; ks < D / 16; ++ks) {
-            x = mma32x32(x, ld8_at(qt + foff[ks] + qb * 64 * D), kf[ks]);
-            dp = mma32x32(dp, ld8_at(ot + foff[ks] + qb * 64 * D), vf[ks]);
+            x = mma32x32(x, ld8_at(qt + foff(ks) + qb * 64 * D), kf[ks]);
+            dp = mma32x32(dp, ld8_at(ot + foff(ks) + qb * 64 * D), vf[ks]);
           }
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -1735,7 +1741,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
           for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-              const uint32_t off = toff[dt] + (32 * qb + 16 * st) * D * 2;
+              const uint32_t off = toff(dt) + (32 * qb + 16 * st) * D * 2;
               const bf16x4 o0 = ld_tr4_at(ot + off), o1 = ld_tr4_at(ot + off + 16 * D);
               const bf16x4 q0v = ld_tr4_at(qt + off), q1v = ld_tr4_at(qt + off + 16 * D);
               bf16x8 fo, fq;
