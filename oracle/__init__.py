@@ -47,19 +47,24 @@ def build(force=True):
     return _LIB
 
 
+def configure(lib):
+    """Set the argument types of a loaded oracle library (this one, or a copy
+    built from modified sources by the mutation tests)."""
+    P = ctypes.POINTER(ctypes.c_double)
+    i, dbl = ctypes.c_int, ctypes.c_double
+    lib.nha_oracle_fwd.argtypes = [i] * 8 + [dbl, dbl] + [P] * 12 + [i]
+    lib.nha_oracle_fwd.restype = i
+    lib.nha_oracle_bwd.argtypes = [i] * 8 + [dbl, dbl] + [P] * 15 + [i]
+    lib.nha_oracle_bwd.restype = i
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build()
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.POINTER(ctypes.c_double)
-        i, dbl = ctypes.c_int, ctypes.c_double
-        lib.nha_oracle_fwd.argtypes = [i] * 8 + [dbl, dbl] + [P] * 12 + [i]
-        lib.nha_oracle_fwd.restype = i
-        lib.nha_oracle_bwd.argtypes = [i] * 8 + [dbl, dbl] + [P] * 15 + [i]
-        lib.nha_oracle_bwd.restype = i
-        _lib = lib
+        _lib = configure(ctypes.CDLL(_LIB))
     return _lib
 
 
