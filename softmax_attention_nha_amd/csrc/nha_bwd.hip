@@ -453,6 +453,7 @@ struct SlotBwdASmemB16 {
   bf16 sA[C * PM];
   bf16 sB[C * PM];   // 2^{E_J - G_u} b_u [u][i]
   float sG[C * SlotPitch<MP>::PG];
+  SlotTab<C, MP> tab;
 };
 
 template <int D, int MP, int C>
@@ -507,6 +508,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
     const float be = (i < m && t < Tn && t >= w) ? 1.f - (float)sm.sA[u * PM + i] : 0.f;
     sm.sB[u * PM + i] = (bf16)(fast_exp2(sm.sG[(u | 15) * PG + i] - sm.sG[u * PG + i]) * be);
   }
+  build_slot_tab<C, MP, NT>(sm.tab, sm.sG, tid);
   __syncthreads();
   BlockedTile<bf16, D, NT, MP> tsk;
   RowTile<bf16, D, NT, C> tkap;
@@ -523,12 +525,12 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   D_t = sum_over_g(D_t);
   if (qvalid && g == 0) Dt[(size_t)bh * Tn + tq] = D_t;
   float lg[NB][4], dp[NB][4];
-  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, df, I, t0, w, Tn, dp);
+  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, df, I, t0, w, Tn, dp, &sm.tab);
   __syncthreads();  // every wave is done with S0^V and nu
   tsk.template store<PD>(sm.tS, tid);
   tkap.template store<PD>(sm.tK, tid);
   __syncthreads();
-  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg, &sm.tab);
   float p[NB][4], dl[NB][4];
   float* sdl_row = sdl + ((size_t)bh * NC * C + urow + t0) * MP;
   float* pp_row = pp + ((size_t)bh * NC * C + urow + t0) * MP;
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   floatx4 accO[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
-  slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, dl, I, t0, w, Tn, accO);
+  slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, dl, I, t0, w, Tn, accO, &sm.tab);
   if (qvalid) {
     bf16* dst = dqs + (((size_t)b * Tn + tq) * H + h) * D;
 #pragma unroll

@@ -605,6 +605,7 @@ struct SlotFwdSmemB16 {
   bf16 sA[C * PM];   // alpha [u][i]
   bf16 sB[C * PM];   // 2^{E_J - G_u} b_u [u][i]
   float sG[C * SlotPitch<MP>::PG];
+  SlotTab<C, MP> tab;
 };
 
 template <int D, int MP, int C>
@@ -652,6 +653,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
     const float be = (i < m && t < Tn && t >= w) ? 1.f - (float)sm.sA[u * PM + i] : 0.f;
     sm.sB[u * PM + i] = (bf16)(fast_exp2(sm.sG[(u | 15) * PG + i] - sm.sG[u * PG + i]) * be);
   }
+  build_slot_tab<C, MP, NT>(sm.tab, sm.sG, tid);
   __syncthreads();
   // the output phase's tiles: loads in flight during the logits
   BlockedTile<bf16, D, NT, MP> tsv;
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   tsv.load(src + (size_t)MP * D, tid);
   tnu.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
   float lg[NB][4];
-  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg);
+  slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg, &sm.tab);
   // the window branch's read for this lane's row (its query row registers
   // are free now): in flight during the slot softmax and the output phase
   WinPartial<bf16, D> wp;
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   floatx4 accO[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
-  slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO);
+  slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO, &sm.tab);
   if (qvalid) wp.store(accO, zs, mx, oL, lseL, b, h, tq, Tn, H, g);
 }
 

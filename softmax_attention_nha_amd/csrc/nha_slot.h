@@ -141,19 +141,77 @@ __device__ __forceinline__ void stage_gates(const T* __restrict__ alpha, float* 
 // decays take the exact fp32 running products: there dalpha's
 // (A - b F) / alpha form cancels, and the same-block terms must stay fp32.
 // Uniform over the wave.
+// (Every load is unconditional and the test is a bitwise and: no branch and
+// no serialised LDS round trip per slot.)
 template <int MP>
 __device__ __forceinline__ bool block_factorizable(const float* sG, int r0) {
   constexpr int NB = MP / 16, PG = SlotPitch<MP>::PG;
   const int g = (threadIdx.x & 63) >> 4;
+  const float keep = r0 > 0 ? 1.f : 0.f;
+  const int rb = r0 > 0 ? r0 - 1 : 0;
   bool ok = true;
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int i = 16 * mb + 4 * g + r;
-      float before = r0 > 0 ? sG[(r0 - 1) * PG + i] : 0.f;
-      ok = ok && (sG[(r0 + 15) * PG + i] - before >= -16.f);
+      const int i = 16 * mb + 4 * g + r;
+      const float before = keep * sG[rb * PG + i];
+      ok &= (sG[(r0 + 15) * PG + i] - before >= -16.f);
     }
+  return __all(ok);
+}
+
+// Per-chunk decay factors of the block-referenced form, built once per chunk
+// from the log2 cumsum G by build_slot_tab (after G's last barrier; a barrier
+// must follow before they are read).  With E_J = G at the last row of 16-row
+// block J and E_{-1} = 0 (the chunk start):
+//   e[J + 1][i] = E_J
+//   f[I][J][i]  = 2^{E_{I-1} - E_J}   (J <= I; <= 1 for J < I; clamped to
+//                                      2^64 for J = I, where it is used only
+//                                      when the block is factorizable, <= 2^16)
+//   z[I][i]     = 2^{E_{I-1}}
+// A slot factor 2^{G_t - E_J} of row t in block I is then the lane's
+// 2^{G_t - E_{I-1}} (<= 1, computed once) times f[I][J]: one product instead
+// of an exponential and two scattered reads per (row, slot, block).
+template <int C, int MP>
+struct SlotTab {
+  static constexpr int NW = C / 16;
+  float e[NW + 1][MP];
+  float f[NW][NW][MP];
+  float z[NW][MP];
+};
+
+template <int C, int MP, int NT>
+__device__ __forceinline__ void build_slot_tab(SlotTab<C, MP>& tb, const float* sG, int tid) {
+  constexpr int NW = C / 16, PG = SlotPitch<MP>::PG;
+  for (int x = tid; x < (NW + 1) * MP; x += NT) {
+    const int J = x / MP - 1, i = x % MP;
+    tb.e[J + 1][i] = J < 0 ? 0.f : sG[(16 * J + 15) * PG + i];
+  }
+  for (int x = tid; x < NW * NW * MP; x += NT) {
+    const int I = x / (NW * MP), J = (x / MP) % NW, i = x % MP;
+    const float ep = I > 0 ? sG[(16 * I - 1) * PG + i] : 0.f;
+    tb.f[I][J][i] = J <= I ? fast_exp2(fminf(ep - sG[(16 * J + 15) * PG + i], 64.f)) : 0.f;
+  }
+  for (int x = tid; x < NW * MP; x += NT) {
+    const int I = x / MP, i = x % MP;
+    tb.z[I][i] = I > 0 ? fast_exp2(sG[(16 * I - 1) * PG + i]) : 1.f;
+  }
+}
+
+// block_factorizable from the table: E_I - E_{I-1} >= -16 for every slot
+template <int C, int MP>
+__device__ __forceinline__ bool block_factorizable(const SlotTab<C, MP>& tb, int I) {
+  constexpr int NB = MP / 16;
+  const int g = (threadIdx.x & 63) >> 4;
+  bool ok = true;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(&tb.e[I][16 * mb + 4 * g]);
+    const floatx4 b = *reinterpret_cast<const floatx4*>(&tb.e[I + 1][16 * mb + 4 * g]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ok &= (b[r] - a[r] >= -16.f);
+  }
   return __all(ok);
 }
 
@@ -164,23 +222,42 @@ __device__ __forceinline__ bool block_factorizable(const float* sG, int r0) {
 template <typename T, int D, int MP, int C, bool TR = false>
 __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* sBt, const float* sG, const T* sA,
                                           const typename Vec<T>::v8* xf, int I, int t0, int w, int Tn,
-                                          float (&out)[MP / 16][4]) {
+                                          float (&out)[MP / 16][4], const SlotTab<C, MP>* tb = nullptr) {
   constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
   constexpr int PG = SlotPitch<MP>::PG;
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
+  // TR: every factor from the table (out accumulates in units of the lane's
+  // F = 2^{G_t - E_{I-1}}, applied at the end); else the exponentials directly
+  float F[NB][4];
+  if constexpr (TR) {
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+      const floatx4 ep = *reinterpret_cast<const floatx4*>(&tb->e[I][16 * mb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) F[mb][r] = fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r] - ep[r]);
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) {
     floatx4 acc = zero4();
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) acc = mma32(acc, ld8<T>(&sS[(16 * mb + cc) * PD + 32 * ks + 8 * g]), xf[ks]);
+    if constexpr (TR) {
+      const floatx4 z4 = *reinterpret_cast<const floatx4*>(&tb->z[I][16 * mb + 4 * g]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) out[mb][r] = fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r]) * acc[r];
+      for (int r = 0; r < 4; ++r) out[mb][r] = z4[r] * acc[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[mb][r] = fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r]) * acc[r];
+    }
   }
   // earlier 16-row blocks J < I of the chunk, and (when factorizable) the
   // block itself with the causal mask u <= t; one block per iteration (not
   // unrolled: the blocks are independent and unrolling only multiplies the
   // live registers)
-  const bool fast = block_factorizable<MP>(sG, r0);
+  bool fast;
+  if constexpr (TR) fast = block_factorizable<C, MP>(*tb, I);
+  else fast = block_factorizable<MP>(sG, r0);
   floatx4 aI = zero4();  // A[u][t] of the wave's own block (exact path)
 #pragma unroll 1
   for (int J = 0; J <= I; ++J) {
@@ -203,13 +280,25 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
         else
           bt = ld4<T>(&sBt[(16 * mb + cc) * PC + 16 * J + 4 * g]);
         floatx4 x = mma16(zero4(), bt, bfr);
+        if constexpr (TR) {
+          const floatx4 f4 = *reinterpret_cast<const floatx4*>(&tb->f[I][J][16 * mb + 4 * g]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int i = 16 * mb + 4 * g + r;
-          out[mb][r] += fast_exp2(sG[urow * PG + i] - sG[(16 * J + 15) * PG + i]) * x[r];
+          for (int r = 0; r < 4; ++r) out[mb][r] += f4[r] * x[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int i = 16 * mb + 4 * g + r;
+            out[mb][r] += fast_exp2(sG[urow * PG + i] - sG[(16 * J + 15) * PG + i]) * x[r];
+          }
         }
       }
     }
+  }
+  if constexpr (TR) {
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[mb][r] *= F[mb][r];
   }
   if (fast) return;
   // same block: exact running products
@@ -250,15 +339,34 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
 template <typename T, int D, int MP, int C, int PCT, bool TR = false>
 __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* sB, const float* sG, const T* sA,
                                          const float (&wgt)[MP / 16][4], int I, int t0, int w, int Tn,
-                                         floatx4 (&accO)[D / 16]) {
+                                         floatx4 (&accO)[D / 16], const SlotTab<C, MP>* tb = nullptr) {
   constexpr int NW = C / 16, NB = MP / 16, PM = pitch_of(MP), PG = SlotPitch<MP>::PG, PD = pitch_of(D);
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc;
+  // TR: wF = wgt * 2^{G_t - E_{I-1}}, the lane's part of every factor (the
+  // block parts come from the table)
+  float wF[NB][4];
+  if constexpr (TR) {
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+      const floatx4 ep = *reinterpret_cast<const floatx4*>(&tb->e[I][16 * mb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        wF[mb][r] = wgt[mb][r] * fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r] - ep[r]);
+    }
+  }
   {
     float ph[NB][4];
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
+    for (int mb = 0; mb < NB; ++mb) {
+      if constexpr (TR) {
+        const floatx4 z4 = *reinterpret_cast<const floatx4*>(&tb->z[I][16 * mb + 4 * g]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ph[mb][r] = wgt[mb][r] * fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r]);
+        for (int r = 0; r < 4; ++r) ph[mb][r] = wF[mb][r] * z4[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ph[mb][r] = wgt[mb][r] * fast_exp2(sG[urow * PG + 16 * mb + 4 * g + r]);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < NB / 2; ++s) {
       typename Vec<T>::v8 bfr = pack8<T>(floatx4{ph[2 * s][0], ph[2 * s][1], ph[2 * s][2], ph[2 * s][3]},
@@ -282,7 +390,9 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
       }
     }
   }
-  const bool fast = block_factorizable<MP>(sG, r0);
+  bool fast;
+  if constexpr (TR) fast = block_factorizable<C, MP>(*tb, I);
+  else fast = block_factorizable<MP>(sG, r0);
 #pragma unroll 1
   for (int J = 0; J <= I; ++J) {
     if (J < I || fast) {
@@ -290,11 +400,21 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
 #pragma unroll
       for (int s = 0; s < NB / 2; ++s) {
         float f[8];
+        if constexpr (TR) {
+          const floatx4 fa = *reinterpret_cast<const floatx4*>(&tb->f[I][J][32 * s + 4 * g]);
+          const floatx4 fb = *reinterpret_cast<const floatx4*>(&tb->f[I][J][32 * s + 16 + 4 * g]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
-          f[r] = wgt[2 * s][r] * fast_exp2(sG[urow * PG + i0] - sG[(16 * J + 15) * PG + i0]);
-          f[4 + r] = wgt[2 * s + 1][r] * fast_exp2(sG[urow * PG + i1] - sG[(16 * J + 15) * PG + i1]);
+          for (int r = 0; r < 4; ++r) {
+            f[r] = wF[2 * s][r] * fa[r];
+            f[4 + r] = wF[2 * s + 1][r] * fb[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
+            f[r] = wgt[2 * s][r] * fast_exp2(sG[urow * PG + i0] - sG[(16 * J + 15) * PG + i0]);
+            f[4 + r] = wgt[2 * s + 1][r] * fast_exp2(sG[urow * PG + i1] - sG[(16 * J + 15) * PG + i1]);
+          }
         }
         at = mma32(at,
                    ld4x2<T>(&sB[(16 * J + cc) * PM + 32 * s + 4 * g], &sB[(16 * J + cc) * PM + 32 * s + 16 + 4 * g]),
