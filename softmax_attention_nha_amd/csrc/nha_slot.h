@@ -259,8 +259,7 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
   if constexpr (TR) fast = block_factorizable<C, MP>(*tb, I);
   else fast = block_factorizable<MP>(sG, r0);
   floatx4 aI = zero4();  // A[u][t] of the wave's own block (exact path)
-#pragma unroll 1
-  for (int J = 0; J <= I; ++J) {
+  auto block = [&](int J) {
     floatx4 av = zero4();  // A[u][t] = key_u . x_t, D layout [u = 16J + 4g + r][t = cc]
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
@@ -293,6 +292,16 @@ __device__ __forceinline__ void slot_read(const T* sS, const T* sKey, const T* s
         }
       }
     }
+  };
+  if constexpr (TR) {
+    // (bf16 kernels: registers to spare -- unrolled, so that the blocks'
+    // reads and products overlap)
+#pragma unroll
+    for (int J = 0; J < NW; ++J)
+      if (J <= I) block(J);
+  } else {
+#pragma unroll 1
+    for (int J = 0; J <= I; ++J) block(J);
   }
   if constexpr (TR) {
 #pragma unroll
@@ -393,8 +402,7 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
   bool fast;
   if constexpr (TR) fast = block_factorizable<C, MP>(*tb, I);
   else fast = block_factorizable<MP>(sG, r0);
-#pragma unroll 1
-  for (int J = 0; J <= I; ++J) {
+  auto block = [&](int J) {
     if (J < I || fast) {
       floatx4 at = zero4();
 #pragma unroll
@@ -435,6 +443,14 @@ __device__ __forceinline__ void slot_mix(const T* sSt, const T* sKeyT, const T* 
         accO[db] = mma16(accO[db], kt, bfr);
       }
     }
+  };
+  if constexpr (TR) {
+#pragma unroll
+    for (int J = 0; J < NW; ++J)
+      if (J <= I) block(J);
+  } else {
+#pragma unroll 1
+    for (int J = 0; J <= I; ++J) block(J);
   }
   if (fast) return;
   float Dp[NB][4];
