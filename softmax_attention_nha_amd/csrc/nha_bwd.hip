@@ -1680,19 +1680,32 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
     const uint32_t ql = lds_addr(&qbuf[0][0]), ol = lds_addr(&obuf[0][0]);
     constexpr uint32_t TB = 64 * D * 2;
     const uint32_t ldo = dma_lane_off<D, NT, 3>(tid, ld);
+    // stage: the tile's lse / D_t values go into registers first (clamped
+    // rows: unconditional loads), then the Q and dO tiles into LDS; commit,
+    // after the current tile's work, writes the values to LDS -- written
+    // right away they would make the wave wait for the tile loads issued
+    // before them (the memory counter counts in issue order)
+    float lse_n = 0.f, dt_n = 0.f;
     auto stage = [&](int n, int buf) {
       const int hh = n / ntiles, q0 = tile_q0(n - hh * ntiles), h = hg * G + hh;
       const size_t base = ((size_t)b * Tn * H + h) * D;
+      if (tid < 64) {
+        const size_t e = ((size_t)b * H + h) * Tn + min(q0 + tid, Tn - 1);
+        lse_n = lse[e];
+        dt_n = Dt[e];
+      }
       dma_tile_async<D, NT, 3>(qr + base, ld, q0, Tn, ql + buf * TB, ldo, tid);
       dma_tile_async<D, NT, 3>(dO + base, ld, q0, Tn, ol + buf * TB, ldo, tid);
+    };
+    auto commit = [&](int n, int buf) {
       if (tid < 64) {
-        const int t = q0 + tid;
-        const size_t e = ((size_t)b * H + h) * Tn + t;
-        nlb[buf][tid] = t < Tn ? -lse[e] * inv_s : 0.f;
-        ndb[buf][tid] = t < Tn ? -Dt[e] : 0.f;
+        const int hh = n / ntiles, t = tile_q0(n - hh * ntiles) + tid;
+        nlb[buf][tid] = t < Tn ? -lse_n * inv_s : 0.f;
+        ndb[buf][tid] = t < Tn ? -dt_n : 0.f;
       }
     };
     stage(0, 0);
+    commit(0, 0);
     wait_vmem();
     __syncthreads();
     for (int n = 0; n < total; ++n) {
@@ -1759,6 +1772,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
             }
         }
       }
+      if (n + 1 < total) commit(n + 1, cb ^ 1);
       wait_vmem();
       __syncthreads();
     }
