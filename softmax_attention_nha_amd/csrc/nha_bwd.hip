@@ -1922,11 +1922,12 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
                          (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H, s.Hkv, s.m, s.sh, s.NC,
                          nitems, s.scale);
     }
-    // the adjoint scan, and beside it on the side stream the window dq (needs
-    // D_t and the slot part of dq), enqueued after the scan so that the scan's
-    // workgroups are placed first; joined before pass B.  A two-stage ring
-    // (41 KB of LDS) leaves room for a dq workgroup (64 KB) beside two scan
-    // waves on a CU and is as fast alone as three stages.
+    // the adjoint scan and pass B, and beside them on the side stream the
+    // window dq (needs D_t and the slot part of dq; nothing after it reads
+    // dq), enqueued after the scan so that the scan's workgroups are placed
+    // first.  A two-stage ring (41 KB of LDS) leaves room for a dq workgroup
+    // (64 KB) beside two scan waves on a CU and is as fast alone as three
+    // stages.
     fk.record(st);
     mk.mark(st);
     if constexpr (sizeof(T) == 2)
@@ -1946,11 +1947,11 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
       hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, sq, qr, kr, v, dOw, lsew, Dw,
                          dqs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
     }
-    fk.join(st);
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
                        (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.sh, s.NC);
-    // the dalpha carry on the side stream, beside the window dk/dv
+    // the dalpha carry on the side stream (after dq and pass B), beside the
+    // window dk/dv
     const hipStream_t sa = fk.begin(st);
     mk.mark(sa);
     hipLaunchKernelGGL((k_dalpha_tail<T, MP, C>), dim3(s.NC, units), dim3(256), 0, sa, alpha, csum, p.dalpha, s.T,
