@@ -1621,8 +1621,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
     const bf16* __restrict__ dkap, const bf16* __restrict__ dnu, const float2* __restrict__ rcs,
     bf16* __restrict__ dk, bf16* __restrict__ dv, int Tn, int H, int Hkv, int w, int sh, float scale) {
   constexpr int NT = NWV * 64, KT = 32 * NWV;
-  __shared__ bf16 qbuf[2][64 * D];
-  __shared__ bf16 obuf[2][64 * D];
+  __shared__ bf16 qobuf[4][64 * D];  // Q tiles [0..1], dO tiles [2..3]; then the output staging
   __shared__ float nlb[2][64], ndb[2][64];  // -lse_t / s and -D_t of the tile's queries
   const int tid = threadIdx.x, W = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hf = l >> 5, c = l & 31,
             jj = l & 15;
@@ -1677,7 +1676,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
   };
   if (total > 0) {
     const size_t ld = (size_t)H * D;
-    const uint32_t ql = lds_addr(&qbuf[0][0]), ol = lds_addr(&obuf[0][0]);
+    const uint32_t ql = lds_addr(&qobuf[0][0]), ol = lds_addr(&qobuf[2][0]);
     constexpr uint32_t TB = 64 * D * 2;
     const uint32_t ldo = dma_lane_off<D, NT, 3>(tid, ld);
     // stage: the tile's lse / D_t values go into registers first (clamped
@@ -1777,14 +1776,21 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
       __syncthreads();
     }
   }
-  if (kvalid) {
+  // dk = s Q^T dl rotated back by R_key^T, dv = dO^T P; plus the slot parts of
+  // the key row (absorbed at step key + sh).  Each wave puts its 32 x D tile
+  // of one output into LDS (the Q / dO buffers are free after the last
+  // barrier; pitch D + 4: conflict-free 8-byte writes) and writes it out in
+  // whole rows, 16 bytes per lane, adding the slot part read the same way --
+  // written straight from the accumulators, each lane would put 8-byte
+  // pieces into 32 rows per instruction.
+  {
     constexpr int HT = D / 64 > 0 ? D / 64 : 1;
     float ok[D / 32][16];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) ok[dt][e] = accK[dt][e] * scale;
-    if (rcs) {
+    if (rcs && kvalid) {
       const float2* cs = rcs + (size_t)key * (D / 2);
       if constexpr (D >= 64) {
 #pragma unroll
@@ -1806,27 +1812,49 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
         }
       }
     }
-    // this key row is also absorbed (at step key + sh); dkap null: no slots
-    const bool slot = dkap != nullptr && key + sh < Tn;
+    constexpr int PS = D + 4, CPR = D / 8, RPI = 64 / CPR;
+    static_assert(NWV * 32 * PS * 2 <= 4 * 64 * D * 2, "staging fits the tile buffers");
+    bf16* stg = &qobuf[0][0] + W * 32 * PS;
+    // (total == 0: no tile was staged and no barrier passed; the buffers were
+    // never used)
+    auto put = [&](int which, const bf16* slotp, bf16* out) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * dt + 8 * i + 4 * hf;
-        floatx4 sk = zero4(), sv = zero4();
-        if (slot) {
-          const bf16x4 xk = ld4<bf16>(dkap + krow + d), xv = ld4<bf16>(dnu + krow + d);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sk[r] = (float)xk[r];
-            sv[r] = (float)xv[r];
-          }
+        for (int i = 0; i < 4; ++i) {
+          const floatx4 x = which == 0 ? floatx4{ok[dt][4 * i], ok[dt][4 * i + 1], ok[dt][4 * i + 2],
+                                                 ok[dt][4 * i + 3]}
+                                       : floatx4{accV[dt][4 * i], accV[dt][4 * i + 1], accV[dt][4 * i + 2],
+                                                 accV[dt][4 * i + 3]};
+          st4<bf16>(stg + c * PS + 32 * dt + 8 * i + 4 * hf, pack4<bf16>(x));
         }
-        st4<bf16>(dk + krow + d, pack4<bf16>(floatx4{ok[dt][4 * i] + sk[0], ok[dt][4 * i + 1] + sk[1],
-                                                     ok[dt][4 * i + 2] + sk[2], ok[dt][4 * i + 3] + sk[3]}));
-        st4<bf16>(dv + krow + d, pack4<bf16>(floatx4{accV[dt][4 * i] + sv[0], accV[dt][4 * i + 1] + sv[1],
-                                                     accV[dt][4 * i + 2] + sv[2], accV[dt][4 * i + 3] + sv[3]}));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 32 / RPI; ++k) {
+        const int row = RPI * k + l / CPR, q = l % CPR, kr_ = kl + row;
+        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(stg + row * PS + 8 * q);
+        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(stg + row * PS + 8 * q + 4);
+        if (kr_ < Tn) {
+          const size_t rw = (((size_t)b * Tn + kr_) * Hkv + hg) * D + 8 * q;
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = (float)a0[e];
+            y[4 + e] = (float)a1[e];
+          }
+          // this key row is also absorbed (at step key + sh); null: no slots
+          if (slotp != nullptr && kr_ + sh < Tn) {
+            const bf16x8 z = ld8<bf16>(slotp + rw);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] += (float)z[e];
+          }
+          st8<bf16>(out + rw, pack8<bf16>(floatx4{y[0], y[1], y[2], y[3]}, floatx4{y[4], y[5], y[6], y[7]}));
+        }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+    put(0, dkap, dk);
+    put(1, dnu, dv);
   }
 }
 
