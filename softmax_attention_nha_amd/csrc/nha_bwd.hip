@@ -1285,8 +1285,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
     const bf16* __restrict__ dqs, const float2* __restrict__ rcs, bf16* __restrict__ dq, int Tn, int H, int Hkv,
     int w, float scale) {
   constexpr int NT = NWV * 64, QT = 32 * NWV;
-  __shared__ bf16 kbuf[2][64 * D];
-  __shared__ bf16 vbuf[2][64 * D];
+  __shared__ bf16 kvbuf[4][64 * D];  // K tiles [0..1], V tiles [2..3]; then the output staging
   const int tid = threadIdx.x, W = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hf = l >> 5, c = l & 31,
             jj = l & 15;
   const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
@@ -1343,7 +1342,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
     const size_t ld = (size_t)Hkv * D;
     const bf16* kbase = kr + ((size_t)b * Tn * Hkv + hg) * D;
     const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * D;
-    const uint32_t kl = lds_addr(&kbuf[0][0]), vl = lds_addr(&vbuf[0][0]);
+    const uint32_t kl = lds_addr(&kvbuf[0][0]), vl = lds_addr(&kvbuf[2][0]);
     constexpr uint32_t TB = 64 * D * 2;
     const uint32_t ldo = dma_lane_off<D, NT, 2>(tid, ld);
     dma_tile_async<D, NT, 2>(kbase, ld, tile_j0(0), Tn, kl, ldo, tid);
@@ -1403,7 +1402,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
       __syncthreads();
     }
   }
-  if (qvalid) {
+  {
     // acc[dt][4 i + rr] = dq_rot[32 dt + 8 i + 4 hf + rr] / scale; rotate back by R_t^T
     constexpr int HT = D / 64 > 0 ? D / 64 : 1;  // column blocks per half (D >= 64)
     float out[D / 32][16];
@@ -1411,7 +1410,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) out[dt][e] = acc[dt][e] * scale;
-    if (rcs) {
+    if (rcs && qvalid) {
       if constexpr (D >= 64) {
         const float2* cs = rcs + (size_t)tq * (D / 2);
 #pragma unroll
@@ -1436,21 +1435,13 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dq_b16(
         }
       }
     }
-    const bf16* sl = dqs + qrow;  // (null: no slots)
-    bf16* dst = dq + qrow;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * dt + 8 * i + 4 * hf;
-        floatx4 s4 = zero4();
-        if (dqs) {
-          const bf16x4 x4 = ld4<bf16>(sl + d);
-          s4 = floatx4{(float)x4[0], (float)x4[1], (float)x4[2], (float)x4[3]};
-        }
-        st4<bf16>(dst + d, pack4<bf16>(floatx4{out[dt][4 * i] + s4[0], out[dt][4 * i + 1] + s4[1],
-                                                out[dt][4 * i + 2] + s4[2], out[dt][4 * i + 3] + s4[3]}));
-      }
+    // plus the slot part (null: no slots), written in whole rows through the
+    // K/V buffers (free after the last barrier; unused when w = 0)
+    static_assert(NWV * 32 * (D + 4) * 2 <= 4 * 64 * D * 2, "staging fits the tile buffers");
+    bf16* stg = &kvbuf[0][0] + W * 32 * (D + 4);
+    auto roff = [&](int row) { return (((size_t)b * Tn + (wl + row)) * H + h) * D; };
+    store_tile_rows<D>([&](int dt, int e) { return out[dt][e]; }, stg, dq, dqs, roff, [](int) { return true; },
+                       min(32, Tn - wl));
   }
 }
 
@@ -1812,49 +1803,16 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_bwd_dkdv_b16(
         }
       }
     }
-    constexpr int PS = D + 4, CPR = D / 8, RPI = 64 / CPR;
-    static_assert(NWV * 32 * PS * 2 <= 4 * 64 * D * 2, "staging fits the tile buffers");
-    bf16* stg = &qobuf[0][0] + W * 32 * PS;
+    static_assert(NWV * 32 * (D + 4) * 2 <= 4 * 64 * D * 2, "staging fits the tile buffers");
     // (total == 0: no tile was staged and no barrier passed; the buffers were
     // never used)
-    auto put = [&](int which, const bf16* slotp, bf16* out) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const floatx4 x = which == 0 ? floatx4{ok[dt][4 * i], ok[dt][4 * i + 1], ok[dt][4 * i + 2],
-                                                 ok[dt][4 * i + 3]}
-                                       : floatx4{accV[dt][4 * i], accV[dt][4 * i + 1], accV[dt][4 * i + 2],
-                                                 accV[dt][4 * i + 3]};
-          st4<bf16>(stg + c * PS + 32 * dt + 8 * i + 4 * hf, pack4<bf16>(x));
-        }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int k = 0; k < 32 / RPI; ++k) {
-        const int row = RPI * k + l / CPR, q = l % CPR, kr_ = kl + row;
-        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(stg + row * PS + 8 * q);
-        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(stg + row * PS + 8 * q + 4);
-        if (kr_ < Tn) {
-          const size_t rw = (((size_t)b * Tn + kr_) * Hkv + hg) * D + 8 * q;
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y[e] = (float)a0[e];
-            y[4 + e] = (float)a1[e];
-          }
-          // this key row is also absorbed (at step key + sh); null: no slots
-          if (slotp != nullptr && kr_ + sh < Tn) {
-            const bf16x8 z = ld8<bf16>(slotp + rw);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] += (float)z[e];
-          }
-          st8<bf16>(out + rw, pack8<bf16>(floatx4{y[0], y[1], y[2], y[3]}, floatx4{y[4], y[5], y[6], y[7]}));
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    };
-    put(0, dkap, dk);
-    put(1, dnu, dv);
+    bf16* stg = &qobuf[0][0] + W * 32 * (D + 4);
+    auto roff = [&](int row) { return (((size_t)b * Tn + (kl + row)) * Hkv + hg) * D; };
+    // this key row is also absorbed (at step key + sh); null: no slots
+    auto absorbed = [&](int row) { return kl + row + sh < Tn; };
+    const int nrows = min(32, Tn - kl);
+    store_tile_rows<D>([&](int dt, int e) { return ok[dt][e]; }, stg, dk, dkap, roff, absorbed, nrows);
+    store_tile_rows<D>([&](int dt, int e) { return accV[dt][e]; }, stg, dv, dnu, roff, absorbed, nrows);
   }
 }
 

@@ -466,6 +466,52 @@ __device__ __forceinline__ void dma_tile(const bf16* __restrict__ base, size_t l
   }
 }
 
+// A wave's 32 x D bf16 output tile in the 32x32 MFMA layout (lane (hf, c)
+// holds row c, columns 32 dt + 8 i + 4 hf + r as val(dt, 4 i + r)) goes out
+// through LDS: the lanes put 8-byte pieces into the wave's staging area stg
+// (32 rows, pitch D + 4: the 8-byte writes of a half-wave hit distinct banks),
+// then each lane writes 16 bytes of one row, so that every store instruction
+// covers whole rows.  out + row_off(r) receives row r (plus add + row_off(r)
+// when add_row(r)), for rows r with r < nrows.  stg is private to the wave;
+// on return its reads are complete.
+template <int D, typename Val, typename RowOff, typename AddRow>
+__device__ __forceinline__ void store_tile_rows(Val val, bf16* stg, bf16* __restrict__ out,
+                                                const bf16* __restrict__ add, RowOff row_off, AddRow add_row,
+                                                int nrows) {
+  constexpr int PS = D + 4, CPR = D / 8, RPI = 64 / CPR;
+  const int l = threadIdx.x & 63, hf = l >> 5, c = l & 31;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const floatx4 x{val(dt, 4 * i), val(dt, 4 * i + 1), val(dt, 4 * i + 2), val(dt, 4 * i + 3)};
+      st4<bf16>(stg + c * PS + 32 * dt + 8 * i + 4 * hf, pack4<bf16>(x));
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = RPI * k + l / CPR, q = l % CPR;
+    const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(stg + row * PS + 8 * q);
+    const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(stg + row * PS + 8 * q + 4);
+    if (row < nrows) {
+      const size_t ro = row_off(row) + 8 * q;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = (float)a0[e];
+        y[4 + e] = (float)a1[e];
+      }
+      if (add != nullptr && add_row(row)) {
+        const bf16x8 z = ld8<bf16>(add + ro);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] += (float)z[e];
+      }
+      st8<bf16>(out + ro, pack8<bf16>(floatx4{y[0], y[1], y[2], y[3]}, floatx4{y[4], y[5], y[6], y[7]}));
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // Wait for this wave's outstanding global loads (including the ones that
 // write LDS directly); a barrier must follow before other waves read them.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -1129,18 +1129,17 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
     }
   }
   const float z = sum_halves(zl);
-  if (qvalid) {
+  // o in whole rows through the K tile buffers (free after the last barrier;
+  // unused when w = 0)
+  {
     const float inv = 1.f / z;
-    bf16* dst = o + qrow;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st4<bf16>(dst + 32 * dt + 8 * i + 4 * hf,
-                  pack4<bf16>(floatx4{acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv, acc[dt][4 * i + 2] * inv,
-                                      acc[dt][4 * i + 3] * inv}));
-    if (hf == 0 && lse) lse[(size_t)bh * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
+    static_assert(NWV * 32 * (D + 4) * 2 <= 3 * 64 * D * 2, "staging fits the K tile buffers");
+    bf16* stg = &kbuf[0][0] + W * 32 * (D + 4);
+    auto roff = [&](int row) { return (((size_t)b * Tn + (wl + row)) * H + h) * D; };
+    store_tile_rows<D>([&](int dt, int e) { return acc[dt][e] * inv; }, stg, o, (const bf16*)nullptr, roff,
+                       [](int) { return false; }, min(32, Tn - wl));
   }
+  if (qvalid && hf == 0 && lse) lse[(size_t)bh * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
 }
 
 // ---------------------------------------------------------------- decode-state export
