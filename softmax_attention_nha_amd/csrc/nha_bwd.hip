@@ -1037,16 +1037,22 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
   if (tq < Tn) {
     float* da = dalpha + (((size_t)b * Tn + tq) * Hkv + hg) * m;
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb)
+    for (int mb = 0; mb < NB; ++mb) {
+      floatx4 v4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        int i = 16 * mb + 4 * g + r;
-        if (i < m) {
-          float v = 0.f;
-          if (absorb) v = sm.sW[urow * PG + i] / to_f<T>(sm.sA[urow * PM + i]) - F[mb][r];
-          da[i] = v;
-        }
+        const int i = 16 * mb + 4 * g + r;
+        v4[r] = absorb ? sm.sW[urow * PG + i] / to_f<T>(sm.sA[urow * PM + i]) - F[mb][r] : 0.f;
       }
+      const int i0 = 16 * mb + 4 * g;
+      if (m % 4 == 0 && i0 + 3 < m) {
+        *reinterpret_cast<floatx4*>(da + i0) = v4;  // (rows of m floats: 16-byte aligned)
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (i0 + r < m) da[i0 + r] = v4[r];
+      }
+    }
   }
 }
 
