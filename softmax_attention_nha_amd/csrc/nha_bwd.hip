@@ -121,13 +121,27 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ o, const
 //   accO (O^T[d][t]) += sum_i bt_t[i] Lam_t[i]
 //   F[mb][r]         += <Lam_t[i], key_t>
 // Cross-block pairs refer to F_I = G at the last row of the wave's block.
+//
+// With a pair table pf (bf16), sW holds the block-referenced weights
+// W_u[i] 2^{G_u - E_{J-1}} (u in block J; E_J = G at the last row of block J,
+// E_{-1} = 0; <= 1) and pf[pair_index(I, J)][i] = 2^{E_{J-1} - E_I}, so the
+// factor 2^{G_u - E_I} of a source row is one product of two LDS values; the
+// exact same-block path then reads the unscaled weights from wg (rows of MP
+// floats in global memory).  Without it (fp32) sW holds W itself.
+template <int NW>
+__host__ __device__ constexpr int pair_index(int I, int J) {
+  return I * NW - I * (I - 1) / 2 + (J - I);
+}
+
 template <typename T, int D, int MP, int C>
 __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const float* sW, const float* sG,
-                                         const T* sA, const typename Vec<T>::v8* keyf,
+                                         const T* sA, const float* pf, const float* wg,
+                                         const typename Vec<T>::v8* keyf,
                                          const float (&bwI)[MP / 16][4], const float (&bt)[MP / 16][4], int I,
                                          int t0, int w, int Tn, floatx4 (&accO)[D / 16], float (&F)[MP / 16][4]) {
   constexpr int NW = C / 16, NB = MP / 16, PD = pitch_of(D), PM = pitch_of(MP), PC = pitch_of(C);
   constexpr int PG = SlotPitch<MP>::PG;
+  constexpr bool TAB = sizeof(T) == 2;
   const int l = threadIdx.x & 63, g = l >> 4, cc = l & 15, r0 = 16 * I, urow = r0 + cc, rl = r0 + 15;
   // later blocks J > I, and (when factorizable) the block itself with u >= t;
   // one block per iteration (not unrolled: the blocks are independent and
@@ -148,15 +162,27 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
     if (J == I) aI = aJ;
     if (J > I || fast) {
       const int uA = 16 * J + cc;  // A-fragment row of this lane
+      const float* pj = TAB ? pf + pair_index<NW>(I, J) * MP : nullptr;
       floatx4 mt = zero4();        // M^T[u][t] = sum_i Y[u][i] bwI[t][i]
 #pragma unroll
       for (int s = 0; s < NB / 2; ++s) {
         float f[8];
+        if constexpr (TAB) {
+          const floatx4 p0 = *reinterpret_cast<const floatx4*>(&pj[32 * s + 4 * g]);
+          const floatx4 p1 = *reinterpret_cast<const floatx4*>(&pj[32 * s + 16 + 4 * g]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
-          f[r] = sW[uA * PG + i0] * fast_exp2(sG[uA * PG + i0] - sG[rl * PG + i0]);
-          f[4 + r] = sW[uA * PG + i1] * fast_exp2(sG[uA * PG + i1] - sG[rl * PG + i1]);
+          for (int r = 0; r < 4; ++r) {
+            int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
+            f[r] = sW[uA * PG + i0] * p0[r];
+            f[4 + r] = sW[uA * PG + i1] * p1[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int i0 = 32 * s + 4 * g + r, i1 = i0 + 16;
+            f[r] = sW[uA * PG + i0] * fast_exp2(sG[uA * PG + i0] - sG[rl * PG + i0]);
+            f[4 + r] = sW[uA * PG + i1] * fast_exp2(sG[uA * PG + i1] - sG[rl * PG + i1]);
+          }
         }
         typename Vec<T>::v8 bfr = pack8<T>(floatx4{bwI[2 * s][0], bwI[2 * s][1], bwI[2 * s][2], bwI[2 * s][3]},
                                            floatx4{bwI[2 * s + 1][0], bwI[2 * s + 1][1], bwI[2 * s + 1][2],
@@ -187,10 +213,16 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
       for (int mb = 0; mb < NB; ++mb) {
         const int iA = 16 * mb + cc;
         floatx4 y;
+        if constexpr (TAB) {
+          const float pa = pj[iA];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int u = 16 * J + 4 * g + r;
-          y[r] = sW[u * PG + iA] * fast_exp2(sG[u * PG + iA] - sG[rl * PG + iA]);
+          for (int r = 0; r < 4; ++r) y[r] = sW[(16 * J + 4 * g + r) * PG + iA] * pa;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            int u = 16 * J + 4 * g + r;
+            y[r] = sW[u * PG + iA] * fast_exp2(sG[u * PG + iA] - sG[rl * PG + iA]);
+          }
         }
         xs[mb] = mma16(xs[mb], pack4<T>(y), afr);
       }
@@ -224,8 +256,12 @@ __device__ __forceinline__ void slot_rev(const T* sVec, const T* sVecT, const fl
 #pragma unroll
       for (int mb = 0; mb < NB; ++mb) {
         floatx4 w4;
+        if constexpr (TAB) {
+          w4 = *reinterpret_cast<const floatx4*>(wg + (size_t)u * MP + 16 * mb + 4 * g);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w4[r] = sW[u * PG + 16 * mb + 4 * g + r];
+          for (int r = 0; r < 4; ++r) w4[r] = sW[u * PG + 16 * mb + 4 * g + r];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           F[mb][r] += Dp[mb][r] * w4[r] * Ad[uu];
@@ -841,6 +877,8 @@ struct SlotBwdBSmem {
   T sA[C * PM];
   float sG[C * SlotPitch<MP>::PG];
   float sW[C * SlotPitch<MP>::PG];  // s dl or p of one head [u][i]; later the (A - bF) tile
+  // bf16: the block-pair decay factors 2^{E_{J-1} - E_I} (J >= I) of slot_rev
+  alignas(16) float pf[TR ? (C / 16) * (C / 16 + 1) / 2 : 1][MP];
 };
 
 // grid (NC, B*Hkv), C/16 waves; all query heads of the KV group.
@@ -883,9 +921,16 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
   auto store_head = [&](const HeadTile& ht) {
 #pragma unroll
     for (int k = 0; k < WIT; ++k) {
-      const int e = (tid + k * NT) * 4, u = e / MP, i = e % MP;
+      const int e = (tid + k * NT) * 4, u = e / MP, i = e % MP, ub = (u & ~15) - 1;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.sW[u * PG + i + r] = ht.xw[k][r];
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (S::TR) {  // block-referenced: W_u 2^{G_u - E_{J-1}}
+          const float ep = ub >= 0 ? sm.sG[ub * PG + i + r] : 0.f;
+          sm.sW[u * PG + i + r] = ht.xw[k][r] * fast_exp2(sm.sG[u * PG + i + r] - ep);
+        } else {
+          sm.sW[u * PG + i + r] = ht.xw[k][r];
+        }
+      }
     }
     ht.tv.template store<PD>(sm.sVec, tid);
     if constexpr (!S::TR) ht.tvt.template store<PC>(sm.sVecT, tid);
@@ -923,6 +968,20 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
   gt.template stage<PG, PM>(sm.sG, sm.sA, t0, Tn, m, w, tid);
   __syncthreads();
   lds_col_cumsum<C, MP, PG, NT>(sm.sG, tid);
+  if constexpr (S::TR) {
+    // pair (I, J >= I): 2^{E_{J-1} - E_I}, clamped to 2^64 for J = I (used
+    // only when block I is factorizable, where it is <= 2^16); the side loop's
+    // first barrier comes before any read
+    constexpr int NW = C / 16;
+    for (int x = tid; x < NW * (NW + 1) / 2 * MP; x += NT) {
+      int p = x / MP, I0 = 0;
+      const int i = x % MP;
+      while (p >= NW - I0) p -= NW - I0++;
+      const int J0 = I0 + p;
+      const float ej = J0 > 0 ? sm.sG[(16 * J0 - 1) * PG + i] : 0.f;
+      sm.pf[pair_index<NW>(I0, J0)][i] = fast_exp2(fminf(ej - sm.sG[(16 * I0 + 15) * PG + i], 64.f));
+    }
+  }
   float bt[NB][4], bwI[NB][4], bwE[NB][4], F[NB][4];
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
@@ -1003,7 +1062,9 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
         store_head(hn);
         __syncthreads();
       }
-      slot_rev<T, D, MP, C>(sm.sVec, sm.sVecT, sm.sW, sm.sG, sm.sA, L.keyf, bwI, bt, I, t0, w, Tn, accO, F);
+      const float* wg = (side ? pp : sdl) + ((size_t)(b * H + hg * G + hh) * NC * C + t0) * MP;
+      slot_rev<T, D, MP, C>(sm.sVec, sm.sVecT, sm.sW, sm.sG, sm.sA, &sm.pf[0][0], wg, L.keyf, bwI, bt, I, t0, w,
+                            Tn, accO, F);
     }
     if (absorb) {
       T* dst = (side ? dnu : dkap) + (((size_t)b * Tn + (tq - w)) * Hkv + hg) * D;
