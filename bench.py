@@ -95,8 +95,11 @@ def stage_work(stage, wl, w, e):
     P^T dO, dS^T Q) in the backward; slot kernels, per query t >= w with c(t)
     earlier absorbed rows of its chunk, one read (2md + (2d+2m)c) and one mix
     (same) in the forward, two reads and one mix in pass A, two reverse reads
-    and two reverse mixes in pass B; scans 4md per absorbed token per KV head
-    (forward) and per token per query head (adjoint).
+    and two reverse mixes in pass B; the state scan 4md per absorbed token per
+    KV head; the adjoint's sources 4md per token per query head (bf16: in
+    pass A, which hands the scan per-chunk sums; the scan then takes 4 flops
+    per slot-state element per chunk and query head: decay, add, both sides;
+    fp32: in the scan).
 
     Algorithmic bytes: the operator's own tensors the kernel reads or writes,
     each once -- q, k, v, alpha, dO (inputs), o, dq, dk, dv, dalpha (outputs),
@@ -127,10 +130,11 @@ def stage_work(stage, wl, w, e):
         "slot_fwd": (fs, 2 * q_b + 2 * kv_b + a_b + row, B * H * NC * 2.0 * mp * d * e + (q_b + row if w else 0)),
         "win_fwd": (fw, q_b + 2 * kv_b, q_b + row),
         "bwd_prep": (0.0, 2 * q_b + row, 0.0),
-        "slot_bwd_a": (1.5 * fs, 3 * q_b + 2 * kv_b + a_b + 2 * row,
-                       B * H * NC * (2.0 * mp * d * e + 2.0 * mp * C * e + 12.0 * C * mp) + q_b),
-        "adj_scan": (4.0 * m * d * B * H * T, 2 * q_b,
-                     units * NC * (G * 2.0 * mp * C * e + 4.0 * mp + 2.0 * mp * d * e)),
+        "slot_bwd_a": (1.5 * fs + (4.0 * m * d * B * H * T if e == 2 else 0.0), 3 * q_b + 2 * kv_b + a_b + 2 * row,
+                       B * H * NC * (2.0 * mp * d * e + 2.0 * mp * (d if e == 2 else C) * e + 12.0 * C * mp) + q_b),
+        "adj_scan": ((4.0 * m * d * units * NC * G, 0.0, units * NC * (G * 2.0 * mp * d * e + 4.0 * mp + 2.0 * mp * d * e))
+                     if e == 2 else
+                     (4.0 * m * d * B * H * T, 2 * q_b, units * NC * (G * 2.0 * mp * C * e + 4.0 * mp + 2.0 * mp * d * e))),
         "slot_bwd_b": (2.0 * fs, 2 * kv_b + a_b + BT * Hkv * m * 4.0 + 2 * q_b,
                        units * NC * (2.0 * mp * d * e + 4.0 * mp + G * 12.0 * C * mp) + 2 * kv_b),
         "dalpha_tail": (0.0, a_b + 2 * BT * Hkv * m * 4.0, units * NC * mp * 4.0),
@@ -153,7 +157,9 @@ def roofline(stage, us, wl, w, e):
     peak = PEAK_TFLOPS[wl.dtype]
     tf = flops / dur / 1e12
     gbs = nbytes / dur / 1e9
-    mfma_bound = flops > 0 and flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    # (no algorithmic bytes -- a kernel on workspace intermediates only: the
+    # intensity is unbounded)
+    mfma_bound = flops > 0 and (nbytes == 0 or flops / nbytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9))
     r = {"kernel": stage}
     if mfma_bound:
         r.update(bound="mfma", achieved=round(tf, 2), peak=peak, unit="TFLOP/s", frac=round(tf / peak, 4))

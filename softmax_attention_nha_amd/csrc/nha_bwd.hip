@@ -24,9 +24,11 @@
 //
 // Kernels, in launch order (after the shared prologue: RoPE, gates, state scan):
 //   k_bwd_prep      D_t = <dO_t, o_t> (fp32; bf16 computes it in slot pass A)
-//   k_bwd_slot_a    per (b, h, chunk): slot p, dp, dl; dq's slot part;
-//                   adjoint weights 2^{G_u} s dl_u, 2^{G_u} p_u; A_t parts
-//   k_adj_scan      reverse over chunks: Lin_c for every chunk (MFMA)
+//   k_bwd_slot_a    per (b, h, chunk): slot p, dp, dl; dq's slot part; A_t
+//                   parts; the chunk's adjoint sources sum_u 2^{G_u} dS_u
+//                   (fp32: the weights 2^{G_u} s dl_u, 2^{G_u} p_u instead)
+//   k_adj_scan      reverse over chunks: Lin_c for every chunk (bf16:
+//                   elementwise on pass A's products; fp32: MFMA)
 //   k_bwd_slot_b    per (b, g, chunk): dk/dv slot parts, F, local dalpha
 //   k_dalpha_tail   dalpha += (sum of the later chunks' (A - b F)) / alpha
 //   k_win_bwd_dq    window dq (+ slot part) -> dq
@@ -42,7 +44,8 @@ struct BwdWs {
   size_t sst, wt, aend, qrot, krot, rcs;  // prologue (same meaning as the forward's)
   size_t dt;                         // D_t: [B][H][T] float
   size_t dqs;                        // slot part of dq: [B][T][H][d] dtype
-  size_t wp;                         // adjoint weights: [B*H][NC][2][mp][C] dtype
+  size_t wp;                         // fp32: adjoint weights [B*H][NC][2][mp][C]; bf16: the chunk
+                                     // products M [B*H][NC][2][d/16][mp][16]
   size_t sdl, pp, acon;              // [B*H][NC*C][mp] float
   size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp x d] dtype
                                      // (fp32 [i][d] rows, bf16 column blocks [d/16][i][16])
@@ -67,7 +70,7 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   L.dqs = off;
   off += align256((size_t)s.B * s.T * s.H * s.d * s.esz);
   L.wp = off;
-  off += align256(BH * s.NC * 2 * (size_t)s.mp * s.C * s.esz);
+  off += align256(BH * s.NC * 2 * (size_t)s.mp * (s.esz == 2 ? s.d : s.C) * s.esz);
   L.sdl = off;
   off += align256(BH * TT * s.mp * 4);
   L.pp = off;
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
     const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
     const bf16* __restrict__ alpha, const bf16* __restrict__ dO, const bf16* __restrict__ o,
     const bf16* __restrict__ sst, const float* __restrict__ lse, float* __restrict__ Dt, bf16* __restrict__ dqs,
-    bf16* __restrict__ wp,
+    bf16* __restrict__ madj,
     float* __restrict__ sdl, float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m,
     int w, int NC, float scale) {
   using S = SlotBwdASmemB16<D, MP, C>;
@@ -600,19 +603,25 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) st4<bf16>(dst + 16 * db + 4 * g, pack4<bf16>(accO[db] * scale));
   }
-  // adjoint weights 2^{G_u} s dl_u[i] and 2^{G_u} p_u[i], [i][u] layout:
-  // transposed through LDS (the row tiles are free once every wave is done)
-  // and written with 16-byte stores
+  // The chunk's part of the adjoint recurrence, for the reverse scan:
+  //   M^K[i][:] = sum_u 2^{G_u} s dl_u[i] q_u,   M^V[i][:] = sum_u 2^{G_u} p_u[i] dO_u
+  // (the weights and this lane's q / dO row go into LDS -- the row tiles are
+  // free once every wave is done -- then each wave takes some of the 16 x 16
+  // output blocks of M^T, a product over the chunk's rows).  Stored like the
+  // adjoint itself: per side, column blocks [d/16][i][16].
   float ew[NB][4];
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) ew[mb][r] = fast_exp2(sm.sG[urow * PG + 16 * mb + 4 * g + r]);
   __syncthreads();
-  constexpr int PW = C + 8;  // row pitch of the [i][u] staging tiles
-  static_assert(2 * MP * PW * sizeof(bf16) <= sizeof(S), "staging tiles fit the shared tiles");
+  constexpr int PW = C + 8;  // row pitch of the [i][u] weight tiles
+  static_assert(2 * MP * PW * sizeof(bf16) + 2 * C * PD * sizeof(bf16) <= sizeof(S),
+                "weight and row tiles fit the shared tiles");
   bf16* tw_k = reinterpret_cast<bf16*>(&sm);
   bf16* tw_v = tw_k + MP * PW;
+  bf16* tq_ = tw_v + MP * PW;  // q rows [u][d]
+  bf16* td_ = tq_ + C * PD;    // dO rows
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
@@ -621,13 +630,41 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
       tw_k[i * PW + urow] = (bf16)(ew[mb][r] * scale * dl[mb][r]);
       tw_v[i * PW + urow] = (bf16)(ew[mb][r] * p[mb][r]);
     }
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    *reinterpret_cast<bf16x8*>(&tq_[urow * PD + 32 * ks + 8 * g]) = qf[ks];
+    *reinterpret_cast<bf16x8*>(&td_[urow * PD + 32 * ks + 8 * g]) = df[ks];
+  }
   __syncthreads();
-  bf16* wk = wp + (((size_t)bh * NC + c) * 2) * MP * C;
-  bf16* wv = wk + (size_t)MP * C;
-  for (int e = tid * 8; e < MP * C; e += NT * 8) {
-    const int i = e / C, u = e % C;
-    st8<bf16>(wk + e, *reinterpret_cast<const bf16x8*>(&tw_k[i * PW + u]));
-    st8<bf16>(wv + e, *reinterpret_cast<const bf16x8*>(&tw_v[i * PW + u]));
+  bf16* mout = madj + ((size_t)bh * NC + c) * 2 * MP * D;
+  constexpr int NW = C / 16, NTILE = 2 * (D / 16) * NB;
+  for (int tt = I; tt < NTILE; tt += NW) {
+    const int side = tt / ((D / 16) * NB), db = (tt / NB) % (D / 16), nb = tt % NB;
+    const bf16* vec = side ? td_ : tq_;
+    const bf16* wt = side ? tw_v : tw_k;
+    const int i = 16 * nb + cc;
+    floatx4 acc = zero4();  // M^T[16 db + 4 g + r][16 nb + cc]
+    if constexpr (C % 32 != 0) {
+#pragma unroll
+      for (int s16 = 0; s16 < C / 16; ++s16) {
+        const bf16x4 a = ld_tr4(&vec[(16 * s16 + 4 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)]);
+        acc = mma16(acc, a, *reinterpret_cast<const bf16x4*>(&wt[i * PW + 16 * s16 + 4 * g]));
+      }
+    } else {
+#pragma unroll
+      for (int s32 = 0; s32 < C / 32; ++s32) {
+        const bf16* ap = &vec[(32 * s32 + 8 * g + (cc >> 2)) * PD + 16 * db + 4 * (cc & 3)];
+        const bf16x4 a0 = ld_tr4(ap), a1 = ld_tr4(ap + 4 * PD);
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = a0[e];
+          a[4 + e] = a1[e];
+        }
+        acc = mma32(acc, a, *reinterpret_cast<const bf16x8*>(&wt[i * PW + 32 * s32 + 8 * g]));
+      }
+    }
+    st4<bf16>(mout + (size_t)side * MP * D + (size_t)db * MP * 16 + i * 16 + 4 * g, pack4<bf16>(acc));
   }
 }
 
@@ -717,150 +754,61 @@ __global__ __launch_bounds__(64) void k_adj_scan(const T* __restrict__ q, const 
   store_slot_state<NB>(LK, LV, ds0k, ds0v, unit, m, d, j0, g, cc);
 }
 
-// bf16 variant: the operands of every (chunk, query head) step -- q and dO
-// rows of the wave's 16 columns, both adjoint weight tiles, aend -- stream
-// into an LDS ring NS steps ahead with direct-to-LDS loads (as in the
-// forward scan).  Steps run over chunks in reverse and over the group's
-// heads inside a chunk; the counter wait allows only the later stages'
-// loads to be outstanding (the state stores are not counted, which can only
-// make it wait longer).
-template <int C, int MP>
-struct AdjStage {
-  static constexpr int KB = C * 32;
-  static constexpr int WB = MP * C * 2;
-  static constexpr int NK = (KB + 1023) / 1024, NWI = WB / 1024;
-  static constexpr int OPS = 2 * NK + 2 * NWI + 1;
-  bf16 q[C * 16];
-  bf16 o[C * 16];
-  bf16 wk[MP * C];  // [i][u], 16-byte chunks XOR-swizzled by i
-  bf16 wv[MP * C];
-  float ae[64];
-};
-
-template <int C, int MP, int NS>
-__global__ __launch_bounds__(64) void k_adj_scan_b16(const bf16* __restrict__ q, const bf16* __restrict__ dO,
-                                                     const bf16* __restrict__ wp, const float* __restrict__ aend,
-                                                     bf16* __restrict__ lin, float* __restrict__ ds0k,
-                                                     float* __restrict__ ds0v, int Tn, int H, int Hkv, int d, int m,
-                                                     int NC) {
-  using St = AdjStage<C, MP>;
-  constexpr int NB = MP / 16, CPR = C / 8;
-  __shared__ St ring[NS];
-  const int l = threadIdx.x, g = l >> 4, cc = l & 15;
-  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
-  const int j0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * 16),
-            unit = __builtin_amdgcn_readfirstlane(L / gridDim.x);
-  const int b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+// bf16 variant on the chunk products M of slot pass A: each step is
+// elementwise, Lin_{c-1} = aend_c (.) Lin_c + sum_h M_{c,h}, over contiguous
+// rows.  grid (ceil(2 mp d / 2048), B*Hkv), 256 threads; a thread keeps 8
+// consecutive elements of one (side, column block, slot) row of the adjoint
+// in fp32 and walks the chunks in reverse (the group's heads inside a chunk),
+// its loads PF steps ahead in registers.
+template <int MP>
+__global__ __launch_bounds__(256) void k_adj_scan_m(const bf16* __restrict__ madj, const float* __restrict__ aend,
+                                                    bf16* __restrict__ lin, float* __restrict__ ds0k,
+                                                    float* __restrict__ ds0v, int H, int Hkv, int d, int m, int NC) {
+  constexpr int PF = 8;
+  const int unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  const int E = 2 * MP * d;  // adjoint elements per (unit, chunk): [2][d/16][mp][16]
+  const int x0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (x0 >= E) return;  // (no barriers below)
+  const int side = x0 / (MP * d), rr = x0 % (MP * d), db = rr / (MP * 16), i = (rr / 16) % MP, col = rr % 16;
   const int nsteps = NC * G;
-  const size_t ld = (size_t)H * d;
-  auto issue = [&](int n, int s) {
+  bf16x8 mr[PF];
+  float ar[PF];
+  auto load = [&](int n, int k) {
     n = min(n, nsteps - 1);
-    const int c = NC - 1 - n / G, hh = n % G, h = hg * G + hh, bh = b * H + h;
-    const uint32_t base = lds_addr(&ring[s]);
-    const bf16* qb = q + ((size_t)b * Tn * H + h) * d + j0;
-    const bf16* ob = dO + ((size_t)b * Tn * H + h) * d + j0;
-#pragma unroll
-    for (int i = 0; i < St::NK; ++i) {
-      const int e = i * 64 + l, u = e >> 1;
-      const int tr = min(c * C + u, Tn - 1);
-      const uint32_t off = (uint32_t)((size_t)tr * ld * 2 + 16 * (e & 1));
-      const uint32_t mq = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, q) + i * 1024);
-      const uint32_t mo = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, o) + i * 1024);
-      if (e * 16 < St::KB) {
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :
-                     : "s"(mq), "v"(off), "s"(sgpr_ptr(qb))
-                     : "memory", "m0");
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :
-                     : "s"(mo), "v"(off), "s"(sgpr_ptr(ob))
-                     : "memory", "m0");
-      }
-    }
-    const bf16* wks = wp + (((size_t)bh * NC + c) * 2) * MP * C;
-    const bf16* wvs = wks + (size_t)MP * C;
-#pragma unroll
-    for (int i = 0; i < St::NWI; ++i) {
-      const int e = i * 64 + l, r = e / CPR, p = e % CPR;
-      const uint32_t off = (uint32_t)(16 * (r * CPR + (p ^ (r & (CPR - 1)))));
-      const uint32_t mk = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, wk) + i * 1024);
-      const uint32_t mv = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, wv) + i * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :
-                   : "s"(mk), "v"(off), "s"(sgpr_ptr(wks))
-                   : "memory", "m0");
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :
-                   : "s"(mv), "v"(off), "s"(sgpr_ptr(wvs))
-                   : "memory", "m0");
-    }
-    {
-      const uint32_t off = (uint32_t)(4 * min(l, MP - 1));
-      const uint32_t ma = __builtin_amdgcn_readfirstlane(base + (uint32_t)offsetof(St, ae));
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                   :
-                   : "s"(ma), "v"(off), "s"(sgpr_ptr(aend + ((size_t)unit * NC + c) * MP))
-                   : "memory", "m0");
-    }
+    const int c = NC - 1 - n / G, hh = n % G;
+    mr[k] = ld8<bf16>(madj + ((size_t)(b * H + hg * G + hh) * NC + c) * E + x0);
+    ar[k] = aend[((size_t)unit * NC + c) * MP + i];
   };
-  floatx4 LK[NB], LV[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) LK[nb] = LV[nb] = zero4();
-  for (int s = 0; s < NS; ++s) issue(s, s);
-  for (int n = 0; n < nsteps; ++n) {
-    const int s = n % NS, c = NC - 1 - n / G, hh = n % G;
-    vm_wait<(NS - 1) * St::OPS>();
-    const St& R = ring[s];
-    if (hh == 0) {
-      // the adjoint entering chunk c from the right, both halves in column
-      // blocks [d/16][i][16] (one contiguous 2 KB piece per half for this wave)
-      bf16* dst = lin + ((size_t)unit * NC + c) * 2 * MP * d + (size_t)j0 * MP;
+  for (int k = 0; k < PF; ++k) load(k, k);
+  float La[8];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int i = 16 * nb + cc;
-        st4<bf16>(dst + i * 16 + 4 * g, pack4<bf16>(LK[nb]));
-        st4<bf16>(dst + (size_t)MP * d + i * 16 + 4 * g, pack4<bf16>(LV[nb]));
-        const float a = R.ae[i];
-        LK[nb] *= a;
-        LV[nb] *= a;
+  for (int e = 0; e < 8; ++e) La[e] = 0.f;
+  for (int n0 = 0; n0 < nsteps; n0 += PF) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int n = n0 + k;
+      if (n < nsteps) {
+        const int c = NC - 1 - n / G;
+        if (n % G == 0) {
+          // the adjoint entering chunk c from the right
+          st8<bf16>(lin + ((size_t)unit * NC + c) * E + x0,
+                    pack8<bf16>(floatx4{La[0], La[1], La[2], La[3]}, floatx4{La[4], La[5], La[6], La[7]}));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) La[e] *= ar[k];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) La[e] += (float)mr[k][e];
+        load(n + PF, k);
       }
     }
-    if constexpr (C % 32 != 0) {
-      const bf16x4 aq = ld_tr4(R.q + (4 * g + (cc >> 2)) * 16 + 4 * (cc & 3));
-      const bf16x4 ao = ld_tr4(R.o + (4 * g + (cc >> 2)) * 16 + 4 * (cc & 3));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int i = 16 * nb + cc, woff = i * C + 8 * ((g >> 1) ^ (i & (CPR - 1))) + 4 * (g & 1);
-        LK[nb] = mma16(LK[nb], aq, *reinterpret_cast<const bf16x4*>(R.wk + woff));
-        LV[nb] = mma16(LV[nb], ao, *reinterpret_cast<const bf16x4*>(R.wv + woff));
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < C / 32; ++ks) {
-      const bf16* qp = R.q + (32 * ks + 8 * g + (cc >> 2)) * 16 + 4 * (cc & 3);
-      const bf16* op = R.o + (32 * ks + 8 * g + (cc >> 2)) * 16 + 4 * (cc & 3);
-      const bf16x4 q0 = ld_tr4(qp), q1 = ld_tr4(qp + 4 * 16), o0 = ld_tr4(op), o1 = ld_tr4(op + 4 * 16);
-      bf16x8 aq, ao;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        aq[e] = q0[e];
-        aq[4 + e] = q1[e];
-        ao[e] = o0[e];
-        ao[4 + e] = o1[e];
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int i = 16 * nb + cc, woff = i * C + 8 * ((4 * ks + g) ^ (i & (CPR - 1)));
-        LK[nb] = mma32(LK[nb], aq, *reinterpret_cast<const bf16x8*>(R.wk + woff));
-        LV[nb] = mma32(LV[nb], ao, *reinterpret_cast<const bf16x8*>(R.wv + woff));
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    issue(n + NS, s);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // the adjoint carried to before the first token: the initial states' gradient
-  store_slot_state<NB>(LK, LV, ds0k, ds0v, unit, m, d, j0, g, cc);
+  if (ds0k && i < m) {
+    float* dst = (side ? ds0v : ds0k) + ((size_t)unit * m + i) * d + 16 * db + col;
+    *reinterpret_cast<floatx4*>(dst) = floatx4{La[0], La[1], La[2], La[3]};
+    *reinterpret_cast<floatx4*>(dst + 4) = floatx4{La[4], La[5], La[6], La[7]};
+  }
 }
 
 // ---------------------------------------------------------------- slot pass B
@@ -1978,14 +1926,13 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     // the adjoint scan and pass B, and beside them on the side stream the
     // window dq (needs D_t and the slot part of dq; nothing after it reads
     // dq), enqueued after the scan so that the scan's workgroups are placed
-    // first.  A two-stage ring (41 KB of LDS) leaves room for a dq workgroup
-    // (64 KB) beside two scan waves on a CU and is as fast alone as three
-    // stages.
+    // first (the bf16 scan holds no LDS: a dq workgroup fits beside it).
     fk.record(st);
     mk.mark(st);
     if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((k_adj_scan_b16<C, MP, 2>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
-                         (const float*)pp.aend, lin, p.ds0k, p.ds0v, s.T, s.H, s.Hkv, D, s.m, s.NC);
+      hipLaunchKernelGGL((k_adj_scan_m<MP>), dim3((2 * MP * D + 2047) / 2048, units), dim3(256), 0, st,
+                         (const bf16*)wpb, (const float*)pp.aend, (bf16*)lin, p.ds0k, p.ds0v, s.H, s.Hkv, D, s.m,
+                         s.NC);
     else
       hipLaunchKernelGGL((k_adj_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
                          (const float*)pp.aend, lin, p.ds0k, p.ds0v, s.T, s.H, s.Hkv, D, s.m, s.NC);
