@@ -50,14 +50,23 @@
  *     hipStreamNonBlocking) and two events (timing disabled), created by the
  *     first nha_fwd, nha_fwd_s0, nha_bwd, nha_bwd_after_fwd or nha_bwd_s0 call
  *     of that thread on that device, kept until nha_release_side_streams().
- *     Those calls fork independent launches onto the side stream (RoPE beside
- *     the slot-state scan; the window dq beside the adjoint scan; the dalpha
- *     carry beside the window dk/dv) after an event recorded on `stream`, and
+ *     Those calls fork independent launches onto the side stream (the window
+ *     branch -- RoPE, then band attention -- beside the gate products and the
+ *     slot-state scan; the window dq beside the adjoint scan and slot pass B;
+ *     the dalpha carry beside the window dk/dv) after an event recorded on
+ *     `stream`, and
  *     make `stream` wait for the side stream before they return, so each call
  *     still behaves as one operation ordered on `stream`.  If the side
  *     stream cannot be created, every launch goes on `stream`.  The *_timed
  *     calls with non-NULL events, the decode step and nha_fwd_noalloc never
  *     use it.  Results are bitwise the same either way.
+ *
+ * Graph capture: the calls enqueue kernel launches and event records / waits
+ * only (no memset, no allocation, no host synchronisation), so a sequence of
+ * them on `stream` can be captured into a HIP graph and replayed; the side
+ * stream joins the capture through its event waits.  Tested: nha_fwd then
+ * nha_bwd_after_fwd captured once and replayed, with eager calls in between,
+ * bitwise equal to the eager results at every replay.
  *   - nha_fwd_noalloc's scratch array (see there).
  *
  * Errors: every argument check runs on the host before any HIP call and
