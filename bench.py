@@ -129,6 +129,10 @@ def stage_work(stage, wl, w, e):
         # merges it and writes o and lse
         "slot_fwd": (fs, 2 * q_b + 2 * kv_b + a_b + row, B * H * NC * 2.0 * mp * d * e + (q_b + row if w else 0)),
         "win_fwd": (fw, q_b + 2 * kv_b, q_b + row),
+        # both branches in one kernel (bf16, C = 64): q, RoPE'd q / k, v, the
+        # absorbed k / v rows, alpha read, o and lse written; the chunk-start
+        # states read
+        "chunk_fwd": (fw + fs, 2 * q_b + 2 * kv_b + a_b + row, B * H * NC * 2.0 * mp * d * e + q_b + kv_b),
         "bwd_prep": (0.0, 2 * q_b + row, 0.0),
         "slot_bwd_a": (1.5 * fs + (4.0 * m * d * B * H * T if e == 2 else 0.0), 3 * q_b + 2 * kv_b + a_b + 2 * row,
                        B * H * NC * (2.0 * mp * d * e + 2.0 * mp * (d if e == 2 else C) * e + 12.0 * C * mp) + q_b),
@@ -319,12 +323,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 STAGE_KERNEL = {  # stage name -> kernel symbol fragment in the profiler's output
     "slot_bwd_b": "k_bwd_slot_b", "slot_bwd_a": "k_bwd_slot_a", "slot_fwd": "k_slot_fwd", "win_fwd": "k_win_fwd",
     "win_bwd_dq": "k_win_bwd_dq", "win_bwd_dkdv": "k_win_bwd_dkdv", "adj_scan": "k_adj_scan",
-    "state_scan": "k_state_scan",
+    "state_scan": "k_state_scan", "chunk_fwd": "k_chunk_fwd",
 }
 
 
 # translation unit of each kernel that counters are taken for
 KERNEL_SOURCE = {"k_bwd_slot_b": "nha_bwd.hip", "k_bwd_slot_a": "nha_bwd.hip", "k_adj_scan": "nha_bwd.hip",
+                 "k_chunk_fwd": "nha_fwd.hip",
                  "k_win_bwd_dq": "nha_bwd.hip", "k_win_bwd_dkdv": "nha_bwd.hip", "k_slot_fwd": "nha_fwd.hip",
                  "k_win_fwd": "nha_fwd.hip", "k_state_scan": "nha_fwd.hip"}
 

@@ -608,19 +608,21 @@ struct SlotFwdSmemB16 {
   SlotTab<C, MP> tab;
 };
 
-template <int D, int MP, int C>
-__global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
-    const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
-    const bf16* __restrict__ alpha, const bf16* __restrict__ sst, const bf16* __restrict__ oW,
-    const float* __restrict__ lseW, bf16* __restrict__ oL, float* __restrict__ lseL, int Tn, int H, int Hkv, int m,
-    int w, int NC, float scale) {
+// One chunk's slot branch for the calling wave's 16 rows (chunk c of head
+// bh, LDS in sm): accO (unnormalised read, O^T layout [16 db + 4 g + r][row
+// cc]), its sum zs and maximum mx (log2 units).  mid() runs right after the
+// logits (its loads then overlap the softmax and the output phase).
+template <int D, int MP, int C, typename Mid>
+__device__ __forceinline__ void slot_chunk_b16(SlotFwdSmemB16<D, MP, C>& sm, const bf16* __restrict__ q,
+                                               const bf16* __restrict__ kk, const bf16* __restrict__ vv,
+                                               const bf16* __restrict__ alpha, const bf16* __restrict__ sst, int c,
+                                               int bh, int Tn, int H, int Hkv, int m, int w, int NC, float scale,
+                                               Mid mid, floatx4 (&accO)[D / 16], float& zs, float& mx) {
   using S = SlotFwdSmemB16<D, MP, C>;
   constexpr int NW = C / 16, NT = NW * 64, NB = MP / 16, PD = S::PD, PM = S::PM;
   constexpr int PG = SlotPitch<MP>::PG;
-  __shared__ S sm;
   const int tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
-  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
-  const int c = L % NC, bh = L / NC, b = bh / H, h = bh % H, G = H / Hkv, hg = h / G;
+  const int b = bh / H, h = bh % H, G = H / Hkv, hg = h / G;
   const int unit = b * Hkv + hg, t0 = c * C;
   const bf16* src = sst + ((size_t)unit * NC + c) * 2 * MP * D;
   // chunk row u <-> token t0 + u, absorbing key row t0 + u - w when t0 + u >= w
@@ -662,13 +664,10 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   tnu.load(vv + rbase * D, (size_t)Hkv * D, w - t0, Tn - t0, tid);
   float lg[NB][4];
   slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg, &sm.tab);
-  // the window branch's read for this lane's row (its query row registers
-  // are free now): in flight during the slot softmax and the output phase
-  WinPartial<bf16, D> wp;
-  wp.load(oW, lseW, b, h, qvalid ? tq : Tn - 1, Tn, H, g);
+  mid();
   // softmax partial over the m slots (log2 domain)
   const float sl2 = scale * NHA_LOG2E;
-  float mx = -INFINITY;
+  mx = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
@@ -678,7 +677,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
       mx = fmaxf(mx, lg[mb][r]);
     }
   mx = max_over_g(mx);
-  float zs = 0.f;
+  zs = 0.f;
   float p[NB][4];
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb)
@@ -692,10 +691,30 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
   tsv.template store<PD>(sm.tS, tid);
   tnu.template store<PD>(sm.tK, tid);
   __syncthreads();
-  floatx4 accO[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) accO[db] = zero4();
   slot_mix<bf16, D, MP, C, PD, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, p, I, t0, w, Tn, accO, &sm.tab);
+}
+
+template <int D, int MP, int C>
+__global__ __launch_bounds__(C / 16 * 64, 2) void k_slot_fwd_b16(
+    const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
+    const bf16* __restrict__ alpha, const bf16* __restrict__ sst, const bf16* __restrict__ oW,
+    const float* __restrict__ lseW, bf16* __restrict__ oL, float* __restrict__ lseL, int Tn, int H, int Hkv, int m,
+    int w, int NC, float scale) {
+  __shared__ SlotFwdSmemB16<D, MP, C> sm;
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int c = L % NC, bh = L / NC, b = bh / H, h = bh % H;
+  const int g = (threadIdx.x & 63) >> 4, tq = c * C + 16 * (threadIdx.x >> 6) + (threadIdx.x & 15);
+  const bool qvalid = tq < Tn;
+  // the window branch's read for this lane's row, issued after the logits
+  // (the query row registers are free then): in flight during the slot
+  // softmax and the output phase
+  WinPartial<bf16, D> wp;
+  floatx4 accO[D / 16];
+  float zs, mx;
+  slot_chunk_b16<D, MP, C>(sm, q, kk, vv, alpha, sst, c, bh, Tn, H, Hkv, m, w, NC, scale,
+                           [&]() { wp.load(oW, lseW, b, h, qvalid ? tq : Tn - 1, Tn, H, g); }, accO, zs, mx);
   if (qvalid) wp.store(accO, zs, mx, oL, lseL, b, h, tq, Tn, H, g);
 }
 
@@ -898,21 +917,21 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd(const T* __restrict__ q
 // runs on the vector ALUs, the matrix cores already compute the scores of
 // tile i+1; masks enter as -inf in the initial value of the score
 // accumulators, so only the tiles that cross the band's edges pay for them.
-template <int D, int NWV>
-__global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restrict__ qr, const bf16* __restrict__ kr,
-                                                             const bf16* __restrict__ vv, const bf16* __restrict__ oL,
-                                                             const float* __restrict__ lseL, bf16* __restrict__ o,
-                                                             float* __restrict__ lse, int Tn, int H, int Hkv, int w,
-                                                             float scale) {
+// The band of the workgroup's QT = 32 NWV queries q0 .. of head bh, with
+// its K / V tiles in kbuf (3 tiles) and vbuf (2 tiles) of LDS; seed(acc, mu,
+// zl, qrow, tqc, qvalid) starts each lane's online softmax (an empty one, or
+// a partial softmax of the same row).  SYNC: a barrier between the seed and
+// the first tile loads (the seed may then sit in the tile buffers).
+template <int D, int NWV, bool SYNC, typename Seed>
+__device__ __forceinline__ void win_band_b16(bf16 (*kbuf)[64 * D], bf16 (*vbuf)[64 * D], const bf16* __restrict__ qr,
+                                             const bf16* __restrict__ kr, const bf16* __restrict__ vv,
+                                             bf16* __restrict__ o, float* __restrict__ lse, int q0, int bh, int Tn,
+                                             int H, int Hkv, int w, float scale, Seed seed) {
   constexpr int NT = NWV * 64, QT = 32 * NWV;
-  __shared__ bf16 kbuf[3][64 * D];
-  __shared__ bf16 vbuf[2][64 * D];
   // wave-uniform quantities are pinned to scalar registers (integer division
   // is expanded on the vector ALUs otherwise)
   const int tid = threadIdx.x, W = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, hf = l >> 5, c = l & 31,
             jj = l & 15;
-  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
-  const int q0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * QT), bh = __builtin_amdgcn_readfirstlane(L / gridDim.x);
   const int b = __builtin_amdgcn_readfirstlane(bh / H), h = __builtin_amdgcn_readfirstlane(bh % H),
             hg = __builtin_amdgcn_readfirstlane(h / (H / Hkv));
   const int wl = q0 + 32 * W;
@@ -923,24 +942,10 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8_sel<bf16>(qr + qrow + 16 * ks + 8 * hf, qvalid);
-  // seed with the slot partial, or (no slots) an empty softmax
-  const bool seeded = oL != nullptr;
-  const float lse_l = seeded ? lseL[(size_t)bh * Tn + tqc] : 0.f;  // unconditional load (clamped row)
-  float mu = qvalid ? (seeded ? lse_l * NHA_LOG2E : kEmptyMax) : 0.f;
-  float zl = (hf == 0 && seeded) ? 1.f : 0.f;
+  float mu, zl;
   floatx16 acc[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    acc[dt] = zero16();
-    if (seeded) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4 x = ld4<bf16>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? (float)x[rr] : 0.f;
-      }
-    }
-  }
+  seed(acc, mu, zl, qrow, tqc, qvalid);
+  if constexpr (SYNC) __syncthreads();
   // per-lane LDS element offsets of the K fragments (row c, logical chunk
   // 2 ks + hf) and of the transposed V reads (rows 4 hf + jj / 4 (+8) of each
   // 16-row step, columns 32 dt + 16 (c / 16) + 4 (jj % 4) ..)
@@ -1142,6 +1147,122 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restr
   if (qvalid && hf == 0 && lse) lse[(size_t)bh * Tn + tq] = (mu + __log2f(z)) * NHA_LN2;
 }
 
+template <int D, int NWV>
+__global__ __launch_bounds__(NWV * 64, 2) void k_win_fwd_b16(const bf16* __restrict__ qr, const bf16* __restrict__ kr,
+                                                             const bf16* __restrict__ vv, const bf16* __restrict__ oL,
+                                                             const float* __restrict__ lseL, bf16* __restrict__ o,
+                                                             float* __restrict__ lse, int Tn, int H, int Hkv, int w,
+                                                             float scale) {
+  constexpr int QT = 32 * NWV;
+  __shared__ bf16 kbuf[3][64 * D];
+  __shared__ bf16 vbuf[2][64 * D];
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int q0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * QT), bh = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  // seed with the slot partial (o_L / Z_L and lse_L in the workspace), or (no
+  // slots) an empty softmax
+  auto seed = [&](floatx16(&acc)[D / 32], float& mu, float& zl, size_t qrow, int tqc, bool qvalid) {
+    const int hf = (threadIdx.x & 63) >> 5;
+    const bool seeded = oL != nullptr;
+    const float lse_l = seeded ? lseL[(size_t)bh * Tn + tqc] : 0.f;  // unconditional load (clamped row)
+    mu = qvalid ? (seeded ? lse_l * NHA_LOG2E : kEmptyMax) : 0.f;
+    zl = (hf == 0 && seeded) ? 1.f : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      acc[dt] = zero16();
+      if (seeded) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x4 x = ld4<bf16>(oL + qrow + 32 * dt + 8 * i + 4 * hf);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? (float)x[rr] : 0.f;
+        }
+      }
+    }
+  };
+  win_band_b16<D, NWV, false>(kbuf, vbuf, qr, kr, vv, o, lse, q0, bh, Tn, H, Hkv, w, scale, seed);
+}
+
+// ---------------------------------------------------------------- forward chunk kernel
+// Both branches of a query tile in one workgroup (bf16, C = 64; the chunk
+// computation of the Paper-Notes page, section 关键设计 > Chunkwise 并行计算:
+// the slot logits and the window logits of a chunk's queries under one
+// softmax, then both aggregations).  grid (ceil(T / 128), B*H), 4 waves.
+// The tile's two chunks first run the slot branch (one after the other, the
+// first chunk's partial kept in registers); both partials -- o_L / Z_L in
+// bf16 and lse_L -- then go into LDS, and the window band starts its online
+// softmax from them (the partial as one key of logit lse_L and value
+// o_L / Z_L) and writes o and lse.  The slot and window phases share the
+// LDS (80 KB, two workgroups per CU); the chunk-start states come from the
+// state scan and the RoPE'd q / k from the RoPE pass.  Co-resident
+// workgroups in different phases overlap the slot branch's memory traffic
+// with the window branch's products, and the window partial makes no HBM
+// round trip.
+template <int D, int MP>
+struct ChunkFwdLds {
+  static constexpr int C = 64, QT = 32 * kWinWaves, SP = D + 8;
+  static_assert(QT == 2 * C, "a window tile is two chunks");
+  static constexpr size_t SLOT = sizeof(SlotFwdSmemB16<D, MP, C>), WIN = 5 * 64 * D * 2,
+                          SEED = (size_t)QT * SP * 2 + QT * 4;
+  static constexpr size_t BYTES = SLOT > WIN ? (SLOT > SEED ? SLOT : SEED) : (WIN > SEED ? WIN : SEED);
+};
+
+template <int D, int MP>
+__global__ __launch_bounds__(kWinWaves * 64, 2) void k_chunk_fwd_b16(
+    const bf16* __restrict__ q, const bf16* __restrict__ kk, const bf16* __restrict__ vv,
+    const bf16* __restrict__ alpha, const bf16* __restrict__ sst, const bf16* __restrict__ qr,
+    const bf16* __restrict__ kr, bf16* __restrict__ o, float* __restrict__ lse, int Tn, int H, int Hkv, int m,
+    int w, int sh, int NC, float scale) {
+  using Lay = ChunkFwdLds<D, MP>;
+  constexpr int C = Lay::C, QT = Lay::QT, SP = Lay::SP;
+  __shared__ __align__(16) unsigned char smem[Lay::BYTES];
+  auto& sm = *reinterpret_cast<SlotFwdSmemB16<D, MP, C>*>(smem);
+  const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int tile = __builtin_amdgcn_readfirstlane(L % gridDim.x), bh = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  const int q0 = tile * QT, tid = threadIdx.x, I = tid >> 6, l = tid & 63, g = l >> 4, cc = l & 15;
+  // slot branch of the two chunks (the second one may lie past the end)
+  floatx4 a0[D / 16], a1[D / 16];
+  float z0, m0, z1 = 1.f, m1 = 0.f;
+  slot_chunk_b16<D, MP, C>(sm, q, kk, vv, alpha, sst, 2 * tile, bh, Tn, H, Hkv, m, sh, NC, scale, []() {}, a0, z0,
+                           m0);
+  const bool two = 2 * tile + 1 < NC;
+  if (two) {
+    __syncthreads();  // every wave is done with the first chunk's tiles
+    slot_chunk_b16<D, MP, C>(sm, q, kk, vv, alpha, sst, 2 * tile + 1, bh, Tn, H, Hkv, m, sh, NC, scale, []() {},
+                             a1, z1, m1);
+  }
+  __syncthreads();
+  // the partials into LDS: rows [QT][SP] of o_L / Z_L (bf16), then lse_L
+  // (log2 units) per row
+  bf16* so = reinterpret_cast<bf16*>(smem);
+  float* sl = reinterpret_cast<float*>(smem + (size_t)QT * SP * 2);
+  auto put = [&](int ch, const floatx4(&a)[D / 16], float z, float mxv) {
+    const int row = ch * C + 16 * I + cc;
+    const float inv = 1.f / z;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) st4<bf16>(so + row * SP + 16 * db + 4 * g, pack4<bf16>(a[db] * inv));
+    if (g == 0) sl[row] = mxv + __log2f(z);
+  };
+  put(0, a0, z0, m0);
+  if (two) put(1, a1, z1, m1);
+  __syncthreads();
+  // each lane's row of the window tile (wave W, lane c: query q0 + 32 W + c)
+  auto seed = [&](floatx16(&acc)[D / 32], float& mu, float& zl, size_t, int, bool qvalid) {
+    const int hf = (threadIdx.x & 63) >> 5, row = 32 * (threadIdx.x >> 6) + (threadIdx.x & 31);
+    mu = qvalid ? sl[row] : 0.f;
+    zl = hf == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(so + row * SP + 32 * dt + 8 * i + 4 * hf);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[dt][4 * i + rr] = qvalid ? (float)x[rr] : 0.f;
+      }
+  };
+  bf16(*kb)[64 * D] = reinterpret_cast<bf16(*)[64 * D]>(smem);
+  win_band_b16<D, kWinWaves, true>(kb, kb + 3, qr, kr, vv, o, lse, q0, bh, Tn, H, Hkv, w, scale, seed);
+}
+
 // ---------------------------------------------------------------- decode-state export
 // Ring rows for positions max(0, T-w) .. T-1 (raw keys, values and, with
 // RoPE, the RoPE'd keys the forward computed) and the position counter; row j
@@ -1279,7 +1400,25 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
                            ws_, qr, kr, v, seed, seed_lse, out, lse_out, s.T, s.H, s.Hkv, s.w, s.scale);
       }
     };
-    if (s.m > 0 && s.win && !p.separate) {
+    if (s.m > 0 && s.win && !p.separate && chunk_fused(s)) {
+      // both branches in the chunk kernel, after the gate products and the
+      // slot-state scan; RoPE on the side stream beside them
+      if constexpr (sizeof(T) == 2 && C == 64) {
+        fk.record(st);
+        mk.mark(st);
+        launch_gates<T, C, MP>(s, alpha, pp, st);
+        mk.mark(st);
+        launch_scan<T, D, C, MP>(s, k, v, pp, st);
+        if (s.rope) {
+          launch_rope<T>(s, th, q, k, pp, mk, fk.follow(st));
+          fk.join(st);
+        }
+        mk.mark(st);
+        hipLaunchKernelGGL((k_chunk_fwd_b16<D, MP>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
+                           dim3(kWinWaves * 64), 0, st, q, k, v, alpha, (const T*)pp.sst, qr, kr, (T*)p.o, p.lse,
+                           s.T, s.H, s.Hkv, s.m, s.w, s.sh, s.NC, s.scale);
+      }
+    } else if (s.m > 0 && s.win && !p.separate) {
       // both branches: the window branch (RoPE, then band attention from an
       // empty softmax into the workspace) on the side stream, beside the gate
       // products and the slot-state scan it does not depend on; the slot
@@ -1400,8 +1539,12 @@ int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
     all[n++] = "rope_cs";
     all[n++] = "rope";
   }
-  if (s.win) all[n++] = "win_fwd";  // (first: the slot kernel merges it)
-  if (s.m > 0) all[n++] = "slot_fwd";
+  if (s.m > 0 && s.win && chunk_fused(s)) {
+    all[n++] = "chunk_fwd";
+  } else {
+    if (s.win) all[n++] = "win_fwd";  // (first: the slot kernel merges it)
+    if (s.m > 0) all[n++] = "slot_fwd";
+  }
   if (with_state) all[n++] = "export_state";
   for (int i = 0; i < n && i < max && names; ++i) names[i] = all[i];
   return n;

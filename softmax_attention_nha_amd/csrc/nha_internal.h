@@ -31,6 +31,11 @@ struct Shape {
   int esz;    // element bytes
 };
 
+// The forward runs both branches in one chunk kernel (bf16 inputs, C = 64:
+// a 128-query window tile is two chunks); otherwise a window kernel and a
+// slot kernel joined through the window partial in the workspace.
+inline bool chunk_fused(const Shape& s) { return s.esz == 2 && s.C == 64; }
+
 constexpr size_t kMaxLds = 160 * 1024;  // LDS bytes per workgroup on gfx950
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
