@@ -7,9 +7,11 @@
 // the linear-channel (slot) logits come from cumulative / reverse gate
 // products, the window logits are ordinary shifted-window attention, both
 // enter one softmax, and the two value aggregations are summed.  Here the two
-// branches run in separate kernels and meet through the standard merge of two
-// partial softmaxes (the slot branch is handed to the window branch as one
-// "super key" with logit lse_L and value o_L / Z_L), which is exact.
+// branches meet through the standard merge of two partial softmaxes (the slot
+// branch is handed to the window branch as one "super key" with logit lse_L
+// and value o_L / Z_L), which is exact: inside one chunk kernel (bf16, C = 64,
+// when the state scan has enough waves to fill the chip), or in a window
+// kernel and a slot kernel that merges the window partial.
 //
 // Per (batch b, KV head g), with a_t = alpha_t and b_t = 1 - alpha_t for
 // t >= w (a_t = 1, b_t = 0 before: nothing is absorbed yet), kappa_t = k_{t-w},
@@ -27,8 +29,12 @@
 //   k_rope          q, k -> R_t q, R_t k (rotate-half RoPE, fp64 angle reduction)
 //   k_chunk_gates   per chunk: W^T[i][u] = 2^{G_end - G_u} b_u and 2^{G_end}
 //   k_state_scan    sequential over chunks: S at every chunk start (MFMA)
-//   k_slot_fwd      slot logits, their softmax partial and o_L (MFMA)
-//   k_win_fwd       band-masked window attention seeded with the slot partial
+//   k_chunk_fwd_b16 both branches of a 128-query tile: the slot partial of
+//                   its two chunks, then the window band seeded with it (MFMA)
+// or, in place of the chunk kernel,
+//   k_win_fwd       band-masked window attention from an empty softmax
+//                   (beside the gate products and the scan, on the side stream)
+//   k_slot_fwd      slot logits and their partial, merged with the window's (MFMA)
 //   k_export_state  ring buffer + position of the decode state (optional)
 #include "nha_common.h"
 #include "nha_internal.h"

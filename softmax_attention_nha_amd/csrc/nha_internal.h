@@ -32,9 +32,15 @@ struct Shape {
 };
 
 // The forward runs both branches in one chunk kernel (bf16 inputs, C = 64:
-// a 128-query window tile is two chunks); otherwise a window kernel and a
-// slot kernel joined through the window partial in the workspace.
-inline bool chunk_fused(const Shape& s) { return s.esz == 2 && s.C == 64; }
+// a 128-query window tile is two chunks) when the slot-state scan has at
+// least 256 waves (one per batch row, KV head and 16 state columns): the scan
+// walks the chunks in order, and with fewer waves the chip is mostly idle
+// while it runs, so a separate window kernel, which needs no states and runs
+// beside the scan on the side stream, does better.  Otherwise a window kernel
+// and a slot kernel joined through the window partial in the workspace.
+inline bool chunk_fused(const Shape& s) {
+  return s.esz == 2 && s.C == 64 && (long long)s.B * s.Hkv * (s.d / 16) >= 256;
+}
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS bytes per workgroup on gfx950
 

@@ -147,6 +147,31 @@ def test_stage_lists():
     assert full[:len(full) - len(after)] == fwd[:len(full) - len(after)]
 
 
+@pytest.mark.parametrize("B,H,Hkv,d,C,dtype,fused", [
+    (4, 16, 16, 128, 64, torch.bfloat16, True),   # 512 scan waves
+    (2, 16, 16, 128, 64, torch.bfloat16, True),   # 256
+    (8, 8, 8, 64, 64, torch.bfloat16, True),      # 256 at d = 64
+    (1, 16, 16, 128, 64, torch.bfloat16, False),  # 128
+    (1, 32, 8, 128, 64, torch.bfloat16, False),   # 64
+    (4, 8, 4, 64, 64, torch.bfloat16, False),     # 64
+    (4, 16, 16, 128, 32, torch.bfloat16, False),  # chunk of 32: not two per 128-query tile
+    (8, 8, 8, 64, 64, torch.float32, False),      # fp32 path
+])
+def test_forward_kernel_choice(B, H, Hkv, d, C, dtype, fused):
+    """The one-kernel forward (both branches per 128-query tile) is taken for
+    bf16 with C = 64 when the state scan has at least 256 waves (one per batch
+    row, KV head and 16 state columns); otherwise window + slot kernels."""
+    dd = nha.make_desc(B, 2048, H, Hkv, d, 64, 512, C, 10000.0, 0.0, dtype)
+    names = nha.stage_names(dd)
+    if fused:
+        assert "chunk_fwd" in names and "win_fwd" not in names and "slot_fwd" not in names, names
+    else:
+        assert "chunk_fwd" not in names and names[-2:] == ["win_fwd", "slot_fwd"], names
+    # no window or no slots: never the chunk kernel
+    for w, m in ((0, 64), (512, 0)):
+        assert "chunk_fwd" not in nha.stage_names(nha.make_desc(B, 2048, H, Hkv, d, m, w, C, 10000.0, 0.0, dtype))
+
+
 def test_decode_argument_errors():
     lib = nha.load()
     d = desc()

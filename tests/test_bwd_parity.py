@@ -123,11 +123,13 @@ def test_bwd_bitwise_deterministic():
             assert torch.equal(g0, g1)
 
 
-@pytest.mark.parametrize("name,T,C", [("1p3b", 300, 64), ("gqa", 260, 32), ("340m", 200, 16)])
-def test_bwd_after_fwd_matches_bwd(name, T, C):
+@pytest.mark.parametrize("name,B,T,C", [("1p3b", 1, 300, 64), ("1p3b", 4, 300, 64), ("gqa", 1, 260, 32),
+                                        ("340m", 1, 200, 16)])
+def test_bwd_after_fwd_matches_bwd(name, B, T, C):
     """nha_bwd_after_fwd reads the forward's first stages from its workspace:
-    bitwise the same gradients as the standalone backward."""
-    wl = WORKLOADS[name].with_(B=1, T=T, seed=56)
+    bitwise the same gradients as the standalone backward (1p3b at B = 4:
+    after the one-kernel forward; at B = 1: after window + slot kernels)."""
+    wl = WORKLOADS[name].with_(B=B, T=T, seed=56)
     q, k, v, a, dO = (x.to("cuda:0") for x in make_inputs(wl, with_grad=True))
     desc = nha.make_desc(wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, wl.w, C, wl.rope_base, 0.0, wl.dtype)
     ws = torch.empty(max(nha.workspace_size(desc), nha.workspace_size(desc, backward=True)), dtype=torch.uint8,
@@ -140,11 +142,13 @@ def test_bwd_after_fwd_matches_bwd(name, T, C):
         assert torch.equal(x, y)
 
 
-def test_side_stream_results_equal_one_stream_results():
+@pytest.mark.parametrize("B,H,Hkv", [(2, 4, 2), (4, 8, 8)])
+def test_side_stream_results_equal_one_stream_results(B, H, Hkv):
     # the production calls run independent launches on the library's side
     # stream; the timed calls run every launch in order on the caller's
-    # stream: both must give bitwise the same results
-    wl = WORKLOADS["1p3b"].with_(B=2, T=640, H=4, Hkv=2, seed=61)
+    # stream: both must give bitwise the same results (B * Hkv = 4: the
+    # window kernel beside the scan; 32: the one-kernel forward)
+    wl = WORKLOADS["1p3b"].with_(B=B, T=640, H=H, Hkv=Hkv, seed=61)
     w = 128
     log("case side stream vs one stream bf16")
     d = torch.device("cuda:0")

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 from parity_util import TOL, compare, f64, gpu_fwd, log, oracle_fwd, unit_slice
+import softmax_attention_nha_amd as nha
 from softmax_attention_nha_amd.inputs import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -81,6 +82,26 @@ def test_bf16_head_dims_ragged_windows(d, w, T):
     check_full(wl, w=w)
 
 
+@pytest.mark.parametrize("B,H,Hkv,d,T,w,fused", [
+    (4, 8, 8, 128, 261, 40, True),     # last 128-query tile holds one chunk
+    (4, 16, 8, 128, 333, 150, True),   # two query heads per KV head
+    (8, 8, 8, 64, 300, 97, True),
+    (2, 16, 16, 128, 700, 512, True),  # the window spans several tiles
+    (1, 32, 32, 128, 200, 64, True),   # exactly 256 scan waves
+    (1, 31, 31, 128, 333, 150, False),  # 248 scan waves: window and slot kernels
+    (2, 4, 2, 128, 640, 128, False),
+])
+def test_bf16_forward_paths(B, H, Hkv, d, T, w, fused):
+    """The forward runs both branches in one chunk kernel when the state scan
+    has at least 256 waves (B * Hkv * d / 16), else a window kernel beside
+    the scan and a slot kernel that merges it: ragged shapes on both sides."""
+    wl = WORKLOADS["1p3b"].with_(B=B, T=T, H=H, Hkv=Hkv, d=d, seed=41)
+    desc = nha.make_desc(B, T, H, Hkv, d, wl.m, w, wl.C, wl.rope_base, 0.0, wl.dtype)
+    names = nha.stage_names(desc)
+    assert ("chunk_fwd" in names) == fused and ("slot_fwd" in names) == (not fused), names
+    check_full(wl, w=w)
+
+
 def test_bf16_stress_logits_and_hard_gates():
     wl = WORKLOADS["1p3b"].with_(B=1, T=448, H=2, Hkv=2, seed=21)
     check_full(wl, w=96, qk_scale=1.0, alpha_mu=-2.0)
@@ -139,11 +160,19 @@ def test_chunk_size_does_not_change_results():
         assert (x - outs[0]).abs().max().item() < 1e-2
 
 
-def test_gqa_equals_mha_with_repeated_kv():
-    wl = WORKLOADS["gqa"].with_(T=384, seed=32)
+@pytest.mark.parametrize("B,H,Hkv", [(1, 8, 2), (4, 32, 8)])
+def test_gqa_equals_mha_with_repeated_kv(B, H, Hkv):
+    """Bitwise, when both calls take the same forward kernels: the kernel
+    choice depends on B * Hkv (window + slot kernels at B = 1 on both sides;
+    the one-kernel forward at B = 4 on both), and the two forms round their
+    bf16 partials at different points."""
+    wl = WORKLOADS["gqa"].with_(B=B, H=H, Hkv=Hkv, T=384, seed=32)
     q, k, v, a = make_inputs(wl)
     G = wl.H // wl.Hkv
     rep = lambda x: x.repeat_interleave(G, dim=2).contiguous()
+    names = [nha.stage_names(nha.make_desc(B, wl.T, H, hk, wl.d, wl.m, 128, 64, wl.rope_base, 0.0, wl.dtype))
+             for hk in (Hkv, H)]
+    assert names[0] == names[1], names
     o1, l1 = gpu_fwd(q, k, v, a, 128, 64, wl.rope_base)
     o2, l2 = gpu_fwd(q, rep(k), rep(v), rep(a), 128, 64, wl.rope_base)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)

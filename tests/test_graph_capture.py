@@ -14,9 +14,12 @@ from softmax_attention_nha_amd.inputs import WORKLOADS, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-def test_fwd_bwd_graph_replays_equal_eager():
-    # the 1.3B head shape over one sequence of 2048 tokens, w = 512
-    wl = WORKLOADS["1p3b"].with_(B=1)
+@pytest.mark.parametrize("B", [1, 4])
+def test_fwd_bwd_graph_replays_equal_eager(B):
+    # the 1.3B head shape over B sequences of 2048 tokens, w = 512 (B = 1:
+    # the window kernel beside the scan on the side stream; B = 4: the
+    # one-kernel forward)
+    wl = WORKLOADS["1p3b"].with_(B=B)
     w = 512
     dev = torch.device("cuda:0")
     q, k, v, a, dO = (x.to(dev) for x in make_inputs(wl, with_grad=True))
