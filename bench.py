@@ -119,6 +119,10 @@ def stage_work(stage, wl, w, e):
     BT = float(B * T)
     q_b, kv_b, a_b = BT * H * d * e, BT * Hkv * d * e, BT * Hkv * m * e  # one of q (or o, dO, dq); k; alpha
     row = BT * H * 4.0  # lse or D
+    # the slot passes' per-(row, slot) exchange: s dl and p (fp16 for bf16
+    # inputs, fp32 otherwise) and A (fp32); the fp32 rows of blocks on the
+    # exact same-block path (strong decays) are not counted
+    xw = 8.0 if e == 2 else 12.0
     table = {
         "rope_cs": (0.0, 0.0, 8.0 * T * (d // 2)),
         "rope": (0.0, q_b + kv_b, q_b + kv_b),
@@ -135,12 +139,12 @@ def stage_work(stage, wl, w, e):
         "chunk_fwd": (fw + fs, 2 * q_b + 2 * kv_b + a_b + row, B * H * NC * 2.0 * mp * d * e + q_b + kv_b),
         "bwd_prep": (0.0, 2 * q_b + row, 0.0),
         "slot_bwd_a": (1.5 * fs + (4.0 * m * d * B * H * T if e == 2 else 0.0), 3 * q_b + 2 * kv_b + a_b + 2 * row,
-                       B * H * NC * (2.0 * mp * d * e + 2.0 * mp * (d if e == 2 else C) * e + 12.0 * C * mp) + q_b),
+                       B * H * NC * (2.0 * mp * d * e + 2.0 * mp * (d if e == 2 else C) * e + xw * C * mp) + q_b),
         "adj_scan": ((4.0 * m * d * units * NC * G, 0.0, units * NC * (G * 2.0 * mp * d * e + 4.0 * mp + 2.0 * mp * d * e))
                      if e == 2 else
                      (4.0 * m * d * B * H * T, 2 * q_b, units * NC * (G * 2.0 * mp * C * e + 4.0 * mp + 2.0 * mp * d * e))),
         "slot_bwd_b": (2.0 * fs, 2 * kv_b + a_b + BT * Hkv * m * 4.0 + 2 * q_b,
-                       units * NC * (2.0 * mp * d * e + 4.0 * mp + G * 12.0 * C * mp) + 2 * kv_b),
+                       units * NC * (2.0 * mp * d * e + 4.0 * mp + G * xw * C * mp) + 2 * kv_b),
         "dalpha_tail": (0.0, a_b + 2 * BT * Hkv * m * 4.0, units * NC * mp * 4.0),
         "win_bwd_dq": (1.5 * fw, 3 * q_b + 2 * kv_b + 2 * row, q_b),
         "win_bwd_dkdv": (2.0 * fw, 2 * q_b + 4 * kv_b + 2 * row, 2 * kv_b),

@@ -46,7 +46,9 @@ struct BwdWs {
   size_t dqs;                        // slot part of dq: [B][T][H][d] dtype
   size_t wp;                         // fp32: adjoint weights [B*H][NC][2][mp][C]; bf16: the chunk
                                      // products M [B*H][NC][2][d/16][mp][16]
-  size_t sdl, pp, acon;              // [B*H][NC*C][mp] float
+  size_t sdl, pp, acon;              // [B*H][NC*C][mp] float (bf16 inputs: sdl and pp hold
+                                     // only the rows of blocks on the exact same-block path)
+  size_t sdlh, pph;                  // bf16 inputs: s dl and p as fp16 [B*H][NC*C][mp], every row
   size_t lin;                        // adjoint entering each chunk: [B*Hkv][NC][2][mp x d] dtype
                                      // (fp32 [i][d] rows, bf16 column blocks [d/16][i][16])
   size_t dkap, dnu;                  // slot parts of dk, dv at the key row: [B][T][Hkv][d] dtype
@@ -77,6 +79,10 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   off += align256(BH * TT * s.mp * 4);
   L.acon = off;
   off += align256(BH * TT * s.mp * 4);
+  L.sdlh = off;
+  off += s.esz == 2 ? align256(BH * TT * s.mp * 2) : 0;
+  L.pph = off;
+  off += s.esz == 2 ? align256(BH * TT * s.mp * 2) : 0;
   L.lin = off;
   off += align256(units * s.NC * 2 * (size_t)s.mp * s.d * s.esz);
   L.dkap = off;
@@ -501,8 +507,8 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
     const bf16* __restrict__ alpha, const bf16* __restrict__ dO, const bf16* __restrict__ o,
     const bf16* __restrict__ sst, const float* __restrict__ lse, float* __restrict__ Dt, bf16* __restrict__ dqs,
     bf16* __restrict__ madj,
-    float* __restrict__ sdl, float* __restrict__ pp, float* __restrict__ acon, int Tn, int H, int Hkv, int m,
-    int w, int NC, float scale) {
+    float* __restrict__ sdl, float* __restrict__ pp, float* __restrict__ acon, f16* __restrict__ sdlh,
+    f16* __restrict__ pph, int Tn, int H, int Hkv, int m, int w, int NC, float scale) {
   using S = SlotBwdASmemB16<D, MP, C>;
   constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM;
   constexpr int PG = SlotPitch<MP>::PG;
@@ -549,6 +555,11 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   }
   build_slot_tab<C, MP, NT>(sm.tab, sm.sG, tid);
   __syncthreads();
+  // this wave's block may go through pass B's exact same-block path (the
+  // same test, at -16, on the same cumulative gates there; -15.75 here
+  // leaves room for last-bit differences): its rows of s dl and p are also
+  // written in fp32, which that path reads
+  const bool exact_blk = !block_factorizable<MP>(sm.sG, r0, -15.75f);
   BlockedTile<bf16, D, NT, MP> tsk;
   RowTile<bf16, D, NT, C> tkap;
   tsk.load(src, tid);
@@ -571,9 +582,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
   __syncthreads();
   slot_read<bf16, D, MP, C, true>(sm.tS, sm.tK, sm.sB, sm.sG, sm.sA, qf, I, t0, w, Tn, lg, &sm.tab);
   float p[NB][4], dl[NB][4];
-  float* sdl_row = sdl + ((size_t)bh * NC * C + urow + t0) * MP;
-  float* pp_row = pp + ((size_t)bh * NC * C + urow + t0) * MP;
-  float* ac_row = acon + ((size_t)bh * NC * C + urow + t0) * MP;
+  const size_t wrow = ((size_t)bh * NC * C + urow + t0) * MP;
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) {
     floatx4 vs, vp, va;
@@ -589,9 +598,14 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_slot_a_b16(
       vp[r] = pv;
       va[r] = dlv * ls + pv * dp[mb][r];
     }
-    *reinterpret_cast<floatx4*>(sdl_row + 16 * mb + 4 * g) = vs;
-    *reinterpret_cast<floatx4*>(pp_row + 16 * mb + 4 * g) = vp;
-    *reinterpret_cast<floatx4*>(ac_row + 16 * mb + 4 * g) = va;
+    const size_t e = wrow + 16 * mb + 4 * g;
+    *reinterpret_cast<f16x4*>(sdlh + e) = __builtin_convertvector(vs, f16x4);
+    *reinterpret_cast<f16x4*>(pph + e) = __builtin_convertvector(vp, f16x4);
+    if (exact_blk) {
+      *reinterpret_cast<floatx4*>(sdl + e) = vs;
+      *reinterpret_cast<floatx4*>(pp + e) = vp;
+    }
+    *reinterpret_cast<floatx4*>(acon + e) = va;
   }
   // slot part of dq: s sum_i dl_t[i] SK_t[i]
   floatx4 accO[D / 16];
@@ -834,9 +848,9 @@ template <typename T, int D, int MP, int C>
 __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slot_b(
     const T* __restrict__ q, const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ alpha,
     const T* __restrict__ dO, const T* __restrict__ lin, const float* __restrict__ sdl,
-    const float* __restrict__ pp, const float* __restrict__ acon, T* __restrict__ dkap,
-    T* __restrict__ dnu, float* __restrict__ dalpha, float* __restrict__ csum, int Tn, int H, int Hkv, int m,
-    int w, int NC) {
+    const float* __restrict__ pp, const float* __restrict__ acon, const f16* __restrict__ sdlh,
+    const f16* __restrict__ pph, T* __restrict__ dkap, T* __restrict__ dnu, float* __restrict__ dalpha,
+    float* __restrict__ csum, int Tn, int H, int Hkv, int m, int w, int NC) {
   using S = SlotBwdBSmem<T, D, MP, C>;
   constexpr int NT = C / 16 * 64, NB = MP / 16, PD = S::PD, PM = S::PM, PC = S::PC;
   constexpr int PG = SlotPitch<MP>::PG;
@@ -862,9 +876,17 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
     const T* vb = (side ? dO : q) + (((size_t)b * Tn + t0) * H + h) * D;
     ht.tv.load(vb, (size_t)H * D, 0, Tn - t0, tid);
     if constexpr (!S::TR) ht.tvt.load(vb, (size_t)H * D, 0, Tn - t0, tid);
-    const float* wsrc = (side ? pp : sdl) + ((size_t)bh * NC * C + t0) * MP;
+    const size_t wo = ((size_t)bh * NC * C + t0) * MP;
+    if constexpr (S::TR) {  // bf16 inputs: the fp16 copies (every row)
+      const f16* wsrc = (side ? pph : sdlh) + wo;
 #pragma unroll
-    for (int k = 0; k < WIT; ++k) ht.xw[k] = *reinterpret_cast<const floatx4*>(wsrc + (tid + k * NT) * 4);
+      for (int k = 0; k < WIT; ++k)
+        ht.xw[k] = __builtin_convertvector(*reinterpret_cast<const f16x4*>(wsrc + (tid + k * NT) * 4), floatx4);
+    } else {
+      const float* wsrc = (side ? pp : sdl) + wo;
+#pragma unroll
+      for (int k = 0; k < WIT; ++k) ht.xw[k] = *reinterpret_cast<const floatx4*>(wsrc + (tid + k * NT) * 4);
+    }
   };
   auto store_head = [&](const HeadTile& ht) {
 #pragma unroll
@@ -1873,6 +1895,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     T* wpb = (T*)(ws + L.wp);
     float* sdl = (float*)(ws + L.sdl);
     float* ppb = (float*)(ws + L.pp);
+    f16* sdlh = s.esz == 2 ? (f16*)(ws + L.sdlh) : nullptr;
+    f16* pph = s.esz == 2 ? (f16*)(ws + L.pph) : nullptr;
     float* acon = (float*)(ws + L.acon);
     T* lin = (T*)(ws + L.lin);
     T* dkap = (T*)(ws + L.dkap);
@@ -1910,8 +1934,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
       // bf16: pass A also computes D_t
       mk.mark(st);
       hipLaunchKernelGGL((k_bwd_slot_a_b16<D, MP, C>), dim3(s.NC, s.B * s.H), dim3(C / 16 * 64), 0, st, q, k, v,
-                         alpha, dO, (const T*)p.o, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, s.T, s.H,
-                         s.Hkv, s.m, s.sh, s.NC, s.scale);
+                         alpha, dO, (const T*)p.o, (const T*)pp.sst, p.lse, Dt, dqs, wpb, sdl, ppb, acon, sdlh, pph,
+                         s.T, s.H, s.Hkv, s.m, s.sh, s.NC, s.scale);
     } else {
       mk.mark(st);
       hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)((nrows * (D / 8) + 255) / 256)), dim3(256), 0, st,
@@ -1949,7 +1973,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     }
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
-                       (const T*)lin, sdl, ppb, acon, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m, s.sh, s.NC);
+                       (const T*)lin, sdl, ppb, acon, sdlh, pph, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m,
+                       s.sh, s.NC);
     // the dalpha carry on the side stream (after dq and pass B), beside the
     // window dk/dv
     const hipStream_t sa = fk.begin(st);

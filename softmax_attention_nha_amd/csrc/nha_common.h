@@ -30,6 +30,10 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// fp16: 10 mantissa bits for [0, 1]-bounded or moderate fp32 tiles handed
+// between kernels (the bf16 MFMA operands they end up in keep 7)
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 
 #define NHA_LOG2E 1.4426950408889634f
 #define NHA_LN2 0.6931471805599453f

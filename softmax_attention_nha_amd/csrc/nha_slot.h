@@ -144,7 +144,7 @@ __device__ __forceinline__ void stage_gates(const T* __restrict__ alpha, float* 
 // (Every load is unconditional and the test is a bitwise and: no branch and
 // no serialised LDS round trip per slot.)
 template <int MP>
-__device__ __forceinline__ bool block_factorizable(const float* sG, int r0) {
+__device__ __forceinline__ bool block_factorizable(const float* sG, int r0, float lim = -16.f) {
   constexpr int NB = MP / 16, PG = SlotPitch<MP>::PG;
   const int g = (threadIdx.x & 63) >> 4;
   const float keep = r0 > 0 ? 1.f : 0.f;
@@ -156,7 +156,7 @@ __device__ __forceinline__ bool block_factorizable(const float* sG, int r0) {
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * mb + 4 * g + r;
       const float before = keep * sG[rb * PG + i];
-      ok &= (sG[(r0 + 15) * PG + i] - before >= -16.f);
+      ok &= (sG[(r0 + 15) * PG + i] - before >= lim);
     }
   return __all(ok);
 }
