@@ -52,9 +52,10 @@
  *     of that thread on that device, kept until nha_release_side_streams().
  *     Those calls fork independent launches onto the side stream (the window
  *     branch -- RoPE, then band attention -- beside the gate products and the
- *     slot-state scan; the window dq beside the adjoint scan and slot pass B;
- *     the dalpha carry beside the window dk/dv) after an event recorded on
- *     `stream`, and
+ *     slot-state scan where the forward runs its two-kernel form, i.e. below
+ *     256 state-scan waves, B * Hkv * d / 16; the window dq beside the
+ *     adjoint scan and slot pass B; the dalpha carry beside the window dk/dv)
+ *     after an event recorded on `stream`, and
  *     make `stream` wait for the side stream before they return, so each call
  *     still behaves as one operation ordered on `stream`.  If the side
  *     stream cannot be created, every launch goes on `stream`.  The *_timed

@@ -92,28 +92,73 @@ __global__ __launch_bounds__(256) void k_rope(const T* __restrict__ q, const T* 
 // grid (NC, B*Hkv), 256 threads.
 // Wt[unit][c][i][u] = 2^{G_end,i - G_u,i} b_u,i   (0 for padded slots / rows)
 // aend[unit][c][i]  = 2^{G_end,i}
+// Thread (part, i) holds rows part*RP .. part*RP + RP-1 of slot i in
+// registers: it sums their log2 gates in row order, the parts' totals meet
+// in LDS, and each part adds the totals of the parts before it in part order
+// -- the same float additions, in the same order, as the LDS column cumsum
+// of the slot kernels -- so its slot row of W^T is RP contiguous elements.
 template <typename T, int C, int MP>
 __global__ __launch_bounds__(256) void k_chunk_gates(const T* __restrict__ alpha, T* __restrict__ Wt,
                                                      float* __restrict__ aend, int Tn, int Hkv, int m, int w,
                                                      int NC) {
-  constexpr int PG = MP + 1, PA = MP + 2, PW = C + 8;
-  __shared__ float sG[C * PG];
-  __shared__ T sA[C * PA];
-  __shared__ T sW[MP * PW];
+  constexpr int NT = 256, PARTS = (NT / MP) < C ? (NT / MP) : C, RP = C / PARTS;
+  static_assert(RP * PARTS == C && (RP == 2 || RP % 4 == 0), "row split");
+  __shared__ float tot[PARTS][MP];
   const int tid = threadIdx.x, c = blockIdx.x, unit = blockIdx.y;
-  const int b = unit / Hkv, hg = unit % Hkv, t0 = c * C;
-  stage_gates<T, C, MP, PG, PA, 256>(alpha, sG, sA, b, hg, t0, Tn, Hkv, m, w, tid);
-  __syncthreads();
-  lds_col_cumsum<C, MP, PG, 256>(sG, tid);
-  for (int e = tid; e < MP * C; e += 256) {
-    int i = e / C, u = e % C, t = t0 + u;
-    float be = (i < m && t < Tn && t >= w) ? 1.f - to_f<T>(sA[u * PA + i]) : 0.f;
-    sW[i * PW + u] = to_t<T>(fast_exp2(sG[(C - 1) * PG + i] - sG[u * PG + i]) * be);
+  const int b = unit / Hkv, hg = unit % Hkv, t0 = c * C, i = tid % MP, part = tid / MP;
+  const bool act = part < PARTS;
+  float av[RP], G[RP];
+  if (act) {
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {  // every load first (rows and slots clamped into range)
+      const int t = t0 + part * RP + k;
+      av[k] = to_f<T>(alpha[(((size_t)b * Tn + (t < Tn ? t : Tn - 1)) * Hkv + hg) * m + (i < m ? i : m - 1)]);
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int t = t0 + part * RP + k;
+      const bool act_t = i < m && t < Tn && t >= w;
+      acc += act_t ? fmaxf(__log2f(av[k]), NHA_LOG2A_MIN) : 0.f;
+      G[k] = acc;
+      av[k] = act_t ? 1.f - av[k] : 0.f;  // b_u from here on
+    }
+    tot[part][i] = acc;
   }
   __syncthreads();
-  T* dst = Wt + ((size_t)unit * NC + c) * MP * C;
-  for (int e = tid * 8; e < MP * C; e += 256 * 8) st8<T>(dst + e, ld8<T>(&sW[(e / C) * PW + (e % C)]));
-  if (tid < MP) aend[((size_t)unit * NC + c) * MP + tid] = fast_exp2(sG[(C - 1) * PG + tid]);
+  if (!act) return;
+  float off = 0.f, ge = 0.f;
+#pragma unroll
+  for (int pp = 0; pp < PARTS - 1; ++pp) {
+    if (pp < part) off += tot[pp][i];
+    ge += tot[pp][i];
+  }
+  ge = tot[PARTS - 1][i] + ge;  // G_end: the last part's rows plus the parts before it
+  T y[RP];
+#pragma unroll
+  for (int k = 0; k < RP; ++k) y[k] = to_t<T>(fast_exp2(ge - (part > 0 ? G[k] + off : G[k])) * av[k]);
+  T* dst = Wt + (((size_t)unit * NC + c) * MP + i) * C + part * RP;
+  if constexpr (RP % 8 == 0) {
+#pragma unroll
+    for (int k = 0; k < RP; k += 8) {
+      typename Vec<T>::v8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = y[k + e];
+      st8<T>(dst + k, v);
+    }
+  } else if constexpr (RP % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < RP; k += 4) {
+      typename Vec<T>::v4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = y[k + e];
+      st4<T>(dst + k, v);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < RP; ++k) dst[k] = y[k];
+  }
+  if (part == 0) aend[((size_t)unit * NC + c) * MP + i] = fast_exp2(ge);
 }
 
 // ---------------------------------------------------------------- state scan
@@ -1407,18 +1452,16 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       }
     };
     if (s.m > 0 && s.win && !p.separate && chunk_fused(s)) {
-      // both branches in the chunk kernel, after the gate products and the
-      // slot-state scan; RoPE on the side stream beside them
+      // both branches in the chunk kernel, after the gate products, the
+      // slot-state scan and RoPE, all in order on the caller's stream: the
+      // scan is a latency-bound walk over the chunks, and RoPE beside it on
+      // the side stream slowed it by more than RoPE takes alone
       if constexpr (sizeof(T) == 2 && C == 64) {
-        fk.record(st);
         mk.mark(st);
         launch_gates<T, C, MP>(s, alpha, pp, st);
         mk.mark(st);
         launch_scan<T, D, C, MP>(s, k, v, pp, st);
-        if (s.rope) {
-          launch_rope<T>(s, th, q, k, pp, mk, fk.follow(st));
-          fk.join(st);
-        }
+        if (s.rope) launch_rope<T>(s, th, q, k, pp, mk, st);
         mk.mark(st);
         hipLaunchKernelGGL((k_chunk_fwd_b16<D, MP>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
                            dim3(kWinWaves * 64), 0, st, q, k, v, alpha, (const T*)pp.sst, qr, kr, (T*)p.o, p.lse,
