@@ -103,6 +103,30 @@ def test_bf16_stress_logits_and_hard_gates():
           rel_override={"dalpha": 5e-2})
 
 
+def test_bf16_blocks_around_the_exact_path_threshold():
+    """Pass B takes its exact same-block path (fp32 weights from the
+    workspace) for 16-row blocks whose decay 2^{sum log2 alpha} falls below
+    2^-16 in some slot; pass A writes the fp32 rows of those blocks, testing
+    at -15.75.  Slot 0's gates cycle over the blocks through alpha = 0.498046875
+    (a block sum of -16.09: exact path in both passes), 0.50390625 (-15.82:
+    pass B factorizes, pass A still writes the fp32 rows) and the workload's
+    mild gates; both values are exact in bf16."""
+    wl = WORKLOADS["1p3b"].with_(B=1, T=320, H=2, Hkv=2, seed=57)
+    w = 16
+    q, k, v, a, dO = make_inputs(wl, with_grad=True)
+    a = a.clone()
+    for blk in range(w // 16, wl.T // 16):
+        val = (0.498046875, 0.50390625, None)[blk % 3]
+        if val is not None:
+            a[:, 16 * blk:16 * blk + 16, :, 0] = val
+    log("case bwd blocks around the exact-path threshold")
+    dq, dk, dv, da = gpu_fwd_bwd(q, k, v, a, dO, w, 64, wl.rope_base)
+    ref = oracle.bwd(f64(q), f64(k), f64(v), f64(a), f64(dO), w, rope_base=wl.rope_base)
+    tol = TOL[wl.dtype]
+    for name, x, r in zip(("dq", "dk", "dv", "dalpha"), (dq, dk, dv, da), ref):
+        compare(name, f64(x), r, tol["grad"], tol["rel"])
+
+
 # ---------------------------------------------------------------- full-size workloads, sampled units
 @pytest.mark.parametrize("name,w,T", [("340m", None, None), ("1p3b", 64, None), ("1p3b", 512, None),
                                       ("1p3b", 2048, None), ("gqa", None, 2048)])
