@@ -123,6 +123,16 @@ def stage_work(stage, wl, w, e):
     # inputs, fp32 otherwise) and A (fp32); the fp32 rows of blocks on the
     # exact same-block path (strong decays) are not counted
     xw = 8.0 if e == 2 else 12.0
+    # segments of the state scan (the library's rule: bf16, fewer than 256
+    # scan waves, at least 384 chunks; up to 768 waves of at least 8 chunks)
+    nseg, base = 1, B * Hkv * (d // 16)
+    if e == 2 and m > 0 and base < 256 and NC >= 384:
+        nseg = min(768 // base, 16, NC // 8)
+        if nseg >= 2:
+            L = -(-NC // nseg)
+            nseg = -(-NC // L)
+        else:
+            nseg = 1
     table = {
         "rope_cs": (0.0, 0.0, 8.0 * T * (d // 2)),
         "rope": (0.0, q_b + kv_b, q_b + kv_b),
@@ -149,6 +159,13 @@ def stage_work(stage, wl, w, e):
         "win_bwd_dq": (1.5 * fw, 3 * q_b + 2 * kv_b + 2 * row, q_b),
         "win_bwd_dkdv": (2.0 * fw, 2 * q_b + 4 * kv_b + 2 * row, 2 * kv_b),
         "export_state": (0.0, 4.0 * B * Hkv * min(w, T) * d * e, 0.0),
+        # the segmented scan (long walks at few waves): segment end states
+        # and decays, their start states, then the walk ("state_scan")
+        "state_scan_seg": (flops_state(B, Hkv, T, d, m, w), 2.0 * B * Hkv * absorbed * d * e,
+                           units * NC * (mp * C * e + 4.0 * mp) + nseg * units * (2.0 * m * d * 4 + 4.0 * mp)),
+        "scan_combine": (0.0, 0.0, nseg * units * (4.0 * m * d * 4 + 4.0 * mp)),
+        # dalpha's exact carries at every 16th chunk: adjoint and state rows
+        "carry_ckpt": (0.0, 0.0, units * ((NC - 1) // 16) * (2 * 2.0 * mp * d * e + 4.0 * mp)),
     }
     return table.get(stage, (None, None, None))
 

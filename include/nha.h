@@ -47,14 +47,16 @@
  *   - a per-device cache of the compute-unit count (read once with
  *     hipDeviceGetAttribute; sizes persistent grids);
  *   - per calling thread and device, ONE side stream (default priority,
- *     hipStreamNonBlocking) and two events (timing disabled), created by the
+ *     hipStreamNonBlocking) and three events (timing disabled), created by the
  *     first nha_fwd, nha_fwd_s0, nha_bwd, nha_bwd_after_fwd or nha_bwd_s0 call
  *     of that thread on that device, kept until nha_release_side_streams().
  *     Those calls fork independent launches onto the side stream (the window
  *     branch -- RoPE, then band attention -- beside the gate products and the
  *     slot-state scan where the forward runs its two-kernel form, i.e. below
  *     256 state-scan waves, B * Hkv * d / 16; the window dq beside the
- *     adjoint scan and slot pass B; the dalpha carry beside the window dk/dv)
+ *     adjoint scan and slot pass B, then (bf16) dalpha's exact carries at
+ *     every 16th chunk once the adjoint scan is done; the dalpha carry beside
+ *     the window dk/dv)
  *     after an event recorded on `stream`, and
  *     make `stream` wait for the side stream before they return, so each call
  *     still behaves as one operation ordered on `stream`.  If the side
@@ -355,7 +357,7 @@ nha_status nha_bwd_after_fwd_timed(const nha_desc* desc, const void* q,
                                    size_t ws_bytes, void* stream,
                                    void* const* events);
 
-/* Destroy the side stream and the two events that nha_fwd, nha_fwd_s0,
+/* Destroy the side stream and the three events that nha_fwd, nha_fwd_s0,
  * nha_bwd, nha_bwd_after_fwd and nha_bwd_s0 created for the CALLING thread
  * (on every device it used); the next such call creates them again.  Work
  * already enqueued on them completes normally (HIP releases the handles once

@@ -108,17 +108,20 @@ Fork side_fork(bool enabled) {
   Fork& c = side_cache[dev];
   if (!c.side) {
     hipStream_t s = nullptr;
-    hipEvent_t a = nullptr, b = nullptr;
+    hipEvent_t a = nullptr, b = nullptr, e = nullptr;
     if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return none;
     if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
       if (a) (void)hipEventDestroy(a);
+      if (b) (void)hipEventDestroy(b);
       (void)hipStreamDestroy(s);
       return none;
     }
     c.side = s;
     c.ev_fork = a;
     c.ev_join = b;
+    c.ev_mid = e;
   }
   return c;
 }
@@ -150,6 +153,7 @@ nha_status nha_release_side_streams(void) {
     if (hipSetDevice(dev) != hipSuccess) rc = NHA_ERR_HIP;
     if (hipEventDestroy(c.ev_fork) != hipSuccess) rc = NHA_ERR_HIP;
     if (hipEventDestroy(c.ev_join) != hipSuccess) rc = NHA_ERR_HIP;
+    if (hipEventDestroy(c.ev_mid) != hipSuccess) rc = NHA_ERR_HIP;
     if (hipStreamDestroy(c.side) != hipSuccess) rc = NHA_ERR_HIP;
     c = Fork();
   }

@@ -41,7 +41,7 @@ namespace nha {
 
 // ---------------------------------------------------------------- workspace
 struct BwdWs {
-  size_t sst, wt, aend, qrot, krot, rcs;  // prologue (same meaning as the forward's)
+  size_t sst, wt, aend, seg, qrot, krot, rcs;  // prologue (same meaning as the forward's)
   size_t dt;                         // D_t: [B][H][T] float
   size_t dqs;                        // slot part of dq: [B][T][H][d] dtype
   size_t wp;                         // fp32: adjoint weights [B*H][NC][2][mp][C]; bf16: the chunk
@@ -53,6 +53,7 @@ struct BwdWs {
                                      // (fp32 [i][d] rows, bf16 column blocks [d/16][i][16])
   size_t dkap, dnu;                  // slot parts of dk, dv at the key row: [B][T][Hkv][d] dtype
   size_t csum;                       // [B*Hkv][NC][mp] float
+  size_t xck;                        // bf16: exact carries at the checkpoint chunks [B*Hkv][(NC-1)/16][mp] float
   size_t total;
 };
 
@@ -62,6 +63,7 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   L.sst = F.sst;
   L.wt = F.wt;
   L.aend = F.aend;
+  L.seg = F.seg;
   L.qrot = F.qrot;
   L.krot = F.krot;
   L.rcs = F.rcs;
@@ -91,6 +93,8 @@ static BwdWs bwd_ws_layout(const Shape& s) {
   off += align256((size_t)s.B * s.T * s.Hkv * s.d * s.esz);
   L.csum = off;
   off += align256(units * s.NC * s.mp * 4);
+  L.xck = off;
+  off += align256(units * (size_t)carry_ckpts(s) * s.mp * 4);
   L.total = off;
   return L;
 }
@@ -1087,38 +1091,81 @@ __global__ __launch_bounds__(C / 16 * 64, sizeof(T) == 2 ? 2 : 1) void k_bwd_slo
   }
 }
 
+// Exact carries at the checkpoint chunks c' = q kCarryStride + kCarryStride - 1
+// < NC - 1 (bf16): xck[unit][q][i] = <Lin_c'[i], S_{c'+1}[i]> over both halves
+// (K and V) -- the adjoint entering chunk c' from the right against the state
+// at the start of chunk c' + 1, both stored as bf16 column blocks
+// [2][d/16][mp][16].  grid ((NC - 1) / kCarryStride, B*Hkv), 256 threads: slot
+// i = tid % MP, its 2 d/16 column blocks split over 256 / MP parts.
+template <int D, int MP>
+__global__ __launch_bounds__(256) void k_carry_ckpt(const bf16* __restrict__ lin, const bf16* __restrict__ sst,
+                                                    float* __restrict__ xck, int NC) {
+  constexpr int NP = 256 / MP, NBLK = 2 * (D / 16);
+  __shared__ float part[NP][MP];
+  const int tid = threadIdx.x, q = blockIdx.x, unit = blockIdx.y, i = tid % MP, pt = tid / MP;
+  const int c = q * kCarryStride + kCarryStride - 1;
+  const size_t ce = 2 * (size_t)MP * D;
+  const bf16* L = lin + ((size_t)unit * NC + c) * ce + i * 16;
+  const bf16* S = sst + ((size_t)unit * NC + c + 1) * ce + i * 16;
+  float acc = 0.f;
+  for (int blk = pt; blk < NBLK; blk += NP) {
+    const size_t o = (size_t)blk * MP * 16;  // (side, d/16) block: [mp][16]
+    const bf16x8 l0 = ld8<bf16>(L + o), l1 = ld8<bf16>(L + o + 8), s0 = ld8<bf16>(S + o), s1 = ld8<bf16>(S + o + 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)l0[e] * (float)s0[e] + (float)l1[e] * (float)s1[e];
+  }
+  part[pt][i] = acc;
+  __syncthreads();
+  if (tid < MP) {
+    float x = 0.f;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) x += part[k][tid];
+    xck[((size_t)unit * gridDim.x + q) * MP + tid] = x;
+  }
+}
+
 // dalpha_t[i] += carry_c[i] / alpha_t[i] for the rows t >= w of chunk c, with
-// carry_c[i] = sum over the later chunks of their totals of (A - b F).
+// carry_c[i] = sum over the later chunks of their totals of (A - b F).  That
+// sum telescopes to <Lin_c[i], S_{c+1}[i]> (the adjoint entering chunk c from
+// the right against the state at the next chunk start, both halves), an O(1)
+// quantity whose terms mostly cancel: summed over a long sequence, their
+// rounding errors would grow with its length.  With checkpoints (xck, bf16
+// inputs) the sum runs only up to the next checkpoint chunk c' (the last of
+// its group of kCarryStride, c' < NC - 1), whose exact carry xck holds:
+// carry_c = sum_{j = c+1 .. c'} total_j + xck[c'].
 // grid (NC, B*Hkv), 256 threads: the carry is summed by 256 / MP strided
 // parts (a fixed order) and combined through LDS.  Loads are issued in
 // batches before their first use (one memory round trip per batch).
 template <typename T, int MP, int C>
 __global__ __launch_bounds__(256) void k_dalpha_tail(const T* __restrict__ alpha, const float* __restrict__ csum,
-                                                     float* __restrict__ dalpha, int Tn, int Hkv, int m, int w,
-                                                     int NC) {
+                                                     const float* __restrict__ xck, float* __restrict__ dalpha,
+                                                     int Tn, int Hkv, int m, int w, int NC) {
   constexpr int NP = 256 / MP, BATCH = 16;
   __shared__ float part[NP][MP];
   __shared__ float carry[MP];
   const int tid = threadIdx.x, c = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv;
+  const int cq = (c / kCarryStride) * kCarryStride + kCarryStride - 1;  // next checkpoint chunk
+  const bool ck = xck != nullptr && cq < NC - 1;
+  const int cend = ck ? cq + 1 : NC;  // totals of chunks c+1 .. cend-1
   {
     const int i = tid % MP, pt = tid / MP;
     const float* cs = csum + (size_t)unit * NC * MP + i;
     float acc = 0.f;
-    for (int c0 = c + 1 + pt; c0 < NC; c0 += BATCH * NP) {
+    for (int c0 = c + 1 + pt; c0 < cend; c0 += BATCH * NP) {
       float x[BATCH];
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         const int c2 = c0 + k * NP;
-        x[k] = cs[(size_t)(c2 < NC ? c2 : NC - 1) * MP];
+        x[k] = cs[(size_t)(c2 < cend ? c2 : cend - 1) * MP];
       }
 #pragma unroll
-      for (int k = 0; k < BATCH; ++k) acc += (c0 + k * NP < NC) ? x[k] : 0.f;
+      for (int k = 0; k < BATCH; ++k) acc += (c0 + k * NP < cend) ? x[k] : 0.f;
     }
     part[pt][i] = acc;
   }
   __syncthreads();
   if (tid < MP) {
-    float x = 0.f;
+    float x = ck ? xck[((size_t)unit * ((NC - 1) / kCarryStride) + cq / kCarryStride) * MP + tid] : 0.f;
 #pragma unroll
     for (int k = 0; k < NP; ++k) x += part[k][tid];
     carry[tid] = x;
@@ -1872,6 +1919,7 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     mk.ev = p.events;
     const Fork fk = side_fork(p.events == nullptr);
     ProloguePtrs pp{ws + L.sst, ws + L.wt, (float*)(ws + L.aend), nullptr, nullptr, nullptr, nullptr, nullptr};
+    pp.seg = (float*)(ws + L.seg);
     pp.s0k = p.s0k;
     pp.s0v = p.s0v;
     if (s.rope && s.win) {
@@ -1960,6 +2008,7 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     else
       hipLaunchKernelGGL((k_adj_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, q, dO, (const T*)wpb,
                          (const float*)pp.aend, lin, p.ds0k, p.ds0v, s.T, s.H, s.Hkv, D, s.m, s.NC);
+    fk.mark_mid(st);  // the adjoints are scanned
     const hipStream_t sq = fk.follow(st);
     mk.mark(sq);
     if constexpr (sizeof(T) == 2) {
@@ -1971,6 +2020,20 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
       hipLaunchKernelGGL((k_win_bwd_dq<T, D>), dim3(s.NQ, s.B * s.H), dim3(256), 0, sq, qr, kr, v, dOw, lsew, Dw,
                          dqs, (T*)p.dq, s.T, s.H, s.Hkv, s.w, s.scale, th, s.rope ? 1 : 0);
     }
+    // (bf16) the exact dalpha carries at the checkpoint chunks, from the
+    // scanned adjoints, after the window dq on the side stream (beside pass B)
+    const float* xckp = nullptr;
+    if constexpr (sizeof(T) == 2) {
+      const int nq = carry_ckpts(s);
+      if (nq > 0) {
+        float* xck = (float*)(ws + L.xck);
+        fk.wait_mid();
+        mk.mark(sq);
+        hipLaunchKernelGGL((k_carry_ckpt<D, MP>), dim3(nq, units), dim3(256), 0, sq, (const bf16*)lin,
+                           (const bf16*)pp.sst, xck, s.NC);
+        xckp = xck;
+      }
+    }
     mk.mark(st);
     hipLaunchKernelGGL((k_bwd_slot_b<T, D, MP, C>), dim3(s.NC, units), dim3(C / 16 * 64), 0, st, q, k, v, alpha, dO,
                        (const T*)lin, sdl, ppb, acon, sdlh, pph, dkap, dnu, p.dalpha, csum, s.T, s.H, s.Hkv, s.m,
@@ -1979,8 +2042,8 @@ static hipError_t bwd_impl(const Shape& s, const RopeTheta& th, const BwdPtrs& p
     // window dk/dv
     const hipStream_t sa = fk.begin(st);
     mk.mark(sa);
-    hipLaunchKernelGGL((k_dalpha_tail<T, MP, C>), dim3(s.NC, units), dim3(256), 0, sa, alpha, csum, p.dalpha, s.T,
-                       s.Hkv, s.m, s.sh, s.NC);
+    hipLaunchKernelGGL((k_dalpha_tail<T, MP, C>), dim3(s.NC, units), dim3(256), 0, sa, alpha, csum, xckp, p.dalpha,
+                       s.T, s.Hkv, s.m, s.sh, s.NC);
     mk.mark(st);
     if constexpr (sizeof(T) == 2) {
       constexpr int NWV = 4;
@@ -2028,6 +2091,10 @@ int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max) {
   if (!after_fwd) {
     if (s.m > 0) {
       all[n++] = "chunk_gates";
+      if (scan_segments(s).n > 1) {
+        all[n++] = "state_scan_seg";
+        all[n++] = "scan_combine";
+      }
       all[n++] = "state_scan";
     }
     if (s.rope && s.win) {
@@ -2046,6 +2113,7 @@ int bwd_stages(const Shape& s, bool after_fwd, const char** names, int max) {
   all[n++] = "slot_bwd_a";
   all[n++] = "adj_scan";
   all[n++] = "win_bwd_dq";
+  if (carry_ckpts(s) > 0) all[n++] = "carry_ckpt";
   all[n++] = "slot_bwd_b";
   all[n++] = "dalpha_tail";
   all[n++] = "win_bwd_dkdv";

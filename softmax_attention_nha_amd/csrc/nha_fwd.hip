@@ -310,27 +310,36 @@ struct ScanStage {
   float ae[64];
 };
 
-template <int C, int MP, int NS>
+// Segments: blockIdx.y = unit * nseg + p walks chunks [p segc, (p+1) segc)
+// from the state s0 of row (unit * nseg + p) (null: zero) and leaves its end
+// state in row (unit * nseg + p) of skout / svout (null: not kept) and, from
+// the workgroup of columns 0-15, the segment's decay, the product of
+// 2^{G_end} over its chunks, in row (unit * nseg + p) of dec [.][MP] (null:
+// not kept); STORE writes the state at every chunk start.  One segment
+// (nseg = 1, segc = NC) is the whole walk.
+template <int C, int MP, int NS, bool STORE>
 __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ kk, const bf16* __restrict__ vv,
                                                        const bf16* __restrict__ Wt, const float* __restrict__ aend,
                                                        bf16* __restrict__ sst, float* __restrict__ skout,
-                                                       float* __restrict__ svout, const float* __restrict__ s0k,
-                                                       const float* __restrict__ s0v, int Tn, int Hkv, int d, int m,
-                                                       int w, int NC) {
+                                                       float* __restrict__ svout, float* __restrict__ dec,
+                                                       const float* __restrict__ s0k, const float* __restrict__ s0v,
+                                                       int Tn, int Hkv, int d, int m, int w, int NC, int nseg,
+                                                       int segc) {
   using St = ScanStage<C, MP>;
   constexpr int NB = MP / 16, CPR = C / 8;  // W^T 16-byte chunks per row
   __shared__ St ring[NS];
   const int l = threadIdx.x, g = l >> 4, cc = l & 15;
   const int L = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
   const int j0 = __builtin_amdgcn_readfirstlane((L % gridDim.x) * 16),
-            unit = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+            useg = __builtin_amdgcn_readfirstlane(L / gridDim.x);
+  const int unit = useg / nseg, c0 = (useg % nseg) * segc, c1 = min(NC, c0 + segc);
   const int b = unit / Hkv, hg = unit % Hkv;
   const size_t ld = (size_t)Hkv * d;
   const bf16* kbase = kk + ((size_t)b * Tn * Hkv + hg) * d + j0;
   const bf16* vbase = vv + ((size_t)b * Tn * Hkv + hg) * d + j0;
-  // issue the direct loads of chunk c (clamped) into ring slot s
+  // issue the direct loads of chunk c (clamped to the segment) into ring slot s
   auto issue = [&](int c, int s) {
-    c = min(c, NC - 1);
+    c = min(c, c1 - 1);
     const uint32_t base = lds_addr(&ring[s]);
 #pragma unroll
     for (int i = 0; i < St::NK; ++i) {
@@ -374,29 +383,35 @@ __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ 
     }
   };
   floatx4 SK[NB], SV[NB];
-  init_slot_state<NB>(SK, SV, s0k, s0v, unit, m, d, j0, g, cc);
+  init_slot_state<NB>(SK, SV, s0k, s0v, useg, m, d, j0, g, cc);
+  float dk[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) dk[nb] = 1.f;
   const size_t chunk_elems = 2 * (size_t)MP * d;
-  for (int s = 0; s < NS; ++s) issue(s, s);
-  for (int c = 0; c < NC; ++c) {
-    const int s = c % NS;
+  for (int s = 0; s < NS; ++s) issue(c0 + s, s);
+  for (int c = c0; c < c1; ++c) {
+    const int s = (c - c0) % NS;
     // loads of chunk c done: the later chunks' loads (St::OPS each) and the
     // state stores of the steps since (2 NB each) may still be in flight
-    vm_wait_steps<NS, St::OPS, 2 * NB>(c);
+    vm_wait_steps<NS, St::OPS, STORE ? 2 * NB : 0>(c - c0);
     const St& R = ring[s];
-    // state at the chunk start, both halves in column blocks [d/16][i][16]:
-    // this wave's block is one contiguous 2 KB piece of each half
-    bf16* dst = sst + ((size_t)unit * NC + c) * chunk_elems + (size_t)j0 * MP;
+    if constexpr (STORE) {
+      // state at the chunk start, both halves in column blocks [d/16][i][16]:
+      // this wave's block is one contiguous 2 KB piece of each half
+      bf16* dst = sst + ((size_t)unit * NC + c) * chunk_elems + (size_t)j0 * MP;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int i = 16 * nb + cc;
-      st4<bf16>(dst + i * 16 + 4 * g, pack4<bf16>(SK[nb]));
-      st4<bf16>(dst + (size_t)MP * d + i * 16 + 4 * g, pack4<bf16>(SV[nb]));
+      for (int nb = 0; nb < NB; ++nb) {
+        const int i = 16 * nb + cc;
+        st4<bf16>(dst + i * 16 + 4 * g, pack4<bf16>(SK[nb]));
+        st4<bf16>(dst + (size_t)MP * d + i * 16 + 4 * g, pack4<bf16>(SV[nb]));
+      }
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float a = R.ae[16 * nb + cc];
       SK[nb] *= a;
       SV[nb] *= a;
+      if constexpr (!STORE) dk[nb] *= a;
     }
     // dS^T[col][i] += sum_u kappa^T[col][u] W^T[i][u]: A = kappa^T (transposed
     // reads of the row-major tile), B = W^T rows
@@ -438,6 +453,12 @@ __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ 
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue(c + NS, s);
   }
+  if constexpr (!STORE) {
+    if (dec && j0 == 0 && g == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dec[(size_t)useg * MP + 16 * nb + cc] = dk[nb];
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (skout) {
 #pragma unroll
@@ -446,8 +467,8 @@ __global__ __launch_bounds__(64) void k_state_scan_b16(const bf16* __restrict__ 
       if (i < m) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          skout[((size_t)unit * m + i) * d + j0 + 4 * g + r] = SK[nb][r];
-          svout[((size_t)unit * m + i) * d + j0 + 4 * g + r] = SV[nb][r];
+          skout[((size_t)useg * m + i) * d + j0 + 4 * g + r] = SK[nb][r];
+          svout[((size_t)useg * m + i) * d + j0 + 4 * g + r] = SV[nb][r];
         }
       }
     }
@@ -1337,6 +1358,37 @@ __global__ void k_export_state(const T* __restrict__ kk, const T* __restrict__ v
   if (blockIdx.x == 0 && threadIdx.x == 0) pos[unit] = pos0 + Tn;
 }
 
+// ---------------------------------------------------------------- segmented scan: start states
+// In place over the segment rows (unit * nseg + p) of segk / segv [.][m][d]:
+// they hold each segment's end state from a zero start and receive its start
+// state, start(0) = s0 (null: zero), start(p + 1) = D_p (.) start(p) + end(p),
+// where D_p[i] = dec[unit * nseg + p][i] is the product of 2^{G_end,i} over
+// the segment's chunks (the recurrence is linear, with one decay per slot
+// row).  The state after the last segment goes to skout / svout when not null.
+// grid (ceil(m d / 256), B*Hkv), 256 threads.
+__global__ __launch_bounds__(256) void k_scan_combine(const float* __restrict__ dec, float* __restrict__ segk,
+                                                      float* __restrict__ segv, const float* __restrict__ s0k,
+                                                      const float* __restrict__ s0v, float* __restrict__ skout,
+                                                      float* __restrict__ svout, int m, int d, int MP, int nseg) {
+  const int unit = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= m * d) return;
+  const int i = e / d;
+  const size_t u0 = (size_t)unit * m * d + e;
+  float sk = s0k ? s0k[u0] : 0.f, sv = s0v ? s0v[u0] : 0.f;
+  for (int p = 0; p < nseg; ++p) {
+    const size_t r = ((size_t)unit * nseg + p) * m * d + e;
+    const float ek = segk[r], ev = segv[r], D = dec[((size_t)unit * nseg + p) * MP + i];
+    segk[r] = sk;
+    segv[r] = sv;
+    sk = D * sk + ek;
+    sv = D * sv + ev;
+  }
+  if (skout) {
+    skout[u0] = sk;
+    svout[u0] = sv;
+  }
+}
+
 // ---------------------------------------------------------------- host launcher
 template <typename T, int C, int MP>
 static void launch_gates(const Shape& s, const T* alpha, const ProloguePtrs& pp, hipStream_t st) {
@@ -1345,13 +1397,33 @@ static void launch_gates(const Shape& s, const T* alpha, const ProloguePtrs& pp,
 }
 
 template <typename T, int D, int C, int MP>
-static void launch_scan(const Shape& s, const T* k, const T* v, const ProloguePtrs& pp, hipStream_t st) {
+static void launch_scan(const Shape& s, const T* k, const T* v, const ProloguePtrs& pp, Marks& mk,
+                        hipStream_t st) {
   const int units = s.B * s.Hkv;
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
-                       (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
-                       s.sh, s.NC);
-  else
+  if constexpr (sizeof(T) == 2) {
+    const ScanSegs sg = scan_segments(s);
+    if (sg.n > 1) {
+      // three launches: segment end states, segment start states, the walk
+      float* sk = pp.seg;
+      float* sv = sk + (size_t)units * sg.n * s.m * D;
+      float* dc = sv + (size_t)units * sg.n * s.m * D;
+      hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4, false>), dim3(D / 16, units * sg.n), dim3(64), 0, st, k, v,
+                         (const T*)pp.wt, (const float*)pp.aend, (T*)pp.sst, sk, sv, dc, (const float*)nullptr,
+                         (const float*)nullptr, s.T, s.Hkv, D, s.m, s.sh, s.NC, sg.n, sg.len);
+      mk.mark(st);
+      hipLaunchKernelGGL(k_scan_combine, dim3((s.m * D + 255) / 256, units), dim3(256), 0, st, (const float*)dc,
+                         sk, sv, pp.s0k, pp.s0v, pp.skout, pp.svout, s.m, D, MP, sg.n);
+      mk.mark(st);
+      hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4, true>), dim3(D / 16, units * sg.n), dim3(64), 0, st, k, v,
+                         (const T*)pp.wt, (const float*)pp.aend, (T*)pp.sst, (float*)nullptr, (float*)nullptr,
+                         (float*)nullptr, (const float*)sk, (const float*)sv, s.T, s.Hkv, D, s.m, s.sh, s.NC, sg.n,
+                         sg.len);
+    } else {
+      hipLaunchKernelGGL((k_state_scan_b16<C, MP, 4, true>), dim3(D / 16, units), dim3(64), 0, st, k, v,
+                         (const T*)pp.wt, (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, (float*)nullptr,
+                         pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m, s.sh, s.NC, 1, s.NC);
+    }
+  } else
     hipLaunchKernelGGL((k_state_scan<T, C, MP>), dim3(D / 16, units), dim3(64), 0, st, k, v, (const T*)pp.wt,
                        (const float*)pp.aend, (T*)pp.sst, pp.skout, pp.svout, pp.s0k, pp.s0v, s.T, s.Hkv, D, s.m,
                        s.sh, s.NC);
@@ -1380,7 +1452,7 @@ static void prologue_impl(const Shape& s, const RopeTheta& th, const T* q, const
   if (s.rope && s.win) fk.record(st);
   if (s.m > 0) {
     mk.mark(st);
-    launch_scan<T, D, C, MP>(s, k, v, pp, st);
+    launch_scan<T, D, C, MP>(s, k, v, pp, mk, st);
   }
   if (s.rope && s.win) {
     // RoPE (HBM-bound, no LDS) on the side stream beside the state scan (bound
@@ -1407,6 +1479,7 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
     mk.ev = p.events;
     StateLayout SL{};
     ProloguePtrs pp{p.ws + L.sst, p.ws + L.wt, (float*)(p.ws + L.aend), nullptr, nullptr, nullptr, nullptr, nullptr};
+    pp.seg = (float*)(p.ws + L.seg);
     pp.s0k = p.s0k;
     pp.s0v = p.s0v;
     if (s.rope && s.win) {
@@ -1460,7 +1533,7 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
         mk.mark(st);
         launch_gates<T, C, MP>(s, alpha, pp, st);
         mk.mark(st);
-        launch_scan<T, D, C, MP>(s, k, v, pp, st);
+        launch_scan<T, D, C, MP>(s, k, v, pp, mk, st);
         if (s.rope) launch_rope<T>(s, th, q, k, pp, mk, st);
         mk.mark(st);
         hipLaunchKernelGGL((k_chunk_fwd_b16<D, MP>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
@@ -1478,7 +1551,7 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       mk.mark(st);
       launch_gates<T, C, MP>(s, alpha, pp, st);
       mk.mark(st);
-      launch_scan<T, D, C, MP>(s, k, v, pp, st);
+      launch_scan<T, D, C, MP>(s, k, v, pp, mk, st);
       const hipStream_t rs = fk.follow(st);
       if (s.rope) launch_rope<T>(s, th, q, k, pp, mk, rs);
       window(rs, nullptr, nullptr, ow, lw);
@@ -1578,10 +1651,14 @@ hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hip
 }
 
 int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
-  const char* all[8];
+  const char* all[12];
   int n = 0;
   if (s.m > 0) {
     all[n++] = "chunk_gates";
+    if (scan_segments(s).n > 1) {
+      all[n++] = "state_scan_seg";
+      all[n++] = "scan_combine";
+    }
     all[n++] = "state_scan";
   }
   if (s.rope && s.win) {

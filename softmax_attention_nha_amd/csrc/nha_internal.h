@@ -42,6 +42,37 @@ inline bool chunk_fused(const Shape& s) {
   return s.esz == 2 && s.C == 64 && (long long)s.B * s.Hkv * (s.d / 16) >= 256;
 }
 
+// Segments of the bf16 slot-state scan.  The scan walks the chunks in order
+// with one single-wave workgroup per (batch row, KV head, 16 state columns);
+// below 256 such waves most of the chip idles through that walk, and on
+// walks of 384 chunks or more the chunks are cut into n segments of len
+// chunks (up to 768 waves in all, at least 8 chunks a segment): every
+// segment's end state from a zero start, then the segments' start states in
+// order, then every segment walked again from its start state, writing the
+// chunk-start states.  On shorter walks the single walk runs beside the
+// window branch, which the segments' extra waves would crowd out.
+struct ScanSegs {
+  int n, len;
+};
+inline ScanSegs scan_segments(const Shape& s) {
+  ScanSegs r{1, s.NC};
+  if (s.esz != 2 || s.m == 0) return r;
+  const long long base = (long long)s.B * s.Hkv * (s.d / 16);
+  if (base >= 256 || s.NC < 384) return r;
+  int n = (int)(768 / base);
+  if (n > 16) n = 16;
+  if (n > s.NC / 8) n = s.NC / 8;
+  if (n < 2) return r;
+  r.len = (s.NC + n - 1) / n;
+  r.n = (s.NC + r.len - 1) / r.len;  // no empty segment
+  return r;
+}
+
+// dalpha's cross-chunk carry (bf16 inputs): exact at every kCarryStride-th
+// chunk, summed from chunk totals in between.
+constexpr int kCarryStride = 16;
+inline int carry_ckpts(const Shape& s) { return s.esz == 2 && s.m > 0 ? (s.NC - 1) / kCarryStride : 0; }
+
 constexpr size_t kMaxLds = 160 * 1024;  // LDS bytes per workgroup on gfx950
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -52,6 +83,7 @@ struct FwdWs {
                  // [i][d] rows, bf16 in column blocks [d/16][i][16]
   size_t wt;     // per-chunk absorption weights W^T: [B*Hkv][NC][mp][C]       (dtype)
   size_t aend;   // per-chunk decay exp(G_end): [B*Hkv][NC][mp]                (float)
+  size_t seg;    // segmented scan: end / start states [2][B*Hkv*n][m][d], decays [B*Hkv*n][mp] (float)
   size_t qrot;   // RoPE'd q: [B][T][H][d]                                       (dtype)
   size_t krot;   // RoPE'd k: [B][T][Hkv][d]                                     (dtype)
   size_t rcs;    // RoPE angles (cos, sin)(t theta_i): [T][d/2]                   (float2)
@@ -70,6 +102,11 @@ inline FwdWs fwd_ws_layout(const Shape& s) {
   off += align256(units * s.NC * (size_t)s.mp * s.C * s.esz);
   L.aend = off;
   off += align256(units * s.NC * (size_t)s.mp * 4);
+  L.seg = off;
+  {
+    const ScanSegs sg = scan_segments(s);
+    if (sg.n > 1) off += align256(units * sg.n * (2 * (size_t)s.m * s.d + s.mp) * 4);
+  }
   L.qrot = off;
   if (s.rope && s.win) off += align256((size_t)s.B * s.T * s.H * s.d * s.esz);
   L.krot = off;
@@ -149,7 +186,7 @@ inline DecodeSplit decode_splits(const Shape& s) {
 // the stream cannot be created.
 struct Fork {
   hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_mid = nullptr;
   // fork point: the side stream's next launches start after everything
   // enqueued on `main` so far (launches enqueued on `main` after this point
   // are not waited for)
@@ -165,6 +202,14 @@ struct Fork {
   hipStream_t begin(hipStream_t main) const {
     record(main);
     return follow(main);
+  }
+  // a later point on `main` (mark_mid) that the side stream's following
+  // launches wait for (wait_mid), without a new fork
+  void mark_mid(hipStream_t main) const {
+    if (side) (void)hipEventRecord(ev_mid, main);
+  }
+  void wait_mid() const {
+    if (side) (void)hipStreamWaitEvent(side, ev_mid, 0);
   }
   // `main` continues after everything enqueued on the side stream so far
   void join(hipStream_t main) const {
@@ -204,6 +249,7 @@ struct ProloguePtrs {
   float* svout;
   const float* s0k = nullptr;  // initial slot states [B*Hkv][m][d], nullable = zero
   const float* s0v = nullptr;
+  float* seg = nullptr;  // the segmented scan's state rows (scan_segments n > 1)
 };
 hipError_t launch_prologue(const Shape& s, const RopeTheta& th, const void* q, const void* k, const void* v,
                            const void* alpha, const ProloguePtrs& pp, Marks& mk, hipStream_t st, const Fork& fk);

@@ -143,7 +143,8 @@ def test_stage_lists():
     d = desc()
     full, after = nha.stage_names(d, backward=1), nha.stage_names(d, backward=2)
     fwd = nha.stage_names(d)
-    assert after == [x for x in full if x not in ("rope_cs", "rope", "chunk_gates", "state_scan")]
+    assert after == [x for x in full if x not in ("rope_cs", "rope", "chunk_gates", "state_scan_seg", "scan_combine",
+                                                  "state_scan")]
     assert full[:len(full) - len(after)] == fwd[:len(full) - len(after)]
 
 
@@ -170,6 +171,29 @@ def test_forward_kernel_choice(B, H, Hkv, d, C, dtype, fused):
     # no window or no slots: never the chunk kernel
     for w, m in ((0, 64), (512, 0)):
         assert "chunk_fwd" not in nha.stage_names(nha.make_desc(B, 2048, H, Hkv, d, m, w, C, 10000.0, 0.0, dtype))
+
+
+@pytest.mark.parametrize("B,H,Hkv,d,T,dtype,segmented", [
+    (1, 16, 16, 128, 32768, torch.bfloat16, True),   # 128 scan waves, 512 chunks
+    (1, 32, 8, 128, 24576, torch.bfloat16, True),    # 64 waves, 384 chunks
+    (1, 16, 16, 128, 24512, torch.bfloat16, False),  # 383 chunks: one walk
+    (1, 16, 16, 128, 8192, torch.bfloat16, False),
+    (2, 16, 16, 128, 32768, torch.bfloat16, False),  # 256 waves: one walk
+    (1, 16, 16, 64, 32768, torch.float32, False),    # fp32 scan: one walk
+])
+def test_state_scan_segments(B, H, Hkv, d, T, dtype, segmented):
+    """Below 256 state-scan waves (B * Hkv * d / 16) and from 384 chunks on,
+    the bf16 scan runs in segments of at least 8 chunks: segment end states,
+    the segments' start states, then the walk (three launches, forward and
+    standalone backward)."""
+    dd = nha.make_desc(B, T, H, Hkv, d, 64, 512, 64, 10000.0, 0.0, dtype)
+    for names in (nha.stage_names(dd), nha.stage_names(dd, backward=1)):
+        i = names.index("state_scan")
+        if segmented:
+            assert names[i - 2:i] == ["state_scan_seg", "scan_combine"], names
+        else:
+            assert "state_scan_seg" not in names and "scan_combine" not in names, names
+    assert "state_scan" not in nha.stage_names(dd, backward=2)
 
 
 def test_decode_argument_errors():

@@ -63,6 +63,17 @@ def test_bf16_initial_state(name, w, T):
     run(wl, w, wl.C, wl.rope_base)
 
 
+def test_bf16_initial_state_segmented_scan():
+    """A walk of 385 chunks with 16 state-scan waves: the bf16 scan runs in
+    segments (end states from zero, the segments' start states from the
+    initial state, then the walk), forward and standalone backward; the
+    exported final state comes from the start-state pass."""
+    wl = WORKLOADS["1p3b"].with_(B=1, T=24576 + 37, H=2, Hkv=2, seed=58)
+    desc = nha.make_desc(wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, 64, wl.C, wl.rope_base, 0.0, wl.dtype)
+    assert "scan_combine" in nha.stage_names(desc) and "scan_combine" in nha.stage_names(desc, backward=1)
+    run(wl, 64, wl.C, wl.rope_base)
+
+
 def test_zero_initial_state_equals_plain_forward_and_backward():
     wl = WORKLOADS["1p3b"].with_(B=1, T=333, H=4, Hkv=2, seed=54)
     w = 64
