@@ -84,6 +84,19 @@ def test_pages_operator_shape_m32_w32(T):
     check_units(wl, 32, [(0, 0), (0, wl.Hkv - 1)], with_bwd=True)
 
 
+@pytest.mark.parametrize("name,T,w,unit", [("long", 32768, None, (0, 5)), ("gqa", 24576 + 37, 256, (0, 3))])
+def test_long_context_backward_segmented_scan(name, T, w, unit):
+    """Forward and backward of one unit over the full length where the state
+    scan runs in segments (fewer than 256 scan waves, 384 chunks or more) and
+    dalpha's cross-chunk carry uses its exact checkpoints: every row and every
+    gradient of the unit against the oracle (GQA: the unit's 4 query heads)."""
+    wl = WORKLOADS[name].with_(T=T)
+    w = wl.w if w is None else w
+    desc = nha.make_desc(wl.B, wl.T, wl.H, wl.Hkv, wl.d, wl.m, w, wl.C, wl.rope_base, 0.0, wl.dtype)
+    assert "scan_combine" in nha.stage_names(desc) and "carry_ckpt" in nha.stage_names(desc, backward=1)
+    check_units(wl, w, [unit], with_bwd=True)
+
+
 # ---------------------------------------------------------------- forward at full length
 @pytest.mark.parametrize("T", [16384, 32768])
 def test_long_context_forward_every_row(T):
