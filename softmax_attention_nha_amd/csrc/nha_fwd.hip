@@ -1525,16 +1525,18 @@ static hipError_t fwd_impl(const Shape& s, const RopeTheta& th, const FwdPtrs& p
       }
     };
     if (s.m > 0 && s.win && !p.separate && chunk_fused(s)) {
-      // both branches in the chunk kernel, after the gate products, the
-      // slot-state scan and RoPE, all in order on the caller's stream: the
-      // scan is a latency-bound walk over the chunks, and RoPE beside it on
-      // the side stream slowed it by more than RoPE takes alone
+      // both branches in the chunk kernel, after RoPE, the gate products and
+      // the slot-state scan, all in order on the caller's stream: the scan is
+      // a latency-bound walk over the chunks, and RoPE beside it on the side
+      // stream slowed it by more than RoPE takes alone (RoPE first: the
+      // chunk-start states the scan writes last are the freshest in the
+      // memory-side cache when the chunk kernel reads them)
       if constexpr (sizeof(T) == 2 && C == 64) {
+        if (s.rope) launch_rope<T>(s, th, q, k, pp, mk, st);
         mk.mark(st);
         launch_gates<T, C, MP>(s, alpha, pp, st);
         mk.mark(st);
         launch_scan<T, D, C, MP>(s, k, v, pp, mk, st);
-        if (s.rope) launch_rope<T>(s, th, q, k, pp, mk, st);
         mk.mark(st);
         hipLaunchKernelGGL((k_chunk_fwd_b16<D, MP>), dim3((s.T + 32 * kWinWaves - 1) / (32 * kWinWaves), s.B * s.H),
                            dim3(kWinWaves * 64), 0, st, q, k, v, alpha, (const T*)pp.sst, qr, kr, (T*)p.o, p.lse,
@@ -1653,6 +1655,11 @@ hipError_t launch_fwd(const Shape& s, const RopeTheta& th, const FwdPtrs& p, hip
 int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
   const char* all[12];
   int n = 0;
+  const bool fused = s.m > 0 && s.win && chunk_fused(s);
+  if (fused && s.rope) {  // the one-kernel form runs RoPE first
+    all[n++] = "rope_cs";
+    all[n++] = "rope";
+  }
   if (s.m > 0) {
     all[n++] = "chunk_gates";
     if (scan_segments(s).n > 1) {
@@ -1661,11 +1668,11 @@ int fwd_stages(const Shape& s, bool with_state, const char** names, int max) {
     }
     all[n++] = "state_scan";
   }
-  if (s.rope && s.win) {
+  if (s.rope && s.win && !fused) {
     all[n++] = "rope_cs";
     all[n++] = "rope";
   }
-  if (s.m > 0 && s.win && chunk_fused(s)) {
+  if (fused) {
     all[n++] = "chunk_fwd";
   } else {
     if (s.win) all[n++] = "win_fwd";  // (first: the slot kernel merges it)
