@@ -54,6 +54,46 @@ __device__ __forceinline__ void ld8f_f32(const float* p, float (&x)[8]) {
   }
 }
 
+// A gate's value from its bits in a 32-bit register (bf16: zero-extended; a
+// bf16 is the upper half of the float it stands for).
+template <typename T>
+__device__ __forceinline__ float gate_from_bits(uint32_t r) {
+  return __uint_as_float(sizeof(T) == 2 ? r << 16 : r);
+}
+
+// The new token's ring entries: thread c < D holds channel c of k_t and v_t,
+// the rotate-half partner channel of k_t and the channel's RoPE frequency.
+// Loaded at kernel entry (they depend on no other load; a per-thread index
+// into the argument block is a memory load too) and stored once every read of
+// the ring row they replace is done.
+template <typename T, int D>
+struct RingPush {
+  T kx, vx, kp;
+  double th;
+  __device__ __forceinline__ void load(const T* __restrict__ kin, const T* __restrict__ vin, size_t src,
+                                       const RopeTheta& rt, int tid) {
+    constexpr int HALF = D / 2;
+    const int c = tid < D ? tid : 0;
+    kx = kin[src + c];
+    vx = vin[src + c];
+    kp = kin[src + (c < HALF ? c + HALF : c - HALF)];
+    th = rt.theta[c % HALF];
+  }
+  // thread tid < D; row dst of the rings, position t
+  __device__ __forceinline__ void store(T* __restrict__ RK, T* __restrict__ RV, T* __restrict__ RKR, size_t dst,
+                                        long long t, int rope, int tid) const {
+    constexpr int HALF = D / 2;
+    RK[dst + tid] = kx;
+    RV[dst + tid] = vx;
+    if (rope) {
+      const float x = to_f<T>(kx), pair = to_f<T>(kp);
+      float cs, sn;
+      dec_angle(th, t, cs, sn);
+      RKR[dst + tid] = to_t<T>(tid < HALF ? x * cs - pair * sn : x * cs + pair * sn);
+    }
+  }
+};
+
 // Sum over the LPK lanes of one key group (lanes 16-aligned blocks of LPK).
 template <int LPK>
 __device__ __forceinline__ float group_sum(float x) {
@@ -93,29 +133,49 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
   __shared__ float wsum[4][kDecGH][D + 1];
   const int tid = threadIdx.x, grp = tid / LPK, li = tid % LPK, wv = tid >> 6;
   const int s = blockIdx.x, unit = blockIdx.y, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  // Every load that does not depend on the position goes out with the
+  // position's, raw (converted only after the last of them is issued), so
+  // that the step waits on two memory round trips: these, then the ring rows
+  // the position selects.
+  const long long t = pos[unit];
+  // this lane's RoPE frequencies (a per-lane index into the argument block
+  // is a memory load)
+  double thv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) thv[e] = th.theta[(8 * li + e) % HALF];
+  // the first head group's query rows
+  typename Vec<T>::v8 q0[kDecGH];
+#pragma unroll
+  for (int hh = 0; hh < kDecGH; ++hh)
+    q0[hh] = ld8<T>(q + ((size_t)b * H + hg * G + (hh < G ? hh : 0)) * D + 8 * li);
+  // the new token, and this group's slot rows and their gates (slot e = key
+  // index e < m; address clamped)
   const size_t krow = ((size_t)b * Hkv + hg) * D + 8 * li;  // this lane's channels of k_t / v_t
-  // rows that do not depend on the position: the new token, its gates and
-  // this group's slot rows (slot e = key index e < m; address clamped)
-  float knew[8], vnew[8];
-  ld8f_row<T>(kin + krow, knew);
-  ld8f_row<T>(vin + krow, vnew);
+  const typename Vec<T>::v8 knew8 = ld8<T>(kin + krow), vnew8 = ld8<T>(vin + krow);
   float* sk = SK + (size_t)unit * m * D + 8 * li;
   float* sv = SV + (size_t)unit * m * D + 8 * li;
+  // through buffer resources over the unit's slot rows and gates: no branch
+  // on m (a branch would place each gate's conversion, and a wait for its
+  // load, before the next row's loads); with m = 0 the resources are empty
+  // and the loads read zeros without touching memory
+  const __amdgpu_buffer_rsrc_t rsk = buf_rsrc(SK + (size_t)unit * m * D, (uint32_t)(m * D * 4));
+  const __amdgpu_buffer_rsrc_t rsv = buf_rsrc(SV + (size_t)unit * m * D, (uint32_t)(m * D * 4));
+  const __amdgpu_buffer_rsrc_t rga = buf_rsrc(alpha + ((size_t)b * Hkv + hg) * m, (uint32_t)(m * sizeof(T)));
   float xk[KPG][8], xv[KPG][8], ga[KPG];
+  uint32_t gar[KPG];  // raw gate bits
 #pragma unroll
   for (int kk = 0; kk < KPG; ++kk) {
-    if (m > 0) {
-      const int e = min(s + NS * (grp + NG * kk), m - 1);
-      ld8f_f32(sk + (size_t)e * D, xk[kk]);
-      ld8f_f32(sv + (size_t)e * D, xv[kk]);
-      ga[kk] = to_f<T>(alpha[((size_t)b * Hkv + hg) * m + e]);
-    } else {  // no slots
+    const int e = max(min(s + NS * (grp + NG * kk), m - 1), 0);
+    const uint32_t off = (uint32_t)(e * D + 8 * li) * 4u;
+    const floatx8 rk8 = buf_ld16(rsk, off, (floatx8*)nullptr), rv8 = buf_ld16(rsv, off, (floatx8*)nullptr);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) xk[kk][r] = xv[kk][r] = 0.f;
-      ga[kk] = 1.f;
+    for (int r = 0; r < 8; ++r) {
+      xk[kk][r] = rk8[r];
+      xv[kk][r] = rv8[r];
     }
+    gar[kk] = sizeof(T) == 2 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rga, (uint32_t)e * 2u, 0, 0)
+                             : __builtin_amdgcn_raw_buffer_load_b32(rga, (uint32_t)e * 4u, 0, 0);
   }
-  const long long t = pos[unit];
   const long long nwin = (w == 0) ? 0 : (t + 1 < w ? t + 1 : w);
   const int nkeys = m + (int)nwin;
   const long long jfirst = t - nwin + 1;
@@ -143,6 +203,14 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
       wvr[kk] = ld8<T>(rv + rr);
     }
   }
+  float knew[8], vnew[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    knew[r] = to_f<T>(knew8[r]);
+    vnew[r] = to_f<T>(vnew8[r]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < KPG; ++kk) ga[kk] = gate_from_bits<T>(gar[kk]);
   if (sh == 0) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -155,7 +223,7 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
   float cs[8], sn[8];
   if (rope) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dec_angle(th.theta[(8 * li + e) % HALF], t, cs[e], sn[e]);
+    for (int e = 0; e < 8; ++e) dec_angle(thv[e], t, cs[e], sn[e]);
   }
   float knr[8];
 #pragma unroll
@@ -203,7 +271,12 @@ __global__ __launch_bounds__(256) void k_dec_split(const T* __restrict__ q, cons
 #pragma unroll
     for (int hh = 0; hh < kDecGH; ++hh) {
       const int h = hg * G + h0 + (hh < nh ? hh : 0);
-      ld8f_row<T>(q + ((size_t)b * H + h) * D + 8 * li, qs[hh]);
+      if (h0 == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[hh][e] = to_f<T>(q0[hh][e]);
+      } else {
+        ld8f_row<T>(q + ((size_t)b * H + h) * D + 8 * li, qs[hh]);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) qr[hh][e] = qs[hh][e];
       if (rope && hh < nh) dec_rope_cs<D>(qr[hh], li, cs, sn);
@@ -335,20 +408,29 @@ __global__ __launch_bounds__(256) void k_dec_merge(const float* __restrict__ par
   __shared__ float zred[SG];
   const int tid = threadIdx.x, unit = blockIdx.x, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
   const long long t = pos[unit];
-  for (int hh = 0; hh < G; ++hh) {
+  // thread (sp, c) sums channel c over the splits sp, sp + SG, ...: every
+  // load first (addresses clamped), then the sums in split order
+  const int c = tid % D, sp = tid / D;
+  float xo[PER], xz[PER], mx;
+  auto load_head = [&](int hh) {
     const float* pr = part + ((size_t)(b * H + hg * G + hh)) * kDecodeSplitMax * PP;
-    // thread (sp, c) sums channel c over the splits sp, sp + SG, ...: every
-    // load first (addresses clamped), then the sums in split order
-    const int c = tid % D, sp = tid / D;
-    float xo[PER], xz[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int sx = min(sp + SG * i, NS - 1);
       xo[i] = pr[sx * PP + 4 + c];
       xz[i] = pr[sx * PP + 1];
     }
+    mx = pr[min(tid & 63, NS - 1) * PP];
+  };
+  load_head(0);
+  // the ring push's rows after the first head's partials: both in flight
+  // together, neither waiting on the other
+  RingPush<T, D> rp;
+  rp.load(kin, vin, ((size_t)b * Hkv + hg) * D, th, tid);
+  for (int hh = 0; hh < G; ++hh) {
+    if (hh > 0) load_head(hh);
     if (tid < 64) {
-      const float mx = tid < NS ? pr[tid * PP] : -INFINITY;
+      if (tid >= NS) mx = -INFINITY;
       float M = mx;
 #pragma unroll
       for (int o2 = 1; o2 < 64; o2 <<= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
@@ -380,19 +462,7 @@ __global__ __launch_bounds__(256) void k_dec_merge(const float* __restrict__ par
     __syncthreads();
   }
   // push (k_t, v_t) into ring row t mod w (and the key with RoPE at t)
-  if (w > 0 && tid < D) {
-    const size_t src = ((size_t)b * Hkv + hg) * D, dst = ((size_t)unit * w + (size_t)(t % w)) * D;
-    const float x = to_f<T>(kin[src + tid]);
-    RK[dst + tid] = kin[src + tid];
-    RV[dst + tid] = vin[src + tid];
-    if (rope) {
-      const int i = tid % HALF;
-      const float pair = to_f<T>(kin[src + (tid < HALF ? tid + HALF : tid - HALF)]);
-      float cs, sn;
-      dec_angle(th.theta[i], t, cs, sn);
-      RKR[dst + tid] = to_t<T>(tid < HALF ? x * cs - pair * sn : x * cs + pair * sn);
-    }
-  }
+  if (w > 0 && tid < D) rp.store(RK, RV, RKR, ((size_t)unit * w + (size_t)(t % w)) * D, t, rope, tid);
   if (tid == 0) pos[unit] = t + 1;
 }
 
@@ -422,6 +492,11 @@ __global__ __launch_bounds__(256) void k_dec_fused(const T* __restrict__ q, cons
   __shared__ float run_m[GH], run_z[GH];
   const int tid = threadIdx.x, grp = tid / LPK, li = tid % LPK, wv = tid >> 6;
   const int unit = blockIdx.x, b = unit / Hkv, hg = unit % Hkv, G = H / Hkv;
+  double thv[8];  // this lane's RoPE frequencies, loaded first (as in k_dec_split)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) thv[e] = th.theta[(8 * li + e) % HALF];
+  RingPush<T, D> rp;
+  rp.load(kin, vin, ((size_t)b * Hkv + hg) * D, th, tid);
   const size_t krow = ((size_t)b * Hkv + hg) * D + 8 * li;
   float knew[8], vnew[8];
   ld8f_row<T>(kin + krow, knew);
@@ -452,7 +527,7 @@ __global__ __launch_bounds__(256) void k_dec_fused(const T* __restrict__ q, cons
   float cs[8], sn[8];
   if (rope) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dec_angle(th.theta[(8 * li + e) % HALF], t, cs[e], sn[e]);
+    for (int e = 0; e < 8; ++e) dec_angle(thv[e], t, cs[e], sn[e]);
   }
   float knr[8];
 #pragma unroll
@@ -647,19 +722,7 @@ __global__ __launch_bounds__(256) void k_dec_fused(const T* __restrict__ q, cons
   }
   // every read of ring row t mod w is behind the barriers above: push (k_t,
   // v_t) there (and the key with RoPE at t) and advance the position
-  if (w > 0 && tid < D) {
-    const size_t src = ((size_t)b * Hkv + hg) * D, dst = ((size_t)unit * w + (size_t)(t % w)) * D;
-    const float x = to_f<T>(kin[src + tid]);
-    RK[dst + tid] = kin[src + tid];
-    RV[dst + tid] = vin[src + tid];
-    if (rope) {
-      const int i = tid % HALF;
-      const float pair = to_f<T>(kin[src + (tid < HALF ? tid + HALF : tid - HALF)]);
-      float c2, s2;
-      dec_angle(th.theta[i], t, c2, s2);
-      RKR[dst + tid] = to_t<T>(tid < HALF ? x * c2 - pair * s2 : x * c2 + pair * s2);
-    }
-  }
+  if (w > 0 && tid < D) rp.store(RK, RV, RKR, ((size_t)unit * w + (size_t)(t % w)) * D, t, rope, tid);
   if (tid == 0) pos[unit] = t + 1;
 }
 
