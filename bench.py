@@ -843,6 +843,10 @@ def main():
 
     dom = max(per, key=per.get)
     roof = roofline(dom, per[dom] * 1e3, wl, w, e)
+    # the next-longest kernel too: where two kernels take about the same time
+    # the dominant one can differ from box to box
+    rest = [n for n in per if n != dom]
+    nxt = max(rest, key=per.get) if rest else None
 
     ok = bool(torch.isfinite(o.float()).all().item())
     if do_bwd:
@@ -885,6 +889,7 @@ def main():
         "kernels_us": {kname: round(x * 1e3, 2) for kname, x in per.items()},
         "outputs_finite": ok,
         "roofline": roof,
+        "roofline_next_kernel": roofline(nxt, per[nxt] * 1e3, wl, w, e) if nxt else None,
     }
     if not args.no_context and args.workload == "headline" and do_bwd:
         line["device_clock"] = device_clock_under_load(step)
