@@ -122,7 +122,13 @@ typedef struct {
 } nha_desc;
 
 /* Workspace bytes that nha_fwd / nha_bwd need for this descriptor; 0 when the
- * descriptor is invalid or unsupported (call nha_check_desc for the reason). */
+ * descriptor is invalid or unsupported (call nha_check_desc for the reason).
+ * nha_check_desc applies the forward's rules.  The backward has one limit
+ * more: its fp32 tiles must fit the 160 KB of LDS of a workgroup, which rules
+ * out fp32 at d = 128 (any m) and at d = 64 with m > 32; there
+ * nha_bwd_workspace_size returns 0 although nha_check_desc returns NHA_OK,
+ * and nha_bwd returns NHA_ERR_UNSUPPORTED.  (bf16 has no such limit; the fp32
+ * forward is unsupported only at d = 128 with m > 32.) */
 size_t nha_fwd_workspace_size(const nha_desc* desc);
 size_t nha_bwd_workspace_size(const nha_desc* desc);
 

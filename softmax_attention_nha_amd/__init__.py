@@ -223,7 +223,11 @@ def workspace_size(desc, backward=False):
     lib = load()
     n = (lib.nha_bwd_workspace_size if backward else lib.nha_fwd_workspace_size)(ctypes.byref(desc))
     if n == 0:
-        raise NhaError(lib.nha_check_desc(ctypes.byref(desc)), "workspace size")
+        # nha_check_desc applies the forward's rules: a descriptor it accepts
+        # with no backward workspace is one the backward does not support
+        rc = lib.nha_check_desc(ctypes.byref(desc))
+        raise NhaError(rc if rc != NHA_OK else NHA_ERR_UNSUPPORTED,
+                       "backward workspace size" if backward else "workspace size")
     return n
 
 
@@ -390,8 +394,12 @@ def weighted_workspace_size(desc):
     lib = load()
     n = lib.nha_weighted_workspace_size(ctypes.byref(desc))
     if n == 0:
+        # past nha_check_desc: m < 1 or w < 1 (invalid for this mode), else
+        # the backward's LDS limit (unsupported)
         rc = lib.nha_check_desc(ctypes.byref(desc))
-        raise NhaError(rc if rc != NHA_OK else NHA_ERR_INVALID_ARG, "weighted workspace size")
+        if rc == NHA_OK:
+            rc = NHA_ERR_INVALID_ARG if desc.m < 1 or desc.w < 1 else NHA_ERR_UNSUPPORTED
+        raise NhaError(rc, "weighted workspace size")
     return n
 
 

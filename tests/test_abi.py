@@ -315,3 +315,31 @@ def test_weighted_fusion_argument_errors():
     assert lib.nha_bwd_weighted(ctypes.byref(d), *args, MIS, A, big, None) == nha.NHA_ERR_INVALID_ARG
     assert lib.nha_bwd_weighted(ctypes.byref(d), *args, None, A, ctypes.c_size_t(n - 1),
                                 None) == nha.NHA_ERR_WORKSPACE
+
+
+def test_backward_lds_limit_is_reported_as_unsupported():
+    # the fp32 backward's tiles exceed a workgroup's LDS at d = 128 (any m)
+    # and at d = 64 with m > 32: no backward workspace, and the binding names
+    # the reason although nha_check_desc (the forward's rules) accepts them
+    lib = nha.load()
+    for d, m, fwd_ok, bwd_ok in [(32, 64, True, True), (64, 32, True, True), (64, 33, True, False),
+                                 (128, 0, True, False), (128, 32, True, False), (128, 33, False, False)]:
+        desc = nha.make_desc(1, 100, 2, 2, d, m, 16, 64, 10000.0, 0.0, torch.float32)
+        assert (lib.nha_fwd_workspace_size(ctypes.byref(desc)) > 0) == fwd_ok, (d, m)
+        assert (lib.nha_bwd_workspace_size(ctypes.byref(desc)) > 0) == bwd_ok, (d, m)
+        if not bwd_ok:
+            with pytest.raises(nha.NhaError) as ei:
+                nha.workspace_size(desc, backward=True)
+            assert ei.value.status == nha.NHA_ERR_UNSUPPORTED
+        if fwd_ok:
+            assert lib.nha_check_desc(ctypes.byref(desc)) == nha.NHA_OK
+        # bf16 has no such limit
+        desc = nha.make_desc(1, 100, 2, 2, d, m, 16, 64, 10000.0, 0.0, torch.bfloat16)
+        assert nha.workspace_size(desc, backward=True) > 0 and nha.workspace_size(desc) > 0
+    # the weighted-fusion mode: m = 0 is invalid there, the LDS limit unsupported
+    with pytest.raises(nha.NhaError) as ei:
+        nha.weighted_workspace_size(nha.make_desc(1, 100, 2, 2, 64, 0, 16, 64, 10000.0, 0.0, torch.float32))
+    assert ei.value.status == nha.NHA_ERR_INVALID_ARG
+    with pytest.raises(nha.NhaError) as ei:
+        nha.weighted_workspace_size(nha.make_desc(1, 100, 2, 2, 128, 16, 16, 64, 10000.0, 0.0, torch.float32))
+    assert ei.value.status == nha.NHA_ERR_UNSUPPORTED
