@@ -71,3 +71,55 @@ def test_random_shape_fwd_bwd(case):
         if m == 0 and name == "dalpha":
             continue  # no gates without slots
         compare(name, f64(x), r, tol["grad"], tol["rel"])
+
+
+def draw_decode_cases(n, seed=20261204):
+    rng = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = rng.choice([torch.bfloat16, torch.bfloat16, torch.float32])
+        d = rng.choice([32, 64, 128])
+        m = rng.choice([0, 1, 7, 32, 33, 64])
+        w = rng.choice([0, 1, 5, 16, 40, 100])
+        if m == 0 and w == 0:
+            continue
+        if dtype == torch.float32 and d == 128 and m > 32:
+            continue  # the fp32 prefill's tiles exceed the LDS there
+        C = rng.choice([16, 32, 64])
+        G = rng.choice([1, 2, 4])
+        # every third case with B * Hkv >= 256 units (one workgroup per unit
+        # fills the chip: the single-launch step)
+        many = len(cases) % 3 == 2
+        Hkv = 16 if many else rng.choice([1, 2, 3])
+        B = 16 if many else rng.choice([1, 2, 3])
+        T0 = rng.randint(0, 150)
+        steps = rng.randint(1, 24)
+        base = rng.choice([10000.0, 500.0, 0.0])
+        cases.append((dtype, B, G * Hkv, Hkv, T0, steps, d, m, w, C, base, rng.randrange(1 << 16)))
+    return cases
+
+
+DECODE_CASES = draw_decode_cases(12)
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=["%s-B%dH%dKV%dT0_%d+%d-d%dm%dw%dC%d-b%g" % (
+    "bf16" if c[0] == torch.bfloat16 else "f32", *c[1:11]) for c in DECODE_CASES])
+def test_random_shape_prefill_then_decode(case):
+    """nha_fwd over the first T0 tokens exporting the state (T0 = 0: the zero
+    state), then one nha_decode_step per token: the outputs equal the oracle's
+    forward over the whole sequence at those rows."""
+    dtype, B, H, Hkv, T0, steps, d, m, w, C, base, seed = case
+    log("case random decode %s" % (case,))
+    wl = WORKLOADS["tiny"].with_(B=B, H=H, Hkv=Hkv, T=T0 + steps, d=d, m=m, w=w, C=C, dtype=dtype, rope_base=base,
+                                 seed=seed)
+    q, k, v, a = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    state = nha.decode_state(B, H, Hkv, d, m, w, base, dtype=dtype, device=dev)
+    if T0 > 0:
+        nha.fwd(*(x[:, :T0].contiguous().to(dev) for x in (q, k, v, a)), w, C=C, rope_base=base, state_out=state)
+    outs = [nha.decode_step(*(x[:, t].contiguous().to(dev) for x in (q, k, v, a)), state, w, rope_base=base)
+            for t in range(T0, T0 + steps)]
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.fwd(f64(q), f64(k), f64(v), f64(a), w, rope_base=base)
+    tol = TOL[dtype]
+    compare("o_dec", f64(torch.stack(outs, 1)), o_ref[:, T0:], tol["o"], tol["rel"])
