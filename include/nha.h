@@ -276,7 +276,9 @@ nha_status nha_bwd_s0(const nha_desc* desc, const void* q, const void* k,
  *   state_out nullable; receives the state after the segment (pos0 + T
  *             tokens); may be state_in itself
  *   ws        device workspace of nha_continue_workspace_size bytes (serves
- *             both calls and every pos0)
+ *             both calls and every pos0; so the size applies the backward's
+ *             LDS limit to both: with fp32 it is 0, and the calls return
+ *             NHA_ERR_UNSUPPORTED, at d = 128 and at d = 64 with m > 32)
  * nha_bwd_continue: gradients of the segment's loss w.r.t. its inputs (dq,
  *   dk, dv, dalpha as nha_bwd), w.r.t. the state's slots (ds0k, ds0v float
  *   [B][Hkv][m][d]) and, nullable, w.r.t. its ring keys and values (drk, drv

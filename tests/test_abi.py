@@ -336,6 +336,12 @@ def test_backward_lds_limit_is_reported_as_unsupported():
         # bf16 has no such limit
         desc = nha.make_desc(1, 100, 2, 2, d, m, 16, 64, 10000.0, 0.0, torch.bfloat16)
         assert nha.workspace_size(desc, backward=True) > 0 and nha.workspace_size(desc) > 0
+    # chunked prefill: one workspace serves the continued forward and
+    # backward, so its size applies the backward's limit to both
+    with pytest.raises(nha.NhaError) as ei:
+        nha.continue_workspace_size(nha.make_desc(1, 100, 2, 2, 128, 7, 16, 64, 10000.0, 0.0, torch.float32))
+    assert ei.value.status == nha.NHA_ERR_UNSUPPORTED
+    assert nha.continue_workspace_size(nha.make_desc(1, 100, 2, 2, 128, 64, 16, 64, 10000.0, 0.0, torch.bfloat16)) > 0
     # the weighted-fusion mode: m = 0 is invalid there, the LDS limit unsupported
     with pytest.raises(nha.NhaError) as ei:
         nha.weighted_workspace_size(nha.make_desc(1, 100, 2, 2, 64, 0, 16, 64, 10000.0, 0.0, torch.float32))

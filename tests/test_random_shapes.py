@@ -123,3 +123,50 @@ def test_random_shape_prefill_then_decode(case):
     o_ref, _ = oracle.fwd(f64(q), f64(k), f64(v), f64(a), w, rope_base=base)
     tol = TOL[dtype]
     compare("o_dec", f64(torch.stack(outs, 1)), o_ref[:, T0:], tol["o"], tol["rel"])
+
+
+def draw_continue_cases(n, seed=20261205):
+    rng = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = rng.choice([torch.bfloat16, torch.bfloat16, torch.float32])
+        d = rng.choice([32, 64, 128])
+        m = rng.choice([0, 1, 7, 32, 33, 64])
+        w = rng.choice([1, 5, 16, 40, 100])  # a window to continue (the ring)
+        if dtype == torch.float32 and (d == 128 or (d == 64 and m > 32)):
+            continue  # one workspace serves the continued backward too: its fp32 LDS limit
+        C = rng.choice([16, 32, 64])
+        G = rng.choice([1, 2, 4])
+        Hkv = rng.choice([1, 2, 3])
+        B = rng.choice([1, 2])
+        T1 = rng.randint(1, 200)
+        T2 = rng.randint(1, 200)
+        base = rng.choice([10000.0, 500.0, 0.0])
+        cases.append((dtype, B, G * Hkv, Hkv, T1, T2, d, m, w, C, base, rng.randrange(1 << 16)))
+    return cases
+
+
+CONTINUE_CASES = draw_continue_cases(10)
+
+
+@pytest.mark.parametrize("case", CONTINUE_CASES, ids=["%s-B%dH%dKV%dT%d+%d-d%dm%dw%dC%d-b%g" % (
+    "bf16" if c[0] == torch.bfloat16 else "f32", *c[1:11]) for c in CONTINUE_CASES])
+def test_random_shape_chunked_prefill(case):
+    """nha_fwd over T1 tokens exporting the decode state, then
+    nha_fwd_continue over the next T2 from that state: the second segment's
+    o and lse equal the oracle's forward over all T1 + T2 tokens at its rows."""
+    dtype, B, H, Hkv, T1, T2, d, m, w, C, base, seed = case
+    log("case random continue %s" % (case,))
+    wl = WORKLOADS["tiny"].with_(B=B, H=H, Hkv=Hkv, T=T1 + T2, d=d, m=m, w=w, C=C, dtype=dtype, rope_base=base,
+                                 seed=seed)
+    q, k, v, a = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    state = nha.decode_state(B, H, Hkv, d, m, w, base, dtype=dtype, device=dev)
+    nha.fwd(*(x[:, :T1].contiguous().to(dev) for x in (q, k, v, a)), w, C=C, rope_base=base, state_out=state)
+    o2, l2 = nha.fwd_continue(*(x[:, T1:].contiguous().to(dev) for x in (q, k, v, a)), w, state, T1, C=C,
+                              rope_base=base)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.fwd(f64(q), f64(k), f64(v), f64(a), w, rope_base=base)
+    tol = TOL[dtype]
+    compare("o", f64(o2), o_ref[:, T1:], tol["o"], tol["rel"])
+    compare("lse", f64(l2), l_ref[:, :, T1:], tol["lse"], tol["rel"])
